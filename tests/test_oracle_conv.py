@@ -1,0 +1,188 @@
+"""Pins of the oracle's modality-aware short convolution (CPU only).
+
+The conv is defined on the Chimera pages (genai-atlas "How it works"; rainbus
+"core method"): a causal 1D depthwise conv over text tokens and a depthwise 3D
+conv over the visual tokens on their (t, h, w) grid, run separately per
+modality.  The oracle is pinned to things other than itself:
+
+* a library routine (torch CPU ``conv1d`` / ``conv3d`` in fp64, groups =
+  channels) with the padding each reading implies;
+* impulse inputs, which reproduce the taps and fix their orientation;
+* all-ones inputs, whose outputs are closed-form sums of the in-bounds taps;
+* modality separation and text causality.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from linear_attention_sequence_modality_amd.inputs import CONFIGS, StreamConfig, make_inputs
+
+
+def _torch_reference(x, wt, wv, n_text, grid, causal_t):
+    """Library-routine statement of the two convs (fp64 torch CPU)."""
+    x = torch.from_numpy(np.asarray(x, dtype=np.float64))
+    B, T, C = x.shape
+    gt, gh, gw = grid
+    wt = torch.from_numpy(np.asarray(wt, dtype=np.float64))
+    wv = torch.from_numpy(np.asarray(wv, dtype=np.float64))
+    kt = wt.shape[1]
+    out = torch.empty_like(x)
+    if n_text:
+        xt = x[:, :n_text].permute(0, 2, 1)                       # [B, C, n_text]
+        xt = F.pad(xt, (kt - 1, 0))
+        out[:, :n_text] = F.conv1d(xt, wt[:, None, :], groups=C).permute(0, 2, 1)
+    if gt * gh * gw:
+        xv = x[:, n_text:].reshape(B, gt, gh, gw, C).permute(0, 4, 1, 2, 3)
+        pad_t = (2, 0) if causal_t else (1, 1)
+        xv = F.pad(xv, (1, 1, 1, 1) + pad_t)
+        yv = F.conv3d(xv, wv.reshape(C, 1, 3, 3, 3), groups=C)
+        out[:, n_text:] = yv.permute(0, 2, 3, 4, 1).reshape(B, gt * gh * gw, C)
+    return out.numpy()
+
+
+@pytest.mark.parametrize("n_text,grid,causal_t", [
+    (5, (3, 4, 5), 0),
+    (5, (3, 4, 5), 1),
+    (0, (2, 3, 3), 0),
+    (7, (1, 6, 4), 0),       # image: only the middle temporal slice contributes
+    (9, (0, 0, 0), 0),       # text only
+    (1, (4, 1, 1), 1),
+])
+def test_conv_matches_torch_conv(n_text, grid, causal_t):
+    rng = np.random.default_rng(7)
+    B, C = 2, 6
+    T = n_text + grid[0] * grid[1] * grid[2]
+    x = rng.standard_normal((B, T, C))
+    wt = rng.standard_normal((C, 4))
+    wv = rng.standard_normal((C, 27))
+    y = oracle.short_conv(x, wt, wv, n_text, grid, causal_t)
+    ref = _torch_reference(x, wt, wv, n_text, grid, causal_t)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_text_impulse_fixes_tap_orientation():
+    C, n_text = 3, 10
+    wt = np.arange(1, 1 + 4 * C, dtype=np.float64).reshape(C, 4)
+    wv = np.zeros((C, 27))
+    i0, c0 = 4, 1
+    x = np.zeros((1, n_text, C))
+    x[0, i0, c0] = 1.0
+    y = oracle.short_conv(x, wt, wv, n_text, (0, 0, 0))
+    # y[i] = w[i0 - i + 3] for i in [i0, i0 + 3]; the current token meets the last tap.
+    for i in range(n_text):
+        j = i0 - i + 3
+        expect = wt[c0, j] if 0 <= j < 4 else 0.0
+        assert y[0, i, c0] == expect
+    assert np.all(y[0, :, [0, 2]] == 0.0)
+
+
+@pytest.mark.parametrize("causal_t", [0, 1])
+def test_visual_impulse_fixes_tap_orientation(causal_t):
+    C, n_text, grid = 2, 3, (4, 5, 6)
+    gt, gh, gw = grid
+    wt = np.zeros((C, 4))
+    wv = np.arange(1, 1 + 27 * C, dtype=np.float64).reshape(C, 27)
+    t0, h0, w0, c0 = 2, 2, 3, 1
+    T = n_text + gt * gh * gw
+    x = np.zeros((1, T, C))
+    x[0, n_text + (t0 * gh + h0) * gw + w0, c0] = 1.0
+    y = oracle.short_conv(x, wt, wv, n_text, grid, causal_t)
+    pt = 2 if causal_t else 1
+    for t in range(gt):
+        for h in range(gh):
+            for w in range(gw):
+                a, b, e = t0 - t + pt, h0 - h + 1, w0 - w + 1
+                inside = 0 <= a < 3 and 0 <= b < 3 and 0 <= e < 3
+                expect = wv[c0, (a * 3 + b) * 3 + e] if inside else 0.0
+                assert y[0, n_text + (t * gh + h) * gw + w, c0] == expect
+    assert np.all(y[0, :n_text] == 0.0)
+
+
+@pytest.mark.parametrize("causal_t", [0, 1])
+def test_all_ones_gives_in_bounds_tap_sums(causal_t):
+    """Closed form: an all-ones stream returns the sum of the taps that land inside."""
+    C, n_text, grid = 2, 6, (3, 4, 5)
+    gt, gh, gw = grid
+    rng = np.random.default_rng(3)
+    wt = rng.standard_normal((C, 4))
+    wv = rng.standard_normal((C, 27))
+    T = n_text + gt * gh * gw
+    y = oracle.short_conv(np.ones((1, T, C)), wt, wv, n_text, grid, causal_t)
+    for i in range(n_text):
+        first = max(0, 3 - i)                     # taps j with i - 3 + j >= 0
+        np.testing.assert_allclose(y[0, i], wt[:, first:].sum(axis=1), rtol=1e-14)
+    pt = 2 if causal_t else 1
+    w3 = wv.reshape(C, 3, 3, 3)
+    for t in range(gt):
+        for h in range(gh):
+            for w in range(gw):
+                ta = [a for a in range(3) if 0 <= t + a - pt < gt]
+                hb = [b for b in range(3) if 0 <= h + b - 1 < gh]
+                we = [e for e in range(3) if 0 <= w + e - 1 < gw]
+                expect = w3[:, ta][:, :, hb][:, :, :, we].sum(axis=(1, 2, 3))
+                np.testing.assert_allclose(y[0, n_text + (t * gh + h) * gw + w], expect,
+                                           rtol=1e-13, atol=1e-14)
+
+
+def test_modalities_never_read_each_other():
+    rng = np.random.default_rng(11)
+    C, n_text, grid = 4, 8, (2, 3, 4)
+    T = n_text + 24
+    x = rng.standard_normal((1, T, C))
+    wt, wv = rng.standard_normal((C, 4)), rng.standard_normal((C, 27))
+    y = oracle.short_conv(x, wt, wv, n_text, grid)
+    x2 = x.copy()
+    x2[0, :n_text] += rng.standard_normal((n_text, C))
+    y2 = oracle.short_conv(x2, wt, wv, n_text, grid)
+    assert np.array_equal(y[0, n_text:], y2[0, n_text:])
+    x3 = x.copy()
+    x3[0, n_text:] += rng.standard_normal((T - n_text, C))
+    y3 = oracle.short_conv(x3, wt, wv, n_text, grid)
+    assert np.array_equal(y[0, :n_text], y3[0, :n_text])
+
+
+def test_text_conv_is_causal():
+    rng = np.random.default_rng(12)
+    C, n_text = 3, 12
+    x = rng.standard_normal((1, n_text, C))
+    wt, wv = rng.standard_normal((C, 4)), rng.standard_normal((C, 27))
+    y = oracle.short_conv(x, wt, wv, n_text, (0, 0, 0))
+    for i in range(n_text - 1):
+        x2 = x.copy()
+        x2[0, i + 1:] = rng.standard_normal((n_text - i - 1, C))
+        y2 = oracle.short_conv(x2, wt, wv, n_text, (0, 0, 0))
+        assert np.array_equal(y[0, :i + 1], y2[0, :i + 1])
+
+
+def test_time_causal_variant_ignores_future_frames():
+    rng = np.random.default_rng(13)
+    C, n_text, grid = 2, 3, (4, 3, 3)
+    gt, gh, gw = grid
+    T = n_text + gt * gh * gw
+    x = rng.standard_normal((1, T, C))
+    wt, wv = rng.standard_normal((C, 4)), rng.standard_normal((C, 27))
+    y = oracle.short_conv(x, wt, wv, n_text, grid, causal_t=1)
+    for t in range(gt - 1):
+        x2 = x.copy()
+        lo = n_text + (t + 1) * gh * gw
+        x2[0, lo:] = rng.standard_normal((T - lo, C))
+        y2 = oracle.short_conv(x2, wt, wv, n_text, grid, causal_t=1)
+        assert np.array_equal(y[0, :lo], y2[0, :lo])
+
+
+def test_conv_on_config0_inputs_matches_torch():
+    cfg = CONFIGS[0]
+    inp = make_inputs(cfg)
+    B, T, H, dk = inp["q"].shape
+    x = inp["k"].double().numpy().reshape(B, T, H * dk)
+    y = oracle.short_conv(x, inp["w_text_k"], inp["w_vis_k"], cfg.n_text, cfg.grid)
+    ref = _torch_reference(x, inp["w_text_k"].double().numpy(), inp["w_vis_k"].double().numpy(),
+                           cfg.n_text, cfg.grid, 0)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_bad_shapes_raise():
+    with pytest.raises(ValueError):
+        oracle.short_conv(np.zeros((1, 5, 2)), np.zeros((2, 4)), np.zeros((2, 27)), 3, (1, 1, 1))
