@@ -1,0 +1,175 @@
+#!/usr/bin/env python3
+"""Throughput of the conv + KDA token mixer forward on one MI355X.
+
+One step = kda_conv_forward (modality-aware short conv of q, k, v) followed by
+kda_forward_chunks + kda_forward_scan (the two kernels of kda_forward) on one
+stream, over one batch of the workload, inputs resident in HBM.  Prints one
+JSON line.  The default workload is the 5-second 480x832 video stream
+(512 text tokens + a 21x30x52 latent-patch grid, T = 33272, 16 heads of
+dk = dv = 128, bf16 with fp32 accumulation).
+
+Per-kernel durations come from HIP events recorded on the launch stream
+between the three calls over the timed steps; the dominant kernel's roofline
+uses the algorithmic bytes per launch of roofline_bytes().
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+
+
+def roofline_bytes(cfg) -> dict:
+    """Algorithmic HBM bytes per launch of each kernel (what its interface must move).
+
+    conv   : read q, k, v and write q', k', v'               6 d elements / token-head
+             (+ the 3 x 31 taps per channel, once per launch)
+    chunks : read q', k', v', alpha (4 d) and beta (1); write the chunk
+             transform W, P, Kh (3 dk) and Ut, Oi (2 dv), plus the fp32
+             chunk decay (dk per 64 tokens)
+    scan   : read that transform back; write o (dv)
+    """
+    es = 4 if cfg.dtype == "f32" else 2
+    th = cfg.B * cfg.T * cfg.H                      # token-heads per launch
+    nch = (cfg.T + 63) // 64
+    chunk_heads = cfg.B * cfg.H * nch
+    conv = th * (3 * cfg.dk + 3 * cfg.dv) * es
+    conv += 31 * cfg.H * (2 * cfg.dk + cfg.dv) * es
+    ws = th * (3 * cfg.dk + 2 * cfg.dv) * es + chunk_heads * cfg.dk * 4
+    chunks = th * ((3 * cfg.dk + cfg.dv) * es + es) + ws
+    scan = ws + th * cfg.dv * es
+    path_min = th * ((3 * cfg.dk + 3 * cfg.dv) * es + (3 * cfg.dk + cfg.dv + 1) * es + cfg.dv * es)
+    return {"conv": conv, "chunks": chunks, "scan": scan, "path_min": path_min}
+
+
+def cpu_baseline(cfg, frames: int) -> dict:
+    """The fp64 oracle, as it stands, on a prefix of the same stream (text + first frames)."""
+    import oracle
+    from linear_attention_sequence_modality_amd.inputs import make_inputs
+
+    gt, gh, gw = cfg.grid
+    frames = gt if frames <= 0 else min(frames, gt)
+    sample = cfg.with_(name=cfg.name + "_prefix", grid=(frames, gh, gw))
+    inp = make_inputs(sample)
+    t0 = time.perf_counter()
+    oracle.conv_kda_forward(inp, sample.n_text, sample.grid)
+    dt = time.perf_counter() - t0
+    return {"value": sample.B * sample.T / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "fp64 C oracle (conv + sequential KDA recurrence, OpenMP over heads) on the "
+                      "first %d of %d latent frames of the same stream: B=%d, T=%d (%d text + %dx%dx%d), "
+                      "H=%d, dk=dv=%d; %.1f s wall" % (sample.grid[0], gt, sample.B, sample.T,
+                                                      sample.n_text, *sample.grid, sample.H, sample.dk, dt)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="video_5s_480x832")
+    ap.add_argument("--cpu-frames", type=int, default=0,
+                    help="latent frames in the CPU-baseline sample (0 = the whole stream)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU path only: the conv + KDA mixer shards by head "
+              "with no communication, and multi-GPU runs are not part of this build "
+              "(got --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        return 2
+
+    import torch
+
+    from linear_attention_sequence_modality_amd import kda
+    from linear_attention_sequence_modality_amd.inputs import CONFIG_BY_NAME, make_inputs
+
+    cfg = CONFIG_BY_NAME[args.workload]
+    torch.cuda.set_device(0)
+    inp = {k: v.cuda() for k, v in make_inputs(cfg).items()}
+    desc = kda.make_desc(cfg.n_text, cfg.grid, causal_t=cfg.causal_t)
+    dt = cfg.torch_dtype
+    qc, kc, vc = (torch.empty_like(inp[s]) for s in ("q", "k", "v"))
+    o = torch.empty_like(inp["v"])
+    ws = torch.empty(kda.kda_forward_workspace_size(desc, cfg.B, cfg.H, cfg.dk, cfg.dv, dt),
+                     dtype=torch.uint8, device="cuda")
+    wt = (inp["w_text_q"], inp["w_text_k"], inp["w_text_v"])
+    wv = (inp["w_vis_q"], inp["w_vis_k"], inp["w_vis_v"])
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        kda.kda_conv_forward(desc, inp["q"], inp["k"], inp["v"], wt, wv, qc, kc, vc, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        kda.kda_forward_chunks(desc, qc, kc, vc, inp["alpha"], inp["beta"], ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        kda.kda_forward_scan(desc, cfg.B, cfg.H, cfg.dk, cfg.dv, dt, ws, o, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    names = ("conv", "chunks", "scan")
+    ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in events) / args.steps for j, n in enumerate(names)}
+    rb = roofline_bytes(cfg)
+    kernels = {}
+    for n in names:
+        gbs = rb[n] / (ms[n] * 1e-3) / 1e9
+        kernels[n] = {"us": round(ms[n] * 1e3, 2), "bytes": rb[n], "GB/s": round(gbs, 1),
+                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    dom = max(names, key=lambda n: ms[n])
+    ms_step = elapsed / args.steps * 1e3
+    tokens = cfg.B * cfg.T
+    value = tokens * args.steps / elapsed
+    path_gbs = rb["path_min"] / (ms_step * 1e-3) / 1e9
+
+    result = {
+        "metric": "conv+KDA forward tokens/s at 1 GPU; % of HBM / bf16-MFMA roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "H": cfg.H, "dk": cfg.dk,
+                   "dv": cfg.dv, "n_text": cfg.n_text, "grid": list(cfg.grid),
+                   "chunk": 64, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB/s"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac_hbm"],
+                     "traffic": None},
+        "kernels": kernels,
+        "path": {"min_bytes": rb["path_min"], "GB/s_vs_path_min": round(path_gbs, 1),
+                 "frac_of_path_roofline": round(path_gbs / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_frames)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,155 @@
+/*
+ * kdaconv: modality-aware short convolution + Kimi Delta Attention (KDA)
+ * forward pass for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation is the token mixer of the KDA layers of the Chimera hybrid
+ * visual diffusion backbone (Chimera: Designing and Chinchilla-Scaling Hybrid
+ * Visual Diffusion Transformers; paper.rainbus.top page, "core method" and
+ * "method step details" steps (2) and (5); genai-atlas page, "How it works"):
+ *
+ *   1. a depthwise short convolution injects local context into q, k and v,
+ *      run separately per modality: causal 1D over the text tokens, 3D over
+ *      the visual tokens on their (t, h, w) latent grid;
+ *   2. a per-head gated delta-rule scan over the single raster-ordered stream
+ *        S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *        o_t = S_t^T q_t
+ *      with a channel-wise forget gate alpha_t in (0,1]^dk and a scalar write
+ *      strength beta_t.
+ *
+ * Stream layout: text tokens first, then visual tokens in time-major raster
+ * order (w fastest): visual token (t, h, w) sits at stream position
+ * n_text + (t * grid_h + h) * grid_w + w.  T = n_text + grid_t*grid_h*grid_w.
+ *
+ * Tensor layouts (row-major, contiguous, element type given by kda_dtype):
+ *   q, k, alpha, q_out, k_out   [B, T, H, dk]
+ *   v, v_out, o                 [B, T, H, dv]
+ *   beta                        [B, T, H]
+ *   w_text[s]                   [H*d_s, k_text]           (s = q, k, v)
+ *   w_vis[s]                    [H*d_s, k_vis, k_vis, k_vis]  (t, h, w taps)
+ *   initial_state, final_state  float32 [B, H, dk, dv]
+ *
+ * Conventions for every entry point:
+ *   - All pointers are device pointers except the descriptor, which is a host
+ *     pointer.  The caller owns all memory.  The library never allocates,
+ *     frees or synchronises; work is enqueued on `hip_stream` (a hipStream_t,
+ *     NULL = the default stream) and the call returns.  Device faults surface
+ *     at the caller's next synchronisation.
+ *   - Every argument check runs on the host before any HIP call; a failing
+ *     check returns a negative status and enqueues nothing.  Nothing aborts,
+ *     exits or throws across the ABI.
+ *   - Device pointers must be 16-byte aligned.  Outputs must not overlap any
+ *     input (the conv reads neighbours of each token).
+ *   - Preconditions that are documented, not checked: 0 < alpha <= 1, all
+ *     inputs finite, and within any 8 consecutive tokens of one head the
+ *     product of alpha over one key channel stays above 2^-120 (the chunked
+ *     scan factorises intra-chunk decays around sub-block midpoints).
+ *   - The library is stateless and re-entrant.
+ */
+#ifndef KDACONV_H
+#define KDACONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Stream structure shared by both entry points. */
+typedef struct {
+    int32_t n_text;   /* text tokens at the head of the stream (>= 0)            */
+    int32_t grid_t;   /* visual latent-patch grid; any extent may be 0 (no video) */
+    int32_t grid_h;
+    int32_t grid_w;
+    int32_t k_text;   /* causal text conv taps; must be 4                         */
+    int32_t k_vis;    /* visual conv edge; must be 3 (3x3x3)                     */
+    int32_t causal_t; /* 0: symmetric zero padding in t (default); 1: time-causal
+                         variant, taps at t-2, t-1, t                            */
+} kda_stream_desc;
+
+typedef enum {
+    KDA_F32 = 0,      /* fp32 in and out; fp32 arithmetic throughout              */
+    KDA_BF16 = 1      /* bf16 in and out; fp32 accumulation                      */
+} kda_dtype;
+
+enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = -1, /* null/misaligned/overlapping pointer, bad sizes   */
+    KDA_ERR_UNSUPPORTED = -2, /* dk/dv not in {64,128}, k_text != 4, k_vis != 3,
+                                 unknown dtype, index space beyond 2^31 tokens    */
+    KDA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required      */
+    KDA_ERR_HIP = -4          /* a kernel launch reported an error               */
+};
+
+/*
+ * Modality-aware depthwise short convolution of q, k and v (the conv of the
+ * Chimera pages' core method; genai-atlas "How it works": causal 1D depthwise
+ * over text tokens, depthwise 3D over visual tokens reshaped to their grid).
+ * For each stream s in {q, k, v} and channel c in [0, H*d_s):
+ *   text token i < n_text:
+ *     out[i, c] = sum_{j=0..3} w_text[s][c, j] * x[i - 3 + j, c]   (x[<0] = 0)
+ *   visual token (t, h, w):
+ *     out[c] = sum_{a,b,e=0..2} w_vis[s][c, a, b, e] * x(t + a - P, h + b - 1, w + e - 1)
+ *     with zero padding outside the grid, P = 1 (symmetric) or 2 (causal_t).
+ * The two modalities never read each other.  No bias, no activation.
+ * Accumulation is fp32; outputs are rounded to the input dtype (RNE).
+ * w_text and w_vis are host arrays of three device pointers each (q, k, v),
+ * in the activation dtype.
+ */
+int kda_conv_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv,
+                     kda_dtype dtype, const void *q, const void *k, const void *v,
+                     const void *const w_text[3], const void *const w_vis[3],
+                     void *q_out, void *k_out, void *v_out, void *hip_stream);
+
+/* Bytes of device workspace kda_forward needs for this shape (0 on bad args). */
+size_t kda_forward_workspace_size(const kda_stream_desc *desc, int B, int H, int dk,
+                                  int dv, kda_dtype dtype);
+
+/*
+ * KDA gated delta-rule scan (the state update of the Chimera pages' method step
+ * (5); the readout o_t = S_t^T q_t uses the post-update state, no scale).
+ * For every batch b and head h, starting from S_0 = initial_state[b, h] (or 0
+ * when initial_state is NULL):
+ *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = S_t^T q_t
+ * o is written in the input dtype; final_state (optional, NULL to skip)
+ * receives S_T in fp32.  The scan is computed chunkwise (64 tokens per chunk):
+ * an intra-chunk kernel forms the chunk's UT/WY transform on matrix cores and
+ * writes it to `workspace`; a state-passing kernel walks the chunks in order
+ * with the state held on chip.  `workspace` (device, >= the size returned by
+ * kda_forward_workspace_size) is scratch owned by the caller; its contents are
+ * undefined afterwards.  initial_state may alias final_state.
+ */
+int kda_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv,
+                kda_dtype dtype, const void *q, const void *k, const void *v,
+                const void *alpha, const void *beta, const float *initial_state,
+                float *final_state, void *o, void *workspace, size_t workspace_bytes,
+                void *hip_stream);
+
+/*
+ * The two kernels of kda_forward, callable separately with the same shapes,
+ * checks and workspace: kda_forward(...) is exactly kda_forward_chunks(...)
+ * followed by kda_forward_scan(...) on one stream.  kda_forward_chunks forms
+ * every chunk's UT/WY transform (fully parallel over chunks) and writes it to
+ * the workspace; kda_forward_scan walks the chunks of each (batch, head) in
+ * order, carrying the state, and writes o and optionally final_state.  The
+ * workspace must not be modified between the two calls.
+ */
+int kda_forward_chunks(const kda_stream_desc *desc, int B, int H, int dk, int dv,
+                       kda_dtype dtype, const void *q, const void *k, const void *v,
+                       const void *alpha, const void *beta, void *workspace,
+                       size_t workspace_bytes, void *hip_stream);
+
+int kda_forward_scan(const kda_stream_desc *desc, int B, int H, int dk, int dv,
+                     kda_dtype dtype, const float *initial_state, float *final_state,
+                     void *o, const void *workspace, size_t workspace_bytes,
+                     void *hip_stream);
+
+/* Static, human-readable text for a status code. */
+const char *kda_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDACONV_H */

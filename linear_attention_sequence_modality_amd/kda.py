@@ -1,0 +1,228 @@
+"""Thin ctypes binding over ``libkdaconv.so`` (argument marshalling only).
+
+The functions carry the C-ABI names of ``include/kdaconv.h``.  Every step of
+the computation runs in the library's HIP kernels; PyTorch only provides
+device memory and the current stream.  If the library is not built the
+binding raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdaconv.so")
+
+KDA_F32 = 0
+KDA_BF16 = 1
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARG = -1
+KDA_ERR_UNSUPPORTED = -2
+KDA_ERR_WORKSPACE = -3
+KDA_ERR_HIP = -4
+
+EXPORTED_SYMBOLS = ("kda_conv_forward", "kda_forward_workspace_size", "kda_forward",
+                    "kda_forward_chunks", "kda_forward_scan", "kda_status_string")
+
+
+class KdaStreamDesc(ctypes.Structure):
+    _fields_ = [("n_text", ctypes.c_int32), ("grid_t", ctypes.c_int32),
+                ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("k_text", ctypes.c_int32), ("k_vis", ctypes.c_int32),
+                ("causal_t", ctypes.c_int32)]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (%d)" % (fn, kda_status_string(status), status))
+        self.status = status
+
+
+_lib = None
+
+
+def load_library():
+    """Load the built library; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libkdaconv.so is not built (expected at %s); run "
+                           "__graft_entry__.build() first" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    desc_p = ctypes.POINTER(KdaStreamDesc)
+    lib.kda_conv_forward.restype = i32
+    lib.kda_conv_forward.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp,
+                                     ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp]
+    lib.kda_forward_workspace_size.restype = ctypes.c_size_t
+    lib.kda_forward_workspace_size.argtypes = [desc_p, i32, i32, i32, i32, i32]
+    lib.kda_forward.restype = i32
+    lib.kda_forward.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                vp, ctypes.c_size_t, vp]
+    lib.kda_forward_chunks.restype = i32
+    lib.kda_forward_chunks.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                       ctypes.c_size_t, vp]
+    lib.kda_forward_scan.restype = i32
+    lib.kda_forward_scan.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                     ctypes.c_size_t, vp]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [i32]
+    _lib = lib
+    return lib
+
+
+def make_desc(n_text: int, grid: Sequence[int], causal_t: int = 0, k_text: int = 4,
+              k_vis: int = 3) -> KdaStreamDesc:
+    gt, gh, gw = (int(x) for x in grid)
+    return KdaStreamDesc(int(n_text), gt, gh, gw, int(k_text), int(k_vis), int(causal_t))
+
+
+def kda_status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return KDA_F32
+    if dt == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % dt)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must have dtype %s" % (name, dtype))
+
+
+def kda_forward_workspace_size(desc: KdaStreamDesc, B: int, H: int, dk: int, dv: int,
+                               dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(load_library().kda_forward_workspace_size(ctypes.byref(desc), B, H, dk, dv, code))
+
+
+def kda_conv_forward(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     w_text: Sequence[torch.Tensor], w_vis: Sequence[torch.Tensor],
+                     q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
+                     v_out: Optional[torch.Tensor] = None, stream=None
+                     ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Modality-aware depthwise short conv of q [B,T,H,dk], k [B,T,H,dk], v [B,T,H,dv]."""
+    lib = load_library()
+    dt = q.dtype
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm, dt)
+    for i in range(3):
+        _check(w_text[i], "w_text[%d]" % i, dt)
+        _check(w_vis[i], "w_vis[%d]" % i, dt)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    v_out = torch.empty_like(v) if v_out is None else v_out
+    wt = (ctypes.c_void_p * 3)(*[w.data_ptr() for w in w_text])
+    wv = (ctypes.c_void_p * 3)(*[w.data_ptr() for w in w_vis])
+    rc = lib.kda_conv_forward(ctypes.byref(desc), B, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k),
+                              _ptr(v), wt, wv, _ptr(q_out), _ptr(k_out), _ptr(v_out),
+                              _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_conv_forward", rc)
+    return q_out, k_out, v_out
+
+
+def kda_forward(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                alpha: torch.Tensor, beta: torch.Tensor,
+                initial_state: Optional[torch.Tensor] = None,
+                final_state: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """KDA gated delta-rule scan; returns o [B,T,H,dv] (final_state filled in place if given)."""
+    lib = load_library()
+    dt = q.dtype
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (alpha, "alpha"), (beta, "beta")):
+        _check(t, nm, dt)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None:
+            _check(t, nm, torch.float32)
+    o = torch.empty_like(v) if o is None else o
+    _check(o, "o", dt)
+    need = kda_forward_workspace_size(desc, B, H, dk, dv, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = lib.kda_forward(ctypes.byref(desc), B, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k),
+                         _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(final_state),
+                         _ptr(o), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                         _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_forward", rc)
+    return o
+
+
+def kda_forward_chunks(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       alpha: torch.Tensor, beta: torch.Tensor, workspace: torch.Tensor,
+                       stream=None) -> torch.Tensor:
+    """First kernel of kda_forward: every chunk's UT/WY transform into ``workspace``."""
+    lib = load_library()
+    dt = q.dtype
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (alpha, "alpha"), (beta, "beta")):
+        _check(t, nm, dt)
+    _check(workspace, "workspace")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    rc = lib.kda_forward_chunks(ctypes.byref(desc), B, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k),
+                                _ptr(v), _ptr(alpha), _ptr(beta), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_forward_chunks", rc)
+    return workspace
+
+
+def kda_forward_scan(desc: KdaStreamDesc, B: int, H: int, dk: int, dv: int, dtype: torch.dtype,
+                     workspace: torch.Tensor, o: torch.Tensor,
+                     initial_state: Optional[torch.Tensor] = None,
+                     final_state: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Second kernel of kda_forward: the ordered state pass writing ``o``."""
+    lib = load_library()
+    _check(workspace, "workspace")
+    _check(o, "o", dtype)
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None:
+            _check(t, nm, torch.float32)
+    rc = lib.kda_forward_scan(ctypes.byref(desc), B, H, dk, dv, _dtype_code(dtype),
+                              _ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_forward_scan", rc)
+    return o
+
+
+def conv_kda_forward(desc: KdaStreamDesc, inp: dict, initial_state=None, final_state=None,
+                     workspace=None, stream=None):
+    """The measured path: kda_conv_forward then kda_forward on one stream.
+
+    ``inp`` holds device tensors q, k, v, alpha, beta, w_text_{q,k,v}, w_vis_{q,k,v}.
+    Returns (q', k', v', o).
+    """
+    qc, kc, vc = kda_conv_forward(desc, inp["q"], inp["k"], inp["v"],
+                                  (inp["w_text_q"], inp["w_text_k"], inp["w_text_v"]),
+                                  (inp["w_vis_q"], inp["w_vis_k"], inp["w_vis_v"]), stream=stream)
+    o = kda_forward(desc, qc, kc, vc, inp["alpha"], inp["beta"], initial_state, final_state,
+                    workspace=workspace, stream=stream)
+    return qc, kc, vc, o

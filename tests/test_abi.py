@@ -1,0 +1,133 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call (CPU only: no compute is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_sequence_modality_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kdaconv.h")
+
+FAKE = 0x7f0000000000          # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.load_library()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert set(names) == set(kda.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert kda.kda_status_string(code) not in ("", "unknown status")
+    assert kda.kda_status_string(-99) == "unknown status"
+
+
+def _desc(n_text=32, grid=(4, 10, 12), **kw):
+    return kda.make_desc(n_text, grid, **kw)
+
+
+def _ptrs(n, base=FAKE):
+    return [ctypes.c_void_p(base + i * (1 << 32)) for i in range(n)]
+
+
+def _conv(lib, desc, B=1, H=2, dk=64, dv=64, dtype=kda.KDA_BF16, ptrs=None, wt=None, wv=None):
+    p = ptrs if ptrs is not None else _ptrs(6)
+    wt = wt if wt is not None else (ctypes.c_void_p * 3)(*[FAKE + (20 + i) * (1 << 32) for i in range(3)])
+    wv = wv if wv is not None else (ctypes.c_void_p * 3)(*[FAKE + (30 + i) * (1 << 32) for i in range(3)])
+    return lib.kda_conv_forward(ctypes.byref(desc) if desc is not None else None, B, H, dk, dv, dtype,
+                                p[0], p[1], p[2], wt, wv, p[3], p[4], p[5], None)
+
+
+def test_conv_rejects_bad_arguments(lib):
+    d = _desc()
+    assert _conv(lib, None) == kda.KDA_ERR_INVALID_ARG
+    assert _conv(lib, d, dtype=7) == kda.KDA_ERR_UNSUPPORTED
+    assert _conv(lib, d, dk=96) == kda.KDA_ERR_UNSUPPORTED
+    assert _conv(lib, d, dv=32) == kda.KDA_ERR_UNSUPPORTED
+    assert _conv(lib, d, H=0) == kda.KDA_ERR_INVALID_ARG
+    assert _conv(lib, d, B=-1) == kda.KDA_ERR_INVALID_ARG
+    assert _conv(lib, _desc(k_text=3)) == kda.KDA_ERR_UNSUPPORTED
+    assert _conv(lib, _desc(k_vis=5)) == kda.KDA_ERR_UNSUPPORTED
+    assert _conv(lib, _desc(causal_t=2)) == kda.KDA_ERR_INVALID_ARG
+    assert _conv(lib, _desc(n_text=0, grid=(0, 0, 0))) == kda.KDA_ERR_INVALID_ARG   # T = 0
+    assert _conv(lib, _desc(n_text=-1)) == kda.KDA_ERR_INVALID_ARG
+    p = _ptrs(6)
+    p[1] = None
+    assert _conv(lib, d, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    p = _ptrs(6)
+    p[2] = ctypes.c_void_p(FAKE + 2 * (1 << 32) + 8)                   # misaligned
+    assert _conv(lib, d, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    p = _ptrs(6)
+    p[3] = ctypes.c_void_p(FAKE + 64)                                  # q_out overlaps q
+    assert _conv(lib, d, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    p = _ptrs(6)
+    p[5] = p[4]                                                        # two outputs alias
+    assert _conv(lib, d, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    wt = (ctypes.c_void_p * 3)(FAKE + 20 * (1 << 32), None, FAKE + 22 * (1 << 32))
+    assert _conv(lib, d, wt=wt) == kda.KDA_ERR_INVALID_ARG
+    # huge index spaces are refused instead of overflowing 32-bit kernel indices
+    assert _conv(lib, _desc(n_text=1 << 30, grid=(1, 1 << 15, 1 << 16))) == kda.KDA_ERR_UNSUPPORTED
+
+
+def test_workspace_size_is_host_arithmetic(lib):
+    d = _desc()                                     # T = 512 -> 8 chunks
+    s1 = kda.kda_forward_workspace_size(d, 1, 2, 64, 64, kda.KDA_F32)
+    s2 = kda.kda_forward_workspace_size(d, 2, 2, 64, 64, kda.KDA_F32)
+    assert s1 > 0 and s2 == 2 * s1 and s1 % (2 * 8) == 0
+    assert kda.kda_forward_workspace_size(_desc(n_text=33), 1, 2, 64, 64, kda.KDA_F32) == \
+        kda.kda_forward_workspace_size(_desc(n_text=32 + 64), 1, 2, 64, 64, kda.KDA_F32)
+    assert kda.kda_forward_workspace_size(d, 1, 2, 128, 128, kda.KDA_BF16) > 0
+    # fp32 scan supports dk = dv = 64 only
+    assert kda.kda_forward_workspace_size(d, 1, 2, 128, 128, kda.KDA_F32) == 0
+    assert kda.kda_forward_workspace_size(d, 1, 2, 96, 64, kda.KDA_BF16) == 0
+
+
+def _fwd(lib, desc, B=1, H=2, dk=64, dv=64, dtype=kda.KDA_BF16, ptrs=None, s0=None, sT=None,
+         ws=FAKE + 40 * (1 << 32), ws_bytes=1 << 40):
+    p = ptrs if ptrs is not None else _ptrs(6)
+    return lib.kda_forward(ctypes.byref(desc) if desc is not None else None, B, H, dk, dv, dtype,
+                           p[0], p[1], p[2], p[3], p[4], s0, sT, p[5],
+                           ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+
+
+def test_forward_rejects_bad_arguments(lib):
+    d = _desc()
+    assert _fwd(lib, None) == kda.KDA_ERR_INVALID_ARG
+    assert _fwd(lib, d, dtype=kda.KDA_F32, dk=128, dv=128) == kda.KDA_ERR_UNSUPPORTED
+    assert _fwd(lib, d, dk=32) == kda.KDA_ERR_UNSUPPORTED
+    p = _ptrs(6)
+    p[4] = None                                                       # beta
+    assert _fwd(lib, d, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    p = _ptrs(6)
+    p[5] = ctypes.c_void_p(FAKE + 2 * (1 << 32))                       # o aliases v
+    assert _fwd(lib, d, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    assert _fwd(lib, d, ws=0) == kda.KDA_ERR_WORKSPACE
+    need = kda.kda_forward_workspace_size(d, 1, 2, 64, 64, kda.KDA_BF16)
+    assert _fwd(lib, d, ws_bytes=need - 1) == kda.KDA_ERR_WORKSPACE
+    assert _fwd(lib, d, ws=FAKE + 40 * (1 << 32) + 4) == kda.KDA_ERR_WORKSPACE   # misaligned
+    assert _fwd(lib, d, ws=FAKE + 16) == kda.KDA_ERR_INVALID_ARG                # overlaps q
+    assert _fwd(lib, d, s0=ctypes.c_void_p(FAKE + 8)) == kda.KDA_ERR_INVALID_ARG
+    assert _fwd(lib, d, sT=ctypes.c_void_p(FAKE + 3 * (1 << 32))) == kda.KDA_ERR_INVALID_ARG  # sT overlaps alpha
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kda.kda_forward(kda.make_desc(4, (0, 0, 0)), x, x, x, x, torch.zeros(1, 4, 1, dtype=torch.bfloat16))

@@ -1,0 +1,203 @@
+"""HIP path vs the fp64 oracle, element by element (needs an MI355X).
+
+Gates (max relative error per (batch, head), over max |ref|): 1e-4 for fp32
+streams, 2e-2 for bf16 streams.  Small streams are compared in full; the full
+sized workloads are compared on every token of sampled heads (the conv is
+depthwise and the scan is per head, so a head's outputs depend only on that
+head's inputs and the oracle can compute them alone).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_sequence_modality_amd import kda
+from linear_attention_sequence_modality_amd.inputs import CONFIGS, StreamConfig, make_inputs
+
+from gpu_common import (TOL, desc_of, heads_slice, oracle_conv_heads, oracle_end_to_end_heads,
+                        rel, run_path, say, to_dev)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+SAMPLED_HEADS = {2: (0, 9), 3: (4, 15), 4: (7, 12)}
+
+
+def _check_stream(cfg, inp, heads=None, S0=None, want_state=False):
+    say("case %s B=%d T=%d H=%d dk=%d dv=%d %s causal_t=%d heads=%s" % (
+        cfg.name, cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv, cfg.dtype, cfg.causal_t, heads))
+    dev = to_dev(inp)
+    qc, kc, vc, o, sT = run_path(cfg, dev, S0=S0, want_state=want_state)
+    heads = tuple(range(cfg.H)) if heads is None else heads
+    rq, rk, rv, ro, rs = oracle_end_to_end_heads(cfg, inp, heads, S0)
+    tol = TOL[cfg.dtype]
+    errs = {"q'": rel(heads_slice(qc, heads), rq), "k'": rel(heads_slice(kc, heads), rk),
+            "v'": rel(heads_slice(vc, heads), rv), "o": rel(heads_slice(o, heads), ro)}
+    if want_state:
+        errs["S_T"] = oracle.rel_err_state(sT[:, list(heads)].double().cpu().numpy(), rs)
+    say("  rel errors: " + ", ".join("%s %.2e" % kv for kv in errs.items()))
+    for name, e in errs.items():
+        assert e <= tol, "%s rel err %.3e > %.1e" % (name, e, tol)
+    return errs
+
+
+def _check_kda_stage(cfg, inp, heads=None):
+    """KDA alone on the generated (already normalised) q, k, v."""
+    dev = to_dev(inp)
+    o = kda.kda_forward(desc_of(cfg), dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"])
+    torch.cuda.synchronize()
+    heads = tuple(range(cfg.H)) if heads is None else heads
+    ro, _ = oracle.kda_recurrence(heads_slice(inp["q"], heads), heads_slice(inp["k"], heads),
+                                  heads_slice(inp["v"], heads), heads_slice(inp["alpha"], heads),
+                                  heads_slice(inp["beta"][..., None], heads)[..., 0], want_state=False)
+    e = rel(heads_slice(o, heads), ro)
+    say("  kda stage %s rel err %.2e" % (cfg.name, e))
+    assert e <= TOL[cfg.dtype]
+
+
+# ---- the five stream workloads -------------------------------------------------
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("idx", [0, 1])
+def test_workload_full(idx):
+    cfg = CONFIGS[idx]
+    inp = make_inputs(cfg)
+    _check_stream(cfg, inp)
+    _check_kda_stage(cfg, inp)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_workload_sampled_heads(idx):
+    cfg = CONFIGS[idx]
+    inp = make_inputs(cfg)
+    _check_stream(cfg, inp, heads=SAMPLED_HEADS[idx])
+    _check_kda_stage(cfg, inp, heads=SAMPLED_HEADS[idx][:1])
+
+
+# ---- edge cases (small, compared in full) -----------------------------------------
+
+def _small(name, **kw):
+    base = dict(B=1, H=2, dk=128, dv=128, n_text=7, grid=(3, 5, 9), dtype="bf16", seed=77)
+    base.update(kw)
+    return StreamConfig(name, **base)
+
+
+EDGE = [
+    _small("tail_0", n_text=64, grid=(1, 8, 8)),              # T = 128: whole chunks
+    _small("tail_1", n_text=1, grid=(1, 8, 8)),               # T = 65: one-token tail
+    _small("tail_63", n_text=63, grid=(1, 8, 8)),             # T = 127
+    _small("text_only", n_text=200, grid=(0, 0, 0)),
+    _small("vision_only", n_text=0, grid=(2, 7, 11)),
+    _small("single_token", n_text=1, grid=(0, 0, 0)),
+    _small("single_visual_token", n_text=0, grid=(1, 1, 1)),
+    _small("image_grid_t1", n_text=3, grid=(1, 12, 20)),
+    _small("batch3", B=3, n_text=5, grid=(2, 6, 7)),
+    _small("causal_t", causal_t=1, grid=(4, 5, 6)),
+    _small("dk64_dv128", dk=64, dv=128),
+    _small("dk128_dv64", dk=128, dv=64),
+    _small("bf16_64", dk=64, dv=64, H=3),
+    _small("fp32_64", dk=64, dv=64, dtype="f32", grid=(2, 9, 13)),
+    _small("fp32_causal", dk=64, dv=64, dtype="f32", causal_t=1, B=2),
+    _small("narrow_w", grid=(3, 4, 1), n_text=2),             # grid_w = 1, ragged w-runs
+    _small("wide_w", grid=(2, 2, 37), n_text=9),
+]
+
+
+@pytest.mark.timeout(120)
+@pytest.mark.parametrize("cfg", EDGE, ids=[c.name for c in EDGE])
+def test_edge_case(cfg):
+    _check_stream(cfg, make_inputs(cfg))
+
+
+@pytest.mark.timeout(120)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_initial_and_final_state(dtype):
+    cfg = _small("state_" + dtype, dk=64, dv=64, dtype=dtype, B=2, H=3, n_text=11, grid=(2, 6, 9))
+    rng = np.random.default_rng(5)
+    S0 = rng.standard_normal((cfg.B, cfg.H, cfg.dk, cfg.dv)) * 0.5
+    _check_stream(cfg, make_inputs(cfg), S0=S0.astype(np.float32), want_state=True)
+
+
+@pytest.mark.timeout(120)
+def test_split_and_resume_matches_one_shot():
+    """KDA over [0, T1) then [T1, T) with the carried state equals one pass."""
+    cfg = _small("resume", dk=128, dv=128, H=2, n_text=0, grid=(1, 10, 19))   # T = 190
+    inp = to_dev(make_inputs(cfg))
+    T, T1 = cfg.T, 77
+    d_all = kda.make_desc(T, (0, 0, 0))
+    sT = torch.empty(cfg.B, cfg.H, cfg.dk, cfg.dv, device="cuda")
+    o = kda.kda_forward(d_all, inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], final_state=sT)
+    part = {k: inp[k] for k in ("q", "k", "v", "alpha", "beta")}
+    # clone: the library requires 16-byte aligned buffers, slices of beta are not
+    first = {k: x[:, :T1].clone() for k, x in part.items()}
+    second = {k: x[:, T1:].clone() for k, x in part.items()}
+    s1 = torch.empty_like(sT)
+    o1 = kda.kda_forward(kda.make_desc(T1, (0, 0, 0)), *[first[k] for k in ("q", "k", "v", "alpha", "beta")],
+                         final_state=s1)
+    s2 = torch.empty_like(sT)
+    o2 = kda.kda_forward(kda.make_desc(T - T1, (0, 0, 0)), *[second[k] for k in ("q", "k", "v", "alpha", "beta")],
+                         initial_state=s1, final_state=s2)
+    torch.cuda.synchronize()
+    oo = torch.cat([o1, o2], dim=1).double().cpu().numpy()
+    e_o = rel(oo, o.double().cpu().numpy())
+    e_s = oracle.rel_err_state(s2.double().cpu().numpy(), sT.double().cpu().numpy())
+    say("  resume rel err o %.2e S %.2e" % (e_o, e_s))
+    assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"]
+
+
+# ---- hygiene -----------------------------------------------------------------------
+
+@pytest.mark.timeout(120)
+def test_deterministic_and_every_output_written():
+    cfg = _small("hygiene", B=2, n_text=13, grid=(3, 7, 10))
+    dev = to_dev(make_inputs(cfg))
+    d = desc_of(cfg)
+    runs = []
+    for poison in (float("nan"), 12345.0):
+        q2 = torch.full_like(dev["q"], poison)
+        k2 = torch.full_like(dev["k"], poison)
+        v2 = torch.full_like(dev["v"], poison)
+        kda.kda_conv_forward(d, dev["q"], dev["k"], dev["v"],
+                             (dev["w_text_q"], dev["w_text_k"], dev["w_text_v"]),
+                             (dev["w_vis_q"], dev["w_vis_k"], dev["w_vis_v"]), q2, k2, v2)
+        need = kda.kda_forward_workspace_size(d, cfg.B, cfg.H, cfg.dk, cfg.dv, torch.bfloat16)
+        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")    # NaN bit patterns
+        o = torch.full_like(dev["v"], poison)
+        kda.kda_forward(d, q2, k2, v2, dev["alpha"], dev["beta"], o=o, workspace=ws)
+        torch.cuda.synchronize()
+        for t in (q2, k2, v2, o):
+            assert torch.isfinite(t.float()).all()
+        runs.append([t.clone() for t in (q2, k2, v2, o)])
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.timeout(120)
+def test_no_writes_outside_outputs():
+    cfg = _small("guard", n_text=9, grid=(2, 5, 6), dk=64, dv=128)
+    dev = to_dev(make_inputs(cfg))
+    d = desc_of(cfg)
+    pad = 4096
+    canary = 77.0
+
+    def guarded(like):
+        buf = torch.full((like.numel() + 2 * pad,), canary, dtype=like.dtype, device="cuda")
+        return buf, buf[pad:pad + like.numel()].view(like.shape)
+
+    bufs = [guarded(dev[s]) for s in ("q", "k", "v")]
+    kda.kda_conv_forward(d, dev["q"], dev["k"], dev["v"],
+                         (dev["w_text_q"], dev["w_text_k"], dev["w_text_v"]),
+                         (dev["w_vis_q"], dev["w_vis_k"], dev["w_vis_v"]), *[b[1] for b in bufs])
+    ob, o = guarded(dev["v"])
+    need = kda.kda_forward_workspace_size(d, cfg.B, cfg.H, cfg.dk, cfg.dv, torch.bfloat16)
+    wsb = torch.full((need + 2 * pad,), 0x5A, dtype=torch.uint8, device="cuda")
+    sb = torch.full((cfg.B * cfg.H * cfg.dk * cfg.dv + 2 * pad,), canary, device="cuda")
+    sT = sb[pad:pad + cfg.B * cfg.H * cfg.dk * cfg.dv].view(cfg.B, cfg.H, cfg.dk, cfg.dv)
+    kda.kda_forward(d, bufs[0][1], bufs[1][1], bufs[2][1], dev["alpha"], dev["beta"], final_state=sT,
+                    o=o, workspace=wsb[pad:pad + need])
+    torch.cuda.synchronize()
+    for buf, _ in bufs + [(ob, None)]:
+        assert torch.all(buf[:pad].float() == canary) and torch.all(buf[-pad:].float() == canary)
+    assert torch.all(wsb[:pad] == 0x5A) and torch.all(wsb[-pad:] == 0x5A)
+    assert torch.all(sb[:pad] == canary) and torch.all(sb[-pad:] == canary)
