@@ -31,9 +31,9 @@ def roofline_bytes(cfg) -> dict:
 
     conv   : read q, k, v and write q', k', v'               6 d elements / token-head
              (+ the 3 x 31 taps per channel, once per launch)
-    chunks : read q', k', v', alpha (4 d) and beta (1); write the chunk
-             transform W, P, Kh (3 dk) and Ut, Oi (2 dv), plus the fp32
-             chunk decay (dk per 64 tokens)
+    chunks : read q', k', v', alpha (3 dk + dv) and beta (1); write the chunk
+             transform W, Qt, Kh (3 dk), Bq (64: a 64x64 block per 64 tokens)
+             and Ut (dv), plus the fp32 chunk decay (dk per 64 tokens)
     scan   : read that transform back; write o (dv)
     """
     es = 4 if cfg.dtype == "f32" else 2
@@ -42,7 +42,7 @@ def roofline_bytes(cfg) -> dict:
     chunk_heads = cfg.B * cfg.H * nch
     conv = th * (3 * cfg.dk + 3 * cfg.dv) * es
     conv += 31 * cfg.H * (2 * cfg.dk + cfg.dv) * es
-    ws = th * (3 * cfg.dk + 2 * cfg.dv) * es + chunk_heads * cfg.dk * 4
+    ws = th * (3 * cfg.dk + 64 + cfg.dv) * es + chunk_heads * cfg.dk * 4
     chunks = th * ((3 * cfg.dk + cfg.dv) * es + es) + ws
     scan = ws + th * cfg.dv * es
     path_min = th * ((3 * cfg.dk + 3 * cfg.dv) * es + (3 * cfg.dk + cfg.dv + 1) * es + cfg.dv * es)

@@ -41,9 +41,11 @@ int check_shape(const kda_stream_desc *d, int B, int H, int dk, int dv, int dtyp
     const int64_t T = (int64_t)d->n_text + nv;
     if (T < 1) return KDA_ERR_INVALID_ARG;
     if (T >= kMaxTokens || (int64_t)B * T >= kMaxTokens || H > 4096) return KDA_ERR_UNSUPPORTED;
-    // every launch indexes threads and work items with 32-bit integers
+    // every launch indexes threads and work items with 32-bit integers, and the
+    // conv addresses one batch's slice of a stream with 32-bit byte offsets
     const int64_t d_max = dk > dv ? dk : dv;
     if ((int64_t)B * T * H * d_max / 2 >= kMaxTokens) return KDA_ERR_UNSUPPORTED;
+    if (T * H * d_max * (dtype == KDA_F32 ? 4 : 2) >= ((int64_t)1 << 32)) return KDA_ERR_UNSUPPORTED;
     *T_out = T;
     return KDA_OK;
 }

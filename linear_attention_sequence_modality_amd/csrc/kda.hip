@@ -1,31 +1,32 @@
 // Chunked Kimi Delta Attention forward for gfx950: intra-chunk UT/WY kernel
 // and the sequential inter-chunk state pass.
 //
-// Per (batch, head), with chunk tokens r = 0..63, key channel c, and
+// Per (batch, head), with chunk tokens r = 0..63, key channel c and
 // G_r = sum_{u<=r} log2 alpha_u (per channel), the gated delta rule
 //   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
 //   o_t = S_t^T q_t                                      (Chimera, method step (5))
 // regroups chunkwise into
-//   A    = strict-lower( sum_c k_r k_s 2^(G_r - G_s) ),   Bqk = lower( sum_c q_r k_s 2^(G_r - G_s) )
-//   Tm   = (I + Diag(beta) A)^-1
-//   W    = Tm Diag(beta) (2^G * K),    Ut = Tm Diag(beta) V,    M = Bqk Tm
-//   P    = 2^G * Q - M Diag(beta) (2^G * K),                   Oi = M Diag(beta) V
-//   Kh   = 2^(G_63 - G) * K,           Gam = 2^(G_63)
+//   A  = strict-lower( sum_c k_r k_s 2^(G_r - G_s) ),   Bq = lower( sum_c q_r k_s 2^(G_r - G_s) )
+//   Tm = (I + Diag(beta) A)^-1
+//   W  = Tm Diag(beta) (2^G * K),   Ut = Tm Diag(beta) V,   Qt = 2^G * Q
+//   Kh = 2^(G_63 - G) * K,          Gam = 2^(G_63)
 // and, walking the chunks in order with the state S (dk x dv, fp32):
-//   U = Ut - W S;   O = Oi + P S;   S <- Diag(Gam) S + Kh^T U.
+//   U = Ut - W S;   O = Qt S + Bq U;   S <- Diag(Gam) S + Kh^T U.
 //
-// Kernel 1 (kda_intra_kernel, one workgroup of 8 waves per chunk, fully
-// parallel) forms W, P, Ut, Oi, Kh, Gam and writes them to the workspace in
-// the exact register-fragment order kernel 2 consumes.
-// Kernel 2 (kda_state_kernel, one workgroup of 4 waves per (batch, head,
+// Kernel 1 (kda_intra_kernel: persistent, one 8-wave workgroup per CU, each
+// chunk fully independent) forms W, Qt, Kh, Bq^T, Ut and Gam and writes them
+// to the workspace in the exact register-fragment order kernel 2 consumes.
+// The next chunk's inputs are loaded into registers while the current chunk
+// is transformed.
+// Kernel 2 (kda_state_kernel: one 4-wave workgroup per (batch, head,
 // 16-column slice of dv)) keeps its state slice in registers, exchanges only
 // the 64 x 16 U block and the bf16 copy of S through LDS, and streams the
-// workspace with one chunk of register prefetch.
+// workspace through a two-deep register ring.
 //
 // Decay factorisation: 2^(G_r - G_s) for s <= r is split around the midpoint
 // m(R) = 16R + 8 of the 16-row sub-block R of row r:
 //   Kr_r = k_r 2^(G_r - G_m(R)),  Qr_r = q_r 2^(G_r - G_m(R)),  Kb_s = k_s 2^(G_m(S) - G_s)
-//   sub-block (R, S <= R):  A_RS = Kr_R Diag(2^(G_m(R) - G_m(S))) Kb_S^T.
+//   sub-block (R, S <= R):  A_RS = Kr_R Diag(2^(G_m(R) - G_m(S))) Kb_S^T  (same for Bq with Qr).
 // Every factor is <= 1 except inside one sub-block, where it spans at most 8
 // tokens; off-diagonal factors never overflow.
 #include "common.h"
@@ -38,23 +39,69 @@ namespace {
 constexpr int C = kChunk;          // 64 tokens per chunk
 constexpr int K1_THREADS = 512;    // 8 waves
 constexpr int K2_THREADS = 256;    // 4 waves
+constexpr int kBufWord3 = 0x00020000;   // 4th descriptor word of a raw gfx9 buffer
 
 constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// ---- workspace layout (per batch, head, chunk) --------------------------------
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// ---- workspace layout (per batch, head, chunk; element type T) ---------------
+// Fragment order: kernel-2 lane l of wave R loads 16 contiguous bytes per
+// fragment.  dk-indexed fragments (W, Qt) hold, in slots 0..3 and 4..7, the
+// channels 32ks + 4g + i and 32ks + 16 + 4g + i (g = l/16), matching the
+// order in which kernel 2 reads its bf16 copy of S; BT is ordered likewise
+// over tokens.  Kh holds 8 consecutive tokens per lane.
 template <typename T, int DK, int DV>
 struct Ws {
-    static constexpr size_t W = 0;                 // [4 R][DK/32][64 lanes][8]
-    static constexpr size_t P = W + 64 * DK;       // same as W
-    static constexpr size_t KH = P + 64 * DK;      // [DK/16][2][64 lanes][8]
-    static constexpr size_t U = KH + 64 * DK;      // [DV/16][4 R][64 lanes][4]
-    static constexpr size_t OI = U + 64 * DV;      // same as U
-    static constexpr size_t ELEMS = OI + 64 * DV;
+    static constexpr size_t W = 0;                 // [4 R][DK/32][64][8]  W rows of block R
+    static constexpr size_t QT = W + 64 * DK;      // [4 R][DK/32][64][8]  Qt
+    static constexpr size_t KH = QT + 64 * DK;     // [DK/16][2][64][8]    Kh^T (dk rows x tokens)
+    static constexpr size_t BT = KH + 64 * DK;     // [4 R][2][64][8]      Bq rows of block R
+    static constexpr size_t U = BT + 64 * 64;      // [DV/16][4 R][64][4]  Ut, accumulator order
+    static constexpr size_t ELEMS = U + 64 * DV;
     static constexpr size_t GAM_BYTE = round_up(ELEMS * sizeof(T), 16);   // fp32 [DK]
     static constexpr size_t BYTES = round_up(GAM_BYTE + DK * sizeof(float), 256);
 };
 
-// ---- kernel 1 shared-memory plan -------------------------------------------------
+// ---- raw 8-element rows (register prefetch without conversion) --------------
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+    uint4 u;
+    __device__ __forceinline__ void load(const bf16_t *p) { u = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void zero() { u = make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ void get(float (&x)[8]) const {
+        x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+        x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z); x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
+    }
+};
+template <> struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = *reinterpret_cast<const float4 *>(p);
+        b = *reinterpret_cast<const float4 *>(p + 4);
+    }
+    __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ void get(float (&x)[8]) const {
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+};
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16_t> {
+    uint2 u;
+    __device__ __forceinline__ void load(const bf16_t *p) { u = *reinterpret_cast<const uint2 *>(p); }
+    __device__ __forceinline__ float get(int i) const {
+        const uint32_t w = i < 2 ? u.x : u.y;
+        return (i & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+};
+template <> struct Raw4<float> {
+    float4 a;
+    __device__ __forceinline__ void load(const float *p) { a = *reinterpret_cast<const float4 *>(p); }
+    __device__ __forceinline__ float get(int i) const { return i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : a.w; }
+};
+
+// ---- kernel 1 shared-memory plan --------------------------------------------------
 template <typename T, int DK, int DV>
 struct K1Smem {
     static constexpr int NPART = K1_THREADS / DK;     // scan partitions per column
@@ -65,23 +112,21 @@ struct K1Smem {
     static constexpr int RKS = 2 * (DK + 8 / (int)sizeof(T));  // row-pair stride of RHS_K
     static constexpr int RVS = 2 * (DV + 8 / (int)sizeof(T));  // row-pair stride of RHS_V
     static constexpr int LS = 64 + 4;                 // fp32 64x64 stride (Lm, Tm32)
-    static constexpr int TS = 64 + KP;                // T 64x64 stride (Bm, Tm16, M16)
+    static constexpr int TS = 64 + KP;                // T 64x64 stride (Tm16)
     static constexpr int SC = 17;                     // 16x16 fp32 scratch stride
 
     static constexpr size_t SZ_G = (size_t)C * GS * 4;
     static constexpr size_t SZ_LM = (size_t)C * LS * 4;
-    static constexpr size_t SZ_T64 = (size_t)C * TS * sizeof(T);
     static constexpr size_t SZ_K = (size_t)C * KS * sizeof(T);
-    static constexpr size_t SZ_SCR = 4 * 4 * 16 * SC * 4;
+    static constexpr size_t SZ_SCR = 8 * 16 * SC * 4;
 
-    static constexpr size_t X1 = 0;   // G | Lm + Bm | M16 (at Lm)
-    static constexpr size_t X1_SZ = round_up(SZ_G > SZ_LM + SZ_T64 ? SZ_G : SZ_LM + SZ_T64, 16);
-    static constexpr size_t X2 = X1 + X1_SZ;   // Kr + Kb | Tm32 + doubling scratch
-    static constexpr size_t X2_SZ =
-        round_up(2 * SZ_K > SZ_LM + SZ_SCR ? 2 * SZ_K : SZ_LM + SZ_SCR, 16);
-    static constexpr size_t X3 = X2 + X2_SZ;   // Tm16
-    static constexpr size_t Q = X3 + round_up(SZ_T64, 16);          // Qr
-    static constexpr size_t RK = Q + round_up(SZ_K, 16);            // RHS_K row pairs
+    static constexpr size_t X1 = 0;   // G (P0-P1) | Lm + Tm32 (P2-P3)
+    static constexpr size_t X1_SZ = round_up(SZ_G > 2 * SZ_LM ? SZ_G : 2 * SZ_LM, 16);
+    static constexpr size_t X2 = X1 + X1_SZ;   // Kr + Kb (P1-P2, Kb until exported) | scratch (P3, at Kr)
+    static constexpr size_t X2_SZ = round_up(2 * SZ_K > SZ_SCR ? 2 * SZ_K : SZ_SCR, 16);
+    static constexpr size_t X3 = X2 + X2_SZ;   // Tm16 (P3-P5)
+    static constexpr size_t Q = X3 + round_up((size_t)C * TS * sizeof(T), 16);   // Qr (P1-P2)
+    static constexpr size_t RK = Q + round_up(SZ_K, 16);            // RHS_K row pairs (P1-P5)
     static constexpr size_t RV = RK + round_up((size_t)32 * RKS * sizeof(T), 16);
     static constexpr size_t TB = RV + round_up((size_t)32 * RVS * sizeof(T), 16);
     // tables (fp32): Pm[4][DK], Kh[4][DK], Fp[6][DK], beta[64], tot[NPART][DK]
@@ -97,12 +142,19 @@ __device__ __forceinline__ int fp_index(int R, int S) { return R * (R - 1) / 2 +
 
 // 16x16x16 fp32 product X*Y with X, Y row-major in LDS; lane holds rows 4g+i of column col.
 __device__ __forceinline__ f32x4_t mm16(const float *X, int ldx, const float *Y, int ldy, int col,
-                                        int g) {
-    f32x4_t acc = zero4();
+                                        int g, f32x4_t acc) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc = mma4(X[col * ldx + 4 * j + g], Y[(4 * j + g) * ldy + col], acc);
     return acc;
 }
+
+// Per-thread register prefetch of one chunk's inputs: rows 2rp, 2rp+1 of 8
+// channels of alpha, k, q (key side) and of v (value side), plus beta.
+template <typename T>
+struct Prefetch {
+    Raw8<T> a[2], k[2], q[2], v[2];
+    float beta;
+};
 
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
@@ -110,24 +162,20 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     using WL = Ws<T, DK, DV>;
     using F = Frag<T>;
     static_assert(SM::BYTES <= 160 * 1024, "LDS plan exceeds 160 KB");
+    constexpr int NCGK = DK / 8, NCGV = DV / 8;   // 8-channel groups
+    constexpr int NKS = DK / 32;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, col = l & 15, g = l >> 4;
     const int nchunks = a.n_chunks;
-    const int item = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = item / nchunks, n = item % nchunks;
-    const int b = bh / a.H, h = bh % a.H;
-    const int t0 = n * C;
-    const int nr = min(C, a.T - t0);   // valid rows in this chunk
+    const int n_items = a.B * a.H * nchunks;
 
     float *Gs = reinterpret_cast<float *>(smem + SM::X1);
     float *Lm = reinterpret_cast<float *>(smem + SM::X1);
-    T *Bm = reinterpret_cast<T *>(smem + SM::X1 + SM::SZ_LM);
-    T *M16 = reinterpret_cast<T *>(smem + SM::X1);
+    float *Tm32 = reinterpret_cast<float *>(smem + SM::X1 + SM::SZ_LM);
     T *Kr = reinterpret_cast<T *>(smem + SM::X2);
     T *Kb = reinterpret_cast<T *>(smem + SM::X2 + SM::SZ_K);
-    float *Tm32 = reinterpret_cast<float *>(smem + SM::X2);
-    float *Scr = reinterpret_cast<float *>(smem + SM::X2 + SM::SZ_LM);
+    float *Scr = reinterpret_cast<float *>(smem + SM::X2);
     T *Tm16 = reinterpret_cast<T *>(smem + SM::X3);
     T *Qr = reinterpret_cast<T *>(smem + SM::Q);
     T *RK = reinterpret_cast<T *>(smem + SM::RK);
@@ -143,258 +191,267 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     const T *gv = static_cast<const T *>(a.v);
     const T *ga = static_cast<const T *>(a.alpha);
     const T *gb = static_cast<const T *>(a.beta);
-    char *wsb = static_cast<char *>(a.ws) + ((size_t)bh * nchunks + n) * WL::BYTES;
-    T *ws = reinterpret_cast<T *>(wsb);
-    float *ws_gam = reinterpret_cast<float *>(wsb + WL::GAM_BYTE);
 
-    auto row_off = [&](int r, int d) -> size_t {   // element offset of token t0 + r, head h
-        return (((size_t)b * a.T + (t0 + r)) * a.H + h) * d;
+    // thread roles of the elementwise phases
+    const bool key_task = tid < 32 * NCGK, val_task = tid < 32 * NCGV;
+    const int krp = tid / NCGK, kc0 = 8 * (tid % NCGK);
+    const int vrp = tid / NCGV, vc0 = 8 * (tid % NCGV);
+
+    auto load_inputs = [&](int item, Prefetch<T> &pf) {
+        const int bh = item / nchunks, n = item % nchunks;
+        const int b = bh / a.H, h = bh % a.H;
+        const int t0 = n * C, nr = min(C, a.T - t0);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int r = 2 * krp + e;
+            if (key_task && r < nr) {
+                const size_t off = (((size_t)b * a.T + (t0 + r)) * a.H + h) * DK + kc0;
+                pf.a[e].load(ga + off);
+                pf.k[e].load(gk + off);
+                pf.q[e].load(gq + off);
+            } else {
+                pf.a[e].zero();
+                pf.k[e].zero();
+                pf.q[e].zero();
+            }
+            const int rv = 2 * vrp + e;
+            if (val_task && rv < nr)
+                pf.v[e].load(gv + (((size_t)b * a.T + (t0 + rv)) * a.H + h) * DV + vc0);
+            else
+                pf.v[e].zero();
+        }
+        pf.beta = (tid < C && tid < nr) ? ElemIO<T>::load(gb + ((size_t)b * a.T + (t0 + tid)) * a.H + h) : 0.f;
     };
 
-    // ---- P0: G = cumsum(log2 alpha) over the chunk, tables ---------------------
-    constexpr int NCGK = DK / 8;   // 8-channel groups along dk
-    constexpr int NCGV = DV / 8;
-    {
-        if (tid < 32 * NCGK) {
-            const int rp = tid / NCGK, cg = tid % NCGK, c0 = 8 * cg;
+    Prefetch<T> pf;
+    int item = blockIdx.x;
+    if (item < n_items) load_inputs(item, pf);
+
+#pragma unroll 1
+    for (; item < n_items; item += gridDim.x) {
+        const int bh = item / nchunks, n = item % nchunks;
+        const int nr = min(C, a.T - n * C);   // valid rows in this chunk
+        char *wsb = static_cast<char *>(a.ws) + ((size_t)bh * nchunks + n) * WL::BYTES;
+        T *ws = reinterpret_cast<T *>(wsb);
+        float *ws_gam = reinterpret_cast<float *>(wsb + WL::GAM_BYTE);
+
+        // ---- P0: G = cumsum(log2 alpha) over the chunk, per-channel tables ------
+        if (key_task) {
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const int r = 2 * rp + e;
+                const int r = 2 * krp + e;
                 float al[8];
-                if (r < nr) {
-                    ld8f<T>(ga + row_off(r, DK) + c0, al);
+                pf.a[e].get(al);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) al[i] = log2f(al[i]);
+                for (int i = 0; i < 8; ++i) al[i] = r < nr ? log2f(al[i]) : 0.f;
+                *reinterpret_cast<float4 *>(Gs + r * SM::GS + kc0) = make_float4(al[0], al[1], al[2], al[3]);
+                *reinterpret_cast<float4 *>(Gs + r * SM::GS + kc0 + 4) = make_float4(al[4], al[5], al[6], al[7]);
+            }
+        }
+        if (tid < C) Bt[tid] = pf.beta;
+        __syncthreads();
+        {
+            // column scan in NPART partitions of RPP rows; Gs keeps the partition-local
+            // prefix sums, Tot the partition totals (G = local + sum of earlier totals)
+            const int c = tid % DK, part = tid / DK;
+            float run = 0.f;
+#pragma unroll
+            for (int i = 0; i < SM::RPP; ++i) {
+                const int r = part * SM::RPP + i;
+                run += Gs[r * SM::GS + c];
+                Gs[r * SM::GS + c] = run;
+            }
+            Tot[part * DK + c] = run;
+            __syncthreads();
+            auto Gat = [&](int r) {   // final G at row r, channel c
+                float v = Gs[r * SM::GS + c];
+                for (int p = 0; p < r / SM::RPP; ++p) v += Tot[p * DK + c];
+                return v;
+            };
+            // 15 per-channel factors: Pm[4], Kh[4], Fp[6], Gam
+            for (int e = part; e < 15; e += SM::NPART) {
+                if (e < 4) {
+                    Pm[e * DK + c] = exp2f(Gat(16 * e + 8));
+                } else if (e < 8) {
+                    const int R = e - 4;
+                    Kh[R * DK + c] = exp2f(Gat(63) - Gat(16 * R + 8));
+                } else if (e < 14) {
+                    const int f = e - 8;
+                    const int R = f < 1 ? 1 : (f < 3 ? 2 : 3);
+                    const int S = f - fp_index(R, 0);
+                    Fp[f * DK + c] = exp2f(Gat(16 * R + 8) - Gat(16 * S + 8));
                 } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) al[i] = 0.f;
+                    ws_gam[c] = exp2f(Gat(63));
                 }
-                *reinterpret_cast<float4 *>(Gs + r * SM::GS + c0) = make_float4(al[0], al[1], al[2], al[3]);
-                *reinterpret_cast<float4 *>(Gs + r * SM::GS + c0 + 4) = make_float4(al[4], al[5], al[6], al[7]);
             }
+            __syncthreads();
         }
-        if (tid < C) {
-            const int r = tid;
-            Bt[r] = r < nr ? ElemIO<T>::load(gb + ((size_t)b * a.T + (t0 + r)) * a.H + h) : 0.f;
-        }
-        __syncthreads();
-        const int c = tid % DK, part = tid / DK;
-        float run = 0.f;
-#pragma unroll
-        for (int i = 0; i < SM::RPP; ++i) {
-            const int r = part * SM::RPP + i;
-            run += Gs[r * SM::GS + c];
-            Gs[r * SM::GS + c] = run;
-        }
-        Tot[part * DK + c] = run;
-        __syncthreads();
-        if (part > 0) {
-            float off = 0.f;
-            for (int p = 0; p < part; ++p) off += Tot[p * DK + c];
-#pragma unroll
-            for (int i = 0; i < SM::RPP; ++i) Gs[(part * SM::RPP + i) * SM::GS + c] += off;
-        }
-        __syncthreads();
-        // 15 per-channel factors: Pm[4], Kh[4], Fp[6], Gam
-        for (int e = part; e < 15; e += SM::NPART) {
-            if (e < 4) {
-                Pm[e * DK + c] = exp2f(Gs[(16 * e + 8) * SM::GS + c]);
-            } else if (e < 8) {
-                const int R = e - 4;
-                Kh[R * DK + c] = exp2f(Gs[63 * SM::GS + c] - Gs[(16 * R + 8) * SM::GS + c]);
-            } else if (e < 14) {
-                const int f = e - 8;
-                const int R = f < 1 ? 1 : (f < 3 ? 2 : 3);
-                const int S = f - fp_index(R, 0);
-                Fp[f * DK + c] = exp2f(Gs[(16 * R + 8) * SM::GS + c] - Gs[(16 * S + 8) * SM::GS + c]);
-            } else {
-                ws_gam[c] = exp2f(Gs[63 * SM::GS + c]);
-            }
-        }
-        __syncthreads();
-    }
 
-    // ---- P1: elementwise operands ------------------------------------------------
-    if (tid < 32 * NCGK) {
-        const int rp = tid / NCGK, cg = tid % NCGK, c0 = 8 * cg;
-        const int s0 = 2 * rp, R = s0 >> 4, m = 16 * R + 8;
-        float rhs[2][8], khv[2][8];
+        // ---- P1: elementwise operands ----------------------------------------------
+        if (key_task) {
+            const int s0 = 2 * krp, R = s0 >> 4, m = 16 * R + 8;
+            float rhs[2][8];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int r = s0 + e;
-            float kx[8], qx[8];
-            if (r < nr) {
-                ld8f<T>(gk + row_off(r, DK) + c0, kx);
-                ld8f<T>(gq + row_off(r, DK) + c0, qx);
-            } else {
+            for (int e = 0; e < 2; ++e) {
+                const int r = s0 + e;
+                float kx[8], qx[8], gr[8], gm[8];
+                pf.k[e].get(kx);
+                pf.q[e].get(qx);
+                const float4 g0 = *reinterpret_cast<const float4 *>(Gs + r * SM::GS + kc0);
+                const float4 g1 = *reinterpret_cast<const float4 *>(Gs + r * SM::GS + kc0 + 4);
+                const float4 m0 = *reinterpret_cast<const float4 *>(Gs + m * SM::GS + kc0);
+                const float4 m1 = *reinterpret_cast<const float4 *>(Gs + m * SM::GS + kc0 + 4);
+                gr[0] = g0.x; gr[1] = g0.y; gr[2] = g0.z; gr[3] = g0.w;
+                gr[4] = g1.x; gr[5] = g1.y; gr[6] = g1.z; gr[7] = g1.w;
+                gm[0] = m0.x; gm[1] = m0.y; gm[2] = m0.z; gm[3] = m0.w;
+                gm[4] = m1.x; gm[5] = m1.y; gm[6] = m1.z; gm[7] = m1.w;
+                // rows r and m lie in partitions r/RPP and m/RPP: add the earlier totals
+                for (int p = 0; p < r / SM::RPP; ++p) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) kx[i] = qx[i] = 0.f;
+                    for (int i = 0; i < 8; ++i) gr[i] += Tot[p * DK + kc0 + i];
+                }
+                for (int p = 0; p < m / SM::RPP; ++p) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) gm[i] += Tot[p * DK + kc0 + i];
+                }
+                const float br = Bt[r];
+                float kr[8], qr[8], kb[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int c = kc0 + i;
+                    const float d = gr[i] - gm[i];
+                    const float e1 = exp2f(d), e2 = exp2f(-d);
+                    kr[i] = kx[i] * e1;
+                    qr[i] = qx[i] * e1;
+                    kb[i] = kx[i] * e2;
+                    rhs[e][i] = br * kr[i] * Pm[R * DK + c];
+                }
+                st8f<T>(Kr + r * SM::KS + kc0, kr);
+                st8f<T>(Qr + r * SM::KS + kc0, qr);
+                st8f<T>(Kb + r * SM::KS + kc0, kb);
             }
-            const float br = Bt[r];
-            float kr[8], qr[8], kb[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int c = c0 + i;
-                const float d = Gs[r * SM::GS + c] - Gs[m * SM::GS + c];
-                const float e1 = exp2f(d), e2 = exp2f(-d);
-                kr[i] = kx[i] * e1;
-                qr[i] = qx[i] * e1;
-                kb[i] = kx[i] * e2;
-                rhs[e][i] = br * kr[i] * Pm[R * DK + c];
-                khv[e][i] = kb[i] * Kh[R * DK + c];
-            }
-            st8f<T>(Kr + r * SM::KS + c0, kr);
-            st8f<T>(Qr + r * SM::KS + c0, qr);
-            st8f<T>(Kb + r * SM::KS + c0, kb);
+            for (int i = 0; i < 8; ++i) st2<T>(RK + krp * SM::RKS + 2 * (kc0 + i), rhs[0][i], rhs[1][i]);
         }
+        if (val_task) {
+            const int s0 = 2 * vrp;
+            float vx0[8], vx1[8];
+            pf.v[0].get(vx0);
+            pf.v[1].get(vx1);
+            const float b0 = Bt[s0], b1 = Bt[s0 + 1];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = c0 + i;
-            st2<T>(RK + rp * SM::RKS + 2 * c, rhs[0][i], rhs[1][i]);
-            // Kh fragment order: [c/16][s/32][lane = c%16 + 16*((s%32)/8)][s%8]
-            const int lane = (c & 15) + 16 * ((s0 & 31) >> 3);
-            const size_t off = WL::KH + ((size_t)((c >> 4) * 2 + (s0 >> 5)) * 64 + lane) * 8 + (s0 & 7);
-            st2<T>(ws + off, khv[0][i], khv[1][i]);
+            for (int i = 0; i < 8; ++i) st2<T>(RV + vrp * SM::RVS + 2 * (vc0 + i), b0 * vx0[i], b1 * vx1[i]);
         }
-    }
-    if (tid < 32 * NCGV) {
-        const int rp = tid / NCGV, cg = tid % NCGV, c0 = 8 * cg;
-        const int s0 = 2 * rp;
-        float vx[2][8];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int r = s0 + e;
-            if (r < nr) {
-                ld8f<T>(gv + row_off(r, DV) + c0, vx[e]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) vx[e][i] = 0.f;
-            }
-        }
-        const float b0 = Bt[s0], b1 = Bt[s0 + 1];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) st2<T>(RV + rp * SM::RVS + 2 * (c0 + i), b0 * vx[0][i], b1 * vx[1][i]);
-    }
-    __syncthreads();
+        // the prefetch registers are consumed: start loading the next chunk
+        if (item + (int)gridDim.x < n_items) load_inputs(item + gridDim.x, pf);
+        __syncthreads();
 
-    // ---- P2: decayed K K^T and Q K^T sub-blocks (MFMA) ------------------------
-    {
+        // ---- P2: decayed K K^T (-> L) and (Q K^T)^T (-> workspace) on MFMA ----------
         for (int ti = wv; ti < 10; ti += 8) {
             const int R = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
             const int S = ti - R * (R + 1) / 2;
             f32x4_t accA = zero4(), accB = zero4();
 #pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks) {
+            for (int ks = 0; ks < NKS; ++ks) {
                 const int c = 32 * ks + 8 * g;
-                const F ak = F::ld8(Kr + (16 * R + col) * SM::KS + c);
-                const F aq = F::ld8(Qr + (16 * R + col) * SM::KS + c);
-                F bk = F::ld8(Kb + (16 * S + col) * SM::KS + c);
+                const F kr = F::ld8(Kr + (16 * R + col) * SM::KS + c);
+                const F qr = F::ld8(Qr + (16 * R + col) * SM::KS + c);
+                F kb = F::ld8(Kb + (16 * S + col) * SM::KS + c);
                 if (S < R) {
                     const float *fp = Fp + fp_index(R, S) * DK + c;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) bk.set(i, bk.get(i) * fp[i]);
+                    for (int i = 0; i < 8; ++i) kb.set(i, kb.get(i) * fp[i]);
                 }
-                accA = mma(ak, bk, accA);
-                accB = mma(aq, bk, accB);
+                accA = mma(kr, kb, accA);   // A[r][s]:  rows r = 16R + 4g + i, column s = 16S + col
+                accB = mma(kb, qr, accB);   // Bq[r][s] at rows s = 16S + 4g + i, column r = 16R + col
             }
+            float bq[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * R + 4 * g + i, s = 16 * S + col;
                 Lm[r * SM::LS + s] = s < r ? Bt[r] * accA[i] : 0.f;
-                Bm[r * SM::TS + s] = (T)(s <= r ? accB[i] : 0.f);
+                bq[i] = (16 * S + 4 * g + i <= 16 * R + col) ? accB[i] : 0.f;
             }
+            st4<T>(ws + WL::BT + ((size_t)(R * 2 + (S >> 1)) * 64 + l) * 8 + (S & 1) * 4, bq);
         }
-        if (wv >= 2) {   // zero the 6 upper sub-blocks of Bm
-            const int u = wv - 2;
-            const int R = u < 3 ? 0 : u < 5 ? 1 : 2;
-            const int S = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Bm[(16 * R + 4 * g + i) * SM::TS + 16 * S + col] = (T)0.f;
+        if (wv == 2 || wv == 3) {   // the upper sub-blocks (0,1) and (2,3) inside kernel 2's k-steps
+            const int R = wv == 2 ? 0 : 2, S = R + 1;
+            const float z[4] = {0.f, 0.f, 0.f, 0.f};
+            st4<T>(ws + WL::BT + ((size_t)(R * 2 + (S >> 1)) * 64 + l) * 8 + (S & 1) * 4, z);
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- P3: Tm = (I + Diag(beta) A)^-1 in fp32 ------------------------------------
-    {
-        float *sc = Scr + wv * (4 * 16 * SM::SC);   // four 16x16 scratch tiles per wave
-        float *sN = sc, *sN2 = sc + 16 * SM::SC, *sN4 = sc + 32 * SM::SC, *sD = sc + 48 * SM::SC;
-        if (wv < 4) {
-            const int R = wv;
+        // ---- P3: Tm = (I + Diag(beta) A)^-1 in fp32 ------------------------------------
+        if (wv == 0) {
+            // diagonal blocks by forward substitution: lane = (block R, column j)
+            const int R = l >> 4, j = l & 15;
+            float x[16];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * g + i;
-                sN[r * SM::SC + col] = -Lm[(16 * R + r) * SM::LS + 16 * R + col];
+            for (int i = 0; i < 16; ++i) {
+                const float *Li = Lm + (16 * R + i) * SM::LS + 16 * R;
+                float s = (i == j) ? 1.f : 0.f;
+#pragma unroll
+                for (int k2 = 0; k2 < i; ++k2) s = __builtin_fmaf(-Li[k2], x[k2], s);
+                x[i] = s;
             }
-        } else {   // zero the upper sub-blocks of Tm32
-            for (int u = wv - 4; u < 6; u += 4) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Tm32[(16 * R + i) * SM::LS + 16 * R + j] = x[i];
+        } else {
+            // waves 1..7: zero the 6 upper sub-blocks of Tm32, then export Kh^T and
+            // Qt to the workspace in fragment order (16 contiguous bytes per task)
+            if (wv >= 2) {
+                const int u = wv - 2;
                 const int R = u < 3 ? 0 : u < 5 ? 1 : 2;
                 const int S = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) Tm32[(16 * R + 4 * g + i) * SM::LS + 16 * S + col] = 0.f;
             }
-        }
-        __syncthreads();
-        // (I + L)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8) with N = -L, N^16 = 0
-        f32x4_t acc;
-        if (wv < 4) {
-            acc = mm16(sN, SM::SC, sN, SM::SC, col, g);   // N^2
+            constexpr int NT = 8 * DK;   // tasks per tensor: DK/16 * 2 * 64 (Kh) == 4 * DK/32 * 64 (Qt)
+            for (int u = tid - 64; u < 2 * NT; u += K1_THREADS - 64) {
+                const int v = u < NT ? u : u - NT, ln = v & 63, gq = ln >> 4;
+                float x[8];
+                if (u < NT) {
+                    // Kh^T fragment (dt, ks, lane): channel 16dt + ln%16, tokens 32ks + 8*(ln/16) + 0..7
+                    const int dt = v >> 7, ks = (v >> 6) & 1;
+                    const int c = 16 * dt + (ln & 15), t0 = 32 * ks + 8 * gq, R = t0 >> 4;
+                    const float kh = Kh[R * DK + c];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sN2[(4 * g + i) * SM::SC + col] = acc[i];
-        }
-        __syncthreads();
-        if (wv < 4) {
-            f32x4_t n4 = mm16(sN2, SM::SC, sN2, SM::SC, col, g);     // N^4
-            f32x4_t d1 = mm16(sN, SM::SC, sN2, SM::SC, col, g);      // N N^2
+                    for (int j = 0; j < 8; ++j) x[j] = (float)Kb[(t0 + j) * SM::KS + c] * kh;
+                    st8f<T>(ws + WL::KH + (size_t)v * 8, x);
+                } else {
+                    // Qt fragment (R, ks, lane): row 16R + ln%16, channels 32ks + 4*(ln/16) + {0..3, 16..19}
+                    const int R = v / (NKS * 64), ks = (v >> 6) % NKS;
+                    const int r = 16 * R + (ln & 15), c0 = 32 * ks + 4 * gq;
+                    float a4[4], b4[4];
+                    ld4<T>(Qr + r * SM::KS + c0, a4);
+                    ld4<T>(Qr + r * SM::KS + c0 + 16, b4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * g + i;
-                sN4[r * SM::SC + col] = n4[i];
-                sD[r * SM::SC + col] = d1[i] + sN[r * SM::SC + col] + sN2[r * SM::SC + col] +
-                                       (r == col ? 1.f : 0.f);       // (I+N)(I+N^2)
-            }
-        }
-        __syncthreads();
-        if (wv < 4) {
-            f32x4_t n8 = mm16(sN4, SM::SC, sN4, SM::SC, col, g);     // N^8
-            f32x4_t d2 = mm16(sD, SM::SC, sN4, SM::SC, col, g);      // D1 N^4
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * g + i;
-                sN2[r * SM::SC + col] = n8[i];
-                sN[r * SM::SC + col] = sD[r * SM::SC + col] + d2[i];   // D1 (I + N^4)
-            }
-        }
-        __syncthreads();
-        if (wv < 4) {
-            const int R = wv;
-            f32x4_t d3 = mm16(sN, SM::SC, sN2, SM::SC, col, g);      // D2 N^8
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * g + i;
-                Tm32[(16 * R + r) * SM::LS + 16 * R + col] = sN[r * SM::SC + col] + d3[i];
-            }
-        }
-        __syncthreads();
-        // off-diagonal: Tm_RS = -D_R sum_{J=S}^{R-1} L_RJ Tm_JS, row block by row block
-        for (int R = 1; R < 4; ++R) {
-            if (wv < R) {
-                const int S = wv;
-                acc = zero4();
-                for (int J = S; J < R; ++J) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc = mma4(Lm[(16 * R + col) * SM::LS + 16 * J + 4 * j + g],
-                                   Tm32[(16 * J + 4 * j + g) * SM::LS + 16 * S + col], acc);
+                    for (int i = 0; i < 4; ++i) {
+                        x[i] = a4[i] * Pm[R * DK + c0 + i];
+                        x[4 + i] = b4[i] * Pm[R * DK + c0 + 16 + i];
+                    }
+                    st8f<T>(ws + WL::QT + (size_t)v * 8, x);
                 }
+            }
+        }
+        __syncthreads();
+        // off-diagonal, by distance d = R - S: Tm_RS = -D_R sum_{J=S}^{R-1} L_RJ Tm_JS
+        for (int d = 1; d < 4; ++d) {
+            float *sc = Scr + wv * 16 * SM::SC;
+            const int R = wv + d, S = wv;
+            if (R < 4) {
+                f32x4_t y = zero4();
+                for (int J = S; J < R; ++J)
+                    y = mm16(Lm + (16 * R) * SM::LS + 16 * J, SM::LS, Tm32 + (16 * J) * SM::LS + 16 * S, SM::LS,
+                             col, g, y);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sN[(4 * g + i) * SM::SC + col] = acc[i];
+                for (int i = 0; i < 4; ++i) sc[(4 * g + i) * SM::SC + col] = y[i];
             }
             __syncthreads();
-            if (wv < R) {
-                const int S = wv;
-                acc = mm16(Tm32 + (16 * R) * SM::LS + 16 * R, SM::LS, sN, SM::SC, col, g);
+            if (R < 4) {
+                const f32x4_t t = mm16(Tm32 + (16 * R) * SM::LS + 16 * R, SM::LS, sc, SM::SC, col, g, zero4());
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Tm32[(16 * R + 4 * g + i) * SM::LS + 16 * S + col] = -acc[i];
+                for (int i = 0; i < 4; ++i) Tm32[(16 * R + 4 * g + i) * SM::LS + 16 * S + col] = -t[i];
             }
             __syncthreads();
         }
@@ -406,92 +463,45 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
             st8f<T>(Tm16 + r * SM::TS + c0, x);
         }
         __syncthreads();
-    }
 
-    // ---- P4: M = Bqk Tm ----------------------------------------------------------
-    {
-        for (int ti = wv; ti < 10; ti += 8) {
-            const int R = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
-            const int S = ti - R * (R + 1) / 2;
-            f32x4_t acc = zero4();
-            for (int ks = S >> 1; ks <= (R >> 1); ++ks) {
-                const F am = F::ld8(Bm + (16 * R + col) * SM::TS + 32 * ks + 8 * g);
-                const F bt = F::ld_strided(Tm16 + (32 * ks + 8 * g) * SM::TS + 16 * S + col, SM::TS);
-                acc = mma(am, bt, acc);
-            }
+        // ---- P5: W^T per 16 key channels, Ut per 16 value columns ------------------
+        {
+            constexpr int NWU = DK / 16, NUU = DV / 16;
+            for (int u = wv; u < NWU + NUU; u += 8) {
+                if (u < NWU) {
+                    const int at = u;
+                    F rk[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) M16[(16 * R + 4 * g + i) * SM::TS + 16 * S + col] = (T)acc[i];
-        }
-        if (wv >= 2) {
-            const int u = wv - 2;
-            const int R = u < 3 ? 0 : u < 5 ? 1 : 2;
-            const int S = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
+                    for (int ks = 0; ks < 2; ++ks)
+                        rk[ks] = F::ld_pairs(RK + (16 * ks + 4 * g) * SM::RKS + 2 * (16 * at + col), SM::RKS);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) M16[(16 * R + 4 * g + i) * SM::TS + 16 * S + col] = (T)0.f;
-        }
-    }
-    __syncthreads();
-
-    // ---- P5: W^T, P^T (per 16 key channels) and Ut, Oi (per 16 value columns) ----
-    {
-        constexpr int NWP = DK / 16, NUO = DV / 16;
-        for (int u = wv; u < NWP + NUO; u += 8) {
-            if (u < NWP) {
-                const int at = u;
-                F rk[2];
+                    for (int R = 0; R < 4; ++R) {
+                        f32x4_t acc = zero4();
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    rk[ks] = F::ld_pairs(RK + (16 * ks + 4 * g) * SM::RKS + 2 * (16 * at + col), SM::RKS);
-#pragma unroll
-                for (int R = 0; R < 4; ++R) {
-                    f32x4_t accW = zero4(), accP = zero4();
-#pragma unroll
-                    for (int ks = 0; ks <= (R >> 1); ++ks) {
-                        const F bT = F::ld8(Tm16 + (16 * R + col) * SM::TS + 32 * ks + 8 * g);
-                        const F bM = F::ld8(M16 + (16 * R + col) * SM::TS + 32 * ks + 8 * g);
-                        accW = mma(rk[ks], bT, accW);
-                        accP = mma(rk[ks], bM, accP);
+                        for (int ks = 0; ks <= (R >> 1); ++ks)
+                            acc = mma(rk[ks], F::ld8(Tm16 + (16 * R + col) * SM::TS + 32 * ks + 8 * g), acc);
+                        const float w4[4] = {acc[0], acc[1], acc[2], acc[3]};
+                        st4<T>(ws + WL::W + ((size_t)(R * NKS + (at >> 1)) * 64 + l) * 8 + (at & 1) * 4, w4);
                     }
-                    const int tok = 16 * R + col, c4 = 16 * at + 4 * g;
-                    float qr4[4], wv4[4], pv4[4];
-                    ld4<T>(Qr + tok * SM::KS + c4, qr4);
+                } else {
+                    const int jt = u - NWU;
+                    F rv[2];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        wv4[i] = accW[i];
-                        pv4[i] = qr4[i] * Pm[R * DK + c4 + i] - accP[i];
+                    for (int ks = 0; ks < 2; ++ks)
+                        rv[ks] = F::ld_pairs(RV + (16 * ks + 4 * g) * SM::RVS + 2 * (16 * jt + col), SM::RVS);
+#pragma unroll
+                    for (int R = 0; R < 4; ++R) {
+                        f32x4_t acc = zero4();
+#pragma unroll
+                        for (int ks = 0; ks <= (R >> 1); ++ks)
+                            acc = mma(F::ld8(Tm16 + (16 * R + col) * SM::TS + 32 * ks + 8 * g), rv[ks], acc);
+                        const float u4[4] = {acc[0], acc[1], acc[2], acc[3]};
+                        st4<T>(ws + WL::U + ((size_t)(jt * 4 + R) * 64 + l) * 4, u4);
                     }
-                    const size_t off = ((size_t)(R * (DK / 32) + (at >> 1)) * 64 + l) * 8 + (at & 1) * 4;
-                    st4<T>(ws + WL::W + off, wv4);
-                    st4<T>(ws + WL::P + off, pv4);
-                }
-            } else {
-                const int jt = u - NWP;
-                F rv[2];
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    rv[ks] = F::ld_pairs(RV + (16 * ks + 4 * g) * SM::RVS + 2 * (16 * jt + col), SM::RVS);
-#pragma unroll
-                for (int R = 0; R < 4; ++R) {
-                    f32x4_t accU = zero4(), accO = zero4();
-#pragma unroll
-                    for (int ks = 0; ks <= (R >> 1); ++ks) {
-                        const F aT = F::ld8(Tm16 + (16 * R + col) * SM::TS + 32 * ks + 8 * g);
-                        const F aM = F::ld8(M16 + (16 * R + col) * SM::TS + 32 * ks + 8 * g);
-                        accU = mma(aT, rv[ks], accU);
-                        accO = mma(aM, rv[ks], accO);
-                    }
-                    float u4[4], o4[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        u4[i] = accU[i];
-                        o4[i] = accO[i];
-                    }
-                    const size_t off = ((size_t)(jt * 4 + R) * 64 + l) * 4;
-                    st4<T>(ws + WL::U + off, u4);
-                    st4<T>(ws + WL::OI + off, o4);
                 }
             }
         }
+        __syncthreads();   // LDS is reused by the next chunk
     }
 }
 
@@ -513,7 +523,17 @@ __global__ __launch_bounds__(K2_THREADS) void kda_state_kernel(KdaArgs a) {
     const int b = bh / a.H, h = bh % a.H;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, col = l & 15, g = l >> 4;
     const int nchunks = a.n_chunks;
-    T *go = static_cast<T *>(a.o);
+
+    // o of this (batch, head, 16 value columns) as a raw buffer: token t at
+    // byte t*H*DV*es.  Rows past the end of the stream fall outside the range
+    // and the hardware drops their stores.  The output tile is produced
+    // transposed (lane: 4 consecutive value columns of one token), so each
+    // lane writes one 4-column piece per chunk.
+    const unsigned es = sizeof(T), orow = (unsigned)a.H * DV * es;
+    char *obase = static_cast<char *>(a.o) + ((((size_t)b * a.T) * a.H + h) * DV + 16 * jt) * es;
+    const unsigned onum = (unsigned)a.T * orow - (unsigned)(h * DV + 16 * jt) * es;
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(obase, 0, (int)onum, kBufWord3);
+    const unsigned ovoff = (unsigned)(16 * w + col) * orow + (unsigned)(4 * g) * es;
 
     f32x4_t S[DTW];
 #pragma unroll
@@ -532,8 +552,9 @@ __global__ __launch_bounds__(K2_THREADS) void kda_state_kernel(KdaArgs a) {
 
     const char *wsh = static_cast<const char *>(a.ws) + (size_t)bh * nchunks * WL::BYTES;
     struct Buf {
-        F Wf[NKS], Pf[NKS], Kf[DTW][2];
-        float ut[4], oi[4], gam[DTW][4];
+        F Wf[NKS], Qf[NKS], Kf[DTW][2], Bf[2];
+        Raw4<T> ut;
+        float4 gam[DTW];
     };
     auto load = [&](Buf &B, int n) {
         const char *base = wsh + (size_t)n * WL::BYTES;
@@ -542,60 +563,99 @@ __global__ __launch_bounds__(K2_THREADS) void kda_state_kernel(KdaArgs a) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             B.Wf[ks] = F::ld8(ws + WL::W + ((size_t)(w * NKS + ks) * 64 + l) * 8);
-            B.Pf[ks] = F::ld8(ws + WL::P + ((size_t)(w * NKS + ks) * 64 + l) * 8);
+            B.Qf[ks] = F::ld8(ws + WL::QT + ((size_t)(w * NKS + ks) * 64 + l) * 8);
         }
 #pragma unroll
         for (int d = 0; d < DTW; ++d) {
             const int dt = w * DTW + d;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) B.Kf[d][ks] = F::ld8(ws + WL::KH + ((size_t)(dt * 2 + ks) * 64 + l) * 8);
-            const float4 gm = *reinterpret_cast<const float4 *>(gam + 16 * dt + 4 * g);
-            B.gam[d][0] = gm.x; B.gam[d][1] = gm.y; B.gam[d][2] = gm.z; B.gam[d][3] = gm.w;
+            B.gam[d] = *reinterpret_cast<const float4 *>(gam + 16 * dt + 4 * g);
         }
-        ld4<T>(ws + WL::U + ((size_t)(jt * 4 + w) * 64 + l) * 4, B.ut);
-        ld4<T>(ws + WL::OI + ((size_t)(jt * 4 + w) * 64 + l) * 4, B.oi);
+        // Unconditional loads (the second Bq fragment of waves 0 and 1 is never
+        // used): the number of loads in flight must not depend on the path, or
+        // the wait before the first use degrades to waiting for all of them.
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) B.Bf[ks] = F::ld8(ws + WL::BT + ((size_t)(w * 2 + ks) * 64 + l) * 8);
+        B.ut.load(ws + WL::U + ((size_t)(jt * 4 + w) * 64 + l) * 4);
     };
 
-    Buf cur, nxt;
-    load(cur, 0);
-    for (int n = 0; n < nchunks; ++n) {
-        if (n + 1 < nchunks) load(nxt, n + 1);
-        f32x4_t accU = zero4(), accO = zero4();
+    auto step = [&](const Buf &B, int n) {
+        // S fragments (bf16 copy, dk order matching W and Qt), all reads issued together
+        F sf[NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const F sf = F::ld4x2(S_lds + col * SSTR + 32 * ks + 4 * g,
-                                  S_lds + col * SSTR + 32 * ks + 16 + 4 * g);
-            accU = mma(cur.Wf[ks], sf, accU);
-            accO = mma(cur.Pf[ks], sf, accO);
-        }
+        for (int ks = 0; ks < NKS; ++ks)
+            sf[ks] = F::ld4x2(S_lds + col * SSTR + 32 * ks + 4 * g, S_lds + col * SSTR + 32 * ks + 16 + 4 * g);
+        __builtin_amdgcn_sched_barrier(0);   // keep the LDS reads ahead of the MFMA chain
+        // U = Ut - W S for this wave's 16 rows
+        f32x4_t accU = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) accU = mma(B.Wf[ks], sf[ks], accU);
         float u4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            u4[i] = cur.ut[i] - accU[i];
-            const int t = n * C + 16 * w + 4 * g + i;
-            if (t < a.T)
-                ElemIO<T>::store(go + (((size_t)b * a.T + t) * a.H + h) * DV + 16 * jt + col,
-                                 cur.oi[i] + accO[i]);
-        }
+        for (int i = 0; i < 4; ++i) u4[i] = B.ut.get(i) - accU[i];
         st4<T>(U_lds + col * USTR + 16 * w + 4 * g, u4);
         __syncthreads();
+        F uf[2], up[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            uf[ks] = F::ld8(U_lds + col * USTR + 32 * ks + 8 * g);
+            up[ks] = F::ld4x2(U_lds + col * USTR + 32 * ks + 4 * g, U_lds + col * USTR + 32 * ks + 16 + 4 * g);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // S <- Diag(Gam) S + Kh^T U for this wave's dk rows
 #pragma unroll
         for (int d = 0; d < DTW; ++d) {
             const int dt = w * DTW + d;
             f32x4_t acc;
+            acc[0] = B.gam[d].x * S[d][0];
+            acc[1] = B.gam[d].y * S[d][1];
+            acc[2] = B.gam[d].z * S[d][2];
+            acc[3] = B.gam[d].w * S[d][3];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = cur.gam[d][i] * S[d][i];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const F uf = F::ld8(U_lds + col * USTR + 32 * ks + 8 * g);
-                acc = mma(cur.Kf[d][ks], uf, acc);
-            }
+            for (int ks = 0; ks < 2; ++ks) acc = mma(B.Kf[d][ks], uf[ks], acc);
             S[d] = acc;
-            float x[4] = {acc[0], acc[1], acc[2], acc[3]};
+            const float x[4] = {acc[0], acc[1], acc[2], acc[3]};
             st4<T>(S_lds + col * SSTR + 16 * dt + 4 * g, x);
         }
+        // O^T = S^T Qt^T + U^T Bq^T (old S; causal inside the chunk: only the
+        // token steps up to this wave's block)
+        f32x4_t accO = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) accO = mma(sf[ks], B.Qf[ks], accO);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            if (ks <= (w >> 1)) accO = mma(up[ks], B.Bf[ks], accO);
+        const unsigned soff = (unsigned)n * C * orow;
+        if (sizeof(T) == 2) {
+            uint2 v;
+            v.x = pack_bf16x2(accO[0], accO[1]);
+            v.y = pack_bf16x2(accO[2], accO[3]);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), orsrc, ovoff, soff, 0);
+        } else {
+            u32x4_t v;
+            v[0] = __float_as_uint(accO[0]);
+            v[1] = __float_as_uint(accO[1]);
+            v[2] = __float_as_uint(accO[2]);
+            v[3] = __float_as_uint(accO[3]);
+            __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, ovoff, soff, 0);
+        }
         __syncthreads();
-        if (n + 1 < nchunks) cur = nxt;
+    };
+
+    // Two-deep ring.  Refills past the last chunk re-read the last chunk
+    // (in bounds, unused) so every iteration issues the same loads.
+    const int last = nchunks - 1;
+    Buf b0, b1;
+    load(b0, 0);
+    load(b1, min(1, last));
+#pragma unroll 1
+    for (int n = 0; n < nchunks; n += 2) {
+        step(b0, n);
+        load(b0, min(n + 2, last));
+        if (n + 1 >= nchunks) break;
+        step(b1, n + 1);
+        load(b1, min(n + 3, last));
     }
     if (a.sT) {
 #pragma unroll
@@ -610,6 +670,19 @@ __global__ __launch_bounds__(K2_THREADS) void kda_state_kernel(KdaArgs a) {
     }
 }
 
+int num_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <typename T, int DK, int DV>
 hipError_t launch_chunks_typed(const KdaArgs &a, hipStream_t stream) {
     using SM = K1Smem<T, DK, DV>;
@@ -620,8 +693,9 @@ hipError_t launch_chunks_typed(const KdaArgs &a, hipStream_t stream) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int n1 = a.B * a.H * a.n_chunks;
-    hipLaunchKernelGGL((kda_intra_kernel<T, DK, DV>), dim3(n1), dim3(K1_THREADS), SM::BYTES, stream, a);
+    const int items = a.B * a.H * a.n_chunks;
+    const int grid = items < num_cus() ? items : num_cus();
+    hipLaunchKernelGGL((kda_intra_kernel<T, DK, DV>), dim3(grid), dim3(K1_THREADS), SM::BYTES, stream, a);
     return hipGetLastError();
 }
 
