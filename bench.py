@@ -78,6 +78,9 @@ def main() -> int:
     ap.add_argument("--cpu-frames", type=int, default=0,
                     help="latent frames in the CPU-baseline sample (0 = the whole stream)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (three times) and "
+                         "exit: the reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -88,6 +91,16 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.arange(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "copies": 3}), flush=True)
+        return 0
 
     from linear_attention_sequence_modality_amd import kda
     from linear_attention_sequence_modality_amd.inputs import CONFIG_BY_NAME, make_inputs

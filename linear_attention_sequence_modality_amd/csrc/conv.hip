@@ -144,29 +144,43 @@ struct VisualWave {
         return (unsigned)(n_text + (t * gh + hh) * gw + ww) * (unsigned)rowb;
     }
 
-    // Input slice ti contributes tap a to output slice ti + PT - a, kept in
-    // accumulator slot (ti + PT - a) mod 3 == (P + PT - a) mod 3.  EDGE: the
-    // w-run touches the left or right grid border (positions must be tested).
+    typename O::XT xs[2][3][WR + 2];   // double-buffered input slice (3 rows x WR+2 positions)
+
+    // Load input slice ti (rows h-1..h+1) into buffer B; rows and positions
+    // outside the grid are zero.  Every condition is wave-uniform.
+    template <int B, bool EDGE>
+    __device__ __forceinline__ void load_slice(int ti) {
+        if (ti >= gt) return;
+#pragma unroll
+        for (int dh = 0; dh < 3; ++dh) {
+            const int hh = h + dh - 1;
+            if (hh < 0 || hh >= gh) continue;
+            const unsigned row = tok_off(ti, hh, w0) - (unsigned)rowb;   // position w0 - 1
+#pragma unroll
+            for (int j = 0; j < WR + 2; ++j) {
+                const unsigned soff = row + (unsigned)j * (unsigned)rowb;
+                if (EDGE) {
+                    const int ww = w0 - 1 + j;
+                    xs[B][dh][j] = (ww >= 0 && ww < gw) ? O::bload(rx, lane_off, soff) : O::zero();
+                } else {
+                    xs[B][dh][j] = O::bload(rx, lane_off, soff);
+                }
+            }
+        }
+    }
+
+    // Step P of the march (slice ti = 6m + P): prefetch slice ti + 1, then apply
+    // slice ti.  Input slice ti contributes tap a to output slice ti + PT - a,
+    // kept in accumulator slot (ti + PT - a) mod 3 == (P + PT - a) mod 3.
     template <int P, bool EDGE>
     __device__ __forceinline__ void step(int ti) {
+        constexpr int CUR = P & 1;
+        load_slice<CUR ^ 1, EDGE>(ti + 1);
         if (ti < gt) {
 #pragma unroll
             for (int dh = 0; dh < 3; ++dh) {
                 const int hh = h + dh - 1;
                 if (hh < 0 || hh >= gh) continue;
-                // scalar offset of position w0 - 1 + j; lanes add their channel offset
-                const unsigned row = tok_off(ti, hh, w0) - (unsigned)rowb;
-                typename O::XT xr[WR + 2];
-#pragma unroll
-                for (int j = 0; j < WR + 2; ++j) {
-                    const unsigned soff = row + (unsigned)j * (unsigned)rowb;
-                    if (EDGE) {
-                        const int ww = w0 - 1 + j;
-                        xr[j] = (ww >= 0 && ww < gw) ? O::bload(rx, lane_off, soff) : O::zero();
-                    } else {
-                        xr[j] = O::bload(rx, lane_off, soff);
-                    }
-                }
 #pragma unroll
                 for (int a = 0; a < 3; ++a) {
                     const int slot = ((P + PT - a) % 3 + 3) % 3;
@@ -174,7 +188,7 @@ struct VisualWave {
                     for (int e = 0; e < 3; ++e)
 #pragma unroll
                         for (int j = 0; j < WR; ++j)
-                            O::mac(taps, (a * 3 + dh) * 3 + e, xr[j + e], acc[slot][j][0], acc[slot][j][1]);
+                            O::mac(taps, (a * 3 + dh) * 3 + e, xs[CUR][dh][j + e], acc[slot][j][0], acc[slot][j][1]);
                 }
             }
         }
@@ -193,14 +207,21 @@ struct VisualWave {
 
     template <bool EDGE>
     __device__ void march() {
+        load_slice<0, EDGE>(0);
         // One extra empty slice (ti == gt) flushes the last output slice.
 #pragma unroll 1
-        for (int ti = 0; ti <= gt; ti += 3) {
+        for (int ti = 0; ti <= gt; ti += 6) {
             step<0, EDGE>(ti);
             if (ti + 1 > gt) break;
             step<1, EDGE>(ti + 1);
             if (ti + 2 > gt) break;
             step<2, EDGE>(ti + 2);
+            if (ti + 3 > gt) break;
+            step<3, EDGE>(ti + 3);
+            if (ti + 4 > gt) break;
+            step<4, EDGE>(ti + 4);
+            if (ti + 5 > gt) break;
+            step<5, EDGE>(ti + 5);
         }
     }
 
@@ -297,7 +318,7 @@ __device__ void text_item(const ConvArgs &a, const Layout &L, int s, int item, i
 }
 
 template <typename T, int PT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void conv_kernel(ConvArgs a, Layout L) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 2 : 3))) void conv_kernel(ConvArgs a, Layout L) {
     int blk = xcd_remap(blockIdx.x, L.nblocks);
     const int wave = uniform(threadIdx.x / LANES), lane = threadIdx.x % LANES;
     constexpr int WPB = NT / LANES;
