@@ -25,6 +25,41 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 
+# HBM byte counters per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, in KiB), taken on
+# the source files whose digest is stored beside them; a kernel whose sources changed since reports
+# traffic null.  A plain 1 GiB device copy reads FETCH_SIZE = 524302 KiB and WRITE_SIZE = 1048576 KiB,
+# hence the scale factors.
+FETCH_SCALE = 1048576.0 / 524302.0
+WRITE_SCALE = 1.0
+KERNEL_SOURCES = {
+    "conv": ("conv.hip", "common.h", "launch.h"),
+    "chunks": ("kda.hip", "mfma.h", "common.h", "launch.h"),
+    "scan": ("kda.hip", "mfma.h", "common.h", "launch.h"),
+}
+MEASURED_TRAFFIC = {
+    ("video_5s_480x832", "conv"): ("3f505f600b28876e", 594372.3, 399264.0),
+    ("video_5s_480x832", "chunks"): ("1bdf00f12a977546", 274548.0, 586607.2),
+    ("video_5s_480x832", "scan"): ("1bdf00f12a977546", 301643.0, 133088.0),
+}
+
+
+def source_digest(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_sequence_modality_amd", "csrc")
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """Counter-measured HBM bytes per launch, or None if not taken on the current sources."""
+    rec = MEASURED_TRAFFIC.get((workload, kernel))
+    if rec is None or rec[0] != source_digest(kernel):
+        return None
+    return int(round((rec[1] * FETCH_SCALE + rec[2] * WRITE_SCALE) * 1024))
+
 
 def roofline_bytes(cfg) -> dict:
     """Algorithmic HBM bytes per launch of each kernel (what its interface must move).
@@ -173,7 +208,7 @@ def main() -> int:
                    "chunk": 64, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB/s"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac_hbm"],
-                     "traffic": None},
+                     "traffic": measured_traffic(cfg.name, dom)},
         "kernels": kernels,
         "path": {"min_bytes": rb["path_min"], "GB/s_vs_path_min": round(path_gbs, 1),
                  "frac_of_path_roofline": round(path_gbs / HBM_PEAK_GBS, 4)},

@@ -18,10 +18,10 @@
 // to the workspace in the exact register-fragment order kernel 2 consumes.
 // The next chunk's inputs are loaded into registers while the current chunk
 // is transformed.
-// Kernel 2 (kda_state_kernel: one 4-wave workgroup per (batch, head,
-// 16-column slice of dv)) keeps its state slice in registers, exchanges only
-// the 64 x 16 U block and the bf16 copy of S through LDS, and streams the
-// workspace through a two-deep register ring.
+// Kernel 2 (kda_state_kernel: one wave per (batch, head, 16-column slice of
+// dv)) keeps its state slice in registers, feeds it to the matrix cores
+// without any LDS exchange or barrier, and streams the workspace through
+// registers one chunk ahead.
 //
 // Decay factorisation: 2^(G_r - G_s) for s <= r is split around the midpoint
 // m(R) = 16R + 8 of the 16-row sub-block R of row r:
@@ -38,7 +38,6 @@ namespace {
 
 constexpr int C = kChunk;          // 64 tokens per chunk
 constexpr int K1_THREADS = 512;    // 8 waves
-constexpr int K2_THREADS = 256;    // 4 waves
 constexpr int kBufWord3 = 0x00020000;   // 4th descriptor word of a raw gfx9 buffer
 
 constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -47,22 +46,28 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---- workspace layout (per batch, head, chunk; element type T) ---------------
-// Fragment order: kernel-2 lane l of wave R loads 16 contiguous bytes per
-// fragment.  dk-indexed fragments (W, Qt) hold, in slots 0..3 and 4..7, the
-// channels 32ks + 4g + i and 32ks + 16 + 4g + i (g = l/16), matching the
-// order in which kernel 2 reads its bf16 copy of S; BT is ordered likewise
-// over tokens.  Kh holds 8 consecutive tokens per lane.
+// Fragment order: kernel-2 lane l loads 16 contiguous bytes per fragment.
+// dk-indexed fragments (W, Qt) hold, in slots 0..3 and 4..7, the channels
+// 32ks + 4g + i and 32ks + 16 + 4g + i (g = l/16), matching the rows kernel 2
+// holds of its state tiles 2ks and 2ks+1; token-indexed fragments (BT, Kh^T)
+// are ordered likewise over tokens.
 template <typename T, int DK, int DV>
 struct Ws {
     static constexpr size_t W = 0;                 // [4 R][DK/32][64][8]  W rows of block R
     static constexpr size_t QT = W + 64 * DK;      // [4 R][DK/32][64][8]  Qt
-    static constexpr size_t KH = QT + 64 * DK;     // [DK/16][2][64][8]    Kh^T (dk rows x tokens)
+    static constexpr size_t KH = QT + 64 * DK;     // [DK/16][2][64][8]    Kh^T (dk rows x tokens, k order as BT)
     static constexpr size_t BT = KH + 64 * DK;     // [4 R][2][64][8]      Bq rows of block R
-    static constexpr size_t U = BT + 64 * 64;      // [DV/16][4 R][64][4]  Ut, accumulator order
+    static constexpr size_t U = BT + 64 * 64;      // [DV/16][64][4 R][4]  Ut, accumulator order
     static constexpr size_t ELEMS = U + 64 * DV;
-    static constexpr size_t GAM_BYTE = round_up(ELEMS * sizeof(T), 16);   // fp32 [DK]
+    static constexpr size_t GAM_BYTE = round_up(ELEMS * sizeof(T), 16);   // fp32 [DK], gam_pos order
     static constexpr size_t BYTES = round_up(GAM_BYTE + DK * sizeof(float), 256);
 };
+
+// Position of key channel c = 16 dt + 4 g + i in the stored chunk decay: the
+// 4 DK/16 values a kernel-2 lane group g needs are contiguous, 2 per lane.
+template <int DK> __device__ __forceinline__ int gam_pos(int c) {
+    return ((c >> 2) & 3) * (DK / 4) + 4 * (c >> 4) + (c & 3);
+}
 
 // ---- raw 8-element rows (register prefetch without conversion) --------------
 template <typename T> struct Raw8;
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
                     const int S = f - fp_index(R, 0);
                     Fp[f * DK + c] = exp2f(Gat(16 * R + 8) - Gat(16 * S + 8));
                 } else {
-                    ws_gam[c] = exp2f(Gat(63));
+                    ws_gam[gam_pos<DK>(c)] = exp2f(Gat(63));
                 }
             }
             __syncthreads();
@@ -411,12 +416,16 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
                 const int v = u < NT ? u : u - NT, ln = v & 63, gq = ln >> 4;
                 float x[8];
                 if (u < NT) {
-                    // Kh^T fragment (dt, ks, lane): channel 16dt + ln%16, tokens 32ks + 8*(ln/16) + 0..7
-                    const int dt = v >> 7, ks = (v >> 6) & 1;
-                    const int c = 16 * dt + (ln & 15), t0 = 32 * ks + 8 * gq, R = t0 >> 4;
-                    const float kh = Kh[R * DK + c];
+                    // Kh^T fragment (dt, kt, lane): channel 16dt + ln%16, tokens
+                    // 32kt + 4*(ln/16) + {0..3} (block 2kt) and 32kt + 16 + 4*(ln/16) + {0..3} (block 2kt+1)
+                    const int dt = v >> 7, kt = (v >> 6) & 1;
+                    const int c = 16 * dt + (ln & 15), t0 = 32 * kt + 4 * gq;
+                    const float kh0 = Kh[(2 * kt) * DK + c], kh1 = Kh[(2 * kt + 1) * DK + c];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) x[j] = (float)Kb[(t0 + j) * SM::KS + c] * kh;
+                    for (int j = 0; j < 4; ++j) {
+                        x[j] = (float)Kb[(t0 + j) * SM::KS + c] * kh0;
+                        x[4 + j] = (float)Kb[(t0 + 16 + j) * SM::KS + c] * kh1;
+                    }
                     st8f<T>(ws + WL::KH + (size_t)v * 8, x);
                 } else {
                     // Qt fragment (R, ks, lane): row 16R + ln%16, channels 32ks + 4*(ln/16) + {0..3, 16..19}
@@ -496,7 +505,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
                         for (int ks = 0; ks <= (R >> 1); ++ks)
                             acc = mma(F::ld8(Tm16 + (16 * R + col) * SM::TS + 32 * ks + 8 * g), rv[ks], acc);
                         const float u4[4] = {acc[0], acc[1], acc[2], acc[3]};
-                        st4<T>(ws + WL::U + ((size_t)(jt * 4 + R) * 64 + l) * 4, u4);
+                        st4<T>(ws + WL::U + ((size_t)(jt * 64 + l) * 4 + R) * 4, u4);
                     }
                 }
             }
@@ -506,165 +515,338 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
 }
 
 // ---- kernel 2: sequential state pass ------------------------------------------------
+// One 3-wave workgroup per (batch, head, 16 value columns):
+//   wave 0 (recurrence): S <- Diag(Gam) S + Kh^T (Ut - W S), chunk after chunk;
+//   wave 1 (output):     O^T = S^T Qt^T + U^T Bq^T from the S and U wave 0 used;
+//   wave 2 (store):      writes O to o.
+// Lane l = 16 g + col of wave 0 holds rows 16 dt + 4 g + i (i = 0..3) of
+// value column col of S in fp32: S is kept as DK/16 accumulator tiles.  Two
+// tiles side by side are directly an MFMA operand whose 32 k-slots are the
+// rows 32 ks + {4g+i, 16+4g+i} -- the B operand of W S (k = key channel) and,
+// unchanged, the A operand of S^T Qt^T -- so the state never leaves wave 0's
+// registers; U becomes an operand the same way (k = token).  The workspace
+// fragments are stored in the matching k order.
+// Wave 0 hands the bf16 operands of S and U to wave 1, and wave 1 the output
+// tiles to wave 2, through small LDS rings guarded by counters: a wave waits
+// only when its ring is empty (consumer) or full (producer).  Keeping loads
+// and stores in different waves lets every wave keep its loads in flight
+// across chunk steps: a wave with both outstanding would drain everything at
+// each wait.  Each wave streams its operands through registers one chunk ahead.
+
+// Lane N of the calling lane's row of 16 (DPP row_newbcast).
+template <int N> __device__ __forceinline__ float row_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xf, 0xf, false));
+}
+// Run-time lane index; folds to one DPP operand once n is a constant after unrolling.
+__device__ __forceinline__ float row_bcast(float x, int n) {
+    switch (n) {
+    case 0: return row_bcast<0>(x);
+    case 1: return row_bcast<1>(x);
+    case 2: return row_bcast<2>(x);
+    case 3: return row_bcast<3>(x);
+    case 4: return row_bcast<4>(x);
+    case 5: return row_bcast<5>(x);
+    case 6: return row_bcast<6>(x);
+    case 7: return row_bcast<7>(x);
+    case 8: return row_bcast<8>(x);
+    case 9: return row_bcast<9>(x);
+    case 10: return row_bcast<10>(x);
+    case 11: return row_bcast<11>(x);
+    case 12: return row_bcast<12>(x);
+    case 13: return row_bcast<13>(x);
+    case 14: return row_bcast<14>(x);
+    default: return row_bcast<15>(x);
+    }
+}
+
+template <typename T> __device__ __forceinline__ Frag<T> tiles_to_frag(const f32x4_t &lo, const f32x4_t &hi);
+template <> __device__ __forceinline__ Frag<bf16_t> tiles_to_frag<bf16_t>(const f32x4_t &lo, const f32x4_t &hi) {
+    const uint4 u = make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                               pack_bf16x2(hi[2], hi[3]));
+    Frag<bf16_t> f;
+    f.v = __builtin_bit_cast(bf16x8_t, u);
+    return f;
+}
+template <> __device__ __forceinline__ Frag<float> tiles_to_frag<float>(const f32x4_t &lo, const f32x4_t &hi) {
+    Frag<float> f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f.v[i] = lo[i];
+        f.v[4 + i] = hi[i];
+    }
+    return f;
+}
+
+// Raw buffer loads: a lane-dependent offset plus a wave-uniform one.
+template <typename T> struct BufLd;
+template <> struct BufLd<bf16_t> {
+    __device__ __forceinline__ static Frag<bf16_t> frag(__amdgpu_buffer_rsrc_t r, unsigned v, unsigned s) {
+        Frag<bf16_t> f;
+        f.v = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, v, s, 0));
+        return f;
+    }
+    __device__ __forceinline__ static void raw8(Raw8<bf16_t> &x, __amdgpu_buffer_rsrc_t r, unsigned v, unsigned s) {
+        x.u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, v, s, 0));
+    }
+};
+template <> struct BufLd<float> {
+    __device__ __forceinline__ static Frag<float> frag(__amdgpu_buffer_rsrc_t r, unsigned v, unsigned s) {
+        const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, v, s, 0);
+        const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, v, s + 16, 0);
+        Frag<float> f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f.v[i] = __uint_as_float(a[i]);
+            f.v[4 + i] = __uint_as_float(b[i]);
+        }
+        return f;
+    }
+    __device__ __forceinline__ static void raw8(Raw8<float> &x, __amdgpu_buffer_rsrc_t r, unsigned v, unsigned s) {
+        x.a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, v, s, 0));
+        x.b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, v, s + 16, 0));
+    }
+};
+
+// Wait until an LDS counter reaches target.  Bounded: a kernel-wide poll
+// budget (far above what a correct run uses) guarantees that every wave exits
+// even if its partner never signals.
+__device__ __forceinline__ void wait_counter(int *ctr, int target, int &budget) {
+    while (budget > 0 && __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+        --budget;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Publish a counter after this wave's earlier LDS writes have completed.
+__device__ __forceinline__ void signal_counter(int *ctr, int value) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0) only
+    __hip_atomic_store(ctr, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+constexpr int kRing = 4;              // chunk steps buffered between the waves
+constexpr int kPollBudget = 1 << 24;  // LDS polls per wave per launch
+
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(K2_THREADS) void kda_state_kernel(KdaArgs a) {
+__global__ __launch_bounds__(192) void kda_state_kernel(KdaArgs a) {
     using WL = Ws<T, DK, DV>;
     using F = Frag<T>;
+    using B = BufLd<T>;
     constexpr int NJT = DV / 16;     // 16-column value slices
     constexpr int NKS = DK / 32;     // contraction steps over dk
-    constexpr int DTW = DK / 64;     // 16-row dk tiles per wave
-    constexpr int SSTR = DK + 16 / (int)sizeof(T);
-    constexpr int USTR = 64 + 16 / (int)sizeof(T);
-    __shared__ __attribute__((aligned(16))) T S_lds[16 * SSTR];   // [dv col][dk]
-    __shared__ __attribute__((aligned(16))) T U_lds[16 * USTR];   // [dv col][token]
+    constexpr int NDT = DK / 16;     // 16-row state tiles
+    constexpr unsigned ES = sizeof(T);
+    // ring slot: S operands (NKS fragments) then U operands (2 fragments), per lane
+    __shared__ F su_ring[kRing][NKS + 2][64];
+    __shared__ f32x4_t o_ring[kRing][4][64];
+    __shared__ int ctr[4];   // S/U produced, S/U consumed, O produced, O consumed
+    if (threadIdx.x < 4) ctr[threadIdx.x] = 0;
+    __syncthreads();
 
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
     const int jt = blk % NJT, bh = blk / NJT;
     const int b = bh / a.H, h = bh % a.H;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, col = l & 15, g = l >> 4;
-    const int nchunks = a.n_chunks;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = threadIdx.x & 63, col = l & 15, g = l >> 4;
+    const int nchunks = a.n_chunks, last = nchunks - 1;
+    int budget = kPollBudget;
 
-    // o of this (batch, head, 16 value columns) as a raw buffer: token t at
-    // byte t*H*DV*es.  Rows past the end of the stream fall outside the range
-    // and the hardware drops their stores.  The output tile is produced
-    // transposed (lane: 4 consecutive value columns of one token), so each
-    // lane writes one 4-column piece per chunk.
-    const unsigned es = sizeof(T), orow = (unsigned)a.H * DV * es;
-    char *obase = static_cast<char *>(a.o) + ((((size_t)b * a.T) * a.H + h) * DV + 16 * jt) * es;
-    const unsigned onum = (unsigned)a.T * orow - (unsigned)(h * DV + 16 * jt) * es;
-    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(obase, 0, (int)onum, kBufWord3);
-    const unsigned ovoff = (unsigned)(16 * w + col) * orow + (unsigned)(4 * g) * es;
-
-    f32x4_t S[DTW];
-#pragma unroll
-    for (int d = 0; d < DTW; ++d) {
-        const int dt = w * DTW + d;
-        float x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * dt + 4 * g + i;
-            x[i] = a.s0 ? a.s0[((size_t)bh * DK + row) * DV + 16 * jt + col] : 0.f;
-            S[d][i] = x[i];
-        }
-        st4<T>(S_lds + col * SSTR + 16 * dt + 4 * g, x);
-    }
-    __syncthreads();
-
+    // this (batch, head)'s workspace: chunk n at byte n * BYTES (< 4 GiB, checked on the host)
     const char *wsh = static_cast<const char *>(a.ws) + (size_t)bh * nchunks * WL::BYTES;
-    struct Buf {
-        F Wf[NKS], Qf[NKS], Kf[DTW][2], Bf[2];
-        Raw4<T> ut;
-        float4 gam[DTW];
-    };
-    auto load = [&](Buf &B, int n) {
-        const char *base = wsh + (size_t)n * WL::BYTES;
-        const T *ws = reinterpret_cast<const T *>(base);
-        const float *gam = reinterpret_cast<const float *>(base + WL::GAM_BYTE);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            B.Wf[ks] = F::ld8(ws + WL::W + ((size_t)(w * NKS + ks) * 64 + l) * 8);
-            B.Qf[ks] = F::ld8(ws + WL::QT + ((size_t)(w * NKS + ks) * 64 + l) * 8);
-        }
-#pragma unroll
-        for (int d = 0; d < DTW; ++d) {
-            const int dt = w * DTW + d;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) B.Kf[d][ks] = F::ld8(ws + WL::KH + ((size_t)(dt * 2 + ks) * 64 + l) * 8);
-            B.gam[d] = *reinterpret_cast<const float4 *>(gam + 16 * dt + 4 * g);
-        }
-        // Unconditional loads (the second Bq fragment of waves 0 and 1 is never
-        // used): the number of loads in flight must not depend on the path, or
-        // the wait before the first use degrades to waiting for all of them.
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) B.Bf[ks] = F::ld8(ws + WL::BT + ((size_t)(w * 2 + ks) * 64 + l) * 8);
-        B.ut.load(ws + WL::U + ((size_t)(jt * 4 + w) * 64 + l) * 4);
-    };
+    const __amdgpu_buffer_rsrc_t wsr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(wsh), 0, (int)(unsigned)((size_t)nchunks * WL::BYTES), kBufWord3);
+    const unsigned lane8 = (unsigned)l * 8 * ES;   // lane's fragment inside a [64][8] block
+    auto cbase = [&](int n) { return (unsigned)n * (unsigned)WL::BYTES; };
 
-    auto step = [&](const Buf &B, int n) {
-        // S fragments (bf16 copy, dk order matching W and Qt), all reads issued together
-        F sf[NKS];
+    if (wave == 0) {
+        // ---------------- recurrence ----------------
+        f32x4_t S[NDT];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            sf[ks] = F::ld4x2(S_lds + col * SSTR + 32 * ks + 4 * g, S_lds + col * SSTR + 32 * ks + 16 + 4 * g);
-        __builtin_amdgcn_sched_barrier(0);   // keep the LDS reads ahead of the MFMA chain
-        // U = Ut - W S for this wave's 16 rows
-        f32x4_t accU = zero4();
+        for (int dt = 0; dt < NDT; ++dt) S[dt] = zero4();
+        if (a.s0) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) accU = mma(B.Wf[ks], sf[ks], accU);
-        float u4[4];
+            for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) u4[i] = B.ut.get(i) - accU[i];
-        st4<T>(U_lds + col * USTR + 16 * w + 4 * g, u4);
-        __syncthreads();
-        F uf[2], up[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            uf[ks] = F::ld8(U_lds + col * USTR + 32 * ks + 8 * g);
-            up[ks] = F::ld4x2(U_lds + col * USTR + 32 * ks + 4 * g, U_lds + col * USTR + 32 * ks + 16 + 4 * g);
+                for (int i = 0; i < 4; ++i)
+                    S[dt][i] = a.s0[((size_t)bh * DK + 16 * dt + 4 * g + i) * DV + 16 * jt + col];
         }
+        F Wf[4][NKS], Kf[NDT][2];
+        Raw8<T> ut[2];   // Ut rows 16R + 4g + i of column col: element 4R + i
+        float2 gam;      // decay of channels 16 dt + 4g + i for dt = col/2, i = 2(col%2) + {0, 1}
+        const unsigned ut_off = (unsigned)(WL::U + (size_t)(jt * 64 + l) * 16) * ES;
+        const unsigned gam_off = (unsigned)WL::GAM_BYTE + 4u * (unsigned)(g * (DK / 4) + 2 * min(col, DK / 8 - 1));
+        auto load_w = [&](int n) {
+            const unsigned c = cbase(n);
+#pragma unroll
+            for (int R = 0; R < 4; ++R)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    Wf[R][ks] = B::frag(wsr, lane8, c + (unsigned)(WL::W + (R * NKS + ks) * 512) * ES);
+        };
+        auto load_u = [&](int n) {
+            const unsigned c = cbase(n);
+            B::raw8(ut[0], wsr, ut_off, c);
+            B::raw8(ut[1], wsr, ut_off, c + 8 * ES);
+        };
+        auto load_k = [&](int n) {
+            const unsigned c = cbase(n);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+                    Kf[dt][kt] = B::frag(wsr, lane8, c + (unsigned)(WL::KH + (dt * 2 + kt) * 512) * ES);
+            const u32x2_t gv = __builtin_amdgcn_raw_buffer_load_b64(wsr, gam_off, c, 0);
+            gam = make_float2(__uint_as_float(gv[0]), __uint_as_float(gv[1]));
+        };
+        // the loop issues W, Ut, then Kh + Gam each step; start in the same order
         __builtin_amdgcn_sched_barrier(0);
-        // S <- Diag(Gam) S + Kh^T U for this wave's dk rows
-#pragma unroll
-        for (int d = 0; d < DTW; ++d) {
-            const int dt = w * DTW + d;
-            f32x4_t acc;
-            acc[0] = B.gam[d].x * S[d][0];
-            acc[1] = B.gam[d].y * S[d][1];
-            acc[2] = B.gam[d].z * S[d][2];
-            acc[3] = B.gam[d].w * S[d][3];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) acc = mma(B.Kf[d][ks], uf[ks], acc);
-            S[d] = acc;
-            const float x[4] = {acc[0], acc[1], acc[2], acc[3]};
-            st4<T>(S_lds + col * SSTR + 16 * dt + 4 * g, x);
-        }
-        // O^T = S^T Qt^T + U^T Bq^T (old S; causal inside the chunk: only the
-        // token steps up to this wave's block)
-        f32x4_t accO = zero4();
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) accO = mma(sf[ks], B.Qf[ks], accO);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            if (ks <= (w >> 1)) accO = mma(up[ks], B.Bf[ks], accO);
-        const unsigned soff = (unsigned)n * C * orow;
-        if (sizeof(T) == 2) {
-            uint2 v;
-            v.x = pack_bf16x2(accO[0], accO[1]);
-            v.y = pack_bf16x2(accO[2], accO[3]);
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), orsrc, ovoff, soff, 0);
-        } else {
-            u32x4_t v;
-            v[0] = __float_as_uint(accO[0]);
-            v[1] = __float_as_uint(accO[1]);
-            v[2] = __float_as_uint(accO[2]);
-            v[3] = __float_as_uint(accO[3]);
-            __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, ovoff, soff, 0);
-        }
-        __syncthreads();
-    };
-
-    // Two-deep ring.  Refills past the last chunk re-read the last chunk
-    // (in bounds, unused) so every iteration issues the same loads.
-    const int last = nchunks - 1;
-    Buf b0, b1;
-    load(b0, 0);
-    load(b1, min(1, last));
+        load_w(0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_u(0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_k(0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll 1
-    for (int n = 0; n < nchunks; n += 2) {
-        step(b0, n);
-        load(b0, min(n + 2, last));
-        if (n + 1 >= nchunks) break;
-        step(b1, n + 1);
-        load(b1, min(n + 3, last));
-    }
-    if (a.sT) {
+        for (int n = 0; n < nchunks; ++n) {
+            const int nx = min(n + 1, last);
+            F(&slot)[NKS + 2][64] = su_ring[n % kRing];
+            F Sb[NKS];
 #pragma unroll
-        for (int d = 0; d < DTW; ++d) {
-            const int dt = w * DTW + d;
+            for (int ks = 0; ks < NKS; ++ks) {
+                Sb[ks] = tiles_to_frag<T>(S[2 * ks], S[2 * ks + 1]);
+                slot[ks][l] = Sb[ks];
+            }
+            // U = Ut - W S  (token rows 16R + 4g + i, value column col)
+            f32x4_t U[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * dt + 4 * g + i;
-                a.sT[((size_t)bh * DK + row) * DV + 16 * jt + col] = S[d][i];
+            for (int R = 0; R < 4; ++R) U[R] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int R = 0; R < 4; ++R) U[R] = mma(Wf[R][ks], Sb[ks], U[R]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_w(nx);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int R = 0; R < 2; ++R) {
+                float x[8];
+                ut[R].get(x);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    U[2 * R][i] = x[i] - U[2 * R][i];
+                    U[2 * R + 1][i] = x[4 + i] - U[2 * R + 1][i];
+                }
+            }
+            const F Ub[2] = {tiles_to_frag<T>(U[0], U[1]), tiles_to_frag<T>(U[2], U[3])};
+            slot[NKS][l] = Ub[0];
+            slot[NKS + 1][l] = Ub[1];
+            signal_counter(&ctr[0], n + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            load_u(nx);
+            __builtin_amdgcn_sched_barrier(0);
+            // S <- Diag(Gam) S + Kh^T U; the decay of (dt, i) sits in lane 2dt + i/2 of the row
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[dt][i] *= row_bcast(i & 1 ? gam.y : gam.x, 2 * dt + (i >> 1));
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) S[dt] = mma(Kf[dt][kt], Ub[kt], S[dt]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_k(nx);
+            __builtin_amdgcn_sched_barrier(0);
+            // the next step overwrites slot (n+1) % kRing: wave 1 must be done with chunk n+1-kRing
+            if (n + 1 < nchunks && n + 1 >= kRing) wait_counter(&ctr[1], n + 2 - kRing, budget);
+        }
+        if (a.sT) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a.sT[((size_t)bh * DK + 16 * dt + 4 * g + i) * DV + 16 * jt + col] = S[dt][i];
+        }
+    } else if (wave == 1) {
+        // ---------------- output: O^T = S^T Qt^T + U^T Bq^T ----------------
+        F Qf[4][NKS], Bf[6];
+        auto load_qb = [&](int n) {
+            const unsigned c = cbase(n);
+#pragma unroll
+            for (int R = 0; R < 4; ++R)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    Qf[R][ks] = B::frag(wsr, lane8, c + (unsigned)(WL::QT + (R * NKS + ks) * 512) * ES);
+            // Bq: k-step 0 of every token block, k-step 1 of blocks 2 and 3
+#pragma unroll
+            for (int R = 0; R < 4; ++R) Bf[R] = B::frag(wsr, lane8, c + (unsigned)(WL::BT + (R * 2) * 512) * ES);
+            Bf[4] = B::frag(wsr, lane8, c + (unsigned)(WL::BT + 5 * 512) * ES);
+            Bf[5] = B::frag(wsr, lane8, c + (unsigned)(WL::BT + 7 * 512) * ES);
+        };
+        load_qb(0);
+#pragma unroll 1
+        for (int n = 0; n < nchunks; ++n) {
+            const int nx = min(n + 1, last);
+            wait_counter(&ctr[0], n + 1, budget);
+            F(&slot)[NKS + 2][64] = su_ring[n % kRing];
+            F Sb[NKS], Ub[2];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) Sb[ks] = slot[ks][l];
+            Ub[0] = slot[NKS][l];
+            Ub[1] = slot[NKS + 1][l];
+            f32x4_t O[4];
+#pragma unroll
+            for (int R = 0; R < 4; ++R) O[R] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int R = 0; R < 4; ++R) O[R] = mma(Sb[ks], Qf[R][ks], O[R]);
+            // causal inside the chunk: token block R sees token k-steps kt <= R/2
+#pragma unroll
+            for (int R = 0; R < 4; ++R) O[R] = mma(Ub[0], Bf[R], O[R]);
+            O[2] = mma(Ub[1], Bf[4], O[2]);
+            O[3] = mma(Ub[1], Bf[5], O[3]);
+            signal_counter(&ctr[1], n + 1);   // slot reads are complete (the MFMAs consumed them)
+            __builtin_amdgcn_sched_barrier(0);
+            load_qb(nx);
+            __builtin_amdgcn_sched_barrier(0);
+            if (n >= kRing) wait_counter(&ctr[3], n + 1 - kRing, budget);
+#pragma unroll
+            for (int R = 0; R < 4; ++R) o_ring[n % kRing][R][l] = O[R];
+            signal_counter(&ctr[2], n + 1);
+        }
+    } else {
+        // ---------------- store ----------------
+        // o of this (batch, head, 16 value columns) as a raw buffer: token t at
+        // byte t*H*DV*es.  Rows past the end of the stream fall outside the range
+        // and the hardware drops their stores.  The output tile is transposed
+        // (lane: 4 consecutive value columns of one token).
+        const unsigned orow = (unsigned)a.H * DV * ES;
+        char *obase = static_cast<char *>(a.o) + ((((size_t)b * a.T) * a.H + h) * DV + 16 * jt) * ES;
+        const unsigned onum = (unsigned)a.T * orow - (unsigned)(h * DV + 16 * jt) * ES;
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(obase, 0, (int)onum, kBufWord3);
+        const unsigned ovoff = (unsigned)col * orow + (unsigned)(4 * g) * ES;
+#pragma unroll 1
+        for (int n = 0; n < nchunks; ++n) {
+            wait_counter(&ctr[2], n + 1, budget);
+            f32x4_t O[4];
+#pragma unroll
+            for (int R = 0; R < 4; ++R) O[R] = o_ring[n % kRing][R][l];
+            signal_counter(&ctr[3], n + 1);
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                const unsigned soff = ((unsigned)n * C + 16u * R) * orow;
+                if (sizeof(T) == 2) {
+                    u32x2_t v;
+                    v[0] = pack_bf16x2(O[R][0], O[R][1]);
+                    v[1] = pack_bf16x2(O[R][2], O[R][3]);
+                    __builtin_amdgcn_raw_buffer_store_b64(v, orsrc, ovoff, soff, 0);
+                } else {
+                    u32x4_t v;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(O[R][i]);
+                    __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, ovoff, soff, 0);
+                }
             }
         }
     }
@@ -702,7 +884,7 @@ hipError_t launch_chunks_typed(const KdaArgs &a, hipStream_t stream) {
 template <typename T, int DK, int DV>
 hipError_t launch_scan_typed(const KdaArgs &a, hipStream_t stream) {
     const int n2 = a.B * a.H * (DV / 16);
-    hipLaunchKernelGGL((kda_state_kernel<T, DK, DV>), dim3(n2), dim3(K2_THREADS), 0, stream, a);
+    hipLaunchKernelGGL((kda_state_kernel<T, DK, DV>), dim3(n2), dim3(192), 0, stream, a);
     return hipGetLastError();
 }
 
