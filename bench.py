@@ -121,7 +121,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures the single-GPU path only: the conv + KDA mixer shards by head "
-              "with no communication, and multi-GPU runs are not part of this build "
+              "with no communication, and this benchmark runs on one GPU only "
               "(got --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
         return 2
 
@@ -138,9 +138,9 @@ def main() -> int:
         return 0
 
     from linear_attention_sequence_modality_amd import kda
-    from linear_attention_sequence_modality_amd.inputs import CONFIG_BY_NAME, make_inputs
+    from linear_attention_sequence_modality_amd.inputs import WORKLOAD, make_inputs
 
-    cfg = CONFIG_BY_NAME[args.workload]
+    cfg = WORKLOAD[args.workload]
     torch.cuda.set_device(0)
     inp = {k: v.cuda() for k, v in make_inputs(cfg).items()}
     desc = kda.make_desc(cfg.n_text, cfg.grid, causal_t=cfg.causal_t)

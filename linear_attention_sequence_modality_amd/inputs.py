@@ -81,7 +81,7 @@ class StreamConfig:
 
 
 # The five stream workloads.  Seeds are 1000 + index.
-CONFIGS = [
+WORKLOADS = [
     StreamConfig("tiny_fp32", B=1, H=2, dk=64, dv=64, n_text=32, grid=(4, 10, 12),
                  dtype="f32", seed=1000),
     StreamConfig("proxy_image_1024px", B=8, H=4, dk=128, dv=128, n_text=512,
@@ -93,7 +93,7 @@ CONFIGS = [
     StreamConfig("video_30s_480x832", B=1, H=16, dk=128, dv=128, n_text=512,
                  grid=latent_grid(481, 480, 832), dtype="bf16", seed=1004),
 ]
-CONFIG_BY_NAME = {c.name: c for c in CONFIGS}
+WORKLOAD = {c.name: c for c in WORKLOADS}
 
 
 def _l2_normalise(x: np.ndarray) -> np.ndarray:

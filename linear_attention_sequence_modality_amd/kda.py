@@ -51,7 +51,7 @@ def load_library():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError("libkdaconv.so is not built (expected at %s); run "
-                           "__graft_entry__.build() first" % LIB_PATH)
+                           "python -m linear_attention_sequence_modality_amd.build first" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32 = ctypes.c_void_p, ctypes.c_int
     desc_p = ctypes.POINTER(KdaStreamDesc)

@@ -11,7 +11,7 @@
  * OpenMP only distributes independent (batch, head) scans and independent
  * channels; it never reorders the arithmetic of one output.
  *
- * Readings of points the pages leave open (each is listed in the design doc):
+ * Readings of points the pages leave open:
  *  - readout o_t = S_t^T q_t with the post-update state, no 1/sqrt(dk) scale;
  *  - q, k and v each go through their own depthwise conv, alpha and beta are
  *    not convolved, there is no bias and no activation after the conv;

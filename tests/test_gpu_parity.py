@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from linear_attention_sequence_modality_amd import kda
-from linear_attention_sequence_modality_amd.inputs import CONFIGS, StreamConfig, make_inputs
+from linear_attention_sequence_modality_amd.inputs import WORKLOAD, StreamConfig, make_inputs
 
 from gpu_common import (TOL, desc_of, heads_slice, oracle_conv_heads, oracle_end_to_end_heads,
                         rel, run_path, say, to_dev)
@@ -20,7 +20,7 @@ from gpu_common import (TOL, desc_of, heads_slice, oracle_conv_heads, oracle_end
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
-SAMPLED_HEADS = {2: (0, 9), 3: (4, 15), 4: (7, 12)}
+SAMPLED_HEADS = {"video_5s_480x832": (0, 9), "image_4096px": (4, 15), "video_30s_480x832": (7, 12)}
 
 
 def _check_stream(cfg, inp, heads=None, S0=None, want_state=False):
@@ -58,21 +58,21 @@ def _check_kda_stage(cfg, inp, heads=None):
 # ---- the five stream workloads -------------------------------------------------
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("idx", [0, 1])
-def test_workload_full(idx):
-    cfg = CONFIGS[idx]
+@pytest.mark.parametrize("name", ["tiny_fp32", "proxy_image_1024px"])
+def test_workload_full(name):
+    cfg = WORKLOAD[name]
     inp = make_inputs(cfg)
     _check_stream(cfg, inp)
     _check_kda_stage(cfg, inp)
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("idx", [2, 3, 4])
-def test_workload_sampled_heads(idx):
-    cfg = CONFIGS[idx]
+@pytest.mark.parametrize("name", list(SAMPLED_HEADS))
+def test_workload_sampled_heads(name):
+    cfg = WORKLOAD[name]
     inp = make_inputs(cfg)
-    _check_stream(cfg, inp, heads=SAMPLED_HEADS[idx])
-    _check_kda_stage(cfg, inp, heads=SAMPLED_HEADS[idx][:1])
+    _check_stream(cfg, inp, heads=SAMPLED_HEADS[name])
+    _check_kda_stage(cfg, inp, heads=SAMPLED_HEADS[name][:1])
 
 
 # ---- edge cases (small, compared in full) -----------------------------------------

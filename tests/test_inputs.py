@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from linear_attention_sequence_modality_amd.inputs import (
-    CONFIGS, PATCHIFY, VAE_COMPRESSION, StreamConfig, latent_grid, make_inputs, token_index)
+    WORKLOADS, WORKLOAD, PATCHIFY, VAE_COMPRESSION, StreamConfig, latent_grid, make_inputs, token_index)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "stream_shapes.json")
 
@@ -27,13 +27,13 @@ def test_grid_arithmetic_matches_pages():
 
 
 def test_config_table():
-    assert [c.T for c in CONFIGS] == [512, 4608, 33272, 66048, 189272]
-    assert [c.B * c.T for c in CONFIGS] == [512, 36864, 33272, 66048, 189272]
-    assert CONFIGS[0].dtype == "f32" and all(c.dtype == "bf16" for c in CONFIGS[1:])
+    assert [c.T for c in WORKLOADS] == [512, 4608, 33272, 66048, 189272]
+    assert [c.B * c.T for c in WORKLOADS] == [512, 36864, 33272, 66048, 189272]
+    assert WORKLOAD["tiny_fp32"].dtype == "f32" and all(c.dtype == "bf16" for c in WORKLOADS[1:])
 
 
 def test_raster_order():
-    cfg = CONFIGS[0]
+    cfg = WORKLOAD["tiny_fp32"]
     t, h, w = cfg.grid
     idx = [token_index(cfg, a, b, c) for a in range(t) for b in range(h) for c in range(w)]
     assert idx == list(range(cfg.n_text, cfg.T))
@@ -59,7 +59,7 @@ def test_inputs_are_seeded_and_follow_the_recipe():
 
 
 def test_fp32_config_keeps_fp32():
-    x = make_inputs(CONFIGS[0])
+    x = make_inputs(WORKLOAD["tiny_fp32"])
     assert x["q"].dtype == torch.float32
 
 

@@ -17,7 +17,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from linear_attention_sequence_modality_amd.inputs import CONFIGS, StreamConfig, make_inputs
+from linear_attention_sequence_modality_amd.inputs import WORKLOAD, StreamConfig, make_inputs
 
 
 def _torch_reference(x, wt, wv, n_text, grid, causal_t):
@@ -173,7 +173,7 @@ def test_time_causal_variant_ignores_future_frames():
 
 
 def test_conv_on_config0_inputs_matches_torch():
-    cfg = CONFIGS[0]
+    cfg = WORKLOAD["tiny_fp32"]
     inp = make_inputs(cfg)
     B, T, H, dk = inp["q"].shape
     x = inp["k"].double().numpy().reshape(B, T, H * dk)
