@@ -7,24 +7,27 @@
 // visual 3x3x3 with zero padding; time offset P = 1 (symmetric) or 2 (causal).
 //
 // Design.  A depthwise conv has no channel contraction, so there is no
-// matrix-core work: 27 multiply-adds per output against 2 bytes in and 2 out
-// make the visual conv VALU-bound on fp32 vector units.  So:
-//   * one wave owns one (stream, batch, h row, run of WR w positions, 128
-//     channels) item and marches over t; lane l owns channels 2l, 2l+1.  All
-//     addressing and every boundary test is wave-uniform: loads and stores are
-//     raw buffer operations whose token offset is a scalar register, and a
-//     lane only supplies its constant channel offset;
-//   * each input slice is loaded once (3 rows x (WR+2) positions, one dword
-//     per lane = 256 contiguous bytes per wave per token) and feeds the three
-//     output slices t-1, t, t+1 from a 3-deep accumulator ring whose slot
-//     index is static after unrolling the march by 3;
-//   * bf16: the loaded dword (channel pair c, c+1 of one token) goes
-//     unconverted into v_dot2_f32_bf16 against the weight pairs (w_c, 0) and
-//     (0, w_c+1): one exact product and fp32 accumulation per instruction, no
-//     bf16 -> fp32 unpacking.  fp32 streams use plain fma;
-//   * blocks are remapped so each XCD works on a contiguous range of rows,
-//     keeping the h-1/h/h+1 halo rows in that XCD's L2;
-//   * text tokens form a separate block range: a wave slides the 4-tap causal
+// matrix-core work: 27 multiply-adds per output against 2 bytes in and 2 out.
+//   * A 4-wave workgroup owns a tile of HR = 4 rows x WR = 8 w positions x 128
+//     channels and marches over t.  For every input slice it stages the
+//     (HR+2) x (WR+2) haloed tile in LDS with direct-to-LDS buffer loads of 16
+//     bytes per lane (one instruction moves 4 positions of 256 bytes), double
+//     buffered: the loads of slice t+1 fly while slice t is computed.  Each
+//     input element thus crosses the vector-memory path 1.9 times instead of
+//     3.75 times for per-wave halos, with a quarter of the instructions.
+//   * Wave w computes row h0 + w; lane l owns channels 2l, 2l+1.  It reads its
+//     3 x (WR+2) window of the slice from LDS (one dword per position) and
+//     applies it to the three output slices t-1, t, t+1 held in a 3-deep
+//     register ring whose slot index is static after unrolling the march.
+//   * bf16: taps are paired so that one v_dot2_f32_bf16 does two useful
+//     multiply-adds: byte permutes form (x[w], x[w+1]) per channel for the
+//     w-taps 0 and 1 of each row, and (x[row0], x[row1]) for w-tap 2 of rows 0
+//     and 1; only w-tap 2 of row 2 uses a zero-padded weight pair.  fp32 streams
+//     use plain fma.
+//   * Blocks run channel block by channel block, row group by row group, and
+//     are remapped so each XCD works on a contiguous range of them: the halo
+//     rows of neighbouring row groups are read by co-resident blocks.
+//   * Text tokens form a separate block range: a wave slides the 4-tap causal
 //     window over TR consecutive text tokens.
 #include "common.h"
 #include "launch.h"
@@ -32,47 +35,83 @@
 namespace kdaconv {
 namespace {
 
-constexpr int WR = 8;     // w positions per wave item
+constexpr int WR = 8;     // w positions per wave (and per workgroup)
+constexpr int HR = 4;     // rows per workgroup (one per wave)
 constexpr int TR = 16;    // text tokens per wave item
 constexpr int NT = 256;   // threads per block (4 waves)
 constexpr int LANES = 64;
-constexpr int CPW = 2 * LANES;   // channels per wave item
+constexpr int CPW = 2 * LANES;          // channels per workgroup
+constexpr int TC = WR + 2;              // tile columns (w halo)
+constexpr int TP = (HR + 2) * TC;       // tile positions per slice
 
 // Fourth descriptor word of a raw (untyped, stride 0) buffer resource on gfx9.
 constexpr int kBufferWord3 = 0x00020000;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 template <typename T> struct Ops;
 
 template <> struct Ops<bf16_t> {
-    typedef uint32_t XT;   // raw channel pair of one token
+    typedef uint32_t XT;   // raw channel pair (c, c+1) of one token
+    // taps of channels c (index 0) and c+1 (index 1), as bf16 pairs:
+    //   pr[a][dh][ch] = (w[a][dh][0], w[a][dh][1])
+    //   p2[a][ch]     = (w[a][0][2],  w[a][1][2])
+    //   s2[a][ch]     = w[a][2][2] in channel ch's half of the pair, 0 in the other
     struct Taps {
-        uint32_t w[27][2];   // (w_c, 0) and (0, w_c+1) as bf16 pairs
+        uint32_t pr[3][3][2], p2[3][2], s2[3][2];
     };
     __device__ __forceinline__ static void load_taps(Taps &tp, const bf16_t *wv, int c0, bool ok) {
         const uint16_t *p = reinterpret_cast<const uint16_t *>(wv);
+        auto w = [&](int ch, int a, int dh, int e) -> uint32_t {
+            return ok ? (uint32_t)p[(size_t)(c0 + ch) * 27 + (a * 3 + dh) * 3 + e] : 0u;
+        };
 #pragma unroll
-        for (int tap = 0; tap < 27; ++tap) {
-            tp.w[tap][0] = ok ? (uint32_t)p[(size_t)c0 * 27 + tap] : 0u;
-            tp.w[tap][1] = ok ? (uint32_t)p[(size_t)(c0 + 1) * 27 + tap] << 16 : 0u;
-        }
+        for (int a = 0; a < 3; ++a)
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+#pragma unroll
+                for (int dh = 0; dh < 3; ++dh) tp.pr[a][dh][ch] = w(ch, a, dh, 0) | w(ch, a, dh, 1) << 16;
+                tp.p2[a][ch] = w(ch, a, 0, 2) | w(ch, a, 1, 2) << 16;
+                tp.s2[a][ch] = ch == 0 ? w(0, a, 2, 2) : w(1, a, 2, 2) << 16;
+            }
     }
-    __device__ __forceinline__ static XT load(const char *p) { return *reinterpret_cast<const uint32_t *>(p); }
-    __device__ __forceinline__ static XT bload(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    __device__ __forceinline__ static XT lds_read(const char *p) { return *reinterpret_cast<const uint32_t *>(p); }
+    __device__ __forceinline__ static XT zero() { return 0u; }
+    __device__ __forceinline__ static float dot2(uint32_t x, uint32_t w, float acc) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), __builtin_bit_cast(bf16x2_t, w), acc,
+                                               false);
+    }
+    // Apply one input slice (rows dh = 0..2 of this wave's window) to the
+    // accumulators of output position j: acc[a] receives tap slice a.
+    __device__ __forceinline__ static void apply(const Taps &tp, const XT (&x)[3][TC], int j, float *acc0[3],
+                                                 float *acc1[3]) {
+#pragma unroll
+        for (int dh = 0; dh < 3; ++dh) {
+            const uint32_t plo = __builtin_amdgcn_perm(x[dh][j + 1], x[dh][j], 0x05040100u);
+            const uint32_t phi = __builtin_amdgcn_perm(x[dh][j + 1], x[dh][j], 0x07060302u);
+#pragma unroll
+            for (int a = 0; a < 3; ++a) {
+                *acc0[a] = dot2(plo, tp.pr[a][dh][0], *acc0[a]);
+                *acc1[a] = dot2(phi, tp.pr[a][dh][1], *acc1[a]);
+            }
+        }
+        const uint32_t qlo = __builtin_amdgcn_perm(x[1][j + 2], x[0][j + 2], 0x05040100u);
+        const uint32_t qhi = __builtin_amdgcn_perm(x[1][j + 2], x[0][j + 2], 0x07060302u);
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            *acc0[a] = dot2(qlo, tp.p2[a][0], *acc0[a]);
+            *acc1[a] = dot2(qhi, tp.p2[a][1], *acc1[a]);
+            *acc0[a] = dot2(x[2][j + 2], tp.s2[a][0], *acc0[a]);
+            *acc1[a] = dot2(x[2][j + 2], tp.s2[a][1], *acc1[a]);
+        }
     }
     __device__ __forceinline__ static void bstore(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
                                                   float a, float b) {
         __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a, b), r, voff, soff, 0);
     }
-    __device__ __forceinline__ static XT zero() { return 0u; }
-    __device__ __forceinline__ static void mac(const Taps &tp, int tap, XT x, float &a0, float &a1) {
-        a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x),
-                                             __builtin_bit_cast(bf16x2_t, tp.w[tap][0]), a0, false);
-        a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x),
-                                             __builtin_bit_cast(bf16x2_t, tp.w[tap][1]), a1, false);
-    }
+    __device__ __forceinline__ static XT load(const char *p) { return *reinterpret_cast<const uint32_t *>(p); }
     __device__ __forceinline__ static void store(char *p, float a, float b) {
         *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(a, b);
     }
@@ -93,12 +132,22 @@ template <> struct Ops<float> {
             tp.w[tap][1] = ok ? wv[(size_t)(c0 + 1) * 27 + tap] : 0.f;
         }
     }
-    __device__ __forceinline__ static XT load(const char *p) { return *reinterpret_cast<const float2 *>(p); }
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    __device__ __forceinline__ static XT bload(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-        const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-        return make_float2(__uint_as_float(u.x), __uint_as_float(u.y));
+    __device__ __forceinline__ static XT lds_read(const char *p) { return *reinterpret_cast<const float2 *>(p); }
+    __device__ __forceinline__ static XT zero() { return make_float2(0.f, 0.f); }
+    __device__ __forceinline__ static void apply(const Taps &tp, const XT (&x)[3][TC], int j, float *acc0[3],
+                                                 float *acc1[3]) {
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+#pragma unroll
+            for (int dh = 0; dh < 3; ++dh)
+#pragma unroll
+                for (int e = 0; e < 3; ++e) {
+                    const int tap = (a * 3 + dh) * 3 + e;
+                    *acc0[a] = __builtin_fmaf(tp.w[tap][0], x[dh][j + e].x, *acc0[a]);
+                    *acc1[a] = __builtin_fmaf(tp.w[tap][1], x[dh][j + e].y, *acc1[a]);
+                }
     }
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     __device__ __forceinline__ static void bstore(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
                                                   float a, float b) {
         u32x2 u;
@@ -106,11 +155,7 @@ template <> struct Ops<float> {
         u.y = __float_as_uint(b);
         __builtin_amdgcn_raw_buffer_store_b64(u, r, voff, soff, 0);
     }
-    __device__ __forceinline__ static XT zero() { return make_float2(0.f, 0.f); }
-    __device__ __forceinline__ static void mac(const Taps &tp, int tap, XT x, float &a0, float &a1) {
-        a0 = __builtin_fmaf(tp.w[tap][0], x.x, a0);
-        a1 = __builtin_fmaf(tp.w[tap][1], x.y, a1);
-    }
+    __device__ __forceinline__ static XT load(const char *p) { return *reinterpret_cast<const float2 *>(p); }
     __device__ __forceinline__ static void store(char *p, float a, float b) {
         *reinterpret_cast<float2 *>(p) = make_float2(a, b);
     }
@@ -121,151 +166,187 @@ template <> struct Ops<float> {
 
 struct Layout {
     int n_cb[3];          // 128-channel blocks per stream
-    int vis_items[3];     // B * gh * n_wrun * n_cb   (one per wave)
-    int txt_items[3];     // B * n_trun * n_cb
-    int vis_blocks[3], txt_blocks[3];
-    int n_wrun, n_trun;
+    int vis_blocks[3];    // B * n_cb * n_hg * n_wrun   (one per workgroup)
+    int txt_items[3];     // B * n_trun * n_cb          (one per wave)
+    int txt_blocks[3];
+    int n_wrun, n_hg, n_trun;
     int nblocks;
 };
 
-// Visual wave item.  Everything except the lane's channel offset is uniform.
+// One workgroup: (stream, batch, 128 channels, rows h0..h0+HR-1, w0..w0+WR-1), all t.
 template <typename T, int PT>
-struct VisualWave {
+struct VisualTile {
     typedef Ops<T> O;
-    __amdgpu_buffer_rsrc_t rx, ry;   // this batch's slice of the input / output stream
-    int rowb;            // bytes per token row (C * sizeof(T))
-    int lane_off;        // lane's channel-pair offset (bytes); the only per-lane address term
-    int n_text, gt, gh, gw, h, w0;
+    static constexpr int POS = CPW * (int)sizeof(T);      // bytes of one tile position
+    static constexpr int LPP = POS / 16;                  // lanes per position in a 16-byte load
+    static constexpr int PPI = LANES / LPP;               // positions per load instruction
+    static constexpr int NI = TP / PPI;                   // load instructions per slice
+    static constexpr int NIW = (NI + 3) / 4;              // per wave (at most)
+    static_assert(TP % PPI == 0, "tile must split into whole load instructions");
+    static constexpr int SLICE = TP * POS;                // LDS bytes per slice buffer
+
+    __amdgpu_buffer_rsrc_t rx, ry;
+    char *lds;            // two slice buffers
+    int wave, lane;
+    int rowb, gt, gh, gw, h0, w0, h;
+    unsigned slice_bytes;  // one t-slice of the grid in the stream
+    unsigned dma_off[NIW]; // lane's byte offset (t = 0) for each of its load instructions
+    unsigned out_off;      // lane's byte offset (t = 0) of output position 0 of its row
     typename O::Taps taps;
     float acc[3][WR][2];
+    typename O::XT x[3][TC];
 
-    // byte offset of token (t, hh, ww) inside the batch slice (< 4 GiB, checked on the host)
-    __device__ __forceinline__ unsigned tok_off(int t, int hh, int ww) const {
-        return (unsigned)(n_text + (t * gh + hh) * gw + ww) * (unsigned)rowb;
-    }
-
-    typename O::XT xs[2][3][WR + 2];   // double-buffered input slice (3 rows x WR+2 positions)
-
-    // Load input slice ti (rows h-1..h+1) into buffer B; rows and positions
-    // outside the grid are zero.  Every condition is wave-uniform.
-    template <int B, bool EDGE>
-    __device__ __forceinline__ void load_slice(int ti) {
-        if (ti >= gt) return;
+    __device__ __forceinline__ void issue_slice(int ti) {
+        char *buf = lds + (ti & 1) * SLICE;
+        const unsigned soff = (unsigned)ti * slice_bytes;
 #pragma unroll
-        for (int dh = 0; dh < 3; ++dh) {
-            const int hh = h + dh - 1;
-            if (hh < 0 || hh >= gh) continue;
-            const unsigned row = tok_off(ti, hh, w0) - (unsigned)rowb;   // position w0 - 1
-#pragma unroll
-            for (int j = 0; j < WR + 2; ++j) {
-                const unsigned soff = row + (unsigned)j * (unsigned)rowb;
-                if (EDGE) {
-                    const int ww = w0 - 1 + j;
-                    xs[B][dh][j] = (ww >= 0 && ww < gw) ? O::bload(rx, lane_off, soff) : O::zero();
-                } else {
-                    xs[B][dh][j] = O::bload(rx, lane_off, soff);
-                }
-            }
+        for (int i = 0; i < NIW; ++i) {
+            const int k = wave + 4 * i;
+            if (k < NI)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(buf + k * 1024), 16, dma_off[i], soff, 0,
+                                                         0);
         }
-    }
-
-    // Step P of the march (slice ti = 6m + P): prefetch slice ti + 1, then apply
-    // slice ti.  Input slice ti contributes tap a to output slice ti + PT - a,
-    // kept in accumulator slot (ti + PT - a) mod 3 == (P + PT - a) mod 3.
-    template <int P, bool EDGE>
-    __device__ __forceinline__ void step(int ti) {
-        constexpr int CUR = P & 1;
-        load_slice<CUR ^ 1, EDGE>(ti + 1);
-        if (ti < gt) {
-#pragma unroll
-            for (int dh = 0; dh < 3; ++dh) {
-                const int hh = h + dh - 1;
-                if (hh < 0 || hh >= gh) continue;
-#pragma unroll
-                for (int a = 0; a < 3; ++a) {
-                    const int slot = ((P + PT - a) % 3 + 3) % 3;
-#pragma unroll
-                    for (int e = 0; e < 3; ++e)
-#pragma unroll
-                        for (int j = 0; j < WR; ++j)
-                            O::mac(taps, (a * 3 + dh) * 3 + e, xs[CUR][dh][j + e], acc[slot][j][0], acc[slot][j][1]);
-                }
-            }
-        }
-        constexpr int done = ((P + PT - 2) % 3 + 3) % 3;   // slot of output slice ti + PT - 2
-        const int t_done = ti + PT - 2;
-        if (t_done >= 0 && t_done < gt) {
-            const unsigned orow = tok_off(t_done, h, w0);
-#pragma unroll
-            for (int j = 0; j < WR; ++j)
-                if (!EDGE || w0 + j < gw)
-                    O::bstore(ry, lane_off, orow + (unsigned)j * (unsigned)rowb, acc[done][j][0], acc[done][j][1]);
-        }
-#pragma unroll
-        for (int j = 0; j < WR; ++j) acc[done][j][0] = acc[done][j][1] = 0.f;
     }
 
     template <bool EDGE>
-    __device__ void march() {
-        load_slice<0, EDGE>(0);
-        // One extra empty slice (ti == gt) flushes the last output slice.
-#pragma unroll 1
-        for (int ti = 0; ti <= gt; ti += 6) {
-            step<0, EDGE>(ti);
-            if (ti + 1 > gt) break;
-            step<1, EDGE>(ti + 1);
-            if (ti + 2 > gt) break;
-            step<2, EDGE>(ti + 2);
-            if (ti + 3 > gt) break;
-            step<3, EDGE>(ti + 3);
-            if (ti + 4 > gt) break;
-            step<4, EDGE>(ti + 4);
-            if (ti + 5 > gt) break;
-            step<5, EDGE>(ti + 5);
+    __device__ __forceinline__ void read_window(int ti) {
+        const char *buf = lds + (ti & 1) * SLICE + lane * (int)(POS / LANES);
+#pragma unroll
+        for (int dh = 0; dh < 3; ++dh) {
+            const int hh = h + dh - 1;
+#pragma unroll
+            for (int jj = 0; jj < TC; ++jj) {
+                const int ww = w0 - 1 + jj;
+                const bool in = !EDGE || (hh >= 0 && hh < gh && ww >= 0 && ww < gw);
+                x[dh][jj] = in ? O::lds_read(buf + ((wave + dh) * TC + jj) * POS) : O::zero();
+            }
         }
     }
 
-    __device__ void run() {
+    template <int P, bool EDGE>
+    __device__ __forceinline__ void flush(int t_done, bool active) {
+        constexpr int slot = ((P + PT) % 3 + 3) % 3;   // slot of output slice ti + PT - 3
+        if (active && t_done >= 0 && t_done < gt) {
+            const unsigned soff = (unsigned)t_done * slice_bytes;
 #pragma unroll
-        for (int s = 0; s < 3; ++s)
+            for (int j = 0; j < WR; ++j)
+                if (!EDGE || w0 + j < gw)
+                    O::bstore(ry, out_off + (unsigned)(j * rowb), soff, acc[slot][j][0], acc[slot][j][1]);
+        }
 #pragma unroll
-            for (int j = 0; j < WR; ++j) acc[s][j][0] = acc[s][j][1] = 0.f;
-        if (w0 >= 1 && w0 + WR < gw)
-            march<false>();
-        else
-            march<true>();
+        for (int j = 0; j < WR; ++j) acc[slot][j][0] = acc[slot][j][1] = 0.f;
+    }
+
+    // Step P of the march (ti = 6m + P).  Input slice ti contributes tap
+    // slice a to output slice ti + PT - a, kept in ring slot (P + PT - a) mod 3.
+    template <int P, bool EDGE>
+    __device__ __forceinline__ void step(int ti, bool active) {
+        if (ti < gt) {
+            // Slice ti has landed once every wave's direct-to-LDS loads of it
+            // have retired: wait for them explicitly (the compiler does not
+            // track them across the loop back-edge), then meet at the barrier,
+            // which also ends every read of slice ti-1.
+            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+            __syncthreads();
+            read_window<EDGE>(ti);
+            if (ti + 1 < gt) issue_slice(ti + 1);
+        }
+        flush<P, EDGE>(ti + PT - 3, active);
+        if (ti < gt && active) {
+            float *a0[3], *a1[3];
+#pragma unroll
+            for (int j = 0; j < WR; ++j) {
+#pragma unroll
+                for (int a = 0; a < 3; ++a) {
+                    constexpr int base = P + PT;
+                    const int slot = ((base - a) % 3 + 3) % 3;
+                    a0[a] = &acc[slot][j][0];
+                    a1[a] = &acc[slot][j][1];
+                }
+                O::apply(taps, x, j, a0, a1);
+            }
+        }
+    }
+
+    template <bool EDGE>
+    __device__ void march(bool active) {
+        issue_slice(0);
+        // empty steps past the last slice flush the last output slices
+        const int last = gt + 2 - PT;
+#pragma unroll 1
+        for (int ti = 0; ti <= last; ti += 6) {
+            step<0, EDGE>(ti, active);
+            if (ti + 1 > last) break;
+            step<1, EDGE>(ti + 1, active);
+            if (ti + 2 > last) break;
+            step<2, EDGE>(ti + 2, active);
+            if (ti + 3 > last) break;
+            step<3, EDGE>(ti + 3, active);
+            if (ti + 4 > last) break;
+            step<4, EDGE>(ti + 4, active);
+            if (ti + 5 > last) break;
+            step<5, EDGE>(ti + 5, active);
+        }
     }
 };
 
 template <typename T, int PT>
-__device__ void visual_item(const ConvArgs &a, const Layout &L, int s, int item, int lane) {
-    const int n_cb = L.n_cb[s];
-    const int cb = item % n_cb;
-    int rest = item / n_cb;
-    const int wrun = rest % L.n_wrun;
-    rest /= L.n_wrun;
-    const int h = rest % a.gh;
-    const int b = rest / a.gh;
+__device__ void visual_block(const ConvArgs &a, const Layout &L, int s, int blk, int wave, int lane, char *lds) {
+    typedef VisualTile<T, PT> V;
+    // channel block outermost, then row groups, then w-runs
+    const int wrun = blk % L.n_wrun;
+    int rest = blk / L.n_wrun;
+    const int hg = rest % L.n_hg;
+    rest /= L.n_hg;
+    const int cb = rest % L.n_cb[s];
+    const int b = rest / L.n_cb[s];
     const int C = a.C[s];
     const int c0 = cb * CPW + 2 * lane;
     const bool ok = c0 < C;   // lanes past the last channel compute zeros and store nothing
-    VisualWave<T, PT> wv;
-    wv.rowb = C * (int)sizeof(T);
-    const size_t bbytes = (size_t)a.T * wv.rowb;   // < 4 GiB, checked on the host
-    wv.rx = __builtin_amdgcn_make_buffer_rsrc(
+
+    V v;
+    v.wave = wave;
+    v.lane = lane;
+    v.lds = lds;
+    v.rowb = C * (int)sizeof(T);
+    v.gt = a.gt;
+    v.gh = a.gh;
+    v.gw = a.gw;
+    v.h0 = hg * HR;
+    v.w0 = wrun * WR;
+    v.h = v.h0 + wave;
+    v.slice_bytes = (unsigned)(a.gh * a.gw) * (unsigned)v.rowb;
+    const size_t bbytes = (size_t)a.T * v.rowb;   // < 4 GiB, checked on the host
+    v.rx = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(static_cast<const char *>(a.x[s])) + (size_t)b * bbytes, 0, (int)(unsigned)bbytes,
         kBufferWord3);
-    wv.ry = __builtin_amdgcn_make_buffer_rsrc(static_cast<char *>(a.y[s]) + (size_t)b * bbytes, 0,
-                                              (int)(unsigned)bbytes, kBufferWord3);
-    wv.lane_off = (ok ? c0 : 0) * (int)sizeof(T);
-    wv.n_text = a.n_text;
-    wv.gt = a.gt;
-    wv.gh = a.gh;
-    wv.gw = a.gw;
-    wv.h = h;
-    wv.w0 = wrun * WR;
-    Ops<T>::load_taps(wv.taps, static_cast<const T *>(a.wv[s]), ok ? c0 : 0, ok);
-    if (ok) wv.run();
+    v.ry = __builtin_amdgcn_make_buffer_rsrc(static_cast<char *>(a.y[s]) + (size_t)b * bbytes, 0,
+                                             (int)(unsigned)bbytes, kBufferWord3);
+    // tile position p of load instruction k: k * PPI + lane / LPP; positions
+    // outside the grid load a clamped in-grid token that is never read
+    const unsigned chan = (unsigned)(cb * V::POS) + (unsigned)(lane % V::LPP) * 16u;
+#pragma unroll
+    for (int i = 0; i < V::NIW; ++i) {
+        const int k = wave + 4 * i;
+        const int p = k * V::PPI + lane / V::LPP;
+        const int hh = min(max(v.h0 - 1 + p / TC, 0), a.gh - 1);
+        const int ww = min(max(v.w0 - 1 + p % TC, 0), a.gw - 1);
+        v.dma_off[i] = (unsigned)(a.n_text + hh * a.gw + ww) * (unsigned)v.rowb + chan;
+    }
+    v.out_off = (unsigned)(a.n_text + min(v.h, a.gh - 1) * a.gw + v.w0) * (unsigned)v.rowb +
+                (unsigned)((ok ? c0 : 0) * (int)sizeof(T));
+    Ops<T>::load_taps(v.taps, static_cast<const T *>(a.wv[s]), ok ? c0 : 0, ok);
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int j = 0; j < WR; ++j) v.acc[r][j][0] = v.acc[r][j][1] = 0.f;
+    // every wave takes part in the loads and barriers; rows past the grid and
+    // lanes past the last channel compute nothing and store nothing
+    const bool active = ok && v.h < a.gh;
+    if (v.h0 >= 1 && v.h0 + HR < a.gh && v.w0 >= 1 && v.w0 + WR < a.gw)
+        v.template march<false>(active);
+    else
+        v.template march<true>(active);
 }
 
 template <typename T>
@@ -318,15 +399,15 @@ __device__ void text_item(const ConvArgs &a, const Layout &L, int s, int item, i
 }
 
 template <typename T, int PT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 2 : 3))) void conv_kernel(ConvArgs a, Layout L) {
+__global__ __launch_bounds__(NT) void conv_kernel(ConvArgs a, Layout L) {
+    __shared__ __attribute__((aligned(1024))) char lds[2 * VisualTile<T, PT>::SLICE];
     int blk = xcd_remap(blockIdx.x, L.nblocks);
     const int wave = uniform(threadIdx.x / LANES), lane = threadIdx.x % LANES;
     constexpr int WPB = NT / LANES;
 #pragma unroll 1
     for (int s = 0; s < 3; ++s) {
         if (blk < L.vis_blocks[s]) {
-            const int item = uniform(blk * WPB + wave);
-            if (item < L.vis_items[s]) visual_item<T, PT>(a, L, s, item, lane);
+            visual_block<T, PT>(a, L, s, blk, wave, lane, lds);
             return;
         }
         blk -= L.vis_blocks[s];
@@ -345,14 +426,14 @@ hipError_t launch_conv(const ConvArgs &a, bool bf16, hipStream_t stream) {
     constexpr int WPB = NT / LANES;
     Layout L;
     L.n_wrun = (a.gw + WR - 1) / WR;
+    L.n_hg = (a.gh + HR - 1) / HR;
     L.n_trun = (a.n_text + TR - 1) / TR;
     const int n_vis = a.gt * a.gh * a.gw;
     L.nblocks = 0;
     for (int s = 0; s < 3; ++s) {
         L.n_cb[s] = (a.C[s] + CPW - 1) / CPW;
-        L.vis_items[s] = n_vis ? a.B * a.gh * L.n_wrun * L.n_cb[s] : 0;
+        L.vis_blocks[s] = n_vis ? a.B * L.n_cb[s] * L.n_hg * L.n_wrun : 0;
         L.txt_items[s] = a.B * L.n_trun * L.n_cb[s];
-        L.vis_blocks[s] = (L.vis_items[s] + WPB - 1) / WPB;
         L.txt_blocks[s] = (L.txt_items[s] + WPB - 1) / WPB;
         L.nblocks += L.vis_blocks[s] + L.txt_blocks[s];
     }

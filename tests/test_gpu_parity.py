@@ -173,6 +173,34 @@ def test_deterministic_and_every_output_written():
         assert torch.equal(a, b)
 
 
+@pytest.mark.timeout(300)
+def test_conv_repeatable_with_the_chip_full():
+    """The conv's tile pipeline at a size that keeps several blocks resident per CU
+    for many t-steps (a multi-frame 30 x 52 grid, 16 heads of 128): two runs into
+    poisoned outputs agree bit for bit, and sampled heads match the oracle."""
+    cfg = WORKLOAD["video_5s_480x832"].with_(name="video_8f", grid=(8, 30, 52))
+    inp = make_inputs(cfg)
+    dev = to_dev(inp)
+    d = desc_of(cfg)
+    say("case %s T=%d H=%d" % (cfg.name, cfg.T, cfg.H))
+    runs = []
+    for poison in (float("nan"), -3.0):
+        outs = [torch.full_like(dev[x], poison) for x in ("q", "k", "v")]
+        kda.kda_conv_forward(d, dev["q"], dev["k"], dev["v"],
+                             (dev["w_text_q"], dev["w_text_k"], dev["w_text_v"]),
+                             (dev["w_vis_q"], dev["w_vis_k"], dev["w_vis_v"]), *outs)
+        torch.cuda.synchronize()
+        runs.append(outs)
+    for a, b in zip(*runs):
+        assert torch.isfinite(a.float()).all()
+        assert torch.equal(a, b)
+    heads = (3, 14)
+    for name, got in zip(("q", "k", "v"), runs[0]):
+        e = rel(heads_slice(got, heads), oracle_conv_heads(cfg, inp, name, heads))
+        say("  %s rel err %.2e" % (name, e))
+        assert e <= TOL[cfg.dtype]
+
+
 @pytest.mark.timeout(120)
 def test_no_writes_outside_outputs():
     cfg = _small("guard", n_text=9, grid=(2, 5, 6), dk=64, dv=128)
