@@ -37,6 +37,18 @@ template <> struct ElemIO<bf16_t> {
     __device__ __forceinline__ static void store(bf16_t *p, float x) { *p = (bf16_t)x; }
 };
 
+// ---- barriers -----------------------------------------------------------------
+// Workgroup barrier ordering LDS only.  __syncthreads() also drains this wave's
+// outstanding global loads and stores (on gfx9 they share one counter), which
+// would throw away any prefetch in flight; phases that hand data over through
+// LDS only need this wave's LDS operations complete before the meeting point.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vector memory left in flight
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---- XCD-aware block remap --------------------------------------------------
 // Workgroups are dealt round-robin over the 8 XCDs (each with its own L2).
 // Remap the hardware block id so that every XCD receives a contiguous range

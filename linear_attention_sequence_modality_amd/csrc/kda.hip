@@ -145,6 +145,13 @@ struct K1Smem {
 
 __device__ __forceinline__ int fp_index(int R, int S) { return R * (R - 1) / 2 + S; }
 
+// Hardware base-2 exponent and logarithm (v_exp_f32, v_log_f32, about 1 ulp).
+// Results below the smallest normal flush to zero, which only affects decay
+// factors far below any term they are added to; alpha is a positive normal
+// number or exactly 1 (log2 = 0).
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+
 // 16x16x16 fp32 product X*Y with X, Y row-major in LDS; lane holds rows 4g+i of column col.
 __device__ __forceinline__ f32x4_t mm16(const float *X, int ldx, const float *Y, int ldy, int col,
                                         int g, f32x4_t acc) {
@@ -158,7 +165,7 @@ __device__ __forceinline__ f32x4_t mm16(const float *X, int ldx, const float *Y,
 template <typename T>
 struct Prefetch {
     Raw8<T> a[2], k[2], q[2], v[2];
-    float beta;
+    T beta;   // raw: converted where it is used, so the load is not waited for at issue
 };
 
 template <typename T, int DK, int DV>
@@ -206,31 +213,32 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
         const int bh = item / nchunks, n = item % nchunks;
         const int b = bh / a.H, h = bh % a.H;
         const int t0 = n * C, nr = min(C, a.T - t0);
+        // Rows past the end of the stream re-read the last row (in bounds) and
+        // are masked where they are used: the loads never depend on the data
+        // and no register is cleared behind a store still in flight.
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int r = 2 * krp + e;
-            if (key_task && r < nr) {
+            if (key_task) {
+                const int r = min(2 * krp + e, nr - 1);
                 const size_t off = (((size_t)b * a.T + (t0 + r)) * a.H + h) * DK + kc0;
                 pf.a[e].load(ga + off);
                 pf.k[e].load(gk + off);
                 pf.q[e].load(gq + off);
-            } else {
-                pf.a[e].zero();
-                pf.k[e].zero();
-                pf.q[e].zero();
             }
-            const int rv = 2 * vrp + e;
-            if (val_task && rv < nr)
+            if (val_task) {
+                const int rv = min(2 * vrp + e, nr - 1);
                 pf.v[e].load(gv + (((size_t)b * a.T + (t0 + rv)) * a.H + h) * DV + vc0);
-            else
-                pf.v[e].zero();
+            }
         }
-        pf.beta = (tid < C && tid < nr) ? ElemIO<T>::load(gb + ((size_t)b * a.T + (t0 + tid)) * a.H + h) : 0.f;
+        if (tid < C) pf.beta = gb[((size_t)b * a.T + (t0 + min(tid, nr - 1))) * a.H + h];
     };
 
     Prefetch<T> pf;
     int item = blockIdx.x;
     if (item < n_items) load_inputs(item, pf);
+    // Enter the loop with the first prefetch retired, as every later iteration
+    // is (see P5): the loop's waits then never cover the stores still in flight.
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
 
 #pragma unroll 1
     for (; item < n_items; item += gridDim.x) {
@@ -248,48 +256,47 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
                 float al[8];
                 pf.a[e].get(al);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) al[i] = r < nr ? log2f(al[i]) : 0.f;
+                for (int i = 0; i < 8; ++i) al[i] = r < nr ? hw_log2(al[i]) : 0.f;
                 *reinterpret_cast<float4 *>(Gs + r * SM::GS + kc0) = make_float4(al[0], al[1], al[2], al[3]);
                 *reinterpret_cast<float4 *>(Gs + r * SM::GS + kc0 + 4) = make_float4(al[4], al[5], al[6], al[7]);
             }
         }
-        if (tid < C) Bt[tid] = pf.beta;
-        __syncthreads();
+        if (tid < C) Bt[tid] = tid < nr ? (float)pf.beta : 0.f;
+        lds_barrier();
         {
-            // column scan in NPART partitions of RPP rows; Gs keeps the partition-local
-            // prefix sums, Tot the partition totals (G = local + sum of earlier totals)
+            // column scan: thread (partition, channel) sums its RPP rows in
+            // registers, then adds the totals of the earlier partitions
             const int c = tid % DK, part = tid / DK;
-            float run = 0.f;
+            float gl[SM::RPP];
 #pragma unroll
-            for (int i = 0; i < SM::RPP; ++i) {
-                const int r = part * SM::RPP + i;
-                run += Gs[r * SM::GS + c];
-                Gs[r * SM::GS + c] = run;
-            }
-            Tot[part * DK + c] = run;
-            __syncthreads();
-            auto Gat = [&](int r) {   // final G at row r, channel c
-                float v = Gs[r * SM::GS + c];
-                for (int p = 0; p < r / SM::RPP; ++p) v += Tot[p * DK + c];
-                return v;
-            };
+            for (int i = 0; i < SM::RPP; ++i) gl[i] = Gs[(part * SM::RPP + i) * SM::GS + c];
+#pragma unroll
+            for (int i = 1; i < SM::RPP; ++i) gl[i] += gl[i - 1];
+            Tot[part * DK + c] = gl[SM::RPP - 1];
+            lds_barrier();
+            float off = 0.f;
+            for (int p = 0; p < part; ++p) off += Tot[p * DK + c];
+#pragma unroll
+            for (int i = 0; i < SM::RPP; ++i) Gs[(part * SM::RPP + i) * SM::GS + c] = gl[i] + off;
+            lds_barrier();
+            auto Gat = [&](int r) { return Gs[r * SM::GS + c]; };
             // 15 per-channel factors: Pm[4], Kh[4], Fp[6], Gam
             for (int e = part; e < 15; e += SM::NPART) {
                 if (e < 4) {
-                    Pm[e * DK + c] = exp2f(Gat(16 * e + 8));
+                    Pm[e * DK + c] = hw_exp2(Gat(16 * e + 8));
                 } else if (e < 8) {
                     const int R = e - 4;
-                    Kh[R * DK + c] = exp2f(Gat(63) - Gat(16 * R + 8));
+                    Kh[R * DK + c] = hw_exp2(Gat(63) - Gat(16 * R + 8));
                 } else if (e < 14) {
                     const int f = e - 8;
                     const int R = f < 1 ? 1 : (f < 3 ? 2 : 3);
                     const int S = f - fp_index(R, 0);
-                    Fp[f * DK + c] = exp2f(Gat(16 * R + 8) - Gat(16 * S + 8));
+                    Fp[f * DK + c] = hw_exp2(Gat(16 * R + 8) - Gat(16 * S + 8));
                 } else {
-                    ws_gam[gam_pos<DK>(c)] = exp2f(Gat(63));
+                    ws_gam[gam_pos<DK>(c)] = hw_exp2(Gat(63));
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
 
         // ---- P1: elementwise operands ----------------------------------------------
@@ -302,6 +309,11 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
                 float kx[8], qx[8], gr[8], gm[8];
                 pf.k[e].get(kx);
                 pf.q[e].get(qx);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {   // rows past the stream end are zero
+                    kx[i] = r < nr ? kx[i] : 0.f;
+                    qx[i] = r < nr ? qx[i] : 0.f;
+                }
                 const float4 g0 = *reinterpret_cast<const float4 *>(Gs + r * SM::GS + kc0);
                 const float4 g1 = *reinterpret_cast<const float4 *>(Gs + r * SM::GS + kc0 + 4);
                 const float4 m0 = *reinterpret_cast<const float4 *>(Gs + m * SM::GS + kc0);
@@ -310,22 +322,13 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
                 gr[4] = g1.x; gr[5] = g1.y; gr[6] = g1.z; gr[7] = g1.w;
                 gm[0] = m0.x; gm[1] = m0.y; gm[2] = m0.z; gm[3] = m0.w;
                 gm[4] = m1.x; gm[5] = m1.y; gm[6] = m1.z; gm[7] = m1.w;
-                // rows r and m lie in partitions r/RPP and m/RPP: add the earlier totals
-                for (int p = 0; p < r / SM::RPP; ++p) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) gr[i] += Tot[p * DK + kc0 + i];
-                }
-                for (int p = 0; p < m / SM::RPP; ++p) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) gm[i] += Tot[p * DK + kc0 + i];
-                }
                 const float br = Bt[r];
                 float kr[8], qr[8], kb[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int c = kc0 + i;
                     const float d = gr[i] - gm[i];
-                    const float e1 = exp2f(d), e2 = exp2f(-d);
+                    const float e1 = hw_exp2(d), e2 = hw_exp2(-d);
                     kr[i] = kx[i] * e1;
                     qr[i] = qx[i] * e1;
                     kb[i] = kx[i] * e2;
@@ -343,13 +346,18 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
             float vx0[8], vx1[8];
             pf.v[0].get(vx0);
             pf.v[1].get(vx1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                vx0[i] = s0 < nr ? vx0[i] : 0.f;
+                vx1[i] = s0 + 1 < nr ? vx1[i] : 0.f;
+            }
             const float b0 = Bt[s0], b1 = Bt[s0 + 1];
 #pragma unroll
             for (int i = 0; i < 8; ++i) st2<T>(RV + vrp * SM::RVS + 2 * (vc0 + i), b0 * vx0[i], b1 * vx1[i]);
         }
         // the prefetch registers are consumed: start loading the next chunk
         if (item + (int)gridDim.x < n_items) load_inputs(item + gridDim.x, pf);
-        __syncthreads();
+        lds_barrier();
 
         // ---- P2: decayed K K^T (-> L) and (Q K^T)^T (-> workspace) on MFMA ----------
         for (int ti = wv; ti < 10; ti += 8) {
@@ -384,7 +392,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
             const float z[4] = {0.f, 0.f, 0.f, 0.f};
             st4<T>(ws + WL::BT + ((size_t)(R * 2 + (S >> 1)) * 64 + l) * 8 + (S & 1) * 4, z);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- P3: Tm = (I + Diag(beta) A)^-1 in fp32 ------------------------------------
         if (wv == 0) {
@@ -443,7 +451,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         // off-diagonal, by distance d = R - S: Tm_RS = -D_R sum_{J=S}^{R-1} L_RJ Tm_JS
         for (int d = 1; d < 4; ++d) {
             float *sc = Scr + wv * 16 * SM::SC;
@@ -456,13 +464,13 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sc[(4 * g + i) * SM::SC + col] = y[i];
             }
-            __syncthreads();
+            lds_barrier();
             if (R < 4) {
                 const f32x4_t t = mm16(Tm32 + (16 * R) * SM::LS + 16 * R, SM::LS, sc, SM::SC, col, g, zero4());
 #pragma unroll
                 for (int i = 0; i < 4; ++i) Tm32[(16 * R + 4 * g + i) * SM::LS + 16 * S + col] = -t[i];
             }
-            __syncthreads();
+            lds_barrier();
         }
         {   // Tm16 <- Tm32
             const int r = tid >> 3, c0 = 8 * (tid & 7);
@@ -471,9 +479,14 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
             for (int i = 0; i < 8; ++i) x[i] = Tm32[r * SM::LS + c0 + i];
             st8f<T>(Tm16 + r * SM::TS + c0, x);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- P5: W^T per 16 key channels, Ut per 16 value columns ------------------
+        // Retire the next chunk's prefetch (issued in P1, long since landed) and
+        // this chunk's earlier stores here, before P5 issues its own: loads and
+        // stores share one counter, so a wait for the prefetch placed after the
+        // P5 stores (at the next P0) would also wait for those fresh stores.
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
         {
             constexpr int NWU = DK / 16, NUU = DV / 16;
             for (int u = wv; u < NWU + NUU; u += 8) {
@@ -510,7 +523,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
                 }
             }
         }
-        __syncthreads();   // LDS is reused by the next chunk
+        lds_barrier();   // LDS is reused by the next chunk
     }
 }
 
@@ -626,20 +639,21 @@ __device__ __forceinline__ void signal_counter(int *ctr, int value) {
 }
 
 constexpr int kRing = 4;              // chunk steps buffered between the waves
+constexpr int kScanSlabs = 1;         // 16-column value slabs per scan workgroup
 constexpr int kPollBudget = 1 << 24;  // LDS polls per wave per launch
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, int NS>
 __global__ __launch_bounds__(192) void kda_state_kernel(KdaArgs a) {
     using WL = Ws<T, DK, DV>;
     using F = Frag<T>;
     using B = BufLd<T>;
-    constexpr int NJT = DV / 16;     // 16-column value slices
-    constexpr int NKS = DK / 32;     // contraction steps over dk
-    constexpr int NDT = DK / 16;     // 16-row state tiles
+    constexpr int NJT = DV / (16 * NS);   // workgroups per head: NS 16-column slabs each
+    constexpr int NKS = DK / 32;          // contraction steps over dk
+    constexpr int NDT = DK / 16;          // 16-row state tiles
     constexpr unsigned ES = sizeof(T);
-    // ring slot: S operands (NKS fragments) then U operands (2 fragments), per lane
-    __shared__ F su_ring[kRing][NKS + 2][64];
-    __shared__ f32x4_t o_ring[kRing][4][64];
+    // ring slot, per lane: S operands (NKS fragments) then U operands (2 fragments), per slab
+    __shared__ F su_ring[kRing][NS][NKS + 2][64];
+    __shared__ f32x4_t o_ring[kRing][NS][4][64];
     __shared__ int ctr[4];   // S/U produced, S/U consumed, O produced, O consumed
     if (threadIdx.x < 4) ctr[threadIdx.x] = 0;
     __syncthreads();
@@ -658,23 +672,28 @@ __global__ __launch_bounds__(192) void kda_state_kernel(KdaArgs a) {
         const_cast<char *>(wsh), 0, (int)(unsigned)((size_t)nchunks * WL::BYTES), kBufWord3);
     const unsigned lane8 = (unsigned)l * 8 * ES;   // lane's fragment inside a [64][8] block
     auto cbase = [&](int n) { return (unsigned)n * (unsigned)WL::BYTES; };
+    auto column = [&](int sl) { return 16 * (NS * jt + sl) + col; };   // value column of slab sl
 
     if (wave == 0) {
         // ---------------- recurrence ----------------
-        f32x4_t S[NDT];
+        f32x4_t S[NS][NDT];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) S[dt] = zero4();
+        for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) S[sl][dt] = zero4();
         if (a.s0) {
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
+            for (int sl = 0; sl < NS; ++sl)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    S[dt][i] = a.s0[((size_t)bh * DK + 16 * dt + 4 * g + i) * DV + 16 * jt + col];
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        S[sl][dt][i] = a.s0[((size_t)bh * DK + 16 * dt + 4 * g + i) * DV + column(sl)];
         }
         F Wf[4][NKS], Kf[NDT][2];
-        Raw8<T> ut[2];   // Ut rows 16R + 4g + i of column col: element 4R + i
-        float2 gam;      // decay of channels 16 dt + 4g + i for dt = col/2, i = 2(col%2) + {0, 1}
-        const unsigned ut_off = (unsigned)(WL::U + (size_t)(jt * 64 + l) * 16) * ES;
+        Raw8<T> ut[NS][2];   // Ut rows 16R + 4g + i of the slab's column: element 4R + i
+        float2 gam;          // decay of channels 16 dt + 4g + i for dt = col/2, i = 2(col%2) + {0, 1}
+        const unsigned ut_off = (unsigned)(WL::U + (size_t)(NS * jt * 64 + l) * 16) * ES;
         const unsigned gam_off = (unsigned)WL::GAM_BYTE + 4u * (unsigned)(g * (DK / 4) + 2 * min(col, DK / 8 - 1));
         auto load_w = [&](int n) {
             const unsigned c = cbase(n);
@@ -686,8 +705,11 @@ __global__ __launch_bounds__(192) void kda_state_kernel(KdaArgs a) {
         };
         auto load_u = [&](int n) {
             const unsigned c = cbase(n);
-            B::raw8(ut[0], wsr, ut_off, c);
-            B::raw8(ut[1], wsr, ut_off, c + 8 * ES);
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl) {
+                B::raw8(ut[sl][0], wsr, ut_off, c + (unsigned)(sl * 64 * 16) * ES);
+                B::raw8(ut[sl][1], wsr, ut_off, c + (unsigned)(sl * 64 * 16 + 8) * ES);
+            }
         };
         auto load_k = [&](int n) {
             const unsigned c = cbase(n);
@@ -710,37 +732,48 @@ __global__ __launch_bounds__(192) void kda_state_kernel(KdaArgs a) {
 #pragma unroll 1
         for (int n = 0; n < nchunks; ++n) {
             const int nx = min(n + 1, last);
-            F(&slot)[NKS + 2][64] = su_ring[n % kRing];
-            F Sb[NKS];
+            F(&slot)[NS][NKS + 2][64] = su_ring[n % kRing];
+            F Sb[NS][NKS];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                Sb[ks] = tiles_to_frag<T>(S[2 * ks], S[2 * ks + 1]);
-                slot[ks][l] = Sb[ks];
-            }
-            // U = Ut - W S  (token rows 16R + 4g + i, value column col)
-            f32x4_t U[4];
+            for (int sl = 0; sl < NS; ++sl)
 #pragma unroll
-            for (int R = 0; R < 4; ++R) U[R] = zero4();
+                for (int ks = 0; ks < NKS; ++ks) {
+                    Sb[sl][ks] = tiles_to_frag<T>(S[sl][2 * ks], S[sl][2 * ks + 1]);
+                    slot[sl][ks][l] = Sb[sl][ks];
+                }
+            // U = Ut - W S  (token rows 16R + 4g + i, value column of each slab)
+            f32x4_t U[NS][4];
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+                for (int R = 0; R < 4; ++R) U[sl][R] = zero4();
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-                for (int R = 0; R < 4; ++R) U[R] = mma(Wf[R][ks], Sb[ks], U[R]);
+                for (int R = 0; R < 4; ++R)
+#pragma unroll
+                    for (int sl = 0; sl < NS; ++sl) U[sl][R] = mma(Wf[R][ks], Sb[sl][ks], U[sl][R]);
             __builtin_amdgcn_sched_barrier(0);
             load_w(nx);
             __builtin_amdgcn_sched_barrier(0);
+            F Ub[NS][2];
 #pragma unroll
-            for (int R = 0; R < 2; ++R) {
-                float x[8];
-                ut[R].get(x);
+            for (int sl = 0; sl < NS; ++sl) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    U[2 * R][i] = x[i] - U[2 * R][i];
-                    U[2 * R + 1][i] = x[4 + i] - U[2 * R + 1][i];
+                for (int R = 0; R < 2; ++R) {
+                    float x[8];
+                    ut[sl][R].get(x);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        U[sl][2 * R][i] = x[i] - U[sl][2 * R][i];
+                        U[sl][2 * R + 1][i] = x[4 + i] - U[sl][2 * R + 1][i];
+                    }
                 }
+                Ub[sl][0] = tiles_to_frag<T>(U[sl][0], U[sl][1]);
+                Ub[sl][1] = tiles_to_frag<T>(U[sl][2], U[sl][3]);
+                slot[sl][NKS][l] = Ub[sl][0];
+                slot[sl][NKS + 1][l] = Ub[sl][1];
             }
-            const F Ub[2] = {tiles_to_frag<T>(U[0], U[1]), tiles_to_frag<T>(U[2], U[3])};
-            slot[NKS][l] = Ub[0];
-            slot[NKS + 1][l] = Ub[1];
             signal_counter(&ctr[0], n + 1);
             __builtin_amdgcn_sched_barrier(0);
             load_u(nx);
@@ -749,11 +782,17 @@ __global__ __launch_bounds__(192) void kda_state_kernel(KdaArgs a) {
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[dt][i] *= row_bcast(i & 1 ? gam.y : gam.x, 2 * dt + (i >> 1));
+                for (int i = 0; i < 4; ++i) {
+                    const float gm = row_bcast(i & 1 ? gam.y : gam.x, 2 * dt + (i >> 1));
+#pragma unroll
+                    for (int sl = 0; sl < NS; ++sl) S[sl][dt][i] *= gm;
+                }
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) S[dt] = mma(Kf[dt][kt], Ub[kt], S[dt]);
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int sl = 0; sl < NS; ++sl) S[sl][dt] = mma(Kf[dt][kt], Ub[sl][kt], S[sl][dt]);
             __builtin_amdgcn_sched_barrier(0);
             load_k(nx);
             __builtin_amdgcn_sched_barrier(0);
@@ -762,10 +801,12 @@ __global__ __launch_bounds__(192) void kda_state_kernel(KdaArgs a) {
         }
         if (a.sT) {
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
+            for (int sl = 0; sl < NS; ++sl)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a.sT[((size_t)bh * DK + 16 * dt + 4 * g + i) * DV + 16 * jt + col] = S[dt][i];
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        a.sT[((size_t)bh * DK + 16 * dt + 4 * g + i) * DV + column(sl)] = S[sl][dt][i];
         }
     } else if (wave == 1) {
         // ---------------- output: O^T = S^T Qt^T + U^T Bq^T ----------------
@@ -788,66 +829,75 @@ __global__ __launch_bounds__(192) void kda_state_kernel(KdaArgs a) {
         for (int n = 0; n < nchunks; ++n) {
             const int nx = min(n + 1, last);
             wait_counter(&ctr[0], n + 1, budget);
-            F(&slot)[NKS + 2][64] = su_ring[n % kRing];
-            F Sb[NKS], Ub[2];
+            F(&slot)[NS][NKS + 2][64] = su_ring[n % kRing];
+            f32x4_t O[NS][4];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) Sb[ks] = slot[ks][l];
-            Ub[0] = slot[NKS][l];
-            Ub[1] = slot[NKS + 1][l];
-            f32x4_t O[4];
+            for (int sl = 0; sl < NS; ++sl) {
+                F Sb[NKS], Ub[2];
 #pragma unroll
-            for (int R = 0; R < 4; ++R) O[R] = zero4();
+                for (int ks = 0; ks < NKS; ++ks) Sb[ks] = slot[sl][ks][l];
+                Ub[0] = slot[sl][NKS][l];
+                Ub[1] = slot[sl][NKS + 1][l];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
+                for (int R = 0; R < 4; ++R) O[sl][R] = zero4();
 #pragma unroll
-                for (int R = 0; R < 4; ++R) O[R] = mma(Sb[ks], Qf[R][ks], O[R]);
-            // causal inside the chunk: token block R sees token k-steps kt <= R/2
+                for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-            for (int R = 0; R < 4; ++R) O[R] = mma(Ub[0], Bf[R], O[R]);
-            O[2] = mma(Ub[1], Bf[4], O[2]);
-            O[3] = mma(Ub[1], Bf[5], O[3]);
+                    for (int R = 0; R < 4; ++R) O[sl][R] = mma(Sb[ks], Qf[R][ks], O[sl][R]);
+                // causal inside the chunk: token block R sees token k-steps kt <= R/2
+#pragma unroll
+                for (int R = 0; R < 4; ++R) O[sl][R] = mma(Ub[0], Bf[R], O[sl][R]);
+                O[sl][2] = mma(Ub[1], Bf[4], O[sl][2]);
+                O[sl][3] = mma(Ub[1], Bf[5], O[sl][3]);
+            }
             signal_counter(&ctr[1], n + 1);   // slot reads are complete (the MFMAs consumed them)
             __builtin_amdgcn_sched_barrier(0);
             load_qb(nx);
             __builtin_amdgcn_sched_barrier(0);
             if (n >= kRing) wait_counter(&ctr[3], n + 1 - kRing, budget);
 #pragma unroll
-            for (int R = 0; R < 4; ++R) o_ring[n % kRing][R][l] = O[R];
+            for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+                for (int R = 0; R < 4; ++R) o_ring[n % kRing][sl][R][l] = O[sl][R];
             signal_counter(&ctr[2], n + 1);
         }
     } else {
         // ---------------- store ----------------
-        // o of this (batch, head, 16 value columns) as a raw buffer: token t at
-        // byte t*H*DV*es.  Rows past the end of the stream fall outside the range
-        // and the hardware drops their stores.  The output tile is transposed
-        // (lane: 4 consecutive value columns of one token).
+        // o of this (batch, head) as a raw buffer: token t at byte t*H*DV*es.
+        // Rows past the end of the stream fall outside the range and the
+        // hardware drops their stores.  The output tile is transposed (lane: 4
+        // consecutive value columns of one token).
         const unsigned orow = (unsigned)a.H * DV * ES;
-        char *obase = static_cast<char *>(a.o) + ((((size_t)b * a.T) * a.H + h) * DV + 16 * jt) * ES;
-        const unsigned onum = (unsigned)a.T * orow - (unsigned)(h * DV + 16 * jt) * ES;
+        char *obase = static_cast<char *>(a.o) + ((((size_t)b * a.T) * a.H + h) * DV + 16 * NS * jt) * ES;
+        const unsigned onum = (unsigned)a.T * orow - (unsigned)(h * DV + 16 * NS * jt) * ES;
         const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(obase, 0, (int)onum, kBufWord3);
         const unsigned ovoff = (unsigned)col * orow + (unsigned)(4 * g) * ES;
 #pragma unroll 1
         for (int n = 0; n < nchunks; ++n) {
             wait_counter(&ctr[2], n + 1, budget);
-            f32x4_t O[4];
+            f32x4_t O[NS][4];
 #pragma unroll
-            for (int R = 0; R < 4; ++R) O[R] = o_ring[n % kRing][R][l];
+            for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+                for (int R = 0; R < 4; ++R) O[sl][R] = o_ring[n % kRing][sl][R][l];
             signal_counter(&ctr[3], n + 1);
 #pragma unroll
-            for (int R = 0; R < 4; ++R) {
-                const unsigned soff = ((unsigned)n * C + 16u * R) * orow;
-                if (sizeof(T) == 2) {
-                    u32x2_t v;
-                    v[0] = pack_bf16x2(O[R][0], O[R][1]);
-                    v[1] = pack_bf16x2(O[R][2], O[R][3]);
-                    __builtin_amdgcn_raw_buffer_store_b64(v, orsrc, ovoff, soff, 0);
-                } else {
-                    u32x4_t v;
+            for (int sl = 0; sl < NS; ++sl)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(O[R][i]);
-                    __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, ovoff, soff, 0);
+                for (int R = 0; R < 4; ++R) {
+                    const unsigned soff = ((unsigned)n * C + 16u * R) * orow + (unsigned)(16 * sl) * ES;
+                    if (sizeof(T) == 2) {
+                        u32x2_t v;
+                        v[0] = pack_bf16x2(O[sl][R][0], O[sl][R][1]);
+                        v[1] = pack_bf16x2(O[sl][R][2], O[sl][R][3]);
+                        __builtin_amdgcn_raw_buffer_store_b64(v, orsrc, ovoff, soff, 0);
+                    } else {
+                        u32x4_t v;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(O[sl][R][i]);
+                        __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, ovoff, soff, 0);
+                    }
                 }
-            }
         }
     }
 }
@@ -883,8 +933,9 @@ hipError_t launch_chunks_typed(const KdaArgs &a, hipStream_t stream) {
 
 template <typename T, int DK, int DV>
 hipError_t launch_scan_typed(const KdaArgs &a, hipStream_t stream) {
-    const int n2 = a.B * a.H * (DV / 16);
-    hipLaunchKernelGGL((kda_state_kernel<T, DK, DV>), dim3(n2), dim3(192), 0, stream, a);
+    constexpr int NS = kScanSlabs;
+    const int n2 = a.B * a.H * (DV / (16 * NS));
+    hipLaunchKernelGGL((kda_state_kernel<T, DK, DV, NS>), dim3(n2), dim3(192), 0, stream, a);
     return hipGetLastError();
 }
 
