@@ -43,6 +43,7 @@ constexpr int kBufWord3 = 0x00020000;   // 4th descriptor word of a raw gfx9 buf
 constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---- workspace layout (per batch, head, chunk; element type T) ---------------
@@ -638,24 +639,76 @@ __device__ __forceinline__ void signal_counter(int *ctr, int value) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-constexpr int kRing = 4;              // chunk steps buffered between the waves
-constexpr int kScanSlabs = 1;         // 16-column value slabs per scan workgroup
+// LDS counter access for a wave that has direct-to-LDS loads in flight.  The
+// compiler makes every LDS access of such a wave wait for all of those loads;
+// these two touch only the counter, so they are written out (the read waits
+// for its own result inside the same block) and the wave keeps its loads in
+// flight.  The caller orders them against its loads with explicit waits.
+typedef __attribute__((address_space(3))) int lds_int_t;
+__device__ __forceinline__ int lds_counter_read(int *ctr) {
+    int v;
+    const unsigned off = (unsigned)(uintptr_t)(lds_int_t *)ctr;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(off) : "memory");
+    return v;
+}
+__device__ __forceinline__ void lds_counter_write(int *ctr, int value) {
+    const unsigned off = (unsigned)(uintptr_t)(lds_int_t *)ctr;
+    asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(off), "v"(value) : "memory");
+}
+// Bounded wait on an LDS counter (see wait_counter) through lds_counter_read.
+__device__ __forceinline__ void wait_counter_dma(int *ctr, int target, int &budget) {
+    while (budget > 0 && lds_counter_read(ctr) < target) {
+        --budget;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+constexpr int kRing = 4;              // chunk steps buffered between recurrence, output, store
+static_assert(kRing % 2 == 0, "slots alternate between the two output waves");
+constexpr int kOpRing = 3;            // chunks of recurrence operands staged in LDS
 constexpr int kPollBudget = 1 << 24;  // LDS polls per wave per launch
 
-template <typename T, int DK, int DV, int NS>
-__global__ __launch_bounds__(192) void kda_state_kernel(KdaArgs a) {
+// s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding: vmcnt split over
+// bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xf00; }
+
+template <typename T, int DK, int DV>
+struct ScanLds {
+    static constexpr int ES = sizeof(T);
+    // one staged chunk of recurrence operands: exact copies of the workspace
+    // ranges W, Kh^T, this workgroup's Ut slice and Gam
+    static constexpr int W_B = 64 * DK * ES;
+    static constexpr int K_B = 64 * DK * ES;
+    static constexpr int U_B = 64 * 16 * ES;
+    static constexpr int G_B = DK * 4;
+    static constexpr int OPB = W_B + K_B + U_B + G_B;
+    static constexpr int NI = (W_B + 1023) / 1024 + (K_B + 1023) / 1024 + (U_B + 1023) / 1024 + (G_B + 1023) / 1024;
+    static_assert(NI < 64, "one staged chunk must fit the vector memory counter");
+};
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(320) void kda_state_kernel(KdaArgs a) {
     using WL = Ws<T, DK, DV>;
+    using SL = ScanLds<T, DK, DV>;
     using F = Frag<T>;
     using B = BufLd<T>;
-    constexpr int NJT = DV / (16 * NS);   // workgroups per head: NS 16-column slabs each
-    constexpr int NKS = DK / 32;          // contraction steps over dk
-    constexpr int NDT = DK / 16;          // 16-row state tiles
+    constexpr int NJT = DV / 16;     // workgroups per head: one 16-column value slab each
+    constexpr int NKS = DK / 32;     // contraction steps over dk
+    constexpr int NDT = DK / 16;     // 16-row state tiles
     constexpr unsigned ES = sizeof(T);
-    // ring slot, per lane: S operands (NKS fragments) then U operands (2 fragments), per slab
-    __shared__ F su_ring[kRing][NS][NKS + 2][64];
-    __shared__ f32x4_t o_ring[kRing][NS][4][64];
-    __shared__ int ctr[4];   // S/U produced, S/U consumed, O produced, O consumed
-    if (threadIdx.x < 4) ctr[threadIdx.x] = 0;
+    __shared__ __attribute__((aligned(1024))) char op_ring[kOpRing][SL::OPB];
+    // per lane: S operands (NKS fragments) then U operands (2 fragments)
+    __shared__ F su_ring[kRing][NKS + 2][64];
+    __shared__ f32x4_t o_ring[kRing][4][64];
+    // counters, each "chunks done" (n + 1 after chunk n):
+    //   kSuProd  S/U operands written (recurrence)
+    //   kSuCons  + parity: S/U slot read (output wave of that parity)
+    //   kOProd   + parity: O tile written (output wave of that parity)
+    //   kOCons   O tile read (store)
+    //   kOpProd  operands staged (loader), kOpCons operands read (recurrence)
+    constexpr int kSuProd = 0, kSuCons = 1, kOProd = 3, kOCons = 5, kOpProd = 6, kOpCons = 7;
+    __shared__ int ctr[8];
+    if (threadIdx.x < 8) ctr[threadIdx.x] = 0;
     __syncthreads();
 
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
@@ -672,144 +725,126 @@ __global__ __launch_bounds__(192) void kda_state_kernel(KdaArgs a) {
         const_cast<char *>(wsh), 0, (int)(unsigned)((size_t)nchunks * WL::BYTES), kBufWord3);
     const unsigned lane8 = (unsigned)l * 8 * ES;   // lane's fragment inside a [64][8] block
     auto cbase = [&](int n) { return (unsigned)n * (unsigned)WL::BYTES; };
-    auto column = [&](int sl) { return 16 * (NS * jt + sl) + col; };   // value column of slab sl
 
-    if (wave == 0) {
+    if (wave == 3) {
+        // ---------------- loader: recurrence operands -> LDS ----------------
+        // Copies the chunk's W, Kh^T, Ut slice and Gam ranges byte for byte
+        // with direct-to-LDS loads (16 bytes per lane, 1 KB per instruction),
+        // kOpRing - 1 chunks ahead of the recurrence.  Loads retire in order,
+        // so after issuing chunk p, vmcnt(NI) means chunk p - 1 has landed.
+        auto copy = [&](char *dst, unsigned src, int bytes, unsigned soff) {
+#pragma unroll
+            for (int i = 0; i < (bytes + 1023) / 1024; ++i)
+                if (i * 1024 + l * 16 < bytes)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(wsr, (lds_void_t *)(dst + i * 1024), 16,
+                                                             src + (unsigned)(i * 1024 + l * 16), soff, 0, 0);
+        };
+#pragma unroll 1
+        for (int p = 0; p < nchunks; ++p) {
+            if (p >= kOpRing) wait_counter_dma(&ctr[kOpCons], p - kOpRing + 1, budget);   // slot's last chunk read
+            char *slot = op_ring[p % kOpRing];
+            const unsigned c = cbase(p);
+            copy(slot, (unsigned)(WL::W * ES), SL::W_B, c);
+            copy(slot + SL::W_B, (unsigned)(WL::KH * ES), SL::K_B, c);
+            copy(slot + SL::W_B + SL::K_B, (unsigned)((WL::U + (size_t)jt * 64 * 16) * ES), SL::U_B, c);
+            copy(slot + SL::W_B + SL::K_B + SL::U_B, (unsigned)WL::GAM_BYTE, SL::G_B, c);
+            if (p >= 1) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(SL::NI));   // chunk p - 1 has landed
+                lds_counter_write(&ctr[kOpProd], p);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        lds_counter_write(&ctr[kOpProd], nchunks);
+    } else if (wave == 0) {
         // ---------------- recurrence ----------------
-        f32x4_t S[NS][NDT];
+        f32x4_t S[NDT];
 #pragma unroll
-        for (int sl = 0; sl < NS; ++sl)
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) S[sl][dt] = zero4();
+        for (int dt = 0; dt < NDT; ++dt) S[dt] = zero4();
         if (a.s0) {
 #pragma unroll
-            for (int sl = 0; sl < NS; ++sl)
+            for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        S[sl][dt][i] = a.s0[((size_t)bh * DK + 16 * dt + 4 * g + i) * DV + column(sl)];
+                for (int i = 0; i < 4; ++i)
+                    S[dt][i] = a.s0[((size_t)bh * DK + 16 * dt + 4 * g + i) * DV + 16 * jt + col];
         }
-        F Wf[4][NKS], Kf[NDT][2];
-        Raw8<T> ut[NS][2];   // Ut rows 16R + 4g + i of the slab's column: element 4R + i
-        float2 gam;          // decay of channels 16 dt + 4g + i for dt = col/2, i = 2(col%2) + {0, 1}
-        const unsigned ut_off = (unsigned)(WL::U + (size_t)(NS * jt * 64 + l) * 16) * ES;
-        const unsigned gam_off = (unsigned)WL::GAM_BYTE + 4u * (unsigned)(g * (DK / 4) + 2 * min(col, DK / 8 - 1));
-        auto load_w = [&](int n) {
-            const unsigned c = cbase(n);
+#pragma unroll 1
+        for (int n = 0; n < nchunks; ++n) {
+            wait_counter(&ctr[kOpProd], n + 1, budget);   // chunk n's operands are staged
+            const char *op = op_ring[n % kOpRing];
+            F Wf[4][NKS], Kf[NDT][2];
+            Raw8<T> ut[2];   // Ut rows 16R + 4g + i of column col: element 4R + i
 #pragma unroll
             for (int R = 0; R < 4; ++R)
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
-                    Wf[R][ks] = B::frag(wsr, lane8, c + (unsigned)(WL::W + (R * NKS + ks) * 512) * ES);
-        };
-        auto load_u = [&](int n) {
-            const unsigned c = cbase(n);
-#pragma unroll
-            for (int sl = 0; sl < NS; ++sl) {
-                B::raw8(ut[sl][0], wsr, ut_off, c + (unsigned)(sl * 64 * 16) * ES);
-                B::raw8(ut[sl][1], wsr, ut_off, c + (unsigned)(sl * 64 * 16 + 8) * ES);
-            }
-        };
-        auto load_k = [&](int n) {
-            const unsigned c = cbase(n);
+                    Wf[R][ks] = *reinterpret_cast<const F *>(op + (R * NKS + ks) * 64 * 8 * ES + lane8);
+            ut[0] = *reinterpret_cast<const Raw8<T> *>(op + SL::W_B + SL::K_B + l * 16 * ES);
+            ut[1] = *reinterpret_cast<const Raw8<T> *>(op + SL::W_B + SL::K_B + l * 16 * ES + 8 * ES);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
-                    Kf[dt][kt] = B::frag(wsr, lane8, c + (unsigned)(WL::KH + (dt * 2 + kt) * 512) * ES);
-            const u32x2_t gv = __builtin_amdgcn_raw_buffer_load_b64(wsr, gam_off, c, 0);
-            gam = make_float2(__uint_as_float(gv[0]), __uint_as_float(gv[1]));
-        };
-        // the loop issues W, Ut, then Kh + Gam each step; start in the same order
-        __builtin_amdgcn_sched_barrier(0);
-        load_w(0);
-        __builtin_amdgcn_sched_barrier(0);
-        load_u(0);
-        __builtin_amdgcn_sched_barrier(0);
-        load_k(0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll 1
-        for (int n = 0; n < nchunks; ++n) {
-            const int nx = min(n + 1, last);
-            F(&slot)[NS][NKS + 2][64] = su_ring[n % kRing];
-            F Sb[NS][NKS];
+                    Kf[dt][kt] = *reinterpret_cast<const F *>(op + SL::W_B + (dt * 2 + kt) * 64 * 8 * ES + lane8);
+            // decay of channels 16 dt + 4g + i for dt = col/2, i = 2(col%2) + {0, 1}
+            const float2 gam = *reinterpret_cast<const float2 *>(
+                op + SL::W_B + SL::K_B + SL::U_B + 4 * (g * (DK / 4) + 2 * min(col, DK / 8 - 1)));
+
+            F(&slot)[NKS + 2][64] = su_ring[n % kRing];
+            F Sb[NKS];
 #pragma unroll
-            for (int sl = 0; sl < NS; ++sl)
+            for (int ks = 0; ks < NKS; ++ks) {
+                Sb[ks] = tiles_to_frag<T>(S[2 * ks], S[2 * ks + 1]);
+                slot[ks][l] = Sb[ks];
+            }
+            // U = Ut - W S  (token rows 16R + 4g + i, value column col)
+            f32x4_t U[4];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    Sb[sl][ks] = tiles_to_frag<T>(S[sl][2 * ks], S[sl][2 * ks + 1]);
-                    slot[sl][ks][l] = Sb[sl][ks];
-                }
-            // U = Ut - W S  (token rows 16R + 4g + i, value column of each slab)
-            f32x4_t U[NS][4];
-#pragma unroll
-            for (int sl = 0; sl < NS; ++sl)
-#pragma unroll
-                for (int R = 0; R < 4; ++R) U[sl][R] = zero4();
+            for (int R = 0; R < 4; ++R) U[R] = zero4();
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-                for (int R = 0; R < 4; ++R)
+                for (int R = 0; R < 4; ++R) U[R] = mma(Wf[R][ks], Sb[ks], U[R]);
 #pragma unroll
-                    for (int sl = 0; sl < NS; ++sl) U[sl][R] = mma(Wf[R][ks], Sb[sl][ks], U[sl][R]);
-            __builtin_amdgcn_sched_barrier(0);
-            load_w(nx);
-            __builtin_amdgcn_sched_barrier(0);
-            F Ub[NS][2];
+            for (int R = 0; R < 2; ++R) {
+                float x[8];
+                ut[R].get(x);
 #pragma unroll
-            for (int sl = 0; sl < NS; ++sl) {
-#pragma unroll
-                for (int R = 0; R < 2; ++R) {
-                    float x[8];
-                    ut[sl][R].get(x);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        U[sl][2 * R][i] = x[i] - U[sl][2 * R][i];
-                        U[sl][2 * R + 1][i] = x[4 + i] - U[sl][2 * R + 1][i];
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    U[2 * R][i] = x[i] - U[2 * R][i];
+                    U[2 * R + 1][i] = x[4 + i] - U[2 * R + 1][i];
                 }
-                Ub[sl][0] = tiles_to_frag<T>(U[sl][0], U[sl][1]);
-                Ub[sl][1] = tiles_to_frag<T>(U[sl][2], U[sl][3]);
-                slot[sl][NKS][l] = Ub[sl][0];
-                slot[sl][NKS + 1][l] = Ub[sl][1];
             }
-            signal_counter(&ctr[0], n + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            load_u(nx);
-            __builtin_amdgcn_sched_barrier(0);
+            const F Ub[2] = {tiles_to_frag<T>(U[0], U[1]), tiles_to_frag<T>(U[2], U[3])};
+            slot[NKS][l] = Ub[0];
+            slot[NKS + 1][l] = Ub[1];
+            signal_counter(&ctr[kSuProd], n + 1);
             // S <- Diag(Gam) S + Kh^T U; the decay of (dt, i) sits in lane 2dt + i/2 of the row
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float gm = row_bcast(i & 1 ? gam.y : gam.x, 2 * dt + (i >> 1));
-#pragma unroll
-                    for (int sl = 0; sl < NS; ++sl) S[sl][dt][i] *= gm;
-                }
+                for (int i = 0; i < 4; ++i) S[dt][i] *= row_bcast(i & 1 ? gam.y : gam.x, 2 * dt + (i >> 1));
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                    for (int sl = 0; sl < NS; ++sl) S[sl][dt] = mma(Kf[dt][kt], Ub[sl][kt], S[sl][dt]);
-            __builtin_amdgcn_sched_barrier(0);
-            load_k(nx);
-            __builtin_amdgcn_sched_barrier(0);
-            // the next step overwrites slot (n+1) % kRing: wave 1 must be done with chunk n+1-kRing
-            if (n + 1 < nchunks && n + 1 >= kRing) wait_counter(&ctr[1], n + 2 - kRing, budget);
+                for (int dt = 0; dt < NDT; ++dt) S[dt] = mma(Kf[dt][kt], Ub[kt], S[dt]);
+            signal_counter(&ctr[kOpCons], n + 1);   // every operand of chunk n has been read
+            // the next step overwrites su slot (n+1) % kRing: chunk n+1-kRing must have been read
+            // (by the output wave of its parity; kRing is even)
+            if (n + 1 < nchunks && n + 1 >= kRing)
+                wait_counter(&ctr[kSuCons + ((n + 1) & 1)], n + 2 - kRing, budget);
         }
         if (a.sT) {
 #pragma unroll
-            for (int sl = 0; sl < NS; ++sl)
+            for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        a.sT[((size_t)bh * DK + 16 * dt + 4 * g + i) * DV + column(sl)] = S[sl][dt][i];
+                for (int i = 0; i < 4; ++i)
+                    a.sT[((size_t)bh * DK + 16 * dt + 4 * g + i) * DV + 16 * jt + col] = S[dt][i];
         }
-    } else if (wave == 1) {
+    } else if (wave == 1 || wave == 2) {
         // ---------------- output: O^T = S^T Qt^T + U^T Bq^T ----------------
+        // two output waves take alternate chunks, so each has two chunk steps
+        // to bring in its Qt and Bq operands
+        const int par = wave - 1;
         F Qf[4][NKS], Bf[6];
         auto load_qb = [&](int n) {
             const unsigned c = cbase(n);
@@ -824,80 +859,70 @@ __global__ __launch_bounds__(192) void kda_state_kernel(KdaArgs a) {
             Bf[4] = B::frag(wsr, lane8, c + (unsigned)(WL::BT + 5 * 512) * ES);
             Bf[5] = B::frag(wsr, lane8, c + (unsigned)(WL::BT + 7 * 512) * ES);
         };
-        load_qb(0);
+        load_qb(min(par, last));
 #pragma unroll 1
-        for (int n = 0; n < nchunks; ++n) {
-            const int nx = min(n + 1, last);
-            wait_counter(&ctr[0], n + 1, budget);
-            F(&slot)[NS][NKS + 2][64] = su_ring[n % kRing];
-            f32x4_t O[NS][4];
+        for (int n = par; n < nchunks; n += 2) {
+            wait_counter(&ctr[kSuProd], n + 1, budget);
+            F(&slot)[NKS + 2][64] = su_ring[n % kRing];
+            F Sb[NKS], Ub[2];
 #pragma unroll
-            for (int sl = 0; sl < NS; ++sl) {
-                F Sb[NKS], Ub[2];
+            for (int ks = 0; ks < NKS; ++ks) Sb[ks] = slot[ks][l];
+            Ub[0] = slot[NKS][l];
+            Ub[1] = slot[NKS + 1][l];
+            f32x4_t O[4];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) Sb[ks] = slot[sl][ks][l];
-                Ub[0] = slot[sl][NKS][l];
-                Ub[1] = slot[sl][NKS + 1][l];
+            for (int R = 0; R < 4; ++R) O[R] = zero4();
 #pragma unroll
-                for (int R = 0; R < 4; ++R) O[sl][R] = zero4();
+            for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
+                for (int R = 0; R < 4; ++R) O[R] = mma(Sb[ks], Qf[R][ks], O[R]);
+            // causal inside the chunk: token block R sees token k-steps kt <= R/2
 #pragma unroll
-                    for (int R = 0; R < 4; ++R) O[sl][R] = mma(Sb[ks], Qf[R][ks], O[sl][R]);
-                // causal inside the chunk: token block R sees token k-steps kt <= R/2
-#pragma unroll
-                for (int R = 0; R < 4; ++R) O[sl][R] = mma(Ub[0], Bf[R], O[sl][R]);
-                O[sl][2] = mma(Ub[1], Bf[4], O[sl][2]);
-                O[sl][3] = mma(Ub[1], Bf[5], O[sl][3]);
-            }
-            signal_counter(&ctr[1], n + 1);   // slot reads are complete (the MFMAs consumed them)
+            for (int R = 0; R < 4; ++R) O[R] = mma(Ub[0], Bf[R], O[R]);
+            O[2] = mma(Ub[1], Bf[4], O[2]);
+            O[3] = mma(Ub[1], Bf[5], O[3]);
+            signal_counter(&ctr[kSuCons + par], n + 1);   // slot reads are complete (the MFMAs consumed them)
             __builtin_amdgcn_sched_barrier(0);
-            load_qb(nx);
+            load_qb(min(n + 2, last));
             __builtin_amdgcn_sched_barrier(0);
-            if (n >= kRing) wait_counter(&ctr[3], n + 1 - kRing, budget);
+            if (n >= kRing) wait_counter(&ctr[kOCons], n + 1 - kRing, budget);
 #pragma unroll
-            for (int sl = 0; sl < NS; ++sl)
-#pragma unroll
-                for (int R = 0; R < 4; ++R) o_ring[n % kRing][sl][R][l] = O[sl][R];
-            signal_counter(&ctr[2], n + 1);
+            for (int R = 0; R < 4; ++R) o_ring[n % kRing][R][l] = O[R];
+            signal_counter(&ctr[kOProd + par], n + 1);
         }
-    } else {
+    } else if (wave == 4) {
         // ---------------- store ----------------
-        // o of this (batch, head) as a raw buffer: token t at byte t*H*DV*es.
-        // Rows past the end of the stream fall outside the range and the
-        // hardware drops their stores.  The output tile is transposed (lane: 4
-        // consecutive value columns of one token).
+        // o of this (batch, head, 16 value columns) as a raw buffer: token t at
+        // byte t*H*DV*es.  Rows past the end of the stream fall outside the range
+        // and the hardware drops their stores.  The output tile is transposed
+        // (lane: 4 consecutive value columns of one token).
         const unsigned orow = (unsigned)a.H * DV * ES;
-        char *obase = static_cast<char *>(a.o) + ((((size_t)b * a.T) * a.H + h) * DV + 16 * NS * jt) * ES;
-        const unsigned onum = (unsigned)a.T * orow - (unsigned)(h * DV + 16 * NS * jt) * ES;
+        char *obase = static_cast<char *>(a.o) + ((((size_t)b * a.T) * a.H + h) * DV + 16 * jt) * ES;
+        const unsigned onum = (unsigned)a.T * orow - (unsigned)(h * DV + 16 * jt) * ES;
         const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(obase, 0, (int)onum, kBufWord3);
         const unsigned ovoff = (unsigned)col * orow + (unsigned)(4 * g) * ES;
 #pragma unroll 1
         for (int n = 0; n < nchunks; ++n) {
-            wait_counter(&ctr[2], n + 1, budget);
-            f32x4_t O[NS][4];
+            wait_counter(&ctr[kOProd + (n & 1)], n + 1, budget);
+            f32x4_t O[4];
 #pragma unroll
-            for (int sl = 0; sl < NS; ++sl)
+            for (int R = 0; R < 4; ++R) O[R] = o_ring[n % kRing][R][l];
+            signal_counter(&ctr[kOCons], n + 1);
 #pragma unroll
-                for (int R = 0; R < 4; ++R) O[sl][R] = o_ring[n % kRing][sl][R][l];
-            signal_counter(&ctr[3], n + 1);
+            for (int R = 0; R < 4; ++R) {
+                const unsigned soff = ((unsigned)n * C + 16u * R) * orow;
+                if (sizeof(T) == 2) {
+                    u32x2_t v;
+                    v[0] = pack_bf16x2(O[R][0], O[R][1]);
+                    v[1] = pack_bf16x2(O[R][2], O[R][3]);
+                    __builtin_amdgcn_raw_buffer_store_b64(v, orsrc, ovoff, soff, 0);
+                } else {
+                    u32x4_t v;
 #pragma unroll
-            for (int sl = 0; sl < NS; ++sl)
-#pragma unroll
-                for (int R = 0; R < 4; ++R) {
-                    const unsigned soff = ((unsigned)n * C + 16u * R) * orow + (unsigned)(16 * sl) * ES;
-                    if (sizeof(T) == 2) {
-                        u32x2_t v;
-                        v[0] = pack_bf16x2(O[sl][R][0], O[sl][R][1]);
-                        v[1] = pack_bf16x2(O[sl][R][2], O[sl][R][3]);
-                        __builtin_amdgcn_raw_buffer_store_b64(v, orsrc, ovoff, soff, 0);
-                    } else {
-                        u32x4_t v;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(O[sl][R][i]);
-                        __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, ovoff, soff, 0);
-                    }
+                    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(O[R][i]);
+                    __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, ovoff, soff, 0);
                 }
+            }
         }
     }
 }
@@ -933,9 +958,8 @@ hipError_t launch_chunks_typed(const KdaArgs &a, hipStream_t stream) {
 
 template <typename T, int DK, int DV>
 hipError_t launch_scan_typed(const KdaArgs &a, hipStream_t stream) {
-    constexpr int NS = kScanSlabs;
-    const int n2 = a.B * a.H * (DV / (16 * NS));
-    hipLaunchKernelGGL((kda_state_kernel<T, DK, DV, NS>), dim3(n2), dim3(192), 0, stream, a);
+    const int n2 = a.B * a.H * (DV / 16);
+    hipLaunchKernelGGL((kda_state_kernel<T, DK, DV>), dim3(n2), dim3(320), 0, stream, a);
     return hipGetLastError();
 }
 
