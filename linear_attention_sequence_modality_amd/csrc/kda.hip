@@ -767,17 +767,24 @@ __global__ __launch_bounds__(320) void kda_state_kernel(KdaArgs a) {
                 for (int i = 0; i < 4; ++i)
                     S[dt][i] = a.s0[((size_t)bh * DK + 16 * dt + 4 * g + i) * DV + 16 * jt + col];
         }
-#pragma unroll 1
-        for (int n = 0; n < nchunks; ++n) {
-            wait_counter(&ctr[kOpProd], n + 1, budget);   // chunk n's operands are staged
+        // Operands of one chunk in registers, refilled from the LDS ring phase
+        // by phase as soon as the current chunk has issued its last use: W after
+        // the U products, Kh^T, Ut and Gam after the state update.  Every LDS
+        // poll and signal waits for all of this wave's LDS operations, so they
+        // come before the refills in each step.
+        F Wf[4][NKS], Kf[NDT][2];
+        Raw8<T> ut[2];   // Ut rows 16R + 4g + i of column col: element 4R + i
+        float2 gam;      // decay of channels 16 dt + 4g + i for dt = col/2, i = 2(col%2) + {0, 1}
+        auto read_w = [&](int n) {
             const char *op = op_ring[n % kOpRing];
-            F Wf[4][NKS], Kf[NDT][2];
-            Raw8<T> ut[2];   // Ut rows 16R + 4g + i of column col: element 4R + i
 #pragma unroll
             for (int R = 0; R < 4; ++R)
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
                     Wf[R][ks] = *reinterpret_cast<const F *>(op + (R * NKS + ks) * 64 * 8 * ES + lane8);
+        };
+        auto read_k = [&](int n) {
+            const char *op = op_ring[n % kOpRing];
             ut[0] = *reinterpret_cast<const Raw8<T> *>(op + SL::W_B + SL::K_B + l * 16 * ES);
             ut[1] = *reinterpret_cast<const Raw8<T> *>(op + SL::W_B + SL::K_B + l * 16 * ES + 8 * ES);
 #pragma unroll
@@ -785,10 +792,17 @@ __global__ __launch_bounds__(320) void kda_state_kernel(KdaArgs a) {
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
                     Kf[dt][kt] = *reinterpret_cast<const F *>(op + SL::W_B + (dt * 2 + kt) * 64 * 8 * ES + lane8);
-            // decay of channels 16 dt + 4g + i for dt = col/2, i = 2(col%2) + {0, 1}
-            const float2 gam = *reinterpret_cast<const float2 *>(
-                op + SL::W_B + SL::K_B + SL::U_B + 4 * (g * (DK / 4) + 2 * min(col, DK / 8 - 1)));
-
+            gam = *reinterpret_cast<const float2 *>(op + SL::W_B + SL::K_B + SL::U_B +
+                                                    4 * (g * (DK / 4) + 2 * min(col, DK / 8 - 1)));
+        };
+        wait_counter(&ctr[kOpProd], 1, budget);
+        read_w(0);
+        read_k(0);
+#pragma unroll 1
+        for (int n = 0; n < nchunks; ++n) {
+            // su slot n % kRing is free once chunk n-kRing has been read by the
+            // output wave of its parity (kRing is even)
+            if (n >= kRing) wait_counter(&ctr[kSuCons + (n & 1)], n + 1 - kRing, budget);
             F(&slot)[NKS + 2][64] = su_ring[n % kRing];
             F Sb[NKS];
 #pragma unroll
@@ -818,20 +832,23 @@ __global__ __launch_bounds__(320) void kda_state_kernel(KdaArgs a) {
             slot[NKS][l] = Ub[0];
             slot[NKS + 1][l] = Ub[1];
             signal_counter(&ctr[kSuProd], n + 1);
+            // chunk n's operands are all in registers: its ring slot may be restaged
+            signal_counter(&ctr[kOpCons], n + 1);
+            const float2 gm = gam;
+            if (n + 1 < nchunks) {
+                wait_counter(&ctr[kOpProd], n + 2, budget);   // chunk n+1's operands are staged
+                read_w(n + 1);
+            }
             // S <- Diag(Gam) S + Kh^T U; the decay of (dt, i) sits in lane 2dt + i/2 of the row
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[dt][i] *= row_bcast(i & 1 ? gam.y : gam.x, 2 * dt + (i >> 1));
+                for (int i = 0; i < 4; ++i) S[dt][i] *= row_bcast(i & 1 ? gm.y : gm.x, 2 * dt + (i >> 1));
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) S[dt] = mma(Kf[dt][kt], Ub[kt], S[dt]);
-            signal_counter(&ctr[kOpCons], n + 1);   // every operand of chunk n has been read
-            // the next step overwrites su slot (n+1) % kRing: chunk n+1-kRing must have been read
-            // (by the output wave of its parity; kRing is even)
-            if (n + 1 < nchunks && n + 1 >= kRing)
-                wait_counter(&ctr[kSuCons + ((n + 1) & 1)], n + 2 - kRing, budget);
+            if (n + 1 < nchunks) read_k(n + 1);
         }
         if (a.sT) {
 #pragma unroll
