@@ -398,8 +398,10 @@ __device__ void text_item(const ConvArgs &a, const Layout &L, int s, int item, i
     }
 }
 
+// bf16: at most 128 VGPRs, so four 4-wave blocks share a CU (LDS: 4 x 30 KB)
 template <typename T, int PT>
-__global__ __launch_bounds__(NT) void conv_kernel(ConvArgs a, Layout L) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 2 : 4))) void conv_kernel(
+    ConvArgs a, Layout L) {
     __shared__ __attribute__((aligned(1024))) char lds[2 * VisualTile<T, PT>::SLICE];
     int blk = xcd_remap(blockIdx.x, L.nblocks);
     const int wave = uniform(threadIdx.x / LANES), lane = threadIdx.x % LANES;
