@@ -37,9 +37,9 @@ KERNEL_SOURCES = {
     "scan": ("kda.hip", "mfma.h", "common.h", "launch.h"),
 }
 MEASURED_TRAFFIC = {
-    ("video_5s_480x832", "conv"): ("3f505f600b28876e", 594372.3, 399264.0),
-    ("video_5s_480x832", "chunks"): ("1bdf00f12a977546", 274548.0, 586607.2),
-    ("video_5s_480x832", "scan"): ("1bdf00f12a977546", 301643.0, 133088.0),
+    ("video_5s_480x832", "conv"): ("8771c56e56c6643b", 253813.4, 399264.0),
+    ("video_5s_480x832", "chunks"): ("2f0bfe69d8d9524b", 274535.3, 586583.0),
+    ("video_5s_480x832", "scan"): ("2f0bfe69d8d9524b", 293352.0, 133094.5),
 }
 
 
