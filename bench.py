@@ -2,14 +2,16 @@
 """Throughput of the conv + KDA token mixer forward on one MI355X.
 
 One step = kda_conv_forward (modality-aware short conv of q, k, v) followed by
-kda_forward_chunks + kda_forward_scan (the two kernels of kda_forward) on one
-stream, over one batch of the workload, inputs resident in HBM.  Prints one
-JSON line.  The default workload is the 5-second 480x832 video stream
+kda_forward (chunk transform and state pass, pipelined over chunk ranges),
+over one batch of the workload, inputs resident in HBM.  Prints one JSON line.
+With --isolated the step is the three kernels one after another on one stream
+(kda_conv_forward, kda_forward_chunks, kda_forward_scan).  The default workload is the 5-second 480x832 video stream
 (512 text tokens + a 21x30x52 latent-patch grid, T = 33272, 16 heads of
 dk = dv = 128, bf16 with fp32 accumulation).
 
 Per-kernel durations come from HIP events recorded on the launch stream
-between the three calls over the timed steps; the dominant kernel's roofline
+between the three calls of the isolated sequence (the timed steps with
+--isolated, else an isolated pass after them); the dominant kernel's roofline
 uses the algorithmic bytes per launch of roofline_bytes().
 """
 from __future__ import annotations
@@ -113,6 +115,9 @@ def main() -> int:
     ap.add_argument("--cpu-frames", type=int, default=0,
                     help="latent frames in the CPU-baseline sample (0 = the whole stream)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--isolated", action="store_true",
+                    help="time conv, chunk transform and state pass one after another on one stream "
+                         "instead of the pipelined kda_forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (three times) and "
                          "exit: the reference kernel for scaling HBM byte counters")
@@ -153,7 +158,8 @@ def main() -> int:
     wv = (inp["w_vis_q"], inp["w_vis_k"], inp["w_vis_v"])
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def isolated_step(ev=None):
+        # the three kernels one after another on one stream, each alone on the chip
         if ev is not None:
             ev[0].record(stream)
         kda.kda_conv_forward(desc, inp["q"], inp["k"], inp["v"], wt, wv, qc, kc, vc, stream=stream)
@@ -166,18 +172,46 @@ def main() -> int:
         if ev is not None:
             ev[3].record(stream)
 
+    def step(ev=None):
+        # the product path: conv, then kda_forward, which overlaps the chunk
+        # transform of each chunk range with the state pass of the previous one
+        if ev is not None:
+            ev[0].record(stream)
+        kda.kda_conv_forward(desc, inp["q"], inp["k"], inp["v"], wt, wv, qc, kc, vc, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        kda.kda_forward(desc, qc, kc, vc, inp["alpha"], inp["beta"], o=o, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    timed = isolated_step if args.isolated else step
     for _ in range(args.warmup):
-        step()
+        timed()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    nev = 4 if args.isolated else 3
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        timed(events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    # Per-kernel durations: the timed steps themselves with --isolated, else an
+    # isolated pass after them (inside kda_forward the state pass runs in
+    # chunk ranges on a second stream, beside the chunk transform).
     names = ("conv", "chunks", "scan")
-    ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in events) / args.steps for j, n in enumerate(names)}
+    if args.isolated:
+        kev = events
+    else:
+        stage_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in events) / args.steps for j in range(2)]
+        n_iso = max(3, args.steps // 4)
+        for _ in range(2):
+            isolated_step()
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_iso)]
+        for i in range(n_iso):
+            isolated_step(kev[i])
+        torch.cuda.synchronize()
+    ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in kev) / len(kev) for j, n in enumerate(names)}
     rb = roofline_bytes(cfg)
     kernels = {}
     for n in names:
@@ -210,6 +244,10 @@ def main() -> int:
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac_hbm"],
                      "traffic": measured_traffic(cfg.name, dom)},
         "kernels": kernels,
+        "kernel_timing": "isolated steps" if args.isolated else
+                         "isolated pass after the timed steps (each kernel alone on the chip)",
+        "timed_step": {"conv_us": round(stage_ms[0] * 1e3, 2), "kda_forward_us": round(stage_ms[1] * 1e3, 2)}
+                      if not args.isolated else None,
         "path": {"min_bytes": rb["path_min"], "GB/s_vs_path_min": round(path_gbs, 1),
                  "frac_of_path_roofline": round(path_gbs / HBM_PEAK_GBS, 4)},
     }

@@ -180,8 +180,9 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, col = l & 15, g = l >> 4;
-    const int nchunks = a.n_chunks;
-    const int n_items = a.B * a.H * nchunks;
+    // items of this launch: chunks [c0, c1) of every (batch, head), chunk-major
+    const int nchunks = a.n_chunks, nbh = a.B * a.H;
+    const int n_items = nbh * (a.c1 - a.c0);
 
     float *Gs = reinterpret_cast<float *>(smem + SM::X1);
     float *Lm = reinterpret_cast<float *>(smem + SM::X1);
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     const int vrp = tid / NCGV, vc0 = 8 * (tid % NCGV);
 
     auto load_inputs = [&](int item, Prefetch<T> &pf) {
-        const int bh = item / nchunks, n = item % nchunks;
+        const int bh = item % nbh, n = a.c0 + item / nbh;
         const int b = bh / a.H, h = bh % a.H;
         const int t0 = n * C, nr = min(C, a.T - t0);
         // Rows past the end of the stream re-read the last row (in bounds) and
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
 
 #pragma unroll 1
     for (; item < n_items; item += gridDim.x) {
-        const int bh = item / nchunks, n = item % nchunks;
+        const int bh = item % nbh, n = a.c0 + item / nbh;
         const int nr = min(C, a.T - n * C);   // valid rows in this chunk
         char *wsb = static_cast<char *>(a.ws) + ((size_t)bh * nchunks + n) * WL::BYTES;
         T *ws = reinterpret_cast<T *>(wsb);
@@ -621,6 +622,11 @@ template <> struct BufLd<float> {
     }
 };
 
+// An empty asm that reads and rewrites x: the value is computed before this
+// point, so the compiler cannot sink the computation towards a later use.
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(f32x4_t &x) { asm volatile("" : "+v"(x)); }
+
 // Wait until an LDS counter reaches target.  Bounded: a kernel-wide poll
 // budget (far above what a correct run uses) guarantees that every wave exits
 // even if its partner never signals.
@@ -663,10 +669,18 @@ __device__ __forceinline__ void wait_counter_dma(int *ctr, int target, int &budg
     }
 }
 
+// Wave roles of the state pass.  Waves are spread over the four SIMDs in
+// turn, so the store wave (little work) shares SIMD 0 with the recurrence.
+constexpr int kOutWaves = 4;          // output waves; chunk n goes to output wave n % kOutWaves
+constexpr int kStoreWave = 4, kLoaderWave = 6;
+__device__ __forceinline__ int out_slot(int wave) {   // output wave index, or -1
+    return wave >= 1 && wave <= 3 ? wave - 1 : wave == 5 ? 3 : -1;
+}
 constexpr int kRing = 4;              // chunk steps buffered between recurrence, output, store
-static_assert(kRing % 2 == 0, "slots alternate between the two output waves");
+static_assert(kRing % kOutWaves == 0, "each ring slot belongs to one output wave");
 constexpr int kOpRing = 3;            // chunks of recurrence operands staged in LDS
 constexpr int kPollBudget = 1 << 24;  // LDS polls per wave per launch
+constexpr int kScanThreads = 448;     // recurrence, four output waves, store, loader
 
 // s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding: vmcnt split over
 // bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima).
@@ -687,7 +701,7 @@ struct ScanLds {
 };
 
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(320) void kda_state_kernel(KdaArgs a) {
+__global__ __launch_bounds__(kScanThreads) void kda_state_kernel(KdaArgs a) {
     using WL = Ws<T, DK, DV>;
     using SL = ScanLds<T, DK, DV>;
     using F = Frag<T>;
@@ -706,9 +720,10 @@ __global__ __launch_bounds__(320) void kda_state_kernel(KdaArgs a) {
     //   kOProd   + parity: O tile written (output wave of that parity)
     //   kOCons   O tile read (store)
     //   kOpProd  operands staged (loader), kOpCons operands read (recurrence)
-    constexpr int kSuProd = 0, kSuCons = 1, kOProd = 3, kOCons = 5, kOpProd = 6, kOpCons = 7;
-    __shared__ int ctr[8];
-    if (threadIdx.x < 8) ctr[threadIdx.x] = 0;
+    constexpr int kSuProd = 0, kSuCons = 1, kOProd = kSuCons + kOutWaves, kOCons = kOProd + kOutWaves,
+                  kOpProd = kOCons + 1, kOpCons = kOpProd + 1, kNumCtr = kOpCons + 1;
+    __shared__ int ctr[kNumCtr];
+    if (threadIdx.x < kNumCtr) ctr[threadIdx.x] = 0;
     __syncthreads();
 
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
@@ -716,17 +731,18 @@ __global__ __launch_bounds__(320) void kda_state_kernel(KdaArgs a) {
     const int b = bh / a.H, h = bh % a.H;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = threadIdx.x & 63, col = l & 15, g = l >> 4;
-    const int nchunks = a.n_chunks, last = nchunks - 1;
+    // this launch walks chunks [c0, c1); loop indices below count from c0
+    const int nchunks = a.c1 - a.c0, last = nchunks - 1;
     int budget = kPollBudget;
 
     // this (batch, head)'s workspace: chunk n at byte n * BYTES (< 4 GiB, checked on the host)
-    const char *wsh = static_cast<const char *>(a.ws) + (size_t)bh * nchunks * WL::BYTES;
+    const char *wsh = static_cast<const char *>(a.ws) + (size_t)bh * a.n_chunks * WL::BYTES;
     const __amdgpu_buffer_rsrc_t wsr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(wsh), 0, (int)(unsigned)((size_t)nchunks * WL::BYTES), kBufWord3);
+        const_cast<char *>(wsh), 0, (int)(unsigned)((size_t)a.n_chunks * WL::BYTES), kBufWord3);
     const unsigned lane8 = (unsigned)l * 8 * ES;   // lane's fragment inside a [64][8] block
-    auto cbase = [&](int n) { return (unsigned)n * (unsigned)WL::BYTES; };
+    auto cbase = [&](int i) { return (unsigned)(a.c0 + i) * (unsigned)WL::BYTES; };
 
-    if (wave == 3) {
+    if (wave == kLoaderWave) {
         // ---------------- loader: recurrence operands -> LDS ----------------
         // Copies the chunk's W, Kh^T, Ut slice and Gam ranges byte for byte
         // with direct-to-LDS loads (16 bytes per lane, 1 KB per instruction),
@@ -800,16 +816,12 @@ __global__ __launch_bounds__(320) void kda_state_kernel(KdaArgs a) {
         read_k(0);
 #pragma unroll 1
         for (int n = 0; n < nchunks; ++n) {
-            // su slot n % kRing is free once chunk n-kRing has been read by the
-            // output wave of its parity (kRing is even)
-            if (n >= kRing) wait_counter(&ctr[kSuCons + (n & 1)], n + 1 - kRing, budget);
-            F(&slot)[NKS + 2][64] = su_ring[n % kRing];
+            // Critical chain of a step: pack S -> U MFMAs -> U = Ut - W S, pack
+            // -> state MFMAs.  The decay of S, the ring traffic and the operand
+            // refills sit in the shadow of the MFMAs.
             F Sb[NKS];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                Sb[ks] = tiles_to_frag<T>(S[2 * ks], S[2 * ks + 1]);
-                slot[ks][l] = Sb[ks];
-            }
+            for (int ks = 0; ks < NKS; ++ks) Sb[ks] = tiles_to_frag<T>(S[2 * ks], S[2 * ks + 1]);
             // U = Ut - W S  (token rows 16R + 4g + i, value column col)
             f32x4_t U[4];
 #pragma unroll
@@ -818,37 +830,50 @@ __global__ __launch_bounds__(320) void kda_state_kernel(KdaArgs a) {
             for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
                 for (int R = 0; R < 4; ++R) U[R] = mma(Wf[R][ks], Sb[ks], U[R]);
+            // S <- Diag(Gam) S; the decay of (dt, i) sits in lane 2dt + i/2 of the row
+            const float2 gm = gam;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[dt][i] *= row_bcast(i & 1 ? gm.y : gm.x, 2 * dt + (i >> 1));
+                pin(S[dt]);   // keeps the decay here, under the MFMAs, rather than next to its use
+            }
+            float x[2][8];
 #pragma unroll
             for (int R = 0; R < 2; ++R) {
-                float x[8];
-                ut[R].get(x);
+                ut[R].get(x[R]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pin(x[R][i]);
+            }
+            // su slot n % kRing is free once chunk n-kRing has been read by the
+            // output wave of its parity (kRing is even)
+            if (n >= kRing) wait_counter(&ctr[kSuCons + n % kOutWaves], n + 1 - kRing, budget);
+            F(&slot)[NKS + 2][64] = su_ring[n % kRing];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) slot[ks][l] = Sb[ks];
+#pragma unroll
+            for (int R = 0; R < 2; ++R)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    U[2 * R][i] = x[i] - U[2 * R][i];
-                    U[2 * R + 1][i] = x[4 + i] - U[2 * R + 1][i];
+                    U[2 * R][i] = x[R][i] - U[2 * R][i];
+                    U[2 * R + 1][i] = x[R][4 + i] - U[2 * R + 1][i];
                 }
-            }
             const F Ub[2] = {tiles_to_frag<T>(U[0], U[1]), tiles_to_frag<T>(U[2], U[3])};
+            // S <- S + Kh^T U
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) S[dt] = mma(Kf[dt][kt], Ub[kt], S[dt]);
             slot[NKS][l] = Ub[0];
             slot[NKS + 1][l] = Ub[1];
             signal_counter(&ctr[kSuProd], n + 1);
             // chunk n's operands are all in registers: its ring slot may be restaged
             signal_counter(&ctr[kOpCons], n + 1);
-            const float2 gm = gam;
             if (n + 1 < nchunks) {
                 wait_counter(&ctr[kOpProd], n + 2, budget);   // chunk n+1's operands are staged
                 read_w(n + 1);
+                read_k(n + 1);
             }
-            // S <- Diag(Gam) S + Kh^T U; the decay of (dt, i) sits in lane 2dt + i/2 of the row
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[dt][i] *= row_bcast(i & 1 ? gm.y : gm.x, 2 * dt + (i >> 1));
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) S[dt] = mma(Kf[dt][kt], Ub[kt], S[dt]);
-            if (n + 1 < nchunks) read_k(n + 1);
         }
         if (a.sT) {
 #pragma unroll
@@ -857,11 +882,11 @@ __global__ __launch_bounds__(320) void kda_state_kernel(KdaArgs a) {
                 for (int i = 0; i < 4; ++i)
                     a.sT[((size_t)bh * DK + 16 * dt + 4 * g + i) * DV + 16 * jt + col] = S[dt][i];
         }
-    } else if (wave == 1 || wave == 2) {
+    } else if (out_slot(wave) >= 0) {
         // ---------------- output: O^T = S^T Qt^T + U^T Bq^T ----------------
-        // two output waves take alternate chunks, so each has two chunk steps
-        // to bring in its Qt and Bq operands
-        const int par = wave - 1;
+        // the output waves take chunks in turn, so each has kOutWaves chunk
+        // steps to bring in its Qt and Bq operands
+        const int par = out_slot(wave);
         F Qf[4][NKS], Bf[6];
         auto load_qb = [&](int n) {
             const unsigned c = cbase(n);
@@ -878,7 +903,7 @@ __global__ __launch_bounds__(320) void kda_state_kernel(KdaArgs a) {
         };
         load_qb(min(par, last));
 #pragma unroll 1
-        for (int n = par; n < nchunks; n += 2) {
+        for (int n = par; n < nchunks; n += kOutWaves) {
             wait_counter(&ctr[kSuProd], n + 1, budget);
             F(&slot)[NKS + 2][64] = su_ring[n % kRing];
             F Sb[NKS], Ub[2];
@@ -900,14 +925,14 @@ __global__ __launch_bounds__(320) void kda_state_kernel(KdaArgs a) {
             O[3] = mma(Ub[1], Bf[5], O[3]);
             signal_counter(&ctr[kSuCons + par], n + 1);   // slot reads are complete (the MFMAs consumed them)
             __builtin_amdgcn_sched_barrier(0);
-            load_qb(min(n + 2, last));
+            load_qb(min(n + kOutWaves, last));
             __builtin_amdgcn_sched_barrier(0);
             if (n >= kRing) wait_counter(&ctr[kOCons], n + 1 - kRing, budget);
 #pragma unroll
             for (int R = 0; R < 4; ++R) o_ring[n % kRing][R][l] = O[R];
             signal_counter(&ctr[kOProd + par], n + 1);
         }
-    } else if (wave == 4) {
+    } else if (wave == kStoreWave) {
         // ---------------- store ----------------
         // o of this (batch, head, 16 value columns) as a raw buffer: token t at
         // byte t*H*DV*es.  Rows past the end of the stream fall outside the range
@@ -920,14 +945,14 @@ __global__ __launch_bounds__(320) void kda_state_kernel(KdaArgs a) {
         const unsigned ovoff = (unsigned)col * orow + (unsigned)(4 * g) * ES;
 #pragma unroll 1
         for (int n = 0; n < nchunks; ++n) {
-            wait_counter(&ctr[kOProd + (n & 1)], n + 1, budget);
+            wait_counter(&ctr[kOProd + n % kOutWaves], n + 1, budget);
             f32x4_t O[4];
 #pragma unroll
             for (int R = 0; R < 4; ++R) O[R] = o_ring[n % kRing][R][l];
             signal_counter(&ctr[kOCons], n + 1);
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
-                const unsigned soff = ((unsigned)n * C + 16u * R) * orow;
+                const unsigned soff = ((unsigned)(a.c0 + n) * C + 16u * R) * orow;
                 if (sizeof(T) == 2) {
                     u32x2_t v;
                     v[0] = pack_bf16x2(O[R][0], O[R][1]);
@@ -944,6 +969,43 @@ __global__ __launch_bounds__(320) void kda_state_kernel(KdaArgs a) {
     }
 }
 
+template <typename T, int DK, int DV>
+hipError_t launch_chunks_typed(const KdaArgs &a, hipStream_t stream) {
+    using SM = K1Smem<T, DK, DV>;
+    static bool attr_set = false;   // per process; setting it twice is harmless
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)kda_intra_kernel<T, DK, DV>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)SM::BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int items = a.B * a.H * (a.c1 - a.c0);
+    const int cap = a.k1_grid > 0 && a.k1_grid < num_cus() ? a.k1_grid : num_cus();
+    const int grid = items < cap ? items : cap;
+    hipLaunchKernelGGL((kda_intra_kernel<T, DK, DV>), dim3(grid), dim3(K1_THREADS), SM::BYTES, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T, int DK, int DV>
+hipError_t launch_scan_typed(const KdaArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((kda_state_kernel<T, DK, DV>), dim3(scan_workgroups(a)), dim3(kScanThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+#define KDA_DISPATCH(FN)                                                                           \
+    if (a.B * a.H * (a.c1 - a.c0) == 0) return hipSuccess;                                         \
+    if (bf16) {                                                                                    \
+        if (a.dk == 64 && a.dv == 64) return FN<bf16_t, 64, 64>(a, stream);                        \
+        if (a.dk == 64 && a.dv == 128) return FN<bf16_t, 64, 128>(a, stream);                      \
+        if (a.dk == 128 && a.dv == 64) return FN<bf16_t, 128, 64>(a, stream);                      \
+        if (a.dk == 128 && a.dv == 128) return FN<bf16_t, 128, 128>(a, stream);                    \
+    } else {                                                                                       \
+        if (a.dk == 64 && a.dv == 64) return FN<float, 64, 64>(a, stream);                         \
+    }                                                                                              \
+    return hipErrorInvalidValue;
+
+}  // namespace
+
 int num_cus() {
     static int cus[64] = {0};
     int dev = 0;
@@ -957,42 +1019,7 @@ int num_cus() {
     return cus[dev];
 }
 
-template <typename T, int DK, int DV>
-hipError_t launch_chunks_typed(const KdaArgs &a, hipStream_t stream) {
-    using SM = K1Smem<T, DK, DV>;
-    static bool attr_set = false;   // per process; setting it twice is harmless
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)kda_intra_kernel<T, DK, DV>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)SM::BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    const int items = a.B * a.H * a.n_chunks;
-    const int grid = items < num_cus() ? items : num_cus();
-    hipLaunchKernelGGL((kda_intra_kernel<T, DK, DV>), dim3(grid), dim3(K1_THREADS), SM::BYTES, stream, a);
-    return hipGetLastError();
-}
-
-template <typename T, int DK, int DV>
-hipError_t launch_scan_typed(const KdaArgs &a, hipStream_t stream) {
-    const int n2 = a.B * a.H * (DV / 16);
-    hipLaunchKernelGGL((kda_state_kernel<T, DK, DV>), dim3(n2), dim3(320), 0, stream, a);
-    return hipGetLastError();
-}
-
-#define KDA_DISPATCH(FN)                                                                           \
-    if (a.B * a.H * a.n_chunks == 0) return hipSuccess;                                            \
-    if (bf16) {                                                                                    \
-        if (a.dk == 64 && a.dv == 64) return FN<bf16_t, 64, 64>(a, stream);                        \
-        if (a.dk == 64 && a.dv == 128) return FN<bf16_t, 64, 128>(a, stream);                      \
-        if (a.dk == 128 && a.dv == 64) return FN<bf16_t, 128, 64>(a, stream);                      \
-        if (a.dk == 128 && a.dv == 128) return FN<bf16_t, 128, 128>(a, stream);                    \
-    } else {                                                                                       \
-        if (a.dk == 64 && a.dv == 64) return FN<float, 64, 64>(a, stream);                         \
-    }                                                                                              \
-    return hipErrorInvalidValue;
-
-}  // namespace
+int scan_workgroups(const KdaArgs &a) { return a.B * a.H * (a.dv / 16); }
 
 size_t kda_chunk_ws_bytes(int dk, int dv, bool bf16) {
 #define WS_CASE(DK_, DV_)                                                                          \

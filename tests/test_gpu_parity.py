@@ -146,6 +146,44 @@ def test_split_and_resume_matches_one_shot():
     assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"]
 
 
+@pytest.mark.timeout(120)
+@pytest.mark.parametrize("T,B", [(64 * 70 + 13, 1), (64 * 300 - 5, 2)])
+def test_pipelined_forward_equals_the_two_kernels(T, B):
+    """kda_forward splits the chunks into ranges (2 and 8 here) and overlaps the
+    chunk transform of one range with the state pass of the previous range on a
+    second stream, carrying the state through the workspace.  Same arithmetic
+    in the same order as kda_forward_chunks + kda_forward_scan: equal bit for
+    bit, final state included, with an initial state that aliases it."""
+    cfg = _small("pipe", B=B, n_text=T, grid=(0, 0, 0))
+    say("case pipelined T=%d B=%d chunks=%d" % (T, B, (T + 63) // 64))
+    inp = to_dev(make_inputs(cfg))
+    d = desc_of(cfg)
+    x = [inp[k] for k in ("q", "k", "v", "alpha", "beta")]
+    g = torch.Generator().manual_seed(5)
+    s0 = (torch.randn(cfg.B, cfg.H, cfg.dk, cfg.dv, generator=g) * 0.1).cuda()
+    need = kda.kda_forward_workspace_size(d, cfg.B, cfg.H, cfg.dk, cfg.dv, torch.bfloat16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o1 = torch.empty_like(inp["v"])
+    s1 = torch.empty_like(s0)
+    kda.kda_forward_chunks(d, *x, ws)
+    kda.kda_forward_scan(d, cfg.B, cfg.H, cfg.dk, cfg.dv, torch.bfloat16, ws, o1, initial_state=s0,
+                         final_state=s1)
+    o2 = torch.full_like(inp["v"], float("nan"))
+    s2 = s0.clone()                       # initial state, overwritten in place by the final state
+    kda.kda_forward(d, *x, initial_state=s2, final_state=s2, o=o2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(s1, s2)
+    # and the two-kernel path itself against the oracle on one head
+    host = make_inputs(cfg)
+    ro, _ = oracle.kda_recurrence(*[heads_slice(host[k], (1,)) for k in ("q", "k", "v", "alpha")],
+                                  heads_slice(host["beta"][..., None], (1,))[..., 0],
+                                  S0=s0[:, 1:2].double().cpu().numpy(), want_state=False)
+    e = rel(heads_slice(o2, (1,)), ro)
+    say("  pipelined rel err o %.2e" % e)
+    assert e <= TOL["bf16"]
+
+
 # ---- hygiene -----------------------------------------------------------------------
 
 @pytest.mark.timeout(120)
