@@ -39,9 +39,9 @@ KERNEL_SOURCES = {
     "scan": ("kda.hip", "mfma.h", "common.h", "launch.h"),
 }
 MEASURED_TRAFFIC = {
-    ("video_5s_480x832", "conv"): ("8771c56e56c6643b", 253813.4, 399264.0),
-    ("video_5s_480x832", "chunks"): ("2f0bfe69d8d9524b", 274535.3, 586583.0),
-    ("video_5s_480x832", "scan"): ("2f0bfe69d8d9524b", 293352.0, 133094.5),
+    ("video_5s_480x832", "conv"): ("2b82e3bee3400eaf", 253082.2, 399264.0),
+    ("video_5s_480x832", "chunks"): ("1f87b38ef9c35f4d", 270468.0, 586560.1),
+    ("video_5s_480x832", "scan"): ("1f87b38ef9c35f4d", 293354.7, 133088.0),
 }
 
 
