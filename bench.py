@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix-core peak, TFLOP/s
 
 # HBM byte counters per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, in KiB), taken on
 # the source files whose digest is stored beside them; a kernel whose sources changed since reports
@@ -84,6 +85,46 @@ def roofline_bytes(cfg) -> dict:
     scan = ws + th * cfg.dv * es
     path_min = th * ((3 * cfg.dk + 3 * cfg.dv) * es + (3 * cfg.dk + cfg.dv + 1) * es + cfg.dv * es)
     return {"conv": conv, "chunks": chunks, "scan": scan, "path_min": path_min}
+
+
+def mfma_flops(cfg) -> dict:
+    """Matrix-core flops per launch as the kernels issue them (dense 16x16 tiles).
+
+    chunks : per chunk-head, the 10 lower-triangle 16x16 tiles of A and Bq over
+             dk (2 products each), W and Ut from the block-lower-triangular Tm
+             (6 tile products per 16 columns), and the fp32 off-diagonal levels
+             of Tm (16 tile products of 16x16x16)
+    scan   : per chunk-head and 16 value columns, U = Ut - W S and
+             S <- Gam S + Kh^T U (2 x 4 x dk/32 tile products) and the output
+             (4 x dk/32 + 6 tile products); each tile product is 16x16x32
+    The conv runs on the vector ALU (paired bf16 dot products), not on MFMA.
+    """
+    nch = (cfg.T + 63) // 64
+    ch = cfg.B * cfg.H * nch
+    t32 = 2 * 16 * 16 * 32                  # one 16x16x32 product
+    nks = cfg.dk // 32
+    chunks = ch * (10 * nks * 2 * t32 + (cfg.dk // 16 + cfg.dv // 16) * 6 * t32 + 16 * 2 * 16 * 16 * 16)
+    scan = ch * (cfg.dv // 16) * ((2 * 4 * nks) + (4 * nks + 6)) * t32
+    return {"chunks": chunks, "scan": scan}
+
+
+def copy_bandwidth(torch, mib: int = 1024, reps: int = 5) -> float:
+    """Measured device-to-device copy rate (read + write bytes / s) of a plain torch copy."""
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbs
 
 
 def cpu_baseline(cfg, frames: int) -> dict:
@@ -199,6 +240,19 @@ def main() -> int:
     # Per-kernel durations: the timed steps themselves with --isolated, else an
     # isolated pass after them (inside kda_forward the state pass runs in
     # chunk ranges on a second stream, beside the chunk transform).
+    step_ms = sorted(e[0].elapsed_time(e[-1]) for e in events)
+    # cold steps: a 1 GiB fill before each one evicts L2 and the 256 MB Infinity Cache
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    n_cold = max(3, args.steps // 4)
+    cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n_cold)]
+    for i in range(n_cold):
+        scratch.fill_(i & 255)
+        timed(cold_ev[i])
+    torch.cuda.synchronize()
+    cold_ms = sorted(e[0].elapsed_time(e[-1]) for e in cold_ev)
+    del scratch
+    copy_gbs = copy_bandwidth(torch)
+
     names = ("conv", "chunks", "scan")
     if args.isolated:
         kev = events
@@ -213,11 +267,17 @@ def main() -> int:
         torch.cuda.synchronize()
     ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in kev) / len(kev) for j, n in enumerate(names)}
     rb = roofline_bytes(cfg)
+    fl = mfma_flops(cfg)
     kernels = {}
     for n in names:
         gbs = rb[n] / (ms[n] * 1e-3) / 1e9
         kernels[n] = {"us": round(ms[n] * 1e3, 2), "bytes": rb[n], "GB/s": round(gbs, 1),
-                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                      "frac_measured_copy": round(gbs / copy_gbs, 4)}
+        if n in fl:
+            tf = fl[n] / (ms[n] * 1e-3) / 1e12
+            kernels[n].update({"mfma_flop": fl[n], "TFLOP/s": round(tf, 1),
+                               "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFS, 4)})
     dom = max(names, key=lambda n: ms[n])
     ms_step = elapsed / args.steps * 1e3
     tokens = cfg.B * cfg.T
@@ -248,6 +308,11 @@ def main() -> int:
                          "isolated pass after the timed steps (each kernel alone on the chip)",
         "timed_step": {"conv_us": round(stage_ms[0] * 1e3, 2), "kda_forward_us": round(stage_ms[1] * 1e3, 2)}
                       if not args.isolated else None,
+        "step_ms": {"median": round(step_ms[len(step_ms) // 2], 4), "min": round(step_ms[0], 4),
+                    "cold_median": round(cold_ms[len(cold_ms) // 2], 4), "cold_min": round(cold_ms[0], 4),
+                    "cold_tokens_per_s": round(tokens / (cold_ms[len(cold_ms) // 2] * 1e-3), 1),
+                    "cold": "each step after a 1 GiB fill that evicts L2 and the Infinity Cache"},
+        "measured_copy_GB/s": round(copy_gbs, 1),
         "path": {"min_bytes": rb["path_min"], "GB/s_vs_path_min": round(path_gbs, 1),
                  "frac_of_path_roofline": round(path_gbs / HBM_PEAK_GBS, 4)},
     }
