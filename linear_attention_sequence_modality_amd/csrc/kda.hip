@@ -110,9 +110,7 @@ template <> struct Raw4<float> {
 // ---- kernel 1 shared-memory plan --------------------------------------------------
 template <typename T, int DK, int DV>
 struct K1Smem {
-    static constexpr int NPART = K1_THREADS / DK;     // scan partitions per column
-    static constexpr int RPP = C / NPART;             // rows per partition
-    static constexpr int GS = DK + 4;                 // fp32 row stride of G
+    static constexpr int NPART = K1_THREADS / DK;     // threads per channel in the table loop
     static constexpr int KP = 16 / (int)sizeof(T);
     static constexpr int KS = DK + KP;                // row stride of Kr, Qr, Kb
     static constexpr int RKS = 2 * (DK + 8 / (int)sizeof(T));  // row-pair stride of RHS_K
@@ -121,6 +119,7 @@ struct K1Smem {
     static constexpr int TS = 64 + KP;                // T 64x64 stride (Tm16)
     static constexpr int SC = 17;                     // 16x16 fp32 scratch stride
 
+    static constexpr int GS = DK + 4;                 // fp32 row stride of G
     static constexpr size_t SZ_G = (size_t)C * GS * 4;
     static constexpr size_t SZ_LM = (size_t)C * LS * 4;
     static constexpr size_t SZ_K = (size_t)C * KS * sizeof(T);
@@ -135,16 +134,40 @@ struct K1Smem {
     static constexpr size_t RK = Q + round_up(SZ_K, 16);            // RHS_K row pairs (P1-P5)
     static constexpr size_t RV = RK + round_up((size_t)32 * RKS * sizeof(T), 16);
     static constexpr size_t TB = RV + round_up((size_t)32 * RVS * sizeof(T), 16);
-    // tables (fp32): Pm[4][DK], Kh[4][DK], Fp[6][DK], beta[64], tot[NPART][DK]
+    // tables (fp32): Pm[4][DK], Kh[4][DK], Fp[6][DK], beta[64]
     static constexpr size_t TB_PM = TB;
     static constexpr size_t TB_KH = TB_PM + 4 * DK * 4;
     static constexpr size_t TB_FP = TB_KH + 4 * DK * 4;
     static constexpr size_t TB_BETA = TB_FP + 6 * DK * 4;
-    static constexpr size_t TB_TOT = TB_BETA + 64 * 4;
-    static constexpr size_t BYTES = round_up(TB_TOT + (size_t)NPART * DK * 4, 16);
+    static constexpr size_t BYTES = round_up(TB_BETA + 64 * 4, 16);
 };
 
 __device__ __forceinline__ int fp_index(int R, int S) { return R * (R - 1) / 2 + S; }
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8
+// inside each 16-lane row (zeros shifted in), then lane 15 of rows 0 and 2
+// into rows 1 and 3, then lane 31 into rows 2 and 3 (DPP row broadcasts).
+template <int CTRL, int ROWS, bool BOUND>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, BOUND));
+}
+// N independent scans, interleaved step by step (each DPP read then finds
+// its source written N instructions earlier).
+template <int N>
+__device__ __forceinline__ void wave_inclusive_sums(float (&x)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f<0x111, 0xf, true>(x[i]);   // row_shr:1
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f<0x112, 0xf, true>(x[i]);   // row_shr:2
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f<0x114, 0xf, true>(x[i]);   // row_shr:4
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f<0x118, 0xf, true>(x[i]);   // row_shr:8
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f<0x142, 0xa, false>(x[i]);  // row_bcast:15 -> rows 1, 3
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f<0x143, 0xc, false>(x[i]);  // row_bcast:31 -> rows 2, 3
+}
 
 // Hardware base-2 exponent and logarithm (v_exp_f32, v_log_f32, about 1 ulp).
 // Results below the smallest normal flush to zero, which only affects decay
@@ -165,7 +188,8 @@ __device__ __forceinline__ f32x4_t mm16(const float *X, int ldx, const float *Y,
 // channels of alpha, k, q (key side) and of v (value side), plus beta.
 template <typename T>
 struct Prefetch {
-    Raw8<T> a[2], k[2], q[2], v[2];
+    Raw8<T> a[2];         // alpha: row (lane) of the wave's channel slice, NA used
+    Raw8<T> k[2], q[2], v[2];
     T beta;   // raw: converted where it is used, so the load is not waited for at issue
 };
 
@@ -176,6 +200,8 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     using F = Frag<T>;
     static_assert(SM::BYTES <= 160 * 1024, "LDS plan exceeds 160 KB");
     constexpr int NCGK = DK / 8, NCGV = DV / 8;   // 8-channel groups
+    constexpr int CPW = DK / 8, NA = CPW / 8;      // P0: alpha channels per wave, 8-element loads per lane
+    static_assert(K1_THREADS == 512 && C == 64 && NA >= 1 && NA <= 2, "P0 maps chunk rows to the 64 lanes of 8 waves");
     constexpr int NKS = DK / 32;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -184,7 +210,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     const int nchunks = a.n_chunks, nbh = a.B * a.H;
     const int n_items = nbh * (a.c1 - a.c0);
 
-    float *Gs = reinterpret_cast<float *>(smem + SM::X1);
+    float *Gs = reinterpret_cast<float *>(smem + SM::X1);   // G, P0-P1 (Lm and Tm32 from P2 on)
     float *Lm = reinterpret_cast<float *>(smem + SM::X1);
     float *Tm32 = reinterpret_cast<float *>(smem + SM::X1 + SM::SZ_LM);
     T *Kr = reinterpret_cast<T *>(smem + SM::X2);
@@ -198,7 +224,6 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     float *Kh = reinterpret_cast<float *>(smem + SM::TB_KH);
     float *Fp = reinterpret_cast<float *>(smem + SM::TB_FP);
     float *Bt = reinterpret_cast<float *>(smem + SM::TB_BETA);
-    float *Tot = reinterpret_cast<float *>(smem + SM::TB_TOT);
 
     const T *gq = static_cast<const T *>(a.q);
     const T *gk = static_cast<const T *>(a.k);
@@ -211,33 +236,42 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     const int krp = tid / NCGK, kc0 = 8 * (tid % NCGK);
     const int vrp = tid / NCGV, vc0 = 8 * (tid % NCGV);
 
-    auto load_inputs = [&](int item, Prefetch<T> &pf) {
+    // The next chunk's inputs are loaded into the prefetch registers part by
+    // part, each as soon as the current chunk has consumed that part, so the
+    // loads drain through the memory pipeline under the compute of P1-P3.
+    constexpr int LD_A = 1, LD_KQ = 2, LD_V = 4;   // alpha and beta | k and q | v
+    auto load_inputs = [&](int item, Prefetch<T> &pf, int parts) {
         const int bh = item % nbh, n = a.c0 + item / nbh;
         const int b = bh / a.H, h = bh % a.H;
         const int t0 = n * C, nr = min(C, a.T - t0);
         // Rows past the end of the stream re-read the last row (in bounds) and
         // are masked where they are used: the loads never depend on the data
         // and no register is cleared behind a store still in flight.
+        if (parts & LD_A) {
+            const int r = min(l, nr - 1);
+            const size_t off = (((size_t)b * a.T + (t0 + r)) * a.H + h) * DK + CPW * wv;
+#pragma unroll
+            for (int j = 0; j < NA; ++j) pf.a[j].load(ga + off + 8 * j);
+            if (tid < C) pf.beta = gb[((size_t)b * a.T + (t0 + min(tid, nr - 1))) * a.H + h];
+        }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            if (key_task) {
+            if ((parts & LD_KQ) && key_task) {
                 const int r = min(2 * krp + e, nr - 1);
                 const size_t off = (((size_t)b * a.T + (t0 + r)) * a.H + h) * DK + kc0;
-                pf.a[e].load(ga + off);
                 pf.k[e].load(gk + off);
                 pf.q[e].load(gq + off);
             }
-            if (val_task) {
+            if ((parts & LD_V) && val_task) {
                 const int rv = min(2 * vrp + e, nr - 1);
                 pf.v[e].load(gv + (((size_t)b * a.T + (t0 + rv)) * a.H + h) * DV + vc0);
             }
         }
-        if (tid < C) pf.beta = gb[((size_t)b * a.T + (t0 + min(tid, nr - 1))) * a.H + h];
     };
 
     Prefetch<T> pf;
     int item = blockIdx.x;
-    if (item < n_items) load_inputs(item, pf);
+    if (item < n_items) load_inputs(item, pf, LD_A | LD_KQ | LD_V);
     // Enter the loop with the first prefetch retired, as every later iteration
     // is (see P5): the loop's waits then never cover the stores still in flight.
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
@@ -250,65 +284,72 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
         T *ws = reinterpret_cast<T *>(wsb);
         float *ws_gam = reinterpret_cast<float *>(wsb + WL::GAM_BYTE);
 
-        // ---- P0: G = cumsum(log2 alpha) over the chunk, per-channel tables ------
-        if (key_task) {
+        // ---- P0: G = cumsum(log2 alpha) over the chunk ------------------------------
+        // Lane l of wave w holds row l of channels CPW*w .. CPW*w + CPW-1, so the
+        // scan over the chunk's rows runs across the lanes of one wave (DPP
+        // shifts inside 16-lane rows, then row broadcasts) with no barrier.
+        {
+            float x[CPW];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int r = 2 * krp + e;
-                float al[8];
-                pf.a[e].get(al);
+            for (int j = 0; j < NA; ++j) {
+                float v[8];
+                pf.a[j].get(v);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) al[i] = r < nr ? hw_log2(al[i]) : 0.f;
-                *reinterpret_cast<float4 *>(Gs + r * SM::GS + kc0) = make_float4(al[0], al[1], al[2], al[3]);
-                *reinterpret_cast<float4 *>(Gs + r * SM::GS + kc0 + 4) = make_float4(al[4], al[5], al[6], al[7]);
+                for (int i = 0; i < 8; ++i) x[8 * j + i] = l < nr ? hw_log2(v[i]) : 0.f;
             }
+            wave_inclusive_sums<CPW>(x);
+            float *d = Gs + l * SM::GS + CPW * wv;
+#pragma unroll
+            for (int i = 0; i < CPW; i += 4) *reinterpret_cast<float4 *>(d + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
         }
         if (tid < C) Bt[tid] = tid < nr ? (float)pf.beta : 0.f;
         lds_barrier();
+        const bool more = item + (int)gridDim.x < n_items;
+        if (more) load_inputs(item + gridDim.x, pf, LD_A);
+        auto Grow = [&](int R) { return Gs + (R < 4 ? 16 * R + 8 : C - 1) * SM::GS; };   // R = 4: the last row
         {
-            // column scan: thread (partition, channel) sums its RPP rows in
-            // registers, then adds the totals of the earlier partitions
+            // 15 per-channel factors for the later phases: Pm[4], Kh[4], Fp[6], Gam
+            // (P1 computes its own Pm values: the tables are read from P2 on).
+            // The five G rows are read once, up front.
             const int c = tid % DK, part = tid / DK;
-            float gl[SM::RPP];
+            float gv[5];
 #pragma unroll
-            for (int i = 0; i < SM::RPP; ++i) gl[i] = Gs[(part * SM::RPP + i) * SM::GS + c];
+            for (int R = 0; R < 5; ++R) gv[R] = Grow(R)[c];
 #pragma unroll
-            for (int i = 1; i < SM::RPP; ++i) gl[i] += gl[i - 1];
-            Tot[part * DK + c] = gl[SM::RPP - 1];
-            lds_barrier();
-            float off = 0.f;
-            for (int p = 0; p < part; ++p) off += Tot[p * DK + c];
-#pragma unroll
-            for (int i = 0; i < SM::RPP; ++i) Gs[(part * SM::RPP + i) * SM::GS + c] = gl[i] + off;
-            lds_barrier();
-            auto Gat = [&](int r) { return Gs[r * SM::GS + c]; };
-            // 15 per-channel factors: Pm[4], Kh[4], Fp[6], Gam
-            for (int e = part; e < 15; e += SM::NPART) {
+            for (int j = 0; j < (15 + SM::NPART - 1) / SM::NPART; ++j) {
+                const int e = part + SM::NPART * j;
                 if (e < 4) {
-                    Pm[e * DK + c] = hw_exp2(Gat(16 * e + 8));
+                    Pm[e * DK + c] = hw_exp2(gv[e & 3]);
                 } else if (e < 8) {
-                    const int R = e - 4;
-                    Kh[R * DK + c] = hw_exp2(Gat(63) - Gat(16 * R + 8));
+                    Kh[(e - 4) * DK + c] = hw_exp2(gv[4] - gv[e & 3]);
                 } else if (e < 14) {
                     const int f = e - 8;
                     const int R = f < 1 ? 1 : (f < 3 ? 2 : 3);
                     const int S = f - fp_index(R, 0);
-                    Fp[f * DK + c] = hw_exp2(Gat(16 * R + 8) - Gat(16 * S + 8));
-                } else {
-                    ws_gam[gam_pos<DK>(c)] = hw_exp2(Gat(63));
+                    Fp[f * DK + c] = hw_exp2(gv[R] - gv[S]);
+                } else if (e == 14) {
+                    ws_gam[gam_pos<DK>(c)] = hw_exp2(gv[4]);
                 }
             }
-            lds_barrier();
         }
 
         // ---- P1: elementwise operands ----------------------------------------------
         if (key_task) {
-            const int s0 = 2 * krp, R = s0 >> 4, m = 16 * R + 8;
+            const int s0 = 2 * krp, R = s0 >> 4;
+            float gm[8], pm[8];   // G at the block midpoint 16R+8, and 2^G there
+            {
+                const float4 m0 = *reinterpret_cast<const float4 *>(Grow(R) + kc0);
+                const float4 m1 = *reinterpret_cast<const float4 *>(Grow(R) + kc0 + 4);
+                gm[0] = m0.x; gm[1] = m0.y; gm[2] = m0.z; gm[3] = m0.w;
+                gm[4] = m1.x; gm[5] = m1.y; gm[6] = m1.z; gm[7] = m1.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pm[i] = hw_exp2(gm[i]);
             float rhs[2][8];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int r = s0 + e;
-                float kx[8], qx[8], gr[8], gm[8];
+                float kx[8], qx[8];
                 pf.k[e].get(kx);
                 pf.q[e].get(qx);
 #pragma unroll
@@ -316,25 +357,16 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
                     kx[i] = r < nr ? kx[i] : 0.f;
                     qx[i] = r < nr ? qx[i] : 0.f;
                 }
-                const float4 g0 = *reinterpret_cast<const float4 *>(Gs + r * SM::GS + kc0);
-                const float4 g1 = *reinterpret_cast<const float4 *>(Gs + r * SM::GS + kc0 + 4);
-                const float4 m0 = *reinterpret_cast<const float4 *>(Gs + m * SM::GS + kc0);
-                const float4 m1 = *reinterpret_cast<const float4 *>(Gs + m * SM::GS + kc0 + 4);
-                gr[0] = g0.x; gr[1] = g0.y; gr[2] = g0.z; gr[3] = g0.w;
-                gr[4] = g1.x; gr[5] = g1.y; gr[6] = g1.z; gr[7] = g1.w;
-                gm[0] = m0.x; gm[1] = m0.y; gm[2] = m0.z; gm[3] = m0.w;
-                gm[4] = m1.x; gm[5] = m1.y; gm[6] = m1.z; gm[7] = m1.w;
                 const float br = Bt[r];
                 float kr[8], qr[8], kb[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const int c = kc0 + i;
-                    const float d = gr[i] - gm[i];
+                    const float d = Gs[r * SM::GS + kc0 + i] - gm[i];
                     const float e1 = hw_exp2(d), e2 = hw_exp2(-d);
                     kr[i] = kx[i] * e1;
                     qr[i] = qx[i] * e1;
                     kb[i] = kx[i] * e2;
-                    rhs[e][i] = br * kr[i] * Pm[R * DK + c];
+                    rhs[e][i] = br * kr[i] * pm[i];
                 }
                 st8f<T>(Kr + r * SM::KS + kc0, kr);
                 st8f<T>(Qr + r * SM::KS + kc0, qr);
@@ -343,6 +375,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) st2<T>(RK + krp * SM::RKS + 2 * (kc0 + i), rhs[0][i], rhs[1][i]);
         }
+        if (more) load_inputs(item + gridDim.x, pf, LD_KQ);
         if (val_task) {
             const int s0 = 2 * vrp;
             float vx0[8], vx1[8];
@@ -357,8 +390,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) st2<T>(RV + vrp * SM::RVS + 2 * (vc0 + i), b0 * vx0[i], b1 * vx1[i]);
         }
-        // the prefetch registers are consumed: start loading the next chunk
-        if (item + (int)gridDim.x < n_items) load_inputs(item + gridDim.x, pf);
+        if (more) load_inputs(item + gridDim.x, pf, LD_V);
         lds_barrier();
 
         // ---- P2: decayed K K^T (-> L) and (Q K^T)^T (-> workspace) on MFMA ----------
@@ -399,15 +431,16 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
         // ---- P3: Tm = (I + Diag(beta) A)^-1 in fp32 ------------------------------------
         if (wv == 0) {
             // diagonal blocks by forward substitution: lane = (block R, column j)
+            // (four partial sums per row keep the dependent chain short)
             const int R = l >> 4, j = l & 15;
             float x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float *Li = Lm + (16 * R + i) * SM::LS + 16 * R;
-                float s = (i == j) ? 1.f : 0.f;
+                float p[4] = {(i == j) ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int k2 = 0; k2 < i; ++k2) s = __builtin_fmaf(-Li[k2], x[k2], s);
-                x[i] = s;
+                for (int k2 = 0; k2 < i; ++k2) p[k2 & 3] = __builtin_fmaf(-Li[k2], x[k2], p[k2 & 3]);
+                x[i] = (p[0] + p[1]) + (p[2] + p[3]);
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) Tm32[(16 * R + i) * SM::LS + 16 * R + j] = x[i];
