@@ -394,9 +394,11 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
         lds_barrier();
 
         // ---- P2: decayed K K^T (-> L) and (Q K^T)^T (-> workspace) on MFMA ----------
-        for (int ti = wv; ti < 10; ti += 8) {
-            const int R = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
-            const int S = ti - R * (R + 1) / 2;
+        // waves 0-5: one off-diagonal tile (R, S) each (f = fp_index(R, S) = wave);
+        // waves 6, 7: two diagonal tiles each, which need no decay scaling
+        for (int t = 0; t < (wv < 6 ? 1 : 2); ++t) {
+            const int R = wv < 6 ? (wv < 1 ? 1 : wv < 3 ? 2 : 3) : 2 * (wv - 6) + t;
+            const int S = wv < 6 ? wv - R * (R - 1) / 2 : R;
             f32x4_t accA = zero4(), accB = zero4();
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -487,7 +489,10 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
             }
         }
         lds_barrier();
-        // off-diagonal, by distance d = R - S: Tm_RS = -D_R sum_{J=S}^{R-1} L_RJ Tm_JS
+        // off-diagonal, by distance d = R - S: Tm_RS = -D_R sum_{J=S}^{R-1} L_RJ Tm_JS.
+        // Wave S owns block (R, S) of each level; the intermediate sum goes
+        // through its own LDS scratch (one wave's LDS accesses complete in
+        // order), so only the levels are separated by barriers.
         for (int d = 1; d < 4; ++d) {
             float *sc = Scr + wv * 16 * SM::SC;
             const int R = wv + d, S = wv;
@@ -498,9 +503,8 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
                              col, g, y);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sc[(4 * g + i) * SM::SC + col] = y[i];
-            }
-            lds_barrier();
-            if (R < 4) {
+                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the scratch writes have completed
+                __builtin_amdgcn_wave_barrier();
                 const f32x4_t t = mm16(Tm32 + (16 * R) * SM::LS + 16 * R, SM::LS, sc, SM::SC, col, g, zero4());
 #pragma unroll
                 for (int i = 0; i < 4; ++i) Tm32[(16 * R + 4 * g + i) * SM::LS + 16 * S + col] = -t[i];
