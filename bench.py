@@ -2,16 +2,14 @@
 """Throughput of the conv + KDA token mixer forward on one MI355X.
 
 One step = kda_conv_forward (modality-aware short conv of q, k, v) followed by
-kda_forward (chunk transform and state pass, pipelined over chunk ranges),
-over one batch of the workload, inputs resident in HBM.  Prints one JSON line.
-With --isolated the step is the three kernels one after another on one stream
-(kda_conv_forward, kda_forward_chunks, kda_forward_scan).  The default workload is the 5-second 480x832 video stream
+kda_forward_chunks + kda_forward_scan (the two kernels of kda_forward) on one
+stream, over one batch of the workload, inputs resident in HBM.  Prints one
+JSON line.  The default workload is the 5-second 480x832 video stream
 (512 text tokens + a 21x30x52 latent-patch grid, T = 33272, 16 heads of
 dk = dv = 128, bf16 with fp32 accumulation).
 
 Per-kernel durations come from HIP events recorded on the launch stream
-between the three calls of the isolated sequence (the timed steps with
---isolated, else an isolated pass after them); the dominant kernel's roofline
+between the three calls over the timed steps; the dominant kernel's roofline
 uses the algorithmic bytes per launch of roofline_bytes().
 """
 from __future__ import annotations
@@ -40,9 +38,15 @@ KERNEL_SOURCES = {
     "scan": ("kda.hip", "mfma.h", "common.h", "launch.h"),
 }
 MEASURED_TRAFFIC = {
-    ("video_5s_480x832", "conv"): ("2b82e3bee3400eaf", 253082.2, 399264.0),
-    ("video_5s_480x832", "chunks"): ("1f87b38ef9c35f4d", 270468.0, 586560.1),
-    ("video_5s_480x832", "scan"): ("1f87b38ef9c35f4d", 293354.7, 133088.0),
+    ("video_5s_480x832", "conv"): ("7e198e465c710873", 253222.8, 399264.0),
+    ("video_5s_480x832", "chunks"): ("c5baddbeded9a8f1", 270460.7, 586560.3),
+    ("video_5s_480x832", "scan"): ("c5baddbeded9a8f1", 293354.0, 133088.0),
+}
+# Matrix-core operations per dispatch (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
+# SQ_INSTS_VALU_MFMA_MOPS_F32, each count is 512 flops), taken the same way.
+MEASURED_MFMA_MOPS = {
+    ("video_5s_480x832", "chunks"): ("c5baddbeded9a8f1", 46858240.0, 2129920.0),
+    ("video_5s_480x832", "scan"): ("c5baddbeded9a8f1", 115015680.0, 0.0),
 }
 
 
@@ -62,6 +66,14 @@ def measured_traffic(workload: str, kernel: str):
     if rec is None or rec[0] != source_digest(kernel):
         return None
     return int(round((rec[1] * FETCH_SCALE + rec[2] * WRITE_SCALE) * 1024))
+
+
+def measured_mfma_flops(workload: str, kernel: str):
+    """Counter-measured matrix-core flops per launch, or None if not taken on the current sources."""
+    rec = MEASURED_MFMA_MOPS.get((workload, kernel))
+    if rec is None or rec[0] != source_digest(kernel):
+        return None
+    return int(round((rec[1] + rec[2]) * 512))
 
 
 def roofline_bytes(cfg) -> dict:
@@ -156,9 +168,6 @@ def main() -> int:
     ap.add_argument("--cpu-frames", type=int, default=0,
                     help="latent frames in the CPU-baseline sample (0 = the whole stream)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--isolated", action="store_true",
-                    help="time conv, chunk transform and state pass one after another on one stream "
-                         "instead of the pipelined kda_forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (three times) and "
                          "exit: the reference kernel for scaling HBM byte counters")
@@ -199,8 +208,7 @@ def main() -> int:
     wv = (inp["w_vis_q"], inp["w_vis_k"], inp["w_vis_v"])
     stream = torch.cuda.current_stream()
 
-    def isolated_step(ev=None):
-        # the three kernels one after another on one stream, each alone on the chip
+    def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         kda.kda_conv_forward(desc, inp["q"], inp["k"], inp["v"], wt, wv, qc, kc, vc, stream=stream)
@@ -213,33 +221,17 @@ def main() -> int:
         if ev is not None:
             ev[3].record(stream)
 
-    def step(ev=None):
-        # the product path: conv, then kda_forward, which overlaps the chunk
-        # transform of each chunk range with the state pass of the previous one
-        if ev is not None:
-            ev[0].record(stream)
-        kda.kda_conv_forward(desc, inp["q"], inp["k"], inp["v"], wt, wv, qc, kc, vc, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        kda.kda_forward(desc, qc, kc, vc, inp["alpha"], inp["beta"], o=o, workspace=ws, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-
-    timed = isolated_step if args.isolated else step
     for _ in range(args.warmup):
-        timed()
+        step()
     torch.cuda.synchronize()
-    nev = 4 if args.isolated else 3
+    nev = 4
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        timed(events[i])
+        step(events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # Per-kernel durations: the timed steps themselves with --isolated, else an
-    # isolated pass after them (inside kda_forward the state pass runs in
-    # chunk ranges on a second stream, beside the chunk transform).
     step_ms = sorted(e[0].elapsed_time(e[-1]) for e in events)
     # cold steps: a 1 GiB fill before each one evicts L2 and the 256 MB Infinity Cache
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -247,25 +239,14 @@ def main() -> int:
     cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n_cold)]
     for i in range(n_cold):
         scratch.fill_(i & 255)
-        timed(cold_ev[i])
+        step(cold_ev[i])
     torch.cuda.synchronize()
     cold_ms = sorted(e[0].elapsed_time(e[-1]) for e in cold_ev)
     del scratch
     copy_gbs = copy_bandwidth(torch)
 
     names = ("conv", "chunks", "scan")
-    if args.isolated:
-        kev = events
-    else:
-        stage_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in events) / args.steps for j in range(2)]
-        n_iso = max(3, args.steps // 4)
-        for _ in range(2):
-            isolated_step()
-        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_iso)]
-        for i in range(n_iso):
-            isolated_step(kev[i])
-        torch.cuda.synchronize()
-    ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in kev) / len(kev) for j, n in enumerate(names)}
+    ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in events) / args.steps for j, n in enumerate(names)}
     rb = roofline_bytes(cfg)
     fl = mfma_flops(cfg)
     kernels = {}
@@ -276,8 +257,8 @@ def main() -> int:
                       "frac_measured_copy": round(gbs / copy_gbs, 4)}
         if n in fl:
             tf = fl[n] / (ms[n] * 1e-3) / 1e12
-            kernels[n].update({"mfma_flop": fl[n], "TFLOP/s": round(tf, 1),
-                               "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFS, 4)})
+            kernels[n].update({"mfma_flop": fl[n], "mfma_flop_counted": measured_mfma_flops(cfg.name, n),
+                               "TFLOP/s": round(tf, 1), "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFS, 4)})
     dom = max(names, key=lambda n: ms[n])
     ms_step = elapsed / args.steps * 1e3
     tokens = cfg.B * cfg.T
@@ -304,10 +285,6 @@ def main() -> int:
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac_hbm"],
                      "traffic": measured_traffic(cfg.name, dom)},
         "kernels": kernels,
-        "kernel_timing": "isolated steps" if args.isolated else
-                         "isolated pass after the timed steps (each kernel alone on the chip)",
-        "timed_step": {"conv_us": round(stage_ms[0] * 1e3, 2), "kda_forward_us": round(stage_ms[1] * 1e3, 2)}
-                      if not args.isolated else None,
         "step_ms": {"median": round(step_ms[len(step_ms) // 2], 4), "min": round(step_ms[0], 4),
                     "cold_median": round(cold_ms[len(cold_ms) // 2], 4), "cold_min": round(cold_ms[0], 4),
                     "cold_tokens_per_s": round(tokens / (cold_ms[len(cold_ms) // 2] * 1e-3), 1),

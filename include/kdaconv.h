@@ -102,9 +102,9 @@ int kda_conv_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv,
                      void *q_out, void *k_out, void *v_out, void *hip_stream);
 
 /* Bytes of device workspace kda_forward needs for this shape: the chunk
- * transforms of every (batch, head, chunk), then an fp32 [B, H, dk, dv] state
- * carried between chunk ranges.  0 on bad or unsupported arguments, including
- * shapes whose per-(batch, head) transforms would reach 4 GiB. */
+ * transforms of every (batch, head, chunk).  0 on bad or unsupported
+ * arguments, including shapes whose per-(batch, head) transforms would reach
+ * 4 GiB. */
 size_t kda_forward_workspace_size(const kda_stream_desc *desc, int B, int H, int dk,
                                   int dv, kda_dtype dtype);
 
@@ -122,14 +122,6 @@ size_t kda_forward_workspace_size(const kda_stream_desc *desc, int B, int H, int
  * with the state held on chip.  `workspace` (device, >= the size returned by
  * kda_forward_workspace_size) is scratch owned by the caller; its contents are
  * undefined afterwards.  initial_state may alias final_state.
- * For 64 or more chunks the two kernels are pipelined over chunk ranges: the
- * chunk transform of a range runs on hip_stream while the state pass of the
- * previous range runs on a side stream that the library creates (default
- * priority, once per device, kept until the process ends), joined back into
- * hip_stream by events; the state passes between ranges through the
- * workspace.  Work enqueued on hip_stream afterwards sees every result; the
- * results are bit-identical to kda_forward_chunks + kda_forward_scan.  Calls
- * from several host threads are serialised while they enqueue.
  */
 int kda_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv,
                 kda_dtype dtype, const void *q, const void *k, const void *v,
@@ -139,9 +131,8 @@ int kda_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv,
 
 /*
  * The two kernels of kda_forward, callable separately with the same shapes,
- * checks and workspace: kda_forward(...) computes exactly what
- * kda_forward_chunks(...) followed by kda_forward_scan(...) on one stream
- * computes, each launched over all chunks.  kda_forward_chunks forms
+ * checks and workspace: kda_forward(...) is exactly kda_forward_chunks(...)
+ * followed by kda_forward_scan(...) on one stream.  kda_forward_chunks forms
  * every chunk's UT/WY transform (fully parallel over chunks) and writes it to
  * the workspace; kda_forward_scan walks the chunks of each (batch, head) in
  * order, carrying the state, and writes o and optionally final_state.  The

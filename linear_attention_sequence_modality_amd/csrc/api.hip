@@ -3,8 +3,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <mutex>
-
 #include "../../include/kdaconv.h"
 #include "launch.h"
 
@@ -51,14 +49,6 @@ int check_shape(const kda_stream_desc *d, int B, int H, int dk, int dv, int dtyp
     *T_out = T;
     return KDA_OK;
 }
-
-// The workspace holds the chunk transforms of every (batch, head, chunk),
-// then an fp32 [B, H, dk, dv] state that carries the scan from one chunk
-// range to the next when kda_forward pipelines its two kernels.
-size_t carry_offset(size_t per, int B, int H, int64_t nch) {
-    return (per * (size_t)B * (size_t)H * (size_t)nch + 255) / 256 * 256;
-}
-size_t carry_bytes(int B, int H, int dk, int dv) { return (size_t)B * H * dk * dv * sizeof(float); }
 
 }  // namespace
 
@@ -135,7 +125,7 @@ size_t kda_forward_workspace_size(const kda_stream_desc *desc, int B, int H, int
     const int64_t nch = (T + kdaconv::kChunk - 1) / kdaconv::kChunk;
     // the state pass addresses one (batch, head)'s chunks with 32-bit offsets
     if ((int64_t)per * nch >= ((int64_t)1 << 32)) return 0;
-    return carry_offset(per, B, H, nch) + carry_bytes(B, H, dk, dv);
+    return per * (size_t)B * (size_t)H * (size_t)nch;
 }
 
 }  // extern "C"
@@ -210,88 +200,7 @@ int prepare_kda(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_d
     out->n_chunks = (int)((T + kdaconv::kChunk - 1) / kdaconv::kChunk);
     out->c0 = 0;
     out->c1 = out->n_chunks;
-    out->k1_grid = 0;
     return KDA_OK;
-}
-
-// Chunk ranges of the pipelined kda_forward: at least kMinPieceChunks chunks
-// each, at most kMaxPieces ranges.
-constexpr int kMinPieceChunks = 32, kMaxPieces = 8;
-int pipeline_pieces(int n_chunks) {
-    const int p = n_chunks / kMinPieceChunks;
-    return p < 1 ? 1 : p > kMaxPieces ? kMaxPieces : p;
-}
-
-// Per-device side stream and events of the pipelined kda_forward, created on
-// first use and kept until the process ends.  One mutex serialises the
-// enqueue sequences of concurrent host threads.
-struct Pipe {
-    hipStream_t side = nullptr;
-    hipEvent_t ev[kMaxPieces + 2] = {};
-};
-std::mutex g_pipe_mutex;
-Pipe g_pipes[64];
-
-hipError_t get_pipe(Pipe **out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    Pipe &p = g_pipes[dev];
-    if (!p.side) {
-        for (auto &ev : p.ev) {
-            e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-            if (e != hipSuccess) return e;
-        }
-        e = hipStreamCreateWithFlags(&p.side, hipStreamNonBlocking);
-        if (e != hipSuccess) return e;
-    }
-    *out = &p;
-    return hipSuccess;
-}
-
-// kda_forward's schedule.  The state pass of one (batch, head) is a chain of
-// dependent chunk steps that occupies one compute unit per 16 value columns
-// and leaves the rest of the chip idle.  So the chunks are split into ranges:
-// the chunk transform of range k (caller's stream) overlaps the state pass of
-// range k - 1 (side stream), which waits for it by event and carries the
-// state through the workspace.
-hipError_t launch_pipelined(KdaArgs a, bool bf16, hipStream_t st) {
-    const int pieces = pipeline_pieces(a.n_chunks);
-    if (pieces == 1) {
-        hipError_t e = kdaconv::launch_kda_chunks(a, bf16, st);
-        return e != hipSuccess ? e : kdaconv::launch_kda_scan(a, bf16, st);
-    }
-    std::lock_guard<std::mutex> lock(g_pipe_mutex);
-    Pipe *p = nullptr;
-    hipError_t e = get_pipe(&p);
-    if (e != hipSuccess) return e;
-    const size_t per = kdaconv::kda_chunk_ws_bytes(a.dk, a.dv, bf16);
-    float *carry = reinterpret_cast<float *>(static_cast<char *>(a.ws) + carry_offset(per, a.B, a.H, a.n_chunks));
-    const float *s0 = a.s0;
-    float *sT = a.sT;
-    // the side stream starts after the caller's earlier work
-    if ((e = hipEventRecord(p->ev[kMaxPieces], st)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(p->side, p->ev[kMaxPieces], 0)) != hipSuccess) return e;
-    const int scan_wgs = kdaconv::scan_workgroups(a);
-    const int free_cus = kdaconv::num_cus() - scan_wgs;
-    for (int k = 0; k < pieces; ++k) {
-        KdaArgs r = a;
-        r.c0 = (int)((int64_t)a.n_chunks * k / pieces);
-        r.c1 = (int)((int64_t)a.n_chunks * (k + 1) / pieces);
-        // from the second range on, the state pass of the previous range holds
-        // scan_wgs compute units
-        r.k1_grid = k > 0 && free_cus > 0 ? free_cus : 0;
-        if ((e = kdaconv::launch_kda_chunks(r, bf16, st)) != hipSuccess) return e;
-        if ((e = hipEventRecord(p->ev[k], st)) != hipSuccess) return e;
-        if ((e = hipStreamWaitEvent(p->side, p->ev[k], 0)) != hipSuccess) return e;
-        r.s0 = k == 0 ? s0 : carry;
-        r.sT = k == pieces - 1 ? sT : carry;
-        if ((e = kdaconv::launch_kda_scan(r, bf16, p->side)) != hipSuccess) return e;
-    }
-    // the caller's stream continues after the last state pass
-    if ((e = hipEventRecord(p->ev[kMaxPieces + 1], p->side)) != hipSuccess) return e;
-    return hipStreamWaitEvent(st, p->ev[kMaxPieces + 1], 0);
 }
 
 }  // namespace
@@ -306,9 +215,10 @@ int kda_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_d
     int rc = prepare_kda(desc, B, H, dk, dv, dtype, q, k, v, alpha, beta, initial_state, final_state,
                          o, workspace, workspace_bytes, true, true, &a);
     if (rc != KDA_OK || B == 0) return rc;
-    return launch_pipelined(a, dtype == KDA_BF16, static_cast<hipStream_t>(hip_stream)) == hipSuccess
-               ? KDA_OK
-               : KDA_ERR_HIP;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (kdaconv::launch_kda_chunks(a, dtype == KDA_BF16, st) != hipSuccess) return KDA_ERR_HIP;
+    if (kdaconv::launch_kda_scan(a, dtype == KDA_BF16, st) != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
 }
 
 int kda_forward_chunks(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,

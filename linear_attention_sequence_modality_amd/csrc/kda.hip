@@ -1017,15 +1017,15 @@ hipError_t launch_chunks_typed(const KdaArgs &a, hipStream_t stream) {
         attr_set = true;
     }
     const int items = a.B * a.H * (a.c1 - a.c0);
-    const int cap = a.k1_grid > 0 && a.k1_grid < num_cus() ? a.k1_grid : num_cus();
-    const int grid = items < cap ? items : cap;
+    const int grid = items < num_cus() ? items : num_cus();
     hipLaunchKernelGGL((kda_intra_kernel<T, DK, DV>), dim3(grid), dim3(K1_THREADS), SM::BYTES, stream, a);
     return hipGetLastError();
 }
 
 template <typename T, int DK, int DV>
 hipError_t launch_scan_typed(const KdaArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((kda_state_kernel<T, DK, DV>), dim3(scan_workgroups(a)), dim3(kScanThreads), 0, stream, a);
+    const int n2 = a.B * a.H * (DV / 16);
+    hipLaunchKernelGGL((kda_state_kernel<T, DK, DV>), dim3(n2), dim3(kScanThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1056,7 +1056,6 @@ int num_cus() {
     return cus[dev];
 }
 
-int scan_workgroups(const KdaArgs &a) { return a.B * a.H * (a.dv / 16); }
 
 size_t kda_chunk_ws_bytes(int dk, int dv, bool bf16) {
 #define WS_CASE(DK_, DV_)                                                                          \

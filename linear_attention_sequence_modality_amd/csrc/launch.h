@@ -30,7 +30,6 @@ struct KdaArgs {
     int B, T, H, dk, dv;
     int n_chunks;        // ceil(T / kChunk)
     int c0, c1;          // chunks [c0, c1) of every (batch, head) processed by one launch
-    int k1_grid;         // chunk-transform workgroups (0: one per compute unit)
 };
 
 // Workspace bytes for one (batch, head, chunk).
@@ -38,8 +37,7 @@ size_t kda_chunk_ws_bytes(int dk, int dv, bool bf16);
 // Kernel 1 (chunk transform -> workspace) and kernel 2 (ordered state pass).
 hipError_t launch_kda_chunks(const KdaArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_kda_scan(const KdaArgs &a, bool bf16, hipStream_t stream);
-// Workgroups of one state-pass launch, and compute units of the current device.
-int scan_workgroups(const KdaArgs &a);
+// Compute units of the current device.
 int num_cus();
 
 }  // namespace kdaconv

@@ -148,14 +148,11 @@ def test_split_and_resume_matches_one_shot():
 
 @pytest.mark.timeout(120)
 @pytest.mark.parametrize("T,B", [(64 * 70 + 13, 1), (64 * 300 - 5, 2)])
-def test_pipelined_forward_equals_the_two_kernels(T, B):
-    """kda_forward splits the chunks into ranges (2 and 8 here) and overlaps the
-    chunk transform of one range with the state pass of the previous range on a
-    second stream, carrying the state through the workspace.  Same arithmetic
-    in the same order as kda_forward_chunks + kda_forward_scan: equal bit for
-    bit, final state included, with an initial state that aliases it."""
+def test_forward_equals_the_two_kernels(T, B):
+    """kda_forward is kda_forward_chunks + kda_forward_scan: equal bit for bit,
+    final state included, with an initial state that aliases the final one."""
     cfg = _small("pipe", B=B, n_text=T, grid=(0, 0, 0))
-    say("case pipelined T=%d B=%d chunks=%d" % (T, B, (T + 63) // 64))
+    say("case forward vs two kernels T=%d B=%d chunks=%d" % (T, B, (T + 63) // 64))
     inp = to_dev(make_inputs(cfg))
     d = desc_of(cfg)
     x = [inp[k] for k in ("q", "k", "v", "alpha", "beta")]
@@ -180,7 +177,7 @@ def test_pipelined_forward_equals_the_two_kernels(T, B):
                                   heads_slice(host["beta"][..., None], (1,))[..., 0],
                                   S0=s0[:, 1:2].double().cpu().numpy(), want_state=False)
     e = rel(heads_slice(o2, (1,)), ro)
-    say("  pipelined rel err o %.2e" % e)
+    say("  forward rel err o %.2e" % e)
     assert e <= TOL["bf16"]
 
 
