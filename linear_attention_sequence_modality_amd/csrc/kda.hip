@@ -18,10 +18,11 @@
 // to the workspace in the exact register-fragment order kernel 2 consumes.
 // The next chunk's inputs are loaded into registers while the current chunk
 // is transformed.
-// Kernel 2 (kda_state_kernel: one wave per (batch, head, 16-column slice of
-// dv)) keeps its state slice in registers, feeds it to the matrix cores
-// without any LDS exchange or barrier, and streams the workspace through
-// registers one chunk ahead.
+// Kernel 2 (kda_state_kernel: one 7-wave workgroup per (batch, head,
+// 16-column slice of dv)) keeps its state slice in the registers of one
+// recurrence wave and feeds it to the matrix cores without any reshuffle; a
+// loader wave stages the chunk operands in an LDS ring, four output waves and
+// a store wave form and write o from the state handed over each step.
 //
 // Decay factorisation: 2^(G_r - G_s) for s <= r is split around the midpoint
 // m(R) = 16R + 8 of the 16-row sub-block R of row r:
@@ -567,10 +568,12 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
 }
 
 // ---- kernel 2: sequential state pass ------------------------------------------------
-// One 3-wave workgroup per (batch, head, 16 value columns):
+// One 7-wave workgroup per (batch, head, 16 value columns):
 //   wave 0 (recurrence): S <- Diag(Gam) S + Kh^T (Ut - W S), chunk after chunk;
-//   wave 1 (output):     O^T = S^T Qt^T + U^T Bq^T from the S and U wave 0 used;
-//   wave 2 (store):      writes O to o.
+//   waves 1, 2, 3, 5 (output): O^T = S^T Qt^T + U^T Bq^T from the S and U wave 0
+//                        used, chunk n on output wave n mod 4;
+//   wave 4 (store):      writes O to o;
+//   wave 6 (loader):     stages W, Kh^T, Ut and Gam of the coming chunks in LDS.
 // Lane l = 16 g + col of wave 0 holds rows 16 dt + 4 g + i (i = 0..3) of
 // value column col of S in fp32: S is kept as DK/16 accumulator tiles.  Two
 // tiles side by side are directly an MFMA operand whose 32 k-slots are the
@@ -578,8 +581,8 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
 // unchanged, the A operand of S^T Qt^T -- so the state never leaves wave 0's
 // registers; U becomes an operand the same way (k = token).  The workspace
 // fragments are stored in the matching k order.
-// Wave 0 hands the bf16 operands of S and U to wave 1, and wave 1 the output
-// tiles to wave 2, through small LDS rings guarded by counters: a wave waits
+// Wave 0 hands the bf16 operands of S and U to the output waves, and they the
+// output tiles to the store wave, through small LDS rings guarded by counters: a wave waits
 // only when its ring is empty (consumer) or full (producer).  Keeping loads
 // and stores in different waves lets every wave keep its loads in flight
 // across chunk steps: a wave with both outstanding would drain everything at
