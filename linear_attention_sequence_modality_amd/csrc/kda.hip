@@ -711,16 +711,17 @@ __device__ __forceinline__ void wait_counter_dma(int *ctr, int target, int &budg
 
 // Wave roles of the state pass.  Waves are spread over the four SIMDs in
 // turn, so the store wave (little work) shares SIMD 0 with the recurrence.
-constexpr int kOutWaves = 4;          // output waves; chunk n goes to output wave n % kOutWaves
-constexpr int kStoreWave = 4, kLoaderWave = 6;
+constexpr int kOutWaves = 2;          // output waves; chunk n goes to output wave n % kOutWaves
+constexpr int kLoaders = 4;           // loader waves; chunk p goes to loader p % kLoaders
+constexpr int kStoreWave = 7, kLoaderWave0 = 3;   // loaders are waves 3..6
 __device__ __forceinline__ int out_slot(int wave) {   // output wave index, or -1
-    return wave >= 1 && wave <= 3 ? wave - 1 : wave == 5 ? 3 : -1;
+    return wave == 1 || wave == 2 ? wave - 1 : -1;
 }
 constexpr int kRing = 4;              // chunk steps buffered between recurrence, output, store
 static_assert(kRing % kOutWaves == 0, "each ring slot belongs to one output wave");
 constexpr int kOpRing = 3;            // chunks of recurrence operands staged in LDS
 constexpr int kPollBudget = 1 << 24;  // LDS polls per wave per launch
-constexpr int kScanThreads = 448;     // recurrence, four output waves, store, loader
+constexpr int kScanThreads = 512;     // recurrence, two output waves, four loaders, store
 
 // s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding: vmcnt split over
 // bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima).
@@ -759,9 +760,9 @@ __global__ __launch_bounds__(kScanThreads) void kda_state_kernel(KdaArgs a) {
     //   kSuCons  + parity: S/U slot read (output wave of that parity)
     //   kOProd   + parity: O tile written (output wave of that parity)
     //   kOCons   O tile read (store)
-    //   kOpProd  operands staged (loader), kOpCons operands read (recurrence)
+    //   kOpProd  + loader: chunks staged by that loader, kOpCons operands read (recurrence)
     constexpr int kSuProd = 0, kSuCons = 1, kOProd = kSuCons + kOutWaves, kOCons = kOProd + kOutWaves,
-                  kOpProd = kOCons + 1, kOpCons = kOpProd + 1, kNumCtr = kOpCons + 1;
+                  kOpProd = kOCons + 1, kOpCons = kOpProd + kLoaders, kNumCtr = kOpCons + 1;
     __shared__ int ctr[kNumCtr];
     if (threadIdx.x < kNumCtr) ctr[threadIdx.x] = 0;
     __syncthreads();
@@ -782,35 +783,52 @@ __global__ __launch_bounds__(kScanThreads) void kda_state_kernel(KdaArgs a) {
     const unsigned lane8 = (unsigned)l * 8 * ES;   // lane's fragment inside a [64][8] block
     auto cbase = [&](int i) { return (unsigned)(a.c0 + i) * (unsigned)WL::BYTES; };
 
-    if (wave == kLoaderWave) {
-        // ---------------- loader: recurrence operands -> LDS ----------------
-        // Copies the chunk's W, Kh^T, Ut slice and Gam ranges byte for byte
-        // with direct-to-LDS loads (16 bytes per lane, 1 KB per instruction),
-        // kOpRing - 1 chunks ahead of the recurrence.  Loads retire in order,
-        // so after issuing chunk p, vmcnt(NI) means chunk p - 1 has landed.
-        auto copy = [&](char *dst, unsigned src, int bytes, unsigned soff) {
+    if (wave >= kLoaderWave0 && wave < kLoaderWave0 + kLoaders) {
+        // ---------------- loaders: recurrence operands -> LDS ----------------
+        // Loader q takes chunks p = q, q + kLoaders, ...: it loads the chunk's
+        // W, Kh^T, Ut slice and Gam into its registers (16 bytes per lane,
+        // 1 KB per instruction), waits until the chunk's ring slot is free,
+        // copies the registers into the slot and signals, then loads its next
+        // chunk.  With kLoaders waves each holding a chunk in flight, the loads
+        // of chunk p are issued about kLoaders + kOpRing - 1 chunk steps before
+        // the recurrence reads it, which covers the memory latency.
+        const int q = wave - kLoaderWave0;
+        u32x4_t r[SL::NI];
+        int nload = 0;   // chunks this loader has staged
+        auto load = [&](int p) {
+            const unsigned c = cbase(p);
+            int k = 0;
+            auto seg = [&](unsigned src, int bytes) {
 #pragma unroll
-            for (int i = 0; i < (bytes + 1023) / 1024; ++i)
-                if (i * 1024 + l * 16 < bytes)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(wsr, (lds_void_t *)(dst + i * 1024), 16,
-                                                             src + (unsigned)(i * 1024 + l * 16), soff, 0, 0);
+                for (int i = 0; i < (bytes + 1023) / 1024; ++i, ++k)
+                    r[k] = __builtin_amdgcn_raw_buffer_load_b128(wsr, src + (unsigned)(i * 1024 + l * 16), c, 0);
+            };
+            seg((unsigned)(WL::W * ES), SL::W_B);
+            seg((unsigned)(WL::KH * ES), SL::K_B);
+            seg((unsigned)((WL::U + (size_t)jt * 64 * 16) * ES), SL::U_B);
+            seg((unsigned)WL::GAM_BYTE, SL::G_B);
+        };
+        auto stage = [&](int p) {
+            char *slot = op_ring[p % kOpRing];
+            int k = 0;
+            auto seg = [&](int off, int bytes) {
+#pragma unroll
+                for (int i = 0; i < (bytes + 1023) / 1024; ++i, ++k)
+                    if (i * 1024 + l * 16 < bytes)
+                        *reinterpret_cast<u32x4_t *>(slot + off + i * 1024 + l * 16) = r[k];
+            };
+            seg(0, SL::W_B);
+            seg(SL::W_B, SL::K_B);
+            seg(SL::W_B + SL::K_B, SL::U_B);
+            seg(SL::W_B + SL::K_B + SL::U_B, SL::G_B);
         };
 #pragma unroll 1
-        for (int p = 0; p < nchunks; ++p) {
-            if (p >= kOpRing) wait_counter_dma(&ctr[kOpCons], p - kOpRing + 1, budget);   // slot's last chunk read
-            char *slot = op_ring[p % kOpRing];
-            const unsigned c = cbase(p);
-            copy(slot, (unsigned)(WL::W * ES), SL::W_B, c);
-            copy(slot + SL::W_B, (unsigned)(WL::KH * ES), SL::K_B, c);
-            copy(slot + SL::W_B + SL::K_B, (unsigned)((WL::U + (size_t)jt * 64 * 16) * ES), SL::U_B, c);
-            copy(slot + SL::W_B + SL::K_B + SL::U_B, (unsigned)WL::GAM_BYTE, SL::G_B, c);
-            if (p >= 1) {
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(SL::NI));   // chunk p - 1 has landed
-                lds_counter_write(&ctr[kOpProd], p);
-            }
+        for (int p = q; p < nchunks; p += kLoaders) {
+            load(p);
+            if (p >= kOpRing) wait_counter(&ctr[kOpCons], p - kOpRing + 1, budget);   // slot's last chunk read
+            stage(p);
+            signal_counter(&ctr[kOpProd + q], ++nload);
         }
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        lds_counter_write(&ctr[kOpProd], nchunks);
     } else if (wave == 0) {
         // ---------------- recurrence ----------------
         f32x4_t S[NDT];
@@ -851,7 +869,9 @@ __global__ __launch_bounds__(kScanThreads) void kda_state_kernel(KdaArgs a) {
             gam = *reinterpret_cast<const float2 *>(op + SL::W_B + SL::K_B + SL::U_B +
                                                     4 * (g * (DK / 4) + 2 * min(col, DK / 8 - 1)));
         };
-        wait_counter(&ctr[kOpProd], 1, budget);
+        // chunk n is staged once loader n % kLoaders has staged n / kLoaders + 1 chunks
+        auto wait_staged = [&](int n) { wait_counter(&ctr[kOpProd + n % kLoaders], n / kLoaders + 1, budget); };
+        wait_staged(0);
         read_w(0);
         read_k(0);
 #pragma unroll 1
@@ -910,7 +930,7 @@ __global__ __launch_bounds__(kScanThreads) void kda_state_kernel(KdaArgs a) {
             // chunk n's operands are all in registers: its ring slot may be restaged
             signal_counter(&ctr[kOpCons], n + 1);
             if (n + 1 < nchunks) {
-                wait_counter(&ctr[kOpProd], n + 2, budget);   // chunk n+1's operands are staged
+                wait_staged(n + 1);
                 read_w(n + 1);
                 read_k(n + 1);
             }
@@ -924,11 +944,12 @@ __global__ __launch_bounds__(kScanThreads) void kda_state_kernel(KdaArgs a) {
         }
     } else if (out_slot(wave) >= 0) {
         // ---------------- output: O^T = S^T Qt^T + U^T Bq^T ----------------
-        // the output waves take chunks in turn, so each has kOutWaves chunk
-        // steps to bring in its Qt and Bq operands
+        // The output waves take chunks in turn.  Each holds the Qt and Bq
+        // operands of its next two chunks in two register sets, so their loads
+        // go out 2 * kOutWaves chunk steps before use.
         const int par = out_slot(wave);
-        F Qf[4][NKS], Bf[6];
-        auto load_qb = [&](int n) {
+        F Qa[4][NKS], Ba[6], Qb[4][NKS], Bb[6];
+        auto load_qb = [&](int n, F (&Qf)[4][NKS], F (&Bf)[6]) {
             const unsigned c = cbase(n);
 #pragma unroll
             for (int R = 0; R < 4; ++R)
@@ -941,36 +962,50 @@ __global__ __launch_bounds__(kScanThreads) void kda_state_kernel(KdaArgs a) {
             Bf[4] = B::frag(wsr, lane8, c + (unsigned)(WL::BT + 5 * 512) * ES);
             Bf[5] = B::frag(wsr, lane8, c + (unsigned)(WL::BT + 7 * 512) * ES);
         };
-        load_qb(min(par, last));
-#pragma unroll 1
-        for (int n = par; n < nchunks; n += kOutWaves) {
-            wait_counter(&ctr[kSuProd], n + 1, budget);
-            F(&slot)[NKS + 2][64] = su_ring[n % kRing];
-            F Sb[NKS], Ub[2];
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) Sb[ks] = slot[ks][l];
-            Ub[0] = slot[NKS][l];
-            Ub[1] = slot[NKS + 1][l];
+        // one chunk with the operand set (Qf, Bf), which is then reloaded with
+        // chunk n + 2 * kOutWaves (clamped: the load count per chunk stays fixed)
+        auto chunk = [&](int n, F (&Qf)[4][NKS], F (&Bf)[6]) {
+            const bool live = n < nchunks;
             f32x4_t O[4];
+            if (live) {
+                wait_counter(&ctr[kSuProd], n + 1, budget);
+                F(&slot)[NKS + 2][64] = su_ring[n % kRing];
+                F Sb[NKS], Ub[2];
 #pragma unroll
-            for (int R = 0; R < 4; ++R) O[R] = zero4();
+                for (int ks = 0; ks < NKS; ++ks) Sb[ks] = slot[ks][l];
+                Ub[0] = slot[NKS][l];
+                Ub[1] = slot[NKS + 1][l];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
+                for (int R = 0; R < 4; ++R) O[R] = zero4();
 #pragma unroll
-                for (int R = 0; R < 4; ++R) O[R] = mma(Sb[ks], Qf[R][ks], O[R]);
-            // causal inside the chunk: token block R sees token k-steps kt <= R/2
+                for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-            for (int R = 0; R < 4; ++R) O[R] = mma(Ub[0], Bf[R], O[R]);
-            O[2] = mma(Ub[1], Bf[4], O[2]);
-            O[3] = mma(Ub[1], Bf[5], O[3]);
-            signal_counter(&ctr[kSuCons + par], n + 1);   // slot reads are complete (the MFMAs consumed them)
+                    for (int R = 0; R < 4; ++R) O[R] = mma(Sb[ks], Qf[R][ks], O[R]);
+                // causal inside the chunk: token block R sees token k-steps kt <= R/2
+#pragma unroll
+                for (int R = 0; R < 4; ++R) O[R] = mma(Ub[0], Bf[R], O[R]);
+                O[2] = mma(Ub[1], Bf[4], O[2]);
+                O[3] = mma(Ub[1], Bf[5], O[3]);
+                signal_counter(&ctr[kSuCons + par], n + 1);   // slot reads are complete (the MFMAs consumed them)
+            }
             __builtin_amdgcn_sched_barrier(0);
-            load_qb(min(n + kOutWaves, last));
+            load_qb(min(n + 2 * kOutWaves, last), Qf, Bf);
             __builtin_amdgcn_sched_barrier(0);
-            if (n >= kRing) wait_counter(&ctr[kOCons], n + 1 - kRing, budget);
+            if (live) {
+                if (n >= kRing) wait_counter(&ctr[kOCons], n + 1 - kRing, budget);
 #pragma unroll
-            for (int R = 0; R < 4; ++R) o_ring[n % kRing][R][l] = O[R];
-            signal_counter(&ctr[kOProd + par], n + 1);
+                for (int R = 0; R < 4; ++R) o_ring[n % kRing][R][l] = O[R];
+                signal_counter(&ctr[kOProd + par], n + 1);
+            }
+        };
+        load_qb(min(par, last), Qa, Ba);
+        __builtin_amdgcn_sched_barrier(0);
+        load_qb(min(par + kOutWaves, last), Qb, Bb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
+        for (int n = par; n < nchunks; n += 2 * kOutWaves) {
+            chunk(n, Qa, Ba);
+            chunk(n + kOutWaves, Qb, Bb);
         }
     } else if (wave == kStoreWave) {
         // ---------------- store ----------------
