@@ -38,15 +38,15 @@ KERNEL_SOURCES = {
     "scan": ("kda.hip", "mfma.h", "common.h", "launch.h"),
 }
 MEASURED_TRAFFIC = {
-    ("video_5s_480x832", "conv"): ("7e198e465c710873", 253222.8, 399264.0),
-    ("video_5s_480x832", "chunks"): ("c5baddbeded9a8f1", 270460.7, 586560.3),
-    ("video_5s_480x832", "scan"): ("c5baddbeded9a8f1", 293354.0, 133088.0),
+    ("video_5s_480x832", "conv"): ("7e198e465c710873", 253085.4, 399264.0),
+    ("video_5s_480x832", "chunks"): ("9c7045035b68aa3e", 270461.1, 586560.1),
+    ("video_5s_480x832", "scan"): ("9c7045035b68aa3e", 293363.9, 133091.6),
 }
 # Matrix-core operations per dispatch (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
 # SQ_INSTS_VALU_MFMA_MOPS_F32, each count is 512 flops), taken the same way.
 MEASURED_MFMA_MOPS = {
-    ("video_5s_480x832", "chunks"): ("c5baddbeded9a8f1", 46858240.0, 2129920.0),
-    ("video_5s_480x832", "scan"): ("c5baddbeded9a8f1", 115015680.0, 0.0),
+    ("video_5s_480x832", "chunks"): ("9c7045035b68aa3e", 46858240.0, 2129920.0),
+    ("video_5s_480x832", "scan"): ("9c7045035b68aa3e", 115015680.0, 0.0),
 }
 
 
