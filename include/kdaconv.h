@@ -101,6 +101,30 @@ int kda_conv_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv,
                      const void *const w_text[3], const void *const w_vis[3],
                      void *q_out, void *k_out, void *v_out, void *hip_stream);
 
+/*
+ * The same conv over one segment of a longer time-causal stream (the
+ * autoregressive, frame-by-frame use of the time-causal conv that the
+ * paper.rainbus.top Chimera page suggests in its limitations section, in the
+ * independent-weaknesses and future-directions paragraphs).  A long video is cut
+ * along t into segments; each segment is passed as its own stream whose
+ * descriptor holds that segment's latent slices (and no text: n_text = 0),
+ * with causal_t = 1.  history[s] (device, per q, k, v: [B, n_hist * h * w,
+ * H, d_s], the stream dtype, 16-byte aligned) holds the conv INPUTS of the
+ * n_hist latent slices just before the segment, oldest first; n_hist = 2
+ * makes the segment's outputs equal to the corresponding slices of one pass
+ * over the whole stream (n_hist = 0 is the start of a stream, i.e. plain
+ * kda_conv_forward).  Together with kda_forward's initial_state/final_state
+ * this processes a stream in segments.
+ * Errors: KDA_ERR_INVALID_ARG when n_hist is not 0..2, or n_hist > 0 with
+ * causal_t != 1, n_text != 0, an empty grid, or a null, misaligned or
+ * output-overlapping history pointer; otherwise as kda_conv_forward.
+ */
+int kda_conv_forward_stream(const kda_stream_desc *desc, int B, int H, int dk, int dv,
+                            kda_dtype dtype, const void *q, const void *k, const void *v,
+                            const void *const history[3], int n_hist,
+                            const void *const w_text[3], const void *const w_vis[3],
+                            void *q_out, void *k_out, void *v_out, void *hip_stream);
+
 /* Bytes of device workspace kda_forward needs for this shape: the chunk
  * transforms of every (batch, head, chunk).  0 on bad or unsupported
  * arguments, including shapes whose per-(batch, head) transforms would reach

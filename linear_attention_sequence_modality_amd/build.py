@@ -50,5 +50,36 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def kernel_resources() -> dict:
+    """Per-kernel register and scratch use as the compiler reports it.
+
+    Compiles the device code only (nothing is written in-tree) and returns
+    {mangled kernel name: {"VGPRs": n, "SGPRs": n, "ScratchSize": bytes/lane,
+    "Occupancy": waves/SIMD}}.
+    """
+    out = {}
+    for src in sources():
+        cmd = ([HIPCC] + [f for f in FLAGS if f not in ("-shared", "-fPIC")] +
+               ["--cuda-device-only", "-c", "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage", src])
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stderr)
+            raise RuntimeError("hipcc failed on " + src)
+        name = None
+        for line in res.stderr.splitlines():
+            if "remark:" not in line:
+                continue
+            body = line.split("remark:", 1)[1].split("[-Rpass")[0].strip()
+            key, _, val = body.partition(":")
+            val = val.strip()
+            if key == "Function Name":
+                name = val
+                out[name] = {}
+            elif name is not None and key in ("VGPRs", "TotalSGPRs", "ScratchSize [bytes/lane]",
+                                              "Occupancy [waves/SIMD]"):
+                out[name][key.split(" ")[0].replace("Total", "")] = int(val)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

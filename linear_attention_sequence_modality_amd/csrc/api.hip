@@ -65,19 +65,28 @@ const char *kda_status_string(int status) {
     }
 }
 
-int kda_conv_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,
-                     const void *q, const void *k, const void *v, const void *const w_text[3],
-                     const void *const w_vis[3], void *q_out, void *k_out, void *v_out,
-                     void *hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// kda_conv_forward and kda_conv_forward_stream: validation, then one launch.
+int conv_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,
+                 const void *q, const void *k, const void *v, const void *const history[3], int n_hist,
+                 const void *const w_text[3], const void *const w_vis[3], void *q_out, void *k_out,
+                 void *v_out, void *hip_stream) {
     int64_t T = 0;
     int rc = check_shape(desc, B, H, dk, dv, dtype, &T);
     if (rc != KDA_OK) return rc;
     if (!w_text || !w_vis) return KDA_ERR_INVALID_ARG;
+    const int64_t slice = (int64_t)desc->grid_h * desc->grid_w;
+    if (n_hist < 0 || n_hist > 2) return KDA_ERR_INVALID_ARG;
+    if (n_hist > 0 && (!history || desc->causal_t != 1 || desc->n_text != 0 || desc->grid_t * slice == 0))
+        return KDA_ERR_INVALID_ARG;
     const size_t es = elem_bytes(dtype);
     const int Cs[3] = {H * dk, H * dk, H * dv};
     const void *in[3] = {q, k, v};
     void *out[3] = {q_out, k_out, v_out};
-    Range rin[9], rout[3];
+    Range rin[12], rout[3];
     for (int s = 0; s < 3; ++s) {
         if (!in[s] || !out[s] || !w_text[s] || !w_vis[s]) return KDA_ERR_INVALID_ARG;
         if (!aligned16(in[s]) || !aligned16(out[s]) || !aligned16(w_text[s]) || !aligned16(w_vis[s]))
@@ -86,10 +95,15 @@ int kda_conv_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv, 
         rin[s] = range_of(in[s], nbytes);
         rin[3 + s] = range_of(w_text[s], (size_t)Cs[s] * 4 * es);
         rin[6 + s] = range_of(w_vis[s], (size_t)Cs[s] * 27 * es);
+        rin[9 + s] = Range{0, 0};
+        if (n_hist > 0) {
+            if (!history[s] || !aligned16(history[s])) return KDA_ERR_INVALID_ARG;
+            rin[9 + s] = range_of(history[s], (size_t)B * (size_t)n_hist * (size_t)slice * (size_t)Cs[s] * es);
+        }
         rout[s] = range_of(out[s], nbytes);
     }
     for (int i = 0; i < 3; ++i) {
-        for (int j = 0; j < 9; ++j)
+        for (int j = 0; j < 12; ++j)
             if (overlaps(rout[i], rin[j])) return KDA_ERR_INVALID_ARG;
         for (int j = 0; j < i; ++j)
             if (overlaps(rout[i], rout[j])) return KDA_ERR_INVALID_ARG;
@@ -103,6 +117,7 @@ int kda_conv_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv, 
         a.wt[s] = w_text[s];
         a.wv[s] = w_vis[s];
         a.C[s] = Cs[s];
+        a.hx[s] = n_hist > 0 ? history[s] : nullptr;
     }
     a.B = B;
     a.T = (int)T;
@@ -112,8 +127,29 @@ int kda_conv_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv, 
     a.gw = desc->grid_w;
     if ((int64_t)desc->grid_t * desc->grid_h * desc->grid_w == 0) a.gt = a.gh = a.gw = 0;
     a.causal_t = desc->causal_t;
+    a.n_hist = n_hist;
     hipError_t e = kdaconv::launch_conv(a, dtype == KDA_BF16, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_conv_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,
+                     const void *q, const void *k, const void *v, const void *const w_text[3],
+                     const void *const w_vis[3], void *q_out, void *k_out, void *v_out,
+                     void *hip_stream) {
+    return conv_forward(desc, B, H, dk, dv, dtype, q, k, v, nullptr, 0, w_text, w_vis, q_out, k_out, v_out,
+                        hip_stream);
+}
+
+int kda_conv_forward_stream(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,
+                            const void *q, const void *k, const void *v, const void *const history[3],
+                            int n_hist, const void *const w_text[3], const void *const w_vis[3], void *q_out,
+                            void *k_out, void *v_out, void *hip_stream) {
+    return conv_forward(desc, B, H, dk, dv, dtype, q, k, v, history, n_hist, w_text, w_vis, q_out, k_out, v_out,
+                        hip_stream);
 }
 
 size_t kda_forward_workspace_size(const kda_stream_desc *desc, int B, int H, int dk, int dv,

@@ -174,7 +174,7 @@ struct Layout {
 };
 
 // One workgroup: (stream, batch, 128 channels, rows h0..h0+HR-1, w0..w0+WR-1), all t.
-template <typename T, int PT>
+template <typename T, int PT, bool HIST>
 struct VisualTile {
     typedef Ops<T> O;
     static constexpr int POS = CPW * (int)sizeof(T);      // bytes of one tile position
@@ -185,8 +185,9 @@ struct VisualTile {
     static_assert(TP % PPI == 0, "tile must split into whole load instructions");
     static constexpr int SLICE = TP * POS;                // LDS bytes per slice buffer
 
-    __amdgpu_buffer_rsrc_t rx, ry;
+    __amdgpu_buffer_rsrc_t rx, ry, rh;   // input, output, history slices
     char *lds;            // two slice buffers
+    int ti0;              // first input slice: -n_hist (history slices first)
     int wave, lane;
     int rowb, gt, gh, gw, h0, w0, h;
     unsigned slice_bytes;  // one t-slice of the grid in the stream
@@ -198,13 +199,16 @@ struct VisualTile {
 
     __device__ __forceinline__ void issue_slice(int ti) {
         char *buf = lds + (ti & 1) * SLICE;
-        const unsigned soff = (unsigned)ti * slice_bytes;
+        // history slice ti < 0 sits at slice ti - ti0 of the history buffer
+        // (which has no text tokens: the segment has none either)
+        const bool hist = HIST && ti < 0;
+        const unsigned soff = (unsigned)(hist ? ti - ti0 : ti) * slice_bytes;
 #pragma unroll
         for (int i = 0; i < NIW; ++i) {
             const int k = wave + 4 * i;
             if (k < NI)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(buf + k * 1024), 16, dma_off[i], soff, 0,
-                                                         0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(hist ? rh : rx, (lds_void_t *)(buf + k * 1024), 16,
+                                                         dma_off[i], soff, 0, 0);
         }
     }
 
@@ -241,7 +245,8 @@ struct VisualTile {
     // slice a to output slice ti + PT - a, kept in ring slot (P + PT - a) mod 3.
     template <int P, bool EDGE>
     __device__ __forceinline__ void step(int ti, bool active) {
-        if (ti < gt) {
+        const bool live = (!HIST || ti >= ti0) && ti < gt;   // steps before ti0 only align the march
+        if (live) {
             // Slice ti has landed once every wave's direct-to-LDS loads of it
             // have retired: wait for them explicitly (the compiler does not
             // track them across the loop back-edge), then meet at the barrier,
@@ -252,7 +257,7 @@ struct VisualTile {
             if (ti + 1 < gt) issue_slice(ti + 1);
         }
         flush<P, EDGE>(ti + PT - 3, active);
-        if (ti < gt && active) {
+        if (live && active) {
             float *a0[3], *a1[3];
 #pragma unroll
             for (int j = 0; j < WR; ++j) {
@@ -270,11 +275,12 @@ struct VisualTile {
 
     template <bool EDGE>
     __device__ void march(bool active) {
-        issue_slice(0);
-        // empty steps past the last slice flush the last output slices
+        issue_slice(HIST ? ti0 : 0);
+        // empty steps past the last slice flush the last output slices; with
+        // history the march starts at -6 so that step<P> still sees ti = P mod 6
         const int last = gt + 2 - PT;
 #pragma unroll 1
-        for (int ti = 0; ti <= last; ti += 6) {
+        for (int ti = HIST ? -6 : 0; ti <= last; ti += 6) {
             step<0, EDGE>(ti, active);
             if (ti + 1 > last) break;
             step<1, EDGE>(ti + 1, active);
@@ -290,9 +296,9 @@ struct VisualTile {
     }
 };
 
-template <typename T, int PT>
+template <typename T, int PT, bool HIST>
 __device__ void visual_block(const ConvArgs &a, const Layout &L, int s, int blk, int wave, int lane, char *lds) {
-    typedef VisualTile<T, PT> V;
+    typedef VisualTile<T, PT, HIST> V;
     // channel block outermost, then row groups, then w-runs
     const int wrun = blk % L.n_wrun;
     int rest = blk / L.n_wrun;
@@ -322,6 +328,13 @@ __device__ void visual_block(const ConvArgs &a, const Layout &L, int s, int blk,
         kBufferWord3);
     v.ry = __builtin_amdgcn_make_buffer_rsrc(static_cast<char *>(a.y[s]) + (size_t)b * bbytes, 0,
                                              (int)(unsigned)bbytes, kBufferWord3);
+    if constexpr (HIST) {
+        v.ti0 = -a.n_hist;
+        const size_t hbytes = (size_t)a.n_hist * v.slice_bytes;   // history of one batch
+        v.rh = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char *>(static_cast<const char *>(a.hx[s])) + (size_t)b * hbytes, 0, (int)(unsigned)hbytes,
+            kBufferWord3);
+    }
     // tile position p of load instruction k: k * PPI + lane / LPP; positions
     // outside the grid load a clamped in-grid token that is never read
     const unsigned chan = (unsigned)(cb * V::POS) + (unsigned)(lane % V::LPP) * 16u;
@@ -399,17 +412,17 @@ __device__ void text_item(const ConvArgs &a, const Layout &L, int s, int item, i
 }
 
 // bf16: at most 128 VGPRs, so four 4-wave blocks share a CU (LDS: 4 x 30 KB)
-template <typename T, int PT>
+template <typename T, int PT, bool HIST>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 2 : 4))) void conv_kernel(
     ConvArgs a, Layout L) {
-    __shared__ __attribute__((aligned(1024))) char lds[2 * VisualTile<T, PT>::SLICE];
+    __shared__ __attribute__((aligned(1024))) char lds[2 * VisualTile<T, PT, HIST>::SLICE];
     int blk = xcd_remap(blockIdx.x, L.nblocks);
     const int wave = uniform(threadIdx.x / LANES), lane = threadIdx.x % LANES;
     constexpr int WPB = NT / LANES;
 #pragma unroll 1
     for (int s = 0; s < 3; ++s) {
         if (blk < L.vis_blocks[s]) {
-            visual_block<T, PT>(a, L, s, blk, wave, lane, lds);
+            visual_block<T, PT, HIST>(a, L, s, blk, wave, lane, lds);
             return;
         }
         blk -= L.vis_blocks[s];
@@ -440,16 +453,23 @@ hipError_t launch_conv(const ConvArgs &a, bool bf16, hipStream_t stream) {
         L.nblocks += L.vis_blocks[s] + L.txt_blocks[s];
     }
     if (L.nblocks == 0) return hipSuccess;
+    // history slices exist only for time-causal segments; a separate
+    // instantiation keeps the extra buffer resource out of the other kernels
+    const bool hist = a.causal_t && a.n_hist > 0;
     if (bf16) {
-        if (a.causal_t)
-            hipLaunchKernelGGL((conv_kernel<bf16_t, 2>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
+        if (hist)
+            hipLaunchKernelGGL((conv_kernel<bf16_t, 2, true>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
+        else if (a.causal_t)
+            hipLaunchKernelGGL((conv_kernel<bf16_t, 2, false>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
         else
-            hipLaunchKernelGGL((conv_kernel<bf16_t, 1>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
+            hipLaunchKernelGGL((conv_kernel<bf16_t, 1, false>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
     } else {
-        if (a.causal_t)
-            hipLaunchKernelGGL((conv_kernel<float, 2>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
+        if (hist)
+            hipLaunchKernelGGL((conv_kernel<float, 2, true>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
+        else if (a.causal_t)
+            hipLaunchKernelGGL((conv_kernel<float, 2, false>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
         else
-            hipLaunchKernelGGL((conv_kernel<float, 1>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
+            hipLaunchKernelGGL((conv_kernel<float, 1, false>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
     }
     return hipGetLastError();
 }

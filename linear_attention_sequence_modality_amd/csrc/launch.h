@@ -15,6 +15,10 @@ struct ConvArgs {
     const void *wv[3];   // visual taps      [C[s], 27]
     int C[3];            // channels per stream (H*dk, H*dk, H*dv)
     int B, T, n_text, gt, gh, gw, causal_t;
+    // time-causal streaming: the n_hist latent slices just before this
+    // segment's first slice, as conv inputs [B, n_hist * gh * gw, C[s]]
+    const void *hx[3];
+    int n_hist;
 };
 hipError_t launch_conv(const ConvArgs &a, bool bf16, hipStream_t stream);
 

@@ -24,7 +24,7 @@ KDA_ERR_UNSUPPORTED = -2
 KDA_ERR_WORKSPACE = -3
 KDA_ERR_HIP = -4
 
-EXPORTED_SYMBOLS = ("kda_conv_forward", "kda_forward_workspace_size", "kda_forward",
+EXPORTED_SYMBOLS = ("kda_conv_forward", "kda_conv_forward_stream", "kda_forward_workspace_size", "kda_forward",
                     "kda_forward_chunks", "kda_forward_scan", "kda_status_string")
 
 
@@ -58,6 +58,10 @@ def load_library():
     lib.kda_conv_forward.restype = i32
     lib.kda_conv_forward.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp,
                                      ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp]
+    lib.kda_conv_forward_stream.restype = i32
+    lib.kda_conv_forward_stream.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp,
+                                            ctypes.POINTER(vp), i32, ctypes.POINTER(vp),
+                                            ctypes.POINTER(vp), vp, vp, vp, vp]
     lib.kda_forward_workspace_size.restype = ctypes.c_size_t
     lib.kda_forward_workspace_size.argtypes = [desc_p, i32, i32, i32, i32, i32]
     lib.kda_forward.restype = i32
@@ -121,9 +125,15 @@ def kda_forward_workspace_size(desc: KdaStreamDesc, B: int, H: int, dk: int, dv:
 def kda_conv_forward(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      w_text: Sequence[torch.Tensor], w_vis: Sequence[torch.Tensor],
                      q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
-                     v_out: Optional[torch.Tensor] = None, stream=None
+                     v_out: Optional[torch.Tensor] = None, stream=None,
+                     history: Optional[Sequence[torch.Tensor]] = None
                      ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Modality-aware depthwise short conv of q [B,T,H,dk], k [B,T,H,dk], v [B,T,H,dv]."""
+    """Modality-aware depthwise short conv of q [B,T,H,dk], k [B,T,H,dk], v [B,T,H,dv].
+
+    ``history`` (time-causal segments, kda_conv_forward_stream): the conv inputs
+    (q, k, v) of the latent slices just before this segment, each
+    [B, n_hist * h * w, H, d] with n_hist in {1, 2}.
+    """
     lib = load_library()
     dt = q.dtype
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
@@ -138,11 +148,25 @@ def kda_conv_forward(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: t
     v_out = torch.empty_like(v) if v_out is None else v_out
     wt = (ctypes.c_void_p * 3)(*[w.data_ptr() for w in w_text])
     wv = (ctypes.c_void_p * 3)(*[w.data_ptr() for w in w_vis])
-    rc = lib.kda_conv_forward(ctypes.byref(desc), B, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k),
-                              _ptr(v), wt, wv, _ptr(q_out), _ptr(k_out), _ptr(v_out),
-                              _stream(stream))
+    if history is None:
+        rc = lib.kda_conv_forward(ctypes.byref(desc), B, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k),
+                                  _ptr(v), wt, wv, _ptr(q_out), _ptr(k_out), _ptr(v_out),
+                                  _stream(stream))
+        if rc != KDA_OK:
+            raise KdaError("kda_conv_forward", rc)
+        return q_out, k_out, v_out
+    for i, t in enumerate(history):
+        _check(t, "history[%d]" % i, dt)
+    slice_tokens = desc.grid_h * desc.grid_w
+    n_hist = history[0].shape[1] // slice_tokens if slice_tokens else 0
+    if any(t.shape[1] != n_hist * slice_tokens or t.shape[0] != B for t in history):
+        raise ValueError("history tensors must be [B, n_hist * h * w, H, d]")
+    hs = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in history])
+    rc = lib.kda_conv_forward_stream(ctypes.byref(desc), B, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k),
+                                     _ptr(v), hs, n_hist, wt, wv, _ptr(q_out), _ptr(k_out), _ptr(v_out),
+                                     _stream(stream))
     if rc != KDA_OK:
-        raise KdaError("kda_conv_forward", rc)
+        raise KdaError("kda_conv_forward_stream", rc)
     return q_out, k_out, v_out
 
 

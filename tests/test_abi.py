@@ -85,6 +85,34 @@ def test_conv_rejects_bad_arguments(lib):
     assert _conv(lib, _desc(n_text=1 << 30, grid=(1, 1 << 15, 1 << 16))) == kda.KDA_ERR_UNSUPPORTED
 
 
+def _conv_stream(lib, desc, n_hist, hist="ok", B=1, H=2, dk=64, dv=64, ptrs=None):
+    p = ptrs if ptrs is not None else _ptrs(6)
+    wt = (ctypes.c_void_p * 3)(*[FAKE + (20 + i) * (1 << 32) for i in range(3)])
+    wv = (ctypes.c_void_p * 3)(*[FAKE + (30 + i) * (1 << 32) for i in range(3)])
+    if hist == "ok":
+        hist = (ctypes.c_void_p * 3)(*[FAKE + (40 + i) * (1 << 32) for i in range(3)])
+    return lib.kda_conv_forward_stream(ctypes.byref(desc), B, H, dk, dv, kda.KDA_BF16, p[0], p[1], p[2],
+                                       hist, n_hist, wt, wv, p[3], p[4], p[5], None)
+
+
+def test_conv_stream_rejects_bad_arguments(lib):
+    seg = _desc(n_text=0, grid=(3, 10, 12), causal_t=1)
+    assert _conv_stream(lib, seg, 3) == kda.KDA_ERR_INVALID_ARG
+    assert _conv_stream(lib, seg, -1) == kda.KDA_ERR_INVALID_ARG
+    assert _conv_stream(lib, _desc(n_text=0, grid=(3, 10, 12)), 2) == kda.KDA_ERR_INVALID_ARG   # symmetric in t
+    assert _conv_stream(lib, _desc(n_text=5, grid=(3, 10, 12), causal_t=1), 2) == kda.KDA_ERR_INVALID_ARG
+    assert _conv_stream(lib, seg, 2, hist=None) == kda.KDA_ERR_INVALID_ARG
+    assert _conv_stream(lib, seg, 2, hist=(ctypes.c_void_p * 3)(FAKE + 40 * (1 << 32), None,
+                                                                FAKE + 42 * (1 << 32))) == kda.KDA_ERR_INVALID_ARG
+    p = _ptrs(6)
+    assert _conv_stream(lib, seg, 2, hist=(ctypes.c_void_p * 3)(p[3].value, FAKE + 41 * (1 << 32),
+                                                                FAKE + 42 * (1 << 32))) == kda.KDA_ERR_INVALID_ARG
+    assert _conv_stream(lib, seg, 2, hist=(ctypes.c_void_p * 3)(FAKE + 40 * (1 << 32) + 8, FAKE + 41 * (1 << 32),
+                                                                FAKE + 42 * (1 << 32))) == kda.KDA_ERR_INVALID_ARG
+    # a valid segment with no batch launches nothing
+    assert _conv_stream(lib, seg, 2, B=0) == kda.KDA_OK
+
+
 def test_workspace_size_is_host_arithmetic(lib):
     d = _desc()                                     # T = 512 -> 8 chunks
     s1 = kda.kda_forward_workspace_size(d, 1, 2, 64, 64, kda.KDA_F32)

@@ -1,0 +1,34 @@
+"""Compiler-reported resources of every gfx950 kernel (CPU only: hipcc cross-compiles).
+
+A kernel that spills to scratch, or that loses the occupancy its launch bounds
+ask for, still computes the right numbers but runs several times slower, so
+the parity tests would not see it.
+"""
+import pytest
+
+from linear_attention_sequence_modality_amd import build
+
+
+@pytest.fixture(scope="module")
+def resources():
+    return build.kernel_resources()
+
+
+def test_every_kernel_reported(resources):
+    names = " ".join(resources)
+    assert len(resources) >= 6
+    for part in ("conv_kernel", "kda_intra_kernel"):
+        assert part in names, part
+
+
+def test_no_kernel_spills(resources):
+    spills = {k: v for k, v in resources.items() if v.get("ScratchSize", 0) != 0}
+    assert not spills, spills
+
+
+def test_conv_keeps_its_occupancy(resources):
+    # bf16: four 4-wave blocks per CU, so at most 128 VGPRs; fp32 two
+    for name, r in resources.items():
+        if "conv_kernel" in name:
+            want = 4 if "DF16b" in name else 2
+            assert r["Occupancy"] >= want, (name, r)

@@ -181,6 +181,55 @@ def test_forward_equals_the_two_kernels(T, B):
     assert e <= TOL["bf16"]
 
 
+@pytest.mark.timeout(120)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_time_causal_stream_in_segments_equals_one_pass(dtype):
+    """A time-causal stream cut along t into segments (text in the first only):
+    each segment's conv, given the inputs of the two latent slices before it
+    (kda_conv_forward_stream), equals the same slices of the one-pass conv bit
+    for bit, and KDA over the segments with the carried state matches the
+    oracle of the whole stream."""
+    kw = dict(dk=64, dv=64) if dtype == "f32" else {}
+    cfg = _small("stream", B=2, n_text=5, grid=(8, 6, 9), causal_t=1, dtype=dtype, **kw)
+    say("case stream in segments %s T=%d" % (dtype, cfg.T))
+    host = make_inputs(cfg)
+    dev = to_dev(host)
+    wt = (dev["w_text_q"], dev["w_text_k"], dev["w_text_v"])
+    wv = (dev["w_vis_q"], dev["w_vis_k"], dev["w_vis_v"])
+    whole = kda.kda_conv_forward(desc_of(cfg), dev["q"], dev["k"], dev["v"], wt, wv)
+    gt, gh, gw = cfg.grid
+    sl = gh * gw
+    cuts = [0, 3, 5, 8]                      # latent slices of each segment
+    state = None
+    outs = []
+    for i in range(3):
+        t0, t1 = cuts[i], cuts[i + 1]
+        lo = 0 if i == 0 else cfg.n_text + t0 * sl
+        hi = cfg.n_text + t1 * sl
+        seg = {k: dev[k][:, lo:hi].contiguous() for k in ("q", "k", "v", "alpha", "beta")}
+        if i == 0:
+            d = kda.make_desc(cfg.n_text, (t1, gh, gw), causal_t=1)
+            conv = kda.kda_conv_forward(d, seg["q"], seg["k"], seg["v"], wt, wv)
+        else:
+            d = kda.make_desc(0, (t1 - t0, gh, gw), causal_t=1)
+            hlo = cfg.n_text + (t0 - 2) * sl
+            hist = [dev[k][:, hlo:lo].contiguous() for k in ("q", "k", "v")]
+            conv = kda.kda_conv_forward(d, seg["q"], seg["k"], seg["v"], wt, wv, history=hist)
+        for c, w in zip(conv, whole):
+            assert torch.equal(c, w[:, lo:hi])
+        fin = torch.empty(cfg.B, cfg.H, cfg.dk, cfg.dv, device="cuda")
+        outs.append(kda.kda_forward(d, *conv, seg["alpha"], seg["beta"], initial_state=state, final_state=fin))
+        state = fin
+    torch.cuda.synchronize()
+    o = torch.cat(outs, dim=1)
+    heads = tuple(range(cfg.H))
+    _, _, _, ro, rs = oracle_end_to_end_heads(cfg, host, heads)
+    e_o = rel(heads_slice(o, heads), ro)
+    e_s = oracle.rel_err_state(state.double().cpu().numpy(), rs)
+    say("  segments rel err o %.2e S %.2e" % (e_o, e_s))
+    assert e_o <= TOL[dtype] and e_s <= TOL[dtype]
+
+
 # ---- hygiene -----------------------------------------------------------------------
 
 @pytest.mark.timeout(120)
