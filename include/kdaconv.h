@@ -43,6 +43,7 @@
  *     inputs finite, and within any 8 consecutive tokens of one head the
  *     product of alpha over one key channel stays above 2^-120 (the chunked
  *     scan factorises intra-chunk decays around sub-block midpoints).
+ *   - A batch of B = 0 streams enqueues nothing and returns KDA_OK.
  *   - The library is stateless and re-entrant.
  */
 #ifndef KDACONV_H
@@ -171,6 +172,40 @@ int kda_forward_scan(const kda_stream_desc *desc, int B, int H, int dk, int dv,
                      kda_dtype dtype, const float *initial_state, float *final_state,
                      void *o, const void *workspace, size_t workspace_bytes,
                      void *hip_stream);
+
+/*
+ * Variable-length batches.  n_seq streams (1 <= n_seq <= KDA_MAX_SEQS), each
+ * with its own layout descs[i] (T_i >= 1 tokens), packed one after another
+ * along the token axis: stream i occupies tokens [P_i, P_i + T_i) with
+ * P_i = T_0 + ... + T_{i-1}, so q, k, alpha, q_out, k_out are
+ * [sum T_i, H, dk], v, v_out, o are [sum T_i, H, dv] and beta is
+ * [sum T_i, H]; initial_state and final_state are float32 [n_seq, H, dk, dv].
+ * The streams are independent: each one's conv sees only its own tokens, and
+ * each one's scan starts from its own initial state.  The result for stream
+ * i equals the uniform entry point called on that stream alone with B = 1.
+ * All streams share H, dk, dv and dtype.  (Batches that mix images, videos
+ * of different lengths or sizes, and text-only streams are the use.)
+ * kda_conv_forward_varlen enqueues one conv launch per stream;
+ * kda_forward_varlen enqueues one launch of each KDA kernel for all streams.
+ * Errors: KDA_ERR_INVALID_ARG for n_seq < 1 or a NULL descs, and whatever a
+ * stream's layout would give with B = 1; KDA_ERR_UNSUPPORTED for
+ * n_seq > KDA_MAX_SEQS or a packed axis past the uniform entry points'
+ * limits; otherwise as kda_conv_forward / kda_forward.
+ */
+#define KDA_MAX_SEQS 64
+size_t kda_forward_varlen_workspace_size(const kda_stream_desc *descs, int n_seq, int H, int dk,
+                                         int dv, kda_dtype dtype);
+
+int kda_forward_varlen(const kda_stream_desc *descs, int n_seq, int H, int dk, int dv,
+                       kda_dtype dtype, const void *q, const void *k, const void *v,
+                       const void *alpha, const void *beta, const float *initial_state,
+                       float *final_state, void *o, void *workspace, size_t workspace_bytes,
+                       void *hip_stream);
+
+int kda_conv_forward_varlen(const kda_stream_desc *descs, int n_seq, int H, int dk, int dv,
+                            kda_dtype dtype, const void *q, const void *k, const void *v,
+                            const void *const w_text[3], const void *const w_vis[3],
+                            void *q_out, void *k_out, void *v_out, void *hip_stream);
 
 /* Static, human-readable text for a status code. */
 const char *kda_status_string(int status);

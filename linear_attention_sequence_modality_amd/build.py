@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wshadow", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # matrix-core accumulators in ordinary VGPRs: the state pass post-processes
     # its MFMA results with vector ALU ops every chunk, and AGPR results would

@@ -12,6 +12,7 @@ using kdaconv::ConvArgs;
 using kdaconv::KdaArgs;
 
 constexpr int64_t kMaxTokens = (int64_t)1 << 31;
+static_assert(kdaconv::kMaxSeqs == KDA_MAX_SEQS, "one limit on the sequences of a batch");
 
 struct Range {
     uintptr_t lo, hi;   // [lo, hi)
@@ -69,36 +70,26 @@ const char *kda_status_string(int status) {
 
 namespace {
 
-// kda_conv_forward and kda_conv_forward_stream: validation, then one launch.
-int conv_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,
-                 const void *q, const void *k, const void *v, const void *const history[3], int n_hist,
-                 const void *const w_text[3], const void *const w_vis[3], void *q_out, void *k_out,
-                 void *v_out, void *hip_stream) {
-    int64_t T = 0;
-    int rc = check_shape(desc, B, H, dk, dv, dtype, &T);
-    if (rc != KDA_OK) return rc;
+// Pointer checks of a conv call over `tokens` tokens of each stream (plus
+// `hist_tokens` history tokens): every pointer set and 16-byte aligned, and no
+// output overlapping an input, a weight, a history buffer or another output.
+int conv_check_pointers(int64_t tokens, int64_t hist_tokens, const int Cs[3], size_t es, const void *const in[3],
+                        const void *const history[3], const void *const w_text[3], const void *const w_vis[3],
+                        void *const out[3]) {
     if (!w_text || !w_vis) return KDA_ERR_INVALID_ARG;
-    const int64_t slice = (int64_t)desc->grid_h * desc->grid_w;
-    if (n_hist < 0 || n_hist > 2) return KDA_ERR_INVALID_ARG;
-    if (n_hist > 0 && (!history || desc->causal_t != 1 || desc->n_text != 0 || desc->grid_t * slice == 0))
-        return KDA_ERR_INVALID_ARG;
-    const size_t es = elem_bytes(dtype);
-    const int Cs[3] = {H * dk, H * dk, H * dv};
-    const void *in[3] = {q, k, v};
-    void *out[3] = {q_out, k_out, v_out};
     Range rin[12], rout[3];
     for (int s = 0; s < 3; ++s) {
         if (!in[s] || !out[s] || !w_text[s] || !w_vis[s]) return KDA_ERR_INVALID_ARG;
         if (!aligned16(in[s]) || !aligned16(out[s]) || !aligned16(w_text[s]) || !aligned16(w_vis[s]))
             return KDA_ERR_INVALID_ARG;
-        const size_t nbytes = (size_t)B * (size_t)T * (size_t)Cs[s] * es;
+        const size_t nbytes = (size_t)tokens * (size_t)Cs[s] * es;
         rin[s] = range_of(in[s], nbytes);
         rin[3 + s] = range_of(w_text[s], (size_t)Cs[s] * 4 * es);
         rin[6 + s] = range_of(w_vis[s], (size_t)Cs[s] * 27 * es);
         rin[9 + s] = Range{0, 0};
-        if (n_hist > 0) {
+        if (hist_tokens > 0) {
             if (!history[s] || !aligned16(history[s])) return KDA_ERR_INVALID_ARG;
-            rin[9 + s] = range_of(history[s], (size_t)B * (size_t)n_hist * (size_t)slice * (size_t)Cs[s] * es);
+            rin[9 + s] = range_of(history[s], (size_t)hist_tokens * (size_t)Cs[s] * es);
         }
         rout[s] = range_of(out[s], nbytes);
     }
@@ -108,12 +99,21 @@ int conv_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_
         for (int j = 0; j < i; ++j)
             if (overlaps(rout[i], rout[j])) return KDA_ERR_INVALID_ARG;
     }
-    if (B == 0) return KDA_OK;
+    return KDA_OK;
+}
 
+// One conv launch over B streams of desc's layout (T tokens each) whose first
+// token is token `tok` of the arrays (a validated call).
+int conv_launch(const kda_stream_desc *desc, int B, int64_t T, int64_t tok, const int Cs[3], kda_dtype dtype,
+                const void *const in[3], const void *const history[3], int n_hist,
+                const void *const w_text[3], const void *const w_vis[3], void *const out[3],
+                void *hip_stream) {
+    const size_t es = elem_bytes(dtype);
     ConvArgs a;
     for (int s = 0; s < 3; ++s) {
-        a.x[s] = in[s];
-        a.y[s] = out[s];
+        const size_t off = (size_t)tok * (size_t)Cs[s] * es;
+        a.x[s] = static_cast<const char *>(in[s]) + off;
+        a.y[s] = static_cast<char *>(out[s]) + off;
         a.wt[s] = w_text[s];
         a.wv[s] = w_vis[s];
         a.C[s] = Cs[s];
@@ -130,6 +130,89 @@ int conv_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_
     a.n_hist = n_hist;
     hipError_t e = kdaconv::launch_conv(a, dtype == KDA_BF16, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// kda_conv_forward and kda_conv_forward_stream: validation, then one launch.
+int conv_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,
+                 const void *q, const void *k, const void *v, const void *const history[3], int n_hist,
+                 const void *const w_text[3], const void *const w_vis[3], void *q_out, void *k_out,
+                 void *v_out, void *hip_stream) {
+    int64_t T = 0;
+    int rc = check_shape(desc, B, H, dk, dv, dtype, &T);
+    if (rc != KDA_OK) return rc;
+    const int64_t slice = (int64_t)desc->grid_h * desc->grid_w;
+    if (n_hist < 0 || n_hist > 2) return KDA_ERR_INVALID_ARG;
+    if (n_hist > 0 && (!history || desc->causal_t != 1 || desc->n_text != 0 || desc->grid_t * slice == 0))
+        return KDA_ERR_INVALID_ARG;
+    const int Cs[3] = {H * dk, H * dk, H * dv};
+    const void *in[3] = {q, k, v};
+    void *out[3] = {q_out, k_out, v_out};
+    rc = conv_check_pointers((int64_t)B * T, (int64_t)B * n_hist * slice, Cs, elem_bytes(dtype), in, history,
+                             w_text, w_vis, out);
+    if (rc != KDA_OK || B == 0) return rc;
+    return conv_launch(desc, B, T, 0, Cs, dtype, in, history, n_hist, w_text, w_vis, out, hip_stream);
+}
+
+// The sequences of one KDA call: B streams of one layout (a uniform batch) or
+// up to kMaxSeqs streams with their own layouts packed along the token axis
+// (a variable-length batch).
+struct Seqs {
+    int n = 0;               // sequences
+    int T = 0;               // uniform batch: tokens per sequence
+    bool varlen = false;
+    int64_t tokens = 0;      // over all sequences
+    int64_t chunks = 0;      // over all sequences
+    int64_t max_chunks = 0;  // of the longest sequence
+    int tok0[kdaconv::kMaxSeqs + 1] = {}, chk0[kdaconv::kMaxSeqs + 1] = {};
+};
+
+int64_t chunks_of(int64_t T) { return (T + kdaconv::kChunk - 1) / kdaconv::kChunk; }
+
+int uniform_seqs(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype, Seqs *sq) {
+    int64_t T = 0;
+    int rc = check_shape(desc, B, H, dk, dv, dtype, &T);
+    if (rc != KDA_OK) return rc;
+    sq->n = B;
+    sq->T = (int)T;
+    sq->tokens = (int64_t)B * T;
+    sq->max_chunks = chunks_of(T);
+    sq->chunks = (int64_t)B * sq->max_chunks;
+    return KDA_OK;
+}
+
+int varlen_seqs(const kda_stream_desc *descs, int n_seq, int H, int dk, int dv, kda_dtype dtype, Seqs *sq) {
+    if (!descs || n_seq < 1) return KDA_ERR_INVALID_ARG;
+    if (n_seq > kdaconv::kMaxSeqs) return KDA_ERR_UNSUPPORTED;
+    int64_t tok = 0, chk = 0;
+    for (int i = 0; i < n_seq; ++i) {
+        int64_t T = 0;
+        int rc = check_shape(&descs[i], 1, H, dk, dv, dtype, &T);
+        if (rc != KDA_OK) return rc;
+        sq->tok0[i] = (int)tok;
+        sq->chk0[i] = (int)chk;
+        tok += T;
+        chk += chunks_of(T);
+        if (chunks_of(T) > sq->max_chunks) sq->max_chunks = chunks_of(T);
+        // the packed token axis obeys the limits of one batch of tok tokens
+        const int64_t d_max = dk > dv ? dk : dv;
+        if (tok >= kMaxTokens || tok * H * d_max / 2 >= kMaxTokens) return KDA_ERR_UNSUPPORTED;
+    }
+    sq->tok0[n_seq] = (int)tok;
+    sq->chk0[n_seq] = (int)chk;
+    sq->n = n_seq;
+    sq->varlen = true;
+    sq->tokens = tok;
+    sq->chunks = chk;
+    return KDA_OK;
+}
+
+// Workspace bytes of a call, or 0 when the configuration is unsupported.
+size_t workspace_bytes_of(const Seqs &sq, int H, int dk, int dv, kda_dtype dtype) {
+    if (dtype == KDA_F32 && (dk != 64 || dv != 64)) return 0;
+    const size_t per = kdaconv::kda_chunk_ws_bytes(dk, dv, dtype == KDA_BF16);
+    // the state pass addresses one (sequence, head)'s chunks with 32-bit offsets
+    if ((int64_t)per * sq.max_chunks >= ((int64_t)1 << 32)) return 0;
+    return per * (size_t)H * (size_t)sq.chunks;
 }
 
 }  // namespace
@@ -154,35 +237,34 @@ int kda_conv_forward_stream(const kda_stream_desc *desc, int B, int H, int dk, i
 
 size_t kda_forward_workspace_size(const kda_stream_desc *desc, int B, int H, int dk, int dv,
                                   kda_dtype dtype) {
-    int64_t T = 0;
-    if (check_shape(desc, B, H, dk, dv, dtype, &T) != KDA_OK) return 0;
-    if (dtype == KDA_F32 && (dk != 64 || dv != 64)) return 0;
-    const size_t per = kdaconv::kda_chunk_ws_bytes(dk, dv, dtype == KDA_BF16);
-    const int64_t nch = (T + kdaconv::kChunk - 1) / kdaconv::kChunk;
-    // the state pass addresses one (batch, head)'s chunks with 32-bit offsets
-    if ((int64_t)per * nch >= ((int64_t)1 << 32)) return 0;
-    return per * (size_t)B * (size_t)H * (size_t)nch;
+    Seqs sq;
+    if (uniform_seqs(desc, B, H, dk, dv, dtype, &sq) != KDA_OK) return 0;
+    return workspace_bytes_of(sq, H, dk, dv, dtype);
+}
+
+size_t kda_forward_varlen_workspace_size(const kda_stream_desc *descs, int n_seq, int H, int dk, int dv,
+                                         kda_dtype dtype) {
+    Seqs sq;
+    if (varlen_seqs(descs, n_seq, H, dk, dv, dtype, &sq) != KDA_OK) return 0;
+    return workspace_bytes_of(sq, H, dk, dv, dtype);
 }
 
 }  // extern "C"
 
 namespace {
 
-// Validation shared by kda_forward, kda_forward_chunks and kda_forward_scan.
-// Null input pointers mean "not used by this entry point" (want_* selects
-// which groups are required).  Fills *out on success.
-int prepare_kda(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,
-                const void *q, const void *k, const void *v, const void *alpha, const void *beta,
-                const float *initial_state, const float *final_state, const void *o,
-                const void *workspace, size_t workspace_bytes, bool want_inputs, bool want_outputs,
-                KdaArgs *out) {
-    int64_t T = 0;
-    int rc = check_shape(desc, B, H, dk, dv, dtype, &T);
-    if (rc != KDA_OK) return rc;
+// Validation shared by kda_forward, kda_forward_chunks, kda_forward_scan and
+// kda_forward_varlen, for the sequences sq (checked already).  Null input
+// pointers mean "not used by this entry point" (want_* selects which groups
+// are required).  Fills *out on success.
+int prepare_kda(const Seqs &sq, int H, int dk, int dv, kda_dtype dtype, const void *q, const void *k,
+                const void *v, const void *alpha, const void *beta, const float *initial_state,
+                const float *final_state, const void *o, const void *workspace, size_t workspace_bytes,
+                bool want_inputs, bool want_outputs, KdaArgs *out) {
     if (dtype == KDA_F32 && (dk != 64 || dv != 64)) return KDA_ERR_UNSUPPORTED;
     const size_t es = elem_bytes(dtype);
-    const size_t BT = (size_t)B * (size_t)T;
-    const size_t sbytes = (size_t)B * H * dk * dv * sizeof(float);
+    const size_t BT = (size_t)sq.tokens;
+    const size_t sbytes = (size_t)sq.n * H * dk * dv * sizeof(float);
     Range rin[6] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}, {0, 0}, {0, 0}};
     if (want_inputs) {
         const void *ins[5] = {q, k, v, alpha, beta};
@@ -210,9 +292,9 @@ int prepare_kda(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_d
             return KDA_ERR_INVALID_ARG;
         if (overlaps(rs, ro)) return KDA_ERR_INVALID_ARG;
     }
-    const size_t need = kda_forward_workspace_size(desc, B, H, dk, dv, dtype);
-    if (need == 0) return KDA_ERR_UNSUPPORTED;
-    if (B > 0) {
+    if (sq.n > 0) {
+        const size_t need = workspace_bytes_of(sq, H, dk, dv, dtype);
+        if (need == 0) return KDA_ERR_UNSUPPORTED;
         if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KDA_ERR_WORKSPACE;
         const Range rw = range_of(workspace, need);
         for (int i = 0; i < 6; ++i)
@@ -228,14 +310,31 @@ int prepare_kda(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_d
     out->sT = const_cast<float *>(final_state);
     out->o = const_cast<void *>(o);
     out->ws = const_cast<void *>(workspace);
-    out->B = B;
-    out->T = (int)T;
+    out->B = sq.n;
+    out->T = sq.T;
     out->H = H;
     out->dk = dk;
     out->dv = dv;
-    out->n_chunks = (int)((T + kdaconv::kChunk - 1) / kdaconv::kChunk);
-    out->c0 = 0;
-    out->c1 = out->n_chunks;
+    out->n_chunks = sq.varlen ? 0 : (int)sq.max_chunks;
+    out->varlen = sq.varlen ? 1 : 0;
+    for (int i = 0; i <= kdaconv::kMaxSeqs; ++i) {
+        out->tok0[i] = sq.tok0[i];
+        out->chk0[i] = sq.chk0[i];
+    }
+    return KDA_OK;
+}
+
+// kda_forward and kda_forward_varlen: both kernels on one stream.
+int forward(const Seqs &sq, int H, int dk, int dv, kda_dtype dtype, const void *q, const void *k,
+            const void *v, const void *alpha, const void *beta, const float *initial_state, float *final_state,
+            void *o, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    KdaArgs a;
+    int rc = prepare_kda(sq, H, dk, dv, dtype, q, k, v, alpha, beta, initial_state, final_state, o, workspace,
+                         workspace_bytes, true, true, &a);
+    if (rc != KDA_OK || sq.n == 0) return rc;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (kdaconv::launch_kda_chunks(a, dtype == KDA_BF16, st) != hipSuccess) return KDA_ERR_HIP;
+    if (kdaconv::launch_kda_scan(a, dtype == KDA_BF16, st) != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
 }
 
@@ -247,23 +346,34 @@ int kda_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_d
                 const void *q, const void *k, const void *v, const void *alpha, const void *beta,
                 const float *initial_state, float *final_state, void *o, void *workspace,
                 size_t workspace_bytes, void *hip_stream) {
-    KdaArgs a;
-    int rc = prepare_kda(desc, B, H, dk, dv, dtype, q, k, v, alpha, beta, initial_state, final_state,
-                         o, workspace, workspace_bytes, true, true, &a);
-    if (rc != KDA_OK || B == 0) return rc;
-    hipStream_t st = static_cast<hipStream_t>(hip_stream);
-    if (kdaconv::launch_kda_chunks(a, dtype == KDA_BF16, st) != hipSuccess) return KDA_ERR_HIP;
-    if (kdaconv::launch_kda_scan(a, dtype == KDA_BF16, st) != hipSuccess) return KDA_ERR_HIP;
-    return KDA_OK;
+    Seqs sq;
+    int rc = uniform_seqs(desc, B, H, dk, dv, dtype, &sq);
+    if (rc != KDA_OK) return rc;
+    return forward(sq, H, dk, dv, dtype, q, k, v, alpha, beta, initial_state, final_state, o, workspace,
+                   workspace_bytes, hip_stream);
+}
+
+int kda_forward_varlen(const kda_stream_desc *descs, int n_seq, int H, int dk, int dv, kda_dtype dtype,
+                       const void *q, const void *k, const void *v, const void *alpha, const void *beta,
+                       const float *initial_state, float *final_state, void *o, void *workspace,
+                       size_t workspace_bytes, void *hip_stream) {
+    Seqs sq;
+    int rc = varlen_seqs(descs, n_seq, H, dk, dv, dtype, &sq);
+    if (rc != KDA_OK) return rc;
+    return forward(sq, H, dk, dv, dtype, q, k, v, alpha, beta, initial_state, final_state, o, workspace,
+                   workspace_bytes, hip_stream);
 }
 
 int kda_forward_chunks(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,
                        const void *q, const void *k, const void *v, const void *alpha,
                        const void *beta, void *workspace, size_t workspace_bytes,
                        void *hip_stream) {
+    Seqs sq;
     KdaArgs a;
-    int rc = prepare_kda(desc, B, H, dk, dv, dtype, q, k, v, alpha, beta, nullptr, nullptr, nullptr,
-                         workspace, workspace_bytes, true, false, &a);
+    int rc = uniform_seqs(desc, B, H, dk, dv, dtype, &sq);
+    if (rc == KDA_OK)
+        rc = prepare_kda(sq, H, dk, dv, dtype, q, k, v, alpha, beta, nullptr, nullptr, nullptr, workspace,
+                         workspace_bytes, true, false, &a);
     if (rc != KDA_OK || B == 0) return rc;
     return kdaconv::launch_kda_chunks(a, dtype == KDA_BF16, static_cast<hipStream_t>(hip_stream)) ==
                    hipSuccess
@@ -274,14 +384,38 @@ int kda_forward_chunks(const kda_stream_desc *desc, int B, int H, int dk, int dv
 int kda_forward_scan(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,
                      const float *initial_state, float *final_state, void *o, const void *workspace,
                      size_t workspace_bytes, void *hip_stream) {
+    Seqs sq;
     KdaArgs a;
-    int rc = prepare_kda(desc, B, H, dk, dv, dtype, nullptr, nullptr, nullptr, nullptr, nullptr,
-                         initial_state, final_state, o, workspace, workspace_bytes, false, true, &a);
+    int rc = uniform_seqs(desc, B, H, dk, dv, dtype, &sq);
+    if (rc == KDA_OK)
+        rc = prepare_kda(sq, H, dk, dv, dtype, nullptr, nullptr, nullptr, nullptr, nullptr, initial_state,
+                         final_state, o, workspace, workspace_bytes, false, true, &a);
     if (rc != KDA_OK || B == 0) return rc;
     return kdaconv::launch_kda_scan(a, dtype == KDA_BF16, static_cast<hipStream_t>(hip_stream)) ==
                    hipSuccess
                ? KDA_OK
                : KDA_ERR_HIP;
+}
+
+int kda_conv_forward_varlen(const kda_stream_desc *descs, int n_seq, int H, int dk, int dv, kda_dtype dtype,
+                            const void *q, const void *k, const void *v, const void *const w_text[3],
+                            const void *const w_vis[3], void *q_out, void *k_out, void *v_out,
+                            void *hip_stream) {
+    Seqs sq;
+    int rc = varlen_seqs(descs, n_seq, H, dk, dv, dtype, &sq);
+    if (rc != KDA_OK) return rc;
+    const int Cs[3] = {H * dk, H * dk, H * dv};
+    const void *in[3] = {q, k, v};
+    void *out[3] = {q_out, k_out, v_out};
+    rc = conv_check_pointers(sq.tokens, 0, Cs, elem_bytes(dtype), in, nullptr, w_text, w_vis, out);
+    if (rc != KDA_OK) return rc;
+    // one launch per sequence, in order on the caller's stream
+    for (int i = 0; i < n_seq; ++i) {
+        rc = conv_launch(&descs[i], 1, sq.tok0[i + 1] - sq.tok0[i], sq.tok0[i], Cs, dtype, in, nullptr, 0, w_text,
+                         w_vis, out, hip_stream);
+        if (rc != KDA_OK) return rc;
+    }
+    return KDA_OK;
 }
 
 }  // extern "C"

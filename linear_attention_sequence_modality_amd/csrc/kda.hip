@@ -18,11 +18,11 @@
 // to the workspace in the exact register-fragment order kernel 2 consumes.
 // The next chunk's inputs are loaded into registers while the current chunk
 // is transformed.
-// Kernel 2 (kda_state_kernel: one 7-wave workgroup per (batch, head,
+// Kernel 2 (kda_state_kernel: one 8-wave workgroup per (batch, head,
 // 16-column slice of dv)) keeps its state slice in the registers of one
-// recurrence wave and feeds it to the matrix cores without any reshuffle; a
-// loader wave stages the chunk operands in an LDS ring, four output waves and
-// a store wave form and write o from the state handed over each step.
+// recurrence wave and feeds it to the matrix cores without any reshuffle;
+// four loader waves stage the chunk operands in an LDS ring, two output waves
+// and a store wave form and write o from the state handed over each step.
 //
 // Decay factorisation: 2^(G_r - G_s) for s <= r is split around the midpoint
 // m(R) = 16R + 8 of the 16-row sub-block R of row r:
@@ -207,9 +207,28 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, col = l & 15, g = l >> 4;
-    // items of this launch: chunks [c0, c1) of every (batch, head), chunk-major
-    const int nchunks = a.n_chunks, nbh = a.B * a.H;
-    const int n_items = nbh * (a.c1 - a.c0);
+    // items: (chunk gc over all sequences, head h), chunk-major: item = gc * H + h
+    const int total = seq_chk0(a, a.B);
+    const int n_items = a.H * total;
+    // an item's chunk: head, chunk index over all sequences, first token, valid rows
+    struct Loc {
+        int h, gc, t0, nr;
+    };
+    auto locate = [&](int it) {
+        Loc L;
+        L.h = it % a.H;
+        L.gc = it / a.H;
+        if (a.varlen) {
+            const int sq = seq_of_chunk(a, L.gc);
+            L.t0 = a.tok0[sq] + (L.gc - a.chk0[sq]) * C;
+            L.nr = min(C, a.tok0[sq + 1] - L.t0);
+        } else {
+            const int sq = L.gc / a.n_chunks, n = L.gc - sq * a.n_chunks;
+            L.t0 = sq * a.T + n * C;
+            L.nr = min(C, a.T - n * C);
+        }
+        return L;
+    };
 
     float *Gs = reinterpret_cast<float *>(smem + SM::X1);   // G, P0-P1 (Lm and Tm32 from P2 on)
     float *Lm = reinterpret_cast<float *>(smem + SM::X1);
@@ -226,11 +245,11 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     float *Fp = reinterpret_cast<float *>(smem + SM::TB_FP);
     float *Bt = reinterpret_cast<float *>(smem + SM::TB_BETA);
 
-    const T *gq = static_cast<const T *>(a.q);
-    const T *gk = static_cast<const T *>(a.k);
-    const T *gv = static_cast<const T *>(a.v);
-    const T *ga = static_cast<const T *>(a.alpha);
-    const T *gb = static_cast<const T *>(a.beta);
+    const T *q_in = static_cast<const T *>(a.q);
+    const T *k_in = static_cast<const T *>(a.k);
+    const T *v_in = static_cast<const T *>(a.v);
+    const T *a_in = static_cast<const T *>(a.alpha);
+    const T *b_in = static_cast<const T *>(a.beta);
 
     // thread roles of the elementwise phases
     const bool key_task = tid < 32 * NCGK, val_task = tid < 32 * NCGV;
@@ -241,47 +260,51 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     // part, each as soon as the current chunk has consumed that part, so the
     // loads drain through the memory pipeline under the compute of P1-P3.
     constexpr int LD_A = 1, LD_KQ = 2, LD_V = 4;   // alpha and beta | k and q | v
-    auto load_inputs = [&](int item, Prefetch<T> &pf, int parts) {
-        const int bh = item % nbh, n = a.c0 + item / nbh;
-        const int b = bh / a.H, h = bh % a.H;
-        const int t0 = n * C, nr = min(C, a.T - t0);
-        // Rows past the end of the stream re-read the last row (in bounds) and
+    auto load_inputs = [&](const Loc &L, Prefetch<T> &pf, int parts) {
+        const int h = L.h, t0 = L.t0, nr = L.nr;
+        // Rows past the end of the sequence re-read the last row (in bounds) and
         // are masked where they are used: the loads never depend on the data
         // and no register is cleared behind a store still in flight.
         if (parts & LD_A) {
             const int r = min(l, nr - 1);
-            const size_t off = (((size_t)b * a.T + (t0 + r)) * a.H + h) * DK + CPW * wv;
+            const size_t off = ((size_t)(t0 + r) * a.H + h) * DK + CPW * wv;
 #pragma unroll
-            for (int j = 0; j < NA; ++j) pf.a[j].load(ga + off + 8 * j);
-            if (tid < C) pf.beta = gb[((size_t)b * a.T + (t0 + min(tid, nr - 1))) * a.H + h];
+            for (int j = 0; j < NA; ++j) pf.a[j].load(a_in + off + 8 * j);
+            if (tid < C) pf.beta = b_in[(size_t)(t0 + min(tid, nr - 1)) * a.H + h];
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             if ((parts & LD_KQ) && key_task) {
                 const int r = min(2 * krp + e, nr - 1);
-                const size_t off = (((size_t)b * a.T + (t0 + r)) * a.H + h) * DK + kc0;
-                pf.k[e].load(gk + off);
-                pf.q[e].load(gq + off);
+                const size_t off = ((size_t)(t0 + r) * a.H + h) * DK + kc0;
+                pf.k[e].load(k_in + off);
+                pf.q[e].load(q_in + off);
             }
             if ((parts & LD_V) && val_task) {
                 const int rv = min(2 * vrp + e, nr - 1);
-                pf.v[e].load(gv + (((size_t)b * a.T + (t0 + rv)) * a.H + h) * DV + vc0);
+                pf.v[e].load(v_in + ((size_t)(t0 + rv) * a.H + h) * DV + vc0);
             }
         }
     };
 
     Prefetch<T> pf;
     int item = blockIdx.x;
-    if (item < n_items) load_inputs(item, pf, LD_A | LD_KQ | LD_V);
+    Loc nxt{0, 0, 0, 0};   // the chunk whose inputs are in the prefetch registers
+    if (item < n_items) {
+        nxt = locate(item);
+        load_inputs(nxt, pf, LD_A | LD_KQ | LD_V);
+    }
     // Enter the loop with the first prefetch retired, as every later iteration
     // is (see P5): the loop's waits then never cover the stores still in flight.
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
 
 #pragma unroll 1
     for (; item < n_items; item += gridDim.x) {
-        const int bh = item % nbh, n = a.c0 + item / nbh;
-        const int nr = min(C, a.T - n * C);   // valid rows in this chunk
-        char *wsb = static_cast<char *>(a.ws) + ((size_t)bh * nchunks + n) * WL::BYTES;
+        const Loc cur = nxt;
+        const int nr = cur.nr;   // valid rows in this chunk
+        const bool more = item + (int)gridDim.x < n_items;
+        if (more) nxt = locate(item + gridDim.x);
+        char *wsb = static_cast<char *>(a.ws) + ((size_t)cur.h * total + cur.gc) * WL::BYTES;
         T *ws = reinterpret_cast<T *>(wsb);
         float *ws_gam = reinterpret_cast<float *>(wsb + WL::GAM_BYTE);
 
@@ -305,8 +328,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
         }
         if (tid < C) Bt[tid] = tid < nr ? (float)pf.beta : 0.f;
         lds_barrier();
-        const bool more = item + (int)gridDim.x < n_items;
-        if (more) load_inputs(item + gridDim.x, pf, LD_A);
+        if (more) load_inputs(nxt, pf, LD_A);
         auto Grow = [&](int R) { return Gs + (R < 4 ? 16 * R + 8 : C - 1) * SM::GS; };   // R = 4: the last row
         {
             // 15 per-channel factors for the later phases: Pm[4], Kh[4], Fp[6], Gam
@@ -376,7 +398,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) st2<T>(RK + krp * SM::RKS + 2 * (kc0 + i), rhs[0][i], rhs[1][i]);
         }
-        if (more) load_inputs(item + gridDim.x, pf, LD_KQ);
+        if (more) load_inputs(nxt, pf, LD_KQ);
         if (val_task) {
             const int s0 = 2 * vrp;
             float vx0[8], vx1[8];
@@ -391,7 +413,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) st2<T>(RV + vrp * SM::RVS + 2 * (vc0 + i), b0 * vx0[i], b1 * vx1[i]);
         }
-        if (more) load_inputs(item + gridDim.x, pf, LD_V);
+        if (more) load_inputs(nxt, pf, LD_V);
         lds_barrier();
 
         // ---- P2: decayed K K^T (-> L) and (Q K^T)^T (-> workspace) on MFMA ----------
@@ -709,11 +731,15 @@ __device__ __forceinline__ void wait_counter_dma(int *ctr, int target, int &budg
     }
 }
 
-// Wave roles of the state pass.  Waves are spread over the four SIMDs in
-// turn, so the store wave (little work) shares SIMD 0 with the recurrence.
+// Wave roles of the state pass.  Waves w and w + 4 of a workgroup run on
+// the same SIMD, so the store wave (little work) is wave 4, beside the
+// recurrence (wave 0); the output waves are 1 and 2, the loaders 3, 5, 6, 7.
 constexpr int kOutWaves = 2;          // output waves; chunk n goes to output wave n % kOutWaves
 constexpr int kLoaders = 4;           // loader waves; chunk p goes to loader p % kLoaders
-constexpr int kStoreWave = 7, kLoaderWave0 = 3;   // loaders are waves 3..6
+constexpr int kStoreWave = 4;
+__device__ __forceinline__ int loader_slot(int wave) {   // loader index, or -1
+    return wave == 3 ? 0 : wave >= 5 ? wave - 4 : -1;
+}
 __device__ __forceinline__ int out_slot(int wave) {   // output wave index, or -1
     return wave == 1 || wave == 2 ? wave - 1 : -1;
 }
@@ -769,21 +795,22 @@ __global__ __launch_bounds__(kScanThreads) void kda_state_kernel(KdaArgs a) {
 
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
     const int jt = blk % NJT, bh = blk / NJT;
-    const int b = bh / a.H, h = bh % a.H;
+    const int sq = bh / a.H, h = bh % a.H;   // sequence, head
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = threadIdx.x & 63, col = l & 15, g = l >> 4;
-    // this launch walks chunks [c0, c1); loop indices below count from c0
-    const int nchunks = a.c1 - a.c0, last = nchunks - 1;
+    // this sequence's chunks [c0, c0 + nchunks) and tokens [tok0, tok0 + ntok)
+    const int c0 = seq_chk0(a, sq), nchunks = seq_chk0(a, sq + 1) - c0, last = nchunks - 1;
+    const int tok0 = seq_tok0(a, sq), ntok = seq_tok0(a, sq + 1) - tok0;
     int budget = kPollBudget;
 
     // this (batch, head)'s workspace: chunk n at byte n * BYTES (< 4 GiB, checked on the host)
-    const char *wsh = static_cast<const char *>(a.ws) + (size_t)bh * a.n_chunks * WL::BYTES;
+    const char *wsh = static_cast<const char *>(a.ws) + ((size_t)h * seq_chk0(a, a.B) + c0) * WL::BYTES;
     const __amdgpu_buffer_rsrc_t wsr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(wsh), 0, (int)(unsigned)((size_t)a.n_chunks * WL::BYTES), kBufWord3);
+        const_cast<char *>(wsh), 0, (int)(unsigned)((size_t)nchunks * WL::BYTES), kBufWord3);
     const unsigned lane8 = (unsigned)l * 8 * ES;   // lane's fragment inside a [64][8] block
-    auto cbase = [&](int i) { return (unsigned)(a.c0 + i) * (unsigned)WL::BYTES; };
+    auto cbase = [&](int i) { return (unsigned)i * (unsigned)WL::BYTES; };
 
-    if (wave >= kLoaderWave0 && wave < kLoaderWave0 + kLoaders) {
+    if (loader_slot(wave) >= 0) {
         // ---------------- loaders: recurrence operands -> LDS ----------------
         // Loader q takes chunks p = q, q + kLoaders, ...: it loads the chunk's
         // W, Kh^T, Ut slice and Gam into its registers (16 bytes per lane,
@@ -792,7 +819,7 @@ __global__ __launch_bounds__(kScanThreads) void kda_state_kernel(KdaArgs a) {
         // chunk.  With kLoaders waves each holding a chunk in flight, the loads
         // of chunk p are issued about kLoaders + kOpRing - 1 chunk steps before
         // the recurrence reads it, which covers the memory latency.
-        const int q = wave - kLoaderWave0;
+        const int q = loader_slot(wave);
         u32x4_t r[SL::NI];
         int nload = 0;   // chunks this loader has staged
         auto load = [&](int p) {
@@ -1014,8 +1041,8 @@ __global__ __launch_bounds__(kScanThreads) void kda_state_kernel(KdaArgs a) {
         // and the hardware drops their stores.  The output tile is transposed
         // (lane: 4 consecutive value columns of one token).
         const unsigned orow = (unsigned)a.H * DV * ES;
-        char *obase = static_cast<char *>(a.o) + ((((size_t)b * a.T) * a.H + h) * DV + 16 * jt) * ES;
-        const unsigned onum = (unsigned)a.T * orow - (unsigned)(h * DV + 16 * jt) * ES;
+        char *obase = static_cast<char *>(a.o) + (((size_t)tok0 * a.H + h) * DV + 16 * jt) * ES;
+        const unsigned onum = (unsigned)ntok * orow - (unsigned)(h * DV + 16 * jt) * ES;
         const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(obase, 0, (int)onum, kBufWord3);
         const unsigned ovoff = (unsigned)col * orow + (unsigned)(4 * g) * ES;
 #pragma unroll 1
@@ -1027,7 +1054,7 @@ __global__ __launch_bounds__(kScanThreads) void kda_state_kernel(KdaArgs a) {
             signal_counter(&ctr[kOCons], n + 1);
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
-                const unsigned soff = ((unsigned)(a.c0 + n) * C + 16u * R) * orow;
+                const unsigned soff = ((unsigned)n * C + 16u * R) * orow;
                 if (sizeof(T) == 2) {
                     u32x2_t v;
                     v[0] = pack_bf16x2(O[R][0], O[R][1]);
@@ -1054,7 +1081,7 @@ hipError_t launch_chunks_typed(const KdaArgs &a, hipStream_t stream) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int items = a.B * a.H * (a.c1 - a.c0);
+    const int items = a.H * seq_chk0(a, a.B);
     const int grid = items < num_cus() ? items : num_cus();
     hipLaunchKernelGGL((kda_intra_kernel<T, DK, DV>), dim3(grid), dim3(K1_THREADS), SM::BYTES, stream, a);
     return hipGetLastError();
@@ -1068,7 +1095,7 @@ hipError_t launch_scan_typed(const KdaArgs &a, hipStream_t stream) {
 }
 
 #define KDA_DISPATCH(FN)                                                                           \
-    if (a.B * a.H * (a.c1 - a.c0) == 0) return hipSuccess;                                         \
+    if (a.B == 0 || seq_chk0(a, a.B) == 0) return hipSuccess;                                      \
     if (bf16) {                                                                                    \
         if (a.dk == 64 && a.dv == 64) return FN<bf16_t, 64, 64>(a, stream);                        \
         if (a.dk == 64 && a.dv == 128) return FN<bf16_t, 64, 128>(a, stream);                      \

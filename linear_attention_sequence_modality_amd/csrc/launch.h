@@ -25,16 +25,39 @@ hipError_t launch_conv(const ConvArgs &a, bool bf16, hipStream_t stream);
 // ---- chunked KDA -----------------------------------------------------------
 constexpr int kChunk = 64;  // tokens per chunk
 
+constexpr int kMaxSeqs = 64;  // sequences of one variable-length batch
+
+// The token axis of q, k, v, alpha, beta and o holds B sequences one after
+// another: all of length T (a uniform batch, [B, T, H, d]), or sequence i at
+// tokens [tok0[i], tok0[i+1]) (a variable-length batch, [1, sum T_i, H, d]).
+// Each sequence is split into chunks of kChunk tokens (its last one ragged);
+// the workspace holds chunk g of head h at index h * total chunks + g, where
+// sequence i owns chunks [chk0[i], chk0[i+1]).
 struct KdaArgs {
     const void *q, *k, *v, *alpha, *beta;
     const float *s0;     // [B, H, dk, dv] or null
     float *sT;           // [B, H, dk, dv] or null
-    void *o;             // [B, T, H, dv]
+    void *o;             // token axis as above, [.., H, dv]
     void *ws;            // chunk workspace
     int B, T, H, dk, dv;
-    int n_chunks;        // ceil(T / kChunk)
-    int c0, c1;          // chunks [c0, c1) of every (batch, head) processed by one launch
+    int n_chunks;        // uniform batch: ceil(T / kChunk)
+    int varlen;          // nonzero: the tables below give the sequences
+    int tok0[kMaxSeqs + 1], chk0[kMaxSeqs + 1];
 };
+// First token and first chunk of sequence i (i = B: the totals).
+__host__ __device__ inline int seq_tok0(const KdaArgs &a, int i) { return a.varlen ? a.tok0[i] : i * a.T; }
+__host__ __device__ inline int seq_chk0(const KdaArgs &a, int i) { return a.varlen ? a.chk0[i] : i * a.n_chunks; }
+// Sequence that owns chunk g (0 <= g < total chunks).
+__device__ inline int seq_of_chunk(const KdaArgs &a, int g) {
+    if (!a.varlen) return g / a.n_chunks;
+    int lo = 0, hi = a.B;   // chk0[lo] <= g < chk0[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.chk0[mid] <= g) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
 
 // Workspace bytes for one (batch, head, chunk).
 size_t kda_chunk_ws_bytes(int dk, int dv, bool bf16);

@@ -24,8 +24,11 @@ KDA_ERR_UNSUPPORTED = -2
 KDA_ERR_WORKSPACE = -3
 KDA_ERR_HIP = -4
 
+KDA_MAX_SEQS = 64   # streams of one variable-length batch
+
 EXPORTED_SYMBOLS = ("kda_conv_forward", "kda_conv_forward_stream", "kda_forward_workspace_size", "kda_forward",
-                    "kda_forward_chunks", "kda_forward_scan", "kda_status_string")
+                    "kda_forward_chunks", "kda_forward_scan", "kda_forward_varlen_workspace_size",
+                    "kda_forward_varlen", "kda_conv_forward_varlen", "kda_status_string")
 
 
 class KdaStreamDesc(ctypes.Structure):
@@ -73,6 +76,14 @@ def load_library():
     lib.kda_forward_scan.restype = i32
     lib.kda_forward_scan.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                      ctypes.c_size_t, vp]
+    lib.kda_forward_varlen_workspace_size.restype = ctypes.c_size_t
+    lib.kda_forward_varlen_workspace_size.argtypes = [desc_p, i32, i32, i32, i32, i32]
+    lib.kda_forward_varlen.restype = i32
+    lib.kda_forward_varlen.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       vp, ctypes.c_size_t, vp]
+    lib.kda_conv_forward_varlen.restype = i32
+    lib.kda_conv_forward_varlen.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp,
+                                            ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [i32]
     _lib = lib
@@ -235,6 +246,85 @@ def kda_forward_scan(desc: KdaStreamDesc, B: int, H: int, dk: int, dv: int, dtyp
     if rc != KDA_OK:
         raise KdaError("kda_forward_scan", rc)
     return o
+
+
+def _desc_array(descs: Sequence[KdaStreamDesc]):
+    arr = (KdaStreamDesc * max(len(descs), 1))()
+    for i, d in enumerate(descs):
+        arr[i] = d
+    return arr
+
+
+def kda_forward_varlen_workspace_size(descs: Sequence[KdaStreamDesc], H: int, dk: int, dv: int,
+                                      dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(load_library().kda_forward_varlen_workspace_size(_desc_array(descs), len(descs), H, dk, dv,
+                                                                code))
+
+
+def kda_forward_varlen(descs: Sequence[KdaStreamDesc], q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       alpha: torch.Tensor, beta: torch.Tensor,
+                       initial_state: Optional[torch.Tensor] = None,
+                       final_state: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """KDA over a variable-length batch: stream i of ``descs`` at its tokens of the packed
+    token axis of q [sum T_i, H, dk] (a leading axis of size 1 is allowed); states are
+    [len(descs), H, dk, dv].  Returns o shaped like v."""
+    lib = load_library()
+    dt = q.dtype
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (alpha, "alpha"), (beta, "beta")):
+        _check(t, nm, dt)
+    H, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    total = sum(d.n_text + d.grid_t * d.grid_h * d.grid_w for d in descs)
+    if q.numel() != total * H * dk or v.numel() != total * H * dv or beta.numel() != total * H:
+        raise ValueError("q, k, v, alpha, beta must hold the %d tokens of the streams" % total)
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None:
+            _check(t, nm, torch.float32)
+    o = torch.empty_like(v) if o is None else o
+    _check(o, "o", dt)
+    need = kda_forward_varlen_workspace_size(descs, H, dk, dv, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = lib.kda_forward_varlen(_desc_array(descs), len(descs), H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k),
+                                _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(final_state),
+                                _ptr(o), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_forward_varlen", rc)
+    return o
+
+
+def kda_conv_forward_varlen(descs: Sequence[KdaStreamDesc], q: torch.Tensor, k: torch.Tensor,
+                            v: torch.Tensor, w_text: Sequence[torch.Tensor], w_vis: Sequence[torch.Tensor],
+                            q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
+                            v_out: Optional[torch.Tensor] = None, stream=None
+                            ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """The short conv over a variable-length batch packed along the token axis."""
+    lib = load_library()
+    dt = q.dtype
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm, dt)
+    for i in range(3):
+        _check(w_text[i], "w_text[%d]" % i, dt)
+        _check(w_vis[i], "w_vis[%d]" % i, dt)
+    H, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    total = sum(d.n_text + d.grid_t * d.grid_h * d.grid_w for d in descs)
+    if q.numel() != total * H * dk or k.numel() != total * H * dk or v.numel() != total * H * dv:
+        raise ValueError("q, k, v must hold the %d tokens of the streams" % total)
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    v_out = torch.empty_like(v) if v_out is None else v_out
+    wt = (ctypes.c_void_p * 3)(*[w.data_ptr() for w in w_text])
+    wv = (ctypes.c_void_p * 3)(*[w.data_ptr() for w in w_vis])
+    rc = lib.kda_conv_forward_varlen(_desc_array(descs), len(descs), H, dk, dv, _dtype_code(dt), _ptr(q),
+                                     _ptr(k), _ptr(v), wt, wv, _ptr(q_out), _ptr(k_out), _ptr(v_out),
+                                     _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_conv_forward_varlen", rc)
+    return q_out, k_out, v_out
 
 
 def conv_kda_forward(desc: KdaStreamDesc, inp: dict, initial_state=None, final_state=None,

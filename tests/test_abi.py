@@ -159,3 +159,78 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         kda.kda_forward(kda.make_desc(4, (0, 0, 0)), x, x, x, x, torch.zeros(1, 4, 1, dtype=torch.bfloat16))
+
+
+def _descs(*ds):
+    arr = (kda.KdaStreamDesc * max(len(ds), 1))()
+    for i, d in enumerate(ds):
+        arr[i] = d
+    return arr
+
+
+def _fwd_varlen(lib, descs, n, H=2, dk=64, dv=64, dtype=kda.KDA_BF16, ptrs=None, ws=FAKE + 40 * (1 << 32),
+                ws_bytes=1 << 40):
+    p = ptrs if ptrs is not None else _ptrs(6)
+    return lib.kda_forward_varlen(descs, n, H, dk, dv, dtype, p[0], p[1], p[2], p[3], p[4], None, None, p[5],
+                                  ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+
+
+def _conv_varlen(lib, descs, n, H=2, dk=64, dv=64, ptrs=None):
+    p = ptrs if ptrs is not None else _ptrs(6)
+    wt = (ctypes.c_void_p * 3)(*[FAKE + (20 + i) * (1 << 32) for i in range(3)])
+    wv = (ctypes.c_void_p * 3)(*[FAKE + (30 + i) * (1 << 32) for i in range(3)])
+    return lib.kda_conv_forward_varlen(descs, n, H, dk, dv, kda.KDA_BF16, p[0], p[1], p[2], wt, wv,
+                                       p[3], p[4], p[5], None)
+
+
+def test_varlen_workspace_is_the_sum_of_the_streams(lib):
+    a, b, c = _desc(n_text=5, grid=(1, 7, 9)), _desc(n_text=0, grid=(3, 10, 12)), _desc(n_text=200, grid=(0, 0, 0))
+    one = [kda.kda_forward_workspace_size(d, 1, 2, 128, 128, kda.KDA_BF16) for d in (a, b, c)]
+    assert all(x > 0 for x in one)
+    assert kda.kda_forward_varlen_workspace_size([a, b, c], 2, 128, 128, torch_bf16()) == sum(one)
+    assert kda.kda_forward_varlen_workspace_size([b], 2, 128, 128, torch_bf16()) == one[1]
+    assert lib.kda_forward_varlen_workspace_size(None, 1, 2, 64, 64, kda.KDA_BF16) == 0
+    assert lib.kda_forward_varlen_workspace_size(_descs(a), 0, 2, 64, 64, kda.KDA_BF16) == 0
+
+
+def torch_bf16():
+    import torch
+    return torch.bfloat16
+
+
+def test_varlen_rejects_bad_arguments(lib):
+    a, b = _desc(n_text=5, grid=(1, 7, 9)), _desc(n_text=0, grid=(3, 10, 12))
+    ok = _descs(a, b)
+    assert _fwd_varlen(lib, None, 2) == kda.KDA_ERR_INVALID_ARG
+    assert _fwd_varlen(lib, ok, 0) == kda.KDA_ERR_INVALID_ARG
+    many = _descs(*([a] * (kda.KDA_MAX_SEQS + 1)))
+    assert _fwd_varlen(lib, many, kda.KDA_MAX_SEQS + 1) == kda.KDA_ERR_UNSUPPORTED
+    assert _conv_varlen(lib, many, kda.KDA_MAX_SEQS + 1) == kda.KDA_ERR_UNSUPPORTED
+    empty = _descs(a, _desc(n_text=0, grid=(0, 0, 0)))                 # a stream of no tokens
+    assert _fwd_varlen(lib, empty, 2) == kda.KDA_ERR_INVALID_ARG
+    assert _conv_varlen(lib, empty, 2) == kda.KDA_ERR_INVALID_ARG
+    assert _fwd_varlen(lib, _descs(a, _desc(k_vis=5)), 2) == kda.KDA_ERR_UNSUPPORTED
+    need = lib.kda_forward_varlen_workspace_size(ok, 2, 2, 64, 64, kda.KDA_BF16)
+    assert need > 0
+    assert _fwd_varlen(lib, ok, 2, ws_bytes=need - 1) == kda.KDA_ERR_WORKSPACE
+    assert _fwd_varlen(lib, ok, 2, ws=0) == kda.KDA_ERR_WORKSPACE
+    p = _ptrs(6)
+    p[5] = ctypes.c_void_p(FAKE + 2 * (1 << 32) + 64)                  # o overlaps v
+    assert _fwd_varlen(lib, ok, 2, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    p = _ptrs(6)
+    p[3] = ctypes.c_void_p(FAKE + 32)                                  # q_out overlaps q
+    assert _conv_varlen(lib, ok, 2, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    # ranges cover the packed axis: o starting right after the last token of v is fine
+    T = 5 + 63 + 360
+    p = _ptrs(6)
+    p[5] = ctypes.c_void_p(FAKE + 2 * (1 << 32) + T * 2 * 64 * 2)
+    p[3] = ctypes.c_void_p(FAKE + 50 * (1 << 32))                      # alpha elsewhere
+    assert _fwd_varlen(lib, ok, 2, ptrs=p, ws=0) == kda.KDA_ERR_WORKSPACE   # got past the overlap checks
+    p[5] = ctypes.c_void_p(FAKE + 2 * (1 << 32) + T * 2 * 64 * 2 - 16)
+    assert _fwd_varlen(lib, ok, 2, ptrs=p, ws=0) == kda.KDA_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op(lib):
+    d = _desc()
+    assert _fwd(lib, d, B=0) == kda.KDA_OK
+    assert _conv(lib, d, B=0) == kda.KDA_OK

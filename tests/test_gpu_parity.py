@@ -230,6 +230,84 @@ def test_time_causal_stream_in_segments_equals_one_pass(dtype):
     assert e_o <= TOL[dtype] and e_s <= TOL[dtype]
 
 
+def _varlen_run(cfgs, s0_scale=0.3):
+    """Pack the streams' inputs (sharing the first stream's conv weights) and run the
+    variable-length conv and KDA; also run each stream alone.  Returns what the checks need."""
+    hosts = [make_inputs(c) for c in cfgs]
+    for h in hosts[1:]:
+        for w in ("w_text_q", "w_text_k", "w_text_v", "w_vis_q", "w_vis_k", "w_vis_v"):
+            h[w] = hosts[0][w]
+    devs = [to_dev(h) for h in hosts]
+    d0 = devs[0]
+    wt = (d0["w_text_q"], d0["w_text_k"], d0["w_text_v"])
+    wv = (d0["w_vis_q"], d0["w_vis_k"], d0["w_vis_v"])
+    descs = [desc_of(c) for c in cfgs]
+    pack = {k: torch.cat([d[k][0] for d in devs], dim=0).contiguous() for k in ("q", "k", "v", "alpha", "beta")}
+    c0 = cfgs[0]
+    g = torch.Generator().manual_seed(11)
+    s0 = (torch.randn(len(cfgs), c0.H, c0.dk, c0.dv, generator=g) * s0_scale).cuda()
+    sT = torch.empty_like(s0)
+    qc, kc, vc = kda.kda_conv_forward_varlen(descs, pack["q"], pack["k"], pack["v"], wt, wv)
+    o = kda.kda_forward_varlen(descs, qc, kc, vc, pack["alpha"], pack["beta"], initial_state=s0, final_state=sT)
+    alone = []
+    for i, (c, d) in enumerate(zip(cfgs, devs)):
+        cq, ck, cv = kda.kda_conv_forward(descs[i], d["q"], d["k"], d["v"], wt, wv)
+        st = torch.empty(1, c.H, c.dk, c.dv, device="cuda")
+        oi = kda.kda_forward(descs[i], cq, ck, cv, d["alpha"], d["beta"], initial_state=s0[i:i + 1].contiguous(),
+                             final_state=st)
+        alone.append((cq, ck, cv, oi, st))
+    torch.cuda.synchronize()
+    return hosts, s0, (qc, kc, vc, o, sT), alone
+
+
+@pytest.mark.timeout(120)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_varlen_batch_equals_each_stream_alone(dtype):
+    """A batch mixing a video, a text-only stream, a one-chunk image, a time-causal
+    video and a one-token stream: each stream's conv outputs, o and final state equal
+    those of the stream run alone, bit for bit, and match the oracle."""
+    kw = dict(dk=64, dv=64) if dtype == "f32" else {}
+    cfgs = [_small("vl_video", n_text=7, grid=(3, 5, 9), dtype=dtype, seed=1, **kw),
+            _small("vl_text", n_text=200, grid=(0, 0, 0), dtype=dtype, seed=2, **kw),
+            _small("vl_image", n_text=0, grid=(1, 8, 8), dtype=dtype, seed=3, **kw),
+            _small("vl_causal", n_text=3, grid=(2, 6, 7), causal_t=1, dtype=dtype, seed=4, **kw),
+            _small("vl_one", n_text=1, grid=(0, 0, 0), dtype=dtype, seed=5, **kw)]
+    say("case varlen %s T=%s" % (dtype, [c.T for c in cfgs]))
+    hosts, s0, packed, alone = _varlen_run(cfgs)
+    qc, kc, vc, o, sT = packed
+    tok = 0
+    heads = tuple(range(cfgs[0].H))
+    for i, (c, h, al) in enumerate(zip(cfgs, hosts, alone)):
+        sl = slice(tok, tok + c.T)
+        for x, y in zip((qc, kc, vc, o), al[:4]):
+            assert torch.equal(x[sl], y[0]), (c.name, "packed != alone")
+        assert torch.equal(sT[i:i + 1], al[4]), (c.name, "state")
+        _, _, _, ro, rs = oracle_end_to_end_heads(c, h, heads, s0[i:i + 1].double().cpu().numpy())
+        e_o = rel(heads_slice(o[sl][None], heads), ro)
+        e_s = oracle.rel_err_state(sT[i:i + 1].double().cpu().numpy(), rs)
+        say("  %s T=%d rel err o %.2e S %.2e" % (c.name, c.T, e_o, e_s))
+        assert e_o <= TOL[dtype] and e_s <= TOL[dtype]
+        tok += c.T
+
+
+@pytest.mark.timeout(120)
+def test_varlen_batch_of_the_most_streams():
+    """KDA_MAX_SEQS text streams of ragged lengths (1 to 150 tokens): every stream's o
+    and final state equal its own call."""
+    rng = np.random.default_rng(9)
+    lens = [int(x) for x in rng.integers(1, 151, size=kda.KDA_MAX_SEQS)]
+    lens[0], lens[-1] = 64, 1
+    cfgs = [_small("vl_%d" % i, n_text=n, grid=(0, 0, 0), H=1, seed=100 + i) for i, n in enumerate(lens)]
+    say("case varlen %d streams, %d tokens" % (len(cfgs), sum(lens)))
+    _, _, packed, alone = _varlen_run(cfgs)
+    o, sT = packed[3], packed[4]
+    tok = 0
+    for i, (c, al) in enumerate(zip(cfgs, alone)):
+        assert torch.equal(o[tok:tok + c.T], al[3][0]), c.name
+        assert torch.equal(sT[i:i + 1], al[4]), c.name
+        tok += c.T
+
+
 # ---- hygiene -----------------------------------------------------------------------
 
 @pytest.mark.timeout(120)
