@@ -138,3 +138,49 @@ def token_index(cfg: StreamConfig, t: int, h: int, w: int) -> int:
     """Stream position of visual token (t, h, w): text first, then raster order."""
     _, gh, gw = cfg.grid
     return cfg.n_text + (t * gh + h) * gw + w
+
+
+# ---- the MLA layers' attention core (one of every four token-mixer layers) ----------
+
+@dataclass(frozen=True)
+class MlaConfig:
+    """Attention-core shapes of one MLA layer over a token stream of T tokens.
+
+    Per head: a d_nope-wide key part decompressed from the latent, a d_dir-wide
+    key part shared by all heads (K_direct), and dv-wide values.
+    """
+
+    name: str
+    B: int
+    T: int
+    H: int
+    d_nope: int = 128
+    d_dir: int = 64
+    dv: int = 128
+    seed: int = 0
+
+    def with_(self, **kw) -> "MlaConfig":
+        return replace(self, **kw)
+
+
+MLA_WORKLOADS = [
+    MlaConfig("mla_tiny", B=2, T=333, H=2, seed=21),
+    MlaConfig("mla_image_1024px", B=8, T=4608, H=4, seed=22),     # the proxy-width image stream
+    MlaConfig("mla_video_5s_480x832", B=1, T=33272, H=16, seed=23),
+]
+MLA_WORKLOAD = {c.name: c for c in MLA_WORKLOADS}
+
+
+def make_mla_inputs(cfg: MlaConfig, seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Seeded bf16 CPU tensors: q_nope, k_nope [B,T,H,d_nope]; q_dir [B,T,H,d_dir];
+    k_dir [B,T,d_dir]; v [B,T,H,dv].  Every entry ~ N(0, 1), drawn in that
+    order in fp32 and rounded to bf16."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    B, T, H = cfg.B, cfg.T, cfg.H
+    f32 = np.float32
+    out = {"q_nope": rng.standard_normal((B, T, H, cfg.d_nope), dtype=f32),
+           "k_nope": rng.standard_normal((B, T, H, cfg.d_nope), dtype=f32),
+           "q_dir": rng.standard_normal((B, T, H, cfg.d_dir), dtype=f32),
+           "k_dir": rng.standard_normal((B, T, cfg.d_dir), dtype=f32),
+           "v": rng.standard_normal((B, T, H, cfg.dv), dtype=f32)}
+    return {name: torch.from_numpy(a).to(torch.bfloat16) for name, a in out.items()}
