@@ -207,6 +207,28 @@ int kda_conv_forward_varlen(const kda_stream_desc *descs, int n_seq, int H, int 
                             const void *const w_text[3], const void *const w_vis[3],
                             void *q_out, void *k_out, void *v_out, void *hip_stream);
 
+/*
+ * Attention core of the MLA layers that fill one of every four token-mixer
+ * layers (Chimera pages, paper.rainbus.top, prerequisites section, the
+ * Multi-head Latent Attention paragraph): keys and values are decompressed
+ * from a latent by plain projections (not part of this call), and every head
+ * also sees one key part shared by all heads (K_direct).  Full bidirectional
+ * softmax attention within each stream: for stream b, head h, query i,
+ *   s_j = scale * (q_nope[b,i,h] . k_nope[b,j,h] + q_dir[b,i,h] . k_dir[b,j])
+ *   o[b,i,h] = sum_j softmax_j(s) v[b,j,h]          (j over all T tokens)
+ * Layouts (row-major, contiguous): q_nope, k_nope [B, T, H, d_nope];
+ * q_dir [B, T, H, d_dir]; k_dir [B, T, d_dir]; v, o [B, T, H, dv].
+ * Supported: KDA_BF16 with d_nope = 128, d_dir = 64, dv = 128 (fp32
+ * accumulation, o rounded to bf16); anything else is KDA_ERR_UNSUPPORTED.
+ * scale must be finite and > 0 (1 / sqrt(d_nope + d_dir) is the usual one).
+ * Errors: KDA_ERR_INVALID_ARG for B < 0, T < 1, H < 1, a bad scale, a NULL
+ * or misaligned pointer, or o overlapping an input.
+ */
+int mla_attention_forward(int B, int T, int H, int d_nope, int d_dir, int dv, kda_dtype dtype,
+                          const void *q_nope, const void *q_dir, const void *k_nope,
+                          const void *k_dir, const void *v, float scale, void *o,
+                          void *hip_stream);
+
 /* Static, human-readable text for a status code. */
 const char *kda_status_string(int status);
 

@@ -1,6 +1,7 @@
 // C-ABI entry points: argument validation (host only, before any HIP call)
 // and kernel launches on the caller's stream.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "../../include/kdaconv.h"
@@ -416,6 +417,42 @@ int kda_conv_forward_varlen(const kda_stream_desc *descs, int n_seq, int H, int 
         if (rc != KDA_OK) return rc;
     }
     return KDA_OK;
+}
+
+int mla_attention_forward(int B, int T, int H, int d_nope, int d_dir, int dv, kda_dtype dtype, const void *q_nope,
+                          const void *q_dir, const void *k_nope, const void *k_dir, const void *v, float scale,
+                          void *o, void *hip_stream) {
+    if (B < 0 || T < 1 || H < 1) return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
+    if (dtype != KDA_BF16 || d_nope != 128 || d_dir != 64 || dv != 128) return KDA_ERR_UNSUPPORTED;
+    if (!(scale > 0.f) || !(scale < INFINITY)) return KDA_ERR_INVALID_ARG;
+    // token and block indices stay in 32 bits
+    if ((int64_t)B * T * H * 128 >= kMaxTokens * 2 || (int64_t)B * H * ((T + 127) / 128) >= kMaxTokens)
+        return KDA_ERR_UNSUPPORTED;
+    const void *ins[5] = {q_nope, q_dir, k_nope, k_dir, v};
+    const size_t es = 2, BT = (size_t)B * (size_t)T;
+    const size_t nbytes[5] = {BT * H * d_nope * es, BT * H * d_dir * es, BT * H * d_nope * es, BT * d_dir * es,
+                              BT * H * dv * es};
+    if (!o || !aligned16(o)) return KDA_ERR_INVALID_ARG;
+    const Range ro = range_of(o, BT * H * dv * es);
+    for (int i = 0; i < 5; ++i) {
+        if (!ins[i] || !aligned16(ins[i])) return KDA_ERR_INVALID_ARG;
+        if (overlaps(ro, range_of(ins[i], nbytes[i]))) return KDA_ERR_INVALID_ARG;
+    }
+    if (B == 0) return KDA_OK;
+    kdaconv::MlaArgs a;
+    a.q_nope = q_nope;
+    a.q_dir = q_dir;
+    a.k_nope = k_nope;
+    a.k_dir = k_dir;
+    a.v = v;
+    a.o = o;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.scale = scale;
+    return kdaconv::launch_mla_attention(a, static_cast<hipStream_t>(hip_stream)) == hipSuccess ? KDA_OK
+                                                                                               : KDA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -49,6 +49,9 @@ __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Fourth descriptor word of a raw (untyped, stride 0) buffer resource on gfx9.
+constexpr int kBufWord3 = 0x00020000;
+
 // ---- XCD-aware block remap --------------------------------------------------
 // Workgroups are dealt round-robin over the 8 XCDs (each with its own L2).
 // Remap the hardware block id so that every XCD receives a contiguous range

@@ -44,9 +44,6 @@ constexpr int CPW = 2 * LANES;          // channels per workgroup
 constexpr int TC = WR + 2;              // tile columns (w halo)
 constexpr int TP = (HR + 2) * TC;       // tile positions per slice
 
-// Fourth descriptor word of a raw (untyped, stride 0) buffer resource on gfx9.
-constexpr int kBufferWord3 = 0x00020000;
-
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -325,15 +322,15 @@ __device__ void visual_block(const ConvArgs &a, const Layout &L, int s, int blk,
     const size_t bbytes = (size_t)a.T * v.rowb;   // < 4 GiB, checked on the host
     v.rx = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(static_cast<const char *>(a.x[s])) + (size_t)b * bbytes, 0, (int)(unsigned)bbytes,
-        kBufferWord3);
+        kBufWord3);
     v.ry = __builtin_amdgcn_make_buffer_rsrc(static_cast<char *>(a.y[s]) + (size_t)b * bbytes, 0,
-                                             (int)(unsigned)bbytes, kBufferWord3);
+                                             (int)(unsigned)bbytes, kBufWord3);
     if constexpr (HIST) {
         v.ti0 = -a.n_hist;
         const size_t hbytes = (size_t)a.n_hist * v.slice_bytes;   // history of one batch
         v.rh = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<char *>(static_cast<const char *>(a.hx[s])) + (size_t)b * hbytes, 0, (int)(unsigned)hbytes,
-            kBufferWord3);
+            kBufWord3);
     }
     // tile position p of load instruction k: k * PPI + lane / LPP; positions
     // outside the grid load a clamped in-grid token that is never read

@@ -39,7 +39,6 @@ namespace {
 
 constexpr int C = kChunk;          // 64 tokens per chunk
 constexpr int K1_THREADS = 512;    // 8 waves
-constexpr int kBufWord3 = 0x00020000;   // 4th descriptor word of a raw gfx9 buffer
 
 constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -67,4 +67,15 @@ hipError_t launch_kda_scan(const KdaArgs &a, bool bf16, hipStream_t stream);
 // Compute units of the current device.
 int num_cus();
 
+// ---- MLA attention core ----------------------------------------------------
+// q_nope, k_nope [B, T, H, 128]; q_dir [B, T, H, 64]; k_dir [B, T, 64] (shared
+// by the heads); v, o [B, T, H, 128]; bf16.
+struct MlaArgs {
+    const void *q_nope, *q_dir, *k_nope, *k_dir, *v;
+    void *o;
+    int B, T, H;
+    float scale;
+};
+hipError_t launch_mla_attention(const MlaArgs &a, hipStream_t stream);
+
 }  // namespace kdaconv

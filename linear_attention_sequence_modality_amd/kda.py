@@ -28,7 +28,8 @@ KDA_MAX_SEQS = 64   # streams of one variable-length batch
 
 EXPORTED_SYMBOLS = ("kda_conv_forward", "kda_conv_forward_stream", "kda_forward_workspace_size", "kda_forward",
                     "kda_forward_chunks", "kda_forward_scan", "kda_forward_varlen_workspace_size",
-                    "kda_forward_varlen", "kda_conv_forward_varlen", "kda_status_string")
+                    "kda_forward_varlen", "kda_conv_forward_varlen", "mla_attention_forward",
+                    "kda_status_string")
 
 
 class KdaStreamDesc(ctypes.Structure):
@@ -84,6 +85,8 @@ def load_library():
     lib.kda_conv_forward_varlen.restype = i32
     lib.kda_conv_forward_varlen.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp,
                                             ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp]
+    lib.mla_attention_forward.restype = i32
+    lib.mla_attention_forward.argtypes = [i32] * 7 + [vp] * 5 + [ctypes.c_float, vp, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [i32]
     _lib = lib
@@ -325,6 +328,31 @@ def kda_conv_forward_varlen(descs: Sequence[KdaStreamDesc], q: torch.Tensor, k: 
     if rc != KDA_OK:
         raise KdaError("kda_conv_forward_varlen", rc)
     return q_out, k_out, v_out
+
+
+def mla_attention_forward(q_nope: torch.Tensor, q_dir: torch.Tensor, k_nope: torch.Tensor,
+                          k_dir: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+                          o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """MLA attention core: q_nope, k_nope [B,T,H,d_nope]; q_dir [B,T,H,d_dir]; k_dir [B,T,d_dir]
+    (shared by the heads); v [B,T,H,dv].  Returns o shaped like v.  ``scale`` defaults to
+    1/sqrt(d_nope + d_dir)."""
+    lib = load_library()
+    dt = q_nope.dtype
+    for t, nm in ((q_nope, "q_nope"), (q_dir, "q_dir"), (k_nope, "k_nope"), (k_dir, "k_dir"), (v, "v")):
+        _check(t, nm, dt)
+    B, T, H, dn = q_nope.shape
+    dr, dv = q_dir.shape[-1], v.shape[-1]
+    if (tuple(q_dir.shape) != (B, T, H, dr) or tuple(k_nope.shape) != (B, T, H, dn)
+            or tuple(k_dir.shape) != (B, T, dr) or tuple(v.shape[:3]) != (B, T, H)):
+        raise ValueError("q_nope/k_nope [B,T,H,dn], q_dir [B,T,H,dr], k_dir [B,T,dr], v [B,T,H,dv] expected")
+    scale = 1.0 / float(dn + dr) ** 0.5 if scale is None else float(scale)
+    o = torch.empty_like(v) if o is None else o
+    _check(o, "o", dt)
+    rc = lib.mla_attention_forward(B, T, H, dn, dr, dv, _dtype_code(dt), _ptr(q_nope), _ptr(q_dir), _ptr(k_nope),
+                                   _ptr(k_dir), _ptr(v), ctypes.c_float(scale), _ptr(o), _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError("mla_attention_forward", rc)
+    return o
 
 
 def conv_kda_forward(desc: KdaStreamDesc, inp: dict, initial_state=None, final_state=None,

@@ -17,7 +17,7 @@ FAKE = 0x7f0000000000          # 16-byte aligned, never dereferenced: every call
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:kda|mla)_[a-z_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -234,3 +234,33 @@ def test_empty_batch_is_a_no_op(lib):
     d = _desc()
     assert _fwd(lib, d, B=0) == kda.KDA_OK
     assert _conv(lib, d, B=0) == kda.KDA_OK
+
+
+def _mla(lib, B=1, T=100, H=2, dn=128, dr=64, dv=128, dtype=kda.KDA_BF16, scale=0.07, ptrs=None):
+    p = ptrs if ptrs is not None else _ptrs(6)
+    return lib.mla_attention_forward(B, T, H, dn, dr, dv, dtype, p[0], p[1], p[2], p[3], p[4],
+                                     ctypes.c_float(scale), p[5], None)
+
+
+def test_mla_rejects_bad_arguments(lib):
+    assert _mla(lib, dtype=kda.KDA_F32) == kda.KDA_ERR_UNSUPPORTED
+    assert _mla(lib, dtype=9) == kda.KDA_ERR_UNSUPPORTED
+    assert _mla(lib, dn=64) == kda.KDA_ERR_UNSUPPORTED
+    assert _mla(lib, dr=32) == kda.KDA_ERR_UNSUPPORTED
+    assert _mla(lib, dv=64) == kda.KDA_ERR_UNSUPPORTED
+    assert _mla(lib, T=0) == kda.KDA_ERR_INVALID_ARG
+    assert _mla(lib, H=0) == kda.KDA_ERR_INVALID_ARG
+    assert _mla(lib, B=-1) == kda.KDA_ERR_INVALID_ARG
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert _mla(lib, scale=bad) == kda.KDA_ERR_INVALID_ARG
+    p = _ptrs(6)
+    p[3] = None                                                       # k_dir
+    assert _mla(lib, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    p = _ptrs(6)
+    p[1] = ctypes.c_void_p(FAKE + (1 << 32) + 2)                       # misaligned q_dir
+    assert _mla(lib, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    p = _ptrs(6)
+    p[5] = ctypes.c_void_p(FAKE + 4 * (1 << 32) + 1024)                # o overlaps v
+    assert _mla(lib, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    assert _mla(lib, B=0) == kda.KDA_OK                                # nothing to do
+    assert _mla(lib, T=1 << 20, H=4096) == kda.KDA_ERR_UNSUPPORTED     # indices past 32 bits

@@ -1,0 +1,88 @@
+"""MLA attention core, HIP path vs the fp64 oracle (needs an MI355X).
+
+Gate: max relative error per (batch, head) over max |ref| <= 2e-2 (bf16 in and
+out, fp32 accumulation).  Small streams are compared in full; the full-size
+streams on sampled query rows of sampled heads (a query row depends on all keys
+of its head only, so the oracle computes those rows alone).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla as oracle_mla
+from linear_attention_sequence_modality_amd import kda
+from linear_attention_sequence_modality_amd.inputs import MLA_WORKLOAD, MlaConfig, make_mla_inputs
+
+from gpu_common import TOL, rel, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+KEYS = ("q_nope", "q_dir", "k_nope", "k_dir", "v")
+
+
+def _run(cfg, scale=None, rows=None, heads=None):
+    say("case %s B=%d T=%d H=%d rows=%s heads=%s scale=%s" % (cfg.name, cfg.B, cfg.T, cfg.H,
+                                                              None if rows is None else len(rows), heads, scale))
+    host = make_mla_inputs(cfg)
+    dev = {k: v.cuda() for k, v in host.items()}
+    o = kda.mla_attention_forward(*[dev[k] for k in KEYS], scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle_mla.mla_attention(*[host[k] for k in KEYS], scale=scale, rows=rows, heads=heads)
+    got = o.double().cpu().numpy()
+    if rows is not None:
+        got = got[:, rows]
+    if heads is not None:
+        got = got[:, :, list(heads)]
+    e = rel(got, ref)
+    say("  rel err o %.2e" % e)
+    assert e <= TOL["bf16"]
+    return o
+
+
+@pytest.mark.timeout(120)
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 127, 128, 129, 333, 700])
+def test_small_streams(T):
+    _run(MlaConfig("mla_T%d" % T, B=2, T=T, H=2, seed=30 + T))
+
+
+@pytest.mark.timeout(120)
+@pytest.mark.parametrize("scale", [0.02, 0.25, 1.0])
+def test_flat_and_peaked_softmax(scale):
+    """From nearly uniform weights to scores spread over tens of units (the online
+    maximum then moves often and far)."""
+    _run(MlaConfig("mla_scale", B=1, T=517, H=3, seed=41), scale=scale)
+
+
+@pytest.mark.timeout(120)
+def test_batches_do_not_mix():
+    """Each batch's queries see only that batch's keys: a batch changed alone
+    leaves the other batches' outputs bit for bit unchanged."""
+    cfg = MlaConfig("mla_mix", B=3, T=200, H=2, seed=43)
+    dev = {k: v.cuda() for k, v in make_mla_inputs(cfg).items()}
+    o1 = kda.mla_attention_forward(*[dev[k] for k in KEYS])
+    dev["k_dir"][1] += 1.0
+    dev["v"][1] *= 2.0
+    o2 = kda.mla_attention_forward(*[dev[k] for k in KEYS])
+    torch.cuda.synchronize()
+    assert torch.equal(o1[0], o2[0]) and torch.equal(o1[2], o2[2])
+    assert not torch.equal(o1[1], o2[1])
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,heads", [("mla_image_1024px", (0, 3)), ("mla_video_5s_480x832", (2, 13))])
+def test_full_size_sampled(name, heads):
+    cfg = MLA_WORKLOAD[name]
+    rng = np.random.default_rng(5)
+    rows = sorted(set([0, 1, 127, 128, cfg.T - 1] + [int(x) for x in rng.integers(0, cfg.T, 59)]))
+    _run(cfg, rows=rows, heads=heads)
+
+
+@pytest.mark.timeout(120)
+def test_deterministic():
+    cfg = MLA_WORKLOAD["mla_tiny"]
+    dev = {k: v.cuda() for k, v in make_mla_inputs(cfg).items()}
+    a = kda.mla_attention_forward(*[dev[k] for k in KEYS])
+    b = kda.mla_attention_forward(*[dev[k] for k in KEYS])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
