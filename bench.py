@@ -159,6 +159,81 @@ def cpu_baseline(cfg, frames: int) -> dict:
                                                       sample.n_text, *sample.grid, sample.H, sample.dk, dt)}
 
 
+def mla_flops(cfg) -> float:
+    """Matrix-core flops of one MLA attention launch: S = Q K^T over d_nope + d_dir and O = P V."""
+    return 2.0 * cfg.B * cfg.H * cfg.T * cfg.T * (cfg.d_nope + cfg.d_dir + cfg.dv)
+
+
+def mla_cpu_baseline(cfg, rows: int) -> dict:
+    """The fp64 MLA oracle, as it stands, on ``rows`` query rows of every head of the same stream."""
+    import numpy as np
+
+    from oracle import mla as oracle_mla
+    from linear_attention_sequence_modality_amd.inputs import make_mla_inputs
+
+    inp = make_mla_inputs(cfg)
+    sel = np.linspace(0, cfg.T - 1, rows).astype(int).tolist()
+    t0 = time.perf_counter()
+    oracle_mla.mla_attention(inp["q_nope"], inp["q_dir"], inp["k_nope"], inp["k_dir"], inp["v"], rows=sel)
+    dt = time.perf_counter() - t0
+    return {"value": cfg.B * rows / dt, "unit": "tokens/s", "cores": int(os.environ.get("OMP_NUM_THREADS", "0")) or
+            os.cpu_count(), "kind": "oracle",
+            "sample": "fp64 numpy oracle (scores, softmax, weighted values per head) on %d of the %d query "
+                      "rows of each of the %d heads, against all %d keys; %.1f s wall; cores = the BLAS "
+                      "threads numpy may use" % (rows, cfg.T, cfg.H, cfg.T, dt)}
+
+
+def mla_main(args, torch) -> int:
+    """One step = one mla_attention_forward launch over the whole stream."""
+    from linear_attention_sequence_modality_amd import kda
+    from linear_attention_sequence_modality_amd.inputs import MLA_WORKLOAD, make_mla_inputs
+
+    cfg = MLA_WORKLOAD[args.mla_workload]
+    torch.cuda.set_device(0)
+    dev = {k: v.cuda() for k, v in make_mla_inputs(cfg).items()}
+    x = [dev[k] for k in ("q_nope", "q_dir", "k_nope", "k_dir", "v")]
+    o = torch.empty_like(dev["v"])
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        kda.mla_attention_forward(*x, o=o, stream=stream)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in events:
+        e[0].record(stream)
+        kda.mla_attention_forward(*x, o=o, stream=stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    fl = mla_flops(cfg)
+    tfs = fl / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "MLA attention core forward tokens/s at 1 GPU; % of bf16-MFMA roofline",
+        "value": round(cfg.B * cfg.T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "H": cfg.H, "d_nope": cfg.d_nope,
+                   "d_dir": cfg.d_dir, "dv": cfg.dv, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "mla_attention", "achieved": round(tfs, 1),
+                     "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                     "traffic": None, "flop_per_launch": fl, "us": round(ms * 1e3, 1)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = mla_cpu_baseline(cfg, args.mla_cpu_rows)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +246,11 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (three times) and "
                          "exit: the reference kernel for scaling HBM byte counters")
+    ap.add_argument("--mla", action="store_true",
+                    help="measure the MLA attention core instead (one launch per step)")
+    ap.add_argument("--mla-workload", default="mla_video_5s_480x832")
+    ap.add_argument("--mla-cpu-rows", type=int, default=512,
+                    help="query rows per head in the MLA CPU-baseline sample")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -191,6 +271,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "copies": 3}), flush=True)
         return 0
+
+    if args.mla:
+        return mla_main(args, torch)
 
     from linear_attention_sequence_modality_amd import kda
     from linear_attention_sequence_modality_amd.inputs import WORKLOAD, make_inputs

@@ -34,7 +34,7 @@ constexpr int kQB = 4 * kQW;            // queries per workgroup
 constexpr int kKT = 64;                 // keys per tile
 constexpr int kDn = 128, kDr = 64, kDqk = kDn + kDr, kDv = 128;
 constexpr int kKs = kDqk + 8;           // key-tile row stride in LDS (elements): 400 B, conflict-free 16 B reads
-constexpr int kVs = kKT + 8;            // value-tile row stride in LDS (elements): 144 B
+constexpr int kVs = kKT + 4;            // value-tile row stride in LDS (elements): 136 B, fewer bank conflicts
 constexpr int kThreads = 256;
 constexpr int kKnPer = kKT * (kDn / 8) / kThreads;   // 16-byte k_nope pieces of a key tile per thread
 constexpr int kKdPer = kKT * (kDr / 8) / kThreads;   // 16-byte k_dir pieces
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     f32x4_t O[kDv / 16][2];   // O^T: value rows 16rt + 4g + i of query column ct
 #pragma unroll
     for (int rt = 0; rt < kDv / 16; ++rt) O[rt][0] = O[rt][1] = zero4();
-    float mrow[2] = {-INFINITY, -INFINITY};   // running maximum of the log2-scaled scores
+    float mrow[2] = {-INFINITY, -INFINITY};   // reference maximum of the raw scores
     float lsum[2] = {0.f, 0.f};               // this lane's part of the running sum
     const float c = a.scale * 1.4426950408889634f;   // scores in log2 units
 
@@ -178,39 +178,50 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         // live through the first product)
         if (j0 + kKT < T) stage(j0 + kKT, st);
         __builtin_amdgcn_sched_barrier(0);
-        const bool ragged = j0 + kKT > T;
+        if (j0 + kKT > T) {   // keys past the end of the stream weigh nothing
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (j0 + 16 * rt + 4 * g + i >= T) S[rt][0][i] = S[rt][1][i] = -INFINITY;
+        }
         BF pf[2][2];   // P^T fragments: query column ct, 32-key step ks
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-            float x[4][4];
+            // maximum over the tile's keys of this query (raw scores; scale > 0)
             float mx = -INFINITY;
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool dead = ragged && j0 + 16 * rt + 4 * g + i >= T;
-                    x[rt][i] = dead ? -INFINITY : S[rt][ct][i] * c;
-                    mx = fmaxf(mx, x[rt][i]);
-                }
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[rt][ct][i]);
             // the four lane groups hold the other keys of the same query
             mx = fmaxf(mx, xor_lanes(mx, 16));
             mx = fmaxf(mx, xor_lanes(mx, 32));
+            // The reference maximum moves only when some query's maximum grew
+            // by more than 8 (log2 units): until then the weights 2^(s c - m c)
+            // stay below 256 and the sums and O keep their common reference,
+            // so the result is the same and O is rescaled far less often.
             const float mnew = fmaxf(mrow[ct], mx);
-            const float resc = __builtin_amdgcn_exp2f(mrow[ct] - mnew);
-            mrow[ct] = mnew;
+            if (__any((mnew - mrow[ct]) * c > 8.f)) {
+                const float resc = __builtin_amdgcn_exp2f((mrow[ct] - mnew) * c);
+                mrow[ct] = mnew;
+                lsum[ct] *= resc;
+#pragma unroll
+                for (int rt = 0; rt < kDv / 16; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) O[rt][ct][i] *= resc;
+            }
+            const float mc = mrow[ct] * c;
+            float x[4][4];
             float ps = 0.f;
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    x[rt][i] = __builtin_amdgcn_exp2f(x[rt][i] - mnew);
+                    x[rt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rt][ct][i], c, -mc));
                     ps += x[rt][i];
                 }
-            lsum[ct] = lsum[ct] * resc + ps;
-#pragma unroll
-            for (int rt = 0; rt < kDv / 16; ++rt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) O[rt][ct][i] *= resc;
+            lsum[ct] += ps;
             // k-slot (g, e) of step ks is key 32ks + 4g + e (e < 4) or 32ks + 16 + 4g + e - 4
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
