@@ -36,17 +36,20 @@ KERNEL_SOURCES = {
     "conv": ("conv.hip", "common.h", "launch.h"),
     "chunks": ("kda.hip", "mfma.h", "common.h", "launch.h"),
     "scan": ("kda.hip", "mfma.h", "common.h", "launch.h"),
+    "mla": ("mla.hip", "mfma.h", "common.h", "launch.h"),
 }
 MEASURED_TRAFFIC = {
-    ("video_5s_480x832", "conv"): ("7e198e465c710873", 253085.4, 399264.0),
-    ("video_5s_480x832", "chunks"): ("9c7045035b68aa3e", 270461.1, 586560.1),
-    ("video_5s_480x832", "scan"): ("9c7045035b68aa3e", 293363.9, 133091.6),
+    ("video_5s_480x832", "conv"): ("d5769c400649ddb8", 253725.2, 399264.0),
+    ("video_5s_480x832", "chunks"): ("90a46e28be760882", 270456.2, 586560.1),
+    ("video_5s_480x832", "scan"): ("90a46e28be760882", 293367.0, 133101.2),
+    ("mla_video_5s_480x832", "mla"): ("85b06fa1fb511ad3", 1537846.8, 133088.0),
 }
 # Matrix-core operations per dispatch (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
 # SQ_INSTS_VALU_MFMA_MOPS_F32, each count is 512 flops), taken the same way.
 MEASURED_MFMA_MOPS = {
-    ("video_5s_480x832", "chunks"): ("9c7045035b68aa3e", 46858240.0, 2129920.0),
-    ("video_5s_480x832", "scan"): ("9c7045035b68aa3e", 115015680.0, 0.0),
+    ("video_5s_480x832", "chunks"): ("90a46e28be760882", 46858240.0, 2129920.0),
+    ("video_5s_480x832", "scan"): ("90a46e28be760882", 115015680.0, 0.0),
+    ("mla_video_5s_480x832", "mla"): ("85b06fa1fb511ad3", 22151168000.0, 0.0),
 }
 
 
@@ -226,7 +229,8 @@ def mla_main(args, torch) -> int:
                    "d_dir": cfg.d_dir, "dv": cfg.dv, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "mla_attention", "achieved": round(tfs, 1),
                      "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
-                     "traffic": None, "flop_per_launch": fl, "us": round(ms * 1e3, 1)},
+                     "traffic": measured_traffic(cfg.name, "mla"), "flop_per_launch": fl,
+                     "mfma_flop_counted": measured_mfma_flops(cfg.name, "mla"), "us": round(ms * 1e3, 1)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = mla_cpu_baseline(cfg, args.mla_cpu_rows)

@@ -30,6 +30,7 @@ namespace kdaconv {
 namespace {
 
 constexpr int kQW = 32;                 // queries per wave
+constexpr int kCT = kQW / 16;           // 16-query column tiles per wave
 constexpr int kQB = 4 * kQW;            // queries per workgroup
 constexpr int kKT = 64;                 // keys per tile
 constexpr int kDn = 128, kDr = 64, kDqk = kDn + kDr, kDv = 128;
@@ -79,9 +80,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // its dims 32s + 8g .. +7.  Queries past the end re-read the last one and
     // are never stored.
     const int q0 = qb * kQB + wave * kQW;
-    BF qf[2][kDqk / 32];
+    BF qf[kCT][kDqk / 32];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < kCT; ++ct) {
         const size_t q = tok0 + (size_t)min(q0 + 16 * ct + c16, T - 1);
         const bf16_t *pn = qn + (q * H + h) * kDn + 8 * g;
         const bf16_t *pd = qd + (q * H + h) * kDr + 8 * g;
@@ -142,11 +143,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
     };
 
-    f32x4_t O[kDv / 16][2];   // O^T: value rows 16rt + 4g + i of query column ct
+    f32x4_t O[kDv / 16][kCT];   // O^T: value rows 16rt + 4g + i of query column ct
 #pragma unroll
-    for (int rt = 0; rt < kDv / 16; ++rt) O[rt][0] = O[rt][1] = zero4();
-    float mrow[2] = {-INFINITY, -INFINITY};   // reference maximum of the raw scores
-    float lsum[2] = {0.f, 0.f};               // this lane's part of the running sum
+    for (int rt = 0; rt < kDv / 16; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < kCT; ++ct) O[rt][ct] = zero4();
+    float mrow[kCT], lsum[kCT];   // reference maximum of the raw scores; this lane's part of the sum
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct) {
+        mrow[ct] = -INFINITY;
+        lsum[ct] = 0.f;
+    }
     const float c = a.scale * 1.4426950408889634f;   // scores in log2 units
 
     Stage st;
@@ -158,16 +165,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         __syncthreads();   // this tile is in LDS
 
         // S^T = K Q^T: key row tile rt (keys 16rt + 4g + i in lane l), query column tile ct
-        f32x4_t S[4][2];
+        f32x4_t S[4][kCT];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) S[rt][0] = S[rt][1] = zero4();
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < kCT; ++ct) S[rt][ct] = zero4();
 #pragma unroll
         for (int s = 0; s < kDqk / 32; ++s) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const BF kf = BF::ld8(Ks + (16 * rt + c16) * kKs + 32 * s + 8 * g);
-                S[rt][0] = mma(kf, qf[0][s], S[rt][0]);
-                S[rt][1] = mma(kf, qf[1][s], S[rt][1]);
+#pragma unroll
+                for (int ct = 0; ct < kCT; ++ct) S[rt][ct] = mma(kf, qf[ct][s], S[rt][ct]);
             }
             // at most one k-step of key fragments in flight: hoisting them all
             // would cost 96 registers
@@ -183,11 +192,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (j0 + 16 * rt + 4 * g + i >= T) S[rt][0][i] = S[rt][1][i] = -INFINITY;
-        }
-        BF pf[2][2];   // P^T fragments: query column ct, 32-key step ks
+                    if (j0 + 16 * rt + 4 * g + i >= T)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+                        for (int ct = 0; ct < kCT; ++ct) S[rt][ct][i] = -INFINITY;
+        }
+        BF pf[kCT][2];   // P^T fragments: query column ct, 32-key step ks
+#pragma unroll
+        for (int ct = 0; ct < kCT; ++ct) {
             // maximum over the tile's keys of this query (raw scores; scale > 0)
             float mx = -INFINITY;
 #pragma unroll
@@ -238,8 +249,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             for (int rt = 0; rt < kDv / 16; ++rt) {
                 const bf16_t *row = Vt + (16 * rt + c16) * kVs + 32 * ks + 4 * g;
                 const BF vf = BF::ld4x2(row, row + 16);
-                O[rt][0] = mma(vf, pf[0][ks], O[rt][0]);
-                O[rt][1] = mma(vf, pf[1][ks], O[rt][1]);
+#pragma unroll
+                for (int ct = 0; ct < kCT; ++ct) O[rt][ct] = mma(vf, pf[ct][ks], O[rt][ct]);
             }
         }
     }
@@ -252,7 +263,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lo));
     const int co = lo & 15, go = lo >> 4;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < kCT; ++ct) {
         float z = lsum[ct];
         z += xor_lanes(z, 16);
         z += xor_lanes(z, 32);

@@ -308,6 +308,51 @@ def test_varlen_batch_of_the_most_streams():
         tok += c.T
 
 
+@pytest.mark.timeout(120)
+def test_graph_capture_replays_match_eager():
+    """The measured step (conv, chunk kernel, state pass) allocates, synchronises and
+    clears nothing inside the library, so it can be captured in a HIP graph: three
+    replays, with eager work and synchronisations between them, each equal the eager
+    result bit for bit."""
+    cfg = _small("graph", B=1, n_text=40, grid=(4, 9, 13))
+    say("case graph capture T=%d" % cfg.T)
+    dev = to_dev(make_inputs(cfg))
+    d = desc_of(cfg)
+    wt = (dev["w_text_q"], dev["w_text_k"], dev["w_text_v"])
+    wv = (dev["w_vis_q"], dev["w_vis_k"], dev["w_vis_v"])
+    qc, kc, vc = (torch.empty_like(dev[s]) for s in ("q", "k", "v"))
+    o = torch.empty_like(dev["v"])
+    sT = torch.empty(cfg.B, cfg.H, cfg.dk, cfg.dv, device="cuda")
+    ws = torch.empty(kda.kda_forward_workspace_size(d, cfg.B, cfg.H, cfg.dk, cfg.dv, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(stream=None):
+        kda.kda_conv_forward(d, dev["q"], dev["k"], dev["v"], wt, wv, qc, kc, vc, stream=stream)
+        kda.kda_forward(d, qc, kc, vc, dev["alpha"], dev["beta"], final_state=sT, o=o, workspace=ws,
+                        stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (qc, kc, vc, o, sT)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(side)            # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream())
+    for rep in range(3):
+        for x in (qc, kc, vc, o, sT):
+            x.fill_(float("nan"))        # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for x, r in zip((qc, kc, vc, o, sT), ref):
+            assert torch.equal(x, r), "replay %d differs from eager" % rep
+
+
 # ---- hygiene -----------------------------------------------------------------------
 
 @pytest.mark.timeout(120)
