@@ -426,8 +426,10 @@ int mla_attention_forward(int B, int T, int H, int d_nope, int d_dir, int dv, kd
     if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
     if (dtype != KDA_BF16 || d_nope != 128 || d_dir != 64 || dv != 128) return KDA_ERR_UNSUPPORTED;
     if (!(scale > 0.f) || !(scale < INFINITY)) return KDA_ERR_INVALID_ARG;
-    // token and block indices stay in 32 bits
-    if ((int64_t)B * T * H * 128 >= kMaxTokens * 2 || (int64_t)B * H * ((T + 127) / 128) >= kMaxTokens)
+    // token and block indices stay in 32 bits, and so do the byte offsets inside one
+    // batch's keys and values (the kernel reads them through 32-bit buffer ranges)
+    if ((int64_t)B * T * H * 128 >= kMaxTokens * 2 || (int64_t)B * H * ((T + 127) / 128) >= kMaxTokens ||
+        (int64_t)T * H * 128 * 2 >= kMaxTokens * 2)
         return KDA_ERR_UNSUPPORTED;
     const void *ins[5] = {q_nope, q_dir, k_nope, k_dir, v};
     const size_t es = 2, BT = (size_t)B * (size_t)T;

@@ -264,3 +264,4 @@ def test_mla_rejects_bad_arguments(lib):
     assert _mla(lib, ptrs=p) == kda.KDA_ERR_INVALID_ARG
     assert _mla(lib, B=0) == kda.KDA_OK                                # nothing to do
     assert _mla(lib, T=1 << 20, H=4096) == kda.KDA_ERR_UNSUPPORTED     # indices past 32 bits
+    assert _mla(lib, T=1 << 20, H=31) == kda.KDA_ERR_UNSUPPORTED       # one batch's keys past 4 GiB

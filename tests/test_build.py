@@ -26,9 +26,15 @@ def test_no_kernel_spills(resources):
     assert not spills, spills
 
 
-def test_conv_keeps_its_occupancy(resources):
-    # bf16: four 4-wave blocks per CU, so at most 128 VGPRs; fp32 two
+def test_kernels_keep_their_occupancy(resources):
+    # waves per SIMD each kernel is laid out for: the bf16 conv runs four 4-wave blocks per CU
+    # (at most 128 VGPRs), the others two waves per SIMD
     for name, r in resources.items():
-        if "conv_kernel" in name:
-            want = 4 if "DF16b" in name else 2
-            assert r["Occupancy"] >= want, (name, r)
+        want = 4 if ("conv_kernel" in name and "DF16b" in name) else 2
+        assert r["Occupancy"] >= want, (name, r)
+
+
+def test_every_kernel_family_is_built(resources):
+    names = " ".join(resources)
+    for part in ("conv_kernel", "kda_intra_kernel", "kda_state_kernel", "mla_attention_kernel"):
+        assert part in names, part
