@@ -86,3 +86,30 @@ def test_deterministic():
     b = kda.mla_attention_forward(*[dev[k] for k in KEYS])
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.timeout(120)
+def test_ragged_tail_reads_nothing_past_the_stream_and_writes_only_o():
+    """Inputs sit in buffers padded with NaN right after their last token: a key
+    tile that ran past the end and used what it read would turn o into NaN.  The
+    output's guard bands must keep their canary."""
+    cfg = MlaConfig("mla_guard", B=2, T=65, H=2, seed=47)
+    host = make_mla_inputs(cfg)
+    pad = 1 << 14
+
+    def guarded(t, fill):
+        buf = torch.full((t.numel() + 2 * pad,), fill, dtype=t.dtype, device="cuda")
+        view = buf[pad:pad + t.numel()].view(t.shape)
+        view.copy_(t.cuda())
+        return buf, view
+
+    ins = {k: guarded(host[k], float("nan")) for k in KEYS}
+    ob, o = guarded(torch.zeros_like(host["v"]), 3.0)
+    kda.mla_attention_forward(*[ins[k][1] for k in KEYS], o=o)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    assert torch.all(ob[:pad].float() == 3.0) and torch.all(ob[-pad:].float() == 3.0)
+    ref = oracle_mla.mla_attention(*[host[k] for k in KEYS])
+    e = rel(o.double().cpu().numpy(), ref)
+    say("  guard rel err o %.2e" % e)
+    assert e <= TOL["bf16"]
