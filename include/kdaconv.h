@@ -208,6 +208,38 @@ int kda_conv_forward_varlen(const kda_stream_desc *descs, int n_seq, int H, int 
                             void *q_out, void *k_out, void *v_out, void *hip_stream);
 
 /*
+ * Backward of the KDA scan, for training (the pages train the backbone end to
+ * end; they do not describe the mixer's backward, which is the exact gradient
+ * of the forward above).  Inputs: the forward's q, k, v (the conv outputs),
+ * alpha, beta and initial_state (NULL = 0); the gradient of o, d_o
+ * [B, T, H, dv] in the stream dtype; the gradient of the final state,
+ * d_final_state (fp32 [B, H, dk, dv], NULL = 0).  Outputs: d_q, d_k
+ * [B, T, H, dk], d_v [B, T, H, dv], d_alpha [B, T, H, dk], d_beta [B, T, H]
+ * in the stream dtype, and d_initial_state (fp32 [B, H, dk, dv], NULL to
+ * skip).  Computed chunk by chunk in fp32: a per-chunk transform, the state
+ * at every chunk start, a reverse pass for the state gradients and a
+ * per-chunk gradient kernel.  workspace (device, >= the size returned by
+ * kda_backward_workspace_size, fp32 records, states and per-workgroup
+ * scratch) is owned by the caller; its contents are undefined afterwards.
+ * Same shapes as kda_forward (dk, dv in {64, 128}, either dtype) plus the
+ * forward's preconditions; additionally the product of alpha over the 64
+ * tokens of a chunk stays above 2^-100 per key channel (the chunk's decays
+ * are applied as exp(G) and exp(-G)).
+ * Errors: KDA_ERR_INVALID_ARG for a NULL or misaligned required pointer or an
+ * output overlapping an input or another output; KDA_ERR_WORKSPACE for a
+ * missing or short workspace; otherwise as kda_forward.
+ */
+size_t kda_backward_workspace_size(const kda_stream_desc *desc, int B, int H, int dk, int dv,
+                                   kda_dtype dtype);
+
+int kda_backward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,
+                 const void *q, const void *k, const void *v, const void *alpha,
+                 const void *beta, const float *initial_state, const void *d_o,
+                 const float *d_final_state, void *d_q, void *d_k, void *d_v, void *d_alpha,
+                 void *d_beta, float *d_initial_state, void *workspace, size_t workspace_bytes,
+                 void *hip_stream);
+
+/*
  * Attention core of the MLA layers that fill one of every four token-mixer
  * layers (Chimera pages, paper.rainbus.top, prerequisites section, the
  * Multi-head Latent Attention paragraph): keys and values are decompressed

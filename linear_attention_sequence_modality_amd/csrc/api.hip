@@ -457,4 +457,111 @@ int mla_attention_forward(int B, int T, int H, int d_nope, int d_dir, int dv, kd
                                                                                                : KDA_ERR_HIP;
 }
 
+// ---- backward ----------------------------------------------------------------
+
+}  // extern "C"
+
+namespace {
+
+struct BwdLayout {
+    size_t rec, states, scratch_blocks, total_floats;
+    int n_chunks;
+};
+
+BwdLayout bwd_layout(int64_t T, int B, int H, int dk, int dv) {
+    BwdLayout L;
+    L.n_chunks = (int)chunks_of(T);
+    const size_t items = (size_t)B * H * L.n_chunks;
+    L.rec = items * kdaconv::kda_bwd_rec_floats(dk, dv);
+    L.states = items * (size_t)dk * dv;
+    const size_t par = items < (size_t)kdaconv::kBwdBlocks ? items : (size_t)kdaconv::kBwdBlocks;
+    const size_t ordered = (size_t)B * H * (dv / 64);
+    L.scratch_blocks = par > ordered ? par : ordered;
+    L.total_floats = L.rec + 2 * L.states + L.scratch_blocks * kdaconv::kda_bwd_scratch_floats(dk, dv);
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_backward_workspace_size(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype) {
+    Seqs sq;
+    if (uniform_seqs(desc, B, H, dk, dv, dtype, &sq) != KDA_OK) return 0;
+    return bwd_layout(sq.T, B, H, dk, dv).total_floats * sizeof(float);
+}
+
+int kda_backward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype, const void *q,
+                 const void *k, const void *v, const void *alpha, const void *beta, const float *initial_state,
+                 const void *d_o, const float *d_final_state, void *d_q, void *d_k, void *d_v, void *d_alpha,
+                 void *d_beta, float *d_initial_state, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    Seqs sq;
+    int rc = uniform_seqs(desc, B, H, dk, dv, dtype, &sq);
+    if (rc != KDA_OK) return rc;
+    const size_t es = elem_bytes(dtype), BT = (size_t)sq.tokens;
+    const size_t sbytes = (size_t)B * H * dk * dv * sizeof(float);
+    const void *ins[8] = {q, k, v, alpha, beta, d_o, initial_state, d_final_state};
+    const size_t inb[8] = {BT * H * dk * es, BT * H * dk * es, BT * H * dv * es, BT * H * dk * es, BT * H * es,
+                           BT * H * dv * es, sbytes, sbytes};
+    void *outs[6] = {d_q, d_k, d_v, d_alpha, d_beta, d_initial_state};
+    const size_t outb[6] = {BT * H * dk * es, BT * H * dk * es, BT * H * dv * es, BT * H * dk * es, BT * H * es,
+                            sbytes};
+    Range rin[8], rout[6];
+    for (int i = 0; i < 8; ++i) {
+        const bool optional = i >= 6;
+        if ((!ins[i] && !optional) || (ins[i] && !aligned16(ins[i]))) return KDA_ERR_INVALID_ARG;
+        rin[i] = ins[i] ? range_of(ins[i], inb[i]) : Range{0, 0};
+    }
+    for (int i = 0; i < 6; ++i) {
+        const bool optional = i == 5;
+        if ((!outs[i] && !optional) || (outs[i] && !aligned16(outs[i]))) return KDA_ERR_INVALID_ARG;
+        rout[i] = outs[i] ? range_of(outs[i], outb[i]) : Range{0, 0};
+        for (int j = 0; j < 8; ++j)
+            if (overlaps(rout[i], rin[j])) return KDA_ERR_INVALID_ARG;
+        for (int j = 0; j < i; ++j)
+            if (overlaps(rout[i], rout[j])) return KDA_ERR_INVALID_ARG;
+    }
+    if (B == 0) return KDA_OK;
+    const BwdLayout L = bwd_layout(sq.T, B, H, dk, dv);
+    const size_t need = L.total_floats * sizeof(float);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KDA_ERR_WORKSPACE;
+    const Range rw = range_of(workspace, need);
+    for (int i = 0; i < 8; ++i)
+        if (overlaps(rw, rin[i])) return KDA_ERR_INVALID_ARG;
+    for (int i = 0; i < 6; ++i)
+        if (overlaps(rw, rout[i])) return KDA_ERR_INVALID_ARG;
+    kdaconv::KdaBwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.dO = d_o;
+    a.s0 = initial_state;
+    a.dsT = d_final_state;
+    a.sT = nullptr;
+    a.dq = d_q;
+    a.dk_out = d_k;
+    a.dv_out = d_v;
+    a.dalpha = d_alpha;
+    a.dbeta = d_beta;
+    a.ds0 = d_initial_state;
+    float *w = static_cast<float *>(workspace);
+    a.rec = w;
+    a.states = w + L.rec;
+    a.dstates = a.states + L.states;
+    a.scratch = a.dstates + L.states;
+    a.rec_floats = kdaconv::kda_bwd_rec_floats(dk, dv);
+    a.scratch_floats = kdaconv::kda_bwd_scratch_floats(dk, dv);
+    a.B = B;
+    a.T = sq.T;
+    a.H = H;
+    a.dk = dk;
+    a.dv = dv;
+    a.n_chunks = L.n_chunks;
+    return kdaconv::launch_kda_backward(a, dtype == KDA_BF16, static_cast<hipStream_t>(hip_stream)) == hipSuccess
+               ? KDA_OK
+               : KDA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -67,6 +67,24 @@ hipError_t launch_kda_scan(const KdaArgs &a, bool bf16, hipStream_t stream);
 // Compute units of the current device.
 int num_cus();
 
+// ---- KDA backward ----------------------------------------------------------
+// Uniform batch [B, T, H, d] as in the forward.  All buffers are caller-owned;
+// rec, states, dstates and scratch are parts of one workspace.
+struct KdaBwdArgs {
+    const void *q, *k, *v, *alpha, *beta, *dO;   // forward inputs and the gradient of o
+    const float *s0, *dsT;                       // initial state, gradient of the final state (or null)
+    float *sT;                                   // unused by the backward (null)
+    void *dq, *dk_out, *dv_out, *dalpha, *dbeta; // gradients, stream dtype
+    float *ds0;                                  // gradient of the initial state (or null)
+    float *rec, *states, *dstates, *scratch;     // workspace parts (fp32)
+    size_t rec_floats, scratch_floats;
+    int B, T, H, dk, dv, n_chunks;
+};
+constexpr int kBwdBlocks = 256;   // workgroups of the two chunk-parallel backward kernels (at most)
+size_t kda_bwd_scratch_floats(int dk, int dv);
+size_t kda_bwd_rec_floats(int dk, int dv);
+hipError_t launch_kda_backward(KdaBwdArgs a, bool bf16, hipStream_t stream);
+
 // ---- MLA attention core ----------------------------------------------------
 // q_nope, k_nope [B, T, H, 128]; q_dir [B, T, H, 64]; k_dir [B, T, 64] (shared
 // by the heads); v, o [B, T, H, 128]; bf16.

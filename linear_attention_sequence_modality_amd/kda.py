@@ -29,7 +29,7 @@ KDA_MAX_SEQS = 64   # streams of one variable-length batch
 EXPORTED_SYMBOLS = ("kda_conv_forward", "kda_conv_forward_stream", "kda_forward_workspace_size", "kda_forward",
                     "kda_forward_chunks", "kda_forward_scan", "kda_forward_varlen_workspace_size",
                     "kda_forward_varlen", "kda_conv_forward_varlen", "mla_attention_forward",
-                    "kda_status_string")
+                    "kda_backward_workspace_size", "kda_backward", "kda_status_string")
 
 
 class KdaStreamDesc(ctypes.Structure):
@@ -85,6 +85,10 @@ def load_library():
     lib.kda_conv_forward_varlen.restype = i32
     lib.kda_conv_forward_varlen.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp,
                                             ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp]
+    lib.kda_backward_workspace_size.restype = ctypes.c_size_t
+    lib.kda_backward_workspace_size.argtypes = [desc_p, i32, i32, i32, i32, i32]
+    lib.kda_backward.restype = i32
+    lib.kda_backward.argtypes = [desc_p, i32, i32, i32, i32, i32] + [vp] * 15 + [ctypes.c_size_t, vp]
     lib.mla_attention_forward.restype = i32
     lib.mla_attention_forward.argtypes = [i32] * 7 + [vp] * 5 + [ctypes.c_float, vp, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -328,6 +332,44 @@ def kda_conv_forward_varlen(descs: Sequence[KdaStreamDesc], q: torch.Tensor, k: 
     if rc != KDA_OK:
         raise KdaError("kda_conv_forward_varlen", rc)
     return q_out, k_out, v_out
+
+
+def kda_backward_workspace_size(desc: KdaStreamDesc, B: int, H: int, dk: int, dv: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(load_library().kda_backward_workspace_size(ctypes.byref(desc), B, H, dk, dv, code))
+
+
+def kda_backward(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 alpha: torch.Tensor, beta: torch.Tensor, d_o: torch.Tensor,
+                 initial_state: Optional[torch.Tensor] = None, d_final_state: Optional[torch.Tensor] = None,
+                 want_d_initial_state: bool = True, workspace: Optional[torch.Tensor] = None,
+                 stream=None) -> dict:
+    """Gradients of the KDA scan: returns dict dq, dk, dv, dalpha, dbeta (stream dtype) and
+    d_initial_state (fp32, or None)."""
+    lib = load_library()
+    dt = q.dtype
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (alpha, "alpha"), (beta, "beta"), (d_o, "d_o")):
+        _check(t, nm, dt)
+    for t, nm in ((initial_state, "initial_state"), (d_final_state, "d_final_state")):
+        if t is not None:
+            _check(t, nm, torch.float32)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dalpha": torch.empty_like(alpha), "dbeta": torch.empty_like(beta),
+           "d_initial_state": (torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device)
+                               if want_d_initial_state else None)}
+    need = kda_backward_workspace_size(desc, B, H, dk, dv, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = lib.kda_backward(ctypes.byref(desc), B, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v),
+                          _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(d_o), _ptr(d_final_state),
+                          _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]),
+                          _ptr(out["dbeta"]), _ptr(out["d_initial_state"]), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_backward", rc)
+    return out
 
 
 def mla_attention_forward(q_nope: torch.Tensor, q_dir: torch.Tensor, k_nope: torch.Tensor,

@@ -265,3 +265,33 @@ def test_mla_rejects_bad_arguments(lib):
     assert _mla(lib, B=0) == kda.KDA_OK                                # nothing to do
     assert _mla(lib, T=1 << 20, H=4096) == kda.KDA_ERR_UNSUPPORTED     # indices past 32 bits
     assert _mla(lib, T=1 << 20, H=31) == kda.KDA_ERR_UNSUPPORTED       # one batch's keys past 4 GiB
+
+
+def _bwd(lib, desc, B=1, H=2, dk=64, dv=64, dtype=kda.KDA_BF16, ins=None, outs=None, ws=FAKE + 60 * (1 << 32),
+         ws_bytes=1 << 40):
+    i = ins if ins is not None else _ptrs(6)
+    o = outs if outs is not None else [ctypes.c_void_p(FAKE + (70 + n) * (1 << 32)) for n in range(6)]
+    return lib.kda_backward(ctypes.byref(desc), B, H, dk, dv, dtype, i[0], i[1], i[2], i[3], i[4], None, i[5],
+                            None, o[0], o[1], o[2], o[3], o[4], o[5], ctypes.c_void_p(ws) if ws else None,
+                            ws_bytes, None)
+
+
+def test_backward_rejects_bad_arguments(lib):
+    d = _desc()
+    assert kda.kda_backward_workspace_size(d, 1, 2, 64, 64, kda.KDA_BF16) > 0
+    assert kda.kda_backward_workspace_size(d, 1, 2, 96, 64, kda.KDA_BF16) == 0
+    assert _bwd(lib, d, dk=96) == kda.KDA_ERR_UNSUPPORTED
+    i = _ptrs(6)
+    i[5] = None                                                        # d_o
+    assert _bwd(lib, d, ins=i) == kda.KDA_ERR_INVALID_ARG
+    o = [ctypes.c_void_p(FAKE + (70 + n) * (1 << 32)) for n in range(6)]
+    o[2] = ctypes.c_void_p(FAKE + 64)                                   # d_v overlaps q
+    assert _bwd(lib, d, outs=o) == kda.KDA_ERR_INVALID_ARG
+    o = [ctypes.c_void_p(FAKE + (70 + n) * (1 << 32)) for n in range(6)]
+    o[4] = o[3]                                                         # d_beta aliases d_alpha
+    assert _bwd(lib, d, outs=o) == kda.KDA_ERR_INVALID_ARG
+    o = [ctypes.c_void_p(FAKE + (70 + n) * (1 << 32)) for n in range(5)] + [None]
+    assert _bwd(lib, d, outs=o, ws=0) == kda.KDA_ERR_WORKSPACE          # d_initial_state is optional
+    need = kda.kda_backward_workspace_size(d, 1, 2, 64, 64, kda.KDA_BF16)
+    assert _bwd(lib, d, ws_bytes=need - 1) == kda.KDA_ERR_WORKSPACE
+    assert _bwd(lib, d, B=0) == kda.KDA_OK
