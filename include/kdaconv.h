@@ -229,6 +229,22 @@ int kda_conv_forward_varlen(const kda_stream_desc *descs, int n_seq, int H, int 
  * output overlapping an input or another output; KDA_ERR_WORKSPACE for a
  * missing or short workspace; otherwise as kda_forward.
  */
+/*
+ * Backward of kda_conv_forward.  Given the conv inputs q, k, v, the taps and
+ * the gradients of the conv outputs (d_q_out, d_k_out, d_v_out, layouts of
+ * q_out, k_out, v_out), writes the gradients of the inputs (d_q, d_k, d_v,
+ * stream dtype) and of the taps (d_w_text[s] fp32 [H*d_s, 4], d_w_vis[s] fp32
+ * [H*d_s, 27], overwritten; summed over the batch).  Each input receives
+ * tap * gradient of every output it feeds; each tap the sum of input *
+ * output gradient.  Errors as kda_conv_forward, plus KDA_ERR_INVALID_ARG for
+ * a NULL, misaligned or overlapping gradient pointer.
+ */
+int kda_conv_backward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,
+                      const void *q, const void *k, const void *v, const void *const w_text[3],
+                      const void *const w_vis[3], const void *d_q_out, const void *d_k_out,
+                      const void *d_v_out, void *d_q, void *d_k, void *d_v,
+                      float *const d_w_text[3], float *const d_w_vis[3], void *hip_stream);
+
 size_t kda_backward_workspace_size(const kda_stream_desc *desc, int B, int H, int dk, int dv,
                                    kda_dtype dtype);
 

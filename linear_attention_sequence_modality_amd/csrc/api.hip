@@ -564,4 +564,62 @@ int kda_backward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_
                : KDA_ERR_HIP;
 }
 
+int kda_conv_backward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype, const void *q,
+                      const void *k, const void *v, const void *const w_text[3], const void *const w_vis[3],
+                      const void *d_q_out, const void *d_k_out, const void *d_v_out, void *d_q, void *d_k, void *d_v,
+                      float *const d_w_text[3], float *const d_w_vis[3], void *hip_stream) {
+    int64_t T = 0;
+    int rc = check_shape(desc, B, H, dk, dv, dtype, &T);
+    if (rc != KDA_OK) return rc;
+    if (!w_text || !w_vis || !d_w_text || !d_w_vis) return KDA_ERR_INVALID_ARG;
+    const size_t es = elem_bytes(dtype);
+    const int Cs[3] = {H * dk, H * dk, H * dv};
+    const void *x[3] = {q, k, v}, *dy[3] = {d_q_out, d_k_out, d_v_out};
+    void *dx[3] = {d_q, d_k, d_v};
+    Range rin[12], rout[9];
+    for (int s = 0; s < 3; ++s) {
+        const size_t nbytes = (size_t)B * (size_t)T * (size_t)Cs[s] * es;
+        const void *req[5] = {x[s], dy[s], w_text[s], w_vis[s], dx[s]};
+        for (int i = 0; i < 5; ++i)
+            if (!req[i] || !aligned16(req[i])) return KDA_ERR_INVALID_ARG;
+        if (!d_w_text[s] || !d_w_vis[s] || !aligned16(d_w_text[s]) || !aligned16(d_w_vis[s])) return KDA_ERR_INVALID_ARG;
+        rin[s] = range_of(x[s], nbytes);
+        rin[3 + s] = range_of(dy[s], nbytes);
+        rin[6 + s] = range_of(w_text[s], (size_t)Cs[s] * 4 * es);
+        rin[9 + s] = range_of(w_vis[s], (size_t)Cs[s] * 27 * es);
+        rout[s] = range_of(dx[s], nbytes);
+        rout[3 + s] = range_of(d_w_text[s], (size_t)Cs[s] * 4 * sizeof(float));
+        rout[6 + s] = range_of(d_w_vis[s], (size_t)Cs[s] * 27 * sizeof(float));
+    }
+    for (int i = 0; i < 9; ++i) {
+        for (int j = 0; j < 12; ++j)
+            if (overlaps(rout[i], rin[j])) return KDA_ERR_INVALID_ARG;
+        for (int j = 0; j < i; ++j)
+            if (overlaps(rout[i], rout[j])) return KDA_ERR_INVALID_ARG;
+    }
+    if (B == 0) return KDA_OK;
+    kdaconv::ConvBwdArgs a;
+    for (int s = 0; s < 3; ++s) {
+        a.x[s] = x[s];
+        a.dy[s] = dy[s];
+        a.dx[s] = dx[s];
+        a.wt[s] = w_text[s];
+        a.wv[s] = w_vis[s];
+        a.dwt[s] = d_w_text[s];
+        a.dwv[s] = d_w_vis[s];
+        a.C[s] = Cs[s];
+    }
+    a.B = B;
+    a.T = (int)T;
+    a.n_text = desc->n_text;
+    a.gt = desc->grid_t;
+    a.gh = desc->grid_h;
+    a.gw = desc->grid_w;
+    if ((int64_t)desc->grid_t * desc->grid_h * desc->grid_w == 0) a.gt = a.gh = a.gw = 0;
+    a.causal_t = desc->causal_t;
+    return kdaconv::launch_conv_backward(a, dtype == KDA_BF16, static_cast<hipStream_t>(hip_stream)) == hipSuccess
+               ? KDA_OK
+               : KDA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -1,0 +1,152 @@
+// Backward of the modality-aware depthwise short conv.
+//
+// The forward sums tap * input over a fixed neighbourhood, so each input
+// receives tap * dy of every output it feeds (the conv with mirrored
+// offsets), and each tap the sum of input * dy over the outputs:
+//   text  (y_i = sum_j w_j x_{i-3+j}):  dx_i = sum_j w_j dy_{i+3-j},   dw_j = sum_i dy_i x_{i-3+j}
+//   visual (y_p = sum_o W_o x_{p+o}):   dx_p = sum_o W_o dy_{p-o},     dW_o = sum_p dy_p x_{p+o}
+// with o = (a - P, b - 1, e - 1) over the 3x3x3 taps (P = 1 symmetric, 2 time-causal)
+// and every term outside the stream's modality region dropped.
+//   * conv_dx_kernel: one thread per (token, channel pair), 4 or 27 gathers of dy.
+//   * conv_dw_kernel: one thread per channel of a 64-channel block over a range
+//     of 256 tokens, 31 running sums in registers, then one fp32 atomic add per
+//     tap into the (zeroed) weight gradients.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace kdaconv {
+namespace {
+
+constexpr int kDxThreads = 256;
+constexpr int kDwThreads = 64;     // channels per block
+constexpr int kDwTokens = 256;     // tokens per block
+
+__device__ __forceinline__ float ldf(const float *p) { return *p; }
+__device__ __forceinline__ float ldf(const bf16_t *p) { return (float)*p; }
+__device__ __forceinline__ void stf(float *p, float x) { *p = x; }
+__device__ __forceinline__ void stf(bf16_t *p, float x) { *p = (bf16_t)x; }
+
+// Stream position of visual (t, h, w), or -1 outside the grid.
+__device__ __forceinline__ int vpos(const ConvBwdArgs &a, int t, int h, int w) {
+    if (t < 0 || t >= a.gt || h < 0 || h >= a.gh || w < 0 || w >= a.gw) return -1;
+    return a.n_text + (t * a.gh + h) * a.gw + w;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kDxThreads) void conv_dx_kernel(ConvBwdArgs a, int s) {
+    const int C = a.C[s], npair = C / 2;
+    const size_t total = (size_t)a.B * a.T * npair;
+    const T *dy = static_cast<const T *>(a.dy[s]);
+    const T *wt = static_cast<const T *>(a.wt[s]), *wv = static_cast<const T *>(a.wv[s]);
+    T *dx = static_cast<T *>(a.dx[s]);
+    const int P = a.causal_t ? 2 : 1;
+    for (size_t e = (size_t)blockIdx.x * kDxThreads + threadIdx.x; e < total; e += (size_t)gridDim.x * kDxThreads) {
+        const int c = 2 * (int)(e % npair);
+        const size_t bt = e / npair;
+        const int i = (int)(bt % a.T);
+        const size_t base = (bt - i) * C;   // this batch's first token
+        float g0 = 0.f, g1 = 0.f;
+        if (i < a.n_text) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int o = i + 3 - j;
+                if (o < a.n_text) {
+                    g0 += ldf(wt + (size_t)c * 4 + j) * ldf(dy + base + (size_t)o * C + c);
+                    g1 += ldf(wt + (size_t)(c + 1) * 4 + j) * ldf(dy + base + (size_t)o * C + c + 1);
+                }
+            }
+        } else {
+            const int p = i - a.n_text, t = p / (a.gh * a.gw), hw = p % (a.gh * a.gw), h = hw / a.gw, w = hw % a.gw;
+#pragma unroll
+            for (int ta = 0; ta < 3; ++ta)
+#pragma unroll
+                for (int tb = 0; tb < 3; ++tb)
+#pragma unroll
+                    for (int te = 0; te < 3; ++te) {
+                        const int o = vpos(a, t - (ta - P), h - (tb - 1), w - (te - 1));
+                        if (o >= 0) {
+                            const int tap = (ta * 3 + tb) * 3 + te;
+                            g0 += ldf(wv + (size_t)c * 27 + tap) * ldf(dy + base + (size_t)o * C + c);
+                            g1 += ldf(wv + (size_t)(c + 1) * 27 + tap) * ldf(dy + base + (size_t)o * C + c + 1);
+                        }
+                    }
+        }
+        stf(dx + base + (size_t)i * C + c, g0);
+        stf(dx + base + (size_t)i * C + c + 1, g1);
+    }
+}
+
+// blockIdx.x = (batch, token range, channel block), flattened.
+template <typename T>
+__global__ __launch_bounds__(kDwThreads) void conv_dw_kernel(ConvBwdArgs a, int s) {
+    const int C = a.C[s], ncb = (C + kDwThreads - 1) / kDwThreads, nrange = (a.T + kDwTokens - 1) / kDwTokens;
+    const int cb = blockIdx.x % ncb, rg = (blockIdx.x / ncb) % nrange, b = blockIdx.x / (ncb * nrange);
+    const int c = cb * kDwThreads + threadIdx.x;
+    if (c >= C) return;
+    const T *x = static_cast<const T *>(a.x[s]) + (size_t)b * a.T * C;
+    const T *dy = static_cast<const T *>(a.dy[s]) + (size_t)b * a.T * C;
+    const int P = a.causal_t ? 2 : 1;
+    float st4[4] = {0.f, 0.f, 0.f, 0.f}, sv[27];
+#pragma unroll
+    for (int k = 0; k < 27; ++k) sv[k] = 0.f;
+    const int i0 = rg * kDwTokens, i1 = min(a.T, i0 + kDwTokens);
+    for (int i = i0; i < i1; ++i) {
+        const float g = ldf(dy + (size_t)i * C + c);
+        if (i < a.n_text) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int src = i - 3 + j;
+                if (src >= 0) st4[j] += g * ldf(x + (size_t)src * C + c);
+            }
+        } else {
+            const int p = i - a.n_text, t = p / (a.gh * a.gw), hw = p % (a.gh * a.gw), h = hw / a.gw, w = hw % a.gw;
+#pragma unroll
+            for (int ta = 0; ta < 3; ++ta)
+#pragma unroll
+                for (int tb = 0; tb < 3; ++tb)
+#pragma unroll
+                    for (int te = 0; te < 3; ++te) {
+                        const int src = vpos(a, t + ta - P, h + tb - 1, w + te - 1);
+                        if (src >= 0) sv[(ta * 3 + tb) * 3 + te] += g * ldf(x + (size_t)src * C + c);
+                    }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (st4[j] != 0.f) atomicAdd(a.dwt[s] + (size_t)c * 4 + j, st4[j]);
+#pragma unroll
+    for (int k = 0; k < 27; ++k)
+        if (sv[k] != 0.f) atomicAdd(a.dwv[s] + (size_t)c * 27 + k, sv[k]);
+}
+
+__global__ void zero_kernel(float *p, size_t n) {
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
+        p[e] = 0.f;
+}
+
+template <typename T>
+hipError_t launch_typed(const ConvBwdArgs &a, hipStream_t stream) {
+    for (int s = 0; s < 3; ++s) {
+        const size_t nz_t = (size_t)a.C[s] * 4, nz_v = (size_t)a.C[s] * 27;
+        hipLaunchKernelGGL(zero_kernel, dim3(64), dim3(256), 0, stream, a.dwt[s], nz_t);
+        hipLaunchKernelGGL(zero_kernel, dim3(64), dim3(256), 0, stream, a.dwv[s], nz_v);
+        const size_t pairs = (size_t)a.B * a.T * (a.C[s] / 2);
+        const size_t want = (pairs + kDxThreads - 1) / kDxThreads;
+        const int gx = (int)(want < 65536 ? want : 65536);
+        hipLaunchKernelGGL((conv_dx_kernel<T>), dim3(gx), dim3(kDxThreads), 0, stream, a, s);
+        const int ncb = (a.C[s] + kDwThreads - 1) / kDwThreads, nrange = (a.T + kDwTokens - 1) / kDwTokens;
+        hipLaunchKernelGGL((conv_dw_kernel<T>), dim3(a.B * nrange * ncb), dim3(kDwThreads), 0, stream, a, s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv_backward(const ConvBwdArgs &a, bool bf16, hipStream_t stream) {
+    if (a.B == 0) return hipSuccess;
+    return bf16 ? launch_typed<bf16_t>(a, stream) : launch_typed<float>(a, stream);
+}
+
+}  // namespace kdaconv

@@ -22,6 +22,17 @@ struct ConvArgs {
 };
 hipError_t launch_conv(const ConvArgs &a, bool bf16, hipStream_t stream);
 
+// Backward of the conv: dx of the inputs (stream dtype) and fp32 tap gradients.
+struct ConvBwdArgs {
+    const void *x[3], *dy[3];   // conv inputs, gradients of the conv outputs [B, T, C[s]]
+    void *dx[3];                // gradients of the conv inputs
+    const void *wt[3], *wv[3];  // taps [C[s], 4] and [C[s], 27]
+    float *dwt[3], *dwv[3];     // their gradients, overwritten
+    int C[3];
+    int B, T, n_text, gt, gh, gw, causal_t;
+};
+hipError_t launch_conv_backward(const ConvBwdArgs &a, bool bf16, hipStream_t stream);
+
 // ---- chunked KDA -----------------------------------------------------------
 constexpr int kChunk = 64;  // tokens per chunk
 

@@ -29,7 +29,7 @@ KDA_MAX_SEQS = 64   # streams of one variable-length batch
 EXPORTED_SYMBOLS = ("kda_conv_forward", "kda_conv_forward_stream", "kda_forward_workspace_size", "kda_forward",
                     "kda_forward_chunks", "kda_forward_scan", "kda_forward_varlen_workspace_size",
                     "kda_forward_varlen", "kda_conv_forward_varlen", "mla_attention_forward",
-                    "kda_backward_workspace_size", "kda_backward", "kda_status_string")
+                    "kda_backward_workspace_size", "kda_backward", "kda_conv_backward", "kda_status_string")
 
 
 class KdaStreamDesc(ctypes.Structure):
@@ -89,6 +89,10 @@ def load_library():
     lib.kda_backward_workspace_size.argtypes = [desc_p, i32, i32, i32, i32, i32]
     lib.kda_backward.restype = i32
     lib.kda_backward.argtypes = [desc_p, i32, i32, i32, i32, i32] + [vp] * 15 + [ctypes.c_size_t, vp]
+    lib.kda_conv_backward.restype = i32
+    lib.kda_conv_backward.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp, ctypes.POINTER(vp),
+                                      ctypes.POINTER(vp), vp, vp, vp, vp, vp, vp, ctypes.POINTER(vp),
+                                      ctypes.POINTER(vp), vp]
     lib.mla_attention_forward.restype = i32
     lib.mla_attention_forward.argtypes = [i32] * 7 + [vp] * 5 + [ctypes.c_float, vp, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -369,6 +373,34 @@ def kda_backward(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: torch
                           workspace.numel() * workspace.element_size(), _stream(stream))
     if rc != KDA_OK:
         raise KdaError("kda_backward", rc)
+    return out
+
+
+def kda_conv_backward(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      w_text: Sequence[torch.Tensor], w_vis: Sequence[torch.Tensor],
+                      d_q_out: torch.Tensor, d_k_out: torch.Tensor, d_v_out: torch.Tensor,
+                      stream=None) -> dict:
+    """Backward of kda_conv_forward: returns dict dq, dk, dv (stream dtype) and
+    dw_text, dw_vis (tuples of fp32 [H*d, 4] / [H*d, 27] per q, k, v)."""
+    lib = load_library()
+    dt = q.dtype
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (d_q_out, "d_q_out"), (d_k_out, "d_k_out"), (d_v_out, "d_v_out")):
+        _check(t, nm, dt)
+    for i in range(3):
+        _check(w_text[i], "w_text[%d]" % i, dt)
+        _check(w_vis[i], "w_vis[%d]" % i, dt)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dw_text": tuple(torch.empty(w.shape, dtype=torch.float32, device=q.device) for w in w_text),
+           "dw_vis": tuple(torch.empty(w.shape, dtype=torch.float32, device=q.device) for w in w_vis)}
+    arr = lambda ts: (ctypes.c_void_p * 3)(*[t.data_ptr() for t in ts])
+    rc = lib.kda_conv_backward(ctypes.byref(desc), B, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v),
+                               arr(w_text), arr(w_vis), _ptr(d_q_out), _ptr(d_k_out), _ptr(d_v_out),
+                               _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), arr(out["dw_text"]),
+                               arr(out["dw_vis"]), _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_conv_backward", rc)
     return out
 
 

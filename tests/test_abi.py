@@ -295,3 +295,29 @@ def test_backward_rejects_bad_arguments(lib):
     need = kda.kda_backward_workspace_size(d, 1, 2, 64, 64, kda.KDA_BF16)
     assert _bwd(lib, d, ws_bytes=need - 1) == kda.KDA_ERR_WORKSPACE
     assert _bwd(lib, d, B=0) == kda.KDA_OK
+
+
+def test_conv_backward_rejects_bad_arguments(lib):
+    d = _desc()
+    p = _ptrs(9)
+    wt = (ctypes.c_void_p * 3)(*[FAKE + (20 + i) * (1 << 32) for i in range(3)])
+    wv = (ctypes.c_void_p * 3)(*[FAKE + (30 + i) * (1 << 32) for i in range(3)])
+    dwt = (ctypes.c_void_p * 3)(*[FAKE + (80 + i) * (1 << 32) for i in range(3)])
+    dwv = (ctypes.c_void_p * 3)(*[FAKE + (90 + i) * (1 << 32) for i in range(3)])
+
+    def call(ptrs=p, B=1, dwt_=dwt, dwv_=dwv, desc=d):
+        return lib.kda_conv_backward(ctypes.byref(desc), B, 2, 64, 64, kda.KDA_BF16, *ptrs[:3], wt, wv, *ptrs[3:6],
+                                     *ptrs[6:9], dwt_, dwv_, None)
+
+    assert call(B=0) == kda.KDA_OK
+    assert call(desc=_desc(k_vis=5)) == kda.KDA_ERR_UNSUPPORTED
+    bad = list(p)
+    bad[4] = None                                                      # d_k_out
+    assert call(ptrs=bad) == kda.KDA_ERR_INVALID_ARG
+    bad = list(p)
+    bad[6] = ctypes.c_void_p(FAKE + 3 * (1 << 32))                      # d_q aliases d_q_out
+    assert call(ptrs=bad) == kda.KDA_ERR_INVALID_ARG
+    assert call(dwt_=(ctypes.c_void_p * 3)(FAKE + 80 * (1 << 32), None, FAKE + 82 * (1 << 32))) == \
+        kda.KDA_ERR_INVALID_ARG
+    assert call(dwv_=(ctypes.c_void_p * 3)(FAKE + 20 * (1 << 32), FAKE + 91 * (1 << 32), FAKE + 92 * (1 << 32))) == \
+        kda.KDA_ERR_INVALID_ARG                                        # a tap gradient over the text taps

@@ -69,3 +69,71 @@ def test_backward_without_state_arguments_and_deterministic():
     e = rel(a["dk"].double().cpu().numpy(), ref["dk"])
     say("  no-state rel err dk %.2e" % e)
     assert e <= TOL[cfg.dtype]
+
+
+CONV_CASES = [
+    StreamConfig("cbwd_bf16", B=2, H=2, dk=128, dv=64, n_text=9, grid=(3, 5, 7), dtype="bf16", seed=91),
+    StreamConfig("cbwd_causal_f32", B=1, H=2, dk=64, dv=64, n_text=5, grid=(4, 3, 6), dtype="f32", causal_t=1, seed=92),
+    StreamConfig("cbwd_text", B=1, H=1, dk=64, dv=64, n_text=70, grid=(0, 0, 0), dtype="bf16", seed=93),
+]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("cfg", CONV_CASES, ids=[c.name for c in CONV_CASES])
+def test_conv_backward_matches_the_adjoint_oracle(cfg):
+    say("case %s B=%d T=%d %s causal_t=%d" % (cfg.name, cfg.B, cfg.T, cfg.dtype, cfg.causal_t))
+    host = make_inputs(cfg)
+    g = np.random.default_rng(cfg.seed)
+    dys = {s: torch.from_numpy(g.standard_normal(tuple(host[s].shape)).astype(np.float32)).to(cfg.torch_dtype)
+           for s in ("q", "k", "v")}
+    dev = {k: v.cuda() for k, v in host.items()}
+    out = kda.kda_conv_backward(desc_of(cfg), dev["q"], dev["k"], dev["v"],
+                                (dev["w_text_q"], dev["w_text_k"], dev["w_text_v"]),
+                                (dev["w_vis_q"], dev["w_vis_k"], dev["w_vis_v"]),
+                                dys["q"].cuda(), dys["k"].cuda(), dys["v"].cuda())
+    torch.cuda.synchronize()
+    for i, s in enumerate(("q", "k", "v")):
+        B, T, H, d = host[s].shape
+        dx, dwt, dwv = ob.short_conv_backward(host[s].reshape(B, T, H * d), host["w_text_" + s], host["w_vis_" + s],
+                                              dys[s].reshape(B, T, H * d), cfg.n_text, cfg.grid, cfg.causal_t)
+        e_x = rel(out["d" + s].double().cpu().numpy(), dx.reshape(B, T, H, d))
+        e_t = float(np.abs(out["dw_text"][i].double().cpu().numpy() - dwt).max() / max(np.abs(dwt).max(), 1e-30))
+        e_v = float(np.abs(out["dw_vis"][i].double().cpu().numpy() - dwv).max() / max(np.abs(dwv).max(), 1e-30))
+        say("  %s: rel err dx %.2e dw_text %.2e dw_vis %.2e" % (s, e_x, e_t, e_v))
+        tol = TOL[cfg.dtype]
+        assert e_x <= tol and e_t <= tol and (cfg.n_vis == 0 or e_v <= tol)
+
+
+@pytest.mark.timeout(300)
+def test_conv_and_kda_backward_chain_matches_the_oracle():
+    """kda_backward then kda_conv_backward: the gradients of the conv inputs, the taps,
+    alpha, beta and the initial state of the whole mixer."""
+    cfg = StreamConfig("chain", B=1, H=2, dk=64, dv=64, n_text=6, grid=(2, 4, 5), dtype="f32", seed=95)
+    say("case chain T=%d" % cfg.T)
+    host = make_inputs(cfg)
+    g = np.random.default_rng(5)
+    dO = torch.from_numpy(g.standard_normal((cfg.B, cfg.T, cfg.H, cfg.dv)).astype(np.float32))
+    S0 = torch.from_numpy((g.standard_normal((cfg.B, cfg.H, cfg.dk, cfg.dv)) * 0.3).astype(np.float32))
+    dev = {k: v.cuda() for k, v in host.items()}
+    d = desc_of(cfg)
+    wt = (dev["w_text_q"], dev["w_text_k"], dev["w_text_v"])
+    wv = (dev["w_vis_q"], dev["w_vis_k"], dev["w_vis_v"])
+    qc, kc, vc = kda.kda_conv_forward(d, dev["q"], dev["k"], dev["v"], wt, wv)
+    gk = kda.kda_backward(d, qc, kc, vc, dev["alpha"], dev["beta"], dO.cuda(), initial_state=S0.cuda())
+    gc = kda.kda_conv_backward(d, dev["q"], dev["k"], dev["v"], wt, wv, gk["dq"], gk["dk"], gk["dv"])
+    torch.cuda.synchronize()
+    ref = ob.conv_kda_backward(host, cfg.n_text, cfg.grid, dO, 0, S0)
+    errs = {"dq": rel(gc["dq"].double().cpu().numpy(), ref["dq"]),
+            "dk": rel(gc["dk"].double().cpu().numpy(), ref["dk"]),
+            "dv": rel(gc["dv"].double().cpu().numpy(), ref["dv"]),
+            "dalpha": rel(gk["dalpha"].double().cpu().numpy(), ref["dalpha"]),
+            "dbeta": rel(gk["dbeta"].double().cpu().numpy()[..., None], ref["dbeta"][..., None]),
+            "dS0": oracle.rel_err_state(gk["d_initial_state"].double().cpu().numpy(), ref["dS0"])}
+    for i, s in enumerate(("q", "k", "v")):
+        for kind, idx in (("dw_text_", 0), ("dw_vis_", 1)):
+            got = (gc["dw_text"] if idx == 0 else gc["dw_vis"])[i].double().cpu().numpy()
+            want = ref[kind + s]
+            errs[kind + s] = float(np.abs(got - want).max() / max(np.abs(want).max(), 1e-30))
+    say("  chain rel errors: " + ", ".join("%s %.1e" % kv for kv in errs.items()))
+    for name, e in errs.items():
+        assert e <= TOL["f32"], name
