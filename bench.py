@@ -238,6 +238,122 @@ def mla_main(args, torch) -> int:
     return 0
 
 
+VALU_FP32_PEAK_TFS = 157.3    # MI355X fp32 vector peak, TFLOP/s
+
+
+def backward_flops(cfg) -> float:
+    """fp32 multiply-add flops of one kda_backward launch sequence: the dense products per
+    (batch, head, chunk) of the per-chunk transform (twice: once for the records, once
+    inside the gradient kernel), the two ordered passes and the gradient kernel."""
+    C, dk, dv = 64, cfg.dk, cfg.dv
+    mm = lambda m, n, k: 2.0 * m * n * k
+    fwd = mm(C, C, dk) * 2 + mm(C, dk, C) + mm(C, dv, C)                 # A, Bq, W, Ut
+    states = mm(C, dv, dk) + mm(dk, dv, C)
+    reverse = mm(C, dv, C) + mm(C, dv, dk) + mm(dk, dv, C) * 2
+    grads = (mm(C, dv, dk) + mm(C, dv, C) + mm(C, dv, dk) + mm(C, C, dv) + mm(C, dk, dv) + mm(C, dk, C)
+             + mm(C, dk, dv) * 2 + mm(C, C, dv) + mm(C, C, dk) + mm(C, C, C) * 2 + mm(C, dv, C) + mm(C, dk, C)
+             + mm(C, dk, C) + mm(C, dk, C) * 2)
+    n_chunks = (cfg.T + C - 1) // C
+    return cfg.B * cfg.H * n_chunks * (2 * fwd + states + reverse + grads)
+
+
+def backward_main(args, torch) -> int:
+    """One step = kda_backward then kda_conv_backward over the whole stream."""
+    import numpy as np
+
+    from linear_attention_sequence_modality_amd import kda
+    from linear_attention_sequence_modality_amd.inputs import WORKLOAD, make_inputs
+
+    cfg = WORKLOAD[args.workload]
+    torch.cuda.set_device(0)
+    inp = {k: v.cuda() for k, v in make_inputs(cfg).items()}
+    desc = kda.make_desc(cfg.n_text, cfg.grid, causal_t=cfg.causal_t)
+    wt = (inp["w_text_q"], inp["w_text_k"], inp["w_text_v"])
+    wv = (inp["w_vis_q"], inp["w_vis_k"], inp["w_vis_v"])
+    qc, kc, vc = kda.kda_conv_forward(desc, inp["q"], inp["k"], inp["v"], wt, wv)
+    g = np.random.default_rng(0)
+    d_o = torch.from_numpy(g.standard_normal((cfg.B, cfg.T, cfg.H, cfg.dv)).astype(np.float32)).to(
+        cfg.torch_dtype).cuda()
+    ws = torch.empty(kda.kda_backward_workspace_size(desc, cfg.B, cfg.H, cfg.dk, cfg.dv, cfg.torch_dtype),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        gk = kda.kda_backward(desc, qc, kc, vc, inp["alpha"], inp["beta"], d_o, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        kda.kda_conv_backward(desc, inp["q"], inp["k"], inp["v"], wt, wv, gk["dq"], gk["dk"], gk["dv"],
+                              stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in events:
+        step(e)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kda_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    conv_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    fl = backward_flops(cfg)
+    tfs = fl / (kda_ms * 1e-3) / 1e12
+    es = 2 if cfg.dtype == "bf16" else 4
+    conv_bytes = 3 * cfg.B * cfg.T * cfg.H * (2 * cfg.dk + cfg.dv) * es   # dy read twice, x read, dx written
+    result = {
+        "metric": "conv+KDA backward tokens/s at 1 GPU; % of fp32 vector-ALU roofline",
+        "value": round(cfg.B * cfg.T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "H": cfg.H, "dk": cfg.dk, "dv": cfg.dv,
+                   "n_text": cfg.n_text, "grid": list(cfg.grid), "chunk": 64, "parallelism": "single GPU"},
+        "roofline": {"bound": "alu", "kernel": "kda_backward", "achieved": round(tfs, 2),
+                     "peak": VALU_FP32_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / VALU_FP32_PEAK_TFS, 4),
+                     "traffic": None, "flop_per_launch": fl},
+        "kernels": {"kda_backward": {"us": round(kda_ms * 1e3, 1), "TFLOP/s": round(tfs, 2)},
+                    "kda_conv_backward": {"us": round(conv_ms * 1e3, 1),
+                                          "GB/s": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1),
+                                          "frac_hbm": round(conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = backward_cpu_baseline(cfg, args.backward_cpu_tokens)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def backward_cpu_baseline(cfg, tokens: int) -> dict:
+    """The fp64 adjoint oracle, as it stands, on the first ``tokens`` text-free tokens of every head."""
+    import numpy as np
+
+    from oracle import backward as ob
+    from linear_attention_sequence_modality_amd.inputs import make_inputs
+
+    sample = cfg.with_(name=cfg.name + "_prefix", n_text=min(cfg.n_text, tokens), grid=(0, 0, 0))
+    inp = make_inputs(sample)
+    g = np.random.default_rng(0)
+    d_o = g.standard_normal((sample.B, sample.T, sample.H, sample.dv))
+    t0 = time.perf_counter()
+    ob.kda_recurrence_backward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], d_o)
+    dt = time.perf_counter() - t0
+    return {"value": sample.B * sample.T / dt, "unit": "tokens/s",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count(), "kind": "oracle",
+            "sample": "fp64 numpy token-level adjoint of the KDA recurrence (no conv) on %d tokens of each of "
+                      "the %d heads (dk=%d, dv=%d); %.1f s wall; cores = the BLAS threads numpy may use" % (
+                          sample.T, sample.H, sample.dk, sample.dv, dt)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +366,10 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (three times) and "
                          "exit: the reference kernel for scaling HBM byte counters")
+    ap.add_argument("--backward", action="store_true",
+                    help="measure the backward (kda_backward + kda_conv_backward) instead")
+    ap.add_argument("--backward-cpu-tokens", type=int, default=512,
+                    help="tokens per head in the backward CPU-baseline sample")
     ap.add_argument("--mla", action="store_true",
                     help="measure the MLA attention core instead (one launch per step)")
     ap.add_argument("--mla-workload", default="mla_video_5s_480x832")
@@ -278,6 +398,8 @@ def main() -> int:
 
     if args.mla:
         return mla_main(args, torch)
+    if args.backward:
+        return backward_main(args, torch)
 
     from linear_attention_sequence_modality_amd import kda
     from linear_attention_sequence_modality_amd.inputs import WORKLOAD, make_inputs

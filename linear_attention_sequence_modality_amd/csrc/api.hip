@@ -474,9 +474,8 @@ BwdLayout bwd_layout(int64_t T, int B, int H, int dk, int dv) {
     const size_t items = (size_t)B * H * L.n_chunks;
     L.rec = items * kdaconv::kda_bwd_rec_floats(dk, dv);
     L.states = items * (size_t)dk * dv;
-    const size_t par = items < (size_t)kdaconv::kBwdBlocks ? items : (size_t)kdaconv::kBwdBlocks;
-    const size_t ordered = (size_t)B * H * (dv / 64);
-    L.scratch_blocks = par > ordered ? par : ordered;
+    // per-workgroup scratch of the two chunk-parallel kernels (the ordered passes work in LDS)
+    L.scratch_blocks = items < (size_t)kdaconv::kBwdBlocks ? items : (size_t)kdaconv::kBwdBlocks;
     L.total_floats = L.rec + 2 * L.states + L.scratch_blocks * kdaconv::kda_bwd_scratch_floats(dk, dv);
     return L;
 }

@@ -19,9 +19,9 @@
 //
 // Four launches, all fp32 inside:
 //   1. bwd_prep:    per (batch, head, chunk), in parallel: Qt, Kh, W, Ut, Bq, exp(gC).
-//   2. bwd_states:  per (batch, head, 64 value columns), in chunk order: the state
+//   2. bwd_states:  per (batch, head, 16 value columns), in chunk order: the state
 //                   at the start of every chunk.
-//   3. bwd_reverse: per (batch, head, 64 value columns), in reverse chunk order:
+//   3. bwd_reverse: per (batch, head, 16 value columns), in reverse chunk order:
 //                   dS' of every chunk and the gradient of the initial state.
 //   4. bwd_intra:   per (batch, head, chunk), in parallel: the gradients of the
 //                   chunk's tokens.
@@ -38,7 +38,6 @@ namespace {
 
 constexpr int BC = kChunk;      // rows per chunk
 constexpr int BT = 256;         // threads per workgroup
-constexpr int VS = 64;          // value columns per workgroup of the two ordered passes
 
 // ---- small dense helpers (all threads of the workgroup take part) ------------
 
@@ -46,37 +45,69 @@ enum Mask { kNoMask = 0, kLower = 1, kStrictLower = 2 };
 
 // C[m][n] = scale * sum_k op(A)[m][k] op(B)[k][n]  (+ C when acc), for m < M, n < N;
 // op(A)[m][k] = TA ? A[k*lda + m] : A[m*lda + k]; op(B)[k][n] = TB ? B[n*ldb + k] : B[k*ldb + n].
-// M, N multiples of 64, K a multiple of 16.  The mask zeroes the result above
-// the diagonal (kLower) or on and above it (kStrictLower).  Ends with a barrier.
+// M, N multiples of 64, K a multiple of 4 and at most 128, leading dimensions multiples
+// of 4 and 16-byte aligned operands.  Per 64 x 64 output tile the whole K panels of both
+// operands are read at once (float4 loads, all in flight together) into LDS as
+// tA[k][m], tB[k][n]; each thread then forms 4 x 4 outputs.  The mask zeroes the
+// result above the diagonal (kLower) or on and above it (kStrictLower).  Ends with a barrier.
+constexpr int kPanel = 128;   // largest K
+constexpr int kPs = 68;       // panel row stride (64 + 4)
 template <bool TA, bool TB>
 __device__ void gemm(float *C, int ldc, const float *A, int lda, const float *B, int ldb, int M, int N, int K,
-                     float scale, bool acc, Mask mask, float (*tA)[65], float (*tB)[65]) {
+                     float scale, bool acc, Mask mask, float (*tA)[kPs], float (*tB)[kPs]) {
     const int tid = threadIdx.x, tr = tid / 16, tc = tid % 16;   // this thread: rows 4tr.., cols 4tc..
     for (int m0 = 0; m0 < M; m0 += 64)
         for (int n0 = 0; n0 < N; n0 += 64) {
-            float c[4][4] = {};
-            for (int k0 = 0; k0 < K; k0 += 16) {
-                // tA[k][m] and tB[k][n] for 16 k and 64 m / n
-                for (int e = tid; e < 16 * 64; e += BT) {
-                    const int kk = e / 64, mm = e % 64;
-                    tA[kk][mm] = TA ? A[(size_t)(k0 + kk) * lda + m0 + mm] : A[(size_t)(m0 + mm) * lda + k0 + kk];
-                    tB[kk][mm] = TB ? B[(size_t)(n0 + mm) * ldb + k0 + kk] : B[(size_t)(k0 + kk) * ldb + n0 + mm];
+            // panels: K x 64 floats each, as float4 pieces, in rounds of 4 pieces per
+            // thread and operand: a round's loads all go out (indices clamped, so no load
+            // sits under a branch) before any of its pieces is stored
+            const int np = K * 16, kq = K / 4;
+            for (int i0 = 0; i0 < np; i0 += 4 * BT) {
+                float4 va[4], vb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = min(i0 + tid + BT * i, np - 1);
+                    va[i] = TA ? *reinterpret_cast<const float4 *>(A + (size_t)(e / 16) * lda + m0 + 4 * (e % 16))
+                               : *reinterpret_cast<const float4 *>(A + (size_t)(m0 + e / kq) * lda + 4 * (e % kq));
+                    vb[i] = TB ? *reinterpret_cast<const float4 *>(B + (size_t)(n0 + e / kq) * ldb + 4 * (e % kq))
+                               : *reinterpret_cast<const float4 *>(B + (size_t)(e / 16) * ldb + n0 + 4 * (e % 16));
                 }
-                __syncthreads();
 #pragma unroll
-                for (int kk = 0; kk < 16; ++kk) {
-                    float a[4], b[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        a[i] = tA[kk][4 * tr + i];
-                        b[i] = tB[kk][4 * tc + i];
+                for (int i = 0; i < 4; ++i) {
+                    const int e = i0 + tid + BT * i;
+                    if (e < np) {
+                        if (TA) {
+                            *reinterpret_cast<float4 *>(&tA[e / 16][4 * (e % 16)]) = va[i];
+                        } else {
+                            const int mm = e / kq, q = e % kq;
+                            tA[4 * q][mm] = va[i].x;
+                            tA[4 * q + 1][mm] = va[i].y;
+                            tA[4 * q + 2][mm] = va[i].z;
+                            tA[4 * q + 3][mm] = va[i].w;
+                        }
+                        if (TB) {
+                            const int nn = e / kq, q = e % kq;
+                            tB[4 * q][nn] = vb[i].x;
+                            tB[4 * q + 1][nn] = vb[i].y;
+                            tB[4 * q + 2][nn] = vb[i].z;
+                            tB[4 * q + 3][nn] = vb[i].w;
+                        } else {
+                            *reinterpret_cast<float4 *>(&tB[e / 16][4 * (e % 16)]) = vb[i];
+                        }
                     }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) c[i][j] = fmaf(a[i], b[j], c[i][j]);
                 }
-                __syncthreads();
+            }
+            __syncthreads();
+            float c[4][4] = {};
+#pragma unroll 4
+            for (int kk = 0; kk < K; ++kk) {
+                const float4 a4 = *reinterpret_cast<const float4 *>(&tA[kk][4 * tr]);
+                const float4 b4 = *reinterpret_cast<const float4 *>(&tB[kk][4 * tc]);
+                const float a[4] = {a4.x, a4.y, a4.z, a4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) c[i][j] = fmaf(a[i], b[j], c[i][j]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -88,8 +119,8 @@ __device__ void gemm(float *C, int ldc, const float *A, int lda, const float *B,
                     float *p = C + (size_t)m * ldc + n;
                     *p = acc ? *p + x : x;
                 }
+            __syncthreads();
         }
-    __syncthreads();
 }
 
 __device__ __forceinline__ float ld(const float *p) { return *p; }
@@ -104,62 +135,141 @@ struct ChunkMats {
     float *beta, *eC;   // [BC], [DK]
 };
 
+// 8 consecutive elements as fp32.
+__device__ __forceinline__ void ld8(const float *p, float (&x)[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p), b = *reinterpret_cast<const float4 *>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void ld8(const bf16_t *p, float (&x)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_lo(w[i]);
+        x[2 * i + 1] = bf16_hi(w[i]);
+    }
+}
+
+// rows x cols (cols a multiple of 8) of token-major input src (row r at src + r * stride)
+// into dst (fp32, row-major, ld = cols); rows >= nr are zero.  Every thread issues the
+// loads of 4 pieces of 8 elements before storing any of them.
+template <typename T, typename D>
+__device__ void stage_rows(D *dst, const T *src, size_t stride, int rows, int cols, int nr) {
+    const int c8 = cols / 8, np = rows * c8;
+    for (int p0 = 0; p0 < np; p0 += 4 * BT) {
+        float x[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = min(p0 + (int)threadIdx.x + BT * i, np - 1), r = p / c8;
+            ld8(src + (size_t)min(r, nr - 1) * stride + 8 * (p % c8), x[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = p0 + threadIdx.x + BT * i;
+            if (p < np) {
+                const int r = p / c8;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dst[r * cols + 8 * (p % c8) + j] = r < nr ? x[i][j] : 0.f;
+            }
+        }
+    }
+}
+
 template <typename T>
-__device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, int n, float (*tA)[65],
-                              float (*tB)[65]) {
+__device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, int n, float (*tA)[kPs],
+                              float (*tB)[kPs]) {
     const int DK = a.dk, DV = a.dv, H = a.H, tid = threadIdx.x;
     const int b = bh / H, h = bh % H, t0 = n * BC, nr = min(BC, a.T - t0);
+    const size_t tok0 = ((size_t)b * a.T + t0) * H + h;   // token t0, head h
     const T *q = static_cast<const T *>(a.q), *k = static_cast<const T *>(a.k), *v = static_cast<const T *>(a.v);
     const T *al = static_cast<const T *>(a.alpha), *be = static_cast<const T *>(a.beta);
-    auto tok = [&](int r) { return ((size_t)b * a.T + t0 + r) * H + h; };
-    for (int e = tid; e < BC * DK; e += BT) {
-        const int r = e / DK, ch = e % DK;
-        const bool ok = r < nr;
-        c.Q[e] = ok ? ld(q + tok(r) * DK + ch) : 0.f;
-        c.K[e] = ok ? ld(k + tok(r) * DK + ch) : 0.f;
-    }
-    for (int e = tid; e < BC * DV; e += BT) {
-        const int r = e / DV, ch = e % DV;
-        c.V[e] = r < nr ? ld(v + tok(r) * DV + ch) : 0.f;
-    }
-    if (tid < BC) c.beta[tid] = tid < nr ? ld(be + tok(tid)) : 0.f;
-    // G: cumulative sum of log alpha down the rows (rows past the end add 0)
+    float *lw = &tA[0][0];   // the panel area as scratch: 2 * kPanel * kPs floats
+    stage_rows(c.Q, q + tok0 * DK, (size_t)H * DK, BC, DK, nr);
+    stage_rows(c.K, k + tok0 * DK, (size_t)H * DK, BC, DK, nr);
+    stage_rows(c.V, v + tok0 * DV, (size_t)H * DV, BC, DV, nr);
+    stage_rows(lw, al + tok0 * DK, (size_t)H * DK, BC, DK, nr);   // alpha (rows past the end: 0, unused)
+    if (tid < BC) c.beta[tid] = tid < nr ? ld(be + tok0 + (size_t)tid * H) : 0.f;
+    __syncthreads();
+    // G: cumulative sum of log alpha down the rows (rows past the end add 0), in LDS
     for (int ch = tid; ch < DK; ch += BT) {
         float g = 0.f;
         for (int r = 0; r < BC; ++r) {
-            if (r < nr) g += logf(ld(al + tok(r) * DK + ch));
-            c.G[r * DK + ch] = g;
+            if (r < nr) g += logf(lw[r * DK + ch]);
+            lw[r * DK + ch] = g;
         }
         c.eC[ch] = expf(g);
+        lw[BC * DK + ch] = g;   // gC
     }
     __syncthreads();
-    for (int e = tid; e < BC * DK; e += BT) {
-        const int ch = e % DK;
-        const float g = c.G[e], gc = logf(c.eC[ch]);
-        const float gm = expf(g), kk = c.K[e];
-        c.Kt[e] = gm * kk;
-        c.Kd[e] = kk / gm;
-        c.Qt[e] = gm * c.Q[e];
-        c.Kh[e] = expf(gc - g) * kk;
+    {
+        float *__restrict__ Gg = c.G;
+        float *__restrict__ Kt = c.Kt;
+        float *__restrict__ Kd = c.Kd;
+        float *__restrict__ Qt = c.Qt;
+        float *__restrict__ Kh = c.Kh;
+        const float *__restrict__ Kk = c.K;
+        const float *__restrict__ Qq = c.Q;
+        for (int e4 = tid; e4 < BC * DK / 4; e4 += BT) {
+            const int e = 4 * e4, ch = e % DK;
+            const float4 kk = *reinterpret_cast<const float4 *>(Kk + e), qq = *reinterpret_cast<const float4 *>(Qq + e);
+            const float kv[4] = {kk.x, kk.y, kk.z, kk.w}, qv[4] = {qq.x, qq.y, qq.z, qq.w};
+            float g4[4], kt[4], kd[4], qt[4], kh[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float g = lw[e + i], gm = expf(g);
+                g4[i] = g;
+                kt[i] = gm * kv[i];
+                kd[i] = kv[i] / gm;
+                qt[i] = gm * qv[i];
+                kh[i] = expf(lw[BC * DK + ch + i] - g) * kv[i];
+            }
+            *reinterpret_cast<float4 *>(Gg + e) = make_float4(g4[0], g4[1], g4[2], g4[3]);
+            *reinterpret_cast<float4 *>(Kt + e) = make_float4(kt[0], kt[1], kt[2], kt[3]);
+            *reinterpret_cast<float4 *>(Kd + e) = make_float4(kd[0], kd[1], kd[2], kd[3]);
+            *reinterpret_cast<float4 *>(Qt + e) = make_float4(qt[0], qt[1], qt[2], qt[3]);
+            *reinterpret_cast<float4 *>(Kh + e) = make_float4(kh[0], kh[1], kh[2], kh[3]);
+        }
     }
     __syncthreads();
     gemm<false, true>(c.A, BC, c.Kt, DK, c.Kd, DK, BC, BC, DK, 1.f, false, kStrictLower, tA, tB);
     gemm<false, true>(c.Bq, BC, c.Qt, DK, c.Kd, DK, BC, BC, DK, 1.f, false, kLower, tA, tB);
-    // Tm = (I + Diag(beta) A)^-1 (unit lower triangular): column j by forward substitution
-    if (tid < BC) {
-        const int j = tid;
-        for (int i = 0; i < BC; ++i) {
-            float x = i == j ? 1.f : 0.f;
-            if (i > j) {
-                float s = 0.f;
-                for (int u = j; u < i; ++u) s += c.A[i * BC + u] * c.Tm[u * BC + j];
-                x = -c.beta[i] * s;
+    // Tm = (I + Diag(beta) A)^-1 (unit lower triangular): column j by forward substitution, in LDS
+    {
+        float *Al = lw, *Tl = lw + BC * BC;
+        stage_rows(Al, c.A, BC, BC, BC, BC);
+        __syncthreads();
+        if (tid < BC) {
+            const int j = tid;
+            for (int i = 0; i < BC; ++i) {
+                float x = i == j ? 1.f : 0.f;
+                if (i > j) {
+                    float sum = 0.f;
+                    for (int u = j; u < i; ++u) sum += Al[i * BC + u] * Tl[u * BC + j];
+                    x = -c.beta[i] * sum;
+                }
+                Tl[i * BC + j] = x;
             }
-            c.Tm[i * BC + j] = x;
+        }
+        __syncthreads();
+        for (int e4 = tid; e4 < BC * BC / 4; e4 += BT)
+            *reinterpret_cast<float4 *>(c.Tm + 4 * e4) = *reinterpret_cast<const float4 *>(Tl + 4 * e4);
+    }
+    {
+        float *__restrict__ X = c.X;
+        float *__restrict__ Y = c.Y;
+        const float *__restrict__ V = c.V;
+        const float *__restrict__ Kt = c.Kt;
+        for (int e4 = tid; e4 < BC * DV / 4; e4 += BT) {
+            const float bb = c.beta[4 * e4 / DV];
+            const float4 x = *reinterpret_cast<const float4 *>(V + 4 * e4);
+            *reinterpret_cast<float4 *>(X + 4 * e4) = make_float4(bb * x.x, bb * x.y, bb * x.z, bb * x.w);
+        }
+        for (int e4 = tid; e4 < BC * DK / 4; e4 += BT) {
+            const float bb = c.beta[4 * e4 / DK];
+            const float4 y = *reinterpret_cast<const float4 *>(Kt + 4 * e4);
+            *reinterpret_cast<float4 *>(Y + 4 * e4) = make_float4(bb * y.x, bb * y.y, bb * y.z, bb * y.w);
         }
     }
-    for (int e = tid; e < BC * DV; e += BT) c.X[e] = c.beta[e / DV] * c.V[e];
-    for (int e = tid; e < BC * DK; e += BT) c.Y[e] = c.beta[e / DK] * c.Kt[e];
     __syncthreads();
     gemm<false, false>(c.W, DK, c.Tm, BC, c.Y, DK, BC, DK, BC, 1.f, false, kNoMask, tA, tB);
     gemm<false, false>(c.Ut, DV, c.Tm, BC, c.X, DV, BC, DV, BC, 1.f, false, kNoMask, tA, tB);
@@ -209,7 +319,7 @@ __device__ Rec rec_at(const KdaBwdArgs &a, int bh, int n) {
 
 template <typename T>
 __global__ __launch_bounds__(BT) void bwd_prep_kernel(KdaBwdArgs a) {
-    __shared__ float tA[16][65], tB[16][65];
+    __shared__ __attribute__((aligned(16))) float tA[kPanel][kPs], tB[kPanel][kPs];
     float *rest;
     const ChunkMats c = carve(a.scratch + (size_t)blockIdx.x * a.scratch_floats, a.dk, a.dv, &rest);
     const int items = a.B * a.H * a.n_chunks;
@@ -230,77 +340,190 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(KdaBwdArgs a) {
     }
 }
 
-// State at the start of every chunk: S_{n+1} = Diag(eC) S_n + Kh^T (Ut - W S_n), per 64 value columns.
-__global__ __launch_bounds__(BT) void bwd_states_kernel(KdaBwdArgs a) {
-    __shared__ float tA[16][65], tB[16][65];
-    const int DK = a.dk, DV = a.dv, nvs = DV / VS;
-    const int bh = blockIdx.x / nvs, j0 = (blockIdx.x % nvs) * VS;
-    float *S = a.scratch + (size_t)blockIdx.x * a.scratch_floats;   // [DK][VS]
-    float *U = S + (size_t)DK * VS;                                  // [BC][VS]
-    for (int e = threadIdx.x; e < DK * VS; e += BT) {
-        const int i = e / VS, j = e % VS;
-        S[e] = a.s0 ? a.s0[((size_t)bh * DK + i) * DV + j0 + j] : 0.f;
+// C[m][n] += scale * sum_k At[k*lda + m] B[k*ldb + n] (C = that sum when !acc), all in
+// LDS, N a multiple of 4.  A thread owns 4 consecutive n of one m: per k it reads one At
+// value (consecutive m across lanes) and one float4 of B (a broadcast among lanes of one
+// n-quad), and keeps 4 independent sums, unrolled over k so the reads run ahead.
+__device__ __forceinline__ void lds_mm(float *C, int ldc, const float *At, int lda, const float *B, int ldb, int M,
+                                       int N, int K, float scale, bool acc) {
+    const int nq = N / 4;
+    for (int e = threadIdx.x; e < M * nq; e += BT) {
+        const int m = e % M, n = 4 * (e / M);
+        float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+#pragma unroll 8
+        for (int k = 0; k < K; ++k) {
+            const float av = At[k * lda + m];
+            const float4 bv = *reinterpret_cast<const float4 *>(B + k * ldb + n);
+            x0 = fmaf(av, bv.x, x0);
+            x1 = fmaf(av, bv.y, x1);
+            x2 = fmaf(av, bv.z, x2);
+            x3 = fmaf(av, bv.w, x3);
+        }
+        float *c = C + m * ldc + n;
+        if (acc) {
+            c[0] += scale * x0;
+            c[1] += scale * x1;
+            c[2] += scale * x2;
+            c[3] += scale * x3;
+        } else {
+            c[0] = scale * x0;
+            c[1] = scale * x1;
+            c[2] = scale * x2;
+            c[3] = scale * x3;
+        }
     }
-    __syncthreads();
-    for (int n = 0; n < a.n_chunks; ++n) {
-        float *Sn = a.states + ((size_t)bh * a.n_chunks + n) * DK * DV;
-        for (int e = threadIdx.x; e < DK * VS; e += BT) Sn[(size_t)(e / VS) * DV + j0 + e % VS] = S[e];
-        const Rec r = rec_at(a, bh, n);
-        for (int e = threadIdx.x; e < BC * VS; e += BT) U[e] = r.Ut[(size_t)(e / VS) * DV + j0 + e % VS];
-        __syncthreads();
-        gemm<false, false>(U, VS, r.W, DK, S, VS, BC, VS, DK, -1.f, true, kNoMask, tA, tB);   // U = Ut - W S
-        for (int e = threadIdx.x; e < DK * VS; e += BT) S[e] *= r.eC[e / VS];
-        __syncthreads();
-        gemm<true, false>(S, VS, r.Kh, DK, U, VS, DK, VS, BC, 1.f, true, kNoMask, tA, tB);    // S += Kh^T U
-    }
-    if (a.sT)
-        for (int e = threadIdx.x; e < DK * VS; e += BT) a.sT[((size_t)bh * DK + e / VS) * DV + j0 + e % VS] = S[e];
 }
 
-// Reverse pass: dS' of every chunk (the gradient of the state after it) and dS0.
+// Copy n floats (a multiple of 4, 16-byte aligned) from global memory to registers, 4 per
+// thread per slot, through a buffer resource: one lane offset for every slot, the slot in
+// the scalar offset, and slots past n read zeros (range-checked), so no load sits under a
+// branch and all of them stay in flight until the values are stored.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+template <int SLOTS>
+struct Pre {
+    f32x4v r[SLOTS];
+    __device__ __forceinline__ void load(const float *src, int n) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src), 0, n * 4, kBufWord3);
+        const unsigned voff = 16u * threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i)
+            r[i] = __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 4096u * i, 0));
+    }
+    // element (r, c) of a row-major [n / cols][cols] matrix to dst[c * ldt + r]
+    __device__ __forceinline__ void store_t(float *dst, int n, int cols, int ldt) const {
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const int e = 4 * (threadIdx.x + BT * i);
+            if (e < n) {
+                const int row = e / cols, col = e % cols;
+                dst[(col + 0) * ldt + row] = r[i].x;
+                dst[(col + 1) * ldt + row] = r[i].y;
+                dst[(col + 2) * ldt + row] = r[i].z;
+                dst[(col + 3) * ldt + row] = r[i].w;
+            }
+        }
+    }
+    __device__ __forceinline__ void store(float *dst, int n) const {
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const int e = 4 * (threadIdx.x + BT * i);
+            if (e < n) *reinterpret_cast<f32x4v *>(dst + e) = r[i];
+        }
+    }
+};
+constexpr int SW = 16;                         // value columns per workgroup of the ordered passes
+constexpr int kMatSlots = BC * 128 / (4 * BT); // float4 slots per thread for a 64 x 128 matrix
+constexpr int kSqSlots = BC * BC / (4 * BT);   // for a 64 x 64 matrix
+
+// Columns j0 .. j0+SW-1 of rows 0..rows-1 of a row-major [rows][ld] matrix, into LDS [rows][SW].
+__device__ __forceinline__ void load_cols(float *dst, const float *src, int rows, int ld, int j0) {
+    for (int e = threadIdx.x; e < rows * SW; e += BT) dst[e] = src[(size_t)(e / SW) * ld + j0 + e % SW];
+}
+
+// State at the start of every chunk: S_{n+1} = Diag(eC) S_n + Kh^T (Ut - W S_n), per SW value
+// columns.  The state and the chunk's operands live in LDS; the next chunk's W and Kh are
+// loaded into registers while the current one is computed.
+__global__ __launch_bounds__(BT) void bwd_states_kernel(KdaBwdArgs a) {
+    __shared__ __attribute__((aligned(16))) float S[128 * SW], U[BC * SW], Wt[128 * (BC + 1)], Khl[BC * 128],
+        Utl[BC * SW], eCl[128];
+    const int DK = a.dk, DV = a.dv, nvs = DV / SW;
+    const int bh = blockIdx.x / nvs, j0 = (blockIdx.x % nvs) * SW;
+    for (int e = threadIdx.x; e < DK * SW; e += BT) S[e] = a.s0 ? a.s0[((size_t)bh * DK + e / SW) * DV + j0 + e % SW] : 0.f;
+    Pre<kMatSlots> pw, pk;
+    {
+        const Rec r = rec_at(a, bh, 0);
+        pw.load(r.W, BC * DK);
+        pk.load(r.Kh, BC * DK);
+    }
+    for (int n = 0; n < a.n_chunks; ++n) {
+        const Rec r = rec_at(a, bh, n);
+        __syncthreads();                       // the previous step is done with the LDS operands
+        pw.store_t(Wt, BC * DK, DK, BC + 1);   // W^T, [DK][BC + 1]
+        pk.store(Khl, BC * DK);
+        load_cols(Utl, r.Ut, BC, DV, j0);
+        for (int e = threadIdx.x; e < DK; e += BT) eCl[e] = r.eC[e];
+        float *Sn = a.states + ((size_t)bh * a.n_chunks + n) * DK * DV;
+        for (int e = threadIdx.x; e < DK * SW; e += BT) Sn[(size_t)(e / SW) * DV + j0 + e % SW] = S[e];
+        __syncthreads();
+        if (n + 1 < a.n_chunks) {
+            const Rec r1 = rec_at(a, bh, n + 1);
+            pw.load(r1.W, BC * DK);
+            pk.load(r1.Kh, BC * DK);
+        }
+        for (int e = threadIdx.x; e < BC * SW; e += BT) U[e] = Utl[e];
+        __syncthreads();
+        lds_mm(U, SW, Wt, BC + 1, S, SW, BC, SW, DK, -1.f, true);            // U = Ut - W S
+        __syncthreads();
+        for (int e = threadIdx.x; e < DK * SW; e += BT) S[e] *= eCl[e / SW];
+        __syncthreads();
+        lds_mm(S, SW, Khl, DK, U, SW, DK, SW, BC, 1.f, true);                // S += Kh^T U
+    }
+}
+
+// Reverse pass: dS' of every chunk (the gradient of the state after it) and dS0, per SW
+// value columns, with the same LDS layout and register prefetch.
 template <typename T>
 __global__ __launch_bounds__(BT) void bwd_reverse_kernel(KdaBwdArgs a) {
-    __shared__ float tA[16][65], tB[16][65];
-    const int DK = a.dk, DV = a.dv, H = a.H, nvs = DV / VS;
-    const int bh = blockIdx.x / nvs, j0 = (blockIdx.x % nvs) * VS, b = bh / H, h = bh % H;
-    float *dS = a.scratch + (size_t)blockIdx.x * a.scratch_floats;   // [DK][VS]
-    float *dSn = dS + (size_t)DK * VS;                               // [DK][VS]
-    float *dU = dSn + (size_t)DK * VS;                               // [BC][VS]
-    float *dO = dU + (size_t)BC * VS;                                // [BC][VS]
+    __shared__ __attribute__((aligned(16))) float dS[128 * SW], dSn[128 * SW], dU[BC * SW], dO[BC * SW],
+        Bql[BC * BC], Kht[128 * (BC + 1)], Qtl[BC * 128], Wl[BC * 128], eCl[128];
+    const int DK = a.dk, DV = a.dv, H = a.H, nvs = DV / SW;
+    const int bh = blockIdx.x / nvs, j0 = (blockIdx.x % nvs) * SW, b = bh / H, h = bh % H;
     const T *go = static_cast<const T *>(a.dO);
-    for (int e = threadIdx.x; e < DK * VS; e += BT) {
-        const int i = e / VS, j = e % VS;
-        dS[e] = a.dsT ? a.dsT[((size_t)bh * DK + i) * DV + j0 + j] : 0.f;
+    for (int e = threadIdx.x; e < DK * SW; e += BT)
+        dS[e] = a.dsT ? a.dsT[((size_t)bh * DK + e / SW) * DV + j0 + e % SW] : 0.f;
+    Pre<kSqSlots> pb;
+    Pre<kMatSlots> pk, pq, pw;
+    {
+        const Rec r = rec_at(a, bh, a.n_chunks - 1);
+        pb.load(r.Bq, BC * BC);
+        pk.load(r.Kh, BC * DK);
+        pq.load(r.Qt, BC * DK);
+        pw.load(r.W, BC * DK);
+    }
+    for (int n = a.n_chunks - 1; n >= 0; --n) {
+        const Rec r = rec_at(a, bh, n);
+        __syncthreads();
+        pb.store(Bql, BC * BC);
+        pk.store_t(Kht, BC * DK, DK, BC + 1);  // Kh^T, [DK][BC + 1]
+        pq.store(Qtl, BC * DK);
+        pw.store(Wl, BC * DK);
+        for (int e = threadIdx.x; e < DK; e += BT) eCl[e] = r.eC[e];
+        const int t0 = n * BC, nr = min(BC, a.T - t0);
+        for (int e = threadIdx.x; e < BC * SW; e += BT) {
+            const int rr = e / SW;
+            dO[e] = rr < nr ? ld(go + (((size_t)b * a.T + t0 + rr) * H + h) * DV + j0 + e % SW) : 0.f;
+        }
+        float *dSp = a.dstates + ((size_t)bh * a.n_chunks + n) * DK * DV;
+        for (int e = threadIdx.x; e < DK * SW; e += BT) dSp[(size_t)(e / SW) * DV + j0 + e % SW] = dS[e];
+        __syncthreads();
+        if (n > 0) {
+            const Rec r1 = rec_at(a, bh, n - 1);
+            pb.load(r1.Bq, BC * BC);
+            pk.load(r1.Kh, BC * DK);
+            pq.load(r1.Qt, BC * DK);
+            pw.load(r1.W, BC * DK);
+        }
+        lds_mm(dU, SW, Bql, BC, dO, SW, BC, SW, BC, 1.f, false);            // dU = Bq^T dO
+        __syncthreads();
+        lds_mm(dU, SW, Kht, BC + 1, dS, SW, BC, SW, DK, 1.f, true);         //    + Kh dS'
+        for (int e = threadIdx.x; e < DK * SW; e += BT) dSn[e] = eCl[e / SW] * dS[e];
+        __syncthreads();
+        lds_mm(dSn, SW, Qtl, DK, dO, SW, DK, SW, BC, 1.f, true);            // + Qt^T dO
+        __syncthreads();
+        lds_mm(dSn, SW, Wl, DK, dU, SW, DK, SW, BC, -1.f, true);            // - W^T dU
+        __syncthreads();
+        for (int e = threadIdx.x; e < DK * SW; e += BT) dS[e] = dSn[e];
     }
     __syncthreads();
-    for (int n = a.n_chunks - 1; n >= 0; --n) {
-        float *dSp = a.dstates + ((size_t)bh * a.n_chunks + n) * DK * DV;
-        for (int e = threadIdx.x; e < DK * VS; e += BT) dSp[(size_t)(e / VS) * DV + j0 + e % VS] = dS[e];
-        const int t0 = n * BC, nr = min(BC, a.T - t0);
-        for (int e = threadIdx.x; e < BC * VS; e += BT) {
-            const int r = e / VS, j = e % VS;
-            dO[e] = r < nr ? ld(go + (((size_t)b * a.T + t0 + r) * H + h) * DV + j0 + j) : 0.f;
-        }
-        __syncthreads();
-        const Rec r = rec_at(a, bh, n);
-        gemm<true, false>(dU, VS, r.Bq, BC, dO, VS, BC, VS, BC, 1.f, false, kNoMask, tA, tB);   // Bq^T dO
-        gemm<false, false>(dU, VS, r.Kh, DK, dS, VS, BC, VS, DK, 1.f, true, kNoMask, tA, tB);   // + Kh dS'
-        for (int e = threadIdx.x; e < DK * VS; e += BT) dSn[e] = r.eC[e / VS] * dS[e];
-        __syncthreads();
-        gemm<true, false>(dSn, VS, r.Qt, DK, dO, VS, DK, VS, BC, 1.f, true, kNoMask, tA, tB);   // + Qt^T dO
-        gemm<true, false>(dSn, VS, r.W, DK, dU, VS, DK, VS, BC, -1.f, true, kNoMask, tA, tB);   // - W^T dU
-        float *t = dS;
-        dS = dSn;
-        dSn = t;
-    }
     if (a.ds0)
-        for (int e = threadIdx.x; e < DK * VS; e += BT) a.ds0[((size_t)bh * DK + e / VS) * DV + j0 + e % VS] = dS[e];
+        for (int e = threadIdx.x; e < DK * SW; e += BT) a.ds0[((size_t)bh * DK + e / SW) * DV + j0 + e % SW] = dS[e];
 }
 
 // Gradients of one chunk's tokens.
 template <typename T>
 __global__ __launch_bounds__(BT) void bwd_intra_kernel(KdaBwdArgs a) {
-    __shared__ float tA[16][65], tB[16][65];
+    __shared__ __attribute__((aligned(16))) float tA[kPanel][kPs], tB[kPanel][kPs];
     const int DK = a.dk, DV = a.dv, H = a.H, tid = threadIdx.x;
     float *s;
     const ChunkMats c = carve(a.scratch + (size_t)blockIdx.x * a.scratch_floats, DK, DV, &s);
@@ -319,7 +542,6 @@ __global__ __launch_bounds__(BT) void bwd_intra_kernel(KdaBwdArgs a) {
     float *dY = s; s += mk;
     float *dKt = s; s += mk;
     float *dKd = s; s += mk;
-    float *dG = s; s += mk;
     T *gq = static_cast<T *>(a.dq), *gk = static_cast<T *>(a.dk_out), *gv = static_cast<T *>(a.dv_out);
     T *ga = static_cast<T *>(a.dalpha), *gb = static_cast<T *>(a.dbeta);
     const T *go = static_cast<const T *>(a.dO), *al = static_cast<const T *>(a.alpha);
@@ -331,11 +553,9 @@ __global__ __launch_bounds__(BT) void bwd_intra_kernel(KdaBwdArgs a) {
         chunk_forward<T>(a, c, bh, n, tA, tB);
         const float *Sn = a.states + ((size_t)bh * a.n_chunks + n) * DK * DV;
         const float *dSp = a.dstates + ((size_t)bh * a.n_chunks + n) * DK * DV;
-        for (int e = tid; e < BC * DV; e += BT) {
-            const int r = e / DV;
-            U[e] = c.Ut[e];
-            dO[e] = r < nr ? ld(go + tok(r) * DV + e % DV) : 0.f;
-        }
+        for (int e4 = tid; e4 < BC * DV / 4; e4 += BT)
+            *reinterpret_cast<float4 *>(U + 4 * e4) = *reinterpret_cast<const float4 *>(c.Ut + 4 * e4);
+        stage_rows(dO, go + tok(0) * DV, (size_t)H * DV, BC, DV, nr);
         __syncthreads();
         gemm<false, false>(U, DV, c.W, DK, Sn, DV, BC, DV, DK, -1.f, true, kNoMask, tA, tB);        // U = Ut - W S
         gemm<true, false>(dU, DV, c.Bq, BC, dO, DV, BC, DV, BC, 1.f, false, kNoMask, tA, tB);       // dU = Bq^T dO
@@ -351,51 +571,117 @@ __global__ __launch_bounds__(BT) void bwd_intra_kernel(KdaBwdArgs a) {
         gemm<false, true>(dM, BC, P, BC, c.Tm, BC, BC, BC, BC, -1.f, false, kNoMask, tA, tB);       // dM
         gemm<true, false>(dX, DV, c.Tm, BC, dU, DV, BC, DV, BC, 1.f, false, kNoMask, tA, tB);       // dX = Tm^T dU
         gemm<true, false>(dY, DK, c.Tm, BC, dW, DK, BC, DK, BC, 1.f, false, kNoMask, tA, tB);       // dY = Tm^T dW
-        // dA = strict_lower(Diag(beta) dM), kept in dM's strict lower part (P reused for it)
+        // dA = strict_lower(Diag(beta) dM), in P
         for (int e = tid; e < BC * BC; e += BT) {
             const int r = e / BC, s2 = e % BC;
             P[e] = s2 < r ? c.beta[r] * dM[e] : 0.f;
         }
-        for (int e = tid; e < BC * DK; e += BT) dKt[e] = c.beta[e / DK] * dY[e];
+        for (int e4 = tid; e4 < BC * DK / 4; e4 += BT) {
+            const float bb = c.beta[4 * e4 / DK];
+            const float4 y = *reinterpret_cast<const float4 *>(dY + 4 * e4);
+            *reinterpret_cast<float4 *>(dKt + 4 * e4) = make_float4(bb * y.x, bb * y.y, bb * y.z, bb * y.w);
+        }
         __syncthreads();
         gemm<false, false>(dKt, DK, P, BC, c.Kd, DK, BC, DK, BC, 1.f, true, kNoMask, tA, tB);       // + dA Kd
         gemm<true, false>(dKd, DK, P, BC, c.Kt, DK, BC, DK, BC, 1.f, false, kNoMask, tA, tB);       // dA^T Kt
         gemm<true, false>(dKd, DK, dBq, BC, c.Qt, DK, BC, DK, BC, 1.f, true, kNoMask, tA, tB);      // + dBq^T Qt
-        // per-token outputs
-        if (tid < BC && tid < nr) {
-            const int r = tid;
+        // the panel area as scratch from here on: dG [BC][DK], alpha [BC][DK], partial sums
+        float *lw = &tA[0][0];
+        float *dGl = lw, *alpha_l = lw + BC * DK, *part = lw + 2 * BC * DK;   // part: 4 BC + 4 DK + 2 DK floats
+        static_assert(2 * BC * 128 + 4 * BC + 6 * 128 <= 2 * kPanel * kPs, "the tail's LDS fits the panel area");
+        stage_rows(alpha_l, al + tok(0) * DK, (size_t)H * DK, BC, DK, nr);
+        // dbeta: four threads per row, each a quarter of the three row sums
+        {
+            const int r = tid / 4, q = tid % 4;
             float db = 0.f;
-            for (int s2 = 0; s2 < r; ++s2) db += dM[r * BC + s2] * c.A[r * BC + s2];
-            for (int j = 0; j < DV; ++j) db += dX[r * DV + j] * c.V[r * DV + j];
-            for (int ch = 0; ch < DK; ++ch) db += dY[r * DK + ch] * c.Kt[r * DK + ch];
-            st(gb + tok(r), db);
-        }
-        for (int e = tid; e < BC * DV; e += BT) {
-            const int r = e / DV;
-            if (r < nr) st(gv + tok(r) * DV + e % DV, c.beta[r] * dX[e]);
-        }
-        for (int e = tid; e < BC * DK; e += BT) {
-            const int r = e / DK, ch = e % DK;
-            const float g = c.G[e], gc = logf(c.eC[ch]), gm = expf(g);
-            if (r < nr) {
-                st(gq + tok(r) * DK + ch, gm * dQt[e]);
-                st(gk + tok(r) * DK + ch, gm * dKt[e] + dKd[e] / gm + expf(gc - g) * dKh[e]);
+            for (int s2 = 16 * q; s2 < min(16 * q + 16, r); ++s2) db += dM[r * BC + s2] * c.A[r * BC + s2];
+            for (int j4 = q * DV / 16; j4 < (q + 1) * DV / 16; ++j4) {
+                const float4 x = *reinterpret_cast<const float4 *>(dX + r * DV + 4 * j4);
+                const float4 w = *reinterpret_cast<const float4 *>(c.V + r * DV + 4 * j4);
+                db += x.x * w.x + x.y * w.y + x.z * w.z + x.w * w.w;
             }
-            dG[e] = dQt[e] * c.Qt[e] + dKt[e] * c.Kt[e] - dKd[e] * c.Kd[e] - dKh[e] * c.Kh[e];
+            for (int c4 = q * DK / 16; c4 < (q + 1) * DK / 16; ++c4) {
+                const float4 x = *reinterpret_cast<const float4 *>(dY + r * DK + 4 * c4);
+                const float4 w = *reinterpret_cast<const float4 *>(c.Kt + r * DK + 4 * c4);
+                db += x.x * w.x + x.y * w.y + x.z * w.z + x.w * w.w;
+            }
+            part[4 * r + q] = db;
+        }
+        // dv, dq, dk and dG (into LDS)
+        for (int e4 = tid; e4 < BC * DV / 4; e4 += BT) {
+            const int e = 4 * e4, r = e / DV;
+            if (r < nr) {
+                const float4 x = *reinterpret_cast<const float4 *>(dX + e);
+                const float bb = c.beta[r];
+                T *d = gv + tok(r) * DV + e % DV;
+                st(d, bb * x.x);
+                st(d + 1, bb * x.y);
+                st(d + 2, bb * x.z);
+                st(d + 3, bb * x.w);
+            }
+        }
+        for (int e4 = tid; e4 < BC * DK / 4; e4 += BT) {
+            const int e = 4 * e4, r = e / DK, ch = e % DK;
+            const float4 g = *reinterpret_cast<const float4 *>(c.G + e);
+            const float4 eC = *reinterpret_cast<const float4 *>(c.eC + ch);
+            const float4 q1 = *reinterpret_cast<const float4 *>(dQt + e), q2 = *reinterpret_cast<const float4 *>(c.Qt + e);
+            const float4 t1 = *reinterpret_cast<const float4 *>(dKt + e), t2 = *reinterpret_cast<const float4 *>(c.Kt + e);
+            const float4 d1 = *reinterpret_cast<const float4 *>(dKd + e), d2 = *reinterpret_cast<const float4 *>(c.Kd + e);
+            const float4 h1 = *reinterpret_cast<const float4 *>(dKh + e), h2 = *reinterpret_cast<const float4 *>(c.Kh + e);
+            const float gv4[4] = {g.x, g.y, g.z, g.w}, ec[4] = {eC.x, eC.y, eC.z, eC.w};
+            const float a1[4] = {q1.x, q1.y, q1.z, q1.w}, a2[4] = {q2.x, q2.y, q2.z, q2.w};
+            const float b1[4] = {t1.x, t1.y, t1.z, t1.w}, b2[4] = {t2.x, t2.y, t2.z, t2.w};
+            const float c1[4] = {d1.x, d1.y, d1.z, d1.w}, c2[4] = {d2.x, d2.y, d2.z, d2.w};
+            const float e1[4] = {h1.x, h1.y, h1.z, h1.w}, e2[4] = {h2.x, h2.y, h2.z, h2.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float gm = expf(gv4[i]);
+                if (r < nr) {
+                    st(gq + tok(r) * DK + ch + i, gm * a1[i]);
+                    st(gk + tok(r) * DK + ch + i, gm * b1[i] + c1[i] / gm + expf(logf(ec[i]) - gv4[i]) * e1[i]);
+                }
+                dGl[e + i] = a1[i] * a2[i] + b1[i] * b2[i] - c1[i] * c2[i] - e1[i] * e2[i];
+            }
+        }
+        // the last row's extra terms: colsum(dKh * Kh) over the rows (four row groups of
+        // sixteen, four channels per thread) and exp(gC) rowsum(dS' * S) over the value columns
+        float *colp = part + 4 * BC, *sdsp = part + 4 * BC + 4 * DK;
+        for (int w = tid; w < 4 * DK / 4; w += BT) {
+            const int c4 = w % (DK / 4), rg = w / (DK / 4);
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int r = 16 * rg; r < 16 * rg + 16; ++r) {
+                const float4 x = *reinterpret_cast<const float4 *>(dKh + r * DK + 4 * c4);
+                const float4 y = *reinterpret_cast<const float4 *>(c.Kh + r * DK + 4 * c4);
+                acc.x += x.x * y.x;
+                acc.y += x.y * y.y;
+                acc.z += x.z * y.z;
+                acc.w += x.w * y.w;
+            }
+            *reinterpret_cast<float4 *>(colp + rg * DK + 4 * c4) = acc;
+        }
+        for (int w = tid; w < 2 * DK; w += BT) {
+            const int ch = w / 2, half = w % 2;
+            float acc = 0.f;
+            for (int j4 = half * DV / 8; j4 < (half + 1) * DV / 8; ++j4) {
+                const float4 x = *reinterpret_cast<const float4 *>(dSp + (size_t)ch * DV + 4 * j4);
+                const float4 y = *reinterpret_cast<const float4 *>(Sn + (size_t)ch * DV + 4 * j4);
+                acc += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+            }
+            sdsp[w] = acc;
         }
         __syncthreads();
-        // the last row's extra terms, then the reverse cumulative sum down the rows
+        if (tid < nr) st(gb + tok(tid), part[4 * tid] + part[4 * tid + 1] + part[4 * tid + 2] + part[4 * tid + 3]);
+        // the chunk's last row is its last valid token: rows past the end contribute nothing;
+        // then the reverse cumulative sum down the rows gives dlog alpha
         for (int ch = tid; ch < DK; ch += BT) {
-            float extra = 0.f, sds = 0.f;
-            for (int r = 0; r < BC; ++r) extra += dKh[r * DK + ch] * c.Kh[r * DK + ch];
-            for (int j = 0; j < DV; ++j) sds += dSp[(size_t)ch * DV + j] * Sn[(size_t)ch * DV + j];
-            // the chunk's last row is its last valid token: rows past the end contribute nothing
+            float extra = 0.f;
+            for (int rg = 0; rg < 4; ++rg) extra += colp[rg * DK + ch];
             const int last = nr - 1;
-            dG[last * DK + ch] += extra + c.eC[ch] * sds;
+            dGl[last * DK + ch] += extra + c.eC[ch] * (sdsp[2 * ch] + sdsp[2 * ch + 1]);
             float run = 0.f;
             for (int r = last; r >= 0; --r) {
-                run += dG[r * DK + ch];
-                st(ga + tok(r) * DK + ch, run / ld(al + tok(r) * DK + ch));
+                run += dGl[r * DK + ch];
+                st(ga + tok(r) * DK + ch, run / alpha_l[r * DK + ch]);
             }
         }
         __syncthreads();
@@ -408,7 +694,7 @@ size_t kda_bwd_scratch_floats(int dk, int dv) {
     const size_t mk = (size_t)BC * dk, mv = (size_t)BC * dv, mc = (size_t)BC * BC;
     // ChunkMats + the intra kernel's temporaries (the largest user)
     const size_t chunk = 9 * mk + 4 * mv + 3 * mc + BC + dk;
-    const size_t intra = 3 * mv + 4 * mc + 6 * mk + mv + mk;
+    const size_t intra = 4 * mv + 4 * mc + 6 * mk;
     return chunk + intra + 64;
 }
 
@@ -418,7 +704,7 @@ hipError_t launch_kda_backward(KdaBwdArgs a, bool bf16, hipStream_t stream) {
     if (a.B * a.H == 0) return hipSuccess;
     const int items = a.B * a.H * a.n_chunks;
     const int g = items < kBwdBlocks ? items : kBwdBlocks;
-    const int ordered = a.B * a.H * (a.dv / VS);
+    const int ordered = a.B * a.H * (a.dv / SW);
     if (bf16) {
         hipLaunchKernelGGL(bwd_prep_kernel<bf16_t>, dim3(g), dim3(BT), 0, stream, a);
         hipLaunchKernelGGL(bwd_states_kernel, dim3(ordered), dim3(BT), 0, stream, a);
