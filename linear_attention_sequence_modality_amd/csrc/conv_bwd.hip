@@ -20,8 +20,8 @@ namespace kdaconv {
 namespace {
 
 constexpr int kDxThreads = 256;
-constexpr int kDwThreads = 64;     // channels per block
-constexpr int kDwTokens = 256;     // tokens per block
+constexpr int kDwThreads = 64;     // threads per block (4 channels each)
+constexpr int kDwTokens = 64;      // tokens per block
 
 __device__ __forceinline__ float ldf(const float *p) { return *p; }
 __device__ __forceinline__ float ldf(const bf16_t *p) { return (float)*p; }
@@ -34,10 +34,11 @@ __device__ __forceinline__ int vpos(const ConvBwdArgs &a, int t, int h, int w) {
     return a.n_text + (t * a.gh + h) * a.gw + w;
 }
 
+// Tokens [0, nt) of every batch (nt = T, or n_text when the visual part is done elsewhere).
 template <typename T>
-__global__ __launch_bounds__(kDxThreads) void conv_dx_kernel(ConvBwdArgs a, int s) {
+__global__ __launch_bounds__(kDxThreads) void conv_dx_kernel(ConvBwdArgs a, int s, int nt) {
     const int C = a.C[s], npair = C / 2;
-    const size_t total = (size_t)a.B * a.T * npair;
+    const size_t total = (size_t)a.B * nt * npair;
     const T *dy = static_cast<const T *>(a.dy[s]);
     const T *wt = static_cast<const T *>(a.wt[s]), *wv = static_cast<const T *>(a.wv[s]);
     T *dx = static_cast<T *>(a.dx[s]);
@@ -45,8 +46,8 @@ __global__ __launch_bounds__(kDxThreads) void conv_dx_kernel(ConvBwdArgs a, int 
     for (size_t e = (size_t)blockIdx.x * kDxThreads + threadIdx.x; e < total; e += (size_t)gridDim.x * kDxThreads) {
         const int c = 2 * (int)(e % npair);
         const size_t bt = e / npair;
-        const int i = (int)(bt % a.T);
-        const size_t base = (bt - i) * C;   // this batch's first token
+        const int i = (int)(bt % nt);
+        const size_t base = (bt / nt) * a.T * C;   // this batch's first token
         float g0 = 0.f, g1 = 0.f;
         if (i < a.n_text) {
 #pragma unroll
@@ -78,27 +79,41 @@ __global__ __launch_bounds__(kDxThreads) void conv_dx_kernel(ConvBwdArgs a, int 
     }
 }
 
-// blockIdx.x = (batch, token range, channel block), flattened.
+// 4 consecutive channels as fp32.
+__device__ __forceinline__ void ld4c(const float *p, float (&x)[4]) {
+    const float4 v = *reinterpret_cast<const float4 *>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+__device__ __forceinline__ void ld4c(const bf16_t *p, float (&x)[4]) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+}
+
+// blockIdx.x = (batch, token range, channel block), flattened; a thread owns 4 channels.
 template <typename T>
 __global__ __launch_bounds__(kDwThreads) void conv_dw_kernel(ConvBwdArgs a, int s) {
-    const int C = a.C[s], ncb = (C + kDwThreads - 1) / kDwThreads, nrange = (a.T + kDwTokens - 1) / kDwTokens;
+    const int C = a.C[s], cpb = 4 * kDwThreads, ncb = (C + cpb - 1) / cpb, nrange = (a.T + kDwTokens - 1) / kDwTokens;
     const int cb = blockIdx.x % ncb, rg = (blockIdx.x / ncb) % nrange, b = blockIdx.x / (ncb * nrange);
-    const int c = cb * kDwThreads + threadIdx.x;
+    const int c = cb * cpb + 4 * threadIdx.x;
     if (c >= C) return;
-    const T *x = static_cast<const T *>(a.x[s]) + (size_t)b * a.T * C;
-    const T *dy = static_cast<const T *>(a.dy[s]) + (size_t)b * a.T * C;
+    const T *x = static_cast<const T *>(a.x[s]) + (size_t)b * a.T * C + c;
+    const T *dy = static_cast<const T *>(a.dy[s]) + (size_t)b * a.T * C + c;
     const int P = a.causal_t ? 2 : 1;
-    float st4[4] = {0.f, 0.f, 0.f, 0.f}, sv[27];
-#pragma unroll
-    for (int k = 0; k < 27; ++k) sv[k] = 0.f;
+    float st4[4][4] = {}, sv[27][4] = {};
     const int i0 = rg * kDwTokens, i1 = min(a.T, i0 + kDwTokens);
     for (int i = i0; i < i1; ++i) {
-        const float g = ldf(dy + (size_t)i * C + c);
+        float g[4];
+        ld4c(dy + (size_t)i * C, g);
         if (i < a.n_text) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int src = i - 3 + j;
-                if (src >= 0) st4[j] += g * ldf(x + (size_t)src * C + c);
+                if (src >= 0) {
+                    float xv[4];
+                    ld4c(x + (size_t)src * C, xv);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) st4[j][u] += g[u] * xv[u];
+                }
             }
         } else {
             const int p = i - a.n_text, t = p / (a.gh * a.gw), hw = p % (a.gh * a.gw), h = hw / a.gw, w = hw % a.gw;
@@ -109,16 +124,30 @@ __global__ __launch_bounds__(kDwThreads) void conv_dw_kernel(ConvBwdArgs a, int 
 #pragma unroll
                     for (int te = 0; te < 3; ++te) {
                         const int src = vpos(a, t + ta - P, h + tb - 1, w + te - 1);
-                        if (src >= 0) sv[(ta * 3 + tb) * 3 + te] += g * ldf(x + (size_t)src * C + c);
+                        float xv[4] = {0.f, 0.f, 0.f, 0.f};
+                        if (src >= 0) ld4c(x + (size_t)src * C, xv);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) sv[(ta * 3 + tb) * 3 + te][u] += g[u] * xv[u];
                     }
         }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        if (st4[j] != 0.f) atomicAdd(a.dwt[s] + (size_t)c * 4 + j, st4[j]);
+    for (int u = 0; u < 4; ++u) {
 #pragma unroll
-    for (int k = 0; k < 27; ++k)
-        if (sv[k] != 0.f) atomicAdd(a.dwv[s] + (size_t)c * 27 + k, sv[k]);
+        for (int j = 0; j < 4; ++j)
+            if (st4[j][u] != 0.f) atomicAdd(a.dwt[s] + (size_t)(c + u) * 4 + j, st4[j][u]);
+#pragma unroll
+        for (int k = 0; k < 27; ++k)
+            if (sv[k][u] != 0.f) atomicAdd(a.dwv[s] + (size_t)(c + u) * 27 + k, sv[k][u]);
+    }
+}
+
+// The visual taps mirrored through the centre (tap 26 - k), in the stream dtype: the
+// symmetric conv's input gradient is the forward conv of dy with these taps.
+template <typename T>
+__global__ void flip_taps_kernel(const T *w, T *out, int C) {
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < C * 27; e += gridDim.x * blockDim.x)
+        out[e] = w[(e / 27) * 27 + 26 - e % 27];
 }
 
 __global__ void zero_kernel(float *p, size_t n) {
@@ -128,15 +157,47 @@ __global__ void zero_kernel(float *p, size_t n) {
 
 template <typename T>
 hipError_t launch_typed(const ConvBwdArgs &a, hipStream_t stream) {
+    const bool vis = a.gt * a.gh * a.gw > 0;
+    // Symmetric time padding: the visual input gradient is the forward conv of dy with
+    // mirrored taps (its text outputs are redone below).  The mirrored taps are parked in
+    // the visual tap-gradient buffers, which are zeroed only after that conv has read them.
+    const bool mirrored = vis && !a.causal_t;
+    if (mirrored) {
+        ConvArgs f;
+        for (int s = 0; s < 3; ++s) {
+            hipLaunchKernelGGL((flip_taps_kernel<T>), dim3(64), dim3(256), 0, stream, static_cast<const T *>(a.wv[s]),
+                               reinterpret_cast<T *>(a.dwv[s]), a.C[s]);
+            f.x[s] = a.dy[s];
+            f.y[s] = a.dx[s];
+            f.wt[s] = a.wt[s];
+            f.wv[s] = a.dwv[s];
+            f.C[s] = a.C[s];
+            f.hx[s] = nullptr;
+        }
+        f.B = a.B;
+        f.T = a.T;
+        f.n_text = a.n_text;
+        f.gt = a.gt;
+        f.gh = a.gh;
+        f.gw = a.gw;
+        f.causal_t = 0;
+        f.n_hist = 0;
+        hipError_t e = launch_conv(f, sizeof(T) == 2, stream);
+        if (e != hipSuccess) return e;
+    }
     for (int s = 0; s < 3; ++s) {
+        // input gradients of the tokens the mirrored conv did not cover (all of them otherwise)
+        const int nt = mirrored ? a.n_text : a.T;
+        const size_t pairs = (size_t)a.B * nt * (a.C[s] / 2);
+        if (pairs) {
+            const size_t want = (pairs + kDxThreads - 1) / kDxThreads;
+            const int gx = (int)(want < 65536 ? want : 65536);
+            hipLaunchKernelGGL((conv_dx_kernel<T>), dim3(gx), dim3(kDxThreads), 0, stream, a, s, nt);
+        }
         const size_t nz_t = (size_t)a.C[s] * 4, nz_v = (size_t)a.C[s] * 27;
         hipLaunchKernelGGL(zero_kernel, dim3(64), dim3(256), 0, stream, a.dwt[s], nz_t);
         hipLaunchKernelGGL(zero_kernel, dim3(64), dim3(256), 0, stream, a.dwv[s], nz_v);
-        const size_t pairs = (size_t)a.B * a.T * (a.C[s] / 2);
-        const size_t want = (pairs + kDxThreads - 1) / kDxThreads;
-        const int gx = (int)(want < 65536 ? want : 65536);
-        hipLaunchKernelGGL((conv_dx_kernel<T>), dim3(gx), dim3(kDxThreads), 0, stream, a, s);
-        const int ncb = (a.C[s] + kDwThreads - 1) / kDwThreads, nrange = (a.T + kDwTokens - 1) / kDwTokens;
+        const int ncb = (a.C[s] + 4 * kDwThreads - 1) / (4 * kDwThreads), nrange = (a.T + kDwTokens - 1) / kDwTokens;
         hipLaunchKernelGGL((conv_dw_kernel<T>), dim3(a.B * nrange * ncb), dim3(kDwThreads), 0, stream, a, s);
     }
     return hipGetLastError();

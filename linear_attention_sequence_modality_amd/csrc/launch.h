@@ -91,7 +91,7 @@ struct KdaBwdArgs {
     size_t rec_floats, scratch_floats;
     int B, T, H, dk, dv, n_chunks;
 };
-constexpr int kBwdBlocks = 256;   // workgroups of the two chunk-parallel backward kernels (at most)
+constexpr int kBwdBlocks = 512;   // workgroups of the two chunk-parallel backward kernels (at most)
 size_t kda_bwd_scratch_floats(int dk, int dv);
 size_t kda_bwd_rec_floats(int dk, int dv);
 hipError_t launch_kda_backward(KdaBwdArgs a, bool bf16, hipStream_t stream);

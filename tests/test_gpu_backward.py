@@ -75,6 +75,8 @@ CONV_CASES = [
     StreamConfig("cbwd_bf16", B=2, H=2, dk=128, dv=64, n_text=9, grid=(3, 5, 7), dtype="bf16", seed=91),
     StreamConfig("cbwd_causal_f32", B=1, H=2, dk=64, dv=64, n_text=5, grid=(4, 3, 6), dtype="f32", causal_t=1, seed=92),
     StreamConfig("cbwd_text", B=1, H=1, dk=64, dv=64, n_text=70, grid=(0, 0, 0), dtype="bf16", seed=93),
+    # visual only, symmetric padding: the input gradient comes from the mirrored-tap conv alone
+    StreamConfig("cbwd_vis_f32", B=2, H=1, dk=64, dv=128, n_text=0, grid=(5, 6, 9), dtype="f32", seed=94),
 ]
 
 
