@@ -8,10 +8,15 @@
 // with o = (a - P, b - 1, e - 1) over the 3x3x3 taps (P = 1 symmetric, 2 time-causal)
 // and every term outside the stream's modality region dropped.
 //   * conv_dx_kernel: one thread per (token, channel pair), 4 or 27 gathers of dy.
-//   * conv_dw_kernel: one thread per channel of a 64-channel block over a range
-//     of 256 tokens, 31 running sums in registers, then one fp32 atomic add per
-//     tap into the (zeroed) weight gradients.
+//   * conv_dw_kernel: about one block per compute unit, each over 256 channels (4 per
+//     lane) and a share of the tokens, 31 x 4 running sums per lane, summed over the
+//     block's waves in LDS and then added with one fp32 atomic per (channel, tap) into
+//     the (zeroed) weight gradients.
+//   * symmetric time padding: the visual input gradient is the forward conv kernel
+//     run on dy with the taps mirrored through the centre.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "launch.h"
@@ -20,8 +25,9 @@ namespace kdaconv {
 namespace {
 
 constexpr int kDxThreads = 256;
-constexpr int kDwThreads = 64;     // threads per block (4 channels each)
-constexpr int kDwTokens = 64;      // tokens per block
+constexpr int kDwWaves = 8;        // waves per tap-gradient block
+constexpr int kDwTokens = 8;       // tokens per wave and token range
+constexpr int kCUs = 256;          // compute units the tap-gradient grid is sized for
 
 __device__ __forceinline__ float ldf(const float *p) { return *p; }
 __device__ __forceinline__ float ldf(const bf16_t *p) { return (float)*p; }
@@ -53,10 +59,10 @@ __global__ __launch_bounds__(kDxThreads) void conv_dx_kernel(ConvBwdArgs a, int 
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int o = i + 3 - j;
-                if (o < a.n_text) {
-                    g0 += ldf(wt + (size_t)c * 4 + j) * ldf(dy + base + (size_t)o * C + c);
-                    g1 += ldf(wt + (size_t)(c + 1) * 4 + j) * ldf(dy + base + (size_t)o * C + c + 1);
-                }
+                const size_t oc = (size_t)(o < a.n_text ? o : i) * C;   // unconditional load, zero weight
+                const float y0 = ldf(dy + base + oc + c), y1 = ldf(dy + base + oc + c + 1);
+                g0 += ldf(wt + (size_t)c * 4 + j) * (o < a.n_text ? y0 : 0.f);
+                g1 += ldf(wt + (size_t)(c + 1) * 4 + j) * (o < a.n_text ? y1 : 0.f);
             }
         } else {
             const int p = i - a.n_text, t = p / (a.gh * a.gw), hw = p % (a.gh * a.gw), h = hw / a.gw, w = hw % a.gw;
@@ -67,11 +73,11 @@ __global__ __launch_bounds__(kDxThreads) void conv_dx_kernel(ConvBwdArgs a, int 
 #pragma unroll
                     for (int te = 0; te < 3; ++te) {
                         const int o = vpos(a, t - (ta - P), h - (tb - 1), w - (te - 1));
-                        if (o >= 0) {
-                            const int tap = (ta * 3 + tb) * 3 + te;
-                            g0 += ldf(wv + (size_t)c * 27 + tap) * ldf(dy + base + (size_t)o * C + c);
-                            g1 += ldf(wv + (size_t)(c + 1) * 27 + tap) * ldf(dy + base + (size_t)o * C + c + 1);
-                        }
+                        const int tap = (ta * 3 + tb) * 3 + te;
+                        const size_t oc = (size_t)(o >= 0 ? o : i) * C;   // unconditional load, zero weight
+                        const float y0 = ldf(dy + base + oc + c), y1 = ldf(dy + base + oc + c + 1);
+                        g0 += ldf(wv + (size_t)c * 27 + tap) * (o >= 0 ? y0 : 0.f);
+                        g1 += ldf(wv + (size_t)(c + 1) * 27 + tap) * (o >= 0 ? y1 : 0.f);
                     }
         }
         stf(dx + base + (size_t)i * C + c, g0);
@@ -89,56 +95,74 @@ __device__ __forceinline__ void ld4c(const bf16_t *p, float (&x)[4]) {
     x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
 }
 
-// blockIdx.x = (batch, token range, channel block), flattened; a thread owns 4 channels.
+// A block owns 256 channels (4 per lane) and walks token ranges of kDwWaves * kDwTokens
+// tokens (one slice of kDwTokens per wave) with a grid stride, keeping 31 x 4 running sums
+// per lane across all of them; at the end the waves add their sums in LDS and the block
+// adds each (channel, tap) total to the zeroed fp32 gradient with one global atomic.  The
+// blocks of a channel block are the ones congruent mod the number of channel blocks.
 template <typename T>
-__global__ __launch_bounds__(kDwThreads) void conv_dw_kernel(ConvBwdArgs a, int s) {
-    const int C = a.C[s], cpb = 4 * kDwThreads, ncb = (C + cpb - 1) / cpb, nrange = (a.T + kDwTokens - 1) / kDwTokens;
-    const int cb = blockIdx.x % ncb, rg = (blockIdx.x / ncb) % nrange, b = blockIdx.x / (ncb * nrange);
-    const int c = cb * cpb + 4 * threadIdx.x;
-    if (c >= C) return;
-    const T *x = static_cast<const T *>(a.x[s]) + (size_t)b * a.T * C + c;
-    const T *dy = static_cast<const T *>(a.dy[s]) + (size_t)b * a.T * C + c;
-    const int P = a.causal_t ? 2 : 1;
-    float st4[4][4] = {}, sv[27][4] = {};
-    const int i0 = rg * kDwTokens, i1 = min(a.T, i0 + kDwTokens);
-    for (int i = i0; i < i1; ++i) {
-        float g[4];
-        ld4c(dy + (size_t)i * C, g);
-        if (i < a.n_text) {
+__global__ __launch_bounds__(64 * kDwWaves) void conv_dw_kernel(ConvBwdArgs a, int s) {
+    __shared__ float red[31][4][64];   // [tap: 4 text then 27 visual][channel of the lane's 4][lane]
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    const int C = a.C[s], ncb = (C + 255) / 256, span = kDwWaves * kDwTokens, nrange = (a.T + span - 1) / span;
+    const int cb = blockIdx.x % ncb, c = cb * 256 + 4 * lane;
+    for (int e = threadIdx.x; e < 31 * 4 * 64; e += 64 * kDwWaves) (&red[0][0][0])[e] = 0.f;
+    __syncthreads();
+    if (c < C) {
+        const int P = a.causal_t ? 2 : 1;
+        // every load is issued unconditionally (a position off the grid reads the token
+        // itself and contributes zero), so a token's loads are in flight together
+        float st4[4][4] = {}, sv[27][4] = {};
+        for (int r = blockIdx.x / ncb; r < a.B * nrange; r += gridDim.x / ncb) {
+            const int b = r / nrange, i0 = (r % nrange) * span + wave * kDwTokens, i1 = min(a.T, i0 + kDwTokens);
+            const T *x = static_cast<const T *>(a.x[s]) + (size_t)b * a.T * C + c;
+            const T *dy = static_cast<const T *>(a.dy[s]) + (size_t)b * a.T * C + c;
+            for (int i = i0; i < i1; ++i) {
+                float g[4];
+                ld4c(dy + (size_t)i * C, g);
+                if (i < a.n_text) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int src = i - 3 + j;
-                if (src >= 0) {
-                    float xv[4];
-                    ld4c(x + (size_t)src * C, xv);
+                    for (int j = 0; j < 4; ++j) {
+                        const int src = i - 3 + j;
+                        float xv[4];
+                        ld4c(x + (size_t)max(src, 0) * C, xv);
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) st4[j][u] += g[u] * xv[u];
+                        for (int u = 0; u < 4; ++u) st4[j][u] += g[u] * (src >= 0 ? xv[u] : 0.f);
+                    }
+                } else {
+                    const int p = i - a.n_text, t = p / (a.gh * a.gw), hw = p % (a.gh * a.gw), h = hw / a.gw,
+                              w = hw % a.gw;
+#pragma unroll
+                    for (int ta = 0; ta < 3; ++ta)
+#pragma unroll
+                        for (int tb = 0; tb < 3; ++tb)
+#pragma unroll
+                            for (int te = 0; te < 3; ++te) {
+                                const int src = vpos(a, t + ta - P, h + tb - 1, w + te - 1);
+                                float xv[4];
+                                ld4c(x + (size_t)(src >= 0 ? src : i) * C, xv);
+#pragma unroll
+                                for (int u = 0; u < 4; ++u)
+                                    sv[(ta * 3 + tb) * 3 + te][u] += g[u] * (src >= 0 ? xv[u] : 0.f);
+                            }
                 }
             }
-        } else {
-            const int p = i - a.n_text, t = p / (a.gh * a.gw), hw = p % (a.gh * a.gw), h = hw / a.gw, w = hw % a.gw;
+        }
 #pragma unroll
-            for (int ta = 0; ta < 3; ++ta)
+        for (int u = 0; u < 4; ++u) {
 #pragma unroll
-                for (int tb = 0; tb < 3; ++tb)
+            for (int j = 0; j < 4; ++j)
+                if (st4[j][u] != 0.f) atomicAdd(&red[j][u][lane], st4[j][u]);
 #pragma unroll
-                    for (int te = 0; te < 3; ++te) {
-                        const int src = vpos(a, t + ta - P, h + tb - 1, w + te - 1);
-                        float xv[4] = {0.f, 0.f, 0.f, 0.f};
-                        if (src >= 0) ld4c(x + (size_t)src * C, xv);
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) sv[(ta * 3 + tb) * 3 + te][u] += g[u] * xv[u];
-                    }
+            for (int k = 0; k < 27; ++k)
+                if (sv[k][u] != 0.f) atomicAdd(&red[4 + k][u][lane], sv[k][u]);
         }
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (st4[j][u] != 0.f) atomicAdd(a.dwt[s] + (size_t)(c + u) * 4 + j, st4[j][u]);
-#pragma unroll
-        for (int k = 0; k < 27; ++k)
-            if (sv[k][u] != 0.f) atomicAdd(a.dwv[s] + (size_t)(c + u) * 27 + k, sv[k][u]);
+    __syncthreads();
+    for (int e = threadIdx.x; e < 31 * 4 * 64; e += 64 * kDwWaves) {
+        const int k = e / 256, u = (e / 64) % 4, l = e % 64, ch = cb * 256 + 4 * l + u;
+        const float v = red[k][u][l];
+        if (ch < C && v != 0.f) atomicAdd(k < 4 ? a.dwt[s] + (size_t)ch * 4 + k : a.dwv[s] + (size_t)ch * 27 + (k - 4), v);
     }
 }
 
@@ -197,8 +221,10 @@ hipError_t launch_typed(const ConvBwdArgs &a, hipStream_t stream) {
         const size_t nz_t = (size_t)a.C[s] * 4, nz_v = (size_t)a.C[s] * 27;
         hipLaunchKernelGGL(zero_kernel, dim3(64), dim3(256), 0, stream, a.dwt[s], nz_t);
         hipLaunchKernelGGL(zero_kernel, dim3(64), dim3(256), 0, stream, a.dwv[s], nz_v);
-        const int ncb = (a.C[s] + 4 * kDwThreads - 1) / (4 * kDwThreads), nrange = (a.T + kDwTokens - 1) / kDwTokens;
-        hipLaunchKernelGGL((conv_dw_kernel<T>), dim3(a.B * nrange * ncb), dim3(kDwThreads), 0, stream, a, s);
+        // one block per compute unit (a multiple of the channel-block count), at most one per range
+        const int ncb = (a.C[s] + 255) / 256, nrange = (a.T + kDwWaves * kDwTokens - 1) / (kDwWaves * kDwTokens);
+        const int per_cb = std::max(1, std::min(a.B * nrange, kCUs / ncb));
+        hipLaunchKernelGGL((conv_dw_kernel<T>), dim3(ncb * per_cb), dim3(64 * kDwWaves), 0, stream, a, s);
     }
     return hipGetLastError();
 }

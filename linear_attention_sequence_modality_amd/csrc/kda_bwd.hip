@@ -416,6 +416,15 @@ constexpr int SW = 16;                         // value columns per workgroup of
 constexpr int kMatSlots = BC * 128 / (4 * BT); // float4 slots per thread for a 64 x 128 matrix
 constexpr int kSqSlots = BC * BC / (4 * BT);   // for a 64 x 64 matrix
 
+// The ordered passes' workgroup index, regrouped so that the column blocks of one (batch,
+// head) run on one XCD and read the chunk operands through its L2: workgroups are dealt to
+// the 8 XCDs round robin, so workgroup i goes to XCD i % 8, and XCD x takes the logical
+// blocks x * n / 8 .. (x + 1) * n / 8 - 1 (a bijection when n is a multiple of 8).
+__device__ __forceinline__ int xcd_grouped_block() {
+    const int i = blockIdx.x, n = gridDim.x;
+    return n % 8 ? i : (i % 8) * (n / 8) + i / 8;
+}
+
 // Columns j0 .. j0+SW-1 of rows 0..rows-1 of a row-major [rows][ld] matrix, into LDS [rows][SW].
 __device__ __forceinline__ void load_cols(float *dst, const float *src, int rows, int ld, int j0) {
     for (int e = threadIdx.x; e < rows * SW; e += BT) dst[e] = src[(size_t)(e / SW) * ld + j0 + e % SW];
@@ -427,8 +436,8 @@ __device__ __forceinline__ void load_cols(float *dst, const float *src, int rows
 __global__ __launch_bounds__(BT) void bwd_states_kernel(KdaBwdArgs a) {
     __shared__ __attribute__((aligned(16))) float S[128 * SW], U[BC * SW], Wt[128 * (BC + 1)], Khl[BC * 128],
         Utl[BC * SW], eCl[128];
-    const int DK = a.dk, DV = a.dv, nvs = DV / SW;
-    const int bh = blockIdx.x / nvs, j0 = (blockIdx.x % nvs) * SW;
+    const int DK = a.dk, DV = a.dv, nvs = DV / SW, L = xcd_grouped_block();
+    const int bh = L / nvs, j0 = (L % nvs) * SW;
     for (int e = threadIdx.x; e < DK * SW; e += BT) S[e] = a.s0 ? a.s0[((size_t)bh * DK + e / SW) * DV + j0 + e % SW] : 0.f;
     Pre<kMatSlots> pw, pk;
     {
@@ -467,8 +476,8 @@ template <typename T>
 __global__ __launch_bounds__(BT) void bwd_reverse_kernel(KdaBwdArgs a) {
     __shared__ __attribute__((aligned(16))) float dS[128 * SW], dSn[128 * SW], dU[BC * SW], dO[BC * SW],
         Bql[BC * BC], Kht[128 * (BC + 1)], Qtl[BC * 128], Wl[BC * 128], eCl[128];
-    const int DK = a.dk, DV = a.dv, H = a.H, nvs = DV / SW;
-    const int bh = blockIdx.x / nvs, j0 = (blockIdx.x % nvs) * SW, b = bh / H, h = bh % H;
+    const int DK = a.dk, DV = a.dv, H = a.H, nvs = DV / SW, L = xcd_grouped_block();
+    const int bh = L / nvs, j0 = (L % nvs) * SW, b = bh / H, h = bh % H;
     const T *go = static_cast<const T *>(a.dO);
     for (int e = threadIdx.x; e < DK * SW; e += BT)
         dS[e] = a.dsT ? a.dsT[((size_t)bh * DK + e / SW) * DV + j0 + e % SW] : 0.f;
@@ -522,7 +531,7 @@ __global__ __launch_bounds__(BT) void bwd_reverse_kernel(KdaBwdArgs a) {
 
 // Gradients of one chunk's tokens.
 template <typename T>
-__global__ __launch_bounds__(BT) void bwd_intra_kernel(KdaBwdArgs a) {
+__global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
     __shared__ __attribute__((aligned(16))) float tA[kPanel][kPs], tB[kPanel][kPs];
     const int DK = a.dk, DV = a.dv, H = a.H, tid = threadIdx.x;
     float *s;
