@@ -17,13 +17,13 @@
 //   dG = dQt Qt + dKt Kt - dKd Kd - dKh Kh  (+ on the last row: colsum(dKh Kh) + exp(gC) rowsum(dS' S)),
 //   dlog alpha = reverse cumulative sum of dG over the chunk, dalpha = dlog alpha / alpha.
 //
-// Four launches, all fp32 inside:
+// Three launches, all fp32 inside:
 //   1. bwd_prep:    per (batch, head, chunk), in parallel: Qt, Kh, W, Ut, Bq, exp(gC).
-//   2. bwd_states:  per (batch, head, 16 value columns), in chunk order: the state
-//                   at the start of every chunk.
-//   3. bwd_reverse: per (batch, head, 16 value columns), in reverse chunk order:
-//                   dS' of every chunk and the gradient of the initial state.
-//   4. bwd_intra:   per (batch, head, chunk), in parallel: the gradients of the
+//   2. bwd_ordered: two independent passes side by side, per (batch, head, 16 value
+//                   columns): in chunk order the state at the start of every chunk,
+//                   and in reverse chunk order dS' of every chunk and the gradient of
+//                   the initial state.
+//   3. bwd_intra:   per (batch, head, chunk), in parallel: the gradients of the
 //                   chunk's tokens.
 // The dense products run through one LDS-tiled fp32 routine (64 x 64 output
 // tiles, 4 x 4 per thread); this pass is written for exactness first.
@@ -433,10 +433,11 @@ __device__ __forceinline__ void load_cols(float *dst, const float *src, int rows
 // State at the start of every chunk: S_{n+1} = Diag(eC) S_n + Kh^T (Ut - W S_n), per SW value
 // columns.  The state and the chunk's operands live in LDS; the next chunk's W and Kh are
 // loaded into registers while the current one is computed.
-__global__ __launch_bounds__(BT) void bwd_states_kernel(KdaBwdArgs a) {
-    __shared__ __attribute__((aligned(16))) float S[128 * SW], U[BC * SW], Wt[128 * (BC + 1)], Khl[BC * 128],
-        Utl[BC * SW], eCl[128];
-    const int DK = a.dk, DV = a.dv, nvs = DV / SW, L = xcd_grouped_block();
+// (L: this workgroup's logical index among the pass's B * H * DV / SW; lds: the LDS area)
+__device__ void states_pass(const KdaBwdArgs &a, int L, float *lds) {
+    float *S = lds, *U = S + 128 * SW, *Wt = U + BC * SW, *Khl = Wt + 128 * (BC + 1), *Utl = Khl + BC * 128,
+          *eCl = Utl + BC * SW;
+    const int DK = a.dk, DV = a.dv, nvs = DV / SW;
     const int bh = L / nvs, j0 = (L % nvs) * SW;
     for (int e = threadIdx.x; e < DK * SW; e += BT) S[e] = a.s0 ? a.s0[((size_t)bh * DK + e / SW) * DV + j0 + e % SW] : 0.f;
     Pre<kMatSlots> pw, pk;
@@ -473,10 +474,10 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(KdaBwdArgs a) {
 // Reverse pass: dS' of every chunk (the gradient of the state after it) and dS0, per SW
 // value columns, with the same LDS layout and register prefetch.
 template <typename T>
-__global__ __launch_bounds__(BT) void bwd_reverse_kernel(KdaBwdArgs a) {
-    __shared__ __attribute__((aligned(16))) float dS[128 * SW], dSn[128 * SW], dU[BC * SW], dO[BC * SW],
-        Bql[BC * BC], Kht[128 * (BC + 1)], Qtl[BC * 128], Wl[BC * 128], eCl[128];
-    const int DK = a.dk, DV = a.dv, H = a.H, nvs = DV / SW, L = xcd_grouped_block();
+__device__ void reverse_pass(const KdaBwdArgs &a, int L, float *lds) {
+    float *dS = lds, *dSn = dS + 128 * SW, *dU = dSn + 128 * SW, *dO = dU + BC * SW, *Bql = dO + BC * SW,
+          *Kht = Bql + BC * BC, *Qtl = Kht + 128 * (BC + 1), *Wl = Qtl + BC * 128, *eCl = Wl + BC * 128;
+    const int DK = a.dk, DV = a.dv, H = a.H, nvs = DV / SW;
     const int bh = L / nvs, j0 = (L % nvs) * SW, b = bh / H, h = bh % H;
     const T *go = static_cast<const T *>(a.dO);
     for (int e = threadIdx.x; e < DK * SW; e += BT)
@@ -527,6 +528,23 @@ __global__ __launch_bounds__(BT) void bwd_reverse_kernel(KdaBwdArgs a) {
     __syncthreads();
     if (a.ds0)
         for (int e = threadIdx.x; e < DK * SW; e += BT) a.ds0[((size_t)bh * DK + e / SW) * DV + j0 + e % SW] = dS[e];
+}
+
+// The two ordered passes need only the per-chunk records, not each other's results, so they
+// run side by side in one launch: workgroups 0 .. n_states-1 (logical) compute the states,
+// the rest the reverse pass, each half over whole XCDs.
+constexpr int kStatesLds = 128 * SW + 2 * BC * SW + 128 * (BC + 1) + BC * 128 + 128;
+constexpr int kReverseLds = 2 * 128 * SW + 2 * BC * SW + BC * BC + 128 * (BC + 1) + 2 * BC * 128 + 128;
+constexpr int kOrderedLds = kStatesLds > kReverseLds ? kStatesLds : kReverseLds;
+static_assert(kOrderedLds * 4 <= 160 * 1024, "the ordered passes' LDS fits a CU");
+template <typename T>
+__global__ __launch_bounds__(BT) void bwd_ordered_kernel(KdaBwdArgs a, int n_states) {
+    __shared__ __attribute__((aligned(16))) float lds[kOrderedLds];
+    const int L = xcd_grouped_block();
+    if (L < n_states)
+        states_pass(a, L, lds);
+    else
+        reverse_pass<T>(a, L - n_states, lds);
 }
 
 // Gradients of one chunk's tokens.
@@ -716,13 +734,11 @@ hipError_t launch_kda_backward(KdaBwdArgs a, bool bf16, hipStream_t stream) {
     const int ordered = a.B * a.H * (a.dv / SW);
     if (bf16) {
         hipLaunchKernelGGL(bwd_prep_kernel<bf16_t>, dim3(g), dim3(BT), 0, stream, a);
-        hipLaunchKernelGGL(bwd_states_kernel, dim3(ordered), dim3(BT), 0, stream, a);
-        hipLaunchKernelGGL(bwd_reverse_kernel<bf16_t>, dim3(ordered), dim3(BT), 0, stream, a);
+        hipLaunchKernelGGL(bwd_ordered_kernel<bf16_t>, dim3(2 * ordered), dim3(BT), 0, stream, a, ordered);
         hipLaunchKernelGGL(bwd_intra_kernel<bf16_t>, dim3(g), dim3(BT), 0, stream, a);
     } else {
         hipLaunchKernelGGL(bwd_prep_kernel<float>, dim3(g), dim3(BT), 0, stream, a);
-        hipLaunchKernelGGL(bwd_states_kernel, dim3(ordered), dim3(BT), 0, stream, a);
-        hipLaunchKernelGGL(bwd_reverse_kernel<float>, dim3(ordered), dim3(BT), 0, stream, a);
+        hipLaunchKernelGGL(bwd_ordered_kernel<float>, dim3(2 * ordered), dim3(BT), 0, stream, a, ordered);
         hipLaunchKernelGGL(bwd_intra_kernel<float>, dim3(g), dim3(BT), 0, stream, a);
     }
     return hipGetLastError();
