@@ -416,6 +416,40 @@ constexpr int SW = 16;                         // value columns per workgroup of
 constexpr int kMatSlots = BC * 128 / (4 * BT); // float4 slots per thread for a 64 x 128 matrix
 constexpr int kSqSlots = BC * BC / (4 * BT);   // for a 64 x 64 matrix
 
+// 4 consecutive elements as fp32.
+__device__ __forceinline__ void ld4(const float *p, float (&x)[4]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
+__device__ __forceinline__ void ld4(const bf16_t *p, float (&x)[4]) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+}
+
+// Register prefetch of an ordered pass's small per-chunk operands: a [BC][SW] column slice
+// of a row-major matrix (4 values per thread: row tid / 4, columns 4 (tid % 4) ..; rows at
+// or past nr are read from row 0 and stored as zeros) and the chunk's DK decay factors.
+// The loads carry no branch, so they stay in flight through the chunk's products.
+template <typename T>
+struct SlicePre {
+    float v[4], e[4];
+    int ok;
+    __device__ __forceinline__ void load(const T *base, size_t row_stride, int nr, const float *eC, int DK) {
+        const int r = threadIdx.x / 4;
+        ok = r < nr;
+        ld4(base + (size_t)(ok ? r : 0) * row_stride + 4 * (threadIdx.x % 4), v);
+        ld4(eC + 4 * min((int)threadIdx.x, DK / 4 - 1), e);
+    }
+    __device__ __forceinline__ void store(float *slice, float *eCl, int DK) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) slice[4 * threadIdx.x + i] = ok ? v[i] : 0.f;
+        if ((int)threadIdx.x < DK / 4)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) eCl[4 * threadIdx.x + i] = e[i];
+    }
+};
+static_assert(BC * SW == 4 * BT, "one 4-value piece of a column slice per thread");
+
 // The ordered passes' workgroup index, regrouped so that the column blocks of one (batch,
 // head) run on one XCD and read the chunk operands through its L2: workgroups are dealt to
 // the 8 XCDs round robin, so workgroup i goes to XCD i % 8, and XCD x takes the logical
@@ -423,11 +457,6 @@ constexpr int kSqSlots = BC * BC / (4 * BT);   // for a 64 x 64 matrix
 __device__ __forceinline__ int xcd_grouped_block() {
     const int i = blockIdx.x, n = gridDim.x;
     return n % 8 ? i : (i % 8) * (n / 8) + i / 8;
-}
-
-// Columns j0 .. j0+SW-1 of rows 0..rows-1 of a row-major [rows][ld] matrix, into LDS [rows][SW].
-__device__ __forceinline__ void load_cols(float *dst, const float *src, int rows, int ld, int j0) {
-    for (int e = threadIdx.x; e < rows * SW; e += BT) dst[e] = src[(size_t)(e / SW) * ld + j0 + e % SW];
 }
 
 // State at the start of every chunk: S_{n+1} = Diag(eC) S_n + Kh^T (Ut - W S_n), per SW value
@@ -441,18 +470,18 @@ __device__ void states_pass(const KdaBwdArgs &a, int L, float *lds) {
     const int bh = L / nvs, j0 = (L % nvs) * SW;
     for (int e = threadIdx.x; e < DK * SW; e += BT) S[e] = a.s0 ? a.s0[((size_t)bh * DK + e / SW) * DV + j0 + e % SW] : 0.f;
     Pre<kMatSlots> pw, pk;
+    SlicePre<float> pu;
     {
         const Rec r = rec_at(a, bh, 0);
         pw.load(r.W, BC * DK);
         pk.load(r.Kh, BC * DK);
+        pu.load(r.Ut + j0, DV, BC, r.eC, DK);
     }
     for (int n = 0; n < a.n_chunks; ++n) {
-        const Rec r = rec_at(a, bh, n);
         __syncthreads();                       // the previous step is done with the LDS operands
         pw.store_t(Wt, BC * DK, DK, BC + 1);   // W^T, [DK][BC + 1]
         pk.store(Khl, BC * DK);
-        load_cols(Utl, r.Ut, BC, DV, j0);
-        for (int e = threadIdx.x; e < DK; e += BT) eCl[e] = r.eC[e];
+        pu.store(Utl, eCl, DK);
         float *Sn = a.states + ((size_t)bh * a.n_chunks + n) * DK * DV;
         for (int e = threadIdx.x; e < DK * SW; e += BT) Sn[(size_t)(e / SW) * DV + j0 + e % SW] = S[e];
         __syncthreads();
@@ -460,6 +489,7 @@ __device__ void states_pass(const KdaBwdArgs &a, int L, float *lds) {
             const Rec r1 = rec_at(a, bh, n + 1);
             pw.load(r1.W, BC * DK);
             pk.load(r1.Kh, BC * DK);
+            pu.load(r1.Ut + j0, DV, BC, r1.eC, DK);
         }
         for (int e = threadIdx.x; e < BC * SW; e += BT) U[e] = Utl[e];
         __syncthreads();
@@ -482,28 +512,27 @@ __device__ void reverse_pass(const KdaBwdArgs &a, int L, float *lds) {
     const T *go = static_cast<const T *>(a.dO);
     for (int e = threadIdx.x; e < DK * SW; e += BT)
         dS[e] = a.dsT ? a.dsT[((size_t)bh * DK + e / SW) * DV + j0 + e % SW] : 0.f;
+    const T *go_bh = go + ((size_t)b * a.T * H + h) * DV + j0;   // dO of this (batch, head), columns j0 ..
+    const size_t chunk_rows = (size_t)BC * H * DV;                  // its offset per chunk
     Pre<kSqSlots> pb;
     Pre<kMatSlots> pk, pq, pw;
+    SlicePre<T> po;
     {
-        const Rec r = rec_at(a, bh, a.n_chunks - 1);
+        const int n = a.n_chunks - 1;
+        const Rec r = rec_at(a, bh, n);
         pb.load(r.Bq, BC * BC);
         pk.load(r.Kh, BC * DK);
         pq.load(r.Qt, BC * DK);
         pw.load(r.W, BC * DK);
+        po.load(go_bh + n * chunk_rows, (size_t)H * DV, min(BC, a.T - n * BC), r.eC, DK);
     }
     for (int n = a.n_chunks - 1; n >= 0; --n) {
-        const Rec r = rec_at(a, bh, n);
         __syncthreads();
         pb.store(Bql, BC * BC);
         pk.store_t(Kht, BC * DK, DK, BC + 1);  // Kh^T, [DK][BC + 1]
         pq.store(Qtl, BC * DK);
         pw.store(Wl, BC * DK);
-        for (int e = threadIdx.x; e < DK; e += BT) eCl[e] = r.eC[e];
-        const int t0 = n * BC, nr = min(BC, a.T - t0);
-        for (int e = threadIdx.x; e < BC * SW; e += BT) {
-            const int rr = e / SW;
-            dO[e] = rr < nr ? ld(go + (((size_t)b * a.T + t0 + rr) * H + h) * DV + j0 + e % SW) : 0.f;
-        }
+        po.store(dO, eCl, DK);
         float *dSp = a.dstates + ((size_t)bh * a.n_chunks + n) * DK * DV;
         for (int e = threadIdx.x; e < DK * SW; e += BT) dSp[(size_t)(e / SW) * DV + j0 + e % SW] = dS[e];
         __syncthreads();
@@ -513,6 +542,7 @@ __device__ void reverse_pass(const KdaBwdArgs &a, int L, float *lds) {
             pk.load(r1.Kh, BC * DK);
             pq.load(r1.Qt, BC * DK);
             pw.load(r1.W, BC * DK);
+            po.load(go_bh + (n - 1) * chunk_rows, (size_t)H * DV, BC, r1.eC, DK);
         }
         lds_mm(dU, SW, Bql, BC, dO, SW, BC, SW, BC, 1.f, false);            // dU = Bq^T dO
         __syncthreads();
