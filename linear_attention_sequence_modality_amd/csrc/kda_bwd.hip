@@ -45,69 +45,89 @@ enum Mask { kNoMask = 0, kLower = 1, kStrictLower = 2 };
 
 // C[m][n] = scale * sum_k op(A)[m][k] op(B)[k][n]  (+ C when acc), for m < M, n < N;
 // op(A)[m][k] = TA ? A[k*lda + m] : A[m*lda + k]; op(B)[k][n] = TB ? B[n*ldb + k] : B[k*ldb + n].
-// M, N multiples of 64, K a multiple of 4 and at most 128, leading dimensions multiples
-// of 4 and 16-byte aligned operands.  Per 64 x 64 output tile the whole K panels of both
-// operands are read at once (float4 loads, all in flight together) into LDS as
-// tA[k][m], tB[k][n]; each thread then forms 4 x 4 outputs.  The mask zeroes the
-// result above the diagonal (kLower) or on and above it (kStrictLower).  Ends with a barrier.
-constexpr int kPanel = 128;   // largest K
+// M, N multiples of 64, K a multiple of 32 and at most 128, leading dimensions multiples
+// of 4 and 16-byte aligned operands.  Per 64 x 64 output tile, K is walked in steps of
+// kKc rows: the panels of step j+1 (float4 loads into registers, two pieces per thread
+// and operand) are in flight while step j is computed from LDS, and the steps alternate
+// between two LDS buffers (tA[k][m], tB[k][n]), so one barrier per step suffices.  Each
+// thread forms 4 x 4 outputs.  The mask zeroes the result above the diagonal (kLower) or
+// on and above it (kStrictLower).  Ends with a barrier.
+constexpr int kPanel = 128;   // rows of the LDS panel area (two buffers of kKc rows in use)
 constexpr int kPs = 68;       // panel row stride (64 + 4)
+constexpr int kKc = 32;       // K rows per pipelined step
+static_assert(kKc * 64 == 8 * BT, "two float4 pieces per thread and operand per step");
+
+__device__ __forceinline__ float4 ld4f(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+
+// This thread's pieces e = tid, tid + BT of the kKc x 64 panels of op(A) (columns m0..) and
+// op(B) (columns n0..) at K rows k0..
 template <bool TA, bool TB>
-__device__ void gemm(float *C, int ldc, const float *A, int lda, const float *B, int ldb, int M, int N, int K,
+__device__ __forceinline__ void panel_fetch(const float *A, int lda, const float *B, int ldb, int m0, int n0, int k0,
+                                            float4 (&va)[2], float4 (&vb)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int e = threadIdx.x + BT * i;
+        va[i] = TA ? ld4f(A + (size_t)(k0 + e / 16) * lda + m0 + 4 * (e % 16))
+                   : ld4f(A + (size_t)(m0 + e / 8) * lda + k0 + 4 * (e % 8));
+        vb[i] = TB ? ld4f(B + (size_t)(n0 + e / 8) * ldb + k0 + 4 * (e % 8))
+                   : ld4f(B + (size_t)(k0 + e / 16) * ldb + n0 + 4 * (e % 16));
+    }
+}
+template <bool TA, bool TB>
+__device__ __forceinline__ void panel_store(float (*pa)[kPs], float (*pb)[kPs], const float4 (&va)[2],
+                                            const float4 (&vb)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int e = threadIdx.x + BT * i;
+        if (TA) {
+            *reinterpret_cast<float4 *>(&pa[e / 16][4 * (e % 16)]) = va[i];
+        } else {
+            const int mm = e / 8, q = e % 8;
+            pa[4 * q][mm] = va[i].x;
+            pa[4 * q + 1][mm] = va[i].y;
+            pa[4 * q + 2][mm] = va[i].z;
+            pa[4 * q + 3][mm] = va[i].w;
+        }
+        if (TB) {
+            const int nn = e / 8, q = e % 8;
+            pb[4 * q][nn] = vb[i].x;
+            pb[4 * q + 1][nn] = vb[i].y;
+            pb[4 * q + 2][nn] = vb[i].z;
+            pb[4 * q + 3][nn] = vb[i].w;
+        } else {
+            *reinterpret_cast<float4 *>(&pb[e / 16][4 * (e % 16)]) = vb[i];
+        }
+    }
+}
+
+template <bool TA, bool TB>
+__device__ __noinline__ void gemm(float *C, int ldc, const float *A, int lda, const float *B, int ldb, int M, int N, int K,
                      float scale, bool acc, Mask mask, float (*tA)[kPs], float (*tB)[kPs]) {
     const int tid = threadIdx.x, tr = tid / 16, tc = tid % 16;   // this thread: rows 4tr.., cols 4tc..
+    const int nk = K / kKc;
     for (int m0 = 0; m0 < M; m0 += 64)
         for (int n0 = 0; n0 < N; n0 += 64) {
-            // panels: K x 64 floats each, as float4 pieces, in rounds of 4 pieces per
-            // thread and operand: a round's loads all go out (indices clamped, so no load
-            // sits under a branch) before any of its pieces is stored
-            const int np = K * 16, kq = K / 4;
-            for (int i0 = 0; i0 < np; i0 += 4 * BT) {
-                float4 va[4], vb[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int e = min(i0 + tid + BT * i, np - 1);
-                    va[i] = TA ? *reinterpret_cast<const float4 *>(A + (size_t)(e / 16) * lda + m0 + 4 * (e % 16))
-                               : *reinterpret_cast<const float4 *>(A + (size_t)(m0 + e / kq) * lda + 4 * (e % kq));
-                    vb[i] = TB ? *reinterpret_cast<const float4 *>(B + (size_t)(n0 + e / kq) * ldb + 4 * (e % kq))
-                               : *reinterpret_cast<const float4 *>(B + (size_t)(e / 16) * ldb + n0 + 4 * (e % 16));
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int e = i0 + tid + BT * i;
-                    if (e < np) {
-                        if (TA) {
-                            *reinterpret_cast<float4 *>(&tA[e / 16][4 * (e % 16)]) = va[i];
-                        } else {
-                            const int mm = e / kq, q = e % kq;
-                            tA[4 * q][mm] = va[i].x;
-                            tA[4 * q + 1][mm] = va[i].y;
-                            tA[4 * q + 2][mm] = va[i].z;
-                            tA[4 * q + 3][mm] = va[i].w;
-                        }
-                        if (TB) {
-                            const int nn = e / kq, q = e % kq;
-                            tB[4 * q][nn] = vb[i].x;
-                            tB[4 * q + 1][nn] = vb[i].y;
-                            tB[4 * q + 2][nn] = vb[i].z;
-                            tB[4 * q + 3][nn] = vb[i].w;
-                        } else {
-                            *reinterpret_cast<float4 *>(&tB[e / 16][4 * (e % 16)]) = vb[i];
-                        }
-                    }
-                }
-            }
-            __syncthreads();
+            float4 va[2], vb[2];
+            panel_fetch<TA, TB>(A, lda, B, ldb, m0, n0, 0, va, vb);
             float c[4][4] = {};
+            for (int kc = 0; kc < nk; ++kc) {
+                float(*pa)[kPs] = tA + (kc & 1) * kKc;
+                float(*pb)[kPs] = tB + (kc & 1) * kKc;
+                panel_store<TA, TB>(pa, pb, va, vb);
+                __syncthreads();
+                // the next step's panels (the last step fetches its own again: no branch, so
+                // the loads need not complete before the products below)
+                panel_fetch<TA, TB>(A, lda, B, ldb, m0, n0, min(kc + 1, nk - 1) * kKc, va, vb);
 #pragma unroll 4
-            for (int kk = 0; kk < K; ++kk) {
-                const float4 a4 = *reinterpret_cast<const float4 *>(&tA[kk][4 * tr]);
-                const float4 b4 = *reinterpret_cast<const float4 *>(&tB[kk][4 * tc]);
-                const float a[4] = {a4.x, a4.y, a4.z, a4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
+                for (int kk = 0; kk < kKc; ++kk) {
+                    const float4 a4 = *reinterpret_cast<const float4 *>(&pa[kk][4 * tr]);
+                    const float4 b4 = *reinterpret_cast<const float4 *>(&pb[kk][4 * tc]);
+                    const float a[4] = {a4.x, a4.y, a4.z, a4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                    for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) c[i][j] = fmaf(a[i], b[j], c[i][j]);
+                        for (int j = 0; j < 4; ++j) c[i][j] = fmaf(a[i], b[j], c[i][j]);
+                }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
