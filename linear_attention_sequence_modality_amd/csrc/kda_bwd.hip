@@ -345,18 +345,16 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(KdaBwdArgs a) {
     const int items = a.B * a.H * a.n_chunks;
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
         const int bh = it / a.n_chunks, n = it % a.n_chunks;
-        chunk_forward<T>(a, c, bh, n, tA, tB);
+        // the matrices the ordered passes read are formed in place in the chunk's record
         const Rec r = rec_at(a, bh, n);
-        const int DK = a.dk, DV = a.dv;
-        for (int e = threadIdx.x; e < BC * DK; e += BT) {
-            r.Qt[e] = c.Qt[e];
-            r.Kh[e] = c.Kh[e];
-            r.W[e] = c.W[e];
-        }
-        for (int e = threadIdx.x; e < BC * DV; e += BT) r.Ut[e] = c.Ut[e];
-        for (int e = threadIdx.x; e < BC * BC; e += BT) r.Bq[e] = c.Bq[e];
-        for (int e = threadIdx.x; e < DK; e += BT) r.eC[e] = c.eC[e];
-        __syncthreads();
+        ChunkMats cr = c;
+        cr.Qt = r.Qt;
+        cr.Kh = r.Kh;
+        cr.W = r.W;
+        cr.Ut = r.Ut;
+        cr.Bq = r.Bq;
+        cr.eC = r.eC;
+        chunk_forward<T>(a, cr, bh, n, tA, tB);   // ends with a barrier
     }
 }
 
@@ -605,7 +603,7 @@ __global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
     float *s;
     const ChunkMats c = carve(a.scratch + (size_t)blockIdx.x * a.scratch_floats, DK, DV, &s);
     const size_t mk = (size_t)BC * DK, mv = (size_t)BC * DV, mc = (size_t)BC * BC;
-    float *U = s; s += mv;
+    float *U = c.Ut;   // U = Ut - W S, formed in place
     float *dO = s; s += mv;
     float *dU = s; s += mv;
     float *dBq = s; s += mc;
@@ -630,8 +628,6 @@ __global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
         chunk_forward<T>(a, c, bh, n, tA, tB);
         const float *Sn = a.states + ((size_t)bh * a.n_chunks + n) * DK * DV;
         const float *dSp = a.dstates + ((size_t)bh * a.n_chunks + n) * DK * DV;
-        for (int e4 = tid; e4 < BC * DV / 4; e4 += BT)
-            *reinterpret_cast<float4 *>(U + 4 * e4) = *reinterpret_cast<const float4 *>(c.Ut + 4 * e4);
         stage_rows(dO, go + tok(0) * DV, (size_t)H * DV, BC, DV, nr);
         __syncthreads();
         gemm<false, false>(U, DV, c.W, DK, Sn, DV, BC, DV, DK, -1.f, true, kNoMask, tA, tB);        // U = Ut - W S
@@ -771,7 +767,7 @@ size_t kda_bwd_scratch_floats(int dk, int dv) {
     const size_t mk = (size_t)BC * dk, mv = (size_t)BC * dv, mc = (size_t)BC * BC;
     // ChunkMats + the intra kernel's temporaries (the largest user)
     const size_t chunk = 9 * mk + 4 * mv + 3 * mc + BC + dk;
-    const size_t intra = 4 * mv + 4 * mc + 6 * mk;
+    const size_t intra = 3 * mv + 4 * mc + 6 * mk;
     return chunk + intra + 64;
 }
 
