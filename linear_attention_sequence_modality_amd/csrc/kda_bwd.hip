@@ -253,22 +253,36 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
     __syncthreads();
     gemm<false, true>(c.A, BC, c.Kt, DK, c.Kd, DK, BC, BC, DK, 1.f, false, kStrictLower, tA, tB);
     gemm<false, true>(c.Bq, BC, c.Qt, DK, c.Kd, DK, BC, BC, DK, 1.f, false, kLower, tA, tB);
-    // Tm = (I + Diag(beta) A)^-1 (unit lower triangular): column j by forward substitution, in LDS
+    // Tm = (I + Diag(beta) A)^-1 (unit lower triangular) by forward substitution: lane j of
+    // wave 0 owns column j in registers (the loops are unrolled), so row i needs only row i
+    // of A, read from LDS as float4s that every lane shares.  Entries above the diagonal
+    // come out as (signed) zeros: their sums only see the column's zeros above the diagonal.
     {
-        float *Al = lw, *Tl = lw + BC * BC;
+        float *Al = lw, *Tl = lw + BC * BC, *bl = Tl + BC * BC;
         stage_rows(Al, c.A, BC, BC, BC, BC);
+        if (tid < BC) bl[tid] = c.beta[tid];
         __syncthreads();
         if (tid < BC) {
             const int j = tid;
+            float t[BC];
+#pragma unroll
             for (int i = 0; i < BC; ++i) {
-                float x = i == j ? 1.f : 0.f;
-                if (i > j) {
-                    float sum = 0.f;
-                    for (int u = j; u < i; ++u) sum += Al[i * BC + u] * Tl[u * BC + j];
-                    x = -c.beta[i] * sum;
+                float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+                for (int u = 0; u + 4 <= i; u += 4) {
+                    const float4 av = *reinterpret_cast<const float4 *>(Al + i * BC + u);
+                    s0 = fmaf(av.x, t[u], s0);
+                    s1 = fmaf(av.y, t[u + 1], s1);
+                    s2 = fmaf(av.z, t[u + 2], s2);
+                    s3 = fmaf(av.w, t[u + 3], s3);
                 }
-                Tl[i * BC + j] = x;
+#pragma unroll
+                for (int u = i & ~3; u < i; ++u) s0 = fmaf(Al[i * BC + u], t[u], s0);
+                const float x = -bl[i] * ((s0 + s1) + (s2 + s3));
+                t[i] = i == j ? 1.f : x;
             }
+#pragma unroll
+            for (int i = 0; i < BC; ++i) Tl[i * BC + j] = t[i];
         }
         __syncthreads();
         for (int e4 = tid; e4 < BC * BC / 4; e4 += BT)
