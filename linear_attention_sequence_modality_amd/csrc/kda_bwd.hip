@@ -32,6 +32,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "mfma.h"
 
 namespace kdaconv {
 namespace {
@@ -373,37 +374,37 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(KdaBwdArgs a) {
 }
 
 // C[m][n] += scale * sum_k At[k*lda + m] B[k*ldb + n] (C = that sum when !acc), all in
-// LDS, N a multiple of 4.  A thread owns 4 consecutive n of one m: per k it reads one At
-// value (consecutive m across lanes) and one float4 of B (a broadcast among lanes of one
-// n-quad), and keeps 4 independent sums, unrolled over k so the reads run ahead.
-__device__ __forceinline__ void lds_mm(float *C, int ldc, const float *At, int lda, const float *B, int ldb, int M,
-                                       int N, int K, float scale, bool acc) {
-    const int nq = N / 4;
-    for (int e = threadIdx.x; e < M * nq; e += BT) {
-        const int m = e % M, n = 4 * (e / M);
-        float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
-#pragma unroll 8
-        for (int k = 0; k < K; ++k) {
-            const float av = At[k * lda + m];
-            const float4 bv = *reinterpret_cast<const float4 *>(B + k * ldb + n);
-            x0 = fmaf(av, bv.x, x0);
-            x1 = fmaf(av, bv.y, x1);
-            x2 = fmaf(av, bv.z, x2);
-            x3 = fmaf(av, bv.w, x3);
+// LDS, for N = 16, M a multiple of 16 and K = 64 or 128, on the fp32 matrix cores:
+// the 16 x 16 output blocks go round the four waves, each a chain of K / 4 steps of
+// v_mfma_f32_16x16x4_f32 (lane l supplies A[l%16][k + l/16] and B[k + l/16][l%16]) over
+// two interleaved accumulators.
+template <int K>
+__device__ __forceinline__ void lds_mm_k(float *C, int ldc, const float *At, int lda, const float *B, int ldb, int M,
+                                         float scale, bool acc) {
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, g = lane / 16, l16 = lane % 16;
+    for (int rb = wave; rb < M / 16; rb += BT / 64) {
+        f32x4_t c0 = zero4(), c1 = zero4();
+        const float *a = At + g * lda + rb * 16 + l16;
+        const float *b = B + g * ldb + l16;
+#pragma unroll
+        for (int k = 0; k < K; k += 8) {
+            c0 = mma4(a[k * lda], b[k * ldb], c0);
+            c1 = mma4(a[(k + 4) * lda], b[(k + 4) * ldb], c1);
         }
-        float *c = C + m * ldc + n;
-        if (acc) {
-            c[0] += scale * x0;
-            c[1] += scale * x1;
-            c[2] += scale * x2;
-            c[3] += scale * x3;
-        } else {
-            c[0] = scale * x0;
-            c[1] = scale * x1;
-            c[2] = scale * x2;
-            c[3] = scale * x3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float *p = C + (rb * 16 + 4 * g + i) * ldc + l16;
+            const float x = scale * (c0[i] + c1[i]);
+            *p = acc ? *p + x : x;
         }
     }
+}
+__device__ __forceinline__ void lds_mm(float *C, int ldc, const float *At, int lda, const float *B, int ldb, int M,
+                                       int K, float scale, bool acc) {
+    if (K == 128)
+        lds_mm_k<128>(C, ldc, At, lda, B, ldb, M, scale, acc);
+    else
+        lds_mm_k<64>(C, ldc, At, lda, B, ldb, M, scale, acc);
 }
 
 // Copy n floats (a multiple of 4, 16-byte aligned) from global memory to registers, 4 per
@@ -448,16 +449,6 @@ constexpr int SW = 16;                         // value columns per workgroup of
 constexpr int kMatSlots = BC * 128 / (4 * BT); // float4 slots per thread for a 64 x 128 matrix
 constexpr int kSqSlots = BC * BC / (4 * BT);   // for a 64 x 64 matrix
 
-// 4 consecutive elements as fp32.
-__device__ __forceinline__ void ld4(const float *p, float (&x)[4]) {
-    const float4 a = *reinterpret_cast<const float4 *>(p);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-}
-__device__ __forceinline__ void ld4(const bf16_t *p, float (&x)[4]) {
-    const uint2 u = *reinterpret_cast<const uint2 *>(p);
-    x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
-}
-
 // Register prefetch of an ordered pass's small per-chunk operands: a [BC][SW] column slice
 // of a row-major matrix (4 values per thread: row tid / 4, columns 4 (tid % 4) ..; rows at
 // or past nr are read from row 0 and stored as zeros) and the chunk's DK decay factors.
@@ -481,6 +472,7 @@ struct SlicePre {
     }
 };
 static_assert(BC * SW == 4 * BT, "one 4-value piece of a column slice per thread");
+static_assert(SW == 16, "the ordered passes' products are 16 columns wide");
 
 // The ordered passes' workgroup index, regrouped so that the column blocks of one (batch,
 // head) run on one XCD and read the chunk operands through its L2: workgroups are dealt to
@@ -525,11 +517,11 @@ __device__ void states_pass(const KdaBwdArgs &a, int L, float *lds) {
         }
         for (int e = threadIdx.x; e < BC * SW; e += BT) U[e] = Utl[e];
         __syncthreads();
-        lds_mm(U, SW, Wt, BC + 1, S, SW, BC, SW, DK, -1.f, true);            // U = Ut - W S
+        lds_mm(U, SW, Wt, BC + 1, S, SW, BC, DK, -1.f, true);            // U = Ut - W S
         __syncthreads();
         for (int e = threadIdx.x; e < DK * SW; e += BT) S[e] *= eCl[e / SW];
         __syncthreads();
-        lds_mm(S, SW, Khl, DK, U, SW, DK, SW, BC, 1.f, true);                // S += Kh^T U
+        lds_mm(S, SW, Khl, DK, U, SW, DK, BC, 1.f, true);                // S += Kh^T U
     }
 }
 
@@ -576,14 +568,14 @@ __device__ void reverse_pass(const KdaBwdArgs &a, int L, float *lds) {
             pw.load(r1.W, BC * DK);
             po.load(go_bh + (n - 1) * chunk_rows, (size_t)H * DV, BC, r1.eC, DK);
         }
-        lds_mm(dU, SW, Bql, BC, dO, SW, BC, SW, BC, 1.f, false);            // dU = Bq^T dO
+        lds_mm(dU, SW, Bql, BC, dO, SW, BC, BC, 1.f, false);            // dU = Bq^T dO
         __syncthreads();
-        lds_mm(dU, SW, Kht, BC + 1, dS, SW, BC, SW, DK, 1.f, true);         //    + Kh dS'
+        lds_mm(dU, SW, Kht, BC + 1, dS, SW, BC, DK, 1.f, true);         //    + Kh dS'
         for (int e = threadIdx.x; e < DK * SW; e += BT) dSn[e] = eCl[e / SW] * dS[e];
         __syncthreads();
-        lds_mm(dSn, SW, Qtl, DK, dO, SW, DK, SW, BC, 1.f, true);            // + Qt^T dO
+        lds_mm(dSn, SW, Qtl, DK, dO, SW, DK, BC, 1.f, true);            // + Qt^T dO
         __syncthreads();
-        lds_mm(dSn, SW, Wl, DK, dU, SW, DK, SW, BC, -1.f, true);            // - W^T dU
+        lds_mm(dSn, SW, Wl, DK, dU, SW, DK, BC, -1.f, true);            // - W^T dU
         __syncthreads();
         for (int e = threadIdx.x; e < DK * SW; e += BT) dS[e] = dSn[e];
     }
