@@ -26,7 +26,7 @@
 //   3. bwd_intra:   per (batch, head, chunk), in parallel: the gradients of the
 //                   chunk's tokens.
 // The dense products run through one LDS-tiled fp32 routine (64 x 64 output
-// tiles, 4 x 4 per thread); this pass is written for exactness first.
+// tiles on the fp32 matrix cores); all arithmetic is fp32.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -50,8 +50,8 @@ enum Mask { kNoMask = 0, kLower = 1, kStrictLower = 2 };
 // of 4 and 16-byte aligned operands.  Per 64 x 64 output tile, K is walked in steps of
 // kKc rows: the panels of step j+1 (float4 loads into registers, two pieces per thread
 // and operand) are in flight while step j is computed from LDS, and the steps alternate
-// between two LDS buffers (tA[k][m], tB[k][n]), so one barrier per step suffices.  Each
-// thread forms 4 x 4 outputs.  The mask zeroes the result above the diagonal (kLower) or
+// between two LDS buffers (tA[k][m], tB[k][n]), so one barrier per step suffices.  The
+// products run on the fp32 matrix cores.  The mask zeroes the result above the diagonal (kLower) or
 // on and above it (kStrictLower).  Ends with a barrier.
 constexpr int kPanel = 128;   // rows of the LDS panel area (two buffers of kKc rows in use)
 constexpr int kPs = 68;       // panel row stride (64 + 4)
@@ -104,13 +104,18 @@ __device__ __forceinline__ void panel_store(float (*pa)[kPs], float (*pb)[kPs], 
 template <bool TA, bool TB>
 __device__ __noinline__ void gemm(float *C, int ldc, const float *A, int lda, const float *B, int ldb, int M, int N, int K,
                      float scale, bool acc, Mask mask, float (*tA)[kPs], float (*tB)[kPs]) {
-    const int tid = threadIdx.x, tr = tid / 16, tc = tid % 16;   // this thread: rows 4tr.., cols 4tc..
+    // wave w forms the 32 x 32 quarter (rows 32 (w / 2) .., columns 32 (w % 2) ..) of each
+    // tile as 2 x 2 blocks of 16 x 16 on the fp32 matrix cores: per 4-deep k step, lane l
+    // supplies A[l%16][k + l/16] and B[k + l/16][l%16] of each block and holds rows
+    // 4 (l/16) + i, column l%16 of each result
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, g = lane / 16, l16 = lane % 16;
+    const int wm = 32 * (wave / 2), wn = 32 * (wave % 2);
     const int nk = K / kKc;
     for (int m0 = 0; m0 < M; m0 += 64)
         for (int n0 = 0; n0 < N; n0 += 64) {
             float4 va[2], vb[2];
             panel_fetch<TA, TB>(A, lda, B, ldb, m0, n0, 0, va, vb);
-            float c[4][4] = {};
+            f32x4_t c[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};
             for (int kc = 0; kc < nk; ++kc) {
                 float(*pa)[kPs] = tA + (kc & 1) * kKc;
                 float(*pb)[kPs] = tB + (kc & 1) * kKc;
@@ -119,27 +124,28 @@ __device__ __noinline__ void gemm(float *C, int ldc, const float *A, int lda, co
                 // the next step's panels (the last step fetches its own again: no branch, so
                 // the loads need not complete before the products below)
                 panel_fetch<TA, TB>(A, lda, B, ldb, m0, n0, min(kc + 1, nk - 1) * kKc, va, vb);
-#pragma unroll 4
-                for (int kk = 0; kk < kKc; ++kk) {
-                    const float4 a4 = *reinterpret_cast<const float4 *>(&pa[kk][4 * tr]);
-                    const float4 b4 = *reinterpret_cast<const float4 *>(&pb[kk][4 * tc]);
-                    const float a[4] = {a4.x, a4.y, a4.z, a4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) c[i][j] = fmaf(a[i], b[j], c[i][j]);
+                for (int k = 0; k < kKc; k += 4) {
+                    const float a0 = pa[k + g][wm + l16], a1 = pa[k + g][wm + 16 + l16];
+                    const float b0 = pb[k + g][wn + l16], b1 = pb[k + g][wn + 16 + l16];
+                    c[0][0] = mma4(a0, b0, c[0][0]);
+                    c[0][1] = mma4(a0, b1, c[0][1]);
+                    c[1][0] = mma4(a1, b0, c[1][0]);
+                    c[1][1] = mma4(a1, b1, c[1][1]);
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int m = m0 + 4 * tr + i, n = n0 + 4 * tc + j;
-                    float x = scale * c[i][j];
-                    if ((mask == kLower && n > m) || (mask == kStrictLower && n >= m)) x = 0.f;
-                    float *p = C + (size_t)m * ldc + n;
-                    *p = acc ? *p + x : x;
-                }
+                for (int bn = 0; bn < 2; ++bn)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = m0 + wm + 16 * bm + 4 * g + i, n = n0 + wn + 16 * bn + l16;
+                        float x = scale * c[bm][bn][i];
+                        if ((mask == kLower && n > m) || (mask == kStrictLower && n >= m)) x = 0.f;
+                        float *p = C + (size_t)m * ldc + n;
+                        *p = acc ? *p + x : x;
+                    }
             __syncthreads();
         }
 }
