@@ -238,7 +238,7 @@ def mla_main(args, torch) -> int:
     return 0
 
 
-VALU_FP32_PEAK_TFS = 157.3    # MI355X fp32 vector peak, TFLOP/s
+MFMA_FP32_PEAK_TFS = 157.3    # MI355X dense fp32 matrix-core peak, TFLOP/s
 
 
 def backward_flops(cfg) -> float:
@@ -305,7 +305,7 @@ def backward_main(args, torch) -> int:
     es = 2 if cfg.dtype == "bf16" else 4
     conv_bytes = 3 * cfg.B * cfg.T * cfg.H * (2 * cfg.dk + cfg.dv) * es   # dy read twice, x read, dx written
     result = {
-        "metric": "conv+KDA backward tokens/s at 1 GPU; % of fp32 vector-ALU roofline",
+        "metric": "conv+KDA backward tokens/s at 1 GPU; % of fp32 matrix-core roofline",
         "value": round(cfg.B * cfg.T * args.steps / elapsed, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -319,8 +319,8 @@ def backward_main(args, torch) -> int:
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "H": cfg.H, "dk": cfg.dk, "dv": cfg.dv,
                    "n_text": cfg.n_text, "grid": list(cfg.grid), "chunk": 64, "parallelism": "single GPU"},
-        "roofline": {"bound": "alu", "kernel": "kda_backward", "achieved": round(tfs, 2),
-                     "peak": VALU_FP32_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / VALU_FP32_PEAK_TFS, 4),
+        "roofline": {"bound": "mfma", "kernel": "kda_backward", "achieved": round(tfs, 2),
+                     "peak": MFMA_FP32_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / MFMA_FP32_PEAK_TFS, 4),
                      "traffic": None, "flop_per_launch": fl},
         "kernels": {"kda_backward": {"us": round(kda_ms * 1e3, 1), "TFLOP/s": round(tfs, 2)},
                     "kda_conv_backward": {"us": round(conv_ms * 1e3, 1),

@@ -677,18 +677,31 @@ __global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
         stage_rows(alpha_l, al + tok(0) * DK, (size_t)H * DK, BC, DK, nr);
         // dbeta: four threads per row, each a quarter of the three row sums
         {
-            const int r = tid / 4, q = tid % 4;
+            // fixed trip counts with masked terms (indices clamped in range), so every load of
+            // a loop is issued before the first sum needs one
+            const int r = tid / 4, q = tid % 4, nv = DV / 16, nk = DK / 16;   // nv, nk: 4 or 8
             float db = 0.f;
-            for (int s2 = 16 * q; s2 < min(16 * q + 16, r); ++s2) db += dM[r * BC + s2] * c.A[r * BC + s2];
-            for (int j4 = q * DV / 16; j4 < (q + 1) * DV / 16; ++j4) {
+#pragma unroll 8
+            for (int i = 0; i < 16; ++i) {
+                const int s2 = 16 * q + i;
+                const float x = dM[r * BC + s2] * c.A[r * BC + s2];
+                db += s2 < r ? x : 0.f;
+            }
+#pragma unroll 4
+            for (int i = 0; i < 8; ++i) {
+                const int j4 = q * nv + min(i, nv - 1);
                 const float4 x = *reinterpret_cast<const float4 *>(dX + r * DV + 4 * j4);
                 const float4 w = *reinterpret_cast<const float4 *>(c.V + r * DV + 4 * j4);
-                db += x.x * w.x + x.y * w.y + x.z * w.z + x.w * w.w;
+                const float d = x.x * w.x + x.y * w.y + x.z * w.z + x.w * w.w;
+                db += i < nv ? d : 0.f;
             }
-            for (int c4 = q * DK / 16; c4 < (q + 1) * DK / 16; ++c4) {
+#pragma unroll 4
+            for (int i = 0; i < 8; ++i) {
+                const int c4 = q * nk + min(i, nk - 1);
                 const float4 x = *reinterpret_cast<const float4 *>(dY + r * DK + 4 * c4);
                 const float4 w = *reinterpret_cast<const float4 *>(c.Kt + r * DK + 4 * c4);
-                db += x.x * w.x + x.y * w.y + x.z * w.z + x.w * w.w;
+                const float d = x.x * w.x + x.y * w.y + x.z * w.z + x.w * w.w;
+                db += i < nk ? d : 0.f;
             }
             part[4 * r + q] = db;
         }
