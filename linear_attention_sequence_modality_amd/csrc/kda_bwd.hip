@@ -202,7 +202,10 @@ __device__ void stage_rows(D *dst, const T *src, size_t stride, int rows, int co
     }
 }
 
-template <typename T>
+// FULL: the whole transform.  Otherwise only what the gradient kernel needs beyond the
+// chunk's record (K, V, beta, G, Kt, Kd, X, Y): Qt, Kh, A, Bq, Tm, W, Ut and exp(gC) are
+// already there (c points at them) from the records pass.
+template <typename T, bool FULL>
 __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, int n, float (*tA)[kPs],
                               float (*tB)[kPs]) {
     const int DK = a.dk, DV = a.dv, H = a.H, tid = threadIdx.x;
@@ -211,7 +214,7 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
     const T *q = static_cast<const T *>(a.q), *k = static_cast<const T *>(a.k), *v = static_cast<const T *>(a.v);
     const T *al = static_cast<const T *>(a.alpha), *be = static_cast<const T *>(a.beta);
     float *lw = &tA[0][0];   // the panel area as scratch: 2 * kPanel * kPs floats
-    stage_rows(c.Q, q + tok0 * DK, (size_t)H * DK, BC, DK, nr);
+    if (FULL) stage_rows(c.Q, q + tok0 * DK, (size_t)H * DK, BC, DK, nr);
     stage_rows(c.K, k + tok0 * DK, (size_t)H * DK, BC, DK, nr);
     stage_rows(c.V, v + tok0 * DV, (size_t)H * DV, BC, DV, nr);
     stage_rows(lw, al + tok0 * DK, (size_t)H * DK, BC, DK, nr);   // alpha (rows past the end: 0, unused)
@@ -224,7 +227,7 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
             if (r < nr) g += logf(lw[r * DK + ch]);
             lw[r * DK + ch] = g;
         }
-        c.eC[ch] = expf(g);
+        if (FULL) c.eC[ch] = expf(g);
         lw[BC * DK + ch] = g;   // gC
     }
     __syncthreads();
@@ -238,7 +241,8 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
         const float *__restrict__ Qq = c.Q;
         for (int e4 = tid; e4 < BC * DK / 4; e4 += BT) {
             const int e = 4 * e4, ch = e % DK;
-            const float4 kk = *reinterpret_cast<const float4 *>(Kk + e), qq = *reinterpret_cast<const float4 *>(Qq + e);
+            const float4 kk = *reinterpret_cast<const float4 *>(Kk + e);
+            const float4 qq = FULL ? *reinterpret_cast<const float4 *>(Qq + e) : make_float4(0.f, 0.f, 0.f, 0.f);
             const float kv[4] = {kk.x, kk.y, kk.z, kk.w}, qv[4] = {qq.x, qq.y, qq.z, qq.w};
             float g4[4], kt[4], kd[4], qt[4], kh[4];
 #pragma unroll
@@ -253,13 +257,18 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
             *reinterpret_cast<float4 *>(Gg + e) = make_float4(g4[0], g4[1], g4[2], g4[3]);
             *reinterpret_cast<float4 *>(Kt + e) = make_float4(kt[0], kt[1], kt[2], kt[3]);
             *reinterpret_cast<float4 *>(Kd + e) = make_float4(kd[0], kd[1], kd[2], kd[3]);
-            *reinterpret_cast<float4 *>(Qt + e) = make_float4(qt[0], qt[1], qt[2], qt[3]);
-            *reinterpret_cast<float4 *>(Kh + e) = make_float4(kh[0], kh[1], kh[2], kh[3]);
+            if (FULL) {
+                *reinterpret_cast<float4 *>(Qt + e) = make_float4(qt[0], qt[1], qt[2], qt[3]);
+                *reinterpret_cast<float4 *>(Kh + e) = make_float4(kh[0], kh[1], kh[2], kh[3]);
+            }
         }
     }
     __syncthreads();
-    gemm<false, true>(c.A, BC, c.Kt, DK, c.Kd, DK, BC, BC, DK, 1.f, false, kStrictLower, tA, tB);
-    gemm<false, true>(c.Bq, BC, c.Qt, DK, c.Kd, DK, BC, BC, DK, 1.f, false, kLower, tA, tB);
+    if (FULL) {
+        gemm<false, true>(c.A, BC, c.Kt, DK, c.Kd, DK, BC, BC, DK, 1.f, false, kStrictLower, tA, tB);
+        gemm<false, true>(c.Bq, BC, c.Qt, DK, c.Kd, DK, BC, BC, DK, 1.f, false, kLower, tA, tB);
+    }
+    if (FULL)
     // Tm = (I + Diag(beta) A)^-1 (unit lower triangular) by forward substitution: lane j of
     // wave 0 owns column j in registers (the loops are unrolled), so row i needs only row i
     // of A, read from LDS as float4s that every lane shares.  Entries above the diagonal
@@ -312,8 +321,10 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
         }
     }
     __syncthreads();
-    gemm<false, false>(c.W, DK, c.Tm, BC, c.Y, DK, BC, DK, BC, 1.f, false, kNoMask, tA, tB);
-    gemm<false, false>(c.Ut, DV, c.Tm, BC, c.X, DV, BC, DV, BC, 1.f, false, kNoMask, tA, tB);
+    if (FULL) {
+        gemm<false, false>(c.W, DK, c.Tm, BC, c.Y, DK, BC, DK, BC, 1.f, false, kNoMask, tA, tB);
+        gemm<false, false>(c.Ut, DV, c.Tm, BC, c.X, DV, BC, DV, BC, 1.f, false, kNoMask, tA, tB);
+    }
 }
 
 // Scratch of one workgroup: the ChunkMats plus the backward's temporaries.
@@ -343,7 +354,7 @@ __device__ ChunkMats carve(float *s, int DK, int DV, float **rest) {
 
 // Per-chunk record written by bwd_prep and read by the two ordered passes.
 struct Rec {
-    float *Qt, *Kh, *W, *Ut, *Bq, *eC;
+    float *Qt, *Kh, *W, *Ut, *Bq, *A, *Tm, *eC;
 };
 __device__ Rec rec_at(const KdaBwdArgs &a, int bh, int n) {
     const size_t mk = (size_t)BC * a.dk, mv = (size_t)BC * a.dv;
@@ -354,6 +365,8 @@ __device__ Rec rec_at(const KdaBwdArgs &a, int bh, int n) {
     r.W = p; p += mk;
     r.Ut = p; p += mv;
     r.Bq = p; p += (size_t)BC * BC;
+    r.A = p; p += (size_t)BC * BC;
+    r.Tm = p; p += (size_t)BC * BC;
     r.eC = p;
     return r;
 }
@@ -374,8 +387,10 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(KdaBwdArgs a) {
         cr.W = r.W;
         cr.Ut = r.Ut;
         cr.Bq = r.Bq;
+        cr.A = r.A;
+        cr.Tm = r.Tm;
         cr.eC = r.eC;
-        chunk_forward<T>(a, cr, bh, n, tA, tB);   // ends with a barrier
+        chunk_forward<T, true>(a, cr, bh, n, tA, tB);   // ends with a barrier
     }
 }
 
@@ -613,9 +628,8 @@ __global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
     __shared__ __attribute__((aligned(16))) float tA[kPanel][kPs], tB[kPanel][kPs];
     const int DK = a.dk, DV = a.dv, H = a.H, tid = threadIdx.x;
     float *s;
-    const ChunkMats c = carve(a.scratch + (size_t)blockIdx.x * a.scratch_floats, DK, DV, &s);
+    const ChunkMats base = carve(a.scratch + (size_t)blockIdx.x * a.scratch_floats, DK, DV, &s);
     const size_t mk = (size_t)BC * DK, mv = (size_t)BC * DV, mc = (size_t)BC * BC;
-    float *U = c.Ut;   // U = Ut - W S, formed in place
     float *dO = s; s += mv;
     float *dU = s; s += mv;
     float *dBq = s; s += mc;
@@ -637,7 +651,20 @@ __global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
         const int bh = it / a.n_chunks, n = it % a.n_chunks, b = bh / H, h = bh % H;
         const int t0 = n * BC, nr = min(BC, a.T - t0);
         auto tok = [&](int r) { return ((size_t)b * a.T + t0 + r) * H + h; };
-        chunk_forward<T>(a, c, bh, n, tA, tB);
+        // the record's matrices (Qt, Kh, A, Bq, Tm, W, Ut, exp(gC)) plus the rest rebuilt;
+        // U = Ut - W S is formed in place of the record's Ut, which nothing reads any more
+        const Rec rc = rec_at(a, bh, n);
+        ChunkMats c = base;
+        c.Qt = rc.Qt;
+        c.Kh = rc.Kh;
+        c.W = rc.W;
+        c.Ut = rc.Ut;
+        c.Bq = rc.Bq;
+        c.A = rc.A;
+        c.Tm = rc.Tm;
+        c.eC = rc.eC;
+        float *U = c.Ut;
+        chunk_forward<T, false>(a, c, bh, n, tA, tB);
         const float *Sn = a.states + ((size_t)bh * a.n_chunks + n) * DK * DV;
         const float *dSp = a.dstates + ((size_t)bh * a.n_chunks + n) * DK * DV;
         stage_rows(dO, go + tok(0) * DV, (size_t)H * DV, BC, DV, nr);
@@ -796,7 +823,7 @@ size_t kda_bwd_scratch_floats(int dk, int dv) {
     return chunk + intra + 64;
 }
 
-size_t kda_bwd_rec_floats(int dk, int dv) { return 3 * (size_t)BC * dk + (size_t)BC * dv + (size_t)BC * BC + dk; }
+size_t kda_bwd_rec_floats(int dk, int dv) { return 3 * (size_t)BC * dk + (size_t)BC * dv + 3 * (size_t)BC * BC + dk; }
 
 hipError_t launch_kda_backward(KdaBwdArgs a, bool bf16, hipStream_t stream) {
     if (a.B * a.H == 0) return hipSuccess;
