@@ -37,6 +37,7 @@ KERNEL_SOURCES = {
     "chunks": ("kda.hip", "mfma.h", "common.h", "launch.h"),
     "scan": ("kda.hip", "mfma.h", "common.h", "launch.h"),
     "mla": ("mla.hip", "mfma.h", "common.h", "launch.h"),
+    "kda_backward": ("kda_bwd.hip", "mfma.h", "common.h", "launch.h"),
 }
 MEASURED_TRAFFIC = {
     ("video_5s_480x832", "conv"): ("d5769c400649ddb8", 253725.2, 399264.0),
@@ -321,7 +322,8 @@ def backward_main(args, torch) -> int:
                    "n_text": cfg.n_text, "grid": list(cfg.grid), "chunk": 64, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "kda_backward", "achieved": round(tfs, 2),
                      "peak": MFMA_FP32_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / MFMA_FP32_PEAK_TFS, 4),
-                     "traffic": None, "flop_per_launch": fl},
+                     "traffic": measured_traffic(cfg.name, "kda_backward"), "flop_per_launch": fl,
+                     "mfma_flop_counted": measured_mfma_flops(cfg.name, "kda_backward")},
         "kernels": {"kda_backward": {"us": round(kda_ms * 1e3, 1), "TFLOP/s": round(tfs, 2)},
                     "kda_conv_backward": {"us": round(conv_ms * 1e3, 1),
                                           "GB/s": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1),
