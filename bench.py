@@ -39,18 +39,21 @@ KERNEL_SOURCES = {
     "mla": ("mla.hip", "mfma.h", "common.h", "launch.h"),
     "kda_backward": ("kda_bwd.hip", "mfma.h", "common.h", "launch.h"),
 }
+# "kda_backward" is the sum over its three launches (records, ordered passes, gradients) per call.
 MEASURED_TRAFFIC = {
-    ("video_5s_480x832", "conv"): ("d5769c400649ddb8", 253725.2, 399264.0),
-    ("video_5s_480x832", "chunks"): ("90a46e28be760882", 270456.2, 586560.1),
-    ("video_5s_480x832", "scan"): ("90a46e28be760882", 293367.0, 133101.2),
-    ("mla_video_5s_480x832", "mla"): ("85b06fa1fb511ad3", 1537846.8, 133088.0),
+    ("video_5s_480x832", "conv"): ("a9c80efba93f3ca5", 253456.1, 399264.0),
+    ("video_5s_480x832", "chunks"): ("ce0c9745cfae1169", 270456.2, 586560.7),
+    ("video_5s_480x832", "scan"): ("ce0c9745cfae1169", 293367.0, 133100.4),
+    ("mla_video_5s_480x832", "mla"): ("fcf382f21189afaf", 1538698.3, 133088.0),
+    ("video_5s_480x832", "kda_backward"): ("2f05464cba478499", 11814683.2, 11635518.4),
 }
 # Matrix-core operations per dispatch (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
 # SQ_INSTS_VALU_MFMA_MOPS_F32, each count is 512 flops), taken the same way.
 MEASURED_MFMA_MOPS = {
-    ("video_5s_480x832", "chunks"): ("90a46e28be760882", 46858240.0, 2129920.0),
-    ("video_5s_480x832", "scan"): ("90a46e28be760882", 115015680.0, 0.0),
-    ("mla_video_5s_480x832", "mla"): ("85b06fa1fb511ad3", 22151168000.0, 0.0),
+    ("video_5s_480x832", "chunks"): ("ce0c9745cfae1169", 46858240.0, 2129920.0),
+    ("video_5s_480x832", "scan"): ("ce0c9745cfae1169", 115015680.0, 0.0),
+    ("mla_video_5s_480x832", "mla"): ("fcf382f21189afaf", 22151168000.0, 0.0),
+    ("video_5s_480x832", "kda_backward"): ("2f05464cba478499", 0.0, 613416960.0),
 }
 
 
@@ -244,8 +247,8 @@ MFMA_FP32_PEAK_TFS = 157.3    # MI355X dense fp32 matrix-core peak, TFLOP/s
 
 def backward_flops(cfg) -> float:
     """fp32 multiply-add flops of one kda_backward launch sequence: the dense products per
-    (batch, head, chunk) of the per-chunk transform (twice: once for the records, once
-    inside the gradient kernel), the two ordered passes and the gradient kernel."""
+    (batch, head, chunk) of the per-chunk transform (once, for the records the later
+    kernels read), the two ordered passes and the gradient kernel."""
     C, dk, dv = 64, cfg.dk, cfg.dv
     mm = lambda m, n, k: 2.0 * m * n * k
     fwd = mm(C, C, dk) * 2 + mm(C, dk, C) + mm(C, dv, C)                 # A, Bq, W, Ut
@@ -255,7 +258,7 @@ def backward_flops(cfg) -> float:
              + mm(C, dk, dv) * 2 + mm(C, C, dv) + mm(C, C, dk) + mm(C, C, C) * 2 + mm(C, dv, C) + mm(C, dk, C)
              + mm(C, dk, C) + mm(C, dk, C) * 2)
     n_chunks = (cfg.T + C - 1) // C
-    return cfg.B * cfg.H * n_chunks * (2 * fwd + states + reverse + grads)
+    return cfg.B * cfg.H * n_chunks * (fwd + states + reverse + grads)
 
 
 def backward_main(args, torch) -> int:
