@@ -77,6 +77,9 @@ CONV_CASES = [
     StreamConfig("cbwd_text", B=1, H=1, dk=64, dv=64, n_text=70, grid=(0, 0, 0), dtype="bf16", seed=93),
     # visual only, symmetric padding: the input gradient comes from the mirrored-tap conv alone
     StreamConfig("cbwd_vis_f32", B=2, H=1, dk=64, dv=128, n_text=0, grid=(5, 6, 9), dtype="f32", seed=94),
+    # the video workload's width (2048 channels: 8 channel blocks) and enough token ranges that
+    # each tap-gradient workgroup walks several of them
+    StreamConfig("cbwd_wide_bf16", B=1, H=16, dk=128, dv=128, n_text=40, grid=(3, 20, 50), dtype="bf16", seed=95),
 ]
 
 
