@@ -142,3 +142,67 @@ def test_conv_and_kda_backward_chain_matches_the_oracle():
     say("  chain rel errors: " + ", ".join("%s %.1e" % kv for kv in errs.items()))
     for name, e in errs.items():
         assert e <= TOL["f32"], name
+
+
+def test_backward_at_the_video_workload_is_exact_along_q_and_v():
+    """At the full 5 s 480x832 stream (B=1, T=33272, H=16, d=128, bf16), in the launch
+    configuration bench.py times: o is linear in q, and in v for fixed k, alpha and beta, so
+    L = sum(dO * o) changes by exactly <dq, dq_step> (and <dv, dv_step>) along a step in q (v).
+    Both gradients depend on every chunk of the ordered passes (dq on the states, dv on the
+    state gradients).  Steps over the whole stream, steps confined to single chunks (q: the
+    identity then holds per token and head), and a step along dv in one chunk; all within
+    bf16 output rounding."""
+    from linear_attention_sequence_modality_amd.inputs import WORKLOAD
+
+    cfg = WORKLOAD["video_5s_480x832"]
+    say("case video_5s_480x832 B=%d T=%d H=%d d=%d %s" % (cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dtype))
+    inp = {k: v.cuda() for k, v in make_inputs(cfg).items()}
+    desc = kda.make_desc(cfg.n_text, cfg.grid, causal_t=cfg.causal_t)
+    g = torch.Generator(device="cpu").manual_seed(96)
+    d_o = torch.randn(cfg.B, cfg.T, cfg.H, cfg.dv, generator=g).to(cfg.torch_dtype).cuda()
+    q, k, v, al, be = inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"]
+    grads = kda.kda_backward(desc, q, k, v, al, be, d_o)
+
+    o_base = kda.kda_forward(desc, q, k, v, al, be)
+    n_chunks = (cfg.T + 63) // 64
+
+    def stepped(x, step):
+        x2 = (x.float() + step.float()).to(x.dtype)
+        return x2, x2.double() - x.double()             # the step the bf16 inputs really take
+
+    # steps over the whole stream: dL = <dq, step> (<dv, step>)
+    for name in ("q", "v"):
+        x, dx = (q, grads["dq"]) if name == "q" else (v, grads["dv"])
+        x2, st = stepped(x, (0.5 * torch.randn(x.shape, generator=g)).to(x.dtype).cuda())
+        o2 = kda.kda_forward(desc, x2, k, v, al, be) if name == "q" else kda.kda_forward(desc, q, k, x2, al, be)
+        lhs = (d_o.double() * (o2.double() - o_base.double())).sum().item()
+        rhs = (dx.double() * st).sum().item()
+        e = abs(lhs - rhs) / abs(rhs)
+        say("  %s step on all chunks: dL %.6e, <d%s, step> %.6e, rel err %.2e" % (name, lhs, name, rhs, e))
+        assert e <= TOL[cfg.dtype]
+    # q steps confined to single chunks (first, middle, last): o_t moves by S_t^T step_t, so the
+    # identity holds per token and head, <dO_t, o2_t - o_t> = <dq_t, step_t>, compared as vectors
+    for chunk in (0, n_chunks // 2, n_chunks - 1):
+        t0, t1 = 64 * chunk, min(cfg.T, 64 * chunk + 64)
+        step = torch.zeros_like(q)
+        step[:, t0:t1] = (0.5 * torch.randn(step[:, t0:t1].shape, generator=g)).to(q.dtype).cuda()
+        x2, st = stepped(q, step)
+        o2 = kda.kda_forward(desc, x2, k, v, al, be)
+        lhs = (d_o[:, t0:t1].double() * (o2[:, t0:t1].double() - o_base[:, t0:t1].double())).sum(-1)
+        rhs = (grads["dq"][:, t0:t1].double() * st[:, t0:t1]).sum(-1)
+        e = ((lhs - rhs).norm() / rhs.norm()).item()
+        say("  q step on chunk %d: per token-head rel err %.2e over %d pairs" % (chunk, e, rhs.numel()))
+        assert e <= TOL[cfg.dtype]
+    # v step confined to the middle chunk, along dv there: dL = <dv, step> > 0 without cancellation
+    chunk = n_chunks // 2
+    t0, t1 = 64 * chunk, 64 * chunk + 64
+    dvc = grads["dv"][:, t0:t1].float()
+    step = torch.zeros_like(v)
+    step[:, t0:t1] = (0.5 * dvc / dvc.abs().max()).to(v.dtype)
+    x2, st = stepped(v, step)
+    o2 = kda.kda_forward(desc, q, k, x2, al, be)
+    lhs = (d_o[:, t0:].double() * (o2[:, t0:].double() - o_base[:, t0:].double())).sum().item()
+    rhs = (grads["dv"].double() * st).sum().item()
+    e = abs(lhs - rhs) / abs(rhs)
+    say("  v step along dv on chunk %d: dL %.6e, <dv, step> %.6e, rel err %.2e" % (chunk, lhs, rhs, e))
+    assert e <= TOL[cfg.dtype]
