@@ -504,6 +504,10 @@ __device__ __forceinline__ int xcd_grouped_block() {
     return n % 8 ? i : (i % 8) * (n / 8) + i / 8;
 }
 
+// The ordered passes share data between their threads through LDS only, so their barriers
+// wait for LDS traffic alone (lds_barrier): the next chunk's register prefetch, issued a
+// matrix at a time between the products, and the per-chunk state stores stay in flight.
+//
 // State at the start of every chunk: S_{n+1} = Diag(eC) S_n + Kh^T (Ut - W S_n), per SW value
 // columns.  The state and the chunk's operands live in LDS; the next chunk's W and Kh are
 // loaded into registers while the current one is computed.
@@ -523,25 +527,25 @@ __device__ void states_pass(const KdaBwdArgs &a, int L, float *lds) {
         pu.load(r.Ut + j0, DV, BC, r.eC, DK);
     }
     for (int n = 0; n < a.n_chunks; ++n) {
-        __syncthreads();                       // the previous step is done with the LDS operands
+        lds_barrier();                         // the previous step is done with the LDS operands
         pw.store_t(Wt, BC * DK, DK, BC + 1);   // W^T, [DK][BC + 1]
         pk.store(Khl, BC * DK);
         pu.store(Utl, eCl, DK);
         float *Sn = a.states + ((size_t)bh * a.n_chunks + n) * DK * DV;
         for (int e = threadIdx.x; e < DK * SW; e += BT) Sn[(size_t)(e / SW) * DV + j0 + e % SW] = S[e];
-        __syncthreads();
-        if (n + 1 < a.n_chunks) {
-            const Rec r1 = rec_at(a, bh, n + 1);
-            pw.load(r1.W, BC * DK);
-            pk.load(r1.Kh, BC * DK);
-            pu.load(r1.Ut + j0, DV, BC, r1.eC, DK);
-        }
+        lds_barrier();
+        // the next chunk's operands, each ahead of the product after which it is stored (the
+        // last step reads its own chunk again, unused)
+        const Rec r1 = rec_at(a, bh, min(n + 1, a.n_chunks - 1));
+        pw.load(r1.W, BC * DK);
+        pu.load(r1.Ut + j0, DV, BC, r1.eC, DK);
         for (int e = threadIdx.x; e < BC * SW; e += BT) U[e] = Utl[e];
-        __syncthreads();
+        lds_barrier();
         lds_mm(U, SW, Wt, BC + 1, S, SW, BC, DK, -1.f, true);            // U = Ut - W S
-        __syncthreads();
+        lds_barrier();
+        pk.load(r1.Kh, BC * DK);
         for (int e = threadIdx.x; e < DK * SW; e += BT) S[e] *= eCl[e / SW];
-        __syncthreads();
+        lds_barrier();
         lds_mm(S, SW, Khl, DK, U, SW, DK, BC, 1.f, true);                // S += Kh^T U
     }
 }
@@ -572,7 +576,7 @@ __device__ void reverse_pass(const KdaBwdArgs &a, int L, float *lds) {
         po.load(go_bh + n * chunk_rows, (size_t)H * DV, min(BC, a.T - n * BC), r.eC, DK);
     }
     for (int n = a.n_chunks - 1; n >= 0; --n) {
-        __syncthreads();
+        lds_barrier();
         pb.store(Bql, BC * BC);
         pk.store_t(Kht, BC * DK, DK, BC + 1);  // Kh^T, [DK][BC + 1]
         pq.store(Qtl, BC * DK);
@@ -580,24 +584,26 @@ __device__ void reverse_pass(const KdaBwdArgs &a, int L, float *lds) {
         po.store(dO, eCl, DK);
         float *dSp = a.dstates + ((size_t)bh * a.n_chunks + n) * DK * DV;
         for (int e = threadIdx.x; e < DK * SW; e += BT) dSp[(size_t)(e / SW) * DV + j0 + e % SW] = dS[e];
-        __syncthreads();
-        if (n > 0) {
-            const Rec r1 = rec_at(a, bh, n - 1);
-            pb.load(r1.Bq, BC * BC);
-            pk.load(r1.Kh, BC * DK);
-            pq.load(r1.Qt, BC * DK);
-            pw.load(r1.W, BC * DK);
-            po.load(go_bh + (n - 1) * chunk_rows, (size_t)H * DV, BC, r1.eC, DK);
-        }
+        lds_barrier();
+        // the next chunk's operands, one matrix ahead of each product so that the loads go
+        // through the memory pipeline under the products (at n = 0 chunk 0 is read again,
+        // unused); the barriers between the products wait for LDS only, leaving them in flight
+        const int np = max(n - 1, 0);
+        const Rec r1 = rec_at(a, bh, np);
+        pb.load(r1.Bq, BC * BC);
+        po.load(go_bh + np * chunk_rows, (size_t)H * DV, min(BC, a.T - np * BC), r1.eC, DK);
         lds_mm(dU, SW, Bql, BC, dO, SW, BC, BC, 1.f, false);            // dU = Bq^T dO
-        __syncthreads();
+        lds_barrier();
+        pk.load(r1.Kh, BC * DK);
         lds_mm(dU, SW, Kht, BC + 1, dS, SW, BC, DK, 1.f, true);         //    + Kh dS'
         for (int e = threadIdx.x; e < DK * SW; e += BT) dSn[e] = eCl[e / SW] * dS[e];
-        __syncthreads();
+        lds_barrier();
+        pq.load(r1.Qt, BC * DK);
         lds_mm(dSn, SW, Qtl, DK, dO, SW, DK, BC, 1.f, true);            // + Qt^T dO
-        __syncthreads();
+        lds_barrier();
+        pw.load(r1.W, BC * DK);
         lds_mm(dSn, SW, Wl, DK, dU, SW, DK, BC, -1.f, true);            // - W^T dU
-        __syncthreads();
+        lds_barrier();
         for (int e = threadIdx.x; e < DK * SW; e += BT) dS[e] = dSn[e];
     }
     __syncthreads();
