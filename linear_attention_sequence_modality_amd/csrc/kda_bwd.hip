@@ -203,8 +203,8 @@ __device__ void stage_rows(D *dst, const T *src, size_t stride, int rows, int co
 }
 
 // FULL: the whole transform.  Otherwise only what the gradient kernel needs beyond the
-// chunk's record (K, V, beta, G, Kt, Kd, X, Y): Qt, Kh, A, Bq, Tm, W, Ut and exp(gC) are
-// already there (c points at them) from the records pass.
+// chunk's record (K, V, beta, G, Kt, Kd): Qt, Kh, A, Bq, Tm, W, Ut and exp(gC) are already
+// there (c points at them) from the records pass.
 template <typename T, bool FULL>
 __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, int n, float (*tA)[kPs],
                               float (*tB)[kPs]) {
@@ -304,7 +304,7 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
         for (int e4 = tid; e4 < BC * BC / 4; e4 += BT)
             *reinterpret_cast<float4 *>(c.Tm + 4 * e4) = *reinterpret_cast<const float4 *>(Tl + 4 * e4);
     }
-    {
+    if (FULL) {   // the gradient kernel folds beta into its products instead
         float *__restrict__ X = c.X;
         float *__restrict__ Y = c.Y;
         const float *__restrict__ V = c.V;
@@ -683,9 +683,13 @@ __global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
         gemm<false, false>(dQt, DK, dBq, BC, c.Kd, DK, BC, DK, BC, 1.f, true, kNoMask, tA, tB);     //     + dBq Kd
         gemm<false, true>(dKh, DK, U, DV, dSp, DV, BC, DK, DV, 1.f, false, kNoMask, tA, tB);        // dKh = U dS'^T
         gemm<false, true>(dW, DK, dU, DV, Sn, DV, BC, DK, DV, -1.f, false, kNoMask, tA, tB);        // dW = -dU S^T
-        gemm<false, true>(dTm, BC, dU, DV, c.X, DV, BC, BC, DV, 1.f, false, kNoMask, tA, tB);       // dTm = dU X^T
-        gemm<false, true>(dTm, BC, dW, DK, c.Y, DK, BC, BC, DK, 1.f, true, kNoMask, tA, tB);        //     + dW Y^T
-        gemm<true, false>(P, BC, c.Tm, BC, dTm, BC, BC, BC, BC, 1.f, false, kNoMask, tA, tB);       // Tm^T dTm
+        // dTm = dU X^T + dW Y^T = (dU V^T + dW Kt^T) Diag(beta), and Tm^T dTm takes the same column
+        // scaling: the products run on V and Kt, and beta scales the columns of Tm^T dTm
+        gemm<false, true>(dTm, BC, dU, DV, c.V, DV, BC, BC, DV, 1.f, false, kNoMask, tA, tB);       // dU V^T
+        gemm<false, true>(dTm, BC, dW, DK, c.Kt, DK, BC, BC, DK, 1.f, true, kNoMask, tA, tB);       //  + dW Kt^T
+        gemm<true, false>(P, BC, c.Tm, BC, dTm, BC, BC, BC, BC, 1.f, false, kNoMask, tA, tB);       // Tm^T (...)
+        for (int e = tid; e < BC * BC; e += BT) P[e] *= c.beta[e % BC];                             //  Diag(beta)
+        __syncthreads();
         gemm<false, true>(dM, BC, P, BC, c.Tm, BC, BC, BC, BC, -1.f, false, kNoMask, tA, tB);       // dM
         gemm<true, false>(dX, DV, c.Tm, BC, dU, DV, BC, DV, BC, 1.f, false, kNoMask, tA, tB);       // dX = Tm^T dU
         gemm<true, false>(dY, DK, c.Tm, BC, dW, DK, BC, DK, BC, 1.f, false, kNoMask, tA, tB);       // dY = Tm^T dW
