@@ -214,8 +214,6 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
     const T *q = static_cast<const T *>(a.q), *k = static_cast<const T *>(a.k), *v = static_cast<const T *>(a.v);
     const T *al = static_cast<const T *>(a.alpha), *be = static_cast<const T *>(a.beta);
     float *lw = &tA[0][0];   // the panel area as scratch: 2 * kPanel * kPs floats
-    if (FULL) stage_rows(c.Q, q + tok0 * DK, (size_t)H * DK, BC, DK, nr);
-    stage_rows(c.K, k + tok0 * DK, (size_t)H * DK, BC, DK, nr);
     stage_rows(c.V, v + tok0 * DV, (size_t)H * DV, BC, DV, nr);
     stage_rows(lw, al + tok0 * DK, (size_t)H * DK, BC, DK, nr);   // alpha (rows past the end: 0, unused)
     if (tid < BC) c.beta[tid] = tid < nr ? ld(be + tok0 + (size_t)tid * H) : 0.f;
@@ -237,13 +235,20 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
         float *__restrict__ Kd = c.Kd;
         float *__restrict__ Qt = c.Qt;
         float *__restrict__ Kh = c.Kh;
-        const float *__restrict__ Kk = c.K;
-        const float *__restrict__ Qq = c.Q;
+        // q and k straight from the inputs (rows past the end read the first row, used as zeros)
+        const T *__restrict__ kin = k + tok0 * DK;
+        const T *__restrict__ qin = q + tok0 * DK;
         for (int e4 = tid; e4 < BC * DK / 4; e4 += BT) {
-            const int e = 4 * e4, ch = e % DK;
-            const float4 kk = *reinterpret_cast<const float4 *>(Kk + e);
-            const float4 qq = FULL ? *reinterpret_cast<const float4 *>(Qq + e) : make_float4(0.f, 0.f, 0.f, 0.f);
-            const float kv[4] = {kk.x, kk.y, kk.z, kk.w}, qv[4] = {qq.x, qq.y, qq.z, qq.w};
+            const int e = 4 * e4, ch = e % DK, r = e / DK;
+            const size_t src = (size_t)(r < nr ? r : 0) * H * DK + ch;
+            float kv[4], qv[4] = {0.f, 0.f, 0.f, 0.f};
+            ld4(kin + src, kv);
+            if (FULL) ld4(qin + src, qv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kv[i] = r < nr ? kv[i] : 0.f;
+                qv[i] = r < nr ? qv[i] : 0.f;
+            }
             float g4[4], kt[4], kd[4], qt[4], kh[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
