@@ -45,7 +45,7 @@ MEASURED_TRAFFIC = {
     ("video_5s_480x832", "chunks"): ("ce0c9745cfae1169", 270456.2, 586560.7),
     ("video_5s_480x832", "scan"): ("ce0c9745cfae1169", 293367.0, 133100.4),
     ("mla_video_5s_480x832", "mla"): ("fcf382f21189afaf", 1538698.3, 133088.0),
-    ("video_5s_480x832", "kda_backward"): ("cdceb1ea8beb5213", 11119862.9, 10420261.1),
+    ("video_5s_480x832", "kda_backward"): ("b0f36027eacb2097", 11119862.9, 10420261.1),
 }
 # Matrix-core operations per dispatch (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
 # SQ_INSTS_VALU_MFMA_MOPS_F32, each count is 512 flops), taken the same way.
@@ -53,7 +53,7 @@ MEASURED_MFMA_MOPS = {
     ("video_5s_480x832", "chunks"): ("ce0c9745cfae1169", 46858240.0, 2129920.0),
     ("video_5s_480x832", "scan"): ("ce0c9745cfae1169", 115015680.0, 0.0),
     ("mla_video_5s_480x832", "mla"): ("fcf382f21189afaf", 22151168000.0, 0.0),
-    ("video_5s_480x832", "kda_backward"): ("cdceb1ea8beb5213", 0.0, 613416960.0),
+    ("video_5s_480x832", "kda_backward"): ("b0f36027eacb2097", 0.0, 613416960.0),
 }
 
 

@@ -18,7 +18,7 @@
 //   dlog alpha = reverse cumulative sum of dG over the chunk, dalpha = dlog alpha / alpha.
 //
 // Three launches, all fp32 inside:
-//   1. bwd_prep:    per (batch, head, chunk), in parallel: Qt, Kh, W, Ut, Bq, exp(gC).
+//   1. bwd_prep:    per (batch, head, chunk), in parallel: Qt, Kh, A, Bq, Tm, W, Ut, exp(gC).
 //   2. bwd_ordered: two independent passes side by side, per (batch, head, 16 value
 //                   columns): in chunk order the state at the start of every chunk,
 //                   and in reverse chunk order dS' of every chunk and the gradient of
