@@ -144,6 +144,11 @@ def kda_forward_workspace_size(desc: KdaStreamDesc, B: int, H: int, dk: int, dv:
     return int(load_library().kda_forward_workspace_size(ctypes.byref(desc), B, H, dk, dv, code))
 
 
+def supports(dtype, dk: int, dv: int) -> bool:
+    """Whether the library runs KDA for this dtype and head size (its workspace query is nonzero)."""
+    return kda_forward_workspace_size(make_desc(1, (0, 0, 0)), 1, 1, dk, dv, dtype) > 0
+
+
 def kda_conv_forward(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      w_text: Sequence[torch.Tensor], w_vis: Sequence[torch.Tensor],
                      q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,

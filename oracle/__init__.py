@@ -141,3 +141,22 @@ def rel_err_state(x, ref) -> float:
     diff = np.abs(x - ref).max(axis=(2, 3))
     den = np.abs(ref).max(axis=(2, 3))
     return float(np.max(diff / np.maximum(den, 1e-300)))
+
+
+def rel_err_elementwise(x, ref, floor: float = 1e-6, layout: str = "tokens") -> float:
+    """Secondary, element-wise relative error (reported beside ``rel_err``, not gated).
+
+    max over elements of |x - ref| / max(|ref|, floor * M), where M is the
+    max |ref| of the element's (b, h) slice: [B, T, H, d] (layout "tokens")
+    or [B, H, dk, dv] (layout "state").  The floor keeps elements whose
+    reference is (close to) zero from dominating.
+    """
+    x, ref = _f64(x), _f64(ref)
+    if layout == "tokens":
+        m = np.abs(ref).max(axis=(1, 3), keepdims=True)
+    elif layout == "state":
+        m = np.abs(ref).max(axis=(2, 3), keepdims=True)
+    else:
+        raise ValueError("layout must be 'tokens' or 'state'")
+    den = np.maximum(np.abs(ref), np.maximum(floor * m, 1e-300))
+    return float(np.max(np.abs(x - ref) / den))

@@ -70,3 +70,37 @@ def oracle_end_to_end_heads(cfg, inp_cpu: dict, heads, S0=None):
 
 def rel(x: np.ndarray, ref: np.ndarray) -> float:
     return oracle.rel_err(x, ref)
+
+
+def rel_elem(x: np.ndarray, ref: np.ndarray, layout: str = "tokens") -> float:
+    """Element-wise relative error (floor 1e-6 of each (b, h)'s max |ref|): reported, not gated."""
+    return oracle.rel_err_elementwise(x, ref, layout=layout)
+
+
+def check_stream(cfg: StreamConfig, inp: dict, heads=None, S0=None, want_state=False):
+    """Conv + KDA on the GPU against the oracle on the chosen heads (all by default).
+
+    Gates the per-(b, h) max relative error of q', k', v', o (and S_T) at the
+    dtype's tolerance; prints the element-wise error of o and S_T beside it.
+    """
+    say("case %s B=%d T=%d H=%d dk=%d dv=%d %s causal_t=%d heads=%s" % (
+        cfg.name, cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv, cfg.dtype, cfg.causal_t, heads))
+    dev = to_dev(inp)
+    qc, kc, vc, o, sT = run_path(cfg, dev, S0=S0, want_state=want_state)
+    heads = tuple(range(cfg.H)) if heads is None else heads
+    rq, rk, rv, ro, rs = oracle_end_to_end_heads(cfg, inp, heads, S0)
+    tol = TOL[cfg.dtype]
+    oh = heads_slice(o, heads)
+    errs = {"q'": rel(heads_slice(qc, heads), rq), "k'": rel(heads_slice(kc, heads), rk),
+            "v'": rel(heads_slice(vc, heads), rv), "o": rel(oh, ro)}
+    extra = {"o elementwise": rel_elem(oh, ro)}
+    if want_state:
+        sh = sT[:, list(heads)].double().cpu().numpy()
+        errs["S_T"] = oracle.rel_err_state(sh, rs)
+        extra["S_T elementwise"] = rel_elem(sh, rs, layout="state")
+    say("  rel errors: " + ", ".join("%s %.2e" % kv for kv in errs.items()) +
+        "  [" + ", ".join("%s %.2e" % kv for kv in extra.items()) + "]")
+    assert np.isfinite(oh).all(), "non-finite o"
+    for name, e in errs.items():
+        assert e <= tol, "%s rel err %.3e > %.1e" % (name, e, tol)
+    return errs
