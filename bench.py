@@ -34,8 +34,8 @@ FETCH_SCALE = 1048576.0 / 524302.0
 WRITE_SCALE = 1.0
 KERNEL_SOURCES = {
     "conv": ("conv.hip", "common.h", "launch.h"),
-    "chunks": ("kda.hip", "mfma.h", "common.h", "launch.h"),
-    "scan": ("kda.hip", "mfma.h", "common.h", "launch.h"),
+    "chunks": ("kda.hip", "kda_ws.h", "mfma.h", "common.h", "launch.h"),
+    "scan": ("kda_scan.hip", "kda_ws.h", "mfma.h", "common.h", "launch.h"),
     "mla": ("mla.hip", "mfma.h", "common.h", "launch.h"),
     "kda_backward": ("kda_bwd.hip", "mfma.h", "common.h", "launch.h"),
 }
@@ -146,8 +146,9 @@ def copy_bandwidth(torch, mib: int = 1024, reps: int = 5) -> float:
     return gbs
 
 
-def cpu_baseline(cfg, frames: int) -> dict:
-    """The fp64 oracle, as it stands, on a prefix of the same stream (text + first frames)."""
+def cpu_baseline(cfg, frames: int, single_tokens: int) -> dict:
+    """The fp64 oracle, as it stands, on a prefix of the same stream (text + first frames), on
+    all the threads OpenMP gives it, and on one thread over a shorter prefix."""
     import oracle
     from linear_attention_sequence_modality_amd.inputs import make_inputs
 
@@ -155,15 +156,31 @@ def cpu_baseline(cfg, frames: int) -> dict:
     frames = gt if frames <= 0 else min(frames, gt)
     sample = cfg.with_(name=cfg.name + "_prefix", grid=(frames, gh, gw))
     inp = make_inputs(sample)
+    threads = oracle.num_threads()
     t0 = time.perf_counter()
     oracle.conv_kda_forward(inp, sample.n_text, sample.grid)
     dt = time.perf_counter() - t0
-    return {"value": sample.B * sample.T / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+    # one thread: the text tokens and as many whole latent frames as fit single_tokens
+    f1 = min(frames, max(1, (single_tokens - cfg.n_text) // max(1, gh * gw))) if gt else 0
+    one = cfg.with_(name=cfg.name + "_prefix1", grid=(f1, gh, gw) if gt else cfg.grid)
+    inp1 = make_inputs(one)
+    oracle.set_num_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.conv_kda_forward(inp1, one.n_text, one.grid)
+        dt1 = time.perf_counter() - t1
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": sample.B * sample.T / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "nproc": os.cpu_count(),
+            "single_thread": {"value": one.B * one.T / dt1, "unit": "tokens/s", "cores": 1,
+                              "sample": "B=%d, T=%d (%d text + %dx%dx%d), H=%d; %.1f s wall" % (
+                                  one.B, one.T, one.n_text, *one.grid, one.H, dt1)},
             "sample": "fp64 C oracle (conv + sequential KDA recurrence, OpenMP over heads) on the "
                       "first %d of %d latent frames of the same stream: B=%d, T=%d (%d text + %dx%dx%d), "
-                      "H=%d, dk=dv=%d; %.1f s wall" % (sample.grid[0], gt, sample.B, sample.T,
-                                                      sample.n_text, *sample.grid, sample.H, sample.dk, dt)}
+                      "H=%d, dk=dv=%d; %.1f s wall on %d threads (host nproc %s)" % (
+                          sample.grid[0], gt, sample.B, sample.T, sample.n_text, *sample.grid, sample.H,
+                          sample.dk, dt, threads, os.cpu_count())}
 
 
 def mla_flops(cfg) -> float:
@@ -367,6 +384,8 @@ def main() -> int:
     ap.add_argument("--workload", default="video_5s_480x832")
     ap.add_argument("--cpu-frames", type=int, default=0,
                     help="latent frames in the CPU-baseline sample (0 = the whole stream)")
+    ap.add_argument("--cpu-single-tokens", type=int, default=4096,
+                    help="tokens per stream in the one-thread CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (three times) and "
@@ -508,7 +527,7 @@ def main() -> int:
                  "frac_of_path_roofline": round(path_gbs / HBM_PEAK_GBS, 4)},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_frames)
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_frames, args.cpu_single_tokens)
     print(json.dumps(result), flush=True)
     return 0
 

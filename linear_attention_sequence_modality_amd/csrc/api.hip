@@ -47,7 +47,9 @@ int check_shape(const kda_stream_desc *d, int B, int H, int dk, int dv, int dtyp
     // conv addresses one batch's slice of a stream with 32-bit byte offsets
     const int64_t d_max = dk > dv ? dk : dv;
     if ((int64_t)B * T * H * d_max / 2 >= kMaxTokens) return KDA_ERR_UNSUPPORTED;
-    if (T * H * d_max * (dtype == KDA_F32 ? 4 : 2) >= ((int64_t)1 << 32)) return KDA_ERR_UNSUPPORTED;
+    // (plus one chunk: the state pass forms the offsets of a ragged chunk's rows past the end)
+    if ((T + kdaconv::kChunk) * H * d_max * (dtype == KDA_F32 ? 4 : 2) >= ((int64_t)1 << 32))
+        return KDA_ERR_UNSUPPORTED;
     *T_out = T;
     return KDA_OK;
 }
@@ -207,13 +209,61 @@ int varlen_seqs(const kda_stream_desc *descs, int n_seq, int H, int dk, int dv, 
     return KDA_OK;
 }
 
-// Workspace bytes of a call, or 0 when the configuration is unsupported.
+// Segments of the state pass: each sequence's chunks are cut into runs of
+// about total chunk-heads / kSegTarget chunks (at most kMaxSegs runs per
+// sequence), so that the replay has about one workgroup per compute unit.
+struct SegPlan {
+    int n_seg_u = 1, seg_len_u = 1;   // uniform batch
+    int seg0[kdaconv::kMaxSeqs + 1] = {}, seg_len[kdaconv::kMaxSeqs] = {};
+    int64_t total = 0;                // segments over all sequences
+};
+
+void plan_segment(int64_t n_chunks, int64_t target_len, int *n_seg, int *seg_len) {
+    int64_t p = (n_chunks + target_len - 1) / target_len;
+    if (p > kdaconv::kMaxSegs) p = kdaconv::kMaxSegs;
+    if (p < 1) p = 1;
+    const int64_t len = (n_chunks + p - 1) / p;
+    *seg_len = (int)len;
+    *n_seg = kdaconv::segs_of((int)n_chunks, (int)len);
+}
+
+SegPlan plan_segments(const Seqs &sq, int H) {
+    SegPlan sp;
+    const int64_t work = sq.chunks * H;
+    const int64_t target_len = work > kdaconv::kSegTarget ? (work + kdaconv::kSegTarget - 1) / kdaconv::kSegTarget : 1;
+    if (!sq.varlen) {
+        plan_segment(sq.max_chunks, target_len, &sp.n_seg_u, &sp.seg_len_u);
+        sp.total = (int64_t)sq.n * sp.n_seg_u;
+        return sp;
+    }
+    int64_t g = 0;
+    for (int i = 0; i < sq.n; ++i) {
+        int n_seg = 1;
+        plan_segment(sq.chk0[i + 1] - sq.chk0[i], target_len, &n_seg, &sp.seg_len[i]);
+        sp.seg0[i] = (int)g;
+        g += n_seg;
+    }
+    sp.seg0[sq.n] = (int)g;
+    sp.total = g;
+    return sp;
+}
+
+// Byte offset of the segment records (after the chunk records), and the
+// workspace bytes of a call, or 0 when the configuration is unsupported.
+size_t chunk_records_bytes(const Seqs &sq, int H, int dk, int dv, kda_dtype dtype) {
+    const size_t per = kdaconv::kda_chunk_ws_bytes(dk, dv, dtype == KDA_BF16);
+    return (per * (size_t)H * (size_t)sq.chunks + 255) / 256 * 256;
+}
+
 size_t workspace_bytes_of(const Seqs &sq, int H, int dk, int dv, kda_dtype dtype) {
     if (dtype == KDA_F32 && (dk != 64 || dv != 64)) return 0;
     const size_t per = kdaconv::kda_chunk_ws_bytes(dk, dv, dtype == KDA_BF16);
     // the state pass addresses one (sequence, head)'s chunks with 32-bit offsets
     if ((int64_t)per * sq.max_chunks >= ((int64_t)1 << 32)) return 0;
-    return per * (size_t)H * (size_t)sq.chunks;
+    const SegPlan sp = plan_segments(sq, H);
+    size_t bytes = chunk_records_bytes(sq, H, dk, dv, dtype);
+    if (sp.total > sq.n) bytes += (size_t)sp.total * H * kdaconv::seg_record_bytes(dk, dv);
+    return bytes;
 }
 
 }  // namespace
@@ -322,6 +372,12 @@ int prepare_kda(const Seqs &sq, int H, int dk, int dv, kda_dtype dtype, const vo
         out->tok0[i] = sq.tok0[i];
         out->chk0[i] = sq.chk0[i];
     }
+    const SegPlan sp = plan_segments(sq, H);
+    out->n_seg_u = sp.n_seg_u;
+    out->seg_len_u = sp.seg_len_u;
+    for (int i = 0; i <= kdaconv::kMaxSeqs; ++i) out->seg0[i] = sp.seg0[i];
+    for (int i = 0; i < kdaconv::kMaxSeqs; ++i) out->seg_len[i] = sp.seg_len[i];
+    out->seg_base = chunk_records_bytes(sq, H, dk, dv, dtype);
     return KDA_OK;
 }
 

@@ -30,9 +30,7 @@
 //   sub-block (R, S <= R):  A_RS = Kr_R Diag(2^(G_m(R) - G_m(S))) Kb_S^T  (same for Bq with Qr).
 // Every factor is <= 1 except inside one sub-block, where it spans at most 8
 // tokens; off-diagonal factors never overflow.
-#include "common.h"
-#include "launch.h"
-#include "mfma.h"
+#include "kda_ws.h"
 
 namespace kdaconv {
 namespace {
@@ -40,72 +38,6 @@ namespace {
 constexpr int C = kChunk;          // 64 tokens per chunk
 constexpr int K1_THREADS = 512;    // 8 waves
 
-constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-
-// ---- workspace layout (per batch, head, chunk; element type T) ---------------
-// Fragment order: kernel-2 lane l loads 16 contiguous bytes per fragment.
-// dk-indexed fragments (W, Qt) hold, in slots 0..3 and 4..7, the channels
-// 32ks + 4g + i and 32ks + 16 + 4g + i (g = l/16), matching the rows kernel 2
-// holds of its state tiles 2ks and 2ks+1; token-indexed fragments (BT, Kh^T)
-// are ordered likewise over tokens.
-template <typename T, int DK, int DV>
-struct Ws {
-    static constexpr size_t W = 0;                 // [4 R][DK/32][64][8]  W rows of block R
-    static constexpr size_t QT = W + 64 * DK;      // [4 R][DK/32][64][8]  Qt
-    static constexpr size_t KH = QT + 64 * DK;     // [DK/16][2][64][8]    Kh^T (dk rows x tokens, k order as BT)
-    static constexpr size_t BT = KH + 64 * DK;     // [4 R][2][64][8]      Bq rows of block R
-    static constexpr size_t U = BT + 64 * 64;      // [DV/16][64][4 R][4]  Ut, accumulator order
-    static constexpr size_t ELEMS = U + 64 * DV;
-    static constexpr size_t GAM_BYTE = round_up(ELEMS * sizeof(T), 16);   // fp32 [DK], gam_pos order
-    static constexpr size_t BYTES = round_up(GAM_BYTE + DK * sizeof(float), 256);
-};
-
-// Position of key channel c = 16 dt + 4 g + i in the stored chunk decay: the
-// 4 DK/16 values a kernel-2 lane group g needs are contiguous, 2 per lane.
-template <int DK> __device__ __forceinline__ int gam_pos(int c) {
-    return ((c >> 2) & 3) * (DK / 4) + 4 * (c >> 4) + (c & 3);
-}
-
-// ---- raw 8-element rows (register prefetch without conversion) --------------
-template <typename T> struct Raw8;
-template <> struct Raw8<bf16_t> {
-    uint4 u;
-    __device__ __forceinline__ void load(const bf16_t *p) { u = *reinterpret_cast<const uint4 *>(p); }
-    __device__ __forceinline__ void zero() { u = make_uint4(0u, 0u, 0u, 0u); }
-    __device__ __forceinline__ void get(float (&x)[8]) const {
-        x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
-        x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z); x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
-    }
-};
-template <> struct Raw8<float> {
-    float4 a, b;
-    __device__ __forceinline__ void load(const float *p) {
-        a = *reinterpret_cast<const float4 *>(p);
-        b = *reinterpret_cast<const float4 *>(p + 4);
-    }
-    __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
-    __device__ __forceinline__ void get(float (&x)[8]) const {
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    }
-};
-template <typename T> struct Raw4;
-template <> struct Raw4<bf16_t> {
-    uint2 u;
-    __device__ __forceinline__ void load(const bf16_t *p) { u = *reinterpret_cast<const uint2 *>(p); }
-    __device__ __forceinline__ float get(int i) const {
-        const uint32_t w = i < 2 ? u.x : u.y;
-        return (i & 1) ? bf16_hi(w) : bf16_lo(w);
-    }
-};
-template <> struct Raw4<float> {
-    float4 a;
-    __device__ __forceinline__ void load(const float *p) { a = *reinterpret_cast<const float4 *>(p); }
-    __device__ __forceinline__ float get(int i) const { return i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : a.w; }
-};
 
 // ---- kernel 1 shared-memory plan --------------------------------------------------
 template <typename T, int DK, int DV>
@@ -588,488 +520,6 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     }
 }
 
-// ---- kernel 2: sequential state pass ------------------------------------------------
-// One 7-wave workgroup per (batch, head, 16 value columns):
-//   wave 0 (recurrence): S <- Diag(Gam) S + Kh^T (Ut - W S), chunk after chunk;
-//   waves 1, 2, 3, 5 (output): O^T = S^T Qt^T + U^T Bq^T from the S and U wave 0
-//                        used, chunk n on output wave n mod 4;
-//   wave 4 (store):      writes O to o;
-//   wave 6 (loader):     stages W, Kh^T, Ut and Gam of the coming chunks in LDS.
-// Lane l = 16 g + col of wave 0 holds rows 16 dt + 4 g + i (i = 0..3) of
-// value column col of S in fp32: S is kept as DK/16 accumulator tiles.  Two
-// tiles side by side are directly an MFMA operand whose 32 k-slots are the
-// rows 32 ks + {4g+i, 16+4g+i} -- the B operand of W S (k = key channel) and,
-// unchanged, the A operand of S^T Qt^T -- so the state never leaves wave 0's
-// registers; U becomes an operand the same way (k = token).  The workspace
-// fragments are stored in the matching k order.
-// Wave 0 hands the bf16 operands of S and U to the output waves, and they the
-// output tiles to the store wave, through small LDS rings guarded by counters: a wave waits
-// only when its ring is empty (consumer) or full (producer).  Keeping loads
-// and stores in different waves lets every wave keep its loads in flight
-// across chunk steps: a wave with both outstanding would drain everything at
-// each wait.  Each wave streams its operands through registers one chunk ahead.
-
-// Lane N of the calling lane's row of 16 (DPP row_newbcast).
-template <int N> __device__ __forceinline__ float row_bcast(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xf, 0xf, false));
-}
-// Run-time lane index; folds to one DPP operand once n is a constant after unrolling.
-__device__ __forceinline__ float row_bcast(float x, int n) {
-    switch (n) {
-    case 0: return row_bcast<0>(x);
-    case 1: return row_bcast<1>(x);
-    case 2: return row_bcast<2>(x);
-    case 3: return row_bcast<3>(x);
-    case 4: return row_bcast<4>(x);
-    case 5: return row_bcast<5>(x);
-    case 6: return row_bcast<6>(x);
-    case 7: return row_bcast<7>(x);
-    case 8: return row_bcast<8>(x);
-    case 9: return row_bcast<9>(x);
-    case 10: return row_bcast<10>(x);
-    case 11: return row_bcast<11>(x);
-    case 12: return row_bcast<12>(x);
-    case 13: return row_bcast<13>(x);
-    case 14: return row_bcast<14>(x);
-    default: return row_bcast<15>(x);
-    }
-}
-
-template <typename T> __device__ __forceinline__ Frag<T> tiles_to_frag(const f32x4_t &lo, const f32x4_t &hi);
-template <> __device__ __forceinline__ Frag<bf16_t> tiles_to_frag<bf16_t>(const f32x4_t &lo, const f32x4_t &hi) {
-    const uint4 u = make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
-                               pack_bf16x2(hi[2], hi[3]));
-    Frag<bf16_t> f;
-    f.v = __builtin_bit_cast(bf16x8_t, u);
-    return f;
-}
-template <> __device__ __forceinline__ Frag<float> tiles_to_frag<float>(const f32x4_t &lo, const f32x4_t &hi) {
-    Frag<float> f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f.v[i] = lo[i];
-        f.v[4 + i] = hi[i];
-    }
-    return f;
-}
-
-// Raw buffer loads: a lane-dependent offset plus a wave-uniform one.
-template <typename T> struct BufLd;
-template <> struct BufLd<bf16_t> {
-    __device__ __forceinline__ static Frag<bf16_t> frag(__amdgpu_buffer_rsrc_t r, unsigned v, unsigned s) {
-        Frag<bf16_t> f;
-        f.v = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, v, s, 0));
-        return f;
-    }
-    __device__ __forceinline__ static void raw8(Raw8<bf16_t> &x, __amdgpu_buffer_rsrc_t r, unsigned v, unsigned s) {
-        x.u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, v, s, 0));
-    }
-};
-template <> struct BufLd<float> {
-    __device__ __forceinline__ static Frag<float> frag(__amdgpu_buffer_rsrc_t r, unsigned v, unsigned s) {
-        const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, v, s, 0);
-        const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, v, s + 16, 0);
-        Frag<float> f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f.v[i] = __uint_as_float(a[i]);
-            f.v[4 + i] = __uint_as_float(b[i]);
-        }
-        return f;
-    }
-    __device__ __forceinline__ static void raw8(Raw8<float> &x, __amdgpu_buffer_rsrc_t r, unsigned v, unsigned s) {
-        x.a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, v, s, 0));
-        x.b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, v, s + 16, 0));
-    }
-};
-
-// An empty asm that reads and rewrites x: the value is computed before this
-// point, so the compiler cannot sink the computation towards a later use.
-__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(f32x4_t &x) { asm volatile("" : "+v"(x)); }
-
-// Wait until an LDS counter reaches target.  Bounded: a kernel-wide poll
-// budget (far above what a correct run uses) guarantees that every wave exits
-// even if its partner never signals.
-__device__ __forceinline__ void wait_counter(int *ctr, int target, int &budget) {
-    while (budget > 0 && __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
-        --budget;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-// Publish a counter after this wave's earlier LDS writes have completed.
-__device__ __forceinline__ void signal_counter(int *ctr, int value) {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0) only
-    __hip_atomic_store(ctr, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// LDS counter access for a wave that has direct-to-LDS loads in flight.  The
-// compiler makes every LDS access of such a wave wait for all of those loads;
-// these two touch only the counter, so they are written out (the read waits
-// for its own result inside the same block) and the wave keeps its loads in
-// flight.  The caller orders them against its loads with explicit waits.
-typedef __attribute__((address_space(3))) int lds_int_t;
-__device__ __forceinline__ int lds_counter_read(int *ctr) {
-    int v;
-    const unsigned off = (unsigned)(uintptr_t)(lds_int_t *)ctr;
-    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(off) : "memory");
-    return v;
-}
-__device__ __forceinline__ void lds_counter_write(int *ctr, int value) {
-    const unsigned off = (unsigned)(uintptr_t)(lds_int_t *)ctr;
-    asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(off), "v"(value) : "memory");
-}
-// Bounded wait on an LDS counter (see wait_counter) through lds_counter_read.
-__device__ __forceinline__ void wait_counter_dma(int *ctr, int target, int &budget) {
-    while (budget > 0 && lds_counter_read(ctr) < target) {
-        --budget;
-        __builtin_amdgcn_s_sleep(1);
-    }
-}
-
-// Wave roles of the state pass.  Waves w and w + 4 of a workgroup run on
-// the same SIMD, so the store wave (little work) is wave 4, beside the
-// recurrence (wave 0); the output waves are 1 and 2, the loaders 3, 5, 6, 7.
-constexpr int kOutWaves = 2;          // output waves; chunk n goes to output wave n % kOutWaves
-constexpr int kLoaders = 4;           // loader waves; chunk p goes to loader p % kLoaders
-constexpr int kStoreWave = 4;
-__device__ __forceinline__ int loader_slot(int wave) {   // loader index, or -1
-    return wave == 3 ? 0 : wave >= 5 ? wave - 4 : -1;
-}
-__device__ __forceinline__ int out_slot(int wave) {   // output wave index, or -1
-    return wave == 1 || wave == 2 ? wave - 1 : -1;
-}
-constexpr int kRing = 4;              // chunk steps buffered between recurrence, output, store
-static_assert(kRing % kOutWaves == 0, "each ring slot belongs to one output wave");
-constexpr int kOpRing = 3;            // chunks of recurrence operands staged in LDS
-constexpr int kPollBudget = 1 << 24;  // LDS polls per wave per launch
-constexpr int kScanThreads = 512;     // recurrence, two output waves, four loaders, store
-
-// s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding: vmcnt split over
-// bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima).
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xf00; }
-
-template <typename T, int DK, int DV>
-struct ScanLds {
-    static constexpr int ES = sizeof(T);
-    // one staged chunk of recurrence operands: exact copies of the workspace
-    // ranges W, Kh^T, this workgroup's Ut slice and Gam
-    static constexpr int W_B = 64 * DK * ES;
-    static constexpr int K_B = 64 * DK * ES;
-    static constexpr int U_B = 64 * 16 * ES;
-    static constexpr int G_B = DK * 4;
-    static constexpr int OPB = W_B + K_B + U_B + G_B;
-    static constexpr int NI = (W_B + 1023) / 1024 + (K_B + 1023) / 1024 + (U_B + 1023) / 1024 + (G_B + 1023) / 1024;
-    static_assert(NI < 64, "one staged chunk must fit the vector memory counter");
-};
-
-template <typename T, int DK, int DV>
-__global__ __launch_bounds__(kScanThreads) void kda_state_kernel(KdaArgs a) {
-    using WL = Ws<T, DK, DV>;
-    using SL = ScanLds<T, DK, DV>;
-    using F = Frag<T>;
-    using B = BufLd<T>;
-    constexpr int NJT = DV / 16;     // workgroups per head: one 16-column value slab each
-    constexpr int NKS = DK / 32;     // contraction steps over dk
-    constexpr int NDT = DK / 16;     // 16-row state tiles
-    constexpr unsigned ES = sizeof(T);
-    __shared__ __attribute__((aligned(1024))) char op_ring[kOpRing][SL::OPB];
-    // per lane: S operands (NKS fragments) then U operands (2 fragments)
-    __shared__ F su_ring[kRing][NKS + 2][64];
-    __shared__ f32x4_t o_ring[kRing][4][64];
-    // counters, each "chunks done" (n + 1 after chunk n):
-    //   kSuProd  S/U operands written (recurrence)
-    //   kSuCons  + parity: S/U slot read (output wave of that parity)
-    //   kOProd   + parity: O tile written (output wave of that parity)
-    //   kOCons   O tile read (store)
-    //   kOpProd  + loader: chunks staged by that loader, kOpCons operands read (recurrence)
-    constexpr int kSuProd = 0, kSuCons = 1, kOProd = kSuCons + kOutWaves, kOCons = kOProd + kOutWaves,
-                  kOpProd = kOCons + 1, kOpCons = kOpProd + kLoaders, kNumCtr = kOpCons + 1;
-    __shared__ int ctr[kNumCtr];
-    if (threadIdx.x < kNumCtr) ctr[threadIdx.x] = 0;
-    __syncthreads();
-
-    const int blk = xcd_remap(blockIdx.x, gridDim.x);
-    const int jt = blk % NJT, bh = blk / NJT;
-    const int sq = bh / a.H, h = bh % a.H;   // sequence, head
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int l = threadIdx.x & 63, col = l & 15, g = l >> 4;
-    // this sequence's chunks [c0, c0 + nchunks) and tokens [tok0, tok0 + ntok)
-    const int c0 = seq_chk0(a, sq), nchunks = seq_chk0(a, sq + 1) - c0, last = nchunks - 1;
-    const int tok0 = seq_tok0(a, sq), ntok = seq_tok0(a, sq + 1) - tok0;
-    int budget = kPollBudget;
-
-    // this (batch, head)'s workspace: chunk n at byte n * BYTES (< 4 GiB, checked on the host)
-    const char *wsh = static_cast<const char *>(a.ws) + ((size_t)h * seq_chk0(a, a.B) + c0) * WL::BYTES;
-    const __amdgpu_buffer_rsrc_t wsr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(wsh), 0, (int)(unsigned)((size_t)nchunks * WL::BYTES), kBufWord3);
-    const unsigned lane8 = (unsigned)l * 8 * ES;   // lane's fragment inside a [64][8] block
-    auto cbase = [&](int i) { return (unsigned)i * (unsigned)WL::BYTES; };
-
-    if (loader_slot(wave) >= 0) {
-        // ---------------- loaders: recurrence operands -> LDS ----------------
-        // Loader q takes chunks p = q, q + kLoaders, ...: it loads the chunk's
-        // W, Kh^T, Ut slice and Gam into its registers (16 bytes per lane,
-        // 1 KB per instruction), waits until the chunk's ring slot is free,
-        // copies the registers into the slot and signals, then loads its next
-        // chunk.  With kLoaders waves each holding a chunk in flight, the loads
-        // of chunk p are issued about kLoaders + kOpRing - 1 chunk steps before
-        // the recurrence reads it, which covers the memory latency.
-        const int q = loader_slot(wave);
-        u32x4_t r[SL::NI];
-        int nload = 0;   // chunks this loader has staged
-        auto load = [&](int p) {
-            const unsigned c = cbase(p);
-            int k = 0;
-            auto seg = [&](unsigned src, int bytes) {
-#pragma unroll
-                for (int i = 0; i < (bytes + 1023) / 1024; ++i, ++k)
-                    r[k] = __builtin_amdgcn_raw_buffer_load_b128(wsr, src + (unsigned)(i * 1024 + l * 16), c, 0);
-            };
-            seg((unsigned)(WL::W * ES), SL::W_B);
-            seg((unsigned)(WL::KH * ES), SL::K_B);
-            seg((unsigned)((WL::U + (size_t)jt * 64 * 16) * ES), SL::U_B);
-            seg((unsigned)WL::GAM_BYTE, SL::G_B);
-        };
-        auto stage = [&](int p) {
-            char *slot = op_ring[p % kOpRing];
-            int k = 0;
-            auto seg = [&](int off, int bytes) {
-#pragma unroll
-                for (int i = 0; i < (bytes + 1023) / 1024; ++i, ++k)
-                    if (i * 1024 + l * 16 < bytes)
-                        *reinterpret_cast<u32x4_t *>(slot + off + i * 1024 + l * 16) = r[k];
-            };
-            seg(0, SL::W_B);
-            seg(SL::W_B, SL::K_B);
-            seg(SL::W_B + SL::K_B, SL::U_B);
-            seg(SL::W_B + SL::K_B + SL::U_B, SL::G_B);
-        };
-#pragma unroll 1
-        for (int p = q; p < nchunks; p += kLoaders) {
-            load(p);
-            if (p >= kOpRing) wait_counter(&ctr[kOpCons], p - kOpRing + 1, budget);   // slot's last chunk read
-            stage(p);
-            signal_counter(&ctr[kOpProd + q], ++nload);
-        }
-    } else if (wave == 0) {
-        // ---------------- recurrence ----------------
-        f32x4_t S[NDT];
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) S[dt] = zero4();
-        if (a.s0) {
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    S[dt][i] = a.s0[((size_t)bh * DK + 16 * dt + 4 * g + i) * DV + 16 * jt + col];
-        }
-        // Operands of one chunk in registers, refilled from the LDS ring phase
-        // by phase as soon as the current chunk has issued its last use: W after
-        // the U products, Kh^T, Ut and Gam after the state update.  Every LDS
-        // poll and signal waits for all of this wave's LDS operations, so they
-        // come before the refills in each step.
-        F Wf[4][NKS], Kf[NDT][2];
-        Raw8<T> ut[2];   // Ut rows 16R + 4g + i of column col: element 4R + i
-        float2 gam;      // decay of channels 16 dt + 4g + i for dt = col/2, i = 2(col%2) + {0, 1}
-        auto read_w = [&](int n) {
-            const char *op = op_ring[n % kOpRing];
-#pragma unroll
-            for (int R = 0; R < 4; ++R)
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    Wf[R][ks] = *reinterpret_cast<const F *>(op + (R * NKS + ks) * 64 * 8 * ES + lane8);
-        };
-        auto read_k = [&](int n) {
-            const char *op = op_ring[n % kOpRing];
-            ut[0] = *reinterpret_cast<const Raw8<T> *>(op + SL::W_B + SL::K_B + l * 16 * ES);
-            ut[1] = *reinterpret_cast<const Raw8<T> *>(op + SL::W_B + SL::K_B + l * 16 * ES + 8 * ES);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-                    Kf[dt][kt] = *reinterpret_cast<const F *>(op + SL::W_B + (dt * 2 + kt) * 64 * 8 * ES + lane8);
-            gam = *reinterpret_cast<const float2 *>(op + SL::W_B + SL::K_B + SL::U_B +
-                                                    4 * (g * (DK / 4) + 2 * min(col, DK / 8 - 1)));
-        };
-        // chunk n is staged once loader n % kLoaders has staged n / kLoaders + 1 chunks
-        auto wait_staged = [&](int n) { wait_counter(&ctr[kOpProd + n % kLoaders], n / kLoaders + 1, budget); };
-        wait_staged(0);
-        read_w(0);
-        read_k(0);
-#pragma unroll 1
-        for (int n = 0; n < nchunks; ++n) {
-            // Critical chain of a step: pack S -> U MFMAs -> U = Ut - W S, pack
-            // -> state MFMAs.  The decay of S, the ring traffic and the operand
-            // refills sit in the shadow of the MFMAs.
-            F Sb[NKS];
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) Sb[ks] = tiles_to_frag<T>(S[2 * ks], S[2 * ks + 1]);
-            // U = Ut - W S  (token rows 16R + 4g + i, value column col)
-            f32x4_t U[4];
-#pragma unroll
-            for (int R = 0; R < 4; ++R) U[R] = zero4();
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-                for (int R = 0; R < 4; ++R) U[R] = mma(Wf[R][ks], Sb[ks], U[R]);
-            // S <- Diag(Gam) S; the decay of (dt, i) sits in lane 2dt + i/2 of the row
-            const float2 gm = gam;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[dt][i] *= row_bcast(i & 1 ? gm.y : gm.x, 2 * dt + (i >> 1));
-                pin(S[dt]);   // keeps the decay here, under the MFMAs, rather than next to its use
-            }
-            float x[2][8];
-#pragma unroll
-            for (int R = 0; R < 2; ++R) {
-                ut[R].get(x[R]);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pin(x[R][i]);
-            }
-            // su slot n % kRing is free once chunk n-kRing has been read by the
-            // output wave of its parity (kRing is even)
-            if (n >= kRing) wait_counter(&ctr[kSuCons + n % kOutWaves], n + 1 - kRing, budget);
-            F(&slot)[NKS + 2][64] = su_ring[n % kRing];
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) slot[ks][l] = Sb[ks];
-#pragma unroll
-            for (int R = 0; R < 2; ++R)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    U[2 * R][i] = x[R][i] - U[2 * R][i];
-                    U[2 * R + 1][i] = x[R][4 + i] - U[2 * R + 1][i];
-                }
-            const F Ub[2] = {tiles_to_frag<T>(U[0], U[1]), tiles_to_frag<T>(U[2], U[3])};
-            // S <- S + Kh^T U
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) S[dt] = mma(Kf[dt][kt], Ub[kt], S[dt]);
-            slot[NKS][l] = Ub[0];
-            slot[NKS + 1][l] = Ub[1];
-            signal_counter(&ctr[kSuProd], n + 1);
-            // chunk n's operands are all in registers: its ring slot may be restaged
-            signal_counter(&ctr[kOpCons], n + 1);
-            if (n + 1 < nchunks) {
-                wait_staged(n + 1);
-                read_w(n + 1);
-                read_k(n + 1);
-            }
-        }
-        if (a.sT) {
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a.sT[((size_t)bh * DK + 16 * dt + 4 * g + i) * DV + 16 * jt + col] = S[dt][i];
-        }
-    } else if (out_slot(wave) >= 0) {
-        // ---------------- output: O^T = S^T Qt^T + U^T Bq^T ----------------
-        // The output waves take chunks in turn.  Each holds the Qt and Bq
-        // operands of its next two chunks in two register sets, so their loads
-        // go out 2 * kOutWaves chunk steps before use.
-        const int par = out_slot(wave);
-        F Qa[4][NKS], Ba[6], Qb[4][NKS], Bb[6];
-        auto load_qb = [&](int n, F (&Qf)[4][NKS], F (&Bf)[6]) {
-            const unsigned c = cbase(n);
-#pragma unroll
-            for (int R = 0; R < 4; ++R)
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    Qf[R][ks] = B::frag(wsr, lane8, c + (unsigned)(WL::QT + (R * NKS + ks) * 512) * ES);
-            // Bq: k-step 0 of every token block, k-step 1 of blocks 2 and 3
-#pragma unroll
-            for (int R = 0; R < 4; ++R) Bf[R] = B::frag(wsr, lane8, c + (unsigned)(WL::BT + (R * 2) * 512) * ES);
-            Bf[4] = B::frag(wsr, lane8, c + (unsigned)(WL::BT + 5 * 512) * ES);
-            Bf[5] = B::frag(wsr, lane8, c + (unsigned)(WL::BT + 7 * 512) * ES);
-        };
-        // one chunk with the operand set (Qf, Bf), which is then reloaded with
-        // chunk n + 2 * kOutWaves (clamped: the load count per chunk stays fixed)
-        auto chunk = [&](int n, F (&Qf)[4][NKS], F (&Bf)[6]) {
-            const bool live = n < nchunks;
-            f32x4_t O[4];
-            if (live) {
-                wait_counter(&ctr[kSuProd], n + 1, budget);
-                F(&slot)[NKS + 2][64] = su_ring[n % kRing];
-                F Sb[NKS], Ub[2];
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) Sb[ks] = slot[ks][l];
-                Ub[0] = slot[NKS][l];
-                Ub[1] = slot[NKS + 1][l];
-#pragma unroll
-                for (int R = 0; R < 4; ++R) O[R] = zero4();
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-                    for (int R = 0; R < 4; ++R) O[R] = mma(Sb[ks], Qf[R][ks], O[R]);
-                // causal inside the chunk: token block R sees token k-steps kt <= R/2
-#pragma unroll
-                for (int R = 0; R < 4; ++R) O[R] = mma(Ub[0], Bf[R], O[R]);
-                O[2] = mma(Ub[1], Bf[4], O[2]);
-                O[3] = mma(Ub[1], Bf[5], O[3]);
-                signal_counter(&ctr[kSuCons + par], n + 1);   // slot reads are complete (the MFMAs consumed them)
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            load_qb(min(n + 2 * kOutWaves, last), Qf, Bf);
-            __builtin_amdgcn_sched_barrier(0);
-            if (live) {
-                if (n >= kRing) wait_counter(&ctr[kOCons], n + 1 - kRing, budget);
-#pragma unroll
-                for (int R = 0; R < 4; ++R) o_ring[n % kRing][R][l] = O[R];
-                signal_counter(&ctr[kOProd + par], n + 1);
-            }
-        };
-        load_qb(min(par, last), Qa, Ba);
-        __builtin_amdgcn_sched_barrier(0);
-        load_qb(min(par + kOutWaves, last), Qb, Bb);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll 1
-        for (int n = par; n < nchunks; n += 2 * kOutWaves) {
-            chunk(n, Qa, Ba);
-            chunk(n + kOutWaves, Qb, Bb);
-        }
-    } else if (wave == kStoreWave) {
-        // ---------------- store ----------------
-        // o of this (batch, head, 16 value columns) as a raw buffer: token t at
-        // byte t*H*DV*es.  Rows past the end of the stream fall outside the range
-        // and the hardware drops their stores.  The output tile is transposed
-        // (lane: 4 consecutive value columns of one token).
-        const unsigned orow = (unsigned)a.H * DV * ES;
-        char *obase = static_cast<char *>(a.o) + (((size_t)tok0 * a.H + h) * DV + 16 * jt) * ES;
-        const unsigned onum = (unsigned)ntok * orow - (unsigned)(h * DV + 16 * jt) * ES;
-        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(obase, 0, (int)onum, kBufWord3);
-        const unsigned ovoff = (unsigned)col * orow + (unsigned)(4 * g) * ES;
-#pragma unroll 1
-        for (int n = 0; n < nchunks; ++n) {
-            wait_counter(&ctr[kOProd + n % kOutWaves], n + 1, budget);
-            f32x4_t O[4];
-#pragma unroll
-            for (int R = 0; R < 4; ++R) O[R] = o_ring[n % kRing][R][l];
-            signal_counter(&ctr[kOCons], n + 1);
-#pragma unroll
-            for (int R = 0; R < 4; ++R) {
-                const unsigned soff = ((unsigned)n * C + 16u * R) * orow;
-                if (sizeof(T) == 2) {
-                    u32x2_t v;
-                    v[0] = pack_bf16x2(O[R][0], O[R][1]);
-                    v[1] = pack_bf16x2(O[R][2], O[R][3]);
-                    __builtin_amdgcn_raw_buffer_store_b64(v, orsrc, ovoff, soff, 0);
-                } else {
-                    u32x4_t v;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(O[R][i]);
-                    __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, ovoff, soff, 0);
-                }
-            }
-        }
-    }
-}
-
 template <typename T, int DK, int DV>
 hipError_t launch_chunks_typed(const KdaArgs &a, hipStream_t stream) {
     using SM = K1Smem<T, DK, DV>;
@@ -1086,24 +536,7 @@ hipError_t launch_chunks_typed(const KdaArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename T, int DK, int DV>
-hipError_t launch_scan_typed(const KdaArgs &a, hipStream_t stream) {
-    const int n2 = a.B * a.H * (DV / 16);
-    hipLaunchKernelGGL((kda_state_kernel<T, DK, DV>), dim3(n2), dim3(kScanThreads), 0, stream, a);
-    return hipGetLastError();
-}
 
-#define KDA_DISPATCH(FN)                                                                           \
-    if (a.B == 0 || seq_chk0(a, a.B) == 0) return hipSuccess;                                      \
-    if (bf16) {                                                                                    \
-        if (a.dk == 64 && a.dv == 64) return FN<bf16_t, 64, 64>(a, stream);                        \
-        if (a.dk == 64 && a.dv == 128) return FN<bf16_t, 64, 128>(a, stream);                      \
-        if (a.dk == 128 && a.dv == 64) return FN<bf16_t, 128, 64>(a, stream);                      \
-        if (a.dk == 128 && a.dv == 128) return FN<bf16_t, 128, 128>(a, stream);                    \
-    } else {                                                                                       \
-        if (a.dk == 64 && a.dv == 64) return FN<float, 64, 64>(a, stream);                         \
-    }                                                                                              \
-    return hipErrorInvalidValue;
 
 }  // namespace
 
@@ -1134,10 +567,6 @@ size_t kda_chunk_ws_bytes(int dk, int dv, bool bf16) {
 
 hipError_t launch_kda_chunks(const KdaArgs &a, bool bf16, hipStream_t stream) {
     KDA_DISPATCH(launch_chunks_typed)
-}
-
-hipError_t launch_kda_scan(const KdaArgs &a, bool bf16, hipStream_t stream) {
-    KDA_DISPATCH(launch_scan_typed)
 }
 
 }  // namespace kdaconv

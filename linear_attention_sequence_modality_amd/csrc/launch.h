@@ -44,6 +44,13 @@ constexpr int kMaxSeqs = 64;  // sequences of one variable-length batch
 // Each sequence is split into chunks of kChunk tokens (its last one ragged);
 // the workspace holds chunk g of head h at index h * total chunks + g, where
 // sequence i owns chunks [chk0[i], chk0[i+1]).
+//
+// The state pass cuts each sequence's chunks into segments of consecutive
+// chunks (sequence i: seg_len(i) chunks each, the last one shorter), which
+// are summarised, chained and replayed in parallel.  The segment records sit
+// after the chunk records in the workspace, at byte seg_base: one per
+// (head, segment) at index h * total segments + segment, each holding the
+// segment's state map (L, Phi) and its start state.
 struct KdaArgs {
     const void *q, *k, *v, *alpha, *beta;
     const float *s0;     // [B, H, dk, dv] or null
@@ -54,10 +61,36 @@ struct KdaArgs {
     int n_chunks;        // uniform batch: ceil(T / kChunk)
     int varlen;          // nonzero: the tables below give the sequences
     int tok0[kMaxSeqs + 1], chk0[kMaxSeqs + 1];
+    // segments: uniform batch n_seg_u per sequence of seg_len_u chunks; a
+    // variable-length batch uses the tables
+    int n_seg_u, seg_len_u;
+    int seg0[kMaxSeqs + 1], seg_len[kMaxSeqs];
+    size_t seg_base;     // byte offset of the segment records in ws
 };
 // First token and first chunk of sequence i (i = B: the totals).
 __host__ __device__ inline int seq_tok0(const KdaArgs &a, int i) { return a.varlen ? a.tok0[i] : i * a.T; }
 __host__ __device__ inline int seq_chk0(const KdaArgs &a, int i) { return a.varlen ? a.chk0[i] : i * a.n_chunks; }
+// First segment of sequence i (i = B: the total), and its segments' length in chunks.
+__host__ __device__ inline int seq_seg0(const KdaArgs &a, int i) { return a.varlen ? a.seg0[i] : i * a.n_seg_u; }
+__host__ __device__ inline int seq_seg_len(const KdaArgs &a, int i) { return a.varlen ? a.seg_len[i] : a.seg_len_u; }
+// Sequence that owns segment g (0 <= g < total segments).
+__device__ inline int seq_of_segment(const KdaArgs &a, int g) {
+    if (!a.varlen) return g / a.n_seg_u;
+    int lo = 0, hi = a.B;   // seg0[lo] <= g < seg0[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.seg0[mid] <= g) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+// Segment plan: chunks per segment aim at kSegTarget (head, segment) pairs in
+// all, at most kMaxSegs segments per sequence (the chain over them is serial).
+constexpr int kSegTarget = 256;
+constexpr int kMaxSegs = 32;
+__host__ __device__ inline int segs_of(int n_chunks, int seg_len) { return (n_chunks + seg_len - 1) / seg_len; }
+// Bytes of one segment record: L [dk, dv], Phi [dk, dk], start state [dk, dv], fp32.
+__host__ __device__ inline size_t seg_record_bytes(int dk, int dv) { return ((size_t)2 * dk * dv + (size_t)dk * dk) * 4; }
 // Sequence that owns chunk g (0 <= g < total chunks).
 __device__ inline int seq_of_chunk(const KdaArgs &a, int g) {
     if (!a.varlen) return g / a.n_chunks;
@@ -72,7 +105,9 @@ __device__ inline int seq_of_chunk(const KdaArgs &a, int g) {
 
 // Workspace bytes for one (batch, head, chunk).
 size_t kda_chunk_ws_bytes(int dk, int dv, bool bf16);
-// Kernel 1 (chunk transform -> workspace) and kernel 2 (ordered state pass).
+// The chunk transform (chunk records into the workspace) and the state pass
+// over them (segment summaries, the chain of segment start states, and the
+// replay of every segment writing o and the final state).
 hipError_t launch_kda_chunks(const KdaArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_kda_scan(const KdaArgs &a, bool bf16, hipStream_t stream);
 // Compute units of the current device.

@@ -32,6 +32,8 @@ def _load():
     lib = ctypes.CDLL(_build.LIB)
     dp = ctypes.POINTER(ctypes.c_double)
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     lib.oracle_short_conv.restype = ctypes.c_int
     lib.oracle_short_conv.argtypes = [ctypes.c_int] * 9 + [dp] * 4
     lib.oracle_kda_recurrence.restype = ctypes.c_int
@@ -54,6 +56,11 @@ def _ptr(a: Optional[np.ndarray]):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """OpenMP threads of the following oracle calls; returns the count in effect."""
+    return int(_load().oracle_set_num_threads(int(n)))
 
 
 def short_conv(x, w_text, w_vis, n_text: int, grid, causal_t: int = 0,

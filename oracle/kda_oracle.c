@@ -39,6 +39,19 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads for the following calls (n >= 1); returns the count now in effect. */
+int oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 /*
  * Depthwise modality-aware short convolution of one projected stream.
  *   x, y    : [B, T, channels], T = n_text + grid_t*grid_h*grid_w

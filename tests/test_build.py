@@ -44,5 +44,6 @@ def test_kernels_keep_their_occupancy(resources):
 
 def test_every_kernel_family_is_built(resources):
     names = " ".join(resources)
-    for part in ("conv_kernel", "kda_intra_kernel", "kda_state_kernel", "mla_attention_kernel"):
+    for part in ("conv_kernel", "kda_intra_kernel", "kda_segsum_kernel", "kda_chain_kernel", "kda_segout_kernel",
+                 "mla_attention_kernel"):
         assert part in names, part
