@@ -14,7 +14,7 @@
 // Each sequence's chunks are cut into segments of consecutive chunks, and the
 // ordered pass becomes three launches:
 //   kda_segsum_kernel  every segment but a sequence's last, all in parallel:
-//                      one workgroup forms L, another Phi (the "summaries");
+//                      one workgroup forms both L and Phi (the "summaries");
 //   kda_chain_kernel   per (sequence, head, 16 state columns), in segment
 //                      order: S_start(p + 1) = Phi_p S_start(p) + L_p, in fp32;
 //   kda_segout_kernel  every segment in parallel, one workgroup per (segment,
@@ -47,11 +47,14 @@ namespace {
 constexpr int kLdsMax = 160 * 1024;   // LDS per workgroup on gfx950
 // Launch bounds of the widest instantiations (a bound that depends on the
 // template arguments keeps the host pass from emitting the kernel's stub).
-constexpr int kSegsumMaxThreads = 64 * (128 / 16 + 1);
+constexpr int kSegsumMaxThreads = 64 * (256 / 32 + 1);
 constexpr int kSegoutMaxThreads = 64 * (128 / 16 + 2);
 
 // s_waitcnt vmcnt(0) alone (expcnt and lgkmcnt at their maxima).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding: vmcnt split over
+// bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xf00; }
 
 // ---- segment records --------------------------------------------------------
 // One per (head, segment): L [DK][DV], Phi [DK][DK], S_start [DK][DV], fp32 row-major.
@@ -139,21 +142,30 @@ __device__ __forceinline__ Frag<T> slot_frag(const char *slot, size_t elem, int 
 }
 
 // ============================================================================
-// kda_segsum_kernel: a segment's state map.  Workgroup (segment g, head h,
-// half): half 0 forms L (the segment from S = 0, with Ut), half 1 forms Phi
-// (the segment from S = I, without Ut).  A sequence's last segment needs no
-// summary; its workgroups return at once.
+// kda_segsum_kernel: a segment's state map.  Workgroup (segment g, head h):
+// the state [L | Phi] of DV + DK columns starts at [0 | I] and runs through
+// the segment's chunks, L with the Ut terms and Phi without.  Compute wave w
+// owns 32 columns (two 16-column slabs): L's columns first, then Phi's.  The
+// loader wave copies each chunk's W, Kh^T, Ut and decay into an LDS slot,
+// NSLOT - 1 chunks ahead.  A sequence's last segment needs no summary; its
+// workgroups return at once.
 // ============================================================================
 template <typename T, int DK, int DV>
 struct SegsumPlan {
     static constexpr int ES = sizeof(T);
-    static constexpr int NCW = (DK > DV ? DK : DV) / 16;   // compute waves, then the loader
-    static constexpr int THREADS = 64 * (NCW + 1);
-    static constexpr int W_B = 64 * DK * ES;                // W, then Kh^T
-    static constexpr int OP_B = 2 * W_B;
-    static constexpr int NOP = OP_B / 1024;
-    static constexpr int LDS_B = 2 * OP_B;
-    static_assert(W_B % 1024 == 0 && LDS_B <= kLdsMax, "segment summary LDS plan");
+    static constexpr int NLW = DV / 32, NCW = (DV + DK) / 32;   // L waves, all compute waves
+    static constexpr int THREADS = 64 * (NCW + 1);             // plus the loader
+    static constexpr int W_B = 64 * DK * ES;                    // W, then Kh^T
+    static constexpr int UG_SRC = (int)(Ws<T, DK, DV>::U * ES);  // Ut, then the decay (GAM_BYTE)
+    static constexpr int UG_B = (int)round_up((size_t)64 * DV * ES + DK * 4, 1024);
+    static constexpr int GAM_OFF = 2 * W_B + (int)(Ws<T, DK, DV>::GAM_BYTE - Ws<T, DK, DV>::U * ES);
+    static constexpr int SLOT = 2 * W_B + UG_B;
+    static constexpr int NOP = SLOT / 1024;
+    // as many slots as fit, at most three: the loader runs NSLOT - 1 chunks ahead
+    static constexpr int NSLOT = 3 * SLOT <= kLdsMax ? 3 : 2 * SLOT <= kLdsMax ? 2 : 1;
+    static constexpr int LDS_B = NSLOT * SLOT;
+    static_assert(W_B % 1024 == 0 && UG_SRC % 1024 == 0 && LDS_B <= kLdsMax, "segment summary LDS plan");
+    static_assert(NOP <= 63, "one chunk's copies must fit the vector memory counter");
     static_assert(THREADS <= kSegsumMaxThreads, "launch bound");
 };
 
@@ -162,12 +174,11 @@ __global__ __launch_bounds__(kSegsumMaxThreads) void kda_segsum_kernel(KdaArgs a
     using P = SegsumPlan<T, DK, DV>;
     using WL = Ws<T, DK, DV>;
     using F = Frag<T>;
-    constexpr int NKS = DK / 32, NDT = DK / 16;
+    constexpr int NKS = DK / 32, NDT = DK / 16, NSLOT = P::NSLOT;
     extern __shared__ __attribute__((aligned(1024))) char lds[];
 
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
-    const int half = blk & 1, gh = blk >> 1;
-    const int g = gh / a.H, h = gh % a.H;
+    const int g = blk / a.H, h = blk % a.H;
     const int sq = seq_of_segment(a, g);
     const int p = g - seq_seg0(a, sq);
     if (g + 1 == seq_seg0(a, sq + 1)) return;   // the last segment of its sequence
@@ -176,88 +187,125 @@ __global__ __launch_bounds__(kSegsumMaxThreads) void kda_segsum_kernel(KdaArgs a
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = threadIdx.x & 63, col = l & 15, gq = l >> 4;
-    const int width = half ? DK : DV;
-    const bool active = wave < width / 16;
-    const int jt = wave;
     const __amdgpu_buffer_rsrc_t wsr = seq_records<T, DK, DV>(a, sq, h);
     auto cbase = [&](int n) { return (unsigned)(n0 + n) * (unsigned)WL::BYTES; };
 
     if (wave == P::NCW) {
-        // loader: chunk n's W and Kh^T into slot n % 2, one chunk ahead
+        // ---- loader: chunk n's W, Kh^T, Ut and decay into slot n % NSLOT ----
         auto issue_ops = [&](int n) {
-            char *slot = lds + (n & 1) * P::OP_B;
+            char *slot = lds + (n % NSLOT) * P::SLOT;
 #pragma unroll
             for (int k = 0; k < P::NOP; ++k) {
-                const int src = k < P::W_B / 1024 ? (int)(WL::W * P::ES) + k * 1024
-                                                   : (int)(WL::KH * P::ES) + (k - P::W_B / 1024) * 1024;
+                const int src = k < P::W_B / 1024       ? (int)(WL::W * P::ES) + k * 1024
+                                : k < 2 * P::W_B / 1024 ? (int)(WL::KH * P::ES) + (k - P::W_B / 1024) * 1024
+                                                        : P::UG_SRC + (k - 2 * P::W_B / 1024) * 1024;
                 dma_1k(wsr, slot + k * 1024, (unsigned)src, cbase(n), l);
             }
         };
-        issue_ops(0);
+        if (NSLOT == 1) {
+            issue_ops(0);
+            wait_vm_all();
+            lds_barrier();
+#pragma unroll 1
+            for (int n = 0; n < N; ++n) {
+                lds_barrier();   // chunk n read
+                if (n + 1 < N) issue_ops(n + 1);
+                wait_vm_all();
+                lds_barrier();
+            }
+            return;
+        }
+        // chunk n + NSLOT - 1 goes into the slot chunk n - 1 used, once every
+        // compute wave has passed the barrier that ends chunk n - 1; before the
+        // barrier that ends chunk n, chunk n + 1 must have landed while chunk
+        // n + NSLOT - 1's copies (the newest NOP) may still fly
+#pragma unroll
+        for (int n = 0; n < NSLOT - 1; ++n)
+            if (n < N) issue_ops(n);
         wait_vm_all();
         lds_barrier();
 #pragma unroll 1
         for (int n = 0; n < N; ++n) {
-            if (n + 1 < N) issue_ops(n + 1);
-            wait_vm_all();
+            if (n + NSLOT - 1 < N) {
+                issue_ops(n + NSLOT - 1);
+                if (NSLOT == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(P::NOP));
+                else wait_vm_all();
+            } else {
+                wait_vm_all();
+            }
             lds_barrier();
         }
         return;
     }
 
-    f32x4_t S[NDT];
+    // compute wave: matrix L (w < NLW) or Phi, slabs 2q and 2q + 1 of it
+    const bool is_l = wave < P::NLW;
+    const int q = is_l ? wave : wave - P::NLW;
+    const int width = is_l ? DV : DK;
+    f32x4_t S[2][NDT];
+    {
+        // Phi starts at I: row 16 dt + 4g + i of column 32 q + 16 s2 + col
+        const int diag = is_l ? -1 : 32 * q + col - 4 * gq;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+        for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[dt][i] = (half && 16 * dt + 4 * gq + i == 16 * jt + col) ? 1.f : 0.f;
-
-    ChunkRegs<T, DK, DV> cur, nxt;
-    if (active) cur.load(wsr, cbase(0), jt, l, half == 0);
-    wait_vm_all();
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[s2][dt][i] = 16 * dt + i == diag + 16 * s2 ? 1.f : 0.f;
+    }
     lds_barrier();
 #pragma unroll 1
     for (int n = 0; n < N; ++n) {
-        const char *slot = lds + (n & 1) * P::OP_B;
-        if (n + 1 < N && active) nxt.load(wsr, cbase(n + 1), jt, l, half == 0);
-        if (active) {
-            F Sb[NKS];
+        const char *slot = lds + (n % NSLOT) * P::SLOT;
+        const float2 gam = *reinterpret_cast<const float2 *>(
+            slot + P::GAM_OFF + 4 * (gq * (DK / 4) + 2 * min(col, DK / 8 - 1)));
+        // one slab after the other: U = Ut - W S (or -W S), S <- Diag(Gam) S + Kh^T U.
+        // The fragments are read from LDS once per slab: one slab's temporaries
+        // keep the wave within its registers at three waves per SIMD.
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) Sb[ks] = tiles_to_frag<T>(S[2 * ks], S[2 * ks + 1]);
+        for (int s2 = 0; s2 < 2; ++s2) {
             f32x4_t U[4];
 #pragma unroll
             for (int R = 0; R < 4; ++R) U[R] = zero4();
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
+            for (int ks = 0; ks < NKS; ++ks) {
+                const F b = tiles_to_frag<T>(S[s2][2 * ks], S[s2][2 * ks + 1]);
 #pragma unroll
                 for (int R = 0; R < 4; ++R)
-                    U[R] = mma(slot_frag<T>(slot, WL::W + (size_t)(R * NKS + ks) * 512, l), Sb[ks], U[R]);
-            decay_rows<NDT>(S, cur.gam);
-            if (half == 0) {
-                ut_minus<T>(U, cur.ut);
+                    U[R] = mma(slot_frag<T>(slot, WL::W + (size_t)(R * NKS + ks) * 512, l), b, U[R]);
+            }
+            decay_rows<NDT>(S[s2], gam);
+            if (is_l) {
+                const char *ut = slot + 2 * P::W_B + ((size_t)(2 * q + s2) * 1024 + (size_t)l * 16) * sizeof(T);
+                const Raw8<T> u8[2] = {*reinterpret_cast<const Raw8<T> *>(ut),
+                                       *reinterpret_cast<const Raw8<T> *>(ut + 8 * sizeof(T))};
+                ut_minus<T>(U, u8);
             } else {
 #pragma unroll
                 for (int R = 0; R < 4; ++R) U[R] = -U[R];
             }
-            const F Ub[2] = {tiles_to_frag<T>(U[0], U[1]), tiles_to_frag<T>(U[2], U[3])};
-            const char *kh = slot + P::W_B;
+            const F u[2] = {tiles_to_frag<T>(U[0], U[1]), tiles_to_frag<T>(U[2], U[3])};
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt)
-                    S[dt] = mma(slot_frag<T>(kh, (size_t)(dt * 2 + kt) * 512, l), Ub[kt], S[dt]);
+                    S[s2][dt] = mma(slot_frag<T>(slot + P::W_B, (size_t)(dt * 2 + kt) * 512, l), u[kt], S[s2][dt]);
         }
-        wait_vm_all();
+        if (NSLOT == 1) lds_barrier();   // chunk n read: the loader may refill the slot
         lds_barrier();
-        cur = nxt;
     }
-    if (active) {
-        const SegRec<DK, DV> rec(a, h, g);
-        float *dst = half ? rec.Phi : rec.L;
+    const SegRec<DK, DV> rec(a, h, g);
+    // this lane's element (row 4g, column 32 q + col), formed here: hoisted above
+    // the loop, the row offsets would take registers for its whole length
+    int e0 = 4 * gq * width + 32 * q + col;
+    asm volatile("" : "+v"(e0));
+    float *dst = (is_l ? rec.L : rec.Phi) + e0;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(16 * dt + 4 * gq + i) * width + 16 * jt + col] = S[dt][i];
-    }
+            for (int i = 0; i < 4; ++i) dst[(16 * dt + i) * width + 16 * s2] = S[s2][dt][i];
 }
 
 // ============================================================================
@@ -265,13 +313,18 @@ __global__ __launch_bounds__(kSegsumMaxThreads) void kda_segsum_kernel(KdaArgs a
 // Workgroup (sequence, head, 16 state columns jt); wave ot computes the 16
 // rows 16 ot .. 16 ot + 15 of S_start(p + 1) = Phi_p S_start(p) + L_p on the
 // fp32 matrix cores.  The k index of the product runs over rows 16 dt + 4g + i
-// for (dt, i) in turn, so lane group g's B operand is its own row of the
-// state, read from the LDS copy shared by the waves.
+// for (dt, i) in turn, so lane group g's B operand is four consecutive rows
+// of its column, one 16-byte read of the transposed LDS copy of the state.
+// Each wave's rows of Phi_p and L_p are loaded into a ring of kChainAhead
+// register sets, kChainAhead steps before their use: a step is one short
+// product, far shorter than the memory latency.
 // ============================================================================
+constexpr int kChainAhead = 4;
+
 template <int DK, int DV>
 __global__ __launch_bounds__(64 * (DK / 16)) void kda_chain_kernel(KdaArgs a) {
-    constexpr int NJT = DV / 16, NDT = DK / 16, SS = 17;   // padded row of the LDS state copy
-    __shared__ float Sl[2][DK][SS];
+    constexpr int NJT = DV / 16, NDT = DK / 16, SS = DK + 4;   // padded column of the LDS state copy
+    __shared__ __attribute__((aligned(16))) float St[2][16][SS];   // St[.][col][row]
     const int jt = blockIdx.x % NJT, bh = blockIdx.x / NJT;
     const int sq = bh / a.H, h = bh % a.H;
     const int ot = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -285,45 +338,56 @@ __global__ __launch_bounds__(64 * (DK / 16)) void kda_chain_kernel(KdaArgs a) {
         acc[i] = a.s0 ? a.s0[((size_t)bh * DK + r0 + i) * DV + 16 * jt + col] : 0.f;
     {
         const SegRec<DK, DV> rec(a, h, sg0);
+        *reinterpret_cast<float4 *>(&St[0][col][r0]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            Sl[0][r0 + i][col] = acc[i];
-            rec.S0[(r0 + i) * DV + 16 * jt + col] = acc[i];
-        }
+        for (int i = 0; i < 4; ++i) rec.S0[(r0 + i) * DV + 16 * jt + col] = acc[i];
     }
-    // Phi_p rows 16 ot + col at columns 16 dt + 4g .. + 3, and L_p at this lane's outputs
-    float4 ph[NDT];
-    float lp[4];
-    auto load_map = [&](int p) {
+    // ring of the maps of steps p .. p + kChainAhead - 1: Phi_p rows 16 ot + col at
+    // columns 16 dt + 4g .. + 3, and L_p at this lane's outputs
+    float4 ph[kChainAhead][NDT];
+    float4 lp[kChainAhead];
+    auto load_map = [&](int p, float4 (&phr)[NDT], float4 &lpr) {
         const SegRec<DK, DV> rec(a, h, sg0 + p);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-            ph[dt] = *reinterpret_cast<const float4 *>(rec.Phi + (16 * ot + col) * DK + 16 * dt + 4 * gq);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lp[i] = rec.L[(r0 + i) * DV + 16 * jt + col];
+            phr[dt] = *reinterpret_cast<const float4 *>(rec.Phi + (16 * ot + col) * DK + 16 * dt + 4 * gq);
+        lpr = make_float4(rec.L[(r0 + 0) * DV + 16 * jt + col], rec.L[(r0 + 1) * DV + 16 * jt + col],
+                          rec.L[(r0 + 2) * DV + 16 * jt + col], rec.L[(r0 + 3) * DV + 16 * jt + col]);
     };
-    if (nseg > 1) load_map(0);
-    lds_barrier();
-#pragma unroll 1
-    for (int p = 0; p + 1 < nseg; ++p) {
-        const int cur = p & 1;
+    const int nsteps = nseg - 1;
+    if (nsteps == 0) return;   // one segment: its start state is written
+    // Straight-line steps: every step loads, computes, stores and meets the
+    // barrier, whatever its index, so the memory-counter waits the compiler
+    // places are exact (a conditional load or store makes it wait for all).
+    // Steps past the last one repeat the last step: it reads the state it
+    // read before (that LDS buffer is not rewritten) and stores the same values.
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = lp[i];
+    for (int j = 0; j < kChainAhead; ++j) load_map(min(j, nsteps - 1), ph[j], lp[j]);
+    lds_barrier();
+    auto step = [&](int p, float4 (&phr)[NDT], float4 &lpr) {
+        const int cur = p & 1;
+        f32x4_t y = {lpr.x, lpr.y, lpr.z, lpr.w};
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            acc = mma4(ph[dt].x, Sl[cur][16 * dt + 4 * gq + 0][col], acc);
-            acc = mma4(ph[dt].y, Sl[cur][16 * dt + 4 * gq + 1][col], acc);
-            acc = mma4(ph[dt].z, Sl[cur][16 * dt + 4 * gq + 2][col], acc);
-            acc = mma4(ph[dt].w, Sl[cur][16 * dt + 4 * gq + 3][col], acc);
+            const float4 b = *reinterpret_cast<const float4 *>(&St[cur][col][16 * dt + 4 * gq]);
+            y = mma4(phr[dt].x, b.x, y);
+            y = mma4(phr[dt].y, b.y, y);
+            y = mma4(phr[dt].z, b.z, y);
+            y = mma4(phr[dt].w, b.w, y);
         }
-        if (p + 2 < nseg) load_map(p + 1);
+        load_map(min(p + kChainAhead, nsteps - 1), phr, lpr);
         const SegRec<DK, DV> rec(a, h, sg0 + p + 1);
+        *reinterpret_cast<float4 *>(&St[cur ^ 1][col][r0]) = make_float4(y[0], y[1], y[2], y[3]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            Sl[cur ^ 1][r0 + i][col] = acc[i];
-            rec.S0[(r0 + i) * DV + 16 * jt + col] = acc[i];
-        }
+        for (int i = 0; i < 4; ++i) rec.S0[(r0 + i) * DV + 16 * jt + col] = y[i];
         lds_barrier();
+    };
+#pragma unroll 1
+    for (int p = 0; p < nsteps; p += kChainAhead) {
+        // a repeated last step keeps the parity of the step it repeats
+        const int last = nsteps - 1;
+#pragma unroll
+        for (int j = 0; j < kChainAhead; ++j) step(min(p + j, last), ph[j], lp[j]);
     }
 }
 
@@ -539,8 +603,8 @@ hipError_t launch_scan_typed(const KdaArgs &a, hipStream_t stream) {
     if (total > a.B) {
         hipError_t e = allow_lds((const void *)kda_segsum_kernel<T, DK, DV>, PS::LDS_B, sum_attr);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((kda_segsum_kernel<T, DK, DV>), dim3(2 * total * a.H), dim3(PS::THREADS), PS::LDS_B,
-                           stream, a);
+        hipLaunchKernelGGL((kda_segsum_kernel<T, DK, DV>), dim3(total * a.H), dim3(PS::THREADS), PS::LDS_B, stream,
+                           a);
         hipLaunchKernelGGL((kda_chain_kernel<DK, DV>), dim3(a.B * a.H * (DV / 16)), dim3(64 * (DK / 16)), 0, stream,
                            a);
     }
