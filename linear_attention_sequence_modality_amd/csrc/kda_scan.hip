@@ -57,7 +57,11 @@ __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f7
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xf00; }
 
 // ---- segment records --------------------------------------------------------
-// One per (head, segment): L [DK][DV], Phi [DK][DK], S_start [DK][DV], fp32 row-major.
+// One per (head, segment), fp32: L and S_start (DK x DV) in state-fragment
+// order, Phi (DK x DK) row-major.  State-fragment order holds element (row
+// 16 dt + 4 g + i, column 16 jt + col) at ((jt * DK/16 + dt) * 64 + 16 g + col) * 4 + i:
+// the four values a lane of the wave owning columns 16 jt .. of a state tile
+// holds are 16 contiguous bytes.
 template <int DK, int DV>
 struct SegRec {
     float *L, *Phi, *S0;
@@ -69,6 +73,10 @@ struct SegRec {
         S0 = Phi + DK * DK;
     }
 };
+
+// Offset (in floats) of lane l's four values of tile (jt, dt) in state-fragment order.
+template <int DK>
+__device__ __forceinline__ int frag_off(int jt, int dt, int l) { return ((jt * (DK / 16) + dt) * 64 + l) * 4; }
 
 // One (sequence, head)'s chunk records as a raw buffer (chunk n at byte n * BYTES;
 // the host checks that a sequence's records stay below 4 GiB).
@@ -241,7 +249,6 @@ __global__ __launch_bounds__(kSegsumMaxThreads) void kda_segsum_kernel(KdaArgs a
     // compute wave: matrix L (w < NLW) or Phi, slabs 2q and 2q + 1 of it
     const bool is_l = wave < P::NLW;
     const int q = is_l ? wave : wave - P::NLW;
-    const int width = is_l ? DV : DK;
     f32x4_t S[2][NDT];
     {
         // Phi starts at I: row 16 dt + 4g + i of column 32 q + 16 s2 + col
@@ -295,17 +302,25 @@ __global__ __launch_bounds__(kSegsumMaxThreads) void kda_segsum_kernel(KdaArgs a
         lds_barrier();
     }
     const SegRec<DK, DV> rec(a, h, g);
-    // this lane's element (row 4g, column 32 q + col), formed here: hoisted above
-    // the loop, the row offsets would take registers for its whole length
-    int e0 = 4 * gq * width + 32 * q + col;
-    asm volatile("" : "+v"(e0));
-    float *dst = (is_l ? rec.L : rec.Phi) + e0;
+    if (is_l) {
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+        for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+            for (int dt = 0; dt < NDT; ++dt)
+                *reinterpret_cast<f32x4_t *>(rec.L + frag_off<DK>(2 * q + s2, dt, l)) = S[s2][dt];
+    } else {
+        // this lane's element (row 4g, column 32 q + col), formed here: hoisted above
+        // the loop, the row offsets would take registers for its whole length
+        int e0 = 4 * gq * DK + 32 * q + col;
+        asm volatile("" : "+v"(e0));
+        float *dst = rec.Phi + e0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(16 * dt + i) * width + 16 * s2] = S[s2][dt][i];
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[(16 * dt + i) * DK + 16 * s2] = S[s2][dt][i];
+    }
 }
 
 // ============================================================================
@@ -325,7 +340,10 @@ template <int DK, int DV>
 __global__ __launch_bounds__(64 * (DK / 16)) void kda_chain_kernel(KdaArgs a) {
     constexpr int NJT = DV / 16, NDT = DK / 16, SS = DK + 4;   // padded column of the LDS state copy
     __shared__ __attribute__((aligned(16))) float St[2][16][SS];   // St[.][col][row]
-    const int jt = blockIdx.x % NJT, bh = blockIdx.x / NJT;
+    // the NJT workgroups of one (sequence, head) read the same maps: kept on one
+    // XCD, its L2 serves the maps to all of them
+    const int blk = xcd_remap(blockIdx.x, gridDim.x);
+    const int jt = blk % NJT, bh = blk / NJT;
     const int sq = bh / a.H, h = bh % a.H;
     const int ot = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = threadIdx.x & 63, col = l & 15, gq = l >> 4;
@@ -339,20 +357,20 @@ __global__ __launch_bounds__(64 * (DK / 16)) void kda_chain_kernel(KdaArgs a) {
     {
         const SegRec<DK, DV> rec(a, h, sg0);
         *reinterpret_cast<float4 *>(&St[0][col][r0]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rec.S0[(r0 + i) * DV + 16 * jt + col] = acc[i];
+        *reinterpret_cast<f32x4_t *>(rec.S0 + frag_off<DK>(jt, ot, l)) = acc;
     }
     // ring of the maps of steps p .. p + kChainAhead - 1: Phi_p rows 16 ot + col at
-    // columns 16 dt + 4g .. + 3, and L_p at this lane's outputs
+    // columns 16 dt + 4g .. + 3, and L_p at this lane's outputs (nine 16-byte loads a
+    // step: with the step's one store, the ring stays within the 63 memory
+    // operations a wave can have in flight)
     float4 ph[kChainAhead][NDT];
-    float4 lp[kChainAhead];
-    auto load_map = [&](int p, float4 (&phr)[NDT], float4 &lpr) {
+    f32x4_t lp[kChainAhead];
+    auto load_map = [&](int p, float4 (&phr)[NDT], f32x4_t &lpr) {
         const SegRec<DK, DV> rec(a, h, sg0 + p);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
             phr[dt] = *reinterpret_cast<const float4 *>(rec.Phi + (16 * ot + col) * DK + 16 * dt + 4 * gq);
-        lpr = make_float4(rec.L[(r0 + 0) * DV + 16 * jt + col], rec.L[(r0 + 1) * DV + 16 * jt + col],
-                          rec.L[(r0 + 2) * DV + 16 * jt + col], rec.L[(r0 + 3) * DV + 16 * jt + col]);
+        lpr = *reinterpret_cast<const f32x4_t *>(rec.L + frag_off<DK>(jt, ot, l));
     };
     const int nsteps = nseg - 1;
     if (nsteps == 0) return;   // one segment: its start state is written
@@ -364,22 +382,26 @@ __global__ __launch_bounds__(64 * (DK / 16)) void kda_chain_kernel(KdaArgs a) {
 #pragma unroll
     for (int j = 0; j < kChainAhead; ++j) load_map(min(j, nsteps - 1), ph[j], lp[j]);
     lds_barrier();
-    auto step = [&](int p, float4 (&phr)[NDT], float4 &lpr) {
+    auto step = [&](int p, float4 (&phr)[NDT], f32x4_t &lpr) {
         const int cur = p & 1;
-        f32x4_t y = {lpr.x, lpr.y, lpr.z, lpr.w};
+        // the whole column of the state first (one LDS wait), then the products
+        // over four independent accumulators, summed at the end
+        float4 b[NDT];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) b[dt] = *reinterpret_cast<const float4 *>(&St[cur][col][16 * dt + 4 * gq]);
+        f32x4_t y4[4] = {lpr, zero4(), zero4(), zero4()};
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const float4 b = *reinterpret_cast<const float4 *>(&St[cur][col][16 * dt + 4 * gq]);
-            y = mma4(phr[dt].x, b.x, y);
-            y = mma4(phr[dt].y, b.y, y);
-            y = mma4(phr[dt].z, b.z, y);
-            y = mma4(phr[dt].w, b.w, y);
+            y4[0] = mma4(phr[dt].x, b[dt].x, y4[0]);
+            y4[1] = mma4(phr[dt].y, b[dt].y, y4[1]);
+            y4[2] = mma4(phr[dt].z, b[dt].z, y4[2]);
+            y4[3] = mma4(phr[dt].w, b[dt].w, y4[3]);
         }
+        const f32x4_t y = (y4[0] + y4[1]) + (y4[2] + y4[3]);
         load_map(min(p + kChainAhead, nsteps - 1), phr, lpr);
         const SegRec<DK, DV> rec(a, h, sg0 + p + 1);
         *reinterpret_cast<float4 *>(&St[cur ^ 1][col][r0]) = make_float4(y[0], y[1], y[2], y[3]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rec.S0[(r0 + i) * DV + 16 * jt + col] = y[i];
+        *reinterpret_cast<f32x4_t *>(rec.S0 + frag_off<DK>(jt, ot, l)) = y;
         lds_barrier();
     };
 #pragma unroll 1
@@ -472,8 +494,12 @@ __global__ __launch_bounds__(kSegoutMaxThreads) void kda_segout_kernel(KdaArgs a
     } else if (wave < P::NCW) {
         const int jt = wave;
         f32x4_t S[NDT];
-        {
-            const float *s0 = chained ? SegRec<DK, DV>(a, h, g).S0 : (a.s0 ? a.s0 + (size_t)bh * DK * DV : nullptr);
+        if (chained) {
+            const float *s0 = SegRec<DK, DV>(a, h, g).S0;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) S[dt] = *reinterpret_cast<const f32x4_t *>(s0 + frag_off<DK>(jt, dt, l));
+        } else {
+            const float *s0 = a.s0 ? a.s0 + (size_t)bh * DK * DV : nullptr;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
