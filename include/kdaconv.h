@@ -155,6 +155,27 @@ int kda_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv,
                 void *hip_stream);
 
 /*
+ * kda_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and checks as kda_forward, with the chunk workspace held
+ * in the library's own device array of KDA_NOALLOC_SCRATCH_BYTES per device
+ * (allocated when the library's code is loaded on a device, kept until the
+ * process ends) instead of a caller's buffer.  The call allocates and frees
+ * nothing.  Shapes whose workspace (kda_forward_workspace_size) exceeds
+ * KDA_NOALLOC_SCRATCH_BYTES return KDA_ERR_WORKSPACE before anything is
+ * enqueued.  Every call on one device uses that device's one array: calls
+ * that overlap in time on one device (different streams, or host threads
+ * without ordering) race and give undefined results; calls ordered on one
+ * stream are safe.  The first call on a device looks up the array's address
+ * (a host-side query, no allocation); a failure there is KDA_ERR_HIP.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int kda_forward_noalloc(const kda_stream_desc *desc, int B, int H, int dk, int dv,
+                        kda_dtype dtype, const void *q, const void *k, const void *v,
+                        const void *alpha, const void *beta, const float *initial_state,
+                        float *final_state, void *o, void *hip_stream);
+
+/*
  * The two kernels of kda_forward, callable separately with the same shapes,
  * checks and workspace: kda_forward(...) is exactly kda_forward_chunks(...)
  * followed by kda_forward_scan(...) on one stream.  kda_forward_chunks forms

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/kdaconv.h"
 #include "launch.h"
 
@@ -311,7 +313,7 @@ namespace {
 int prepare_kda(const Seqs &sq, int H, int dk, int dv, kda_dtype dtype, const void *q, const void *k,
                 const void *v, const void *alpha, const void *beta, const float *initial_state,
                 const float *final_state, const void *o, const void *workspace, size_t workspace_bytes,
-                bool want_inputs, bool want_outputs, KdaArgs *out) {
+                bool want_inputs, bool want_outputs, KdaArgs *out, bool own_scratch = false) {
     if (dtype == KDA_F32 && (dk != 64 || dv != 64)) return KDA_ERR_UNSUPPORTED;
     const size_t es = elem_bytes(dtype);
     const size_t BT = (size_t)sq.tokens;
@@ -346,7 +348,11 @@ int prepare_kda(const Seqs &sq, int H, int dk, int dv, kda_dtype dtype, const vo
     if (sq.n > 0) {
         const size_t need = workspace_bytes_of(sq, H, dk, dv, dtype);
         if (need == 0) return KDA_ERR_UNSUPPORTED;
-        if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KDA_ERR_WORKSPACE;
+        if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    }
+    if (sq.n > 0 && !own_scratch) {
+        const size_t need = workspace_bytes_of(sq, H, dk, dv, dtype);
+        if (!workspace || !aligned16(workspace)) return KDA_ERR_WORKSPACE;
         const Range rw = range_of(workspace, need);
         for (int i = 0; i < 6; ++i)
             if (overlaps(rw, rin[i])) return KDA_ERR_INVALID_ARG;
@@ -419,6 +425,62 @@ int kda_forward_varlen(const kda_stream_desc *descs, int n_seq, int H, int dk, i
     if (rc != KDA_OK) return rc;
     return forward(sq, H, dk, dv, dtype, q, k, v, alpha, beta, initial_state, final_state, o, workspace,
                    workspace_bytes, hip_stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---- the allocation-free forward --------------------------------------------
+// kda_forward_noalloc keeps its chunk workspace in this file-scope device
+// array instead of a caller's buffer.  Each device that loads the library
+// holds its own copy until the process ends; host code reaches it only
+// through the address hipGetSymbolAddress returns for the current device (the
+// array's name is a host-side stand-in, not a device address).
+constexpr size_t kScratchBytes = (size_t)64 << 20;   // KDA_NOALLOC_SCRATCH_BYTES
+static_assert(kScratchBytes == KDA_NOALLOC_SCRATCH_BYTES, "one stated scratch size");
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, looked up once per device.
+int scratch_of_current_device(void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KDA_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *ptr = scratch_ptr[dev];
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_forward_noalloc(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,
+                        const void *q, const void *k, const void *v, const void *alpha, const void *beta,
+                        const float *initial_state, float *final_state, void *o, void *hip_stream) {
+    Seqs sq;
+    KdaArgs a;
+    int rc = uniform_seqs(desc, B, H, dk, dv, dtype, &sq);
+    if (rc == KDA_OK)
+        rc = prepare_kda(sq, H, dk, dv, dtype, q, k, v, alpha, beta, initial_state, final_state, o, nullptr,
+                         kScratchBytes, true, true, &a, true);
+    if (rc != KDA_OK || B == 0) return rc;
+    void *ws = nullptr;
+    rc = scratch_of_current_device(&ws);
+    if (rc != KDA_OK) return rc;
+    a.ws = ws;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (kdaconv::launch_kda_chunks(a, dtype == KDA_BF16, st) != hipSuccess) return KDA_ERR_HIP;
+    if (kdaconv::launch_kda_scan(a, dtype == KDA_BF16, st) != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
 }
 
 int kda_forward_chunks(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,

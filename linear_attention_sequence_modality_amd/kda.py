@@ -29,7 +29,9 @@ KDA_MAX_SEQS = 64   # streams of one variable-length batch
 EXPORTED_SYMBOLS = ("kda_conv_forward", "kda_conv_forward_stream", "kda_forward_workspace_size", "kda_forward",
                     "kda_forward_chunks", "kda_forward_scan", "kda_forward_varlen_workspace_size",
                     "kda_forward_varlen", "kda_conv_forward_varlen", "mla_attention_forward",
-                    "kda_backward_workspace_size", "kda_backward", "kda_conv_backward", "kda_status_string")
+                    "kda_backward_workspace_size", "kda_backward", "kda_conv_backward", "kda_status_string",
+                    "kda_forward_noalloc")
+KDA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class KdaStreamDesc(ctypes.Structure):
@@ -71,6 +73,8 @@ def load_library():
     lib.kda_forward.restype = i32
     lib.kda_forward.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                 vp, ctypes.c_size_t, vp]
+    lib.kda_forward_noalloc.restype = i32
+    lib.kda_forward_noalloc.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_forward_chunks.restype = i32
     lib.kda_forward_chunks.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                        ctypes.c_size_t, vp]
@@ -223,6 +227,33 @@ def kda_forward(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: torch.
                          _stream(stream))
     if rc != KDA_OK:
         raise KdaError("kda_forward", rc)
+    return o
+
+
+def kda_forward_noalloc(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        alpha: torch.Tensor, beta: torch.Tensor,
+                        initial_state: Optional[torch.Tensor] = None,
+                        final_state: Optional[torch.Tensor] = None, o: torch.Tensor = None,
+                        stream=None) -> torch.Tensor:
+    """kda_forward with the workspace in the library's own device array: the call allocates
+    nothing, so ``o`` (and ``final_state`` if wanted) must be passed in."""
+    lib = load_library()
+    dt = q.dtype
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (alpha, "alpha"), (beta, "beta")):
+        _check(t, nm, dt)
+    if o is None:
+        raise ValueError("kda_forward_noalloc allocates nothing: pass o")
+    _check(o, "o", dt)
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None:
+            _check(t, nm, torch.float32)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    rc = lib.kda_forward_noalloc(ctypes.byref(desc), B, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(final_state), _ptr(o),
+                                 _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_forward_noalloc", rc)
     return o
 
 
