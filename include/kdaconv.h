@@ -127,9 +127,11 @@ int kda_conv_forward_stream(const kda_stream_desc *desc, int B, int H, int dk, i
                             void *q_out, void *k_out, void *v_out, void *hip_stream);
 
 /* Bytes of device workspace kda_forward needs for this shape: the chunk
- * transforms of every (batch, head, chunk).  0 on bad or unsupported
- * arguments, including shapes whose per-(batch, head) transforms would reach
- * 4 GiB. */
+ * transforms of every (batch, head, chunk), plus, when the state pass cuts the
+ * streams into segments, one record per (batch, head, segment) of fp32
+ * 2 dk dv + dk dk values.  Host arithmetic only (no HIP call); the same for
+ * every device.  0 on bad or unsupported arguments, including shapes whose
+ * per-(batch, head) transforms would reach 4 GiB. */
 size_t kda_forward_workspace_size(const kda_stream_desc *desc, int B, int H, int dk,
                                   int dv, kda_dtype dtype);
 
@@ -141,12 +143,16 @@ size_t kda_forward_workspace_size(const kda_stream_desc *desc, int B, int H, int
  *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
  *   o_t = S_t^T q_t
  * o is written in the input dtype; final_state (optional, NULL to skip)
- * receives S_T in fp32.  The scan is computed chunkwise (64 tokens per chunk):
- * an intra-chunk kernel forms the chunk's UT/WY transform on matrix cores and
- * writes it to `workspace`; a state-passing kernel walks the chunks in order
- * with the state held on chip.  `workspace` (device, >= the size returned by
- * kda_forward_workspace_size) is scratch owned by the caller; its contents are
- * undefined afterwards.  initial_state may alias final_state.
+ * receives S_T in fp32.  Supported: dk, dv in {64, 128} in either dtype.  The
+ * scan is computed chunkwise (64 tokens per chunk): an intra-chunk kernel forms
+ * every chunk's UT/WY transform on matrix cores and writes it to `workspace`;
+ * the state pass then cuts each stream's chunks into segments (about
+ * 256 / (B H) of them, at most 32), forms each segment's affine state map
+ * S -> Phi S + L in parallel, chains the segments' start states in fp32, and
+ * replays every segment from its start state, in parallel, writing o.
+ * `workspace` (device, >= the size returned by kda_forward_workspace_size) is
+ * scratch owned by the caller; its contents are undefined afterwards.
+ * initial_state may alias final_state.
  */
 int kda_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv,
                 kda_dtype dtype, const void *q, const void *k, const void *v,
@@ -176,13 +182,13 @@ int kda_forward_noalloc(const kda_stream_desc *desc, int B, int H, int dk, int d
                         float *final_state, void *o, void *hip_stream);
 
 /*
- * The two kernels of kda_forward, callable separately with the same shapes,
+ * The two stages of kda_forward, callable separately with the same shapes,
  * checks and workspace: kda_forward(...) is exactly kda_forward_chunks(...)
  * followed by kda_forward_scan(...) on one stream.  kda_forward_chunks forms
  * every chunk's UT/WY transform (fully parallel over chunks) and writes it to
- * the workspace; kda_forward_scan walks the chunks of each (batch, head) in
- * order, carrying the state, and writes o and optionally final_state.  The
- * workspace must not be modified between the two calls.
+ * the workspace; kda_forward_scan runs the segmented state pass (segment
+ * maps, chain of start states, replay) and writes o and optionally
+ * final_state.  The workspace must not be modified between the two calls.
  */
 int kda_forward_chunks(const kda_stream_desc *desc, int B, int H, int dk, int dv,
                        kda_dtype dtype, const void *q, const void *k, const void *v,

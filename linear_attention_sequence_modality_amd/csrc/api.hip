@@ -258,7 +258,6 @@ size_t chunk_records_bytes(const Seqs &sq, int H, int dk, int dv, kda_dtype dtyp
 }
 
 size_t workspace_bytes_of(const Seqs &sq, int H, int dk, int dv, kda_dtype dtype) {
-    if (dtype == KDA_F32 && (dk != 64 || dv != 64)) return 0;
     const size_t per = kdaconv::kda_chunk_ws_bytes(dk, dv, dtype == KDA_BF16);
     // the state pass addresses one (sequence, head)'s chunks with 32-bit offsets
     if ((int64_t)per * sq.max_chunks >= ((int64_t)1 << 32)) return 0;
@@ -314,7 +313,6 @@ int prepare_kda(const Seqs &sq, int H, int dk, int dv, kda_dtype dtype, const vo
                 const void *v, const void *alpha, const void *beta, const float *initial_state,
                 const float *final_state, const void *o, const void *workspace, size_t workspace_bytes,
                 bool want_inputs, bool want_outputs, KdaArgs *out, bool own_scratch = false) {
-    if (dtype == KDA_F32 && (dk != 64 || dv != 64)) return KDA_ERR_UNSUPPORTED;
     const size_t es = elem_bytes(dtype);
     const size_t BT = (size_t)sq.tokens;
     const size_t sbytes = (size_t)sq.n * H * dk * dv * sizeof(float);

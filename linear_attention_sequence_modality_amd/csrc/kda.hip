@@ -45,8 +45,6 @@ struct K1Smem {
     static constexpr int NPART = K1_THREADS / DK;     // threads per channel in the table loop
     static constexpr int KP = 16 / (int)sizeof(T);
     static constexpr int KS = DK + KP;                // row stride of Kr, Qr, Kb
-    static constexpr int RKS = 2 * (DK + 8 / (int)sizeof(T));  // row-pair stride of RHS_K
-    static constexpr int RVS = 2 * (DV + 8 / (int)sizeof(T));  // row-pair stride of RHS_V
     static constexpr int LS = 64 + 4;                 // fp32 64x64 stride (Lm, Tm32)
     static constexpr int TS = 64 + KP;                // T 64x64 stride (Tm16)
     static constexpr int SC = 17;                     // 16x16 fp32 scratch stride
@@ -63,9 +61,18 @@ struct K1Smem {
     static constexpr size_t X2_SZ = round_up(2 * SZ_K > SZ_SCR ? 2 * SZ_K : SZ_SCR, 16);
     static constexpr size_t X3 = X2 + X2_SZ;   // Tm16 (P3-P5)
     static constexpr size_t Q = X3 + round_up((size_t)C * TS * sizeof(T), 16);   // Qr (P1-P2)
-    static constexpr size_t RK = Q + round_up(SZ_K, 16);            // RHS_K row pairs (P1-P5)
-    static constexpr size_t RV = RK + round_up((size_t)32 * RKS * sizeof(T), 16);
-    static constexpr size_t TB = RV + round_up((size_t)32 * RVS * sizeof(T), 16);
+    // RHS_K = Diag(beta) 2^G K and RHS_V = Diag(beta) V as row pairs (P1-P5): in LDS
+    // when everything fits, else (fp32 at dk = 128) in the chunk's own record, in
+    // the W and Ut slots that P5 overwrites last (row-pair strides 2 dk and 2 dv)
+    static constexpr size_t TAB_B = (size_t)(14 * DK + 64) * 4;
+    static constexpr size_t RKV_LDS_B = round_up((size_t)32 * 2 * (DK + 8 / sizeof(T)) * sizeof(T), 16) +
+                                        round_up((size_t)32 * 2 * (DV + 8 / sizeof(T)) * sizeof(T), 16);
+    static constexpr bool RKV_LDS = round_up(Q + round_up(SZ_K, 16) + RKV_LDS_B + TAB_B, 16) <= 160 * 1024;
+    static constexpr int RKS = RKV_LDS ? 2 * (DK + 8 / (int)sizeof(T)) : 2 * DK;   // row-pair stride of RHS_K
+    static constexpr int RVS = RKV_LDS ? 2 * (DV + 8 / (int)sizeof(T)) : 2 * DV;   // row-pair stride of RHS_V
+    static constexpr size_t RK = Q + round_up(SZ_K, 16);
+    static constexpr size_t RV = RK + (RKV_LDS ? round_up((size_t)32 * RKS * sizeof(T), 16) : 0);
+    static constexpr size_t TB = RV + (RKV_LDS ? round_up((size_t)32 * RVS * sizeof(T), 16) : 0);
     // tables (fp32): Pm[4][DK], Kh[4][DK], Fp[6][DK], beta[64]
     static constexpr size_t TB_PM = TB;
     static constexpr size_t TB_KH = TB_PM + 4 * DK * 4;
@@ -169,8 +176,8 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     float *Scr = reinterpret_cast<float *>(smem + SM::X2);
     T *Tm16 = reinterpret_cast<T *>(smem + SM::X3);
     T *Qr = reinterpret_cast<T *>(smem + SM::Q);
-    T *RK = reinterpret_cast<T *>(smem + SM::RK);
-    T *RV = reinterpret_cast<T *>(smem + SM::RV);
+    T *const RK_lds = reinterpret_cast<T *>(smem + SM::RK);
+    T *const RV_lds = reinterpret_cast<T *>(smem + SM::RV);
     float *Pm = reinterpret_cast<float *>(smem + SM::TB_PM);
     float *Kh = reinterpret_cast<float *>(smem + SM::TB_KH);
     float *Fp = reinterpret_cast<float *>(smem + SM::TB_FP);
@@ -237,6 +244,8 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
         if (more) nxt = locate(item + gridDim.x);
         char *wsb = static_cast<char *>(a.ws) + ((size_t)cur.h * total + cur.gc) * WL::BYTES;
         T *ws = reinterpret_cast<T *>(wsb);
+        T *const RK = SM::RKV_LDS ? RK_lds : ws + WL::W;
+        T *const RV = SM::RKV_LDS ? RV_lds : ws + WL::U;
         float *ws_gam = reinterpret_cast<float *>(wsb + WL::GAM_BYTE);
 
         // ---- P0: G = cumsum(log2 alpha) over the chunk ------------------------------
@@ -482,38 +491,63 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
         {
             constexpr int NWU = DK / 16, NUU = DV / 16;
-            for (int u = wv; u < NWU + NUU; u += 8) {
+            static_assert(NWU + NUU <= 16, "at most two P5 units per wave");
+            // unit u < NWU: W^T rows of key channels 16 u ..; else Ut columns 16 (u - NWU) ..
+            auto load_unit = [&](int u, F (&op)[2]) {
+                const bool wu = u < NWU;
+                const int c16 = 16 * (wu ? u : u - NWU) + col;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    op[ks] = wu ? F::ld_pairs(RK + (16 * ks + 4 * g) * SM::RKS + 2 * c16, SM::RKS)
+                                : F::ld_pairs(RV + (16 * ks + 4 * g) * SM::RVS + 2 * c16, SM::RVS);
+            };
+            auto compute_unit = [&](int u, const F (&op)[2]) {
                 if (u < NWU) {
                     const int at = u;
-                    F rk[2];
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        rk[ks] = F::ld_pairs(RK + (16 * ks + 4 * g) * SM::RKS + 2 * (16 * at + col), SM::RKS);
 #pragma unroll
                     for (int R = 0; R < 4; ++R) {
                         f32x4_t acc = zero4();
 #pragma unroll
                         for (int ks = 0; ks <= (R >> 1); ++ks)
-                            acc = mma(rk[ks], F::ld8(Tm16 + (16 * R + col) * SM::TS + 32 * ks + 8 * g), acc);
+                            acc = mma(op[ks], F::ld8(Tm16 + (16 * R + col) * SM::TS + 32 * ks + 8 * g), acc);
                         const float w4[4] = {acc[0], acc[1], acc[2], acc[3]};
                         st4<T>(ws + WL::W + ((size_t)(R * NKS + (at >> 1)) * 64 + l) * 8 + (at & 1) * 4, w4);
                     }
                 } else {
                     const int jt = u - NWU;
-                    F rv[2];
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        rv[ks] = F::ld_pairs(RV + (16 * ks + 4 * g) * SM::RVS + 2 * (16 * jt + col), SM::RVS);
 #pragma unroll
                     for (int R = 0; R < 4; ++R) {
                         f32x4_t acc = zero4();
 #pragma unroll
                         for (int ks = 0; ks <= (R >> 1); ++ks)
-                            acc = mma(F::ld8(Tm16 + (16 * R + col) * SM::TS + 32 * ks + 8 * g), rv[ks], acc);
+                            acc = mma(F::ld8(Tm16 + (16 * R + col) * SM::TS + 32 * ks + 8 * g), op[ks], acc);
                         const float u4[4] = {acc[0], acc[1], acc[2], acc[3]};
                         st4<T>(ws + WL::U + ((size_t)(jt * 64 + l) * 4 + R) * 4, u4);
                     }
                 }
+            };
+            if constexpr (SM::RKV_LDS) {
+                for (int u = wv; u < NWU + NUU; u += 8) {
+                    F op[2];
+                    load_unit(u, op);
+                    compute_unit(u, op);
+                }
+            } else {
+                // RHS_K and RHS_V sit in the W and Ut slots the results overwrite.  Wave
+                // w owns W unit w and Ut unit w + 8 (dk = 128).  Every wave's P1 stores
+                // are visible after the first barrier; every wave holds its RHS_K operands
+                // before the second lets W be stored; no Ut is stored before the third,
+                // so the RHS_V reads between the two can still find their values.
+                static_assert(NWU == 8, "the record slots stand in for LDS only at dk = 128");
+                __syncthreads();
+                F op[2];
+                load_unit(wv, op);
+                __syncthreads();
+                compute_unit(wv, op);
+                const bool has_u = wv + 8 < NWU + NUU;
+                if (has_u) load_unit(wv + 8, op);
+                __syncthreads();
+                if (has_u) compute_unit(wv + 8, op);
             }
         }
         lds_barrier();   // LDS is reused by the next chunk

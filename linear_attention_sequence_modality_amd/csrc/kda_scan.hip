@@ -173,7 +173,7 @@ struct SegsumPlan {
     static constexpr int NSLOT = 3 * SLOT <= kLdsMax ? 3 : 2 * SLOT <= kLdsMax ? 2 : 1;
     static constexpr int LDS_B = NSLOT * SLOT;
     static_assert(W_B % 1024 == 0 && UG_SRC % 1024 == 0 && LDS_B <= kLdsMax, "segment summary LDS plan");
-    static_assert(NOP <= 63, "one chunk's copies must fit the vector memory counter");
+    static_assert(NSLOT < 3 || NOP <= 63, "the partial wait counts one chunk's copies in the vector memory counter");
     static_assert(THREADS <= kSegsumMaxThreads, "launch bound");
 };
 

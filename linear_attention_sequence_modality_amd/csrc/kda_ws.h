@@ -156,6 +156,9 @@ __device__ __forceinline__ void pin(f32x4_t &x) { asm volatile("" : "+v"(x)); }
         if (a.dk == 128 && a.dv == 128) return FN<bf16_t, 128, 128>(a, stream);                    \
     } else {                                                                                       \
         if (a.dk == 64 && a.dv == 64) return FN<float, 64, 64>(a, stream);                         \
+        if (a.dk == 64 && a.dv == 128) return FN<float, 64, 128>(a, stream);                       \
+        if (a.dk == 128 && a.dv == 64) return FN<float, 128, 64>(a, stream);                       \
+        if (a.dk == 128 && a.dv == 128) return FN<float, 128, 128>(a, stream);                     \
     }                                                                                              \
     return hipErrorInvalidValue;
 

@@ -120,10 +120,16 @@ def test_workspace_size_is_host_arithmetic(lib):
     assert s1 > 0 and s2 == 2 * s1 and s1 % (2 * 8) == 0
     assert kda.kda_forward_workspace_size(_desc(n_text=33), 1, 2, 64, 64, kda.KDA_F32) == \
         kda.kda_forward_workspace_size(_desc(n_text=32 + 64), 1, 2, 64, 64, kda.KDA_F32)
-    assert kda.kda_forward_workspace_size(d, 1, 2, 128, 128, kda.KDA_BF16) > 0
-    # fp32 scan supports dk = dv = 64 only
-    assert kda.kda_forward_workspace_size(d, 1, 2, 128, 128, kda.KDA_F32) == 0
-    assert kda.kda_forward_workspace_size(d, 1, 2, 96, 64, kda.KDA_BF16) == 0
+    # both dtypes at every head size in {64, 128}; nothing else
+    for dt in (kda.KDA_BF16, kda.KDA_F32):
+        for dk in (64, 128):
+            for dv in (64, 128):
+                assert kda.kda_forward_workspace_size(d, 1, 2, dk, dv, dt) > 0, (dt, dk, dv)
+        assert kda.kda_forward_workspace_size(d, 1, 2, 96, 64, dt) == 0
+        assert kda.kda_forward_workspace_size(d, 1, 2, 128, 32, dt) == 0
+    # fp32 records are twice the bf16 ones
+    assert kda.kda_forward_workspace_size(d, 1, 2, 128, 128, kda.KDA_F32) > \
+        kda.kda_forward_workspace_size(d, 1, 2, 128, 128, kda.KDA_BF16)
 
 
 def _fwd(lib, desc, B=1, H=2, dk=64, dv=64, dtype=kda.KDA_BF16, ptrs=None, s0=None, sT=None,
@@ -137,7 +143,7 @@ def _fwd(lib, desc, B=1, H=2, dk=64, dv=64, dtype=kda.KDA_BF16, ptrs=None, s0=No
 def test_forward_rejects_bad_arguments(lib):
     d = _desc()
     assert _fwd(lib, None) == kda.KDA_ERR_INVALID_ARG
-    assert _fwd(lib, d, dtype=kda.KDA_F32, dk=128, dv=128) == kda.KDA_ERR_UNSUPPORTED
+    assert _fwd(lib, d, dtype=kda.KDA_F32, dk=96, dv=128) == kda.KDA_ERR_UNSUPPORTED
     assert _fwd(lib, d, dk=32) == kda.KDA_ERR_UNSUPPORTED
     p = _ptrs(6)
     p[4] = None                                                       # beta

@@ -87,6 +87,9 @@ EDGE = [
     _small("bf16_64", dk=64, dv=64, H=3),
     _small("fp32_64", dk=64, dv=64, dtype="f32", grid=(2, 9, 13)),
     _small("fp32_causal", dk=64, dv=64, dtype="f32", causal_t=1, B=2),
+    _small("fp32_128", dtype="f32", grid=(3, 9, 13)),
+    _small("fp32_128_64", dk=128, dv=64, dtype="f32"),
+    _small("fp32_64_128", dk=64, dv=128, dtype="f32", B=2),
     _small("narrow_w", grid=(3, 4, 1), n_text=2),             # grid_w = 1, ragged w-runs
     _small("wide_w", grid=(2, 2, 37), n_text=9),
 ]
