@@ -8,22 +8,30 @@
 //
 // Design.  A depthwise conv has no channel contraction, so there is no
 // matrix-core work: 27 multiply-adds per output against 2 bytes in and 2 out.
+// At the video stream's size the vector-ALU work (about 130 us) and the memory
+// traffic (a copy of the same bytes takes about 160 us) are of one size, so
+// the kernel keeps both lean and overlaps them.
 //   * A 4-wave workgroup owns a tile of HR = 4 rows x WR = 8 w positions x 128
 //     channels and marches over t.  For every input slice it stages the
 //     (HR+2) x (WR+2) haloed tile in LDS with direct-to-LDS buffer loads of 16
 //     bytes per lane (one instruction moves 4 positions of 256 bytes), double
-//     buffered: the loads of slice t+1 fly while slice t is computed.  Each
-//     input element thus crosses the vector-memory path 1.9 times instead of
-//     3.75 times for per-wave halos, with a quarter of the instructions.
-//   * Wave w computes row h0 + w; lane l owns channels 2l, 2l+1.  It reads its
-//     3 x (WR+2) window of the slice from LDS (one dword per position) and
-//     applies it to the three output slices t-1, t, t+1 held in a 3-deep
-//     register ring whose slot index is static after unrolling the march.
+//     buffered: the loads of slice t+1 fly while slice t is computed.  Tile
+//     positions outside the grid are never loaded; their LDS bytes are zeroed
+//     once, which is the conv's zero padding, so edge tiles run the same
+//     branch-free window reads as interior ones.
+//   * Wave w computes all 4 rows at positions w0 + 2w, w0 + 2w + 1; lane l
+//     owns channels 2l, 2l+1.  It reads its 6 x 4 window of the slice from LDS
+//     (one dword per position) and applies it to the three output slices
+//     t-1, t, t+1 held in a 3-deep register ring whose slot index is static
+//     after unrolling the march.  Taking all rows in one wave lets each
+//     window row's byte permutes serve the three output rows that use it.
 //   * bf16: taps are paired so that one v_dot2_f32_bf16 does two useful
 //     multiply-adds: byte permutes form (x[w], x[w+1]) per channel for the
 //     w-taps 0 and 1 of each row, and (x[row0], x[row1]) for w-tap 2 of rows 0
-//     and 1; only w-tap 2 of row 2 uses a zero-padded weight pair.  fp32 streams
-//     use plain fma.
+//     and 1; only w-tap 2 of row 2 uses a zero-padded weight pair.  The first
+//     term of each output starts from an inline zero.  fp32 streams use fma.
+//   * Output stores are issued before the next slice's loads, so the wait for
+//     those loads mostly finds them done.
 //   * Blocks run channel block by channel block, row group by row group, and
 //     are remapped so each XCD works on a contiguous range of them: the halo
 //     rows of neighbouring row groups are read by co-resident blocks.
@@ -35,8 +43,9 @@
 namespace kdaconv {
 namespace {
 
-constexpr int WR = 8;     // w positions per wave (and per workgroup)
-constexpr int HR = 4;     // rows per workgroup (one per wave)
+constexpr int WR = 8;     // w positions per workgroup
+constexpr int HR = 4;     // rows per workgroup
+constexpr int JW = 2;     // w positions per wave (every wave computes all HR rows)
 constexpr int TR = 16;    // text tokens per wave item
 constexpr int NT = 256;   // threads per block (4 waves)
 constexpr int LANES = 64;
@@ -45,6 +54,7 @@ constexpr int TC = WR + 2;              // tile columns (w halo)
 constexpr int TP = (HR + 2) * TC;       // tile positions per slice
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -80,29 +90,12 @@ template <> struct Ops<bf16_t> {
         return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), __builtin_bit_cast(bf16x2_t, w), acc,
                                                false);
     }
-    // Apply one input slice (rows dh = 0..2 of this wave's window) to the
-    // accumulators of output position j: acc[a] receives tap slice a.
-    __device__ __forceinline__ static void apply(const Taps &tp, const XT (&x)[3][TC], int j, float *acc0[3],
-                                                 float *acc1[3]) {
-#pragma unroll
-        for (int dh = 0; dh < 3; ++dh) {
-            const uint32_t plo = __builtin_amdgcn_perm(x[dh][j + 1], x[dh][j], 0x05040100u);
-            const uint32_t phi = __builtin_amdgcn_perm(x[dh][j + 1], x[dh][j], 0x07060302u);
-#pragma unroll
-            for (int a = 0; a < 3; ++a) {
-                *acc0[a] = dot2(plo, tp.pr[a][dh][0], *acc0[a]);
-                *acc1[a] = dot2(phi, tp.pr[a][dh][1], *acc1[a]);
-            }
-        }
-        const uint32_t qlo = __builtin_amdgcn_perm(x[1][j + 2], x[0][j + 2], 0x05040100u);
-        const uint32_t qhi = __builtin_amdgcn_perm(x[1][j + 2], x[0][j + 2], 0x07060302u);
-#pragma unroll
-        for (int a = 0; a < 3; ++a) {
-            *acc0[a] = dot2(qlo, tp.p2[a][0], *acc0[a]);
-            *acc1[a] = dot2(qhi, tp.p2[a][1], *acc1[a]);
-            *acc0[a] = dot2(x[2][j + 2], tp.s2[a][0], *acc0[a]);
-            *acc1[a] = dot2(x[2][j + 2], tp.s2[a][1], *acc1[a]);
-        }
+    // dot2 onto a zero accumulator: the three-operand form with an inline 0
+    // (the compiler otherwise zeroes a register for the two-operand form)
+    __device__ __forceinline__ static float dot2_0(uint32_t x, uint32_t w) {
+        float r;
+        asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(x), "v"(w));
+        return r;
     }
     __device__ __forceinline__ static void bstore(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
                                                   float a, float b) {
@@ -131,19 +124,6 @@ template <> struct Ops<float> {
     }
     __device__ __forceinline__ static XT lds_read(const char *p) { return *reinterpret_cast<const float2 *>(p); }
     __device__ __forceinline__ static XT zero() { return make_float2(0.f, 0.f); }
-    __device__ __forceinline__ static void apply(const Taps &tp, const XT (&x)[3][TC], int j, float *acc0[3],
-                                                 float *acc1[3]) {
-#pragma unroll
-        for (int a = 0; a < 3; ++a)
-#pragma unroll
-            for (int dh = 0; dh < 3; ++dh)
-#pragma unroll
-                for (int e = 0; e < 3; ++e) {
-                    const int tap = (a * 3 + dh) * 3 + e;
-                    *acc0[a] = __builtin_fmaf(tp.w[tap][0], x[dh][j + e].x, *acc0[a]);
-                    *acc1[a] = __builtin_fmaf(tp.w[tap][1], x[dh][j + e].y, *acc1[a]);
-                }
-    }
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     __device__ __forceinline__ static void bstore(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
                                                   float a, float b) {
@@ -186,15 +166,32 @@ struct VisualTile {
     char *lds;            // two slice buffers
     int ti0;              // first input slice: -n_hist (history slices first)
     int wave, lane;
-    int rowb, gt, gh, gw, h0, w0, h;
+    int rowb, gt, gh, gw, h0, w0, wj;   // wj: first w position of this wave
     unsigned slice_bytes;  // one t-slice of the grid in the stream
     unsigned dma_off[NIW]; // lane's byte offset (t = 0) for each of its load instructions
-    unsigned out_off;      // lane's byte offset (t = 0) of output position 0 of its row
+    unsigned inb;          // bit i: load instruction i's position of this lane lies in the grid
+    unsigned out_off;      // lane's byte offset (t = 0) of output (h0, wj)
     typename O::Taps taps;
-    float acc[3][WR][2];
-    typename O::XT x[3][TC];
+    float acc[3][HR][JW][2];          // ring slot, row, position, channel
+    typename O::XT x[HR + 2][JW + 2]; // the wave's window of the current slice
 
-    __device__ __forceinline__ void issue_slice(int ti) {
+    // Positions outside the grid are never loaded: their 16 bytes of both slice
+    // buffers hold zeros, written once before the march (the zero padding).
+    template <bool EDGE>
+    __device__ __forceinline__ void zero_outside() {
+        if (!EDGE) return;
+#pragma unroll
+        for (int i = 0; i < NIW; ++i) {
+            const int k = wave + 4 * i;
+            if (k < NI && !(inb >> i & 1u))
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    *reinterpret_cast<u32x4_t *>(lds + b * SLICE + k * 1024 + lane * 16) = u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+
+    // mask: bit i set if load instruction i is issued for this lane
+    __device__ __forceinline__ void issue_slice(int ti, unsigned mask) {
         char *buf = lds + (ti & 1) * SLICE;
         // history slice ti < 0 sits at slice ti - ti0 of the history buffer
         // (which has no text tokens: the segment has none either)
@@ -203,25 +200,18 @@ struct VisualTile {
 #pragma unroll
         for (int i = 0; i < NIW; ++i) {
             const int k = wave + 4 * i;
-            if (k < NI)
+            if (k < NI && (mask >> i & 1u))
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(hist ? rh : rx, (lds_void_t *)(buf + k * 1024), 16,
                                                          dma_off[i], soff, 0, 0);
         }
     }
 
-    template <bool EDGE>
     __device__ __forceinline__ void read_window(int ti) {
-        const char *buf = lds + (ti & 1) * SLICE + lane * (int)(POS / LANES);
+        const char *buf = lds + (ti & 1) * SLICE + lane * (int)(POS / LANES) + JW * wave * POS;
 #pragma unroll
-        for (int dh = 0; dh < 3; ++dh) {
-            const int hh = h + dh - 1;
+        for (int r = 0; r < HR + 2; ++r)
 #pragma unroll
-            for (int jj = 0; jj < TC; ++jj) {
-                const int ww = w0 - 1 + jj;
-                const bool in = !EDGE || (hh >= 0 && hh < gh && ww >= 0 && ww < gw);
-                x[dh][jj] = in ? O::lds_read(buf + ((wave + dh) * TC + jj) * POS) : O::zero();
-            }
-        }
+            for (int c = 0; c < JW + 2; ++c) x[r][c] = O::lds_read(buf + (r * TC + c) * POS);
     }
 
     template <int P, bool EDGE>
@@ -230,12 +220,76 @@ struct VisualTile {
         if (active && t_done >= 0 && t_done < gt) {
             const unsigned soff = (unsigned)t_done * slice_bytes;
 #pragma unroll
-            for (int j = 0; j < WR; ++j)
-                if (!EDGE || w0 + j < gw)
-                    O::bstore(ry, out_off + (unsigned)(j * rowb), soff, acc[slot][j][0], acc[slot][j][1]);
-        }
+            for (int r = 0; r < HR; ++r)
 #pragma unroll
-        for (int j = 0; j < WR; ++j) acc[slot][j][0] = acc[slot][j][1] = 0.f;
+                for (int j = 0; j < JW; ++j)
+                    if (!EDGE || (h0 + r < gh && wj + j < gw))
+                        O::bstore(ry, out_off + (unsigned)((r * gw + j) * rowb), soff, acc[slot][r][j][0],
+                                  acc[slot][r][j][1]);
+        }
+    }
+
+    // Input slice ti (ti = P mod 6) into the three output slices it feeds.  The
+    // window rows rr are taken in order, so each accumulator still receives its
+    // taps in the order dh = 0, 1, 2 (then, for bf16, the paired and the single
+    // w-tap 2 terms): the window row rr is row dh = rr - r of output row r.
+    template <int P>
+    __device__ __forceinline__ void compute() {
+        constexpr int SL[3] = {((P + PT) % 3 + 3) % 3, ((P + PT - 1) % 3 + 3) % 3, ((P + PT - 2) % 3 + 3) % 3};
+#pragma unroll
+        for (int rr = 0; rr < HR + 2; ++rr)
+#pragma unroll
+            for (int j = 0; j < JW; ++j) {
+                if constexpr (sizeof(T) == 2) {
+                    const uint32_t plo = __builtin_amdgcn_perm(x[rr][j + 1], x[rr][j], 0x05040100u);
+                    const uint32_t phi = __builtin_amdgcn_perm(x[rr][j + 1], x[rr][j], 0x07060302u);
+#pragma unroll
+                    for (int dh = 0; dh < 3; ++dh) {
+                        const int r = rr - dh;
+                        if (r < 0 || r >= HR) continue;
+#pragma unroll
+                        for (int a = 0; a < 3; ++a) {
+                            float &c0 = acc[SL[a]][r][j][0], &c1 = acc[SL[a]][r][j][1];
+                            if (a == 0 && dh == 0) {   // first term of output slice ti + PT
+                                c0 = O::dot2_0(plo, taps.pr[a][dh][0]);
+                                c1 = O::dot2_0(phi, taps.pr[a][dh][1]);
+                            } else {
+                                c0 = O::dot2(plo, taps.pr[a][dh][0], c0);
+                                c1 = O::dot2(phi, taps.pr[a][dh][1], c1);
+                            }
+                        }
+                    }
+                    if (rr >= 2) {
+                        const int r = rr - 2;
+                        const uint32_t qlo = __builtin_amdgcn_perm(x[r + 1][j + 2], x[r][j + 2], 0x05040100u);
+                        const uint32_t qhi = __builtin_amdgcn_perm(x[r + 1][j + 2], x[r][j + 2], 0x07060302u);
+#pragma unroll
+                        for (int a = 0; a < 3; ++a) {
+                            float &c0 = acc[SL[a]][r][j][0], &c1 = acc[SL[a]][r][j][1];
+                            c0 = O::dot2(qlo, taps.p2[a][0], c0);
+                            c1 = O::dot2(qhi, taps.p2[a][1], c1);
+                            c0 = O::dot2(x[rr][j + 2], taps.s2[a][0], c0);
+                            c1 = O::dot2(x[rr][j + 2], taps.s2[a][1], c1);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int dh = 0; dh < 3; ++dh) {
+                        const int r = rr - dh;
+                        if (r < 0 || r >= HR) continue;
+#pragma unroll
+                        for (int a = 0; a < 3; ++a)
+#pragma unroll
+                            for (int e = 0; e < 3; ++e) {
+                                const int tap = (a * 3 + dh) * 3 + e;
+                                float &c0 = acc[SL[a]][r][j][0], &c1 = acc[SL[a]][r][j][1];
+                                const bool fresh = tap == 0;   // first term of output slice ti + PT
+                                c0 = __builtin_fmaf(taps.w[tap][0], x[rr][j + e].x, fresh ? 0.f : c0);
+                                c1 = __builtin_fmaf(taps.w[tap][1], x[rr][j + e].y, fresh ? 0.f : c1);
+                            }
+                    }
+                }
+            }
     }
 
     // Step P of the march (ti = 6m + P).  Input slice ti contributes tap
@@ -243,36 +297,26 @@ struct VisualTile {
     template <int P, bool EDGE>
     __device__ __forceinline__ void step(int ti, bool active) {
         const bool live = (!HIST || ti >= ti0) && ti < gt;   // steps before ti0 only align the march
+        // Slice ti has landed once every wave's direct-to-LDS loads of it have
+        // retired: wait for them explicitly (the compiler does not track them
+        // across the loop back-edge), then meet at the barrier, which also ends
+        // every read of slice ti-1.  The wait covers this wave's output stores
+        // of the previous step too; they are issued before the slice loads, so
+        // they are mostly done by the time the loads are.
         if (live) {
-            // Slice ti has landed once every wave's direct-to-LDS loads of it
-            // have retired: wait for them explicitly (the compiler does not
-            // track them across the loop back-edge), then meet at the barrier,
-            // which also ends every read of slice ti-1.
             __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
-            __syncthreads();
-            read_window<EDGE>(ti);
-            if (ti + 1 < gt) issue_slice(ti + 1);
+            lds_barrier();
+            read_window(ti);
         }
         flush<P, EDGE>(ti + PT - 3, active);
-        if (live && active) {
-            float *a0[3], *a1[3];
-#pragma unroll
-            for (int j = 0; j < WR; ++j) {
-#pragma unroll
-                for (int a = 0; a < 3; ++a) {
-                    constexpr int base = P + PT;
-                    const int slot = ((base - a) % 3 + 3) % 3;
-                    a0[a] = &acc[slot][j][0];
-                    a1[a] = &acc[slot][j][1];
-                }
-                O::apply(taps, x, j, a0, a1);
-            }
-        }
+        if (live && ti + 1 < gt) issue_slice(ti + 1, EDGE ? inb : ~0u);
+        if (live && active) compute<P>();
     }
 
     template <bool EDGE>
     __device__ void march(bool active) {
-        issue_slice(HIST ? ti0 : 0);
+        zero_outside<EDGE>();
+        issue_slice(HIST ? ti0 : 0, EDGE ? inb : ~0u);
         // empty steps past the last slice flush the last output slices; with
         // history the march starts at -6 so that step<P> still sees ti = P mod 6
         const int last = gt + 2 - PT;
@@ -317,7 +361,7 @@ __device__ void visual_block(const ConvArgs &a, const Layout &L, int s, int blk,
     v.gw = a.gw;
     v.h0 = hg * HR;
     v.w0 = wrun * WR;
-    v.h = v.h0 + wave;
+    v.wj = v.w0 + JW * wave;
     v.slice_bytes = (unsigned)(a.gh * a.gw) * (unsigned)v.rowb;
     const size_t bbytes = (size_t)a.T * v.rowb;   // < 4 GiB, checked on the host
     v.rx = __builtin_amdgcn_make_buffer_rsrc(
@@ -333,26 +377,32 @@ __device__ void visual_block(const ConvArgs &a, const Layout &L, int s, int blk,
             kBufWord3);
     }
     // tile position p of load instruction k: k * PPI + lane / LPP; positions
-    // outside the grid load a clamped in-grid token that is never read
+    // outside the grid are not loaded (their offsets are clamped into the grid
+    // all the same)
     const unsigned chan = (unsigned)(cb * V::POS) + (unsigned)(lane % V::LPP) * 16u;
+    v.inb = 0u;
 #pragma unroll
     for (int i = 0; i < V::NIW; ++i) {
         const int k = wave + 4 * i;
         const int p = k * V::PPI + lane / V::LPP;
-        const int hh = min(max(v.h0 - 1 + p / TC, 0), a.gh - 1);
-        const int ww = min(max(v.w0 - 1 + p % TC, 0), a.gw - 1);
+        const int hu = v.h0 - 1 + p / TC, wu = v.w0 - 1 + p % TC;
+        const int hh = min(max(hu, 0), a.gh - 1);
+        const int ww = min(max(wu, 0), a.gw - 1);
         v.dma_off[i] = (unsigned)(a.n_text + hh * a.gw + ww) * (unsigned)v.rowb + chan;
+        if (hu == hh && wu == ww) v.inb |= 1u << i;
     }
-    v.out_off = (unsigned)(a.n_text + min(v.h, a.gh - 1) * a.gw + v.w0) * (unsigned)v.rowb +
-                (unsigned)((ok ? c0 : 0) * (int)sizeof(T));
+    v.out_off = (unsigned)(a.n_text + v.h0 * a.gw + v.wj) * (unsigned)v.rowb + (unsigned)((ok ? c0 : 0) * (int)sizeof(T));
     Ops<T>::load_taps(v.taps, static_cast<const T *>(a.wv[s]), ok ? c0 : 0, ok);
 #pragma unroll
-    for (int r = 0; r < 3; ++r)
+    for (int sl = 0; sl < 3; ++sl)
 #pragma unroll
-        for (int j = 0; j < WR; ++j) v.acc[r][j][0] = v.acc[r][j][1] = 0.f;
-    // every wave takes part in the loads and barriers; rows past the grid and
-    // lanes past the last channel compute nothing and store nothing
-    const bool active = ok && v.h < a.gh;
+        for (int r = 0; r < HR; ++r)
+#pragma unroll
+            for (int j = 0; j < JW; ++j) v.acc[sl][r][j][0] = v.acc[sl][r][j][1] = 0.f;
+    // every wave takes part in the loads and barriers; waves whose positions
+    // all lie past the grid and lanes past the last channel compute nothing and
+    // store nothing
+    const bool active = ok && v.wj < a.gw;
     if (v.h0 >= 1 && v.h0 + HR < a.gh && v.w0 >= 1 && v.w0 + WR < a.gw)
         v.template march<false>(active);
     else
