@@ -69,10 +69,18 @@ template <> struct Ops<bf16_t> {
     struct Taps {
         uint32_t pr[3][3][2], p2[3][2], s2[3][2];
     };
+    // c0 (even, a valid channel) and c0+1 hold 54 consecutive taps = 27 dwords;
+    // all are loaded at once, without conditions (!ok lanes zero them after)
     __device__ __forceinline__ static void load_taps(Taps &tp, const bf16_t *wv, int c0, bool ok) {
-        const uint16_t *p = reinterpret_cast<const uint16_t *>(wv);
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(wv) + (size_t)c0 * 27 / 2;
+        uint32_t d[27];
+#pragma unroll
+        for (int i = 0; i < 27; ++i) d[i] = p[i];
+#pragma unroll
+        for (int i = 0; i < 27; ++i) d[i] = ok ? d[i] : 0u;
         auto w = [&](int ch, int a, int dh, int e) -> uint32_t {
-            return ok ? (uint32_t)p[(size_t)(c0 + ch) * 27 + (a * 3 + dh) * 3 + e] : 0u;
+            const int i = ch * 27 + (a * 3 + dh) * 3 + e;
+            return (i & 1) ? d[i >> 1] >> 16 : d[i >> 1] & 0xffffu;
         };
 #pragma unroll
         for (int a = 0; a < 3; ++a)
@@ -115,11 +123,18 @@ template <> struct Ops<float> {
     struct Taps {
         float w[27][2];
     };
+    // channels c0 (a valid channel) and c0+1: 54 consecutive taps, loaded without conditions
     __device__ __forceinline__ static void load_taps(Taps &tp, const float *wv, int c0, bool ok) {
+        const float *p = wv + (size_t)c0 * 27;
 #pragma unroll
         for (int tap = 0; tap < 27; ++tap) {
-            tp.w[tap][0] = ok ? wv[(size_t)c0 * 27 + tap] : 0.f;
-            tp.w[tap][1] = ok ? wv[(size_t)(c0 + 1) * 27 + tap] : 0.f;
+            tp.w[tap][0] = p[tap];
+            tp.w[tap][1] = p[27 + tap];
+        }
+#pragma unroll
+        for (int tap = 0; tap < 27; ++tap) {
+            tp.w[tap][0] = ok ? tp.w[tap][0] : 0.f;
+            tp.w[tap][1] = ok ? tp.w[tap][1] : 0.f;
         }
     }
     __device__ __forceinline__ static XT lds_read(const char *p) { return *reinterpret_cast<const float2 *>(p); }
@@ -432,16 +447,17 @@ __device__ void text_item(const ConvArgs &a, const Layout &L, int s, int item, i
     }
     const int i0 = trun * TR;
     float xin[TR + 3][2];
+    // all TR + 3 loads at once from clamped (valid) tokens; tokens outside the
+    // text are zero (the causal padding, and the end of the text)
+    typename O::XT raw[TR + 3];
+#pragma unroll
+    for (int m = 0; m < TR + 3; ++m) raw[m] = O::load(x + (size_t)min(max(i0 - 3 + m, 0), a.n_text - 1) * rowb);
 #pragma unroll
     for (int m = 0; m < TR + 3; ++m) {
         const int src = i0 - 3 + m;
-        if (src >= 0 && src < a.n_text) {
-            const typename O::XT v = O::load(x + (size_t)src * rowb);
-            xin[m][0] = O::lo(v);
-            xin[m][1] = O::hi(v);
-        } else {
-            xin[m][0] = xin[m][1] = 0.f;
-        }
+        const bool in = src >= 0 && src < a.n_text;
+        xin[m][0] = in ? O::lo(raw[m]) : 0.f;
+        xin[m][1] = in ? O::hi(raw[m]) : 0.f;
     }
 #pragma unroll
     for (int m = 0; m < TR; ++m) {

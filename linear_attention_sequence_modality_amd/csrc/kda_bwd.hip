@@ -213,7 +213,7 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
     const size_t tok0 = ((size_t)b * a.T + t0) * H + h;   // token t0, head h
     const T *q = static_cast<const T *>(a.q), *k = static_cast<const T *>(a.k), *v = static_cast<const T *>(a.v);
     const T *al = static_cast<const T *>(a.alpha), *be = static_cast<const T *>(a.beta);
-    float *lw = &tA[0][0];   // the panel area as scratch: 2 * kPanel * kPs floats
+    float *lw = &tA[0][0];   // the panel area as scratch: 2 * kPanel * kPs floats (tB follows tA)
     stage_rows(c.V, v + tok0 * DV, (size_t)H * DV, BC, DV, nr);
     stage_rows(lw, al + tok0 * DK, (size_t)H * DK, BC, DK, nr);   // alpha (rows past the end: 0, unused)
     if (tid < BC) c.beta[tid] = tid < nr ? ld(be + tok0 + (size_t)tid * H) : 0.f;
@@ -378,7 +378,10 @@ __device__ Rec rec_at(const KdaBwdArgs &a, int bh, int n) {
 
 template <typename T>
 __global__ __launch_bounds__(BT) void bwd_prep_kernel(KdaBwdArgs a) {
-    __shared__ __attribute__((aligned(16))) float tA[kPanel][kPs], tB[kPanel][kPs];
+    // one panel area: the two panels of the products, and scratch of 2 kPanel rows elsewhere
+    __shared__ __attribute__((aligned(16))) float panels[2 * kPanel][kPs];
+    float(*tA)[kPs] = panels;
+    float(*tB)[kPs] = panels + kPanel;
     float *rest;
     const ChunkMats c = carve(a.scratch + (size_t)blockIdx.x * a.scratch_floats, a.dk, a.dv, &rest);
     const int items = a.B * a.H * a.n_chunks;
@@ -636,7 +639,10 @@ __global__ __launch_bounds__(BT) void bwd_ordered_kernel(KdaBwdArgs a, int n_sta
 // Gradients of one chunk's tokens.
 template <typename T>
 __global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
-    __shared__ __attribute__((aligned(16))) float tA[kPanel][kPs], tB[kPanel][kPs];
+    // one panel area: the two panels of the products, and scratch of 2 kPanel rows elsewhere
+    __shared__ __attribute__((aligned(16))) float panels[2 * kPanel][kPs];
+    float(*tA)[kPs] = panels;
+    float(*tB)[kPs] = panels + kPanel;
     const int DK = a.dk, DV = a.dv, H = a.H, tid = threadIdx.x;
     float *s;
     const ChunkMats base = carve(a.scratch + (size_t)blockIdx.x * a.scratch_floats, DK, DV, &s);

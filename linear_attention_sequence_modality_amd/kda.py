@@ -133,6 +133,25 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _torch_stream(stream, device) -> Optional["torch.cuda.Stream"]:
+    if stream is None or isinstance(stream, torch.cuda.Stream):
+        return stream
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.ExternalStream(handle, device=device)
+
+
+def _hand_over(stream, device, *tensors):
+    """Tensors a wrapper allocated (on the current stream) and handed to kernels enqueued on
+    ``stream``: when that is another stream, tell the caching allocator, so that their memory
+    is not given to a new allocation before that stream's work on them is done."""
+    s = _torch_stream(stream, device)
+    if s is None or s.cuda_stream == torch.cuda.current_stream(device).cuda_stream:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(s)
+
+
 def _check(t: torch.Tensor, name: str, dtype=None):
     if not t.is_cuda:
         raise ValueError("%s must be a device tensor" % name)
@@ -174,9 +193,11 @@ def kda_conv_forward(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: t
         _check(w_vis[i], "w_vis[%d]" % i, dt)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
+    made = [t is None for t in (q_out, k_out, v_out)]
     q_out = torch.empty_like(q) if q_out is None else q_out
     k_out = torch.empty_like(k) if k_out is None else k_out
     v_out = torch.empty_like(v) if v_out is None else v_out
+    _hand_over(stream, q.device, *[t for t, m in zip((q_out, k_out, v_out), made) if m])
     wt = (ctypes.c_void_p * 3)(*[w.data_ptr() for w in w_text])
     wv = (ctypes.c_void_p * 3)(*[w.data_ptr() for w in w_vis])
     if history is None:
@@ -216,11 +237,13 @@ def kda_forward(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: torch.
     for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
         if t is not None:
             _check(t, nm, torch.float32)
+    made_o, made_ws = o is None, workspace is None
     o = torch.empty_like(v) if o is None else o
     _check(o, "o", dt)
     need = kda_forward_workspace_size(desc, B, H, dk, dv, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _hand_over(stream, q.device, o if made_o else None, workspace if made_ws else None)
     rc = lib.kda_forward(ctypes.byref(desc), B, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k),
                          _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(final_state),
                          _ptr(o), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -329,11 +352,13 @@ def kda_forward_varlen(descs: Sequence[KdaStreamDesc], q: torch.Tensor, k: torch
     for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
         if t is not None:
             _check(t, nm, torch.float32)
+    made_o, made_ws = o is None, workspace is None
     o = torch.empty_like(v) if o is None else o
     _check(o, "o", dt)
     need = kda_forward_varlen_workspace_size(descs, H, dk, dv, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _hand_over(stream, q.device, o if made_o else None, workspace if made_ws else None)
     rc = lib.kda_forward_varlen(_desc_array(descs), len(descs), H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k),
                                 _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(final_state),
                                 _ptr(o), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -361,9 +386,11 @@ def kda_conv_forward_varlen(descs: Sequence[KdaStreamDesc], q: torch.Tensor, k: 
     total = sum(d.n_text + d.grid_t * d.grid_h * d.grid_w for d in descs)
     if q.numel() != total * H * dk or k.numel() != total * H * dk or v.numel() != total * H * dv:
         raise ValueError("q, k, v must hold the %d tokens of the streams" % total)
+    made = [t is None for t in (q_out, k_out, v_out)]
     q_out = torch.empty_like(q) if q_out is None else q_out
     k_out = torch.empty_like(k) if k_out is None else k_out
     v_out = torch.empty_like(v) if v_out is None else v_out
+    _hand_over(stream, q.device, *[t for t, m in zip((q_out, k_out, v_out), made) if m])
     wt = (ctypes.c_void_p * 3)(*[w.data_ptr() for w in w_text])
     wv = (ctypes.c_void_p * 3)(*[w.data_ptr() for w in w_vis])
     rc = lib.kda_conv_forward_varlen(_desc_array(descs), len(descs), H, dk, dv, _dtype_code(dt), _ptr(q),
@@ -400,8 +427,10 @@ def kda_backward(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: torch
            "d_initial_state": (torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device)
                                if want_d_initial_state else None)}
     need = kda_backward_workspace_size(desc, B, H, dk, dv, dt)
+    made_ws = workspace is None
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _hand_over(stream, q.device, *out.values(), workspace if made_ws else None)
     rc = lib.kda_backward(ctypes.byref(desc), B, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v),
                           _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(d_o), _ptr(d_final_state),
                           _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]),
@@ -430,6 +459,7 @@ def kda_conv_backward(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: 
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
            "dw_text": tuple(torch.empty(w.shape, dtype=torch.float32, device=q.device) for w in w_text),
            "dw_vis": tuple(torch.empty(w.shape, dtype=torch.float32, device=q.device) for w in w_vis)}
+    _hand_over(stream, q.device, out["dq"], out["dk"], out["dv"], *out["dw_text"], *out["dw_vis"])
     arr = lambda ts: (ctypes.c_void_p * 3)(*[t.data_ptr() for t in ts])
     rc = lib.kda_conv_backward(ctypes.byref(desc), B, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v),
                                arr(w_text), arr(w_vis), _ptr(d_q_out), _ptr(d_k_out), _ptr(d_v_out),
@@ -456,8 +486,10 @@ def mla_attention_forward(q_nope: torch.Tensor, q_dir: torch.Tensor, k_nope: tor
             or tuple(k_dir.shape) != (B, T, dr) or tuple(v.shape[:3]) != (B, T, H)):
         raise ValueError("q_nope/k_nope [B,T,H,dn], q_dir [B,T,H,dr], k_dir [B,T,dr], v [B,T,H,dv] expected")
     scale = 1.0 / float(dn + dr) ** 0.5 if scale is None else float(scale)
+    made_o = o is None
     o = torch.empty_like(v) if o is None else o
     _check(o, "o", dt)
+    _hand_over(stream, q_nope.device, o if made_o else None)
     rc = lib.mla_attention_forward(B, T, H, dn, dr, dv, _dtype_code(dt), _ptr(q_nope), _ptr(q_dir), _ptr(k_nope),
                                    _ptr(k_dir), _ptr(v), ctypes.c_float(scale), _ptr(o), _stream(stream))
     if rc != KDA_OK:

@@ -344,6 +344,30 @@ def test_graph_capture_replays_match_eager():
             assert torch.equal(x, r), "replay %d differs from eager" % rep
 
 
+@pytest.mark.timeout(120)
+def test_wrapper_allocations_on_a_side_stream():
+    """The binding allocates o, the conv outputs and the workspace on the current stream;
+    launched on a side stream that is not made current, the kernels must still own that
+    memory until they are done.  Allocations on the current stream right after the call
+    (which would reuse freed blocks) must not disturb the result."""
+    cfg = WORKLOAD["proxy_image_1024px"].with_(name="side_stream", B=2)
+    say("case side stream T=%d B=%d" % (cfg.T, cfg.B))
+    dev = to_dev(make_inputs(cfg))
+    d = desc_of(cfg)
+    ref = kda.conv_kda_forward(d, dev)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    got = kda.conv_kda_forward(d, dev, stream=side)
+    churn = []
+    for _ in range(8):   # fill freed blocks on the current stream with NaN
+        churn.append(torch.full((64 << 20,), float("nan"), device="cuda"))
+    side.synchronize()
+    torch.cuda.synchronize()
+    del churn
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
+
+
 # ---- hygiene -----------------------------------------------------------------------
 
 @pytest.mark.timeout(120)
