@@ -37,6 +37,7 @@ KERNEL_SOURCES = {
     "chunks": ("kda.hip", "kda_ws.h", "mfma.h", "common.h", "launch.h"),
     "scan": ("kda_scan.hip", "kda_ws.h", "mfma.h", "common.h", "launch.h"),
     "mla": ("mla.hip", "mfma.h", "common.h", "launch.h"),
+    "mla_latent": ("mla_proj.hip", "mfma.h", "common.h", "launch.h"),
     "kda_backward": ("kda_bwd.hip", "mfma.h", "common.h", "launch.h"),
 }
 # "kda_backward" is the sum over its three launches (records, ordered passes, gradients) per call.
@@ -189,52 +190,77 @@ def mla_flops(cfg) -> float:
 
 
 def mla_cpu_baseline(cfg, rows: int) -> dict:
-    """The fp64 MLA oracle, as it stands, on ``rows`` query rows of every head of the same stream."""
+    """The fp64 MLA oracle, as it stands, on the same layer: the latent projections of every
+    token, then attention for ``rows`` query rows of every head."""
     import numpy as np
 
     from oracle import mla as oracle_mla
-    from linear_attention_sequence_modality_amd.inputs import make_mla_inputs
+    from linear_attention_sequence_modality_amd.inputs import make_mla_latent_inputs
 
-    inp = make_mla_inputs(cfg)
+    inp = make_mla_latent_inputs(cfg)
     sel = np.linspace(0, cfg.T - 1, rows).astype(int).tolist()
     t0 = time.perf_counter()
-    oracle_mla.mla_attention(inp["q_nope"], inp["q_dir"], inp["k_nope"], inp["k_dir"], inp["v"], rows=sel)
+    oracle_mla.mla_layer(inp["x"], inp["q_nope"], inp["q_dir"], inp["w_dkv"], inp["w_kr"], inp["w_uk"], inp["w_uv"],
+                         rows=sel)
     dt = time.perf_counter() - t0
     return {"value": cfg.B * rows / dt, "unit": "tokens/s", "cores": int(os.environ.get("OMP_NUM_THREADS", "0")) or
             os.cpu_count(), "kind": "oracle",
-            "sample": "fp64 numpy oracle (scores, softmax, weighted values per head) on %d of the %d query "
-                      "rows of each of the %d heads, against all %d keys; %.1f s wall; cores = the BLAS "
-                      "threads numpy may use" % (rows, cfg.T, cfg.H, cfg.T, dt)}
+            "sample": "fp64 numpy oracle: the latent projections of all %d tokens, then scores, softmax and "
+                      "weighted values for %d of the query rows of each of the %d heads against all keys; "
+                      "%.1f s wall; cores = the BLAS threads numpy may use" % (cfg.B * cfg.T, rows, cfg.H, dt)}
+
+
+def mla_latent_flops(cfg) -> float:
+    """Matrix-core flops of the latent projections: x W_dkv^T, x W_kr^T, c W_uk^T, c W_uv^T."""
+    rows = cfg.B * cfg.T
+    return 2.0 * rows * (cfg.model_width * (cfg.latent_width + cfg.d_dir)
+                         + cfg.latent_width * cfg.H * (cfg.d_nope + cfg.dv))
 
 
 def mla_main(args, torch) -> int:
-    """One step = one mla_attention_forward launch over the whole stream."""
+    """One step = the MLA token mixer from hidden states: mla_latent_forward (two launches)
+    then mla_attention_forward, each timed with HIP events on the launch stream."""
     from linear_attention_sequence_modality_amd import kda
-    from linear_attention_sequence_modality_amd.inputs import MLA_WORKLOAD, make_mla_inputs
+    from linear_attention_sequence_modality_amd.inputs import MLA_WORKLOAD, make_mla_latent_inputs
 
     cfg = MLA_WORKLOAD[args.mla_workload]
     torch.cuda.set_device(0)
-    dev = {k: v.cuda() for k, v in make_mla_inputs(cfg).items()}
-    x = [dev[k] for k in ("q_nope", "q_dir", "k_nope", "k_dir", "v")]
-    o = torch.empty_like(dev["v"])
+    dev = {k: v.cuda() for k, v in make_mla_latent_inputs(cfg).items()}
+    w = [dev[k] for k in ("w_dkv", "w_kr", "w_uk", "w_uv")]
+    lat = [torch.empty(cfg.B, cfg.T, cfg.latent_width, dtype=torch.bfloat16, device="cuda"),
+           torch.empty(cfg.B, cfg.T, cfg.d_dir, dtype=torch.bfloat16, device="cuda"),
+           torch.empty(cfg.B, cfg.T, cfg.H, cfg.d_nope, dtype=torch.bfloat16, device="cuda"),
+           torch.empty(cfg.B, cfg.T, cfg.H, cfg.dv, dtype=torch.bfloat16, device="cuda")]
+    o = torch.empty_like(lat[3])
     stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        kda.mla_latent_forward(dev["x"], *w, cfg.H, outputs=lat, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        kda.mla_attention_forward(dev["q_nope"], dev["q_dir"], lat[2], lat[1], lat[3], o=o, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
     for _ in range(args.warmup):
-        kda.mla_attention_forward(*x, o=o, stream=stream)
+        step()
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for e in events:
-        e[0].record(stream)
-        kda.mla_attention_forward(*x, o=o, stream=stream)
-        e[1].record(stream)
+        step(e)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    fl = mla_flops(cfg)
-    tfs = fl / (ms * 1e-3) / 1e12
+    ms_lat = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    ms_att = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    fl_att, fl_lat = mla_flops(cfg), mla_latent_flops(cfg)
+    tfs_att = fl_att / (ms_att * 1e-3) / 1e12
+    tfs_lat = fl_lat / (ms_lat * 1e-3) / 1e12
     result = {
-        "metric": "MLA attention core forward tokens/s at 1 GPU; % of bf16-MFMA roofline",
+        "metric": "MLA token mixer forward (latent projections + attention) tokens/s at 1 GPU; "
+                  "% of bf16-MFMA roofline",
         "value": round(cfg.B * cfg.T * args.steps / elapsed, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -246,12 +272,18 @@ def mla_main(args, torch) -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "H": cfg.H, "d_nope": cfg.d_nope,
-                   "d_dir": cfg.d_dir, "dv": cfg.dv, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "mla_attention", "achieved": round(tfs, 1),
-                     "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
-                     "traffic": measured_traffic(cfg.name, "mla"), "flop_per_launch": fl,
-                     "mfma_flop_counted": measured_mfma_flops(cfg.name, "mla"), "us": round(ms * 1e3, 1)},
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "H": cfg.H, "d_model": cfg.model_width,
+                   "d_c": cfg.latent_width, "d_nope": cfg.d_nope, "d_dir": cfg.d_dir, "dv": cfg.dv,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "mla_attention", "achieved": round(tfs_att, 1),
+                     "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs_att / MFMA_BF16_PEAK_TFS, 4),
+                     "traffic": measured_traffic(cfg.name, "mla"), "flop_per_launch": fl_att,
+                     "mfma_flop_counted": measured_mfma_flops(cfg.name, "mla"), "us": round(ms_att * 1e3, 1)},
+        "kernels": {"latent": {"us": round(ms_lat * 1e3, 1), "flop": fl_lat, "TFLOP/s": round(tfs_lat, 1),
+                               "frac_mfma_bf16": round(tfs_lat / MFMA_BF16_PEAK_TFS, 4),
+                               "traffic": measured_traffic(cfg.name, "mla_latent")},
+                    "attention": {"us": round(ms_att * 1e3, 1), "flop": fl_att, "TFLOP/s": round(tfs_att, 1),
+                                  "frac_mfma_bf16": round(tfs_att / MFMA_BF16_PEAK_TFS, 4)}},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = mla_cpu_baseline(cfg, args.mla_cpu_rows)

@@ -286,7 +286,7 @@ int kda_backward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_
  * Attention core of the MLA layers that fill one of every four token-mixer
  * layers (Chimera pages, paper.rainbus.top, prerequisites section, the
  * Multi-head Latent Attention paragraph): keys and values are decompressed
- * from a latent by plain projections (not part of this call), and every head
+ * from a latent by plain projections (mla_latent_forward), and every head
  * also sees one key part shared by all heads (K_direct).  Full bidirectional
  * softmax attention within each stream: for stream b, head h, query i,
  *   s_j = scale * (q_nope[b,i,h] . k_nope[b,j,h] + q_dir[b,i,h] . k_dir[b,j])
@@ -303,6 +303,32 @@ int mla_attention_forward(int B, int T, int H, int d_nope, int d_dir, int dv, kd
                           const void *q_nope, const void *q_dir, const void *k_nope,
                           const void *k_dir, const void *v, float scale, void *o,
                           void *hip_stream);
+
+/*
+ * Latent projections of the MLA layers (Chimera pages, paper.rainbus.top,
+ * prerequisites section, the Multi-head Latent Attention paragraph): the
+ * hidden state is compressed into a low-dimensional latent, keys and values
+ * are decompressed from it, and the key part shared by all heads (K_direct)
+ * is projected from the hidden state beside the latent.  With every weight
+ * stored as a linear layer's [out_features, in_features] (row-major):
+ *   c      = x W_dkv^T     x [rows, d_model], w_dkv [d_c, d_model]  -> c [rows, d_c]
+ *   k_dir  = x W_kr^T      w_kr [d_dir, d_model]                    -> k_dir [rows, d_dir]
+ *   k_nope = c W_uk^T      w_uk [H * d_nope, d_c]                   -> k_nope [rows, H, d_nope]
+ *   v      = c W_uv^T      w_uv [H * dv, d_c]                       -> v [rows, H, dv]
+ * rows = B * T tokens; k_nope, k_dir and v are then the inputs of
+ * mla_attention_forward.  The latent c is written (bf16) and the
+ * decompression reads it back, as the layer's KV cache would hold it.
+ * Supported: KDA_BF16 (fp32 accumulation, every output rounded to bf16),
+ * d_model a multiple of 32; d_c, d_dir, H * d_nope and H * dv multiples of
+ * 64; anything else is KDA_ERR_UNSUPPORTED.  Two launches on hip_stream; the
+ * caller owns every buffer.
+ * Errors: KDA_ERR_INVALID_ARG for a negative or zero size (rows = 0 is a
+ * no-op), a NULL or not 16-byte aligned pointer, or an output overlapping an
+ * input or another output.
+ */
+int mla_latent_forward(int64_t rows, int d_model, int d_c, int d_dir, int H, int d_nope, int dv,
+                       kda_dtype dtype, const void *x, const void *w_dkv, const void *w_kr, const void *w_uk,
+                       const void *w_uv, void *c, void *k_dir, void *k_nope, void *v, void *hip_stream);
 
 /* Static, human-readable text for a status code. */
 const char *kda_status_string(int status);

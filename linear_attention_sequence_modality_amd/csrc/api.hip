@@ -573,6 +573,62 @@ int mla_attention_forward(int B, int T, int H, int d_nope, int d_dir, int dv, kd
                                                                                                : KDA_ERR_HIP;
 }
 
+int mla_latent_forward(int64_t rows, int d_model, int d_c, int d_dir, int H, int d_nope, int dv,
+                       kda_dtype dtype, const void *x, const void *w_dkv, const void *w_kr, const void *w_uk,
+                       const void *w_uv, void *c, void *k_dir, void *k_nope, void *v, void *hip_stream) {
+    if (rows < 0 || d_model < 1 || d_c < 1 || d_dir < 1 || H < 1 || d_nope < 1 || dv < 1)
+        return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
+    if (dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    // the projection kernel's tiling: contraction in steps of 32, output columns in tiles of 64
+    if (d_model % 32 || d_c % 64 || d_dir % 64 || ((int64_t)H * d_nope) % 64 || ((int64_t)H * dv) % 64)
+        return KDA_ERR_UNSUPPORTED;
+    const int64_t nk = (int64_t)H * d_nope, nv = (int64_t)H * dv;
+    if (nk + nv > (1 << 20) || d_model > (1 << 20) || d_c > (1 << 20) ||
+        (rows + 255) / 256 * ((nk + nv) / 64) >= kMaxTokens)
+        return KDA_ERR_UNSUPPORTED;
+    const size_t es = 2, R = (size_t)rows;
+    const void *ins[5] = {x, w_dkv, w_kr, w_uk, w_uv};
+    const size_t in_bytes[5] = {R * d_model * es, (size_t)d_c * d_model * es, (size_t)d_dir * d_model * es,
+                                (size_t)nk * d_c * es, (size_t)nv * d_c * es};
+    void *outs[4] = {c, k_dir, k_nope, v};
+    const size_t out_bytes[4] = {R * d_c * es, R * d_dir * es, R * nk * es, R * nv * es};
+    for (int i = 0; i < 5; ++i)
+        if (!ins[i] || !aligned16(ins[i])) return KDA_ERR_INVALID_ARG;
+    for (int i = 0; i < 4; ++i) {
+        if (!outs[i] || !aligned16(outs[i])) return KDA_ERR_INVALID_ARG;
+        const Range ro = range_of(outs[i], out_bytes[i]);
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(ro, range_of(ins[j], in_bytes[j]))) return KDA_ERR_INVALID_ARG;
+        for (int j = 0; j < i; ++j)
+            if (overlaps(ro, range_of(outs[j], out_bytes[j]))) return KDA_ERR_INVALID_ARG;
+    }
+    if (rows == 0) return KDA_OK;
+    const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    kdaconv::MlaProjArgs down;
+    down.X = x;
+    down.W1 = w_dkv;
+    down.W2 = w_kr;
+    down.Y1 = c;
+    down.Y2 = k_dir;
+    down.M = rows;
+    down.K = d_model;
+    down.N1 = d_c;
+    down.N2 = d_dir;
+    if (kdaconv::launch_mla_proj(down, st) != hipSuccess) return KDA_ERR_HIP;
+    kdaconv::MlaProjArgs up;
+    up.X = c;
+    up.W1 = w_uk;
+    up.W2 = w_uv;
+    up.Y1 = k_nope;
+    up.Y2 = v;
+    up.M = rows;
+    up.K = d_c;
+    up.N1 = (int)nk;
+    up.N2 = (int)nv;
+    return kdaconv::launch_mla_proj(up, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 // ---- backward ----------------------------------------------------------------
 
 }  // extern "C"

@@ -142,4 +142,15 @@ struct MlaArgs {
 };
 hipError_t launch_mla_attention(const MlaArgs &a, hipStream_t stream);
 
+// Y = X W^T for two weight/output pairs: X [M, K]; W1 [N1, K] -> Y1 [M, N1];
+// W2 [N2, K] -> Y2 [M, N2]; bf16, row-major.  K % 32 == 0, N1 % 64 == 0,
+// N2 % 64 == 0, 16-byte aligned rows.
+struct MlaProjArgs {
+    const void *X, *W1, *W2;
+    void *Y1, *Y2;
+    int64_t M;
+    int K, N1, N2;
+};
+hipError_t launch_mla_proj(const MlaProjArgs &a, hipStream_t stream);
+
 }  // namespace kdaconv

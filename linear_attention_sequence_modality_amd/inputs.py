@@ -147,7 +147,10 @@ class MlaConfig:
     """Attention-core shapes of one MLA layer over a token stream of T tokens.
 
     Per head: a d_nope-wide key part decompressed from the latent, a d_dir-wide
-    key part shared by all heads (K_direct), and dv-wide values.
+    key part shared by all heads (K_direct), and dv-wide values.  The latent
+    path maps d_model-wide hidden states to a d_c-wide latent; d_c = d_model / 4
+    is a reading (the pages fix the compression ratio across scales but do not
+    state it), d_model = H * 128 the layer widths of the pages' models.
     """
 
     name: str
@@ -158,6 +161,16 @@ class MlaConfig:
     d_dir: int = 64
     dv: int = 128
     seed: int = 0
+    d_model: int = 0      # 0: H * 128
+    d_c: int = 0          # 0: d_model / 4
+
+    @property
+    def model_width(self) -> int:
+        return self.d_model or self.H * 128
+
+    @property
+    def latent_width(self) -> int:
+        return self.d_c or self.model_width // 4
 
     def with_(self, **kw) -> "MlaConfig":
         return replace(self, **kw)
@@ -184,3 +197,26 @@ def make_mla_inputs(cfg: MlaConfig, seed: Optional[int] = None) -> Dict[str, tor
            "k_dir": rng.standard_normal((B, T, cfg.d_dir), dtype=f32),
            "v": rng.standard_normal((B, T, H, cfg.dv), dtype=f32)}
     return {name: torch.from_numpy(a).to(torch.bfloat16) for name, a in out.items()}
+
+
+def make_mla_latent_inputs(cfg: MlaConfig, seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Seeded bf16 CPU tensors of one MLA layer from hidden states: x [B,T,d_model] ~ N(0, 1);
+    linear-layer weights w_dkv [d_c, d_model], w_kr [d_dir, d_model], w_uk [H*d_nope, d_c],
+    w_uv [H*dv, d_c], each ~ N(0, 1/fan_in) so that every projection stays of unit scale;
+    queries q_nope [B,T,H,d_nope], q_dir [B,T,H,d_dir] ~ N(0, 1).  Drawn in that order in fp32
+    and rounded to bf16."""
+    rng = np.random.default_rng((cfg.seed if seed is None else seed) + 1000)
+    B, T, H = cfg.B, cfg.T, cfg.H
+    dm, dc = cfg.model_width, cfg.latent_width
+    f32 = np.float32
+
+    def w(rows, fan_in):
+        return (rng.standard_normal((rows, fan_in), dtype=f32) / np.sqrt(fan_in)).astype(f32)
+
+    out = {"x": rng.standard_normal((B, T, dm), dtype=f32),
+           "w_dkv": w(dc, dm), "w_kr": w(cfg.d_dir, dm),
+           "w_uk": w(H * cfg.d_nope, dc), "w_uv": w(H * cfg.dv, dc),
+           "q_nope": rng.standard_normal((B, T, H, cfg.d_nope), dtype=f32),
+           "q_dir": rng.standard_normal((B, T, H, cfg.d_dir), dtype=f32)}
+    return {name: torch.from_numpy(a).to(torch.bfloat16) for name, a in out.items()}
+

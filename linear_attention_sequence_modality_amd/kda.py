@@ -30,7 +30,7 @@ EXPORTED_SYMBOLS = ("kda_conv_forward", "kda_conv_forward_stream", "kda_forward_
                     "kda_forward_chunks", "kda_forward_scan", "kda_forward_varlen_workspace_size",
                     "kda_forward_varlen", "kda_conv_forward_varlen", "mla_attention_forward",
                     "kda_backward_workspace_size", "kda_backward", "kda_conv_backward", "kda_status_string",
-                    "kda_forward_noalloc")
+                    "kda_forward_noalloc", "mla_latent_forward")
 KDA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -99,6 +99,8 @@ def load_library():
                                       ctypes.POINTER(vp), vp]
     lib.mla_attention_forward.restype = i32
     lib.mla_attention_forward.argtypes = [i32] * 7 + [vp] * 5 + [ctypes.c_float, vp, vp]
+    lib.mla_latent_forward.restype = i32
+    lib.mla_latent_forward.argtypes = [ctypes.c_int64] + [i32] * 7 + [vp] * 10
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [i32]
     _lib = lib
@@ -495,6 +497,55 @@ def mla_attention_forward(q_nope: torch.Tensor, q_dir: torch.Tensor, k_nope: tor
     if rc != KDA_OK:
         raise KdaError("mla_attention_forward", rc)
     return o
+
+
+def mla_latent_forward(x: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor, w_uk: torch.Tensor,
+                       w_uv: torch.Tensor, H: int, outputs: Optional[Sequence[torch.Tensor]] = None,
+                       stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+    """MLA latent projections of hidden states x [..., d_model] with linear-layer weights
+    w_dkv [d_c, d_model], w_kr [d_dir, d_model], w_uk [H*d_nope, d_c], w_uv [H*dv, d_c].
+    Returns (c [..., d_c], k_dir [..., d_dir], k_nope [..., H, d_nope], v [..., H, dv])."""
+    lib = load_library()
+    dt = x.dtype
+    for t, nm in ((x, "x"), (w_dkv, "w_dkv"), (w_kr, "w_kr"), (w_uk, "w_uk"), (w_uv, "w_uv")):
+        _check(t, nm, dt)
+    d_model = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    rows = x.numel() // d_model if d_model else 0
+    d_c, d_dir = w_dkv.shape[0], w_kr.shape[0]
+    if (tuple(w_dkv.shape) != (d_c, d_model) or tuple(w_kr.shape) != (d_dir, d_model)
+            or w_uk.shape[1] != d_c or w_uv.shape[1] != d_c or w_uk.shape[0] % H or w_uv.shape[0] % H):
+        raise ValueError("w_dkv [d_c, d_model], w_kr [d_dir, d_model], w_uk [H*d_nope, d_c], "
+                         "w_uv [H*dv, d_c] expected")
+    d_nope, dv = w_uk.shape[0] // H, w_uv.shape[0] // H
+    shapes = (lead + (d_c,), lead + (d_dir,), lead + (H, d_nope), lead + (H, dv))
+    if outputs is None:
+        outs = [torch.empty(sh, dtype=dt, device=x.device) for sh in shapes]
+        _hand_over(stream, x.device, *outs)
+    else:
+        outs = list(outputs)
+        for t, sh, nm in zip(outs, shapes, ("c", "k_dir", "k_nope", "v")):
+            _check(t, nm, dt)
+            if tuple(t.shape) != sh:
+                raise ValueError("%s must have shape %s" % (nm, sh))
+    rc = lib.mla_latent_forward(rows, d_model, d_c, d_dir, H, d_nope, dv, _dtype_code(dt), _ptr(x), _ptr(w_dkv),
+                                _ptr(w_kr), _ptr(w_uk), _ptr(w_uv), *[_ptr(t) for t in outs], _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError("mla_latent_forward", rc)
+    return tuple(outs)
+
+
+def mla_layer_forward(x: torch.Tensor, q_nope: torch.Tensor, q_dir: torch.Tensor, weights: dict,
+                      scale: Optional[float] = None, stream=None) -> Tuple[torch.Tensor, tuple]:
+    """The MLA token mixer from hidden states: latent projections (mla_latent_forward) then
+    attention (mla_attention_forward).  x [B,T,d_model]; q_nope [B,T,H,d_nope]; q_dir
+    [B,T,H,d_dir]; weights w_dkv, w_kr, w_uk, w_uv.  Returns (o, (c, k_dir, k_nope, v))."""
+    H = q_nope.shape[2]
+    lat = mla_latent_forward(x, weights["w_dkv"], weights["w_kr"], weights["w_uk"], weights["w_uv"], H,
+                             stream=stream)
+    c, k_dir, k_nope, v = lat
+    o = mla_attention_forward(q_nope, q_dir, k_nope, k_dir, v, scale=scale, stream=stream)
+    return o, lat
 
 
 def conv_kda_forward(desc: KdaStreamDesc, inp: dict, initial_state=None, final_state=None,

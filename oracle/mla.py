@@ -17,6 +17,16 @@ stream b, head h, query i and key j:
 Readings (the pages give neither): scale = 1 / sqrt(d_nope + d_dir) by
 default, and the shared part is a plain second dot product (no position
 encoding: the backbone has none).
+
+The latent path (same paragraph): the hidden state x is compressed to the
+latent c by one projection, the per-head key part and the values are
+decompressed from c by two more, and K_direct is a projection of x beside the
+latent.  Weights are stored as a linear layer's [out, in]:
+
+    c = x W_dkv^T,   k_dir = x W_kr^T,   k_nope = c W_uk^T,   v = c W_uv^T
+
+with k_nope and v split into H heads of d_nope and dv.  The queries are taken
+as given (the paragraph compresses keys and values only).
 """
 from __future__ import annotations
 
@@ -59,3 +69,26 @@ def mla_attention(q_nope, q_dir, k_nope, k_dir, v, scale: Optional[float] = None
             p = np.exp(s)
             out[b, :, hi] = (p @ vv[b, :, h]) / p.sum(axis=1, keepdims=True)
     return out
+
+
+def mla_latent(x, w_dkv, w_kr, w_uk, w_uv, H: int):
+    """The latent projections in fp64: x [..., d_model] -> (c [..., d_c], k_dir [..., d_dir],
+    k_nope [..., H, d_nope], v [..., H, dv]).  The decompression reads the unrounded latent."""
+    X, Wd, Wr, Wk, Wv = (_f64(a) for a in (x, w_dkv, w_kr, w_uk, w_uv))
+    lead = X.shape[:-1]
+    X2 = X.reshape(-1, X.shape[-1])
+    c = X2 @ Wd.T
+    k_dir = X2 @ Wr.T
+    k_nope = c @ Wk.T
+    v = c @ Wv.T
+    return (c.reshape(lead + (Wd.shape[0],)), k_dir.reshape(lead + (Wr.shape[0],)),
+            k_nope.reshape(lead + (H, Wk.shape[0] // H)), v.reshape(lead + (H, Wv.shape[0] // H)))
+
+
+def mla_layer(x, q_nope, q_dir, w_dkv, w_kr, w_uk, w_uv, scale: Optional[float] = None,
+              rows: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None) -> np.ndarray:
+    """o of the MLA token mixer from hidden states: the latent projections, then attention."""
+    H = q_nope.shape[2]
+    _, k_dir, k_nope, v = mla_latent(x, w_dkv, w_kr, w_uk, w_uv, H)
+    return mla_attention(q_nope, q_dir, k_nope, k_dir, v, scale=scale, rows=rows, heads=heads)
+

@@ -11,7 +11,7 @@ import torch
 
 from oracle import mla as oracle_mla
 from linear_attention_sequence_modality_amd import kda
-from linear_attention_sequence_modality_amd.inputs import MLA_WORKLOAD, MlaConfig, make_mla_inputs
+from linear_attention_sequence_modality_amd.inputs import MLA_WORKLOAD, MlaConfig, make_mla_inputs, make_mla_latent_inputs
 
 from gpu_common import TOL, rel, say
 
@@ -113,3 +113,111 @@ def test_ragged_tail_reads_nothing_past_the_stream_and_writes_only_o():
     e = rel(o.double().cpu().numpy(), ref)
     say("  guard rel err o %.2e" % e)
     assert e <= TOL["bf16"]
+
+
+# ---- the latent path (mla_latent_forward) ----------------------------------------------
+
+LATENT_W = ("w_dkv", "w_kr", "w_uk", "w_uv")
+
+
+def _latent_check(cfg, host, got, rows=None):
+    """got: (c, k_dir, k_nope, v) device tensors; compared with the fp64 oracle on token rows
+    ``rows`` (default: all) under the gate metric, per head for k_nope and v."""
+    x = host["x"] if rows is None else host["x"][:, rows]
+    ref = oracle_mla.mla_latent(x, *[host[k] for k in LATENT_W], cfg.H)
+    errs = []
+    for name, g, r in zip(("c", "k_dir", "k_nope", "v"), got, ref):
+        g = g.double().cpu().numpy()
+        if rows is not None:
+            g = g[:, rows]
+        if g.ndim == 3:
+            g, r = g[:, :, None], r[:, :, None]
+        errs.append(rel(g, r))
+        assert np.isfinite(g).all()
+    say("  rel err c %.2e k_dir %.2e k_nope %.2e v %.2e" % tuple(errs))
+    assert max(errs) <= TOL["bf16"]
+
+
+@pytest.mark.timeout(120)
+@pytest.mark.parametrize("name", ["mla_tiny", "mla_image_1024px"])
+def test_latent_projections(name):
+    cfg = MLA_WORKLOAD[name]
+    say("case latent %s B=%d T=%d H=%d d_model=%d d_c=%d" % (cfg.name, cfg.B, cfg.T, cfg.H, cfg.model_width,
+                                                            cfg.latent_width))
+    host = make_mla_latent_inputs(cfg)
+    dev = {k: v.cuda() for k, v in host.items()}
+    got = kda.mla_latent_forward(dev["x"], *[dev[k] for k in LATENT_W], cfg.H)
+    torch.cuda.synchronize()
+    _latent_check(cfg, host, got)
+
+
+@pytest.mark.timeout(120)
+@pytest.mark.parametrize("T", [1, 255, 256, 257, 511])
+def test_latent_ragged_row_counts(T):
+    """Row counts around the 256-row tile, at widths where the latent, K_direct, keys and
+    values are one or a few 64-column tiles."""
+    cfg = MlaConfig("latent_T%d" % T, B=1, T=T, H=1, seed=60 + T, d_model=96, d_c=64, d_nope=64, dv=64)
+    say("case latent ragged T=%d" % T)
+    host = make_mla_latent_inputs(cfg)
+    dev = {k: v.cuda() for k, v in host.items()}
+    got = kda.mla_latent_forward(dev["x"], *[dev[k] for k in LATENT_W], cfg.H)
+    torch.cuda.synchronize()
+    _latent_check(cfg, host, got)
+
+
+@pytest.mark.timeout(300)
+def test_latent_at_the_video_layer_size_sampled_rows():
+    cfg = MLA_WORKLOAD["mla_video_5s_480x832"]
+    say("case latent %s T=%d d_model=%d d_c=%d" % (cfg.name, cfg.T, cfg.model_width, cfg.latent_width))
+    host = make_mla_latent_inputs(cfg)
+    dev = {k: v.cuda() for k, v in host.items()}
+    got = kda.mla_latent_forward(dev["x"], *[dev[k] for k in LATENT_W], cfg.H)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    rows = sorted(set([0, 255, 256, cfg.T - 1] + [int(x) for x in rng.integers(0, cfg.T, 120)]))
+    _latent_check(cfg, host, got, rows=rows)
+    # and twice gives the same bits
+    again = kda.mla_latent_forward(dev["x"], *[dev[k] for k in LATENT_W], cfg.H)
+    torch.cuda.synchronize()
+    for a, b in zip(got, again):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.timeout(120)
+def test_layer_from_hidden_states():
+    """The whole MLA mixer from hidden states: latent projections then attention, against the
+    oracle's layer (which decompresses from the unrounded latent)."""
+    cfg = MLA_WORKLOAD["mla_tiny"]
+    say("case mla layer %s" % cfg.name)
+    host = make_mla_latent_inputs(cfg)
+    dev = {k: v.cuda() for k, v in host.items()}
+    o, _ = kda.mla_layer_forward(dev["x"], dev["q_nope"], dev["q_dir"], {k: dev[k] for k in LATENT_W})
+    torch.cuda.synchronize()
+    ref = oracle_mla.mla_layer(host["x"], host["q_nope"], host["q_dir"], *[host[k] for k in LATENT_W])
+    e = rel(o.double().cpu().numpy(), ref)
+    say("  rel err o %.2e" % e)
+    assert e <= TOL["bf16"]
+
+
+@pytest.mark.timeout(60)
+def test_latent_refusals():
+    """Host-side refusals, before any launch: fp32, a latent width off the 64-column tiling,
+    a misaligned pointer."""
+    cfg = MLA_WORKLOAD["mla_tiny"]
+    host = make_mla_latent_inputs(cfg)
+    dev = {k: v.cuda() for k, v in host.items()}
+    with pytest.raises(kda.KdaError) as e:
+        kda.mla_latent_forward(dev["x"].float(), *[dev[k].float() for k in LATENT_W], cfg.H)
+    assert e.value.status == kda.KDA_ERR_UNSUPPORTED
+    dm = cfg.model_width
+    w_dkv = torch.zeros(96, dm, dtype=torch.bfloat16, device="cuda")
+    w_uk = torch.zeros(cfg.H * cfg.d_nope, 96, dtype=torch.bfloat16, device="cuda")
+    w_uv = torch.zeros(cfg.H * cfg.dv, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(kda.KdaError) as e:
+        kda.mla_latent_forward(dev["x"], w_dkv, dev["w_kr"], w_uk, w_uv, cfg.H)
+    assert e.value.status == kda.KDA_ERR_UNSUPPORTED
+    buf = torch.empty(dev["x"].numel() + 8, dtype=torch.bfloat16, device="cuda")
+    x_mis = buf[1:1 + dev["x"].numel()].view(dev["x"].shape)
+    with pytest.raises(kda.KdaError) as e:
+        kda.mla_latent_forward(x_mis, *[dev[k] for k in LATENT_W], cfg.H)
+    assert e.value.status == kda.KDA_ERR_INVALID_ARG

@@ -141,3 +141,91 @@ def test_planted_mistakes_are_caught(plant):
         assert not np.allclose(bad, good[:, :, 0], equal_nan=False)
         return
     assert not np.allclose(bad, ref, rtol=0, atol=1e-6)
+
+
+# ---- the latent path ------------------------------------------------------------------
+
+def _latent_rand(seed, M=7, dm=6, dc=3, dr=2, H=2, dn=4, dv=5):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((M, dm)), r.standard_normal((dc, dm)), r.standard_normal((dr, dm)),
+            r.standard_normal((H * dn, dc)), r.standard_normal((H * dv, dc)))
+
+
+def test_latent_matches_element_loops():
+    """Every output element as an explicit sum over the contracted index, in Python floats:
+    c[m, i] = sum_k x[m, k] w_dkv[i, k]; k_nope[m, h, d] = sum_i c[m, i] w_uk[h d_nope + d, i]."""
+    x, wd, wr, wk, wv = _latent_rand(3)
+    H = 2
+    c, kd, kn, v = mla.mla_latent(x, wd, wr, wk, wv, H)
+    M, dm = x.shape
+    dc, dr, dn, dvv = wd.shape[0], wr.shape[0], wk.shape[0] // H, wv.shape[0] // H
+    for m in range(M):
+        cl = [sum(float(x[m, k]) * float(wd[i, k]) for k in range(dm)) for i in range(dc)]
+        for i in range(dc):
+            assert c[m, i] == pytest.approx(cl[i], rel=1e-12, abs=1e-12)
+        for i in range(dr):
+            assert kd[m, i] == pytest.approx(sum(float(x[m, k]) * float(wr[i, k]) for k in range(dm)),
+                                             rel=1e-12, abs=1e-12)
+        for h in range(H):
+            for d in range(dn):
+                ref = sum(cl[i] * float(wk[h * dn + d, i]) for i in range(dc))
+                assert kn[m, h, d] == pytest.approx(ref, rel=1e-12, abs=1e-12)
+            for d in range(dvv):
+                ref = sum(cl[i] * float(wv[h * dvv + d, i]) for i in range(dc))
+                assert v[m, h, d] == pytest.approx(ref, rel=1e-12, abs=1e-12)
+
+
+def test_keys_and_values_have_the_latent_rank():
+    """Keys and values are decompressed from a d_c-wide latent, so the token-by-feature matrix
+    [k_nope | v] has rank d_c < d_model; a path that projected x directly would have rank d_model."""
+    r = np.random.default_rng(11)
+    M, dm, dc, H, dn, dv = 40, 16, 5, 3, 6, 4
+    x = r.standard_normal((M, dm))
+    wd, wr = r.standard_normal((dc, dm)), r.standard_normal((2, dm))
+    wk, wv = r.standard_normal((H * dn, dc)), r.standard_normal((H * dv, dc))
+    _, _, kn, v = mla.mla_latent(x, wd, wr, wk, wv, H)
+    kv = np.concatenate([kn.reshape(M, -1), v.reshape(M, -1)], axis=1)
+    assert np.linalg.matrix_rank(kv) == dc
+    # K_direct comes from x itself: full rank min(M, d_dir)
+    _, kd, _, _ = mla.mla_latent(x, wd, wr, wk, wv, H)
+    assert np.linalg.matrix_rank(kd) == 2
+
+
+def test_absorbed_queries_score_against_the_latent():
+    """q_h . k_nope[j, h] = (W_uk,h^T q_h) . c_j: scoring the latent with the head's absorbed
+    query gives the same logits, which fixes the head split and the orientation of W_uk."""
+    x, wd, wr, wk, wv = _latent_rand(5, M=9, dm=8, dc=4, H=3, dn=5)
+    H, dn = 3, 5
+    c, _, kn, _ = mla.mla_latent(x, wd, wr, wk, wv, H)
+    q = np.random.default_rng(6).standard_normal((H, dn))
+    for h in range(H):
+        wkh = wk[h * dn:(h + 1) * dn]             # [d_nope, d_c]: head h's rows
+        direct = kn[:, h] @ q[h]
+        absorbed = c @ (wkh.T @ q[h])
+        np.testing.assert_allclose(direct, absorbed, rtol=1e-12, atol=1e-12)
+
+
+def test_identity_compression_reduces_to_one_projection():
+    """d_c = d_model with W_dkv = I: the latent is x itself, and k_nope, v are single
+    projections of x."""
+    r = np.random.default_rng(8)
+    M, dm, H, dn, dv = 5, 6, 2, 3, 2
+    x = r.standard_normal((M, dm))
+    wk, wv, wr = r.standard_normal((H * dn, dm)), r.standard_normal((H * dv, dm)), r.standard_normal((2, dm))
+    c, kd, kn, v = mla.mla_latent(x, np.eye(dm), wr, wk, wv, H)
+    np.testing.assert_array_equal(c, x)
+    np.testing.assert_allclose(kn.reshape(M, -1), np.einsum("mk,nk->mn", x, wk), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(v.reshape(M, -1), np.einsum("mk,nk->mn", x, wv), rtol=1e-13, atol=1e-13)
+
+
+def test_layer_is_latent_then_attention():
+    """mla_layer on a tiny stream equals the element-loop attention of the latent's keys and values."""
+    r = np.random.default_rng(9)
+    B, T, H, dm, dc, dn, dr, dv = 1, 6, 2, 8, 4, 3, 2, 3
+    x = r.standard_normal((B, T, dm))
+    wd, wr = r.standard_normal((dc, dm)), r.standard_normal((dr, dm))
+    wk, wv = r.standard_normal((H * dn, dc)), r.standard_normal((H * dv, dc))
+    qn, qd = r.standard_normal((B, T, H, dn)), r.standard_normal((B, T, H, dr))
+    o = mla.mla_layer(x, qn, qd, wd, wr, wk, wv, scale=0.4)
+    _, kd, kn, v = mla.mla_latent(x, wd, wr, wk, wv, H)
+    np.testing.assert_allclose(o, _loops(qn, qd, kn, kd, v, 0.4), rtol=1e-12, atol=1e-12)
