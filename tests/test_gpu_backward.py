@@ -206,3 +206,40 @@ def test_backward_at_the_video_workload_is_exact_along_q_and_v():
     e = abs(lhs - rhs) / abs(rhs)
     say("  v step along dv on chunk %d: dL %.6e, <dv, step> %.6e, rel err %.2e" % (chunk, lhs, rhs, e))
     assert e <= TOL[cfg.dtype]
+
+
+@pytest.mark.timeout(600)
+def test_backward_at_the_video_workload_one_head_against_the_oracle():
+    """Every gradient (dq, dk, dv, dalpha, dbeta, dS0) of one sampled head of the full 5 s
+    480x832 stream (T=33272, H=16, d=128, bf16), with an initial state and a final-state
+    gradient, in the launch configuration bench.py times, against the fp64 adjoint oracle run
+    on that head alone (heads are independent)."""
+    from linear_attention_sequence_modality_amd.inputs import WORKLOAD
+
+    cfg = WORKLOAD["video_5s_480x832"]
+    h = 5
+    say("case video_5s_480x832 backward head %d B=%d T=%d H=%d d=%d %s" % (h, cfg.B, cfg.T, cfg.H, cfg.dk,
+                                                                          cfg.dtype))
+    host = make_inputs(cfg)
+    g = np.random.default_rng(97)
+    dO = torch.from_numpy(g.standard_normal((cfg.B, cfg.T, cfg.H, cfg.dv)).astype(np.float32)).to(cfg.torch_dtype)
+    S0 = torch.from_numpy((g.standard_normal((cfg.B, cfg.H, cfg.dk, cfg.dv)) * 0.3).astype(np.float32))
+    dST = torch.from_numpy(g.standard_normal((cfg.B, cfg.H, cfg.dk, cfg.dv)).astype(np.float32))
+    dev = {k: v.cuda() for k, v in host.items()}
+    out = kda.kda_backward(desc_of(cfg), dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dO.cuda(),
+                           initial_state=S0.cuda(), d_final_state=dST.cuda())
+    torch.cuda.synchronize()
+    sl = slice(h, h + 1)
+    ref = ob.kda_recurrence_backward(host["q"][:, :, sl], host["k"][:, :, sl], host["v"][:, :, sl],
+                                     host["alpha"][:, :, sl], host["beta"][:, :, sl], dO[:, :, sl],
+                                     S0[:, sl], dST[:, sl])
+    errs = {}
+    for name in ("dq", "dk", "dv", "dalpha"):
+        got = out[name][:, :, sl].double().cpu().numpy()
+        assert np.isfinite(got).all()
+        errs[name] = rel(got, ref[name])
+    errs["dbeta"] = rel(out["dbeta"][:, :, sl].double().cpu().numpy()[..., None], ref["dbeta"][..., None])
+    errs["dS0"] = oracle.rel_err_state(out["d_initial_state"][:, sl].double().cpu().numpy(), ref["dS0"])
+    say("  rel errors: " + ", ".join("%s %.2e" % kv for kv in errs.items()))
+    for name, e in errs.items():
+        assert e <= TOL[cfg.dtype], "%s rel err %.3e" % (name, e)
