@@ -92,7 +92,10 @@ def roofline_bytes(cfg) -> dict:
     chunks : read q', k', v', alpha (3 dk + dv) and beta (1); write the chunk
              transform W, Qt, Kh (3 dk), Bq (64: a 64x64 block per 64 tokens)
              and Ut (dv), plus the fp32 chunk decay (dk per 64 tokens)
-    scan   : read that transform back; write o (dv)
+    scan   : read that transform back; write o (dv).  (The segmented state pass
+             reads the W, Kh, Ut and Gam of every chunk outside a stream's last
+             segment a second time, for the segment summaries: traffic above
+             these bytes, reported by the counters.)
     """
     es = 4 if cfg.dtype == "f32" else 2
     th = cfg.B * cfg.T * cfg.H                      # token-heads per launch
@@ -107,6 +110,17 @@ def roofline_bytes(cfg) -> dict:
     return {"conv": conv, "chunks": chunks, "scan": scan, "path_min": path_min}
 
 
+def seg_plan(cfg):
+    """The state pass's cut of each stream's chunks into segments (as the library plans it):
+    about 256 (segment, head) units over the chip, at most 32 segments per stream."""
+    nch = (cfg.T + 63) // 64
+    work = cfg.B * nch * cfg.H
+    target = (work + 255) // 256 if work > 256 else 1
+    p = min(32, max(1, (nch + target - 1) // target))
+    length = (nch + p - 1) // p
+    return (nch + length - 1) // length, length
+
+
 def mfma_flops(cfg) -> dict:
     """Matrix-core flops per launch as the kernels issue them (dense 16x16 tiles).
 
@@ -114,9 +128,15 @@ def mfma_flops(cfg) -> dict:
              dk (2 products each), W and Ut from the block-lower-triangular Tm
              (6 tile products per 16 columns), and the fp32 off-diagonal levels
              of Tm (16 tile products of 16x16x16)
-    scan   : per chunk-head and 16 value columns, U = Ut - W S and
-             S <- Gam S + Kh^T U (2 x 4 x dk/32 tile products) and the output
-             (4 x dk/32 + 6 tile products); each tile product is 16x16x32
+    scan   : the segmented state pass, bf16 products (each a 16x16x32 tile):
+             segment summaries, per chunk-head of every segment but a stream's
+             last, U = Ut - W S and S <- Gam S + Kh^T U for L (dv columns) and
+             for Phi (dk columns); the replay, per chunk-head and 16 value
+             columns, U and S as above (2 x 4 x dk/32) and the output
+             (4 x dk/32 + 6)
+    scan_f32 : the chain of segment start states on fp32 16x16x4 products: per
+             (stream, head, 16 state columns) and step (rounded up to whole
+             groups of four), (dk/16)^2 x 4 products
     The conv runs on the vector ALU (paired bf16 dot products), not on MFMA.
     """
     nch = (cfg.T + 63) // 64
@@ -124,8 +144,13 @@ def mfma_flops(cfg) -> dict:
     t32 = 2 * 16 * 16 * 32                  # one 16x16x32 product
     nks = cfg.dk // 32
     chunks = ch * (10 * nks * 2 * t32 + (cfg.dk // 16 + cfg.dv // 16) * 6 * t32 + 16 * 2 * 16 * 16 * 16)
-    scan = ch * (cfg.dv // 16) * ((2 * 4 * nks) + (4 * nks + 6)) * t32
-    return {"chunks": chunks, "scan": scan}
+    replay = ch * (cfg.dv // 16) * ((2 * 4 * nks) + (4 * nks + 6)) * t32
+    nseg, length = seg_plan(cfg)
+    summed = cfg.B * cfg.H * (nseg - 1) * length if nseg > 1 else 0
+    per_chunk = sum(4 * (w // 16) * nks + (cfg.dk // 16) * (w // 16) * 2 for w in (cfg.dv, cfg.dk))
+    steps = ((nseg - 1 + 3) // 4) * 4 if nseg > 1 else 0
+    chain = cfg.B * cfg.H * (cfg.dv // 16) * steps * (cfg.dk // 16) ** 2 * 4 * (2 * 16 * 16 * 4)
+    return {"chunks": chunks, "scan": replay + summed * per_chunk * t32, "scan_f32": chain}
 
 
 def copy_bandwidth(torch, mib: int = 1024, reps: int = 5) -> float:
@@ -524,6 +549,8 @@ def main() -> int:
             tf = fl[n] / (ms[n] * 1e-3) / 1e12
             kernels[n].update({"mfma_flop": fl[n], "mfma_flop_counted": measured_mfma_flops(cfg.name, n),
                                "TFLOP/s": round(tf, 1), "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFS, 4)})
+        if n + "_f32" in fl:
+            kernels[n]["mfma_flop_f32"] = fl[n + "_f32"]
     dom = max(names, key=lambda n: ms[n])
     ms_step = elapsed / args.steps * 1e3
     tokens = cfg.B * cfg.T
