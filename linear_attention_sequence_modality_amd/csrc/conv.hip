@@ -35,6 +35,8 @@
 //   * Blocks run channel block by channel block, row group by row group, and
 //     are remapped so each XCD works on a contiguous range of them: the halo
 //     rows of neighbouring row groups are read by co-resident blocks.
+//   * Single-slice grids (images) have nothing to march over in t: their
+//     workgroups march down a column strip over row groups instead (below).
 //   * Text tokens form a separate block range: a wave slides the 4-tap causal
 //     window over TR consecutive text tokens.
 #include "common.h"
@@ -162,6 +164,7 @@ struct Layout {
     int txt_items[3];     // B * n_trun * n_cb          (one per wave)
     int txt_blocks[3];
     int n_wrun, n_hg, n_trun;
+    int n_gch;            // single-slice grids: runs of IG row groups
     int nblocks;
 };
 
@@ -424,6 +427,205 @@ __device__ void visual_block(const ConvArgs &a, const Layout &L, int s, int blk,
         v.template march<true>(active);
 }
 
+// ---- single-slice grids (images: grid_t = 1) ------------------------------------
+// With one latent slice only the centre time taps (slice PT of the three) see
+// data, and there is nothing to march over in t.  A workgroup instead owns a
+// column strip (8 w positions x 128 channels) of IG consecutive row groups of
+// 4 rows and marches down it: step g stages the haloed 6 x 10 tile of row
+// group g (double buffered, the loads of group g+1 in flight under the
+// compute of group g), computes its 4 x 8 outputs from that tile alone and
+// stores them a step later.  Tile positions outside the grid (the image's
+// border, which moves with the row group at the top and bottom) are written
+// as zeros into the tile by the lane that would have loaded them.
+constexpr int IG = 8;   // row groups per workgroup
+
+template <typename T, int PT>
+struct ImageTile {
+    typedef Ops<T> O;
+    static constexpr int POS = CPW * (int)sizeof(T);
+    static constexpr int LPP = POS / 16;
+    static constexpr int PPI = LANES / LPP;
+    static constexpr int NI = TP / PPI;
+    static constexpr int NIW = (NI + 3) / 4;
+    static constexpr int SLICE = TP * POS;
+    static constexpr int AC = PT;   // the time tap slice that meets the single input slice
+
+    __amdgpu_buffer_rsrc_t rx, ry;
+    char *lds;
+    int wave, lane, rowb, gh, gw, w0, wj, n_hg, g0;
+    unsigned group_bytes;   // one row group of the grid in the stream
+    unsigned base_off[NIW]; // lane's byte offset of its load instructions' positions for row group 0 (mod 2^32)
+    int prow[NIW], pcol[NIW];   // tile row and column of those positions
+    unsigned out_off;     // lane's byte offset of output (row 0, wj)
+    typename O::Taps taps;
+    float acc[2][HR][JW][2];
+    typename O::XT x[HR + 2][JW + 2];
+
+    __device__ __forceinline__ void issue(int g) {   // row group g (absolute) into buffer g & 1
+        char *buf = lds + (g & 1) * SLICE;
+#pragma unroll
+        for (int i = 0; i < NIW; ++i) {
+            const int k = wave + 4 * i;
+            if (k >= NI) continue;
+            const int hu = HR * g - 1 + prow[i], wu = w0 - 1 + pcol[i];
+            if (hu >= 0 && hu < gh && wu >= 0 && wu < gw)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(buf + k * 1024), 16,
+                                                         base_off[i] + (unsigned)g * group_bytes, 0, 0, 0);
+            else
+                *reinterpret_cast<u32x4_t *>(buf + k * 1024 + lane * 16) = u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+
+    __device__ __forceinline__ void read_window(int g) {
+        const char *buf = lds + (g & 1) * SLICE + lane * (int)(POS / LANES) + JW * wave * POS;
+#pragma unroll
+        for (int r = 0; r < HR + 2; ++r)
+#pragma unroll
+            for (int c = 0; c < JW + 2; ++c) x[r][c] = O::lds_read(buf + (r * TC + c) * POS);
+    }
+
+    template <int SLOT>
+    __device__ __forceinline__ void flush(int g, bool active) {   // outputs of row group g
+        if (!active || g < g0 || g >= n_hg) return;
+        const unsigned goff = (unsigned)g * group_bytes;
+#pragma unroll
+        for (int r = 0; r < HR; ++r)
+#pragma unroll
+            for (int j = 0; j < JW; ++j)
+                if (HR * g + r < gh && wj + j < gw)
+                    O::bstore(ry, out_off + goff + (unsigned)((r * gw + j) * rowb), 0u, acc[SLOT][r][j][0],
+                              acc[SLOT][r][j][1]);
+    }
+
+    // tap slice AC of the window into slot SLOT, every accumulator fresh; the
+    // per-accumulator order of terms is that of the slice marches
+    template <int SLOT>
+    __device__ __forceinline__ void compute() {
+#pragma unroll
+        for (int rr = 0; rr < HR + 2; ++rr)
+#pragma unroll
+            for (int j = 0; j < JW; ++j) {
+                if constexpr (sizeof(T) == 2) {
+                    const uint32_t plo = __builtin_amdgcn_perm(x[rr][j + 1], x[rr][j], 0x05040100u);
+                    const uint32_t phi = __builtin_amdgcn_perm(x[rr][j + 1], x[rr][j], 0x07060302u);
+#pragma unroll
+                    for (int dh = 0; dh < 3; ++dh) {
+                        const int r = rr - dh;
+                        if (r < 0 || r >= HR) continue;
+                        float &c0 = acc[SLOT][r][j][0], &c1 = acc[SLOT][r][j][1];
+                        if (dh == 0) {
+                            c0 = O::dot2_0(plo, taps.pr[AC][0][0]);
+                            c1 = O::dot2_0(phi, taps.pr[AC][0][1]);
+                        } else {
+                            c0 = O::dot2(plo, taps.pr[AC][dh][0], c0);
+                            c1 = O::dot2(phi, taps.pr[AC][dh][1], c1);
+                        }
+                    }
+                    if (rr >= 2) {
+                        const int r = rr - 2;
+                        const uint32_t qlo = __builtin_amdgcn_perm(x[r + 1][j + 2], x[r][j + 2], 0x05040100u);
+                        const uint32_t qhi = __builtin_amdgcn_perm(x[r + 1][j + 2], x[r][j + 2], 0x07060302u);
+                        float &c0 = acc[SLOT][r][j][0], &c1 = acc[SLOT][r][j][1];
+                        c0 = O::dot2(qlo, taps.p2[AC][0], c0);
+                        c1 = O::dot2(qhi, taps.p2[AC][1], c1);
+                        c0 = O::dot2(x[rr][j + 2], taps.s2[AC][0], c0);
+                        c1 = O::dot2(x[rr][j + 2], taps.s2[AC][1], c1);
+                    }
+                } else {
+#pragma unroll
+                    for (int dh = 0; dh < 3; ++dh) {
+                        const int r = rr - dh;
+                        if (r < 0 || r >= HR) continue;
+#pragma unroll
+                        for (int e = 0; e < 3; ++e) {
+                            const int tap = (AC * 3 + dh) * 3 + e;
+                            float &c0 = acc[SLOT][r][j][0], &c1 = acc[SLOT][r][j][1];
+                            const bool fresh = dh == 0 && e == 0;
+                            c0 = __builtin_fmaf(taps.w[tap][0], x[rr][j + e].x, fresh ? 0.f : c0);
+                            c1 = __builtin_fmaf(taps.w[tap][1], x[rr][j + e].y, fresh ? 0.f : c1);
+                        }
+                    }
+                }
+            }
+    }
+
+    template <int SLOT>
+    __device__ __forceinline__ void step(int g, bool active) {
+        const int g1 = min(g0 + IG, n_hg);
+        if (g < g1) {
+            // row group g has landed once every wave's loads of it have retired;
+            // the barrier also ends every read of group g - 1's buffer
+            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+            lds_barrier();
+            read_window(g);
+        }
+        flush<SLOT ^ 1>(g - 1, active);
+        if (g + 1 < g1) issue(g + 1);
+        if (g < g1 && active) compute<SLOT>();
+    }
+
+    __device__ void march(bool active) {
+        issue(g0);
+        const int g1 = min(g0 + IG, n_hg);
+#pragma unroll 1
+        for (int g = g0; g <= g1; g += 2) {   // one step past the last group stores it
+            step<0>(g, active);
+            if (g + 1 > g1) break;
+            step<1>(g + 1, active);
+        }
+    }
+};
+
+template <typename T, int PT>
+__device__ void image_block(const ConvArgs &a, const Layout &L, int s, int blk, int wave, int lane, char *lds) {
+    typedef ImageTile<T, PT> V;
+    // channel block outermost, then row-group runs, then w-runs
+    const int wrun = blk % L.n_wrun;
+    int rest = blk / L.n_wrun;
+    const int gch = rest % L.n_gch;
+    rest /= L.n_gch;
+    const int cb = rest % L.n_cb[s];
+    const int b = rest / L.n_cb[s];
+    const int C = a.C[s];
+    const int c0 = cb * CPW + 2 * lane;
+    const bool ok = c0 < C;
+
+    V v;
+    v.wave = wave;
+    v.lane = lane;
+    v.lds = lds;
+    v.rowb = C * (int)sizeof(T);
+    v.gh = a.gh;
+    v.gw = a.gw;
+    v.w0 = wrun * WR;
+    v.wj = v.w0 + JW * wave;
+    v.n_hg = L.n_hg;
+    v.g0 = gch * IG;
+    v.group_bytes = (unsigned)(HR * a.gw) * (unsigned)v.rowb;
+    const size_t bbytes = (size_t)a.T * v.rowb;   // < 4 GiB, checked on the host
+    v.rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(static_cast<const char *>(a.x[s])) + (size_t)b * bbytes, 0, (int)(unsigned)bbytes,
+        kBufWord3);
+    v.ry = __builtin_amdgcn_make_buffer_rsrc(static_cast<char *>(a.y[s]) + (size_t)b * bbytes, 0,
+                                             (int)(unsigned)bbytes, kBufWord3);
+    const int chan = cb * V::POS + (lane % V::LPP) * 16;
+#pragma unroll
+    for (int i = 0; i < V::NIW; ++i) {
+        const int k = wave + 4 * i;
+        const int p = k * V::PPI + lane / V::LPP;
+        v.prow[i] = p / TC;
+        v.pcol[i] = p % TC;
+        // row group 0's position (row prow - 1, column w0 - 1 + pcol), modulo 2^32:
+        // "negative" for the halo row above the image, which row group 0 never
+        // loads; adding g row groups gives the true offset wherever one is loaded
+        v.base_off[i] = (unsigned)(a.n_text + (v.prow[i] - 1) * a.gw + v.w0 - 1 + v.pcol[i]) * (unsigned)v.rowb +
+                        (unsigned)chan;
+    }
+    v.out_off = (unsigned)(a.n_text + v.wj) * (unsigned)v.rowb + (unsigned)((ok ? c0 : 0) * (int)sizeof(T));
+    Ops<T>::load_taps(v.taps, static_cast<const T *>(a.wv[s]), ok ? c0 : 0, ok);
+    v.march(ok && v.wj < a.gw);
+}
+
 template <typename T>
 __device__ void text_item(const ConvArgs &a, const Layout &L, int s, int item, int lane) {
     typedef Ops<T> O;
@@ -474,8 +676,9 @@ __device__ void text_item(const ConvArgs &a, const Layout &L, int s, int item, i
     }
 }
 
-// bf16: at most 128 VGPRs, so four 4-wave blocks share a CU (LDS: 4 x 30 KB)
-template <typename T, int PT, bool HIST>
+// bf16: at most 128 VGPRs, so four 4-wave blocks share a CU (LDS: 4 x 30 KB).
+// IMG: the single-slice grid variant (grid_t = 1, no history).
+template <typename T, int PT, bool HIST, bool IMG>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 2 : 4))) void conv_kernel(
     ConvArgs a, Layout L) {
     __shared__ __attribute__((aligned(1024))) char lds[2 * VisualTile<T, PT, HIST>::SLICE];
@@ -485,7 +688,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
 #pragma unroll 1
     for (int s = 0; s < 3; ++s) {
         if (blk < L.vis_blocks[s]) {
-            visual_block<T, PT, HIST>(a, L, s, blk, wave, lane, lds);
+            if constexpr (IMG)
+                image_block<T, PT>(a, L, s, blk, wave, lane, lds);
+            else
+                visual_block<T, PT, HIST>(a, L, s, blk, wave, lane, lds);
             return;
         }
         blk -= L.vis_blocks[s];
@@ -502,38 +708,63 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
 
 hipError_t launch_conv(const ConvArgs &a, bool bf16, hipStream_t stream) {
     constexpr int WPB = NT / LANES;
+    // history slices exist only for time-causal segments; a separate
+    // instantiation keeps the extra buffer resource out of the other kernels
+    const bool hist = a.causal_t && a.n_hist > 0;
+    const bool img = a.gt == 1 && !hist;   // one latent slice: march down the rows instead
     Layout L;
     L.n_wrun = (a.gw + WR - 1) / WR;
     L.n_hg = (a.gh + HR - 1) / HR;
+    L.n_gch = (L.n_hg + IG - 1) / IG;
     L.n_trun = (a.n_text + TR - 1) / TR;
     const int n_vis = a.gt * a.gh * a.gw;
     L.nblocks = 0;
     for (int s = 0; s < 3; ++s) {
         L.n_cb[s] = (a.C[s] + CPW - 1) / CPW;
-        L.vis_blocks[s] = n_vis ? a.B * L.n_cb[s] * L.n_hg * L.n_wrun : 0;
+        L.vis_blocks[s] = n_vis ? a.B * L.n_cb[s] * (img ? L.n_gch : L.n_hg) * L.n_wrun : 0;
         L.txt_items[s] = a.B * L.n_trun * L.n_cb[s];
         L.txt_blocks[s] = (L.txt_items[s] + WPB - 1) / WPB;
         L.nblocks += L.vis_blocks[s] + L.txt_blocks[s];
     }
     if (L.nblocks == 0) return hipSuccess;
-    // history slices exist only for time-causal segments; a separate
-    // instantiation keeps the extra buffer resource out of the other kernels
-    const bool hist = a.causal_t && a.n_hist > 0;
+#define KC_LAUNCH(TT, PTT, HISTT, IMGT) \
+    hipLaunchKernelGGL((conv_kernel<TT, PTT, HISTT, IMGT>), dim3(L.nblocks), dim3(NT), 0, stream, a, L)
     if (bf16) {
         if (hist)
-            hipLaunchKernelGGL((conv_kernel<bf16_t, 2, true>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
+            KC_LAUNCH(bf16_t, 2, true, false);
         else if (a.causal_t)
-            hipLaunchKernelGGL((conv_kernel<bf16_t, 2, false>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
+            {
+            if (img)
+                KC_LAUNCH(bf16_t, 2, false, true);
+            else
+                KC_LAUNCH(bf16_t, 2, false, false);
+        }
         else
-            hipLaunchKernelGGL((conv_kernel<bf16_t, 1, false>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
+            {
+            if (img)
+                KC_LAUNCH(bf16_t, 1, false, true);
+            else
+                KC_LAUNCH(bf16_t, 1, false, false);
+        }
     } else {
         if (hist)
-            hipLaunchKernelGGL((conv_kernel<float, 2, true>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
+            KC_LAUNCH(float, 2, true, false);
         else if (a.causal_t)
-            hipLaunchKernelGGL((conv_kernel<float, 2, false>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
+            {
+            if (img)
+                KC_LAUNCH(float, 2, false, true);
+            else
+                KC_LAUNCH(float, 2, false, false);
+        }
         else
-            hipLaunchKernelGGL((conv_kernel<float, 1, false>), dim3(L.nblocks), dim3(NT), 0, stream, a, L);
+            {
+            if (img)
+                KC_LAUNCH(float, 1, false, true);
+            else
+                KC_LAUNCH(float, 1, false, false);
+        }
     }
+#undef KC_LAUNCH
     return hipGetLastError();
 }
 

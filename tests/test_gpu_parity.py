@@ -92,6 +92,12 @@ EDGE = [
     _small("fp32_64_128", dk=64, dv=128, dtype="f32", B=2),
     _small("narrow_w", grid=(3, 4, 1), n_text=2),             # grid_w = 1, ragged w-runs
     _small("wide_w", grid=(2, 2, 37), n_text=9),
+    # single-slice grids take the conv's row-group march: several runs of 8 row
+    # groups, a ragged last group, both paddings, both dtypes
+    _small("image_tall", grid=(1, 70, 9), n_text=4),
+    _small("image_causal", causal_t=1, grid=(1, 41, 23), n_text=2),
+    _small("fp32_image", dk=64, dv=64, dtype="f32", grid=(1, 37, 19), n_text=5),
+    _small("fp32_image_causal", dk=64, dv=64, dtype="f32", causal_t=1, grid=(1, 9, 9)),
 ]
 
 
