@@ -40,21 +40,24 @@ KERNEL_SOURCES = {
     "mla_latent": ("mla_proj.hip", "mfma.h", "common.h", "launch.h"),
     "kda_backward": ("kda_bwd.hip", "mfma.h", "common.h", "launch.h"),
 }
-# "kda_backward" is the sum over its three launches (records, ordered passes, gradients) per call.
+# "kda_backward" is the sum over its three launches (records, ordered passes, gradients) per call,
+# "scan" over the state pass's three (summaries, chain, replay), "mla_latent" over its two.
 MEASURED_TRAFFIC = {
-    ("video_5s_480x832", "conv"): ("a9c80efba93f3ca5", 253456.1, 399264.0),
-    ("video_5s_480x832", "chunks"): ("ce0c9745cfae1169", 270456.2, 586560.7),
-    ("video_5s_480x832", "scan"): ("ce0c9745cfae1169", 293367.0, 133100.4),
-    ("mla_video_5s_480x832", "mla"): ("fcf382f21189afaf", 1538698.3, 133088.0),
-    ("video_5s_480x832", "kda_backward"): ("b0f36027eacb2097", 11119862.9, 10420261.1),
+    ("video_5s_480x832", "conv"): ("d19542cd614d8499", 230197.2, 399264.0),
+    ("video_5s_480x832", "chunks"): ("3bea7ce458061024", 270474.6, 586560.1),
+    ("video_5s_480x832", "scan"): ("2cd0a30b31fb9f68", 517495.2, 180226.9),
+    ("mla_video_5s_480x832", "mla"): ("72e96049fb485bdc", 1537965.9, 133088.0),
+    ("mla_video_5s_480x832", "mla_latent"): ("4c9672c9ad11681c", 233771.0, 303607.0),
+    ("video_5s_480x832", "kda_backward"): ("af4dff09be9cb5a8", 11119571.2, 10399914.0),
 }
 # Matrix-core operations per dispatch (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
 # SQ_INSTS_VALU_MFMA_MOPS_F32, each count is 512 flops), taken the same way.
 MEASURED_MFMA_MOPS = {
-    ("video_5s_480x832", "chunks"): ("ce0c9745cfae1169", 46858240.0, 2129920.0),
-    ("video_5s_480x832", "scan"): ("ce0c9745cfae1169", 115015680.0, 0.0),
-    ("mla_video_5s_480x832", "mla"): ("fcf382f21189afaf", 22151168000.0, 0.0),
-    ("video_5s_480x832", "kda_backward"): ("b0f36027eacb2097", 0.0, 613416960.0),
+    ("video_5s_480x832", "chunks"): ("3bea7ce458061024", 46858240.0, 2129920.0),
+    ("video_5s_480x832", "scan"): ("2cd0a30b31fb9f68", 244776960.0, 2097152.0),
+    ("mla_video_5s_480x832", "mla"): ("72e96049fb485bdc", 22151168000.0, 0.0),
+    ("mla_video_5s_480x832", "mla_latent"): ("4c9672c9ad11681c", 425984000.0, 0.0),
+    ("video_5s_480x832", "kda_backward"): ("af4dff09be9cb5a8", 0.0, 613416960.0),
 }
 
 

@@ -23,8 +23,11 @@
 //     step s+1 are in registers before the MFMAs of step s start and go to
 //     the other buffer after them; one barrier per step.
 //   * The tile leaves through LDS, so each lane stores 16 contiguous bytes.
-//   * The blocks of one 256-row slab are consecutive and kept on one XCD:
-//     the slab of X comes from HBM once and from L2 for its other column tiles.
+//   * Block order: with a multiple of 8 column tiles (the decompression),
+//     each XCD takes one eighth of them over every row slab, so its share of
+//     W stays in its L2 and each slab of X is read once per XCD; otherwise
+//     the column tiles of one slab are consecutive on one XCD, so the slab
+//     comes from HBM once (the whole W is small there).
 #include "common.h"
 #include "launch.h"
 #include "mfma.h"
@@ -48,7 +51,20 @@ __global__ __launch_bounds__(PTHREADS) __attribute__((amdgpu_waves_per_eu(3))) v
     __shared__ __attribute__((aligned(16))) bf16_t sm[2 * (A_EL + B_EL)];
     const int n_tiles = (a.N1 + a.N2) / PN;
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
-    const int mt = blk / n_tiles, nt = blk % n_tiles;
+    int mt, nt;
+    if (n_tiles % 8 == 0) {
+        // eighths of the column tiles, one per XCD, each walked slab by slab:
+        // an XCD keeps its eighth of W (n_tiles / 8 tiles of PN rows) in L2 and
+        // reads each row slab of X once
+        const int tg = n_tiles / 8, n_mt = gridDim.x / n_tiles;
+        const int grp = blk / (n_mt * tg), rem = blk % (n_mt * tg);
+        mt = rem / tg;
+        nt = grp * tg + rem % tg;
+    } else {
+        // the column tiles of one slab together: the slab is read once from HBM
+        mt = blk / n_tiles;
+        nt = blk % n_tiles;
+    }
     const int64_t m0 = (int64_t)mt * PM;
     const int n0 = nt * PN;
     const bool second = n0 >= a.N1;
