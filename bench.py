@@ -156,6 +156,22 @@ def mfma_flops(cfg) -> dict:
     return {"chunks": chunks, "scan": replay + summed * per_chunk * t32, "scan_f32": chain}
 
 
+def gemm_tflops(torch, n: int = 8192, reps: int = 5) -> float:
+    """Measured dense bf16 matrix-core rate of a plain library GEMM (torch.matmul, n^3, fp32
+    accumulation inside the library), beside the vendor peak: the matrix-core calibration."""
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
 def copy_bandwidth(torch, mib: int = 1024, reps: int = 5) -> float:
     """Measured device-to-device copy rate (read + write bytes / s) of a plain torch copy."""
     n = mib * (1 << 20)
@@ -175,9 +191,11 @@ def copy_bandwidth(torch, mib: int = 1024, reps: int = 5) -> float:
     return gbs
 
 
-def cpu_baseline(cfg, frames: int, single_tokens: int) -> dict:
+def cpu_baseline(cfg, frames: int, single_tokens: int):
     """The fp64 oracle, as it stands, on a prefix of the same stream (text + first frames), on
-    all the threads OpenMP gives it, and on one thread over a shorter prefix."""
+    all the threads OpenMP gives it, and on one thread over a shorter prefix.  Returns (the
+    oracle's outputs (q', k', v', o, S_T) when the prefix is the whole stream, else None; the
+    baseline record)."""
     import oracle
     from linear_attention_sequence_modality_amd.inputs import make_inputs
 
@@ -187,11 +205,16 @@ def cpu_baseline(cfg, frames: int, single_tokens: int) -> dict:
     inp = make_inputs(sample)
     threads = oracle.num_threads()
     t0 = time.perf_counter()
-    oracle.conv_kda_forward(inp, sample.n_text, sample.grid)
+    ref = oracle.conv_kda_forward(inp, sample.n_text, sample.grid, sample.causal_t)
     dt = time.perf_counter() - t0
     # one thread: the text tokens and as many whole latent frames as fit single_tokens
     f1 = min(frames, max(1, (single_tokens - cfg.n_text) // max(1, gh * gw))) if gt else 0
     one = cfg.with_(name=cfg.name + "_prefix1", grid=(f1, gh, gw) if gt else cfg.grid)
+    outs = None
+    if frames == gt:
+        # the sample is the whole stream (same seed, same draws): keep the oracle's
+        # outputs for the parity figures of the run
+        outs = ref
     inp1 = make_inputs(one)
     oracle.set_num_threads(1)
     try:
@@ -200,7 +223,7 @@ def cpu_baseline(cfg, frames: int, single_tokens: int) -> dict:
         dt1 = time.perf_counter() - t1
     finally:
         oracle.set_num_threads(threads)
-    return {"value": sample.B * sample.T / dt, "unit": "tokens/s", "cores": threads,
+    return outs, {"value": sample.B * sample.T / dt, "unit": "tokens/s", "cores": threads,
             "kind": "oracle", "nproc": os.cpu_count(),
             "single_thread": {"value": one.B * one.T / dt1, "unit": "tokens/s", "cores": 1,
                               "sample": "B=%d, T=%d (%d text + %dx%dx%d), H=%d; %.1f s wall" % (
@@ -210,6 +233,30 @@ def cpu_baseline(cfg, frames: int, single_tokens: int) -> dict:
                       "H=%d, dk=dv=%d; %.1f s wall on %d threads (host nproc %s)" % (
                           sample.grid[0], gt, sample.B, sample.T, sample.n_text, *sample.grid, sample.H,
                           sample.dk, dt, threads, os.cpu_count())}
+
+
+def stage_parity(torch, kda, cfg, desc, inp, ws, ref) -> dict:
+    """The run's outputs against the oracle's on the whole stream: the gate metric (max over
+    (b, h) of max |x - ref| / max |ref|) and the element-wise figure, per stage."""
+    import oracle
+
+    dt = cfg.torch_dtype
+    wt = (inp["w_text_q"], inp["w_text_k"], inp["w_text_v"])
+    wv = (inp["w_vis_q"], inp["w_vis_k"], inp["w_vis_v"])
+    qc, kc, vc = kda.kda_conv_forward(desc, inp["q"], inp["k"], inp["v"], wt, wv)
+    sT = torch.empty(cfg.B, cfg.H, cfg.dk, cfg.dv, dtype=torch.float32, device="cuda")
+    o = kda.kda_forward(desc, qc, kc, vc, inp["alpha"], inp["beta"], final_state=sT, workspace=ws)
+    torch.cuda.synchronize()
+    out = {}
+    for name, got, want in zip(("q'", "k'", "v'", "o"), (qc, kc, vc, o), ref[:4]):
+        g = got.double().cpu().numpy()
+        out[name] = {"rel_err": float("%.3g" % oracle.rel_err(g, want)),
+                     "elementwise": float("%.3g" % oracle.rel_err_elementwise(g, want))}
+    g = sT.double().cpu().numpy()
+    out["S_T"] = {"rel_err": float("%.3g" % oracle.rel_err_state(g, ref[4])),
+                  "elementwise": float("%.3g" % oracle.rel_err_elementwise(g, ref[4], layout="state"))}
+    out["gate"] = 2e-2 if dt == torch.bfloat16 else 1e-4
+    return out
 
 
 def mla_flops(cfg) -> float:
@@ -537,6 +584,7 @@ def main() -> int:
     cold_ms = sorted(e[0].elapsed_time(e[-1]) for e in cold_ev)
     del scratch
     copy_gbs = copy_bandwidth(torch)
+    gemm_tfs = gemm_tflops(torch)
 
     names = ("conv", "chunks", "scan")
     ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in events) / args.steps for j, n in enumerate(names)}
@@ -585,11 +633,14 @@ def main() -> int:
                     "cold_tokens_per_s": round(tokens / (cold_ms[len(cold_ms) // 2] * 1e-3), 1),
                     "cold": "each step after a 1 GiB fill that evicts L2 and the Infinity Cache"},
         "measured_copy_GB/s": round(copy_gbs, 1),
+        "measured_bf16_gemm_TFLOP/s": round(gemm_tfs, 1),
         "path": {"min_bytes": rb["path_min"], "GB/s_vs_path_min": round(path_gbs, 1),
                  "frac_of_path_roofline": round(path_gbs / HBM_PEAK_GBS, 4)},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_frames, args.cpu_single_tokens)
+        ref, result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_frames, args.cpu_single_tokens)
+        if ref is not None:
+            result["parity"] = stage_parity(torch, kda, cfg, desc, inp, ws, ref)
     print(json.dumps(result), flush=True)
     return 0
 
