@@ -48,7 +48,7 @@ MEASURED_TRAFFIC = {
     ("video_5s_480x832", "scan"): ("2cd0a30b31fb9f68", 517495.2, 180226.9),
     ("mla_video_5s_480x832", "mla"): ("72e96049fb485bdc", 1537965.9, 133088.0),
     ("mla_video_5s_480x832", "mla_latent"): ("4c9672c9ad11681c", 233771.0, 303607.0),
-    ("video_5s_480x832", "kda_backward"): ("af4dff09be9cb5a8", 11119571.2, 10399914.0),
+    ("video_5s_480x832", "kda_backward"): ("1cc43b6c37d87564", 11417481.2, 10702388.6),
 }
 # Matrix-core operations per dispatch (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
 # SQ_INSTS_VALU_MFMA_MOPS_F32, each count is 512 flops), taken the same way.
@@ -57,7 +57,7 @@ MEASURED_MFMA_MOPS = {
     ("video_5s_480x832", "scan"): ("2cd0a30b31fb9f68", 244776960.0, 2097152.0),
     ("mla_video_5s_480x832", "mla"): ("72e96049fb485bdc", 22151168000.0, 0.0),
     ("mla_video_5s_480x832", "mla_latent"): ("4c9672c9ad11681c", 425984000.0, 0.0),
-    ("video_5s_480x832", "kda_backward"): ("af4dff09be9cb5a8", 0.0, 613416960.0),
+    ("video_5s_480x832", "kda_backward"): ("1cc43b6c37d87564", 0.0, 575078400.0),
 }
 
 
@@ -372,15 +372,26 @@ MFMA_FP32_PEAK_TFS = 157.3    # MI355X dense fp32 matrix-core peak, TFLOP/s
 def backward_flops(cfg) -> float:
     """fp32 multiply-add flops of one kda_backward launch sequence: the dense products per
     (batch, head, chunk) of the per-chunk transform (once, for the records the later
-    kernels read), the two ordered passes and the gradient kernel."""
+    kernels read), the two ordered passes and the gradient kernel.  The decayed products
+    inside a chunk (A and Bq in the transform, two row-side and two column-side products in
+    the gradient kernel) cover the 10 block pairs on and below the diagonal of 16-row
+    blocks, each 16 x 16 with the contraction over the channels (A, Bq) or over the 16 rows
+    of a block (the others)."""
     C, dk, dv = 64, cfg.dk, cfg.dv
     mm = lambda m, n, k: 2.0 * m * n * k
-    fwd = mm(C, C, dk) * 2 + mm(C, dk, C) + mm(C, dv, C)                 # A, Bq, W, Ut
+    tri_form = 10 * mm(16, 16, dk)
+    tri_apply = 10 * mm(16, dk, 16)
+    fwd = tri_form * 2 + mm(C, dk, C) + mm(C, dv, C)                   # A, Bq, W, Ut
     states = mm(C, dv, dk) + mm(dk, dv, C)
     reverse = mm(C, dv, C) + mm(C, dv, dk) + mm(dk, dv, C) * 2
-    grads = (mm(C, dv, dk) + mm(C, dv, C) + mm(C, dv, dk) + mm(C, C, dv) + mm(C, dk, dv) + mm(C, dk, C)
-             + mm(C, dk, dv) * 2 + mm(C, C, dv) + mm(C, C, dk) + mm(C, C, C) * 2 + mm(C, dv, C) + mm(C, dk, C)
-             + mm(C, dk, C) + mm(C, dk, C) * 2)
+    grads = (mm(C, dv, dk)                      # U = Ut - W S
+             + mm(C, dv, C) + mm(C, dv, dk)     # dU = Bq^T dO + Kh dS'
+             + mm(C, C, dv)                     # dBq
+             + mm(C, dk, dv) * 3                # dQt = dO S^T, dKh = U dS'^T, dW = -dU S^T
+             + mm(C, C, dv) + mm(C, C, dk)      # dTm = dU V^T + dW Kt^T
+             + mm(C, C, C) * 2                  # Tm^T dTm, dM
+             + mm(C, dv, C) + mm(C, dk, C)      # dX, dY
+             + tri_apply * 4)                   # R(dA, K), R(dBq, K), C(dA, K), C(dBq, Q)
     n_chunks = (cfg.T + C - 1) // C
     return cfg.B * cfg.H * n_chunks * (fwd + states + reverse + grads)
 

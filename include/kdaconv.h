@@ -248,10 +248,12 @@ int kda_conv_forward_varlen(const kda_stream_desc *descs, int n_seq, int H, int 
  * per-chunk gradient kernel.  workspace (device, >= the size returned by
  * kda_backward_workspace_size, fp32 records, states and per-workgroup
  * scratch) is owned by the caller; its contents are undefined afterwards.
- * Same shapes as kda_forward (dk, dv in {64, 128}, either dtype) plus the
- * forward's preconditions; additionally the product of alpha over the 64
- * tokens of a chunk stays above 2^-100 per key channel (the chunk's decays
- * are applied as exp(G) and exp(-G)).
+ * Same shapes and preconditions as kda_forward (dk, dv in {64, 128}, either
+ * dtype; the decay of any 8 consecutive tokens of a channel above 2^-120):
+ * the decays inside a chunk are split at 16-token block references as in the
+ * forward, so a chunk may decay by any amount.  Where alpha is tiny, d_alpha
+ * = d(log alpha) / alpha carries the rounding of d(log alpha), a running sum
+ * of terms of order one, divided by alpha.
  * Errors: KDA_ERR_INVALID_ARG for a NULL or misaligned required pointer or an
  * output overlapping an input or another output; KDA_ERR_WORKSPACE for a
  * missing or short workspace; otherwise as kda_forward.

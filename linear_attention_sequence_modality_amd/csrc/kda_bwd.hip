@@ -1,21 +1,28 @@
 // Backward pass of the KDA scan (gradients of q, k, v, alpha, beta and the
 // initial state, given those of o and the final state), chunk by chunk.
 //
-// Per chunk of C = 64 rows r (G_r = sum_{u<=r} log alpha_u per key channel,
-// gam = 2^(G log2 e), gC = G of the last row), the forward is regrouped as
-//   Kt = gam K, Kd = K / gam, Qt = gam Q, Kh = exp(gC - G) K,
-//   A = strict_lower(Kt Kd^T), Bq = lower(Qt Kd^T), Tm = (I + Diag(beta) A)^-1,
-//   X = Diag(beta) V, Y = Diag(beta) Kt, W = Tm Y, Ut = Tm X,
-//   U = Ut - W S, O = Qt S + Bq U, S' = Diag(exp(gC)) S + Kh^T U
+// Per chunk of C = 64 rows r (G_r = sum_{u<=r} log2 alpha_u per key channel,
+// gam = 2^G, gC = G of the last row, e(r, s) = 2^(G_r - G_s) <= 1 for s <= r), the
+// forward is regrouped as
+//   Kt = gam K, Qt = gam Q, Kh = 2^(gC - G) K,
+//   A[r][s] = sum_c K[r][c] K[s][c] e(r, s, c) (s < r), Bq[r][s] = sum_c Q[r][c] K[s][c] e(r, s, c) (s <= r),
+//   Tm = (I + Diag(beta) A)^-1, X = Diag(beta) V, Y = Diag(beta) Kt, W = Tm Y, Ut = Tm X,
+//   U = Ut - W S, O = Qt S + Bq U, S' = Diag(2^gC) S + Kh^T U
 // and its adjoint, for dO and dS' (the gradient of the state after the chunk), is
-//   dU = Bq^T dO + Kh dS',  dS = Qt^T dO + Diag(exp(gC)) dS' - W^T dU,
-//   dBq = lower(dO U^T), dQt = dO S^T + dBq Kd, dKh = U dS'^T, dW = -dU S^T,
+//   dU = Bq^T dO + Kh dS',  dS = Qt^T dO + Diag(2^gC) dS' - W^T dU,
+//   dBq = lower(dO U^T), dQt = dO S^T, dKh = U dS'^T, dW = -dU S^T,
 //   dTm = dU X^T + dW Y^T, dM = -Tm^T dTm Tm^T, dA = strict_lower(Diag(beta) dM),
-//   dX = Tm^T dU, dY = Tm^T dW, dKt = Diag(beta) dY + dA Kd, dKd = dA^T Kt + dBq^T Qt,
-//   dbeta = rowsum(dM A) + rowsum(dX V) + rowsum(dY Kt), dV = Diag(beta) dX,
-//   dQ = gam dQt, dK = gam dKt + dKd / gam + exp(gC - G) dKh,
-//   dG = dQt Qt + dKt Kt - dKd Kd - dKh Kh  (+ on the last row: colsum(dKh Kh) + exp(gC) rowsum(dS' S)),
-//   dlog alpha = reverse cumulative sum of dG over the chunk, dalpha = dlog alpha / alpha.
+//   dX = Tm^T dU, dY = Tm^T dW, dbeta = rowsum(dM A) + rowsum(dX V) + rowsum(dY Kt), dV = Diag(beta) dX,
+//   dQ  = gam dQt + R(dBq, K),                       R(P, Y)[r] = sum_{s<=r} P[r][s] Y[s] e(r, s)
+//   dKx = gam Diag(beta) dY + R(dA, K),  dKy = C(dA, K) + C(dBq, Q),  C(P, X)[s] = sum_{r>=s} P[r][s] X[r] e(r, s)
+//   dKh' = 2^(gC - G) dKh,  dK = dKx + dKy + dKh',
+//   dG = Q dQ + K (dKx - dKy - dKh')  (+ on the last row: colsum(dKh Kh) + 2^gC rowsum(dS' S)),
+//   dlog alpha = reverse cumulative sum of dG over the chunk (natural-log units), dalpha = dlog alpha / alpha.
+// (dQ, dKx, dKy and dKh' are the gradients reaching q and k through Qt, Kt, the
+// column side of A and Bq, and Kh; G enters each of them through its decay.)
+// The decayed products A, Bq, R and C split e(r, s) at a row between r and s
+// (tri_form, tri_rows, tri_cols below), so no factor exceeds the inverse of an
+// 8-token decay: the range is the forward's.
 //
 // Three launches, all fp32 inside:
 //   1. bwd_prep:    per (batch, head, chunk), in parallel: Qt, Kh, A, Bq, Tm, W, Ut, exp(gC).
@@ -150,6 +157,236 @@ __device__ __noinline__ void gemm(float *C, int ldc, const float *A, int lda, co
         }
 }
 
+// ---- decayed triangular products ---------------------------------------------------
+//
+// Row r of a chunk sees an earlier row s <= r of channel c through the decay
+// e(r, s, c) = 2^(G[r][c] - G[s][c]) <= 1.  Formed as 2^G times 2^-G over the whole chunk,
+// the second factor leaves the fp32 range once a chunk decays by more than 2^-126.  Here
+// the factor is split at a reference row between r and s, with the rows in 16-row blocks:
+//   * r in block i, s in an earlier block j: the last row of block i - 1 (tri_form,
+//     tri_rows) or of block j (tri_cols) lies between them, so both halves are decays;
+//   * r and s in one block: its row 7, so each half is at most the inverse of an
+//     8-token decay (the forward chunk transform's bound).
+// X, Y, G, Z are fp32 row-major [BC][DK] and P, C [BC][BC], in global memory (the
+// workgroup's scratch or the chunk's record); DK is 64 or 128.  The products run on
+// v_mfma_f32_16x16x4_f32: per step lane l supplies A[l%16][l/16] and B[l/16][l%16] and
+// the result leaves rows 4 (l/16) + i, column l%16 in lane l; the step's contraction
+// index l/16 stands for index 4 (l/16) + v of a 16-wide block, v the step, so each lane
+// reads 4 consecutive elements.  Every thread of the workgroup calls these; each ends
+// with a barrier.
+
+// 2^x on the hardware exponential (about 1 ulp; results below 2^-126, negligible
+// beside the terms they join, come out as zero).
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A matrix of the decayed products (global memory) read and written through a buffer
+// resource: its base in scalar registers (every lane passes the same pointer), the lane's
+// part of an address in one vector register and the constant part (a row offset known at
+// compile time) as an immediate or scalar offset, so the many loads of a product need
+// no 64-bit address each.  Offsets are in elements.
+struct GMat {
+    __amdgpu_buffer_rsrc_t rs;
+    __device__ __forceinline__ GMat(const float *p, int n) {
+        // readfirstlane returns a signed int: widen each half through uint32_t, or a low
+        // word with bit 31 set would sign-extend over the high word
+        const uint64_t a = reinterpret_cast<uint64_t>(p);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+        const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
+        rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(u), 0, 4 * n, kBufWord3);
+    }
+    __device__ __forceinline__ float at(int lane_off, int off) const {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane_off, 4 * off, 0));
+    }
+    __device__ __forceinline__ float4 at4(int lane_off, int off) const {
+        return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * lane_off, 4 * off, 0));
+    }
+    __device__ __forceinline__ void put(float x, int lane_off, int off) const {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rs, 4 * lane_off, 4 * off, 0);
+    }
+};
+
+// The 16 block pairs (i, j) of a 64 x 64 result: the 10 on and below the diagonal first,
+// row by row, then the 6 above it (zero), so that the four waves share the work evenly.
+__device__ __forceinline__ void block_pair(int p, int &i, int &j) {
+    if (p < 10) {
+        i = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+        j = p - i * (i + 1) / 2;
+    } else {
+        const int q = p - 10;
+        i = q < 3 ? 0 : q < 5 ? 1 : 2;
+        j = i + 1 + q - (i == 0 ? 0 : i == 1 ? 3 : 5);
+    }
+}
+
+// C[r][s] = sum_c X[r][c] Y[s][c] e(r, s, c) for s <= r (s < r when strict), 0 above.
+// The contraction runs over channels; every load of a pair is issued before its products.
+template <int DK>
+__device__ __noinline__ void tri_form_k(float *C, const float *X, const float *Y, const float *G, bool strict) {
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, g = lane / 16, l16 = lane % 16;
+    const GMat Cm(C, BC * BC), Xm(X, BC * DK), Ym(Y, BC * DK), Gm(G, BC * DK);
+    constexpr int NU = DK / 16;
+    for (int p = wave; p < 16; p += BT / 64) {
+        int i, j;
+        block_pair(p, i, j);
+        f32x4_t acc = zero4();
+        if (j <= i) {
+            const int ref = j < i ? 16 * i - 1 : 16 * i + 7;
+            const int xo = (16 * i + l16) * DK + 4 * g, yo = (16 * j + l16) * DK + 4 * g, ro = ref * DK + 4 * g;
+            float4 xv[NU], xg[NU], yv[NU], yg[NU], rg[NU];
+#pragma unroll
+            for (int t = 0; t < NU; ++t) {
+                xv[t] = Xm.at4(xo, 16 * t);
+                xg[t] = Gm.at4(xo, 16 * t);
+                yv[t] = Ym.at4(yo, 16 * t);
+                yg[t] = Gm.at4(yo, 16 * t);
+                rg[t] = Gm.at4(ro, 16 * t);
+            }
+#pragma unroll
+            for (int t = 0; t < NU; ++t) {
+                acc = mma4(xv[t].x * ex2(xg[t].x - rg[t].x), yv[t].x * ex2(rg[t].x - yg[t].x), acc);
+                acc = mma4(xv[t].y * ex2(xg[t].y - rg[t].y), yv[t].y * ex2(rg[t].y - yg[t].y), acc);
+                acc = mma4(xv[t].z * ex2(xg[t].z - rg[t].z), yv[t].z * ex2(rg[t].z - yg[t].z), acc);
+                acc = mma4(xv[t].w * ex2(xg[t].w - rg[t].w), yv[t].w * ex2(rg[t].w - yg[t].w), acc);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = 16 * i + 4 * g + q, s2 = 16 * j + l16;
+            // a select, not a product: inside a diagonal block the terms above the
+            // diagonal may overflow
+            Cm.put((s2 > r || (strict && s2 == r)) ? 0.f : acc[q], r * BC + s2, 0);
+        }
+    }
+    __syncthreads();
+}
+
+// Z[r][c] (+)= sum_{s <= r} P[r][s] Y[s][c] e(r, s, c); P is zero above its diagonal.
+// Per 16-column tile, a lane reads its 16 rows of Y and G once (rows 16 j + 4 (l/16) + v:
+// the contraction rows of every block j and, the same rows, its outputs).
+template <int DK>
+__device__ __noinline__ void tri_rows_k(float *Z, const float *P, const float *Y, const float *G, bool acc) {
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, g = lane / 16, l16 = lane % 16;
+    const GMat Zm(Z, BC * DK), Pm(P, BC * BC), Ym(Y, BC * DK), Gm(G, BC * DK);
+#pragma unroll 1
+    for (int n = wave; n < DK / 16; n += BT / 64) {
+        const int c = 16 * n + l16, lo = 4 * g * DK + c;   // the lane's row 4 g, column c
+        float yv[16], gv[16], gm[4], ge[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                yv[4 * j + v] = Ym.at(lo, (16 * j + v) * DK);
+                gv[4 * j + v] = Gm.at(lo, (16 * j + v) * DK);
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            gm[i] = Gm.at(c, (16 * i + 7) * DK);
+            ge[i] = i ? Gm.at(c, (16 * i - 1) * DK) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float4 pv[4];
+#pragma unroll
+            for (int j = 0; j <= i; ++j) pv[j] = Pm.at4(l16 * BC + 4 * g, 16 * i * BC + 16 * j);
+            f32x4_t off = zero4(), dia = zero4();
+#pragma unroll
+            for (int j = 0; j <= i; ++j) {
+                const float gref = j < i ? ge[i] : gm[i];
+                float b[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) b[v] = yv[4 * j + v] * ex2(gref - gv[4 * j + v]);
+                f32x4_t &t = j < i ? off : dia;
+                t = mma4(pv[j].x, b[0], t);
+                t = mma4(pv[j].y, b[1], t);
+                t = mma4(pv[j].z, b[2], t);
+                t = mma4(pv[j].w, b[3], t);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float gr = gv[4 * i + q];
+                float z = ex2(gr - gm[i]) * dia[q];
+                if (i) z += ex2(gr - ge[i]) * off[q];
+                const int ro = (16 * i + q) * DK;
+                Zm.put(acc ? Zm.at(lo, ro) + z : z, lo, ro);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Z[s][c] (+)= sum_{r >= s} P[r][s] X[r][c] e(r, s, c); P is zero above its diagonal.
+// The lane's P entries of the 10 block pairs are read once; per 16-column tile, its 16 rows
+// of X and G once.
+template <int DK>
+__device__ __noinline__ void tri_cols_k(float *Z, const float *P, const float *X, const float *G, bool acc) {
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, g = lane / 16, l16 = lane % 16;
+    const GMat Zm(Z, BC * DK), Pm(P, BC * BC), Xm(X, BC * DK), Gm(G, BC * DK);
+    float pa[4][4][4];   // [i][j][v] = P[16 i + 4 g + v][16 j + l16], i >= j
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j <= i; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) pa[i][j][v] = Pm.at(4 * g * BC + l16, (16 * i + v) * BC + 16 * j);
+#pragma unroll 1
+    for (int n = wave; n < DK / 16; n += BT / 64) {
+        const int c = 16 * n + l16, lo = 4 * g * DK + c;
+        float xv[16], gv[16], gm[4], ge[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                xv[4 * i + v] = Xm.at(lo, (16 * i + v) * DK);
+                gv[4 * i + v] = Gm.at(lo, (16 * i + v) * DK);
+            }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            gm[j] = Gm.at(c, (16 * j + 7) * DK);
+            ge[j] = Gm.at(c, (16 * j + 15) * DK);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x4_t off = zero4(), dia = zero4();
+#pragma unroll
+            for (int i = j; i < 4; ++i) {
+                const float gref = i > j ? ge[j] : gm[j];
+                f32x4_t &t = i > j ? off : dia;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) t = mma4(pa[i][j][v], xv[4 * i + v] * ex2(gv[4 * i + v] - gref), t);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float gs = gv[4 * j + q];
+                float z = ex2(gm[j] - gs) * dia[q];
+                if (j < 3) z += ex2(ge[j] - gs) * off[q];
+                const int ro = (16 * j + q) * DK;
+                Zm.put(acc ? Zm.at(lo, ro) + z : z, lo, ro);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void tri_form(float *C, const float *X, const float *Y, const float *G, int DK, bool strict) {
+    if (DK == 128)
+        tri_form_k<128>(C, X, Y, G, strict);
+    else
+        tri_form_k<64>(C, X, Y, G, strict);
+}
+__device__ __forceinline__ void tri_rows(float *Z, const float *P, const float *Y, const float *G, int DK, bool acc) {
+    if (DK == 128)
+        tri_rows_k<128>(Z, P, Y, G, acc);
+    else
+        tri_rows_k<64>(Z, P, Y, G, acc);
+}
+__device__ __forceinline__ void tri_cols(float *Z, const float *P, const float *X, const float *G, int DK, bool acc) {
+    if (DK == 128)
+        tri_cols_k<128>(Z, P, X, G, acc);
+    else
+        tri_cols_k<64>(Z, P, X, G, acc);
+}
+
 __device__ __forceinline__ float ld(const float *p) { return *p; }
 __device__ __forceinline__ float ld(const bf16_t *p) { return (float)*p; }
 __device__ __forceinline__ void st(float *p, float x) { *p = x; }
@@ -158,7 +395,7 @@ __device__ __forceinline__ void st(bf16_t *p, float x) { *p = (bf16_t)x; }
 // Per-chunk matrices rebuilt from the inputs (fp32, row-major, in the
 // workgroup's scratch): the chunk's rows past the stream's end are zero.
 struct ChunkMats {
-    float *Q, *K, *V, *G, *Kt, *Kd, *Qt, *Kh, *A, *Bq, *Tm, *X, *Y, *W, *Ut;
+    float *Q, *K, *V, *G, *Kt, *Qt, *Kh, *A, *Bq, *Tm, *X, *Y, *W, *Ut;
     float *beta, *eC;   // [BC], [DK]
 };
 
@@ -203,8 +440,8 @@ __device__ void stage_rows(D *dst, const T *src, size_t stride, int rows, int co
 }
 
 // FULL: the whole transform.  Otherwise only what the gradient kernel needs beyond the
-// chunk's record (K, V, beta, G, Kt, Kd): Qt, Kh, A, Bq, Tm, W, Ut and exp(gC) are already
-// there (c points at them) from the records pass.
+// chunk's record (Q, K, V, beta, G, Kt): Qt, Kh, A, Bq, Tm, W, Ut and 2^gC are already
+// there (c points at them) from the records pass.  G is in log2 units.
 template <typename T, bool FULL>
 __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, int n, float (*tA)[kPs],
                               float (*tB)[kPs]) {
@@ -218,21 +455,22 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
     stage_rows(lw, al + tok0 * DK, (size_t)H * DK, BC, DK, nr);   // alpha (rows past the end: 0, unused)
     if (tid < BC) c.beta[tid] = tid < nr ? ld(be + tok0 + (size_t)tid * H) : 0.f;
     __syncthreads();
-    // G: cumulative sum of log alpha down the rows (rows past the end add 0), in LDS
+    // G: cumulative sum of log2 alpha down the rows (rows past the end add 0), in LDS
     for (int ch = tid; ch < DK; ch += BT) {
         float g = 0.f;
         for (int r = 0; r < BC; ++r) {
-            if (r < nr) g += logf(lw[r * DK + ch]);
+            if (r < nr) g += log2f(lw[r * DK + ch]);
             lw[r * DK + ch] = g;
         }
-        if (FULL) c.eC[ch] = expf(g);
+        if (FULL) c.eC[ch] = exp2f(g);
         lw[BC * DK + ch] = g;   // gC
     }
     __syncthreads();
     {
         float *__restrict__ Gg = c.G;
         float *__restrict__ Kt = c.Kt;
-        float *__restrict__ Kd = c.Kd;
+        float *__restrict__ Kr = c.K;
+        float *__restrict__ Qr = c.Q;
         float *__restrict__ Qt = c.Qt;
         float *__restrict__ Kh = c.Kh;
         // q and k straight from the inputs (rows past the end read the first row, used as zeros)
@@ -243,25 +481,25 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
             const size_t src = (size_t)(r < nr ? r : 0) * H * DK + ch;
             float kv[4], qv[4] = {0.f, 0.f, 0.f, 0.f};
             ld4(kin + src, kv);
-            if (FULL) ld4(qin + src, qv);
+            ld4(qin + src, qv);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 kv[i] = r < nr ? kv[i] : 0.f;
                 qv[i] = r < nr ? qv[i] : 0.f;
             }
-            float g4[4], kt[4], kd[4], qt[4], kh[4];
+            float g4[4], kt[4], qt[4], kh[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float g = lw[e + i], gm = expf(g);
+                const float g = lw[e + i], gm = exp2f(g);
                 g4[i] = g;
                 kt[i] = gm * kv[i];
-                kd[i] = kv[i] / gm;
                 qt[i] = gm * qv[i];
-                kh[i] = expf(lw[BC * DK + ch + i] - g) * kv[i];
+                kh[i] = exp2f(lw[BC * DK + ch + i] - g) * kv[i];
             }
             *reinterpret_cast<float4 *>(Gg + e) = make_float4(g4[0], g4[1], g4[2], g4[3]);
             *reinterpret_cast<float4 *>(Kt + e) = make_float4(kt[0], kt[1], kt[2], kt[3]);
-            *reinterpret_cast<float4 *>(Kd + e) = make_float4(kd[0], kd[1], kd[2], kd[3]);
+            *reinterpret_cast<float4 *>(Kr + e) = make_float4(kv[0], kv[1], kv[2], kv[3]);
+            *reinterpret_cast<float4 *>(Qr + e) = make_float4(qv[0], qv[1], qv[2], qv[3]);
             if (FULL) {
                 *reinterpret_cast<float4 *>(Qt + e) = make_float4(qt[0], qt[1], qt[2], qt[3]);
                 *reinterpret_cast<float4 *>(Kh + e) = make_float4(kh[0], kh[1], kh[2], kh[3]);
@@ -270,8 +508,8 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
     }
     __syncthreads();
     if (FULL) {
-        gemm<false, true>(c.A, BC, c.Kt, DK, c.Kd, DK, BC, BC, DK, 1.f, false, kStrictLower, tA, tB);
-        gemm<false, true>(c.Bq, BC, c.Qt, DK, c.Kd, DK, BC, BC, DK, 1.f, false, kLower, tA, tB);
+        tri_form(c.A, c.K, c.K, c.G, DK, true);
+        tri_form(c.Bq, c.Q, c.K, c.G, DK, false);
     }
     if (FULL)
     // Tm = (I + Diag(beta) A)^-1 (unit lower triangular) by forward substitution: lane j of
@@ -341,7 +579,6 @@ __device__ ChunkMats carve(float *s, int DK, int DV, float **rest) {
     c.V = s; s += mv;
     c.G = s; s += mk;
     c.Kt = s; s += mk;
-    c.Kd = s; s += mk;
     c.Qt = s; s += mk;
     c.Kh = s; s += mk;
     c.A = s; s += mc;
@@ -658,8 +895,9 @@ __global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
     float *dM = s; s += mc;
     float *dX = s; s += mv;
     float *dY = s; s += mk;
-    float *dKt = s; s += mk;
-    float *dKd = s; s += mk;
+    float *dKx = s; s += mk;   // R(dA, K): the row side of A
+    float *dKy = s; s += mk;   // C(dA, K) + C(dBq, Q): the column side of A and Bq
+    float *dQi = dW;           // R(dBq, K), once dW is spent
     T *gq = static_cast<T *>(a.dq), *gk = static_cast<T *>(a.dk_out), *gv = static_cast<T *>(a.dv_out);
     T *ga = static_cast<T *>(a.dalpha), *gb = static_cast<T *>(a.dbeta);
     const T *go = static_cast<const T *>(a.dO), *al = static_cast<const T *>(a.alpha);
@@ -691,7 +929,6 @@ __global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
         gemm<false, false>(dU, DV, c.Kh, DK, dSp, DV, BC, DV, DK, 1.f, true, kNoMask, tA, tB);      //    + Kh dS'
         gemm<false, true>(dBq, BC, dO, DV, U, DV, BC, BC, DV, 1.f, false, kLower, tA, tB);          // dBq
         gemm<false, true>(dQt, DK, dO, DV, Sn, DV, BC, DK, DV, 1.f, false, kNoMask, tA, tB);        // dQt = dO S^T
-        gemm<false, false>(dQt, DK, dBq, BC, c.Kd, DK, BC, DK, BC, 1.f, true, kNoMask, tA, tB);     //     + dBq Kd
         gemm<false, true>(dKh, DK, U, DV, dSp, DV, BC, DK, DV, 1.f, false, kNoMask, tA, tB);        // dKh = U dS'^T
         gemm<false, true>(dW, DK, dU, DV, Sn, DV, BC, DK, DV, -1.f, false, kNoMask, tA, tB);        // dW = -dU S^T
         // dTm = dU X^T + dW Y^T = (dU V^T + dW Kt^T) Diag(beta), and Tm^T dTm takes the same column
@@ -709,15 +946,11 @@ __global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
             const int r = e / BC, s2 = e % BC;
             P[e] = s2 < r ? c.beta[r] * dM[e] : 0.f;
         }
-        for (int e4 = tid; e4 < BC * DK / 4; e4 += BT) {
-            const float bb = c.beta[4 * e4 / DK];
-            const float4 y = *reinterpret_cast<const float4 *>(dY + 4 * e4);
-            *reinterpret_cast<float4 *>(dKt + 4 * e4) = make_float4(bb * y.x, bb * y.y, bb * y.z, bb * y.w);
-        }
         __syncthreads();
-        gemm<false, false>(dKt, DK, P, BC, c.Kd, DK, BC, DK, BC, 1.f, true, kNoMask, tA, tB);       // + dA Kd
-        gemm<true, false>(dKd, DK, P, BC, c.Kt, DK, BC, DK, BC, 1.f, false, kNoMask, tA, tB);       // dA^T Kt
-        gemm<true, false>(dKd, DK, dBq, BC, c.Qt, DK, BC, DK, BC, 1.f, true, kNoMask, tA, tB);      // + dBq^T Qt
+        tri_rows(dKx, P, c.K, c.G, DK, false);          // R(dA, K)
+        tri_rows(dQi, dBq, c.K, c.G, DK, false);        // R(dBq, K)
+        tri_cols(dKy, P, c.K, c.G, DK, false);          // C(dA, K)
+        tri_cols(dKy, dBq, c.Q, c.G, DK, true);         //  + C(dBq, Q)
         // the panel area as scratch from here on: dG [BC][DK], alpha [BC][DK], partial sums
         float *lw = &tA[0][0];
         float *dGl = lw, *alpha_l = lw + BC * DK, *part = lw + 2 * BC * DK;   // part: 4 BC + 4 DK + 2 DK floats
@@ -768,25 +1001,29 @@ __global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
         }
         for (int e4 = tid; e4 < BC * DK / 4; e4 += BT) {
             const int e = 4 * e4, r = e / DK, ch = e % DK;
-            const float4 g = *reinterpret_cast<const float4 *>(c.G + e);
-            const float4 eC = *reinterpret_cast<const float4 *>(c.eC + ch);
-            const float4 q1 = *reinterpret_cast<const float4 *>(dQt + e), q2 = *reinterpret_cast<const float4 *>(c.Qt + e);
-            const float4 t1 = *reinterpret_cast<const float4 *>(dKt + e), t2 = *reinterpret_cast<const float4 *>(c.Kt + e);
-            const float4 d1 = *reinterpret_cast<const float4 *>(dKd + e), d2 = *reinterpret_cast<const float4 *>(c.Kd + e);
-            const float4 h1 = *reinterpret_cast<const float4 *>(dKh + e), h2 = *reinterpret_cast<const float4 *>(c.Kh + e);
-            const float gv4[4] = {g.x, g.y, g.z, g.w}, ec[4] = {eC.x, eC.y, eC.z, eC.w};
-            const float a1[4] = {q1.x, q1.y, q1.z, q1.w}, a2[4] = {q2.x, q2.y, q2.z, q2.w};
-            const float b1[4] = {t1.x, t1.y, t1.z, t1.w}, b2[4] = {t2.x, t2.y, t2.z, t2.w};
-            const float c1[4] = {d1.x, d1.y, d1.z, d1.w}, c2[4] = {d2.x, d2.y, d2.z, d2.w};
-            const float e1[4] = {h1.x, h1.y, h1.z, h1.w}, e2[4] = {h2.x, h2.y, h2.z, h2.w};
+            const float bb = c.beta[r];
+            float g4[4], gc[4], q1[4], qi[4], y1[4], kx[4], ky[4], h1[4], qr[4], kr[4];
+            ld4(c.G + e, g4);
+            ld4(c.G + (BC - 1) * DK + ch, gc);   // gC: rows past the end repeat the last valid row's G
+            ld4(dQt + e, q1);
+            ld4(dQi + e, qi);
+            ld4(dY + e, y1);
+            ld4(dKx + e, kx);
+            ld4(dKy + e, ky);
+            ld4(dKh + e, h1);
+            ld4(c.Q + e, qr);
+            ld4(c.K + e, kr);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float gm = expf(gv4[i]);
+                const float gm = exp2f(g4[i]);
+                const float dq = gm * q1[i] + qi[i];
+                const float dkx = gm * bb * y1[i] + kx[i];
+                const float dkh = exp2f(gc[i] - g4[i]) * h1[i];
                 if (r < nr) {
-                    st(gq + tok(r) * DK + ch + i, gm * a1[i]);
-                    st(gk + tok(r) * DK + ch + i, gm * b1[i] + c1[i] / gm + expf(logf(ec[i]) - gv4[i]) * e1[i]);
+                    st(gq + tok(r) * DK + ch + i, dq);
+                    st(gk + tok(r) * DK + ch + i, dkx + ky[i] + dkh);
                 }
-                dGl[e + i] = a1[i] * a2[i] + b1[i] * b2[i] - c1[i] * c2[i] - e1[i] * e2[i];
+                dGl[e + i] = qr[i] * dq + kr[i] * (dkx - ky[i] - dkh);
             }
         }
         // the last row's extra terms: colsum(dKh * Kh) over the rows (four row groups of
@@ -839,7 +1076,7 @@ __global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
 size_t kda_bwd_scratch_floats(int dk, int dv) {
     const size_t mk = (size_t)BC * dk, mv = (size_t)BC * dv, mc = (size_t)BC * BC;
     // ChunkMats + the intra kernel's temporaries (the largest user)
-    const size_t chunk = 9 * mk + 4 * mv + 3 * mc + BC + dk;
+    const size_t chunk = 8 * mk + 4 * mv + 3 * mc + BC + dk;
     const size_t intra = 3 * mv + 4 * mc + 6 * mk;
     return chunk + intra + 64;
 }

@@ -104,3 +104,19 @@ def check_stream(cfg: StreamConfig, inp: dict, heads=None, S0=None, want_state=F
     for name, e in errs.items():
         assert e <= tol, "%s rel err %.3e > %.1e" % (name, e, tol)
     return errs
+
+
+def edge_alpha(cfg: StreamConfig, inp: dict) -> np.ndarray:
+    """alpha = 2^-14 (exact in bf16 and fp32) on runs of tokens of chosen channels: any 8
+    consecutive tokens then decay by 2^-112, just inside the 2^-120 the chunk
+    factorisation accepts.  Runs start at several offsets from the chunk and
+    16-token sub-block boundaries and one covers whole chunks."""
+    a = inp["alpha"].float().numpy().copy()
+    T, dk = cfg.T, cfg.dk
+    tiny = np.float32(2.0 ** -14)
+    runs = [(0, 8, range(0, dk, 5)), (13, 9, range(1, dk, 3)), (56, 16, range(2, dk, 7)),
+            (64 + 7, 8, range(0, dk)), (128, 128, range(3, dk, 4)), (T - 11, 11, range(0, dk, 2))]
+    for t0, n, chans in runs:
+        t0 = min(max(t0, 0), T - 1)
+        a[:, t0:min(t0 + n, T), :, list(chans)] = tiny
+    return a

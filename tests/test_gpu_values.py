@@ -22,7 +22,7 @@ import oracle
 from linear_attention_sequence_modality_amd import kda
 from linear_attention_sequence_modality_amd.inputs import StreamConfig, make_inputs
 
-from gpu_common import TOL, check_stream, heads_slice, rel, rel_elem, say, to_dev
+from gpu_common import TOL, check_stream, edge_alpha, heads_slice, rel, rel_elem, say, to_dev
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -64,29 +64,13 @@ def test_strong_forgetting(dtype, d):
     check_stream(cfg, make_inputs(cfg, alpha_mean=-3.0), S0=_s0(cfg), want_state=True)
 
 
-def _edge_alpha(cfg, inp):
-    """alpha = 2^-14 (exact in bf16 and fp32) on runs of tokens of chosen channels: any 8
-    consecutive tokens then decay by 2^-112, just inside the 2^-120 the chunk
-    factorisation accepts.  Runs start at several offsets from the chunk and
-    16-token sub-block boundaries and one covers whole chunks."""
-    a = inp["alpha"].float().numpy().copy()
-    T, dk = cfg.T, cfg.dk
-    tiny = np.float32(2.0 ** -14)
-    runs = [(0, 8, range(0, dk, 5)), (13, 9, range(1, dk, 3)), (56, 16, range(2, dk, 7)),
-            (64 + 7, 8, range(0, dk)), (128, 128, range(3, dk, 4)), (T - 11, 11, range(0, dk, 2))]
-    for t0, n, chans in runs:
-        t0 = min(max(t0, 0), T - 1)
-        a[:, t0:min(t0 + n, T), :, list(chans)] = tiny
-    return a
-
-
 @pytest.mark.timeout(120)
 @pytest.mark.parametrize("dtype,d", DTYPES, ids=IDS)
 def test_alpha_at_the_factorisation_edge(dtype, d):
     _skip_unsupported(dtype, d)
     cfg = _cfg("alpha_edge", dtype, d, n_text=40, grid=(3, 8, 11))
     inp = make_inputs(cfg)
-    check_stream(cfg, _with(inp, cfg, alpha=_edge_alpha(cfg, inp)), S0=_s0(cfg), want_state=True)
+    check_stream(cfg, _with(inp, cfg, alpha=edge_alpha(cfg, inp)), S0=_s0(cfg), want_state=True)
 
 
 @pytest.mark.timeout(120)
