@@ -7,6 +7,7 @@ import numpy as np
 import torch
 
 import oracle
+from oracle import backward as ob
 from linear_attention_sequence_modality_amd import kda
 from linear_attention_sequence_modality_amd.inputs import StreamConfig, make_inputs
 
@@ -120,3 +121,37 @@ def edge_alpha(cfg: StreamConfig, inp: dict) -> np.ndarray:
         t0 = min(max(t0, 0), T - 1)
         a[:, t0:min(t0 + n, T), :, list(chans)] = tiny
     return a
+
+
+def check_backward(cfg: StreamConfig, host: dict, dalpha_tol=None, S0_scale=0.3):
+    """kda_backward on the GPU against the fp64 adjoint oracle: every gradient (q, k, v,
+    alpha, beta, the initial state) gated per (batch, head) at the dtype's tolerance, with a
+    seeded dO, initial state and final-state gradient.  dalpha_tol: gate d alpha there and
+    d log alpha = alpha * d alpha at the standard tolerance (where alpha is tiny)."""
+    say("case %s B=%d T=%d H=%d dk=%d dv=%d %s" % (cfg.name, cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv, cfg.dtype))
+    g = np.random.default_rng(cfg.seed)
+    dO = torch.from_numpy(g.standard_normal((cfg.B, cfg.T, cfg.H, cfg.dv)).astype(np.float32)).to(cfg.torch_dtype)
+    S0 = torch.from_numpy((g.standard_normal((cfg.B, cfg.H, cfg.dk, cfg.dv)) * S0_scale).astype(np.float32))
+    dST = torch.from_numpy(g.standard_normal((cfg.B, cfg.H, cfg.dk, cfg.dv)).astype(np.float32))
+    dev = {k: v.cuda() for k, v in host.items()}
+    out = kda.kda_backward(desc_of(cfg), dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dO.cuda(),
+                           initial_state=S0.cuda(), d_final_state=dST.cuda())
+    torch.cuda.synchronize()
+    ref = ob.kda_recurrence_backward(host["q"], host["k"], host["v"], host["alpha"], host["beta"], dO, S0, dST)
+    errs = {}
+    for name in ("dq", "dk", "dv", "dalpha"):
+        errs[name] = rel(out[name].double().cpu().numpy(), ref[name])
+    errs["dbeta"] = rel(out["dbeta"].double().cpu().numpy()[..., None], ref["dbeta"][..., None])
+    errs["dS0"] = oracle.rel_err_state(out["d_initial_state"].double().cpu().numpy(), ref["dS0"])
+    gates = {name: TOL[cfg.dtype] for name in errs}
+    if dalpha_tol is not None:
+        # d log alpha = alpha * d alpha at the standard gate; d alpha at its own
+        a = host["alpha"].double().numpy()
+        errs["alpha*dalpha"] = rel(a * out["dalpha"].double().cpu().numpy(), a * ref["dalpha"])
+        gates["alpha*dalpha"] = TOL[cfg.dtype]
+        gates["dalpha"] = dalpha_tol
+    say("  rel errors: " + ", ".join("%s %.2e" % kv for kv in errs.items()))
+    for name in ("dq", "dk", "dv", "dalpha", "dbeta"):
+        assert torch.isfinite(out[name].float()).all(), "non-finite " + name
+    for name, e in errs.items():
+        assert e <= gates[name], "%s rel err %.3e > %.1e" % (name, e, gates[name])

@@ -13,7 +13,7 @@ from oracle import backward as ob
 from linear_attention_sequence_modality_amd import kda
 from linear_attention_sequence_modality_amd.inputs import StreamConfig, make_inputs
 
-from gpu_common import TOL, desc_of, edge_alpha, rel, say
+from gpu_common import TOL, check_backward, desc_of, edge_alpha, rel, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -27,40 +27,10 @@ CASES = [
 ]
 
 
-def _check_backward(cfg, host, dalpha_tol=None):
-    say("case %s B=%d T=%d H=%d dk=%d dv=%d %s" % (cfg.name, cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv, cfg.dtype))
-    g = np.random.default_rng(cfg.seed)
-    dO = torch.from_numpy(g.standard_normal((cfg.B, cfg.T, cfg.H, cfg.dv)).astype(np.float32)).to(cfg.torch_dtype)
-    S0 = torch.from_numpy((g.standard_normal((cfg.B, cfg.H, cfg.dk, cfg.dv)) * 0.3).astype(np.float32))
-    dST = torch.from_numpy(g.standard_normal((cfg.B, cfg.H, cfg.dk, cfg.dv)).astype(np.float32))
-    dev = {k: v.cuda() for k, v in host.items()}
-    out = kda.kda_backward(desc_of(cfg), dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dO.cuda(),
-                           initial_state=S0.cuda(), d_final_state=dST.cuda())
-    torch.cuda.synchronize()
-    ref = ob.kda_recurrence_backward(host["q"], host["k"], host["v"], host["alpha"], host["beta"], dO, S0, dST)
-    errs = {}
-    for name in ("dq", "dk", "dv", "dalpha"):
-        errs[name] = rel(out[name].double().cpu().numpy(), ref[name])
-    errs["dbeta"] = rel(out["dbeta"].double().cpu().numpy()[..., None], ref["dbeta"][..., None])
-    errs["dS0"] = oracle.rel_err_state(out["d_initial_state"].double().cpu().numpy(), ref["dS0"])
-    gates = {name: TOL[cfg.dtype] for name in errs}
-    if dalpha_tol is not None:
-        # d log alpha = alpha * d alpha at the standard gate; d alpha at its own
-        a = host["alpha"].double().numpy()
-        errs["alpha*dalpha"] = rel(a * out["dalpha"].double().cpu().numpy(), a * ref["dalpha"])
-        gates["alpha*dalpha"] = TOL[cfg.dtype]
-        gates["dalpha"] = dalpha_tol
-    say("  rel errors: " + ", ".join("%s %.2e" % kv for kv in errs.items()))
-    for name in ("dq", "dk", "dv", "dalpha", "dbeta"):
-        assert torch.isfinite(out[name].float()).all(), "non-finite " + name
-    for name, e in errs.items():
-        assert e <= gates[name], "%s rel err %.3e > %.1e" % (name, e, gates[name])
-
-
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
 def test_backward_matches_the_adjoint_oracle(cfg):
-    _check_backward(cfg, make_inputs(cfg))
+    check_backward(cfg, make_inputs(cfg))
 
 
 DECAY = [("bf16", 128), ("f32", 64), ("f32", 128)]
@@ -94,7 +64,7 @@ def test_backward_under_strong_decay(kind, dtype, d):
     else:
         host = make_inputs(cfg)
         host["alpha"] = torch.from_numpy(edge_alpha(cfg, host)).to(cfg.torch_dtype)
-    _check_backward(cfg, host, dalpha_tol=2e-2 if kind == "edge" else None)
+    check_backward(cfg, host, dalpha_tol=2e-2 if kind == "edge" else None)
 
 
 @pytest.mark.timeout(120)

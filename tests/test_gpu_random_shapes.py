@@ -1,4 +1,5 @@
-"""Conv + KDA on seeded random stream shapes against the oracle (needs an MI355X).
+"""Conv + KDA forward and KDA backward on seeded random stream shapes against the
+oracle (needs an MI355X).
 
 Each case draws a layout (text length, (t, h, w) grid, batch, heads, head sizes,
 dtype, time padding, an initial state or not) from a fixed seed, so the cases are
@@ -13,7 +14,7 @@ import torch
 
 from linear_attention_sequence_modality_amd.inputs import StreamConfig, make_inputs
 
-from gpu_common import check_stream
+from gpu_common import check_backward, check_stream
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -59,3 +60,28 @@ def test_random_shape(i):
         S0 = (np.random.default_rng(cfg.seed).standard_normal((cfg.B, cfg.H, cfg.dk, cfg.dv)) * 0.4).astype(
             np.float32)
     check_stream(cfg, make_inputs(cfg), S0=S0, want_state=True)
+
+
+def _bwd_case(i):
+    r = np.random.default_rng(9700 + i)
+    dtype = ["bf16", "f32"][int(r.integers(0, 2))]
+    gt = int(r.choice([0, 1, 2, 3]))
+    gh = int(r.integers(1, 20)) if gt else 0
+    gw = int(r.integers(1, 24)) if gt else 0
+    return StreamConfig("brand%02d" % i, B=int(r.integers(1, 3)), H=int(r.integers(1, 3)),
+                        dk=int(r.choice([64, 128])), dv=int(r.choice([64, 128])),
+                        n_text=int(r.integers(0 if gt else 1, 200)), grid=(gt, gh, gw), dtype=dtype,
+                        seed=9800 + i), float(r.choice([3.0, 1.0, -1.5]))
+
+
+BWD_CASES = [_bwd_case(i) for i in range(10)]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("i", range(len(BWD_CASES)), ids=[c[0].name for c in BWD_CASES])
+def test_random_shape_backward(i):
+    """kda_backward on seeded random layouts (ragged chunk tails, one to a few chunks
+    per stream, both dtypes, dk and dv drawn independently, alpha centred on
+    sigmoid(3), sigmoid(1) or sigmoid(-1.5)) against the fp64 adjoint oracle."""
+    cfg, alpha_mean = BWD_CASES[i]
+    check_backward(cfg, make_inputs(cfg, alpha_mean=alpha_mean))
