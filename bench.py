@@ -10,7 +10,8 @@ dk = dv = 128, bf16 with fp32 accumulation).
 
 Per-kernel durations come from HIP events recorded on the launch stream
 between the three calls over the timed steps; the dominant kernel's roofline
-uses the algorithmic bytes per launch of roofline_bytes().
+uses the algorithmic bytes per launch of roofline_bytes() (the measurement plan's
+per-token-head figures).
 """
 from __future__ import annotations
 
@@ -88,29 +89,40 @@ def measured_mfma_flops(workload: str, kernel: str):
 
 
 def roofline_bytes(cfg) -> dict:
-    """Algorithmic HBM bytes per launch of each kernel (what its interface must move).
+    """Algorithmic HBM bytes per launch of each kernel: the per-token-head figures of the
+    measurement plan (at d = dk = dv = 128 in bf16: conv 1536, chunk transform 2306, state
+    pass 1536, path minimum 2818) times the token-heads of one launch.
 
-    conv   : read q, k, v and write q', k', v'               6 d elements / token-head
-             (+ the 3 x 31 taps per channel, once per launch)
-    chunks : read q', k', v', alpha (3 dk + dv) and beta (1); write the chunk
-             transform W, Qt, Kh (3 dk), Bq (64: a 64x64 block per 64 tokens)
-             and Ut (dv), plus the fp32 chunk decay (dk per 64 tokens)
-    scan   : read that transform back; write o (dv).  (The segmented state pass
-             reads the W, Kh, Ut and Gam of every chunk outside a stream's last
-             segment a second time, for the segment summaries: traffic above
-             these bytes, reported by the counters.)
+    conv     : read q, k, v and write q', k', v'                  (3 dk + 3 dv) elements
+               (+ the 3 x 31 taps per channel, once per launch)
+    chunks   : read q', k', v', alpha (3 dk + dv) and beta (1); write a chunk
+               workspace of five vectors per token (three over dk: W, the output
+               operator, Kh; two over dv: Ut and the intra-chunk output)
+                                                                  (6 dk + 3 dv + 1)
+    scan     : read that workspace back and write o               (3 dk + 3 dv)
+    path_min : conv in and out, KDA in and out (no workspace)
+    The workspace these kernels exchange is smaller than those five vectors: W, Qt and
+    Kh over dk, Bq as 64 values and Ut over dv per token-head, plus the fp32 chunk decay
+    per chunk.  What their interfaces move with it is in chunks_interface and
+    scan_interface.  (The segmented state pass reads the W, Kh, Ut and decay of every
+    chunk outside a stream's last segment a second time, for the segment summaries:
+    traffic above these bytes, reported by the counters.)
     """
     es = 4 if cfg.dtype == "f32" else 2
     th = cfg.B * cfg.T * cfg.H                      # token-heads per launch
+    dk, dv = cfg.dk, cfg.dv
     nch = (cfg.T + 63) // 64
     chunk_heads = cfg.B * cfg.H * nch
-    conv = th * (3 * cfg.dk + 3 * cfg.dv) * es
-    conv += 31 * cfg.H * (2 * cfg.dk + cfg.dv) * es
-    ws = th * (3 * cfg.dk + 64 + cfg.dv) * es + chunk_heads * cfg.dk * 4
-    chunks = th * ((3 * cfg.dk + cfg.dv) * es + es) + ws
-    scan = ws + th * cfg.dv * es
-    path_min = th * ((3 * cfg.dk + 3 * cfg.dv) * es + (3 * cfg.dk + cfg.dv + 1) * es + cfg.dv * es)
-    return {"conv": conv, "chunks": chunks, "scan": scan, "path_min": path_min}
+    conv = th * (3 * dk + 3 * dv) * es
+    conv += 31 * cfg.H * (2 * dk + dv) * es
+    chunks = th * (6 * dk + 3 * dv + 1) * es
+    scan = th * (3 * dk + 3 * dv) * es
+    ws = th * (3 * dk + 64 + dv) * es + chunk_heads * dk * 4
+    chunks_if = th * ((3 * dk + dv) * es + es) + ws
+    scan_if = ws + th * dv * es
+    path_min = th * ((3 * dk + 3 * dv) * es + (3 * dk + dv + 1) * es + dv * es)
+    return {"conv": conv, "chunks": chunks, "scan": scan, "path_min": path_min,
+            "chunks_interface": chunks_if, "scan_interface": scan_if}
 
 
 def seg_plan(cfg):
@@ -494,6 +506,36 @@ def backward_cpu_baseline(cfg, tokens: int) -> dict:
                           sample.T, sample.H, sample.dk, sample.dv, dt)}
 
 
+def fused_path(torch, kda, cfg, desc, inp, steps, warmup, ms_step):
+    """The same step through kda_conv_kda_forward (the conv formed inside the chunk
+    transform; q', k', v' never written): its time per step beside the two-call path's,
+    and the activation memory it does without."""
+    wt = (inp["w_text_q"], inp["w_text_k"], inp["w_text_v"])
+    wv = (inp["w_vis_q"], inp["w_vis_k"], inp["w_vis_v"])
+    ws = torch.empty(kda.kda_conv_kda_forward_workspace_size(desc, cfg.B, cfg.H, cfg.dk, cfg.dv,
+                                                             cfg.torch_dtype), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(inp["v"])
+    stream = torch.cuda.current_stream()
+
+    def call():
+        kda.kda_conv_kda_forward(desc, inp["q"], inp["k"], inp["v"], wt, wv, inp["alpha"], inp["beta"], o=o,
+                                 workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    es = 4 if cfg.dtype == "f32" else 2
+    return {"call": "kda_conv_kda_forward", "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
+            "time_vs_two_calls": round(ms / ms_step, 3),
+            "activation_bytes_not_held": cfg.B * cfg.T * cfg.H * (2 * cfg.dk + cfg.dv) * es}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -594,6 +636,7 @@ def main() -> int:
     torch.cuda.synchronize()
     cold_ms = sorted(e[0].elapsed_time(e[-1]) for e in cold_ev)
     del scratch
+    fused = fused_path(torch, kda, cfg, desc, inp, args.steps, args.warmup, ms_step=elapsed / args.steps * 1e3)
     copy_gbs = copy_bandwidth(torch)
     gemm_tfs = gemm_tflops(torch)
 
@@ -613,6 +656,8 @@ def main() -> int:
                                "TFLOP/s": round(tf, 1), "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFS, 4)})
         if n + "_f32" in fl:
             kernels[n]["mfma_flop_f32"] = fl[n + "_f32"]
+        if n + "_interface" in rb:
+            kernels[n]["interface_bytes"] = rb[n + "_interface"]
     dom = max(names, key=lambda n: ms[n])
     ms_step = elapsed / args.steps * 1e3
     tokens = cfg.B * cfg.T
@@ -647,6 +692,7 @@ def main() -> int:
         "measured_bf16_gemm_TFLOP/s": round(gemm_tfs, 1),
         "path": {"min_bytes": rb["path_min"], "GB/s_vs_path_min": round(path_gbs, 1),
                  "frac_of_path_roofline": round(path_gbs / HBM_PEAK_GBS, 4)},
+        "fused_path": fused,
     }
     if not args.no_cpu_baseline:
         ref, result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_frames, args.cpu_single_tokens)

@@ -182,6 +182,36 @@ int kda_forward_noalloc(const kda_stream_desc *desc, int B, int H, int dk, int d
                         float *final_state, void *o, void *hip_stream);
 
 /*
+ * The conv and KDA in one call, with the conv inside the chunk transform: the
+ * chunk transform forms the conv outputs q', k', v' of each chunk's rows itself,
+ * from the conv inputs q, k, v and the taps (the operations of kda_conv_forward
+ * above, summed in fp32 in tap order and rounded to the stream dtype), so they
+ * are never written to memory; then the state pass of kda_forward.  This is the
+ * conv-into-KDA fusion that follows from the Chimera pages' core method, where
+ * the modality-aware short conv feeds every KDA update (genai-atlas "How it
+ * works"; paper.rainbus.top 技术新颖性 on the fused conv).  Inputs and outputs
+ * as kda_conv_forward (q, k, v, w_text, w_vis) and kda_forward (alpha, beta,
+ * initial_state, final_state, o) for a uniform batch; the same errors.
+ * Against kda_conv_forward + kda_forward it saves the q', k', v' buffers (3 of
+ * the 5 stream-sized activations a step holds) at the price of time: each
+ * chunk gathers its 3x3x3 neighbourhoods from the conv inputs through the
+ * caches instead of reading q', k', v' once.  o agrees with the two-call path
+ * to the rounding of q', k', v' (the two sum the taps in different orders).
+ * workspace (device, 16-byte aligned, caller-owned, contents undefined after):
+ * at least kda_conv_kda_forward_workspace_size bytes, which is
+ * kda_forward_workspace_size rounded up to 256 bytes plus the three streams'
+ * taps, 31 per channel in the stream dtype.
+ */
+size_t kda_conv_kda_forward_workspace_size(const kda_stream_desc *desc, int B, int H, int dk,
+                                           int dv, kda_dtype dtype);
+int kda_conv_kda_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv,
+                         kda_dtype dtype, const void *q, const void *k, const void *v,
+                         const void *const w_text[3], const void *const w_vis[3],
+                         const void *alpha, const void *beta, const float *initial_state,
+                         float *final_state, void *o, void *workspace, size_t workspace_bytes,
+                         void *hip_stream);
+
+/*
  * The two stages of kda_forward, callable separately with the same shapes,
  * checks and workspace: kda_forward(...) is exactly kda_forward_chunks(...)
  * followed by kda_forward_scan(...) on one stream.  kda_forward_chunks forms

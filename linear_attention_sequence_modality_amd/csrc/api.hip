@@ -382,6 +382,11 @@ int prepare_kda(const Seqs &sq, int H, int dk, int dv, kda_dtype dtype, const vo
     for (int i = 0; i <= kdaconv::kMaxSeqs; ++i) out->seg0[i] = sp.seg0[i];
     for (int i = 0; i < kdaconv::kMaxSeqs; ++i) out->seg_len[i] = sp.seg_len[i];
     out->seg_base = chunk_records_bytes(sq, H, dk, dv, dtype);
+    // no conv inside the chunk transform unless kda_conv_kda_forward sets it up
+    out->cw = nullptr;
+    for (int s = 0; s < 3; ++s) out->cw_off[s] = 0;
+    out->n_text = out->gt = out->gh = out->gw = 0;
+    out->pt = 1;
     return KDA_OK;
 }
 
@@ -412,6 +417,77 @@ int kda_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_d
     if (rc != KDA_OK) return rc;
     return forward(sq, H, dk, dv, dtype, q, k, v, alpha, beta, initial_state, final_state, o, workspace,
                    workspace_bytes, hip_stream);
+}
+
+// The fused entry point's workspace: kda_forward's, then the three streams' taps
+// tap-major (31 per channel, the stream dtype), 256-byte aligned.
+static size_t conv_taps_bytes(int H, int dk, int dv, kda_dtype dtype) {
+    return ((size_t)kdaconv::kConvTaps * (size_t)(2 * H * dk + H * dv) * elem_bytes(dtype) + 255) / 256 * 256;
+}
+
+size_t kda_conv_kda_forward_workspace_size(const kda_stream_desc *desc, int B, int H, int dk, int dv,
+                                           kda_dtype dtype) {
+    Seqs sq;
+    if (uniform_seqs(desc, B, H, dk, dv, dtype, &sq) != KDA_OK) return 0;
+    const size_t ws = workspace_bytes_of(sq, H, dk, dv, dtype);
+    return ws ? (ws + 255) / 256 * 256 + conv_taps_bytes(H, dk, dv, dtype) : 0;
+}
+
+int kda_conv_kda_forward(const kda_stream_desc *desc, int B, int H, int dk, int dv, kda_dtype dtype,
+                         const void *q, const void *k, const void *v, const void *const w_text[3],
+                         const void *const w_vis[3], const void *alpha, const void *beta,
+                         const float *initial_state, float *final_state, void *o, void *workspace,
+                         size_t workspace_bytes, void *hip_stream) {
+    Seqs sq;
+    int rc = uniform_seqs(desc, B, H, dk, dv, dtype, &sq);
+    if (rc != KDA_OK) return rc;
+    // the taps: set, aligned, and not overlapping the outputs (checked with the rest below)
+    if (!w_text || !w_vis) return KDA_ERR_INVALID_ARG;
+    const int Cs[3] = {H * dk, H * dk, H * dv};
+    const size_t es = elem_bytes(dtype);
+    for (int s = 0; s < 3; ++s)
+        if (!w_text[s] || !w_vis[s] || !aligned16(w_text[s]) || !aligned16(w_vis[s])) return KDA_ERR_INVALID_ARG;
+    const size_t need = kda_conv_kda_forward_workspace_size(desc, B, H, dk, dv, dtype);
+    if (B > 0 && need == 0) return KDA_ERR_UNSUPPORTED;
+    if (B > 0 && workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    KdaArgs a;
+    rc = prepare_kda(sq, H, dk, dv, dtype, q, k, v, alpha, beta, initial_state, final_state, o, workspace,
+                     workspace_bytes, true, true, &a);
+    if (rc != KDA_OK) return rc;
+    if (B == 0) return KDA_OK;
+    const size_t kda_ws = (workspace_bytes_of(sq, H, dk, dv, dtype) + 255) / 256 * 256;
+    const Range rtaps = range_of(static_cast<char *>(workspace) + kda_ws, conv_taps_bytes(H, dk, dv, dtype));
+    const Range ro = range_of(o, (size_t)sq.tokens * H * dv * es);
+    const Range rs = final_state ? range_of(final_state, (size_t)B * H * dk * dv * sizeof(float)) : Range{0, 0};
+    for (int s = 0; s < 3; ++s) {
+        const Range rw[2] = {range_of(w_text[s], (size_t)Cs[s] * 4 * es), range_of(w_vis[s], (size_t)Cs[s] * 27 * es)};
+        for (const Range &r : rw)
+            if (overlaps(r, ro) || overlaps(r, rs) || overlaps(r, rtaps)) return KDA_ERR_INVALID_ARG;
+    }
+    // the whole fused workspace clear of the inputs and outputs
+    const Range rall = range_of(workspace, need);
+    const Range rin[5] = {range_of(q, (size_t)sq.tokens * Cs[0] * es), range_of(k, (size_t)sq.tokens * Cs[1] * es),
+                          range_of(v, (size_t)sq.tokens * Cs[2] * es), range_of(alpha, (size_t)sq.tokens * Cs[0] * es),
+                          range_of(beta, (size_t)sq.tokens * H * es)};
+    for (const Range &r : rin)
+        if (overlaps(rall, r)) return KDA_ERR_INVALID_ARG;
+    if (overlaps(rall, ro) || overlaps(rall, rs)) return KDA_ERR_INVALID_ARG;
+    const int off[3] = {0, Cs[0] * kdaconv::kConvTaps, 2 * Cs[0] * kdaconv::kConvTaps};
+    void *cw = static_cast<char *>(workspace) + kda_ws;
+    a.cw = cw;
+    for (int s = 0; s < 3; ++s) a.cw_off[s] = off[s];
+    a.n_text = desc->n_text;
+    a.gt = desc->grid_t;
+    a.gh = desc->grid_h;
+    a.gw = desc->grid_w;
+    if ((int64_t)desc->grid_t * desc->grid_h * desc->grid_w == 0) a.gt = a.gh = a.gw = 0;
+    a.pt = desc->causal_t ? 2 : 1;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (kdaconv::launch_conv_taps_tapmajor(w_text, w_vis, Cs, off, cw, dtype == KDA_BF16, st) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (kdaconv::launch_kda_chunks_conv(a, dtype == KDA_BF16, st) != hipSuccess) return KDA_ERR_HIP;
+    if (kdaconv::launch_kda_scan(a, dtype == KDA_BF16, st) != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
 }
 
 int kda_forward_varlen(const kda_stream_desc *descs, int n_seq, int H, int dk, int dv, kda_dtype dtype,

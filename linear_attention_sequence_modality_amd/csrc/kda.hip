@@ -79,6 +79,12 @@ struct K1Smem {
     static constexpr size_t TB_FP = TB_KH + 4 * DK * 4;
     static constexpr size_t TB_BETA = TB_FP + 6 * DK * 4;
     static constexpr size_t BYTES = round_up(TB_BETA + 64 * 4, 16);
+    // the fused variant (conv in the loader): one head's taps for q, k and v, tap-major
+    // [31][DK | DK | DV] in the stream dtype, after everything else, when they fit
+    static constexpr size_t CW = BYTES;
+    static constexpr size_t CW_BYTES = (size_t)31 * (2 * DK + DV) * sizeof(T);
+    static constexpr bool CW_LDS = round_up(CW + CW_BYTES, 16) <= 160 * 1024;
+    static constexpr size_t BYTES_CONV = CW_LDS ? round_up(CW + CW_BYTES, 16) : BYTES;
 };
 
 __device__ __forceinline__ int fp_index(int R, int S) { return R * (R - 1) / 2 + S; }
@@ -132,12 +138,103 @@ struct Prefetch {
     T beta;   // raw: converted where it is used, so the load is not waited for at issue
 };
 
-template <typename T, int DK, int DV>
+// ---- the conv inside the loader (launch_kda_chunks_conv) ----------------------
+// The modality-aware depthwise conv of the Chimera core method (genai-atlas "How it
+// works"): a text token sums 4 causal taps over the text tokens up to it, a visual
+// token the 3x3x3 neighbourhood of its (t, h, w) cell, with zeros outside the grid
+// (taps at t-1..t+1, or t-2..t with time-causal padding).  A token's taps are
+// walked as 27 slots: visual slot j is tap j = a*9 + b*3 + e; text slot j < 4 is
+// tap 27 + j (token tr - 3 + j), and the other slots are empty.
+struct ConvPlace {
+    int tr;           // stream-relative token
+    int ft, fy, fx;   // its grid cell (visual tokens)
+    bool text;
+};
+__device__ __forceinline__ ConvPlace conv_place(const KdaArgs &a, int tr) {
+    ConvPlace P;
+    P.tr = tr;
+    P.text = tr < a.n_text;
+    const int p = P.text ? 0 : tr - a.n_text, hw = a.gh * a.gw;
+    P.ft = hw ? p / hw : 0;
+    const int rem = p - P.ft * hw;
+    P.fy = a.gw ? rem / a.gw : 0;
+    P.fx = rem - P.fy * a.gw;
+    return P;
+}
+// Slot j of a token: the token it reads (the token itself for an empty slot, whose
+// term is dropped, so every load is in bounds and none waits on a branch), the tap
+// (its weight row) and whether the term counts.
+__device__ __forceinline__ int conv_slot(const KdaArgs &a, const ConvPlace &P, int j, int &tap, bool &ok) {
+    if (P.text) {
+        const int t = P.tr - 3 + j;
+        ok = j < 4 && t >= 0;
+        tap = 27 + (j < 4 ? j : 0);
+        return ok ? t : P.tr;
+    }
+    const int ta = j / 9, tb = (j / 3) % 3, te = j % 3;
+    const int tt = P.ft + ta - a.pt, yy = P.fy + tb - 1, xx = P.fx + te - 1;
+    ok = tt >= 0 && tt < a.gt && yy >= 0 && yy < a.gh && xx >= 0 && xx < a.gw;
+    tap = j;
+    return ok ? a.n_text + (tt * a.gh + yy) * a.gw + xx : P.tr;
+}
+// One conv output row of 8 channels: its stream's tokens (of one sequence) through a
+// buffer resource, C channels per token, channel c0 of the row at element xo of a
+// token, and of tap 0 at element wo of the tap-major taps.
+struct ConvRow {
+    __amdgpu_buffer_rsrc_t x;
+    int C, xo, wo;   // wo: taps in global memory (element offset of tap 0, channel c0; C per tap)
+    int lo, D;       // or in LDS: element offset of tap 0, channel c0, and D per tap
+    ConvPlace P;
+};
+// NO output rows at once, TPR slots per round: each round issues all its loads (the
+// rows' neighbours and taps, one 32-bit offset each) before the first multiply-add.
+// fp32 sums in slot order, rounded to T.
+template <typename T, int NO, int TPR, bool WLDS>
+__device__ __forceinline__ void conv_rows(const KdaArgs &a, __amdgpu_buffer_rsrc_t wr, const T *wl,
+                                          const ConvRow (&o)[NO], Raw8<T> (&out)[NO]) {
+    static_assert(27 % TPR == 0, "whole rounds of slots");
+    constexpr unsigned ES = sizeof(T);
+    float acc[NO][8];
+#pragma unroll
+    for (int n = 0; n < NO; ++n)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[n][i] = 0.f;
+#pragma unroll 1
+    for (int j0 = 0; j0 < 27; j0 += TPR) {
+        Raw8<T> xv[NO][TPR], wv[NO][TPR];
+        bool okv[NO][TPR];
+        int tapv[NO][TPR];
+#pragma unroll
+        for (int u = 0; u < TPR; ++u)
+#pragma unroll
+            for (int n = 0; n < NO; ++n) {
+                const int tok = conv_slot(a, o[n].P, j0 + u, tapv[n][u], okv[n][u]);
+                xv[n][u].load_buf(o[n].x, (unsigned)(tok * o[n].C + o[n].xo) * ES);
+                if constexpr (!WLDS) wv[n][u].load_buf(wr, (unsigned)(tapv[n][u] * o[n].C + o[n].wo) * ES);
+            }
+#pragma unroll
+        for (int u = 0; u < TPR; ++u)
+#pragma unroll
+            for (int n = 0; n < NO; ++n) {
+                // taps in LDS are read where they are used: a round holds only its inputs
+                if constexpr (WLDS) wv[n][u].load(wl + tapv[n][u] * o[n].D + o[n].lo);
+                float xf[8], wf[8];
+                xv[n][u].get(xf);
+                wv[n][u].get(wf);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[n][i] = fmaf(okv[n][u] ? wf[i] : 0.f, xf[i], acc[n][i]);
+            }
+    }
+#pragma unroll
+    for (int n = 0; n < NO; ++n) out[n].set(acc[n]);
+}
+
+template <typename T, int DK, int DV, bool CONV = false>
 __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     using SM = K1Smem<T, DK, DV>;
     using WL = Ws<T, DK, DV>;
     using F = Frag<T>;
-    static_assert(SM::BYTES <= 160 * 1024, "LDS plan exceeds 160 KB");
+    static_assert(SM::BYTES <= 160 * 1024 && SM::BYTES_CONV <= 160 * 1024, "LDS plan exceeds 160 KB");
     constexpr int NCGK = DK / 8, NCGV = DV / 8;   // 8-channel groups
     constexpr int CPW = DK / 8, NA = CPW / 8;      // P0: alpha channels per wave, 8-element loads per lane
     static_assert(K1_THREADS == 512 && C == 64 && NA >= 1 && NA <= 2, "P0 maps chunk rows to the 64 lanes of 8 waves");
@@ -151,6 +248,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     // an item's chunk: head, chunk index over all sequences, first token, valid rows
     struct Loc {
         int h, gc, t0, nr;
+        int sq, tr0;   // sequence and stream-relative first token (uniform batch; the conv loader)
     };
     auto locate = [&](int it) {
         Loc L;
@@ -164,6 +262,10 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
             const int sq = L.gc / a.n_chunks, n = L.gc - sq * a.n_chunks;
             L.t0 = sq * a.T + n * C;
             L.nr = min(C, a.T - n * C);
+            if constexpr (CONV) {
+                L.sq = sq;
+                L.tr0 = n * C;
+            }
         }
         return L;
     };
@@ -210,24 +312,105 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
             for (int j = 0; j < NA; ++j) pf.a[j].load(a_in + off + 8 * j);
             if (tid < C) pf.beta = b_in[(size_t)(t0 + min(tid, nr - 1)) * a.H + h];
         }
+        if constexpr (!CONV) {   // (with the conv, q', k', v' come from conv_inputs)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            if ((parts & LD_KQ) && key_task) {
-                const int r = min(2 * krp + e, nr - 1);
-                const size_t off = ((size_t)(t0 + r) * a.H + h) * DK + kc0;
-                pf.k[e].load(k_in + off);
-                pf.q[e].load(q_in + off);
+            for (int e = 0; e < 2; ++e) {
+                if ((parts & LD_KQ) && key_task) {
+                    const int r = min(2 * krp + e, nr - 1);
+                    const size_t off = ((size_t)(t0 + r) * a.H + h) * DK + kc0;
+                    pf.k[e].load(k_in + off);
+                    pf.q[e].load(q_in + off);
+                }
+                if ((parts & LD_V) && val_task) {
+                    const int rv = min(2 * vrp + e, nr - 1);
+                    pf.v[e].load(v_in + ((size_t)(t0 + rv) * a.H + h) * DV + vc0);
+                }
             }
-            if ((parts & LD_V) && val_task) {
-                const int rv = min(2 * vrp + e, nr - 1);
-                pf.v[e].load(v_in + ((size_t)(t0 + rv) * a.H + h) * DV + vc0);
+        }
+    };
+
+    // The conv inside the loader: q', k', v' of chunk L's rows (the rows this thread
+    // consumes in P1, rows past the end repeating the last row) formed from the conv
+    // inputs, at the top of the chunk's iteration, where little else is live.
+    // (with SM::CW_LDS the head's taps sit in LDS, copied there when the head changes)
+    T *const cw_lds = reinterpret_cast<T *>(smem + SM::CW);
+    int cw_head = -1;
+    auto conv_inputs = [&](const Loc &L, Prefetch<T> &pf) {
+        const int h = L.h, nr = L.nr;
+        const int CK = a.H * DK, CV = a.H * DV;
+        const size_t tk = (size_t)a.T * CK, tv = (size_t)a.T * CV;   // one sequence of a stream, elements
+        // the item's sequence of each stream (the same for every lane) and the taps
+        auto rsrc = [](const void *p, size_t bytes) {
+            return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)(unsigned)bytes, kBufWord3);
+        };
+        const __amdgpu_buffer_rsrc_t wr = rsrc(a.cw, (size_t)kConvTaps * (2 * CK + CV) * sizeof(T));
+        if constexpr (SM::CW_LDS) {
+            if (h != cw_head) {   // uniform: every lane holds the same item
+                // LDS row j of stream s: [s = 0: q | 1: k | 2: v] at (j * (2 DK + DV) + s * DK)
+                constexpr int RW = 2 * DK + DV, PIECES = kConvTaps * RW / 8;
+                const T *g = static_cast<const T *>(a.cw);
+                for (int pc = tid; pc < PIECES; pc += K1_THREADS) {
+                    const int j = pc / (RW / 8), e = 8 * (pc - j * (RW / 8));
+                    const int st = e < DK ? 0 : (e < 2 * DK ? 1 : 2);
+                    const int c = e - st * DK, Cs = st < 2 ? CK : CV, D = st < 2 ? DK : DV;
+                    Raw8<T> w;
+                    w.load(g + a.cw_off[st] + (size_t)j * Cs + h * D + c);
+                    *reinterpret_cast<Raw8<T> *>(cw_lds + j * RW + e) = w;
+                }
+                __syncthreads();
+                cw_head = h;
             }
+        }
+        // every thread forms two rows of k, q and v; a thread past the value rows
+        // (dv < dk) forms rows of its clamped place too and drops them
+        const __amdgpu_buffer_rsrc_t rk = rsrc(k_in + (size_t)L.sq * tk, tk * sizeof(T));
+        const __amdgpu_buffer_rsrc_t rq = rsrc(q_in + (size_t)L.sq * tk, tk * sizeof(T));
+        const __amdgpu_buffer_rsrc_t rv = rsrc(v_in + (size_t)L.sq * tv, tv * sizeof(T));
+        const int xk = h * DK + kc0, xv = h * DV + vc0, RW = 2 * DK + DV;
+        const ConvPlace P0 = conv_place(a, L.tr0 + min(2 * krp, nr - 1));
+        const ConvPlace P1 = conv_place(a, L.tr0 + min(2 * krp + 1, nr - 1));
+        const ConvPlace V0 = conv_place(a, L.tr0 + min(2 * vrp, nr - 1));
+        const ConvPlace V1 = conv_place(a, L.tr0 + min(2 * vrp + 1, nr - 1));
+        const ConvRow rk2[2] = {{rk, CK, xk, a.cw_off[1] + xk, DK + kc0, RW, P0},
+                                {rk, CK, xk, a.cw_off[1] + xk, DK + kc0, RW, P1}};
+        const ConvRow rq2[2] = {{rq, CK, xk, a.cw_off[0] + xk, kc0, RW, P0}, {rq, CK, xk, a.cw_off[0] + xk, kc0, RW, P1}};
+        const ConvRow rv2[2] = {{rv, CV, xv, a.cw_off[2] + xv, 2 * DK + vc0, RW, V0},
+                                {rv, CV, xv, a.cw_off[2] + xv, 2 * DK + vc0, RW, V1}};
+        // as many slots per round (loads in flight) as the registers left at the top of
+        // the iteration hold without spilling
+        Raw8<T> res_v[2];
+        if constexpr (SM::CW_LDS) {
+            const ConvRow rkq[4] = {rk2[0], rk2[1], rq2[0], rq2[1]};
+            Raw8<T> res[4];
+            conv_rows<T, 4, 3, true>(a, wr, cw_lds, rkq, res);
+            pf.k[0] = res[0];
+            pf.k[1] = res[1];
+            pf.q[0] = res[2];
+            pf.q[1] = res[3];
+            conv_rows<T, 2, 3, true>(a, wr, cw_lds, rv2, res_v);
+        } else if constexpr (sizeof(T) == 2) {
+            const ConvRow rkq[4] = {rk2[0], rk2[1], rq2[0], rq2[1]};
+            Raw8<T> res[4];
+            conv_rows<T, 4, 1, false>(a, wr, cw_lds, rkq, res);
+            pf.k[0] = res[0];
+            pf.k[1] = res[1];
+            pf.q[0] = res[2];
+            pf.q[1] = res[3];
+            conv_rows<T, 2, 1, false>(a, wr, cw_lds, rv2, res_v);
+        } else {
+            conv_rows<T, 2, 1, false>(a, wr, cw_lds, rk2, pf.k);
+            conv_rows<T, 2, 1, false>(a, wr, cw_lds, rq2, pf.q);
+            conv_rows<T, 2, 1, false>(a, wr, cw_lds, rv2, res_v);
+        }
+        if (val_task) {
+            pf.v[0] = res_v[0];
+            pf.v[1] = res_v[1];
         }
     };
 
     Prefetch<T> pf;
     int item = blockIdx.x;
-    Loc nxt{0, 0, 0, 0};   // the chunk whose inputs are in the prefetch registers
+    Loc nxt{0, 0, 0, 0, 0, 0};   // the chunk whose inputs are in the prefetch registers
     if (item < n_items) {
         nxt = locate(item);
         load_inputs(nxt, pf, LD_A | LD_KQ | LD_V);
@@ -240,6 +423,7 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     for (; item < n_items; item += gridDim.x) {
         const Loc cur = nxt;
         const int nr = cur.nr;   // valid rows in this chunk
+        if constexpr (CONV) conv_inputs(cur, pf);
         const bool more = item + (int)gridDim.x < n_items;
         if (more) nxt = locate(item + gridDim.x);
         char *wsb = static_cast<char *>(a.ws) + ((size_t)cur.h * total + cur.gc) * WL::BYTES;
@@ -570,6 +754,45 @@ hipError_t launch_chunks_typed(const KdaArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <typename T, int DK, int DV>
+hipError_t launch_chunks_conv_typed(const KdaArgs &a, hipStream_t stream) {
+    using SM = K1Smem<T, DK, DV>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)kda_intra_kernel<T, DK, DV, true>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)SM::BYTES_CONV);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int items = a.H * seq_chk0(a, a.B);
+    const int grid = items < num_cus() ? items : num_cus();
+    hipLaunchKernelGGL((kda_intra_kernel<T, DK, DV, true>), dim3(grid), dim3(K1_THREADS), SM::BYTES_CONV, stream,
+                       a);
+    return hipGetLastError();
+}
+
+// Taps to tap-major: one thread per (stream, tap, channel).
+struct TapArgs {
+    const void *wt[3], *wv[3];
+    void *cw;
+    int C[3], off[3];
+};
+template <typename T>
+__global__ __launch_bounds__(256) void conv_taps_kernel(TapArgs a) {
+    int i = blockIdx.x * 256 + threadIdx.x;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        const int n = kConvTaps * a.C[s];
+        if (i >= 0 && i < n) {
+            const int tap = i / a.C[s], c = i - tap * a.C[s];
+            const T *src = tap < 27 ? static_cast<const T *>(a.wv[s]) + (size_t)c * 27 + tap
+                                    : static_cast<const T *>(a.wt[s]) + (size_t)c * 4 + (tap - 27);
+            static_cast<T *>(a.cw)[a.off[s] + i] = *src;
+        }
+        i -= n;
+    }
+}
+
 
 
 }  // namespace
@@ -601,6 +824,32 @@ size_t kda_chunk_ws_bytes(int dk, int dv, bool bf16) {
 
 hipError_t launch_kda_chunks(const KdaArgs &a, bool bf16, hipStream_t stream) {
     KDA_DISPATCH(launch_chunks_typed)
+}
+
+hipError_t launch_kda_chunks_conv(const KdaArgs &a, bool bf16, hipStream_t stream) {
+    if (a.varlen) return hipErrorInvalidValue;
+    KDA_DISPATCH(launch_chunks_conv_typed)
+}
+
+hipError_t launch_conv_taps_tapmajor(const void *const wt[3], const void *const wv[3], const int Cs[3],
+                                     const int off[3], void *cw, bool bf16, hipStream_t stream) {
+    TapArgs a;
+    int64_t total = 0;
+    for (int s = 0; s < 3; ++s) {
+        a.wt[s] = wt[s];
+        a.wv[s] = wv[s];
+        a.C[s] = Cs[s];
+        a.off[s] = off[s];
+        total += (int64_t)kConvTaps * Cs[s];
+    }
+    a.cw = cw;
+    if (total == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    if (bf16)
+        hipLaunchKernelGGL(conv_taps_kernel<bf16_t>, dim3(blocks), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(conv_taps_kernel<float>, dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace kdaconv

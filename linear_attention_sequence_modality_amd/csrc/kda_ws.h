@@ -48,6 +48,15 @@ template <typename T> struct Raw8;
 template <> struct Raw8<bf16_t> {
     uint4 u;
     __device__ __forceinline__ void load(const bf16_t *p) { u = *reinterpret_cast<const uint4 *>(p); }
+    // 8 elements at byte offset off of a buffer resource
+    __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+    // fp32 values rounded to bf16 (nearest even)
+    __device__ __forceinline__ void set(const float (&x)[8]) {
+        u = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                       pack_bf16x2(x[6], x[7]));
+    }
     __device__ __forceinline__ void zero() { u = make_uint4(0u, 0u, 0u, 0u); }
     __device__ __forceinline__ void get(float (&x)[8]) const {
         x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
@@ -61,6 +70,14 @@ template <> struct Raw8<float> {
         b = *reinterpret_cast<const float4 *>(p + 4);
     }
     __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u, 0, 0));
+    }
+    __device__ __forceinline__ void set(const float (&x)[8]) {
+        a = make_float4(x[0], x[1], x[2], x[3]);
+        b = make_float4(x[4], x[5], x[6], x[7]);
+    }
     __device__ __forceinline__ void get(float (&x)[8]) const {
         x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
     }

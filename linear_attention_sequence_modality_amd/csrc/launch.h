@@ -66,6 +66,16 @@ struct KdaArgs {
     int n_seg_u, seg_len_u;
     int seg0[kMaxSeqs + 1], seg_len[kMaxSeqs];
     size_t seg_base;     // byte offset of the segment records in ws
+    // The conv inside the chunk transform (launch_kda_chunks_conv, a uniform
+    // batch): q, k and v above are the conv INPUTS, and the chunk transform
+    // forms q', k', v' itself.  cw + cw_off[s] elements holds stream s's taps
+    // tap-major in the stream dtype, [31][C[s]] (visual tap a*9 + b*3 + e, then
+    // the 4 text taps), written by launch_conv_taps_tapmajor; n_text, gt, gh, gw
+    // give the stream layout and pt the time offset of the visual taps (1:
+    // symmetric padding, 2: time-causal).
+    const void *cw;
+    int cw_off[3];
+    int n_text, gt, gh, gw, pt;
 };
 // First token and first chunk of sequence i (i = B: the totals).
 __host__ __device__ inline int seq_tok0(const KdaArgs &a, int i) { return a.varlen ? a.tok0[i] : i * a.T; }
@@ -109,6 +119,13 @@ size_t kda_chunk_ws_bytes(int dk, int dv, bool bf16);
 // over them (segment summaries, the chain of segment start states, and the
 // replay of every segment writing o and the final state).
 hipError_t launch_kda_chunks(const KdaArgs &a, bool bf16, hipStream_t stream);
+// The chunk transform with the conv in its loader (the conv fields of KdaArgs set).
+hipError_t launch_kda_chunks_conv(const KdaArgs &a, bool bf16, hipStream_t stream);
+// Taps of the three streams, w_text [C[s], 4] and w_vis [C[s], 27] in the stream
+// dtype, into cw tap-major (same dtype): stream s at element off[s], [31][C[s]].
+constexpr int kConvTaps = 31;
+hipError_t launch_conv_taps_tapmajor(const void *const wt[3], const void *const wv[3], const int Cs[3],
+                                     const int off[3], void *cw, bool bf16, hipStream_t stream);
 hipError_t launch_kda_scan(const KdaArgs &a, bool bf16, hipStream_t stream);
 // Compute units of the current device.
 int num_cus();

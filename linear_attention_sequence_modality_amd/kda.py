@@ -30,7 +30,8 @@ EXPORTED_SYMBOLS = ("kda_conv_forward", "kda_conv_forward_stream", "kda_forward_
                     "kda_forward_chunks", "kda_forward_scan", "kda_forward_varlen_workspace_size",
                     "kda_forward_varlen", "kda_conv_forward_varlen", "mla_attention_forward",
                     "kda_backward_workspace_size", "kda_backward", "kda_conv_backward", "kda_status_string",
-                    "kda_forward_noalloc", "mla_latent_forward")
+                    "kda_forward_noalloc", "mla_latent_forward", "kda_conv_kda_forward_workspace_size",
+                    "kda_conv_kda_forward")
 KDA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -99,6 +100,11 @@ def load_library():
                                       ctypes.POINTER(vp), vp]
     lib.mla_attention_forward.restype = i32
     lib.mla_attention_forward.argtypes = [i32] * 7 + [vp] * 5 + [ctypes.c_float, vp, vp]
+    lib.kda_conv_kda_forward_workspace_size.restype = ctypes.c_size_t
+    lib.kda_conv_kda_forward_workspace_size.argtypes = [desc_p, i32, i32, i32, i32, i32]
+    lib.kda_conv_kda_forward.restype = i32
+    lib.kda_conv_kda_forward.argtypes = [desc_p, i32, i32, i32, i32, i32, vp, vp, vp, ctypes.POINTER(vp),
+                                         ctypes.POINTER(vp), vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.mla_latent_forward.restype = i32
     lib.mla_latent_forward.argtypes = [ctypes.c_int64] + [i32] * 7 + [vp] * 10
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -167,6 +173,51 @@ def kda_forward_workspace_size(desc: KdaStreamDesc, B: int, H: int, dk: int, dv:
                                dtype) -> int:
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     return int(load_library().kda_forward_workspace_size(ctypes.byref(desc), B, H, dk, dv, code))
+
+
+def kda_conv_kda_forward_workspace_size(desc: KdaStreamDesc, B: int, H: int, dk: int, dv: int,
+                                        dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(load_library().kda_conv_kda_forward_workspace_size(ctypes.byref(desc), B, H, dk, dv, code))
+
+
+def kda_conv_kda_forward(desc: KdaStreamDesc, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         w_text: Sequence[torch.Tensor], w_vis: Sequence[torch.Tensor],
+                         alpha: torch.Tensor, beta: torch.Tensor,
+                         initial_state: Optional[torch.Tensor] = None,
+                         final_state: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Conv + KDA in one call, the conv formed inside the chunk transform (q', k', v' are
+    never written); q, k, v are the conv inputs.  Returns o [B,T,H,dv] (final_state filled
+    in place if given)."""
+    lib = load_library()
+    dt = q.dtype
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (alpha, "alpha"), (beta, "beta")):
+        _check(t, nm, dt)
+    for i in range(3):
+        _check(w_text[i], "w_text[%d]" % i, dt)
+        _check(w_vis[i], "w_vis[%d]" % i, dt)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None:
+            _check(t, nm, torch.float32)
+    made_o, made_ws = o is None, workspace is None
+    o = torch.empty_like(v) if o is None else o
+    _check(o, "o", dt)
+    need = kda_conv_kda_forward_workspace_size(desc, B, H, dk, dv, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _hand_over(stream, q.device, o if made_o else None, workspace if made_ws else None)
+    wt = (ctypes.c_void_p * 3)(*[w.data_ptr() for w in w_text])
+    wv = (ctypes.c_void_p * 3)(*[w.data_ptr() for w in w_vis])
+    rc = lib.kda_conv_kda_forward(ctypes.byref(desc), B, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v),
+                                  wt, wv, _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(final_state),
+                                  _ptr(o), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError("kda_conv_kda_forward", rc)
+    return o
 
 
 def supports(dtype, dk: int, dv: int) -> bool:

@@ -62,12 +62,17 @@ def test_mfma_model_equals_the_recorded_counters():
 
 
 def test_algorithmic_bytes_per_token_head():
+    """The measurement plan's figures at d = 128 in bf16: conv 1536, chunk transform 2306,
+    state pass 1536, path minimum 2818 bytes per token-head."""
     cfg = WORKLOAD["video_5s_480x832"]
     th = cfg.B * cfg.T * cfg.H
     rb = bench.roofline_bytes(cfg)
     taps = 31 * cfg.H * (2 * cfg.dk + cfg.dv) * 2
-    assert rb["conv"] == th * 6 * 128 * 2 + taps          # q, k, v in and out
+    assert rb["conv"] == th * 1536 + taps                 # q, k, v in and out
+    assert rb["chunks"] == th * 2306                      # q', k', v', alpha, beta in; 5 d workspace out
+    assert rb["scan"] == th * 1536                        # 5 d workspace in; o out
     assert rb["path_min"] == th * 2818                    # conv in/out + KDA in/out
     nch = (cfg.T + 63) // 64
     ws = th * (3 * 128 + 64 + 128) * 2 + cfg.B * cfg.H * nch * 128 * 4
-    assert rb["scan"] == ws + th * 128 * 2                # the workspace once, o once
+    assert rb["scan_interface"] == ws + th * 128 * 2      # this design's workspace once, o once
+    assert rb["chunks_interface"] == th * (4 * 128 + 1) * 2 + ws
