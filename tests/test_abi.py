@@ -160,6 +160,45 @@ def test_forward_rejects_bad_arguments(lib):
     assert _fwd(lib, d, sT=ctypes.c_void_p(FAKE + 3 * (1 << 32))) == kda.KDA_ERR_INVALID_ARG  # sT overlaps alpha
 
 
+def _fused(lib, desc, B=1, H=2, dk=64, dv=64, dtype=kda.KDA_BF16, ptrs=None, wt=None, wv=None, sT=None,
+           ws=FAKE + 40 * (1 << 32), ws_bytes=1 << 40):
+    p = ptrs if ptrs is not None else _ptrs(6)
+    wt = wt if wt is not None else (ctypes.c_void_p * 3)(*[FAKE + (20 + i) * (1 << 32) for i in range(3)])
+    wv = wv if wv is not None else (ctypes.c_void_p * 3)(*[FAKE + (30 + i) * (1 << 32) for i in range(3)])
+    return lib.kda_conv_kda_forward(ctypes.byref(desc) if desc is not None else None, B, H, dk, dv, dtype,
+                                    p[0], p[1], p[2], wt, wv, p[3], p[4], None, sT, p[5],
+                                    ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+
+
+def test_fused_workspace_and_argument_checks(lib):
+    """kda_conv_kda_forward: its workspace is kda_forward's plus the taps, and it rejects
+    bad arguments (every call below fails validation before any HIP call)."""
+    d = _desc()
+    for dt in (kda.KDA_BF16, kda.KDA_F32):
+        base = kda.kda_forward_workspace_size(d, 1, 2, 64, 128, dt)
+        fused = kda.kda_conv_kda_forward_workspace_size(d, 1, 2, 64, 128, dt)
+        es = 2 if dt == kda.KDA_BF16 else 4
+        assert fused == (base + 255) // 256 * 256 + (31 * (2 * 2 * 64 + 2 * 128) * es + 255) // 256 * 256
+    assert kda.kda_conv_kda_forward_workspace_size(d, 1, 2, 96, 64, kda.KDA_BF16) == 0
+    assert _fused(lib, None) == kda.KDA_ERR_INVALID_ARG
+    assert _fused(lib, d, dk=32) == kda.KDA_ERR_UNSUPPORTED
+    wt = (ctypes.c_void_p * 3)(FAKE + 20 * (1 << 32), None, FAKE + 22 * (1 << 32))
+    assert _fused(lib, d, wt=wt) == kda.KDA_ERR_INVALID_ARG                        # a null tap array
+    wv = (ctypes.c_void_p * 3)(FAKE + 30 * (1 << 32), FAKE + 31 * (1 << 32) + 2, FAKE + 32 * (1 << 32))
+    assert _fused(lib, d, wv=wv) == kda.KDA_ERR_INVALID_ARG                        # misaligned taps
+    need = kda.kda_conv_kda_forward_workspace_size(d, 1, 2, 64, 64, kda.KDA_BF16)
+    assert _fused(lib, d, ws_bytes=need - 1) == kda.KDA_ERR_WORKSPACE               # kda_forward's is not enough
+    assert _fused(lib, d, ws=0) == kda.KDA_ERR_WORKSPACE
+    p = _ptrs(6)
+    p[5] = ctypes.c_void_p(FAKE + 2 * (1 << 32))                                    # o aliases v
+    assert _fused(lib, d, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    p = _ptrs(6)
+    p[5] = ctypes.c_void_p(FAKE + 21 * (1 << 32))                                   # o over the k taps
+    assert _fused(lib, d, ptrs=p) == kda.KDA_ERR_INVALID_ARG
+    wt = (ctypes.c_void_p * 3)(FAKE + 20 * (1 << 32), FAKE + 40 * (1 << 32) + need - 64, FAKE + 22 * (1 << 32))
+    assert _fused(lib, d, wt=wt) == kda.KDA_ERR_INVALID_ARG                        # taps inside the workspace
+
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
