@@ -44,9 +44,9 @@ KERNEL_SOURCES = {
 # "kda_backward" is the sum over its three launches (records, ordered passes, gradients) per call,
 # "scan" over the state pass's three (summaries, chain, replay), "mla_latent" over its two.
 MEASURED_TRAFFIC = {
-    ("video_5s_480x832", "conv"): ("f5a252ae652253e0", 229826.0, 399264.0),
-    ("video_5s_480x832", "chunks"): ("aab278612c3b235c", 270457.2, 586560.4),
-    ("video_5s_480x832", "scan"): ("f47b4b38c6e4a7fe", 517495.3, 180305.8),
+    ("video_5s_480x832", "conv"): ("f5a252ae652253e0", 231076.8, 399264.0),
+    ("video_5s_480x832", "chunks"): ("cfa2c67a3dfbdee9", 270451.6, 586560.9),
+    ("video_5s_480x832", "scan"): ("f47b4b38c6e4a7fe", 517495.3, 180238.0),
     ("mla_video_5s_480x832", "mla"): ("9bcc320e76aca060", 1537386.9, 133088.0),
     ("mla_video_5s_480x832", "mla_latent"): ("e6aee03f454abe42", 235091.0, 303607.0),
     ("video_5s_480x832", "kda_backward"): ("13098d71929cd177", 11418126.2, 10718472.9),
@@ -54,7 +54,7 @@ MEASURED_TRAFFIC = {
 # Matrix-core operations per dispatch (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
 # SQ_INSTS_VALU_MFMA_MOPS_F32, each count is 512 flops), taken the same way.
 MEASURED_MFMA_MOPS = {
-    ("video_5s_480x832", "chunks"): ("aab278612c3b235c", 46858240.0, 2129920.0),
+    ("video_5s_480x832", "chunks"): ("cfa2c67a3dfbdee9", 46858240.0, 2129920.0),
     ("video_5s_480x832", "scan"): ("f47b4b38c6e4a7fe", 244776960.0, 2097152.0),
     ("mla_video_5s_480x832", "mla"): ("9bcc320e76aca060", 22151168000.0, 0.0),
     ("mla_video_5s_480x832", "mla_latent"): ("e6aee03f454abe42", 425984000.0, 0.0),

@@ -229,6 +229,66 @@ __device__ __forceinline__ void conv_rows(const KdaArgs &a, __amdgpu_buffer_rsrc
     for (int n = 0; n < NO; ++n) out[n].set(acc[n]);
 }
 
+// Two consecutive visual rows, tokens P0.tr and P0.tr + 1 of one sequence (the pair of rows
+// a thread consumes in P1), of NT tensors, with the taps in LDS (RW elements per tap).  The
+// neighbour (t + a - pt, h + b - 1, w + e - 1) of token tr is token tr + off + e - 1 with
+// off = (a - pt) h w + (b - 1) w wherever it lies in the grid, so for each (a, b) the three
+// e taps of both rows read the 4 tokens P0.tr + off - 1 .. P0.tr + off + 2: 4 NT loads a
+// round, 9 rounds.  Tokens outside the stream are clamped into it (only empty taps read
+// them).  A second row past the chunk's end repeats the first (P1 = P0): it is formed from
+// the wrong tokens and dropped where it is used.
+template <typename T, int NT>
+__device__ __forceinline__ void conv_pair_visual(const KdaArgs &a, const T *wl, int RW, const ConvPlace &P0,
+                                                 const ConvPlace &P1, const ConvRow (&o)[NT],
+                                                 Raw8<T> (&out)[NT][2]) {
+    constexpr unsigned ES = sizeof(T);
+    float acc[NT][2][8];
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[n][0][i] = acc[n][1][i] = 0.f;
+    const int hw = a.gh * a.gw, last = a.T - 1;
+#pragma unroll 1
+    for (int ab = 0; ab < 9; ++ab) {
+        const int ta = ab / 3, tb = ab - 3 * ta;
+        const int base = P0.tr + (ta - a.pt) * hw + (tb - 1) * a.gw - 1;
+        Raw8<T> xv[NT][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int tok = min(max(base + q, 0), last);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) xv[n][q].load_buf(o[n].x, (unsigned)(tok * o[n].C + o[n].xo) * ES);
+        }
+        const int tt0 = P0.ft + ta - a.pt, yy0 = P0.fy + tb - 1, tt1 = P1.ft + ta - a.pt, yy1 = P1.fy + tb - 1;
+        const bool in0 = tt0 >= 0 && tt0 < a.gt && yy0 >= 0 && yy0 < a.gh;
+        const bool in1 = tt1 >= 0 && tt1 < a.gt && yy1 >= 0 && yy1 < a.gh;
+#pragma unroll
+        for (int e = 0; e < 3; ++e) {
+            const bool ok0 = in0 && P0.fx + e - 1 >= 0 && P0.fx + e - 1 < a.gw;
+            const bool ok1 = in1 && P1.fx + e - 1 >= 0 && P1.fx + e - 1 < a.gw;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                Raw8<T> w;
+                w.load(wl + (ab * 3 + e) * RW + o[n].lo);
+                float wf[8], x0[8], x1[8];
+                w.get(wf);
+                xv[n][e].get(x0);
+                xv[n][e + 1].get(x1);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    acc[n][0][i] = fmaf(ok0 ? wf[i] : 0.f, x0[i], acc[n][0][i]);
+                    acc[n][1][i] = fmaf(ok1 ? wf[i] : 0.f, x1[i], acc[n][1][i]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        out[n][0].set(acc[n][0]);
+        out[n][1].set(acc[n][1]);
+    }
+}
+
 template <typename T, int DK, int DV, bool CONV = false>
 __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
     using SM = K1Smem<T, DK, DV>;
@@ -376,18 +436,48 @@ __global__ __launch_bounds__(K1_THREADS) void kda_intra_kernel(KdaArgs a) {
         const ConvRow rq2[2] = {{rq, CK, xk, a.cw_off[0] + xk, kc0, RW, P0}, {rq, CK, xk, a.cw_off[0] + xk, kc0, RW, P1}};
         const ConvRow rv2[2] = {{rv, CV, xv, a.cw_off[2] + xv, 2 * DK + vc0, RW, V0},
                                 {rv, CV, xv, a.cw_off[2] + xv, 2 * DK + vc0, RW, V1}};
-        // as many slots per round (loads in flight) as the registers left at the top of
-        // the iteration hold without spilling
+        // as many loads per round as the registers left at the top of the iteration hold
+        // without spilling; a visual pair of rows shares its neighbours (conv_pair_visual),
+        // and at dk = dv the k, q and v rows are the same two tokens
         Raw8<T> res_v[2];
-        if constexpr (SM::CW_LDS) {
-            const ConvRow rkq[4] = {rk2[0], rk2[1], rq2[0], rq2[1]};
-            Raw8<T> res[4];
-            conv_rows<T, 4, 3, true>(a, wr, cw_lds, rkq, res);
-            pf.k[0] = res[0];
-            pf.k[1] = res[1];
-            pf.q[0] = res[2];
-            pf.q[1] = res[3];
-            conv_rows<T, 2, 3, true>(a, wr, cw_lds, rv2, res_v);
+        if constexpr (SM::CW_LDS && DK == DV) {
+            if (!P0.text) {
+                const ConvRow r3[3] = {rk2[0], rq2[0], rv2[0]};
+                Raw8<T> res[3][2];
+                conv_pair_visual<T, 3>(a, cw_lds, RW, P0, P1, r3, res);
+                pf.k[0] = res[0][0];
+                pf.k[1] = res[0][1];
+                pf.q[0] = res[1][0];
+                pf.q[1] = res[1][1];
+                res_v[0] = res[2][0];
+                res_v[1] = res[2][1];
+            } else {   // text rows (the first chunks of a stream): slot by slot
+                conv_rows<T, 2, 3, true>(a, wr, cw_lds, rk2, pf.k);
+                conv_rows<T, 2, 3, true>(a, wr, cw_lds, rq2, pf.q);
+                conv_rows<T, 2, 3, true>(a, wr, cw_lds, rv2, res_v);
+            }
+        } else if constexpr (SM::CW_LDS) {
+            if (!P0.text) {
+                const ConvRow rkq[2] = {rk2[0], rq2[0]};
+                Raw8<T> res[2][2];
+                conv_pair_visual<T, 2>(a, cw_lds, RW, P0, P1, rkq, res);
+                pf.k[0] = res[0][0];
+                pf.k[1] = res[0][1];
+                pf.q[0] = res[1][0];
+                pf.q[1] = res[1][1];
+            } else {
+                conv_rows<T, 2, 3, true>(a, wr, cw_lds, rk2, pf.k);
+                conv_rows<T, 2, 3, true>(a, wr, cw_lds, rq2, pf.q);
+            }
+            if (!V0.text) {
+                const ConvRow rv1[1] = {rv2[0]};
+                Raw8<T> res[1][2];
+                conv_pair_visual<T, 1>(a, cw_lds, RW, V0, V1, rv1, res);
+                res_v[0] = res[0][0];
+                res_v[1] = res[0][1];
+            } else {
+                conv_rows<T, 2, 3, true>(a, wr, cw_lds, rv2, res_v);
+            }
         } else if constexpr (sizeof(T) == 2) {
             const ConvRow rkq[4] = {rk2[0], rk2[1], rq2[0], rq2[1]};
             Raw8<T> res[4];
