@@ -15,7 +15,7 @@ from linear_attention_sequence_modality_amd import kda
 from linear_attention_sequence_modality_amd.inputs import WORKLOAD, StreamConfig, make_inputs
 
 from gpu_common import (TOL, check_stream, desc_of, heads_slice, oracle_conv_heads, oracle_end_to_end_heads,
-                        rel, say, to_dev)
+                        rel, run_path, say, to_dev)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -79,6 +79,7 @@ EDGE = [
     _small("vision_only", n_text=0, grid=(2, 7, 11)),
     _small("single_token", n_text=1, grid=(0, 0, 0)),
     _small("single_visual_token", n_text=0, grid=(1, 1, 1)),
+    _small("single_token_fp32", n_text=1, grid=(0, 0, 0), dk=64, dv=64, dtype="f32"),
     _small("image_grid_t1", n_text=3, grid=(1, 12, 20)),
     _small("batch3", B=3, n_text=5, grid=(2, 6, 7)),
     _small("causal_t", causal_t=1, grid=(4, 5, 6)),
@@ -105,6 +106,48 @@ EDGE = [
 @pytest.mark.parametrize("cfg", EDGE, ids=[c.name for c in EDGE])
 def test_edge_case(cfg):
     _check_stream(cfg, make_inputs(cfg))
+
+
+@pytest.mark.timeout(120)
+@pytest.mark.parametrize("name", ["single_token", "single_visual_token"])
+def test_one_token_error_is_the_rounding_of_q_and_k(name):
+    """A one-token bf16 stream with no initial state has o = beta (q'.k') v'.
+
+    The dot product cancels: q'.k' is small next to sum |q'_i k'_i|, and the
+    bf16 rounding of the stored q' and k' moves it by up to 2u times that sum
+    (u = 2^-8). So against the fp64 oracle the error of o is the cancellation
+    ratio kappa = sum |q'_i k'_i| / |q'.k'| times the rounding, and kappa, not
+    the path, sets the error.
+
+    Fed the oracle's own conv outputs rounded to bf16 (round to nearest even
+    through fp32, as the path stores them), the oracle must agree with the path
+    to the three roundings that are left: q'.k' and beta v' as operands of the
+    product, and o itself. Each is at most u relative, so the gate is 3u, with no
+    kappa in it."""
+    cfg = next(c for c in EDGE if c.name == name)
+    inp = make_inputs(cfg)
+    qc, kc, vc, o, _ = run_path(cfg, to_dev(inp))
+    heads = tuple(range(cfg.H))
+    rq, rk, rv, ro, _ = oracle_end_to_end_heads(cfg, inp, heads)
+
+    def bf16(x):
+        return torch.from_numpy(x).float().bfloat16().double().numpy()
+
+    beta = heads_slice(inp["beta"][..., None], heads)[..., 0]
+    ro_r, _ = oracle.kda_recurrence(bf16(rq), bf16(rk), bf16(rv), heads_slice(inp["alpha"], heads), beta,
+                                    want_state=False)
+    oh = heads_slice(o, heads)
+    u = 2.0 ** -8
+    kappa = np.abs(rq * rk).sum(-1) / np.abs((rq * rk).sum(-1))          # [B, 1, H]
+    e_full, e_round = rel(oh, ro), rel(oh, ro_r)
+    say("  %s: kappa per head %s; o vs oracle %.2e (2 u kappa = %.2e), vs oracle on bf16 q', k', v' %.2e "
+        "(gate 3u = %.2e)" % (name, np.array2string(kappa.ravel(), precision=1), e_full,
+                              2 * u * kappa.max(), e_round, 3 * u))
+    assert e_full <= TOL["bf16"]
+    assert e_round <= 3 * u
+    # the closed form the two oracles follow at T = 1
+    closed = beta[..., None] * (rq * rk).sum(-1, keepdims=True) * rv
+    assert np.allclose(ro, closed, rtol=1e-12, atol=1e-12 * np.abs(closed).max())
 
 
 @pytest.mark.timeout(120)
