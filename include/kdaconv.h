@@ -200,7 +200,9 @@ int kda_forward_noalloc(const kda_stream_desc *desc, int B, int H, int dk, int d
  * workspace (device, 16-byte aligned, caller-owned, contents undefined after):
  * at least kda_conv_kda_forward_workspace_size bytes, which is
  * kda_forward_workspace_size rounded up to 256 bytes plus the three streams'
- * taps, 31 per channel in the stream dtype.
+ * taps, 31 per channel in the stream dtype.  KDA_ERR_INVALID_ARG also when a
+ * tap array overlaps o, final_state or the workspace, or the workspace
+ * overlaps any input or output (the call writes all of the workspace).
  */
 size_t kda_conv_kda_forward_workspace_size(const kda_stream_desc *desc, int B, int H, int dk,
                                            int dv, kda_dtype dtype);

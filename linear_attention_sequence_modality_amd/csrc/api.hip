@@ -456,16 +456,16 @@ int kda_conv_kda_forward(const kda_stream_desc *desc, int B, int H, int dk, int 
     if (rc != KDA_OK) return rc;
     if (B == 0) return KDA_OK;
     const size_t kda_ws = (workspace_bytes_of(sq, H, dk, dv, dtype) + 255) / 256 * 256;
-    const Range rtaps = range_of(static_cast<char *>(workspace) + kda_ws, conv_taps_bytes(H, dk, dv, dtype));
     const Range ro = range_of(o, (size_t)sq.tokens * H * dv * es);
     const Range rs = final_state ? range_of(final_state, (size_t)B * H * dk * dv * sizeof(float)) : Range{0, 0};
+    // the whole fused workspace (chunk records, then the tap-major taps) clear of the taps,
+    // the other inputs and the outputs: the call writes all of it
+    const Range rall = range_of(workspace, need);
     for (int s = 0; s < 3; ++s) {
         const Range rw[2] = {range_of(w_text[s], (size_t)Cs[s] * 4 * es), range_of(w_vis[s], (size_t)Cs[s] * 27 * es)};
         for (const Range &r : rw)
-            if (overlaps(r, ro) || overlaps(r, rs) || overlaps(r, rtaps)) return KDA_ERR_INVALID_ARG;
+            if (overlaps(r, ro) || overlaps(r, rs) || overlaps(r, rall)) return KDA_ERR_INVALID_ARG;
     }
-    // the whole fused workspace clear of the inputs and outputs
-    const Range rall = range_of(workspace, need);
     const Range rin[5] = {range_of(q, (size_t)sq.tokens * Cs[0] * es), range_of(k, (size_t)sq.tokens * Cs[1] * es),
                           range_of(v, (size_t)sq.tokens * Cs[2] * es), range_of(alpha, (size_t)sq.tokens * Cs[0] * es),
                           range_of(beta, (size_t)sq.tokens * H * es)};

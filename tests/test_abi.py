@@ -197,6 +197,8 @@ def test_fused_workspace_and_argument_checks(lib):
     assert _fused(lib, d, ptrs=p) == kda.KDA_ERR_INVALID_ARG
     wt = (ctypes.c_void_p * 3)(FAKE + 20 * (1 << 32), FAKE + 40 * (1 << 32) + need - 64, FAKE + 22 * (1 << 32))
     assert _fused(lib, d, wt=wt) == kda.KDA_ERR_INVALID_ARG                        # taps inside the workspace
+    wv = (ctypes.c_void_p * 3)(FAKE + 30 * (1 << 32), FAKE + 40 * (1 << 32) + 4096, FAKE + 32 * (1 << 32))
+    assert _fused(lib, d, wv=wv) == kda.KDA_ERR_INVALID_ARG                        # taps among the chunk records
 
 
 def test_binding_refuses_host_tensors():
