@@ -94,6 +94,14 @@ def test_fused_at_the_video_workload_sampled_heads():
     _check(WORKLOAD["video_5s_480x832"], heads=(5, 12))
 
 
+@pytest.mark.timeout(600)
+def test_fused_at_the_image_workload_sampled_heads():
+    """The 4096x4096 image stream (T = 66 048: one latent slice of 256 x 256, 16 heads,
+    bf16), whose chunks each span a quarter of an image row: o and S_T of two heads
+    against the oracle, and the whole o against the two-call path."""
+    _check(WORKLOAD["image_4096px"], heads=(3, 10))
+
+
 @pytest.mark.timeout(120)
 def test_fused_refusals():
     cfg = CASES[3]
