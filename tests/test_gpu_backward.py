@@ -125,6 +125,45 @@ def test_conv_backward_matches_the_adjoint_oracle(cfg):
         assert e_x <= tol and e_t <= tol and (cfg.n_vis == 0 or e_v <= tol)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,h", [("video_5s_480x832", 7), ("image_4096px", 2)])
+def test_conv_backward_at_full_size_one_head(name, h):
+    """kda_conv_backward over a whole workload stream (every channel, in the launch
+    configuration of bench.py --backward): the input and tap gradients of one head's
+    channels of q, k and v against the adjoint oracle run on those channels alone (the
+    conv is depthwise).  The 4096x4096 image is a single latent slice, so its tap
+    gradients sum every tap over 65 536 tokens and its mirrored-tap conv takes the
+    single-slice path."""
+    from linear_attention_sequence_modality_amd.inputs import WORKLOAD
+
+    cfg = WORKLOAD[name]
+    say("case %s conv backward head %d B=%d T=%d H=%d d=%d %s" % (name, h, cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dtype))
+    host = make_inputs(cfg)
+    g = np.random.default_rng(cfg.seed + 7)
+    dys = {s: torch.from_numpy(g.standard_normal(tuple(host[s].shape)).astype(np.float32)).to(cfg.torch_dtype)
+           for s in ("q", "k", "v")}
+    dev = {k: v.cuda() for k, v in host.items()}
+    out = kda.kda_conv_backward(desc_of(cfg), dev["q"], dev["k"], dev["v"],
+                                (dev["w_text_q"], dev["w_text_k"], dev["w_text_v"]),
+                                (dev["w_vis_q"], dev["w_vis_k"], dev["w_vis_v"]),
+                                dys["q"].cuda(), dys["k"].cuda(), dys["v"].cuda())
+    torch.cuda.synchronize()
+    for i, s in enumerate(("q", "k", "v")):
+        B, T, H, d = host[s].shape
+        ch = slice(h * d, (h + 1) * d)
+        dx, dwt, dwv = ob.short_conv_backward(host[s][:, :, h], host["w_text_" + s][ch], host["w_vis_" + s][ch],
+                                              dys[s][:, :, h], cfg.n_text, cfg.grid, cfg.causal_t)
+        e_x = rel(out["d" + s][:, :, h:h + 1].double().cpu().numpy(), dx[:, :, None, :])
+        gwt = out["dw_text"][i][ch].double().cpu().numpy()
+        gwv = out["dw_vis"][i][ch].double().cpu().numpy()
+        e_t = float(np.abs(gwt - dwt).max() / max(np.abs(dwt).max(), 1e-30))
+        e_v = float(np.abs(gwv - dwv).max() / max(np.abs(dwv).max(), 1e-30))
+        say("  %s: rel err dx %.2e dw_text %.2e dw_vis %.2e" % (s, e_x, e_t, e_v))
+        tol = TOL[cfg.dtype]
+        assert np.isfinite(gwt).all() and np.isfinite(gwv).all()
+        assert e_x <= tol and e_t <= tol and e_v <= tol
+
+
 @pytest.mark.timeout(300)
 def test_conv_and_kda_backward_chain_matches_the_oracle():
     """kda_backward then kda_conv_backward: the gradients of the conv inputs, the taps,
