@@ -264,17 +264,17 @@ def test_backward_at_the_video_workload_is_exact_along_q_and_v():
 
 
 @pytest.mark.timeout(600)
-def test_backward_at_the_video_workload_one_head_against_the_oracle():
-    """Every gradient (dq, dk, dv, dalpha, dbeta, dS0) of one sampled head of the full 5 s
-    480x832 stream (T=33272, H=16, d=128, bf16), with an initial state and a final-state
-    gradient, in the launch configuration bench.py times, against the fp64 adjoint oracle run
-    on that head alone (heads are independent)."""
+@pytest.mark.parametrize("name,h", [("video_5s_480x832", 5), ("image_4096px", 11)])
+def test_backward_at_full_size_one_head_against_the_oracle(name, h):
+    """Every gradient (dq, dk, dv, dalpha, dbeta, dS0) of one sampled head of a full workload
+    stream (the 5 s 480x832 video, T=33272, 520 chunks; the 4096x4096 image, T=66048, 1032
+    chunks; H=16, d=128, bf16), with an initial state and a final-state gradient, in the
+    launch configuration bench.py times, against the fp64 adjoint oracle run on that head
+    alone (heads are independent)."""
     from linear_attention_sequence_modality_amd.inputs import WORKLOAD
 
-    cfg = WORKLOAD["video_5s_480x832"]
-    h = 5
-    say("case video_5s_480x832 backward head %d B=%d T=%d H=%d d=%d %s" % (h, cfg.B, cfg.T, cfg.H, cfg.dk,
-                                                                          cfg.dtype))
+    cfg = WORKLOAD[name]
+    say("case %s backward head %d B=%d T=%d H=%d d=%d %s" % (name, h, cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dtype))
     host = make_inputs(cfg)
     g = np.random.default_rng(97)
     dO = torch.from_numpy(g.standard_normal((cfg.B, cfg.T, cfg.H, cfg.dv)).astype(np.float32)).to(cfg.torch_dtype)
