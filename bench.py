@@ -46,7 +46,7 @@ KERNEL_SOURCES = {
 MEASURED_TRAFFIC = {
     ("video_5s_480x832", "conv"): ("f5a252ae652253e0", 231076.8, 399264.0),
     ("video_5s_480x832", "chunks"): ("cfa2c67a3dfbdee9", 270451.6, 586560.9),
-    ("video_5s_480x832", "scan"): ("f47b4b38c6e4a7fe", 517495.3, 180238.0),
+    ("video_5s_480x832", "scan"): ("9026246c558a04e4", 517482.5, 180197.6),
     ("mla_video_5s_480x832", "mla"): ("9bcc320e76aca060", 1537386.9, 133088.0),
     ("mla_video_5s_480x832", "mla_latent"): ("e6aee03f454abe42", 235091.0, 303607.0),
     ("video_5s_480x832", "kda_backward"): ("13098d71929cd177", 11418126.2, 10718472.9),
@@ -55,7 +55,7 @@ MEASURED_TRAFFIC = {
 # SQ_INSTS_VALU_MFMA_MOPS_F32, each count is 512 flops), taken the same way.
 MEASURED_MFMA_MOPS = {
     ("video_5s_480x832", "chunks"): ("cfa2c67a3dfbdee9", 46858240.0, 2129920.0),
-    ("video_5s_480x832", "scan"): ("f47b4b38c6e4a7fe", 244776960.0, 2097152.0),
+    ("video_5s_480x832", "scan"): ("9026246c558a04e4", 244776960.0, 2097152.0),
     ("mla_video_5s_480x832", "mla"): ("9bcc320e76aca060", 22151168000.0, 0.0),
     ("mla_video_5s_480x832", "mla_latent"): ("e6aee03f454abe42", 425984000.0, 0.0),
     ("video_5s_480x832", "kda_backward"): ("13098d71929cd177", 0.0, 575078400.0),

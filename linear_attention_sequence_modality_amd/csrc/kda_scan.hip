@@ -52,9 +52,6 @@ constexpr int kSegoutMaxThreads = 64 * (128 / 16 + 2);
 
 // s_waitcnt vmcnt(0) alone (expcnt and lgkmcnt at their maxima).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
-// s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding: vmcnt split over
-// bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima).
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xf00; }
 
 // ---- segment records --------------------------------------------------------
 // One per (head, segment), fp32: L and S_start (DK x DV) in state-fragment
@@ -154,9 +151,11 @@ __device__ __forceinline__ Frag<T> slot_frag(const char *slot, size_t elem, int 
 // the state [L | Phi] of DV + DK columns starts at [0 | I] and runs through
 // the segment's chunks, L with the Ut terms and Phi without.  Compute wave w
 // owns 32 columns (two 16-column slabs): L's columns first, then Phi's.  The
-// loader wave copies each chunk's W, Kh^T, Ut and decay into an LDS slot,
-// NSLOT - 1 chunks ahead.  A sequence's last segment needs no summary; its
-// workgroups return at once.
+// loader wave copies each chunk's W, Kh^T, Ut and decay into an LDS slot, one
+// chunk ahead into the other slot when two fit.  A third slot (two chunks
+// ahead) measured slower: one wave can hold at most 63 memory operations in
+// flight, fewer than two chunks' copies, so the loader stalled at issue.  A
+// sequence's last segment needs no summary; its workgroups return at once.
 // ============================================================================
 template <typename T, int DK, int DV>
 struct SegsumPlan {
@@ -169,11 +168,10 @@ struct SegsumPlan {
     static constexpr int GAM_OFF = 2 * W_B + (int)(Ws<T, DK, DV>::GAM_BYTE - Ws<T, DK, DV>::U * ES);
     static constexpr int SLOT = 2 * W_B + UG_B;
     static constexpr int NOP = SLOT / 1024;
-    // as many slots as fit, at most three: the loader runs NSLOT - 1 chunks ahead
-    static constexpr int NSLOT = 3 * SLOT <= kLdsMax ? 3 : 2 * SLOT <= kLdsMax ? 2 : 1;
+    // two slots when they fit (the loader one chunk ahead), else one
+    static constexpr int NSLOT = 2 * SLOT <= kLdsMax ? 2 : 1;
     static constexpr int LDS_B = NSLOT * SLOT;
     static_assert(W_B % 1024 == 0 && UG_SRC % 1024 == 0 && LDS_B <= kLdsMax, "segment summary LDS plan");
-    static_assert(NSLOT < 3 || NOP <= 63, "the partial wait counts one chunk's copies in the vector memory counter");
     static_assert(THREADS <= kSegsumMaxThreads, "launch bound");
 };
 
@@ -223,24 +221,16 @@ __global__ __launch_bounds__(kSegsumMaxThreads) void kda_segsum_kernel(KdaArgs a
             }
             return;
         }
-        // chunk n + NSLOT - 1 goes into the slot chunk n - 1 used, once every
-        // compute wave has passed the barrier that ends chunk n - 1; before the
-        // barrier that ends chunk n, chunk n + 1 must have landed while chunk
-        // n + NSLOT - 1's copies (the newest NOP) may still fly
-#pragma unroll
-        for (int n = 0; n < NSLOT - 1; ++n)
-            if (n < N) issue_ops(n);
+        // chunk n + 1 goes into the slot chunk n - 1 used, once every compute
+        // wave has passed the barrier that ends chunk n - 1, and has landed
+        // before the barrier that ends chunk n
+        if (N > 0) issue_ops(0);
         wait_vm_all();
         lds_barrier();
 #pragma unroll 1
         for (int n = 0; n < N; ++n) {
-            if (n + NSLOT - 1 < N) {
-                issue_ops(n + NSLOT - 1);
-                if (NSLOT == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(P::NOP));
-                else wait_vm_all();
-            } else {
-                wait_vm_all();
-            }
+            if (n + 1 < N) issue_ops(n + 1);
+            wait_vm_all();
             lds_barrier();
         }
         return;
