@@ -8,10 +8,23 @@
 // with o = (a - P, b - 1, e - 1) over the 3x3x3 taps (P = 1 symmetric, 2 time-causal)
 // and every term outside the stream's modality region dropped.
 //   * conv_dx_kernel: one thread per (token, channel pair), 4 or 27 gathers of dy.
-//   * conv_dw_kernel: about one block per compute unit, each over 256 channels (4 per
-//     lane) and a share of the tokens, 31 x 4 running sums per lane, summed over the
-//     block's waves in LDS and then added with one fp32 atomic per (channel, tap) into
-//     the (zeroed) weight gradients.
+//   * conv_dw_visual_kernel: the visual tap gradients.  A 4-wave block walks tiles of
+//     4 rows x 8 w positions x 128 channels (those of one channel block, about as many
+//     blocks as fit the chip at once) and marches each over t like the forward conv:
+//     each step stages one new haloed x slice (a 3-slice ring in LDS: the slices t - P,
+//     t - P + 1, t - P + 2 that dy slice t meets) and dy slice t, zero outside the grid,
+//     so every input is read from memory once per tile.  Wave r takes tile row r, lane l
+//     channels 2l, 2l + 1; per (a, b) tap row it reads the 10 x values of its window row
+//     from LDS once (the next row's reads in flight under the current row's products) and
+//     uses them for the three w taps of all 8 positions; in bf16, byte permutes pair
+//     neighbouring positions so that each v_dot2_f32_bf16 does two multiply-adds.  The 27 x 2
+//     running sums run on across the block's tiles, are added over the waves in LDS and
+//     then into the (zeroed) weight gradients with one fp32 atomic per (channel, tap) and
+//     block: per-tile atomics (113 M of them at a 4096 x 4096 image) were the bound.
+//   * conv_dw_text_kernel: the text tap gradients: about one block per compute unit, each
+//     over 256 channels (4 per lane) and a share of the text tokens, 4 x 4 running sums per
+//     lane, summed over the block's waves in LDS and then added with one fp32 atomic per
+//     (channel, tap).
 //   * symmetric time padding: the visual input gradient is the forward conv kernel
 //     run on dy with the taps mirrored through the centre.
 #include <hip/hip_runtime.h>
@@ -26,7 +39,7 @@ namespace {
 
 constexpr int kDxThreads = 256;
 constexpr int kDwWaves = 8;        // waves per tap-gradient block
-constexpr int kDwTokens = 8;       // tokens per wave and token range
+constexpr int kDwTokens = 2;       // text tokens per wave and token range
 constexpr int kCUs = 256;          // compute units the tap-gradient grid is sized for
 
 __device__ __forceinline__ float ldf(const float *p) { return *p; }
@@ -95,74 +108,251 @@ __device__ __forceinline__ void ld4c(const bf16_t *p, float (&x)[4]) {
     x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
 }
 
-// A block owns 256 channels (4 per lane) and walks token ranges of kDwWaves * kDwTokens
-// tokens (one slice of kDwTokens per wave) with a grid stride, keeping 31 x 4 running sums
-// per lane across all of them; at the end the waves add their sums in LDS and the block
-// adds each (channel, tap) total to the zeroed fp32 gradient with one global atomic.  The
-// blocks of a channel block are the ones congruent mod the number of channel blocks.
+// Text tap gradients.  A block owns 256 channels (4 per lane) and walks ranges of
+// kDwWaves * kDwTokens text tokens (kDwTokens per wave) with a grid stride, keeping 4 x 4
+// running sums per lane; at the end the waves add their sums in LDS and the block adds each
+// (channel, tap) total to the zeroed fp32 gradient with one global atomic.  The blocks of a
+// channel block are the ones congruent mod the number of channel blocks.
 template <typename T>
-__global__ __launch_bounds__(64 * kDwWaves) void conv_dw_kernel(ConvBwdArgs a, int s) {
-    __shared__ float red[31][4][64];   // [tap: 4 text then 27 visual][channel of the lane's 4][lane]
-    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-    const int C = a.C[s], ncb = (C + 255) / 256, span = kDwWaves * kDwTokens, nrange = (a.T + span - 1) / span;
+__global__ __launch_bounds__(64 * kDwWaves) void conv_dw_text_kernel(ConvBwdArgs a, int s) {
+    __shared__ float red[4][4][64];   // [tap][channel of the lane's 4][lane]
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, nt = a.n_text;
+    const int C = a.C[s], ncb = (C + 255) / 256, span = kDwWaves * kDwTokens, nrange = (nt + span - 1) / span;
     const int cb = blockIdx.x % ncb, c = cb * 256 + 4 * lane;
-    for (int e = threadIdx.x; e < 31 * 4 * 64; e += 64 * kDwWaves) (&red[0][0][0])[e] = 0.f;
+    for (int e = threadIdx.x; e < 4 * 4 * 64; e += 64 * kDwWaves) (&red[0][0][0])[e] = 0.f;
     __syncthreads();
     if (c < C) {
-        const int P = a.causal_t ? 2 : 1;
-        // every load is issued unconditionally (a position off the grid reads the token
-        // itself and contributes zero), so a token's loads are in flight together
-        float st4[4][4] = {}, sv[27][4] = {};
+        // every load is issued unconditionally (a tap before the first token reads token 0
+        // and contributes zero), so a token's loads are in flight together
+        float st4[4][4] = {};
         for (int r = blockIdx.x / ncb; r < a.B * nrange; r += gridDim.x / ncb) {
-            const int b = r / nrange, i0 = (r % nrange) * span + wave * kDwTokens, i1 = min(a.T, i0 + kDwTokens);
+            const int b = r / nrange, i0 = (r % nrange) * span + wave * kDwTokens, i1 = min(nt, i0 + kDwTokens);
             const T *x = static_cast<const T *>(a.x[s]) + (size_t)b * a.T * C + c;
             const T *dy = static_cast<const T *>(a.dy[s]) + (size_t)b * a.T * C + c;
             for (int i = i0; i < i1; ++i) {
                 float g[4];
                 ld4c(dy + (size_t)i * C, g);
-                if (i < a.n_text) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int src = i - 3 + j;
-                        float xv[4];
-                        ld4c(x + (size_t)max(src, 0) * C, xv);
+                for (int j = 0; j < 4; ++j) {
+                    const int src = i - 3 + j;
+                    float xv[4];
+                    ld4c(x + (size_t)max(src, 0) * C, xv);
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) st4[j][u] += g[u] * (src >= 0 ? xv[u] : 0.f);
-                    }
-                } else {
-                    const int p = i - a.n_text, t = p / (a.gh * a.gw), hw = p % (a.gh * a.gw), h = hw / a.gw,
-                              w = hw % a.gw;
-#pragma unroll
-                    for (int ta = 0; ta < 3; ++ta)
-#pragma unroll
-                        for (int tb = 0; tb < 3; ++tb)
-#pragma unroll
-                            for (int te = 0; te < 3; ++te) {
-                                const int src = vpos(a, t + ta - P, h + tb - 1, w + te - 1);
-                                float xv[4];
-                                ld4c(x + (size_t)(src >= 0 ? src : i) * C, xv);
-#pragma unroll
-                                for (int u = 0; u < 4; ++u)
-                                    sv[(ta * 3 + tb) * 3 + te][u] += g[u] * (src >= 0 ? xv[u] : 0.f);
-                            }
+                    for (int u = 0; u < 4; ++u) st4[j][u] += g[u] * (src >= 0 ? xv[u] : 0.f);
                 }
             }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (st4[j][u] != 0.f) atomicAdd(&red[j][u][lane], st4[j][u]);
-#pragma unroll
-            for (int k = 0; k < 27; ++k)
-                if (sv[k][u] != 0.f) atomicAdd(&red[4 + k][u][lane], sv[k][u]);
-        }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < 31 * 4 * 64; e += 64 * kDwWaves) {
+    for (int e = threadIdx.x; e < 4 * 4 * 64; e += 64 * kDwWaves) {
         const int k = e / 256, u = (e / 64) % 4, l = e % 64, ch = cb * 256 + 4 * l + u;
         const float v = red[k][u][l];
-        if (ch < C && v != 0.f) atomicAdd(k < 4 ? a.dwt[s] + (size_t)ch * 4 + k : a.dwv[s] + (size_t)ch * 27 + (k - 4), v);
+        if (ch < C && v != 0.f) atomicAdd(a.dwt[s] + (size_t)ch * 4 + k, v);
+    }
+}
+
+constexpr int kGW = 8;     // w positions per visual tap-gradient tile
+constexpr int kGH = 4;     // rows per tile (one wave each)
+constexpr int kGC = 128;   // channels per tile (two per lane)
+
+constexpr int kGX = kGW + 2;   // positions of a window row (w halo)
+
+// The products of one window row: acc[te][ch] += sum_j dy[j][ch] x[j + te][ch] for the
+// kGW positions j of a tile row and the three w taps te, on lane l's two channels.
+template <typename T> struct DwOps;
+template <> struct DwOps<bf16_t> {
+    typedef uint32_t Raw;   // one position's channel pair (2l, 2l + 1), as stored
+    // dy as bf16 pairs along w: (dy[2k][ch], dy[2k + 1][ch]) for channel ch = lo, hi
+    struct Dy {
+        uint32_t lo[kGW / 2], hi[kGW / 2];
+    };
+    __device__ __forceinline__ static Raw read(const char *p) { return *reinterpret_cast<const uint32_t *>(p); }
+    __device__ __forceinline__ static void make_dy(const Raw (&d)[kGW], Dy &o) {
+#pragma unroll
+        for (int k = 0; k < kGW / 2; ++k) {
+            o.lo[k] = __builtin_amdgcn_perm(d[2 * k + 1], d[2 * k], 0x05040100u);
+            o.hi[k] = __builtin_amdgcn_perm(d[2 * k + 1], d[2 * k], 0x07060302u);
+        }
+    }
+    __device__ __forceinline__ static float dot2(uint32_t x, uint32_t w, float acc) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), __builtin_bit_cast(bf16x2_t, w), acc,
+                                               false);
+    }
+    // byte permutes pair neighbouring positions of one channel, so each dot2 does the
+    // multiply-adds of two positions
+    __device__ __forceinline__ static void row(const Raw (&x)[kGX], const Dy &dy, float (*acc)[2]) {
+        uint32_t plo[kGX - 1], phi[kGX - 1];   // (x[k][ch], x[k + 1][ch])
+#pragma unroll
+        for (int k = 0; k < kGX - 1; ++k) {
+            plo[k] = __builtin_amdgcn_perm(x[k + 1], x[k], 0x05040100u);
+            phi[k] = __builtin_amdgcn_perm(x[k + 1], x[k], 0x07060302u);
+        }
+#pragma unroll
+        for (int te = 0; te < 3; ++te)
+#pragma unroll
+            for (int k = 0; k < kGW / 2; ++k) {
+                acc[te][0] = dot2(dy.lo[k], plo[2 * k + te], acc[te][0]);
+                acc[te][1] = dot2(dy.hi[k], phi[2 * k + te], acc[te][1]);
+            }
+    }
+};
+template <> struct DwOps<float> {
+    typedef float2 Raw;
+    struct Dy {
+        float2 v[kGW];
+    };
+    __device__ __forceinline__ static Raw read(const char *p) { return *reinterpret_cast<const float2 *>(p); }
+    __device__ __forceinline__ static void make_dy(const Raw (&d)[kGW], Dy &o) {
+#pragma unroll
+        for (int j = 0; j < kGW; ++j) o.v[j] = d[j];
+    }
+    __device__ __forceinline__ static void row(const Raw (&x)[kGX], const Dy &dy, float (*acc)[2]) {
+#pragma unroll
+        for (int te = 0; te < 3; ++te)
+#pragma unroll
+            for (int j = 0; j < kGW; ++j) {
+                acc[te][0] = fmaf(dy.v[j].x, x[j + te].x, acc[te][0]);
+                acc[te][1] = fmaf(dy.v[j].y, x[j + te].y, acc[te][1]);
+            }
+    }
+};
+
+// dW[c][a][b][e] += sum over visual positions p = (t, h, w) of dy[p][c] x[t + a - P][h + b - 1][w + e - 1][c]
+// for one tile of kGH rows x kGW positions x kGC channels, marching over t.
+template <typename T>
+__global__ __launch_bounds__(256) void conv_dw_visual_kernel(ConvBwdArgs a, int s) {
+    constexpr int ES = sizeof(T);
+    constexpr int XR = kGH + 2, XC = kGX;       // haloed x tile
+    constexpr int ROWB = kGC * ES;              // bytes of one position's channels
+    constexpr int NCH = ROWB / 16;              // 16-byte pieces per position
+    constexpr int SLOT = XR * XC * ROWB;
+    constexpr int XPIECES = XR * XC * NCH, DPIECES = kGH * kGW * NCH;
+    constexpr int XIT = (XPIECES + 255) / 256, DIT = (DPIECES + 255) / 256;
+    static_assert(27 * kGC * 4 <= 3 * SLOT, "the reduction fits the x ring");
+    __shared__ __attribute__((aligned(16))) char xs[3 * SLOT];          // x slices, ring by slice index mod 3
+    __shared__ __attribute__((aligned(16))) char ds[kGH * kGW * ROWB];  // dy slice t
+
+    const int C = a.C[s], gt = a.gt, gh = a.gh, gw = a.gw;
+    const int nwr = (gw + kGW - 1) / kGW, nrg = (gh + kGH - 1) / kGH, ncb = (C + kGC - 1) / kGC;
+    const int ntile = nwr * nrg, per = gridDim.x / (a.B * ncb);   // tiles and workgroups per (batch, channel block)
+    // consecutive logical blocks (the workgroups of one channel block) on one XCD, so the
+    // halo positions of neighbouring tiles come from its L2
+    int blk = xcd_remap(blockIdx.x, gridDim.x);
+    const int j0 = blk % per;
+    blk /= per;
+    const int cb = blk % ncb, b = blk / ncb;
+    const int c0 = cb * kGC;
+    const int nch = (min(kGC, C - c0) * ES) / 16;   // valid pieces per position (C is a multiple of 8)
+    const int P = a.causal_t ? 2 : 1;
+    const int tid = threadIdx.x, r = tid >> 6, l = tid & 63;
+    const char *xg = static_cast<const char *>(a.x[s]) + ((size_t)b * a.T + a.n_text) * C * ES + (size_t)c0 * ES;
+    const char *dg = static_cast<const char *>(a.dy[s]) + ((size_t)b * a.T + a.n_text) * C * ES + (size_t)c0 * ES;
+    int w0 = 0, h0 = 0;   // the current tile
+    auto slot_of = [](int sl) { return ((sl % 3) + 3) % 3; };
+    // The loads of a step's x slice sl (zeros outside the grid or outside [0, gt)) and dy
+    // slice t go into registers one step ahead, so they fly under the previous step's
+    // products; the stores to LDS follow that step's closing barrier.
+    uint4 vx[XIT], vd[DIT];
+    auto load_x = [&](int sl) {
+#pragma unroll
+        for (int i = 0; i < XIT; ++i) {
+            const int e = tid + 256 * i, pos = e / NCH, pc = e % NCH;
+            const int h = h0 + pos / XC - 1, w = w0 + pos % XC - 1;
+            const bool ok = e < XPIECES && pc < nch && sl >= 0 && sl < gt && h >= 0 && h < gh && w >= 0 && w < gw;
+            vx[i] = ok ? *reinterpret_cast<const uint4 *>(xg + ((size_t)(sl * gh + h) * gw + w) * C * ES + 16 * pc)
+                       : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto store_x = [&](int sl) {
+        char *d = xs + slot_of(sl) * SLOT;
+#pragma unroll
+        for (int i = 0; i < XIT; ++i) {
+            const int e = tid + 256 * i;
+            if (e < XPIECES) *reinterpret_cast<uint4 *>(d + (e / NCH) * ROWB + 16 * (e % NCH)) = vx[i];
+        }
+    };
+    auto load_dy = [&](int t) {
+#pragma unroll
+        for (int i = 0; i < DIT; ++i) {
+            const int e = tid + 256 * i, pos = e / NCH, pc = e % NCH;
+            const int h = h0 + pos / kGW, w = w0 + pos % kGW;
+            const bool ok = t < gt && e < DPIECES && pc < nch && h < gh && w < gw;
+            vd[i] = ok ? *reinterpret_cast<const uint4 *>(dg + ((size_t)(t * gh + h) * gw + w) * C * ES + 16 * pc)
+                       : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto store_dy = [&]() {
+#pragma unroll
+        for (int i = 0; i < DIT; ++i) {
+            const int e = tid + 256 * i;
+            if (e < DPIECES) *reinterpret_cast<uint4 *>(ds + (e / NCH) * ROWB + 16 * (e % NCH)) = vd[i];
+        }
+    };
+
+    float acc[27][2];
+#pragma unroll
+    for (int k = 0; k < 27; ++k) acc[k][0] = acc[k][1] = 0.f;
+    // the workgroup's tiles of its channel block, each marched over t; the sums run on
+    // across them (the previous tile's last step ended with every wave done with LDS)
+#pragma unroll 1
+    for (int tile = j0; tile < ntile; tile += per) {
+        w0 = (tile % nwr) * kGW;
+        h0 = (tile / nwr) * kGH;
+        load_x(-P);
+        store_x(-P);
+        load_x(1 - P);
+        store_x(1 - P);
+        load_x(2 - P);
+        load_dy(0);
+    #pragma unroll 1
+        for (int t = 0; t < gt; ++t) {
+            store_x(t - P + 2);   // its slot last held slice t - P - 1, which no wave reads any more
+            store_dy();
+            lds_barrier();        // LDS only: the next step's loads below stay in flight
+            load_x(t - P + 3);    // the next step's (past the last step: zeros, unused)
+            load_dy(t + 1);
+            using Ops = DwOps<T>;
+            typename Ops::Raw d[kGW], xr[2][kGX];
+#pragma unroll
+            for (int j = 0; j < kGW; ++j) d[j] = Ops::read(ds + (r * kGW + j) * ROWB + 2 * ES * l);
+            // window row i = (ta, tb): row r + tb of slice t - P + ta; the next row's LDS
+            // reads are issued before the current row's products
+            auto read_row = [&](int i, typename Ops::Raw(&x)[kGX]) {
+                const char *src = xs + slot_of(t - P + i / 3) * SLOT + (r + i % 3) * XC * ROWB + 2 * ES * l;
+#pragma unroll
+                for (int c = 0; c < kGX; ++c) x[c] = Ops::read(src + c * ROWB);
+            };
+            read_row(0, xr[0]);
+            typename Ops::Dy dyp;
+            Ops::make_dy(d, dyp);
+#pragma unroll
+            for (int i = 0; i < 9; ++i) {
+                if (i + 1 < 9) read_row(i + 1, xr[(i + 1) & 1]);
+                Ops::row(xr[i & 1], dyp, &acc[3 * i]);
+            }
+            lds_barrier();     // every wave is done with dy slice t and x slice t - P
+        }
+    }
+    // the four waves' sums, added in LDS (the x ring as [27][kGC] fp32), then one atomic
+    // per (channel, tap) into the zeroed gradient
+    float *red = reinterpret_cast<float *>(xs);
+    for (int e = tid; e < 27 * kGC; e += 256) red[e] = 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 27; ++k) {
+        atomicAdd(&red[k * kGC + 2 * l], acc[k][0]);
+        atomicAdd(&red[k * kGC + 2 * l + 1], acc[k][1]);
+    }
+    __syncthreads();
+    for (int e = tid; e < 27 * kGC; e += 256) {
+        const int k = e / kGC, ch = c0 + e % kGC;
+        const float v = red[e];
+        if (ch < C && v != 0.f) atomicAdd(a.dwv[s] + (size_t)ch * 27 + k, v);
     }
 }
 
@@ -221,10 +411,22 @@ hipError_t launch_typed(const ConvBwdArgs &a, hipStream_t stream) {
         const size_t nz_t = (size_t)a.C[s] * 4, nz_v = (size_t)a.C[s] * 27;
         hipLaunchKernelGGL(zero_kernel, dim3(64), dim3(256), 0, stream, a.dwt[s], nz_t);
         hipLaunchKernelGGL(zero_kernel, dim3(64), dim3(256), 0, stream, a.dwv[s], nz_v);
-        // one block per compute unit (a multiple of the channel-block count), at most one per range
-        const int ncb = (a.C[s] + 255) / 256, nrange = (a.T + kDwWaves * kDwTokens - 1) / (kDwWaves * kDwTokens);
-        const int per_cb = std::max(1, std::min(a.B * nrange, kCUs / ncb));
-        hipLaunchKernelGGL((conv_dw_kernel<T>), dim3(ncb * per_cb), dim3(64 * kDwWaves), 0, stream, a, s);
+        if (a.n_text > 0) {
+            // text taps: one block per compute unit (a multiple of the channel-block count),
+            // at most one per token range
+            const int ncb = (a.C[s] + 255) / 256;
+            const int nrange = (a.n_text + kDwWaves * kDwTokens - 1) / (kDwWaves * kDwTokens);
+            const int per_cb = std::max(1, std::min(a.B * nrange, kCUs / ncb));
+            hipLaunchKernelGGL((conv_dw_text_kernel<T>), dim3(ncb * per_cb), dim3(64 * kDwWaves), 0, stream, a, s);
+        }
+        if (vis) {
+            // about as many workgroups as fit the chip at once (two per compute unit for bf16
+            // by their LDS, one for fp32), dealt over the (batch, channel block) pairs
+            const int nwr = (a.gw + kGW - 1) / kGW, nrg = (a.gh + kGH - 1) / kGH, ncb = (a.C[s] + kGC - 1) / kGC;
+            const int slots = kCUs * (sizeof(T) == 2 ? 2 : 1);
+            const int per = std::max(1, std::min(nwr * nrg, slots / (a.B * ncb)));
+            hipLaunchKernelGGL((conv_dw_visual_kernel<T>), dim3(a.B * ncb * per), dim3(256), 0, stream, a, s);
+        }
     }
     return hipGetLastError();
 }
