@@ -149,8 +149,9 @@ __global__ __launch_bounds__(64 * kDwWaves) void conv_dw_text_kernel(ConvBwdArgs
                 if (st4[j][u] != 0.f) atomicAdd(&red[j][u][lane], st4[j][u]);
     }
     __syncthreads();
+    // in the gradient's address order ([channel][4]): a wave's atomics cover one 1 KB run
     for (int e = threadIdx.x; e < 4 * 4 * 64; e += 64 * kDwWaves) {
-        const int k = e / 256, u = (e / 64) % 4, l = e % 64, ch = cb * 256 + 4 * l + u;
+        const int k = e % 4, cl = e / 4, u = cl % 4, l = cl / 4, ch = cb * 256 + cl;
         const float v = red[k][u][l];
         if (ch < C && v != 0.f) atomicAdd(a.dwt[s] + (size_t)ch * 4 + k, v);
     }
@@ -349,10 +350,12 @@ __global__ __launch_bounds__(256) void conv_dw_visual_kernel(ConvBwdArgs a, int 
         atomicAdd(&red[k * kGC + 2 * l + 1], acc[k][1]);
     }
     __syncthreads();
+    // in the gradient's address order ([channel][27]), so a wave's atomics cover two
+    // consecutive cache lines instead of one line per lane
     for (int e = tid; e < 27 * kGC; e += 256) {
-        const int k = e / kGC, ch = c0 + e % kGC;
-        const float v = red[e];
-        if (ch < C && v != 0.f) atomicAdd(a.dwv[s] + (size_t)ch * 27 + k, v);
+        const int k = e % 27, cl = e / 27, ch = c0 + cl;
+        const float v = red[k * kGC + cl];
+        if (ch < C && v != 0.f) atomicAdd(a.dwv[s] + (size_t)c0 * 27 + e, v);
     }
 }
 
