@@ -158,8 +158,11 @@ __global__ __launch_bounds__(64 * kDwWaves) void conv_dw_text_kernel(ConvBwdArgs
 }
 
 constexpr int kGW = 8;     // w positions per visual tap-gradient tile
-constexpr int kGH = 4;     // rows per tile (one wave each)
 constexpr int kGC = 128;   // channels per tile (two per lane)
+constexpr int kGHMax = 8;  // rows per tile (one wave each): 8 in bf16, 4 in fp32 (its LDS)
+template <typename T> struct DwTile {
+    static constexpr int GH = sizeof(T) == 2 ? 8 : 4;
+};
 
 constexpr int kGX = kGW + 2;   // positions of a window row (w halo)
 
@@ -226,14 +229,15 @@ template <> struct DwOps<float> {
 // dW[c][a][b][e] += sum over visual positions p = (t, h, w) of dy[p][c] x[t + a - P][h + b - 1][w + e - 1][c]
 // for one tile of kGH rows x kGW positions x kGC channels, marching over t.
 template <typename T>
-__global__ __launch_bounds__(256) void conv_dw_visual_kernel(ConvBwdArgs a, int s) {
+__global__ __launch_bounds__(64 * DwTile<T>::GH) void conv_dw_visual_kernel(ConvBwdArgs a, int s) {
     constexpr int ES = sizeof(T);
+    constexpr int kGH = DwTile<T>::GH, NT = 64 * kGH;   // rows per tile, one wave each; threads
     constexpr int XR = kGH + 2, XC = kGX;       // haloed x tile
     constexpr int ROWB = kGC * ES;              // bytes of one position's channels
     constexpr int NCH = ROWB / 16;              // 16-byte pieces per position
     constexpr int SLOT = XR * XC * ROWB;
     constexpr int XPIECES = XR * XC * NCH, DPIECES = kGH * kGW * NCH;
-    constexpr int XIT = (XPIECES + 255) / 256, DIT = (DPIECES + 255) / 256;
+    constexpr int XIT = (XPIECES + NT - 1) / NT, DIT = (DPIECES + NT - 1) / NT;
     static_assert(27 * kGC * 4 <= 3 * SLOT, "the reduction fits the x ring");
     __shared__ __attribute__((aligned(16))) char xs[3 * SLOT];          // x slices, ring by slice index mod 3
     __shared__ __attribute__((aligned(16))) char ds[kGH * kGW * ROWB];  // dy slice t
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(256) void conv_dw_visual_kernel(ConvBwdArgs a, int 
     auto load_x = [&](int sl) {
 #pragma unroll
         for (int i = 0; i < XIT; ++i) {
-            const int e = tid + 256 * i, pos = e / NCH, pc = e % NCH;
+            const int e = tid + NT * i, pos = e / NCH, pc = e % NCH;
             const int h = h0 + pos / XC - 1, w = w0 + pos % XC - 1;
             const bool ok = e < XPIECES && pc < nch && sl >= 0 && sl < gt && h >= 0 && h < gh && w >= 0 && w < gw;
             vx[i] = ok ? *reinterpret_cast<const uint4 *>(xg + ((size_t)(sl * gh + h) * gw + w) * C * ES + 16 * pc)
@@ -273,14 +277,14 @@ __global__ __launch_bounds__(256) void conv_dw_visual_kernel(ConvBwdArgs a, int 
         char *d = xs + slot_of(sl) * SLOT;
 #pragma unroll
         for (int i = 0; i < XIT; ++i) {
-            const int e = tid + 256 * i;
+            const int e = tid + NT * i;
             if (e < XPIECES) *reinterpret_cast<uint4 *>(d + (e / NCH) * ROWB + 16 * (e % NCH)) = vx[i];
         }
     };
     auto load_dy = [&](int t) {
 #pragma unroll
         for (int i = 0; i < DIT; ++i) {
-            const int e = tid + 256 * i, pos = e / NCH, pc = e % NCH;
+            const int e = tid + NT * i, pos = e / NCH, pc = e % NCH;
             const int h = h0 + pos / kGW, w = w0 + pos % kGW;
             const bool ok = t < gt && e < DPIECES && pc < nch && h < gh && w < gw;
             vd[i] = ok ? *reinterpret_cast<const uint4 *>(dg + ((size_t)(t * gh + h) * gw + w) * C * ES + 16 * pc)
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(256) void conv_dw_visual_kernel(ConvBwdArgs a, int 
     auto store_dy = [&]() {
 #pragma unroll
         for (int i = 0; i < DIT; ++i) {
-            const int e = tid + 256 * i;
+            const int e = tid + NT * i;
             if (e < DPIECES) *reinterpret_cast<uint4 *>(ds + (e / NCH) * ROWB + 16 * (e % NCH)) = vd[i];
         }
     };
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(256) void conv_dw_visual_kernel(ConvBwdArgs a, int 
     // the four waves' sums, added in LDS (the x ring as [27][kGC] fp32), then one atomic
     // per (channel, tap) into the zeroed gradient
     float *red = reinterpret_cast<float *>(xs);
-    for (int e = tid; e < 27 * kGC; e += 256) red[e] = 0.f;
+    for (int e = tid; e < 27 * kGC; e += NT) red[e] = 0.f;
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < 27; ++k) {
@@ -352,7 +356,7 @@ __global__ __launch_bounds__(256) void conv_dw_visual_kernel(ConvBwdArgs a, int 
     __syncthreads();
     // in the gradient's address order ([channel][27]), so a wave's atomics cover two
     // consecutive cache lines instead of one line per lane
-    for (int e = tid; e < 27 * kGC; e += 256) {
+    for (int e = tid; e < 27 * kGC; e += NT) {
         const int k = e % 27, cl = e / 27, ch = c0 + cl;
         const float v = red[k * kGC + cl];
         if (ch < C && v != 0.f) atomicAdd(a.dwv[s] + (size_t)c0 * 27 + e, v);
@@ -423,12 +427,12 @@ hipError_t launch_typed(const ConvBwdArgs &a, hipStream_t stream) {
             hipLaunchKernelGGL((conv_dw_text_kernel<T>), dim3(ncb * per_cb), dim3(64 * kDwWaves), 0, stream, a, s);
         }
         if (vis) {
-            // about as many workgroups as fit the chip at once (two per compute unit for bf16
-            // by their LDS, one for fp32), dealt over the (batch, channel block) pairs
-            const int nwr = (a.gw + kGW - 1) / kGW, nrg = (a.gh + kGH - 1) / kGH, ncb = (a.C[s] + kGC - 1) / kGC;
-            const int slots = kCUs * (sizeof(T) == 2 ? 2 : 1);
-            const int per = std::max(1, std::min(nwr * nrg, slots / (a.B * ncb)));
-            hipLaunchKernelGGL((conv_dw_visual_kernel<T>), dim3(a.B * ncb * per), dim3(256), 0, stream, a, s);
+            // about as many workgroups as fit the chip at once (one per compute unit by their
+            // LDS), dealt over the (batch, channel block) pairs
+            constexpr int gh = DwTile<T>::GH;
+            const int nwr = (a.gw + kGW - 1) / kGW, nrg = (a.gh + gh - 1) / gh, ncb = (a.C[s] + kGC - 1) / kGC;
+            const int per = std::max(1, std::min(nwr * nrg, kCUs / (a.B * ncb)));
+            hipLaunchKernelGGL((conv_dw_visual_kernel<T>), dim3(a.B * ncb * per), dim3(64 * gh), 0, stream, a, s);
         }
     }
     return hipGetLastError();
