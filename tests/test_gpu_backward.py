@@ -96,6 +96,12 @@ CONV_CASES = [
     # the video workload's width (2048 channels: 8 channel blocks) and enough token ranges that
     # each tap-gradient workgroup walks several of them
     StreamConfig("cbwd_wide_bf16", B=1, H=16, dk=128, dv=128, n_text=40, grid=(3, 20, 50), dtype="bf16", seed=95),
+    # 64 channels per stream: half a 128-channel tap-gradient block; time-causal, two batches,
+    # row and w counts off the 8 x 8 tile
+    StreamConfig("cbwd_narrow_causal_bf16", B=2, H=1, dk=64, dv=64, n_text=3, grid=(4, 9, 10), dtype="bf16",
+                 causal_t=1, seed=96),
+    # one latent slice (an image): every tile is a single step of the march
+    StreamConfig("cbwd_image_bf16", B=1, H=2, dk=128, dv=64, n_text=5, grid=(1, 17, 19), dtype="bf16", seed=97),
 ]
 
 
