@@ -44,7 +44,7 @@ KERNEL_SOURCES = {
 # "kda_backward" is the sum over its three launches (records, ordered passes, gradients) per call,
 # "scan" over the state pass's three (summaries, chain, replay), "mla_latent" over its two.
 MEASURED_TRAFFIC = {
-    ("video_5s_480x832", "conv"): ("f5a252ae652253e0", 231076.8, 399264.0),
+    ("video_5s_480x832", "conv"): ("1e1ee127d724456d", 213833.5, 399264.5),
     ("video_5s_480x832", "chunks"): ("cfa2c67a3dfbdee9", 270451.6, 586560.9),
     ("video_5s_480x832", "scan"): ("9026246c558a04e4", 517482.5, 180197.6),
     ("mla_video_5s_480x832", "mla"): ("9bcc320e76aca060", 1537386.9, 133088.0),

@@ -56,6 +56,11 @@ constexpr int TC = WR + 2;              // tile columns (w halo)
 constexpr int TP = (HR + 2) * TC;       // tile positions per slice
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Cache policy of the output stores: non-temporal (the nt bit of gfx9.4+ buffer stores), so
+// the 400 MB output stream does not push the input halo rows that neighbouring tiles still
+// read out of L2.
+constexpr int kStoreNT = 2;
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -109,7 +114,7 @@ template <> struct Ops<bf16_t> {
     }
     __device__ __forceinline__ static void bstore(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
                                                   float a, float b) {
-        __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a, b), r, voff, soff, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a, b), r, voff, soff, kStoreNT);
     }
     __device__ __forceinline__ static XT load(const char *p) { return *reinterpret_cast<const uint32_t *>(p); }
     __device__ __forceinline__ static void store(char *p, float a, float b) {
@@ -147,7 +152,7 @@ template <> struct Ops<float> {
         u32x2 u;
         u.x = __float_as_uint(a);
         u.y = __float_as_uint(b);
-        __builtin_amdgcn_raw_buffer_store_b64(u, r, voff, soff, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u, r, voff, soff, kStoreNT);
     }
     __device__ __forceinline__ static XT load(const char *p) { return *reinterpret_cast<const float2 *>(p); }
     __device__ __forceinline__ static void store(char *p, float a, float b) {
