@@ -102,6 +102,10 @@ CONV_CASES = [
                  causal_t=1, seed=96),
     # one latent slice (an image): every tile is a single step of the march
     StreamConfig("cbwd_image_bf16", B=1, H=2, dk=128, dv=64, n_text=5, grid=(1, 17, 19), dtype="bf16", seed=97),
+    # 20 batches x 16 channel blocks: more (batch, channel block) pairs than compute units, so
+    # each visual tap-gradient block walks every tile of its pair
+    StreamConfig("cbwd_many_pairs_bf16", B=20, H=16, dk=128, dv=128, n_text=3, grid=(2, 3, 9), dtype="bf16",
+                 seed=98),
 ]
 
 
