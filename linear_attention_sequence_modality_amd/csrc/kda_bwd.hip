@@ -6,7 +6,8 @@
 // forward is regrouped as
 //   Kt = gam K, Qt = gam Q, Kh = 2^(gC - G) K,
 //   A[r][s] = sum_c K[r][c] K[s][c] e(r, s, c) (s < r), Bq[r][s] = sum_c Q[r][c] K[s][c] e(r, s, c) (s <= r),
-//   Tm = (I + Diag(beta) A)^-1, X = Diag(beta) V, Y = Diag(beta) Kt, W = Tm Y, Ut = Tm X,
+//   Tm = (I + Diag(beta) A)^-1, X = Diag(beta) V, Y = Diag(beta) Kt, W = Tm Y, Ut = Tm X
+//   (formed as (Tm Diag(beta)) Kt and (Tm Diag(beta)) V),
 //   U = Ut - W S, O = Qt S + Bq U, S' = Diag(2^gC) S + Kh^T U
 // and its adjoint, for dO and dS' (the gradient of the state after the chunk), is
 //   dU = Bq^T dO + Kh dS',  dS = Qt^T dO + Diag(2^gC) dS' - W^T dU,
@@ -395,7 +396,7 @@ __device__ __forceinline__ void st(bf16_t *p, float x) { *p = (bf16_t)x; }
 // Per-chunk matrices rebuilt from the inputs (fp32, row-major, in the
 // workgroup's scratch): the chunk's rows past the stream's end are zero.
 struct ChunkMats {
-    float *Q, *K, *V, *G, *Kt, *Qt, *Kh, *A, *Bq, *Tm, *X, *Y, *W, *Ut;
+    float *Q, *K, *V, *G, *Kt, *Qt, *Kh, *A, *Bq, *Tm, *TmB, *W, *Ut;   // TmB = Tm Diag(beta)
     float *beta, *eC;   // [BC], [DK]
 };
 
@@ -544,29 +545,22 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
             for (int i = 0; i < BC; ++i) Tl[i * BC + j] = t[i];
         }
         __syncthreads();
-        for (int e4 = tid; e4 < BC * BC / 4; e4 += BT)
-            *reinterpret_cast<float4 *>(c.Tm + 4 * e4) = *reinterpret_cast<const float4 *>(Tl + 4 * e4);
-    }
-    if (FULL) {   // the gradient kernel folds beta into its products instead
-        float *__restrict__ X = c.X;
-        float *__restrict__ Y = c.Y;
-        const float *__restrict__ V = c.V;
-        const float *__restrict__ Kt = c.Kt;
-        for (int e4 = tid; e4 < BC * DV / 4; e4 += BT) {
-            const float bb = c.beta[4 * e4 / DV];
-            const float4 x = *reinterpret_cast<const float4 *>(V + 4 * e4);
-            *reinterpret_cast<float4 *>(X + 4 * e4) = make_float4(bb * x.x, bb * x.y, bb * x.z, bb * x.w);
-        }
-        for (int e4 = tid; e4 < BC * DK / 4; e4 += BT) {
-            const float bb = c.beta[4 * e4 / DK];
-            const float4 y = *reinterpret_cast<const float4 *>(Kt + 4 * e4);
-            *reinterpret_cast<float4 *>(Y + 4 * e4) = make_float4(bb * y.x, bb * y.y, bb * y.z, bb * y.w);
+        // Tm to the record, and Tm Diag(beta) for W = Tm Diag(beta) Kt and
+        // Ut = Tm Diag(beta) V: the column scaling of one 64 x 64 matrix instead of scaled
+        // copies of Kt and V
+        float *__restrict__ TmB = c.TmB;
+        for (int e4 = tid; e4 < BC * BC / 4; e4 += BT) {
+            const float4 t = *reinterpret_cast<const float4 *>(Tl + 4 * e4);
+            const int j = (4 * e4) % BC;
+            *reinterpret_cast<float4 *>(c.Tm + 4 * e4) = t;
+            *reinterpret_cast<float4 *>(TmB + 4 * e4) =
+                make_float4(t.x * bl[j], t.y * bl[j + 1], t.z * bl[j + 2], t.w * bl[j + 3]);
         }
     }
     __syncthreads();
-    if (FULL) {
-        gemm<false, false>(c.W, DK, c.Tm, BC, c.Y, DK, BC, DK, BC, 1.f, false, kNoMask, tA, tB);
-        gemm<false, false>(c.Ut, DV, c.Tm, BC, c.X, DV, BC, DV, BC, 1.f, false, kNoMask, tA, tB);
+    if (FULL) {   // (the gradient kernel folds beta into its products instead)
+        gemm<false, false>(c.W, DK, c.TmB, BC, c.Kt, DK, BC, DK, BC, 1.f, false, kNoMask, tA, tB);
+        gemm<false, false>(c.Ut, DV, c.TmB, BC, c.V, DV, BC, DV, BC, 1.f, false, kNoMask, tA, tB);
     }
 }
 
@@ -584,8 +578,8 @@ __device__ ChunkMats carve(float *s, int DK, int DV, float **rest) {
     c.A = s; s += mc;
     c.Bq = s; s += mc;
     c.Tm = s; s += mc;
-    c.X = s; s += mv;
-    c.Y = s; s += mk;
+    c.TmB = s; s += mv;   // (64 x 64 in use; sized as before)
+    s += mk;
     c.W = s; s += mk;
     c.Ut = s; s += mv;
     c.beta = s; s += BC;
