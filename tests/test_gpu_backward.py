@@ -106,6 +106,11 @@ CONV_CASES = [
     # each visual tap-gradient block walks every tile of its pair
     StreamConfig("cbwd_many_pairs_bf16", B=20, H=16, dk=128, dv=128, n_text=3, grid=(2, 3, 9), dtype="bf16",
                  seed=98),
+    # one visual token and nothing else: every tap but the centre falls outside the grid
+    StreamConfig("cbwd_one_visual_bf16", B=2, H=1, dk=64, dv=64, n_text=0, grid=(1, 1, 1), dtype="bf16", seed=99),
+    # a column of two latent slices, time-causal: only the a = 1, 2 taps meet the grid
+    StreamConfig("cbwd_column_causal_f32", B=1, H=2, dk=128, dv=64, n_text=2, grid=(2, 1, 1), dtype="f32",
+                 causal_t=1, seed=100),
 ]
 
 
