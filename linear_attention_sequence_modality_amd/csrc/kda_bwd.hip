@@ -22,7 +22,7 @@
 // (dQ, dKx, dKy and dKh' are the gradients reaching q and k through Qt, Kt, the
 // column side of A and Bq, and Kh; G enters each of them through its decay.)
 // The decayed products A, Bq, R and C split e(r, s) at a row between r and s
-// (tri_form, tri_rows, tri_cols below), so no factor exceeds the inverse of an
+// (tri_form, tri_rows2, tri_cols2 below), so no factor exceeds the inverse of an
 // 8-token decay: the range is the forward's.
 //
 // Three launches, all fp32 inside:
@@ -165,7 +165,7 @@ __device__ __noinline__ void gemm(float *C, int ldc, const float *A, int lda, co
 // the second factor leaves the fp32 range once a chunk decays by more than 2^-126.  Here
 // the factor is split at a reference row between r and s, with the rows in 16-row blocks:
 //   * r in block i, s in an earlier block j: the last row of block i - 1 (tri_form,
-//     tri_rows) or of block j (tri_cols) lies between them, so both halves are decays;
+//     tri_rows2) or of block j (tri_cols2) lies between them, so both halves are decays;
 //   * r and s in one block: its row 7, so each half is at most the inverse of an
 //     8-token decay (the forward chunk transform's bound).
 // X, Y, G, Z are fp32 row-major [BC][DK] and P, C [BC][BC], in global memory (the
@@ -262,13 +262,17 @@ __device__ __noinline__ void tri_form_k(float *C, const float *X, const float *Y
     __syncthreads();
 }
 
-// Z[r][c] (+)= sum_{s <= r} P[r][s] Y[s][c] e(r, s, c); P is zero above its diagonal.
-// Per 16-column tile, a lane reads its 16 rows of Y and G once (rows 16 j + 4 (l/16) + v:
-// the contraction rows of every block j and, the same rows, its outputs).
+// Z1[r][c] = sum_{s <= r} P1[r][s] Y[s][c] e(r, s, c) and Z2 the same with P2 (P1, P2 zero
+// above their diagonals): the two row-side products that share Y, so the decayed operand
+// Y[s][c] e(ref, s, c) is formed once for both.  Per 16-column tile, a lane reads its 16 rows
+// of Y and G once (rows 16 j + 4 (l/16) + v: the contraction rows of every block j and, the
+// same rows, its outputs).
 template <int DK>
-__device__ __noinline__ void tri_rows_k(float *Z, const float *P, const float *Y, const float *G, bool acc) {
+__device__ __noinline__ void tri_rows2_k(float *Z1, const float *P1, float *Z2, const float *P2, const float *Y,
+                                         const float *G) {
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, g = lane / 16, l16 = lane % 16;
-    const GMat Zm(Z, BC * DK), Pm(P, BC * BC), Ym(Y, BC * DK), Gm(G, BC * DK);
+    const GMat Z1m(Z1, BC * DK), Z2m(Z2, BC * DK), P1m(P1, BC * BC), P2m(P2, BC * BC), Ym(Y, BC * DK),
+        Gm(G, BC * DK);
 #pragma unroll 1
     for (int n = wave; n < DK / 16; n += BT / 64) {
         const int c = 16 * n + l16, lo = 4 * g * DK + c;   // the lane's row 4 g, column c
@@ -287,58 +291,70 @@ __device__ __noinline__ void tri_rows_k(float *Z, const float *P, const float *Y
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float4 pv[4];
+            float4 p1[4], p2[4];
 #pragma unroll
-            for (int j = 0; j <= i; ++j) pv[j] = Pm.at4(l16 * BC + 4 * g, 16 * i * BC + 16 * j);
-            f32x4_t off = zero4(), dia = zero4();
+            for (int j = 0; j <= i; ++j) {
+                p1[j] = P1m.at4(l16 * BC + 4 * g, 16 * i * BC + 16 * j);
+                p2[j] = P2m.at4(l16 * BC + 4 * g, 16 * i * BC + 16 * j);
+            }
+            f32x4_t off1 = zero4(), dia1 = zero4(), off2 = zero4(), dia2 = zero4();
 #pragma unroll
             for (int j = 0; j <= i; ++j) {
                 const float gref = j < i ? ge[i] : gm[i];
-                float b[4];
+                float bv[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) b[v] = yv[4 * j + v] * ex2(gref - gv[4 * j + v]);
-                f32x4_t &t = j < i ? off : dia;
-                t = mma4(pv[j].x, b[0], t);
-                t = mma4(pv[j].y, b[1], t);
-                t = mma4(pv[j].z, b[2], t);
-                t = mma4(pv[j].w, b[3], t);
+                for (int v = 0; v < 4; ++v) bv[v] = yv[4 * j + v] * ex2(gref - gv[4 * j + v]);
+                f32x4_t &t1 = j < i ? off1 : dia1;
+                f32x4_t &t2 = j < i ? off2 : dia2;
+                t1 = mma4(p1[j].x, bv[0], t1);
+                t1 = mma4(p1[j].y, bv[1], t1);
+                t1 = mma4(p1[j].z, bv[2], t1);
+                t1 = mma4(p1[j].w, bv[3], t1);
+                t2 = mma4(p2[j].x, bv[0], t2);
+                t2 = mma4(p2[j].y, bv[1], t2);
+                t2 = mma4(p2[j].z, bv[2], t2);
+                t2 = mma4(p2[j].w, bv[3], t2);
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float gr = gv[4 * i + q];
-                float z = ex2(gr - gm[i]) * dia[q];
-                if (i) z += ex2(gr - ge[i]) * off[q];
+                const float gr = gv[4 * i + q], edia = ex2(gr - gm[i]), eoff = i ? ex2(gr - ge[i]) : 0.f;
+                float z1 = edia * dia1[q], z2 = edia * dia2[q];
+                if (i) {
+                    z1 += eoff * off1[q];
+                    z2 += eoff * off2[q];
+                }
                 const int ro = (16 * i + q) * DK;
-                Zm.put(acc ? Zm.at(lo, ro) + z : z, lo, ro);
+                Z1m.put(z1, lo, ro);
+                Z2m.put(z2, lo, ro);
             }
         }
     }
     __syncthreads();
 }
 
-// Z[s][c] (+)= sum_{r >= s} P[r][s] X[r][c] e(r, s, c); P is zero above its diagonal.
-// The lane's P entries of the 10 block pairs are read once; per 16-column tile, its 16 rows
-// of X and G once.
+// Z[s][c] = sum_{r >= s} (P1[r][s] X1[r][c] + P2[r][s] X2[r][c]) e(r, s, c) (P1, P2 zero above
+// their diagonals): the two column-side products that accumulate into one output, so the
+// decay factor e(r, ref, c) is formed once for both and Z is written once.  Per 16-column
+// tile, the lane reads its 16 rows of X1, X2 and G once, and per output block column j its
+// P1 and P2 entries of the block pairs (i >= j, j) just before their products.
+// (inlined into its one caller: as a call it would need more scalar registers than a callee
+// may use without saving the caller's)
 template <int DK>
-__device__ __noinline__ void tri_cols_k(float *Z, const float *P, const float *X, const float *G, bool acc) {
+__device__ __forceinline__ void tri_cols2_k(float *Z, const float *P1, const float *X1, const float *P2, const float *X2,
+                                         const float *G) {
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, g = lane / 16, l16 = lane % 16;
-    const GMat Zm(Z, BC * DK), Pm(P, BC * BC), Xm(X, BC * DK), Gm(G, BC * DK);
-    float pa[4][4][4];   // [i][j][v] = P[16 i + 4 g + v][16 j + l16], i >= j
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j <= i; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) pa[i][j][v] = Pm.at(4 * g * BC + l16, (16 * i + v) * BC + 16 * j);
+    const GMat Zm(Z, BC * DK), P1m(P1, BC * BC), P2m(P2, BC * BC), X1m(X1, BC * DK), X2m(X2, BC * DK),
+        Gm(G, BC * DK);
 #pragma unroll 1
     for (int n = wave; n < DK / 16; n += BT / 64) {
         const int c = 16 * n + l16, lo = 4 * g * DK + c;
-        float xv[16], gv[16], gm[4], ge[4];
+        float x1[16], x2[16], gv[16], gm[4], ge[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                xv[4 * i + v] = Xm.at(lo, (16 * i + v) * DK);
+                x1[4 * i + v] = X1m.at(lo, (16 * i + v) * DK);
+                x2[4 * i + v] = X2m.at(lo, (16 * i + v) * DK);
                 gv[4 * i + v] = Gm.at(lo, (16 * i + v) * DK);
             }
 #pragma unroll
@@ -348,21 +364,32 @@ __device__ __noinline__ void tri_cols_k(float *Z, const float *P, const float *X
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            float pa1[4][4], pa2[4][4];   // [i][v] = P[16 i + 4 g + v][16 j + l16], i >= j
+#pragma unroll
+            for (int i = j; i < 4; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    pa1[i][v] = P1m.at(4 * g * BC + l16, (16 * i + v) * BC + 16 * j);
+                    pa2[i][v] = P2m.at(4 * g * BC + l16, (16 * i + v) * BC + 16 * j);
+                }
             f32x4_t off = zero4(), dia = zero4();
 #pragma unroll
             for (int i = j; i < 4; ++i) {
                 const float gref = i > j ? ge[j] : gm[j];
                 f32x4_t &t = i > j ? off : dia;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) t = mma4(pa[i][j][v], xv[4 * i + v] * ex2(gv[4 * i + v] - gref), t);
+                for (int v = 0; v < 4; ++v) {
+                    const float e = ex2(gv[4 * i + v] - gref);
+                    t = mma4(pa1[i][v], x1[4 * i + v] * e, t);
+                    t = mma4(pa2[i][v], x2[4 * i + v] * e, t);
+                }
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float gs = gv[4 * j + q];
                 float z = ex2(gm[j] - gs) * dia[q];
                 if (j < 3) z += ex2(ge[j] - gs) * off[q];
-                const int ro = (16 * j + q) * DK;
-                Zm.put(acc ? Zm.at(lo, ro) + z : z, lo, ro);
+                Zm.put(z, lo, (16 * j + q) * DK);
             }
         }
     }
@@ -375,17 +402,19 @@ __device__ __forceinline__ void tri_form(float *C, const float *X, const float *
     else
         tri_form_k<64>(C, X, Y, G, strict);
 }
-__device__ __forceinline__ void tri_rows(float *Z, const float *P, const float *Y, const float *G, int DK, bool acc) {
+__device__ __forceinline__ void tri_rows2(float *Z1, const float *P1, float *Z2, const float *P2, const float *Y,
+                                          const float *G, int DK) {
     if (DK == 128)
-        tri_rows_k<128>(Z, P, Y, G, acc);
+        tri_rows2_k<128>(Z1, P1, Z2, P2, Y, G);
     else
-        tri_rows_k<64>(Z, P, Y, G, acc);
+        tri_rows2_k<64>(Z1, P1, Z2, P2, Y, G);
 }
-__device__ __forceinline__ void tri_cols(float *Z, const float *P, const float *X, const float *G, int DK, bool acc) {
+__device__ __forceinline__ void tri_cols2(float *Z, const float *P1, const float *X1, const float *P2, const float *X2,
+                                          const float *G, int DK) {
     if (DK == 128)
-        tri_cols_k<128>(Z, P, X, G, acc);
+        tri_cols2_k<128>(Z, P1, X1, P2, X2, G);
     else
-        tri_cols_k<64>(Z, P, X, G, acc);
+        tri_cols2_k<64>(Z, P1, X1, P2, X2, G);
 }
 
 __device__ __forceinline__ float ld(const float *p) { return *p; }
@@ -941,10 +970,8 @@ __global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
             P[e] = s2 < r ? c.beta[r] * dM[e] : 0.f;
         }
         __syncthreads();
-        tri_rows(dKx, P, c.K, c.G, DK, false);          // R(dA, K)
-        tri_rows(dQi, dBq, c.K, c.G, DK, false);        // R(dBq, K)
-        tri_cols(dKy, P, c.K, c.G, DK, false);          // C(dA, K)
-        tri_cols(dKy, dBq, c.Q, c.G, DK, true);         //  + C(dBq, Q)
+        tri_rows2(dKx, P, dQi, dBq, c.K, c.G, DK);      // R(dA, K), R(dBq, K)
+        tri_cols2(dKy, P, c.K, dBq, c.Q, c.G, DK);      // C(dA, K) + C(dBq, Q)
         // the panel area as scratch from here on: dG [BC][DK], alpha [BC][DK], partial sums
         float *lw = &tA[0][0];
         float *dGl = lw, *alpha_l = lw + BC * DK, *part = lw + 2 * BC * DK;   // part: 4 BC + 4 DK + 2 DK floats
