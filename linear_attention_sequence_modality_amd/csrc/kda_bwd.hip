@@ -158,6 +158,82 @@ __device__ __noinline__ void gemm(float *C, int ldc, const float *A, int lda, co
         }
 }
 
+// C1 = s1 A1 B^T and C2 = s2 A2 B^T (A1, A2 row-major M x K, B row-major N x K, as gemm's
+// TA = false, TB = true): two products that share B^T, so each step stages B's panel once for
+// both.  The second A's panels use the other half of the A panel area (rows 2 kKc ..).
+__device__ __noinline__ void gemm2_nt(float *C1, float s1, const float *A1, float *C2, float s2, const float *A2,
+                                      int lda, const float *B, int ldb, int ldc, int M, int N, int K,
+                                      float (*tA)[kPs], float (*tB)[kPs]) {
+    static_assert(4 * kKc <= kPanel, "two double-buffered A panels fit the panel area");
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, g = lane / 16, l16 = lane % 16;
+    const int wm = 32 * (wave / 2), wn = 32 * (wave % 2);
+    const int nk = K / kKc;
+    // this thread's pieces of the second A's kKc x 64 panel (as panel_fetch / panel_store
+    // do for A with TA = false)
+    auto fetch2 = [&](int m0, int k0, float4 (&v)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = threadIdx.x + BT * i;
+            v[i] = ld4f(A2 + (size_t)(m0 + e / 8) * lda + k0 + 4 * (e % 8));
+        }
+    };
+    auto store2 = [&](float (*pa)[kPs], const float4 (&v)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = threadIdx.x + BT * i, mm = e / 8, q = e % 8;
+            pa[4 * q][mm] = v[i].x;
+            pa[4 * q + 1][mm] = v[i].y;
+            pa[4 * q + 2][mm] = v[i].z;
+            pa[4 * q + 3][mm] = v[i].w;
+        }
+    };
+    for (int m0 = 0; m0 < M; m0 += 64)
+        for (int n0 = 0; n0 < N; n0 += 64) {
+            float4 va[2], vb[2], va2[2];
+            panel_fetch<false, true>(A1, lda, B, ldb, m0, n0, 0, va, vb);
+            fetch2(m0, 0, va2);
+            f32x4_t c1[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};
+            f32x4_t c2[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};
+            for (int kc = 0; kc < nk; ++kc) {
+                float(*pa)[kPs] = tA + (kc & 1) * kKc;
+                float(*pa2)[kPs] = tA + 2 * kKc + (kc & 1) * kKc;
+                float(*pb)[kPs] = tB + (kc & 1) * kKc;
+                panel_store<false, true>(pa, pb, va, vb);
+                store2(pa2, va2);
+                __syncthreads();
+                // the next step's panels (the last step fetches its own again: no branch)
+                const int k1 = min(kc + 1, nk - 1) * kKc;
+                panel_fetch<false, true>(A1, lda, B, ldb, m0, n0, k1, va, vb);
+                fetch2(m0, k1, va2);
+#pragma unroll 4
+                for (int k = 0; k < kKc; k += 4) {
+                    const float b0 = pb[k + g][wn + l16], b1 = pb[k + g][wn + 16 + l16];
+                    const float a0 = pa[k + g][wm + l16], a1 = pa[k + g][wm + 16 + l16];
+                    const float d0 = pa2[k + g][wm + l16], d1 = pa2[k + g][wm + 16 + l16];
+                    c1[0][0] = mma4(a0, b0, c1[0][0]);
+                    c1[0][1] = mma4(a0, b1, c1[0][1]);
+                    c1[1][0] = mma4(a1, b0, c1[1][0]);
+                    c1[1][1] = mma4(a1, b1, c1[1][1]);
+                    c2[0][0] = mma4(d0, b0, c2[0][0]);
+                    c2[0][1] = mma4(d0, b1, c2[0][1]);
+                    c2[1][0] = mma4(d1, b0, c2[1][0]);
+                    c2[1][1] = mma4(d1, b1, c2[1][1]);
+                }
+            }
+#pragma unroll
+            for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+                for (int bn = 0; bn < 2; ++bn)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const size_t o = (size_t)(m0 + wm + 16 * bm + 4 * g + i) * ldc + n0 + wn + 16 * bn + l16;
+                        C1[o] = s1 * c1[bm][bn][i];
+                        C2[o] = s2 * c2[bm][bn][i];
+                    }
+            __syncthreads();
+        }
+}
+
 // ---- decayed triangular products ---------------------------------------------------
 //
 // Row r of a chunk sees an earlier row s <= r of channel c through the decay
@@ -951,9 +1027,8 @@ __global__ __launch_bounds__(BT, 2) void bwd_intra_kernel(KdaBwdArgs a) {
         gemm<true, false>(dU, DV, c.Bq, BC, dO, DV, BC, DV, BC, 1.f, false, kNoMask, tA, tB);       // dU = Bq^T dO
         gemm<false, false>(dU, DV, c.Kh, DK, dSp, DV, BC, DV, DK, 1.f, true, kNoMask, tA, tB);      //    + Kh dS'
         gemm<false, true>(dBq, BC, dO, DV, U, DV, BC, BC, DV, 1.f, false, kLower, tA, tB);          // dBq
-        gemm<false, true>(dQt, DK, dO, DV, Sn, DV, BC, DK, DV, 1.f, false, kNoMask, tA, tB);        // dQt = dO S^T
+        gemm2_nt(dQt, 1.f, dO, dW, -1.f, dU, DV, Sn, DV, DK, BC, DK, DV, tA, tB);                   // dQt = dO S^T, dW = -dU S^T
         gemm<false, true>(dKh, DK, U, DV, dSp, DV, BC, DK, DV, 1.f, false, kNoMask, tA, tB);        // dKh = U dS'^T
-        gemm<false, true>(dW, DK, dU, DV, Sn, DV, BC, DK, DV, -1.f, false, kNoMask, tA, tB);        // dW = -dU S^T
         // dTm = dU X^T + dW Y^T = (dU V^T + dW Kt^T) Diag(beta), and Tm^T dTm takes the same column
         // scaling: the products run on V and Kt, and beta scales the columns of Tm^T dTm
         gemm<false, true>(dTm, BC, dU, DV, c.V, DV, BC, BC, DV, 1.f, false, kNoMask, tA, tB);       // dU V^T
