@@ -22,7 +22,7 @@
 // (dQ, dKx, dKy and dKh' are the gradients reaching q and k through Qt, Kt, the
 // column side of A and Bq, and Kh; G enters each of them through its decay.)
 // The decayed products A, Bq, R and C split e(r, s) at a row between r and s
-// (tri_form, tri_rows2, tri_cols2 below), so no factor exceeds the inverse of an
+// (tri_form2, tri_rows2, tri_cols2 below), so no factor exceeds the inverse of an
 // 8-token decay: the range is the forward's.
 //
 // Three launches, all fp32 inside:
@@ -240,7 +240,7 @@ __device__ __noinline__ void gemm2_nt(float *C1, float s1, const float *A1, floa
 // e(r, s, c) = 2^(G[r][c] - G[s][c]) <= 1.  Formed as 2^G times 2^-G over the whole chunk,
 // the second factor leaves the fp32 range once a chunk decays by more than 2^-126.  Here
 // the factor is split at a reference row between r and s, with the rows in 16-row blocks:
-//   * r in block i, s in an earlier block j: the last row of block i - 1 (tri_form,
+//   * r in block i, s in an earlier block j: the last row of block i - 1 (tri_form2,
 //     tri_rows2) or of block j (tri_cols2) lies between them, so both halves are decays;
 //   * r and s in one block: its row 7, so each half is at most the inverse of an
 //     8-token decay (the forward chunk transform's bound).
@@ -296,43 +296,54 @@ __device__ __forceinline__ void block_pair(int p, int &i, int &j) {
     }
 }
 
-// C[r][s] = sum_c X[r][c] Y[s][c] e(r, s, c) for s <= r (s < r when strict), 0 above.
-// The contraction runs over channels; every load of a pair is issued before its products.
+// A[r][s] = sum_c K[r][c] K[s][c] e(r, s, c) for s < r and Bq[r][s] = sum_c Q[r][c] K[s][c]
+// e(r, s, c) for s <= r, 0 above: one pass, since both read the same rows of K (as the
+// right factor) and of G, so the decayed right factor and the left decay are formed once.
+// Every load of a block pair is issued before its products.
 template <int DK>
-__device__ __noinline__ void tri_form_k(float *C, const float *X, const float *Y, const float *G, bool strict) {
+__device__ __noinline__ void tri_form2_k(float *Ac, float *Bc, const float *K, const float *Q, const float *G) {
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, g = lane / 16, l16 = lane % 16;
-    const GMat Cm(C, BC * BC), Xm(X, BC * DK), Ym(Y, BC * DK), Gm(G, BC * DK);
+    const GMat Am(Ac, BC * BC), Bm(Bc, BC * BC), Km(K, BC * DK), Qm(Q, BC * DK), Gm(G, BC * DK);
     constexpr int NU = DK / 16;
     for (int p = wave; p < 16; p += BT / 64) {
         int i, j;
         block_pair(p, i, j);
-        f32x4_t acc = zero4();
+        f32x4_t acc = zero4(), bcc = zero4();
         if (j <= i) {
             const int ref = j < i ? 16 * i - 1 : 16 * i + 7;
             const int xo = (16 * i + l16) * DK + 4 * g, yo = (16 * j + l16) * DK + 4 * g, ro = ref * DK + 4 * g;
-            float4 xv[NU], xg[NU], yv[NU], yg[NU], rg[NU];
+            float4 kx[NU], qx[NU], xg[NU], yv[NU], yg[NU], rg[NU];
 #pragma unroll
             for (int t = 0; t < NU; ++t) {
-                xv[t] = Xm.at4(xo, 16 * t);
+                kx[t] = Km.at4(xo, 16 * t);
+                qx[t] = Qm.at4(xo, 16 * t);
                 xg[t] = Gm.at4(xo, 16 * t);
-                yv[t] = Ym.at4(yo, 16 * t);
+                yv[t] = Km.at4(yo, 16 * t);
                 yg[t] = Gm.at4(yo, 16 * t);
                 rg[t] = Gm.at4(ro, 16 * t);
             }
 #pragma unroll
             for (int t = 0; t < NU; ++t) {
-                acc = mma4(xv[t].x * ex2(xg[t].x - rg[t].x), yv[t].x * ex2(rg[t].x - yg[t].x), acc);
-                acc = mma4(xv[t].y * ex2(xg[t].y - rg[t].y), yv[t].y * ex2(rg[t].y - yg[t].y), acc);
-                acc = mma4(xv[t].z * ex2(xg[t].z - rg[t].z), yv[t].z * ex2(rg[t].z - yg[t].z), acc);
-                acc = mma4(xv[t].w * ex2(xg[t].w - rg[t].w), yv[t].w * ex2(rg[t].w - yg[t].w), acc);
+                const float ex[4] = {ex2(xg[t].x - rg[t].x), ex2(xg[t].y - rg[t].y), ex2(xg[t].z - rg[t].z),
+                                     ex2(xg[t].w - rg[t].w)};
+                const float y[4] = {yv[t].x * ex2(rg[t].x - yg[t].x), yv[t].y * ex2(rg[t].y - yg[t].y),
+                                    yv[t].z * ex2(rg[t].z - yg[t].z), yv[t].w * ex2(rg[t].w - yg[t].w)};
+                const float kk[4] = {kx[t].x, kx[t].y, kx[t].z, kx[t].w};
+                const float qq[4] = {qx[t].x, qx[t].y, qx[t].z, qx[t].w};
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    acc = mma4(kk[v] * ex[v], y[v], acc);
+                    bcc = mma4(qq[v] * ex[v], y[v], bcc);
+                }
             }
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int r = 16 * i + 4 * g + q, s2 = 16 * j + l16;
-            // a select, not a product: inside a diagonal block the terms above the
+            // selects, not products: inside a diagonal block the terms above the
             // diagonal may overflow
-            Cm.put((s2 > r || (strict && s2 == r)) ? 0.f : acc[q], r * BC + s2, 0);
+            Am.put(s2 >= r ? 0.f : acc[q], r * BC + s2, 0);
+            Bm.put(s2 > r ? 0.f : bcc[q], r * BC + s2, 0);
         }
     }
     __syncthreads();
@@ -472,11 +483,11 @@ __device__ __forceinline__ void tri_cols2_k(float *Z, const float *P1, const flo
     __syncthreads();
 }
 
-__device__ __forceinline__ void tri_form(float *C, const float *X, const float *Y, const float *G, int DK, bool strict) {
+__device__ __forceinline__ void tri_form2(float *Ac, float *Bc, const float *K, const float *Q, const float *G, int DK) {
     if (DK == 128)
-        tri_form_k<128>(C, X, Y, G, strict);
+        tri_form2_k<128>(Ac, Bc, K, Q, G);
     else
-        tri_form_k<64>(C, X, Y, G, strict);
+        tri_form2_k<64>(Ac, Bc, K, Q, G);
 }
 __device__ __forceinline__ void tri_rows2(float *Z1, const float *P1, float *Z2, const float *P2, const float *Y,
                                           const float *G, int DK) {
@@ -614,8 +625,7 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
     }
     __syncthreads();
     if (FULL) {
-        tri_form(c.A, c.K, c.K, c.G, DK, true);
-        tri_form(c.Bq, c.Q, c.K, c.G, DK, false);
+        tri_form2(c.A, c.Bq, c.K, c.Q, c.G, DK);
     }
     if (FULL)
     // Tm = (I + Diag(beta) A)^-1 (unit lower triangular) by forward substitution: lane j of
