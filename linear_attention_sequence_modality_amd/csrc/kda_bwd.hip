@@ -34,7 +34,9 @@
 //   3. bwd_intra:   per (batch, head, chunk), in parallel: the gradients of the
 //                   chunk's tokens.
 // The dense products run through one LDS-tiled fp32 routine (64 x 64 output
-// tiles on the fp32 matrix cores); all arithmetic is fp32.
+// tiles on the fp32 matrix cores; a two-output form for a pair that shares its
+// right operand), and products that share operands are formed in one pass
+// (tri_form2, tri_rows2, tri_cols2, gemm2_nt); all arithmetic is fp32.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
