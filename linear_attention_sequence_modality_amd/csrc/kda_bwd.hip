@@ -34,9 +34,9 @@
 //   3. bwd_intra:   per (batch, head, chunk), in parallel: the gradients of the
 //                   chunk's tokens.
 // The dense products run through one LDS-tiled fp32 routine (64 x 64 output
-// tiles on the fp32 matrix cores; a two-output form for a pair that shares its
-// right operand), and products that share operands are formed in one pass
-// (tri_form2, tri_rows2, tri_cols2, gemm2_nt); all arithmetic is fp32.
+// tiles on the fp32 matrix cores; two-output forms for pairs that share an
+// operand), and products that share operands are formed in one pass
+// (tri_form2, tri_rows2, tri_cols2, gemm2_nt, gemm2_nn); all arithmetic is fp32.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -231,6 +231,80 @@ __device__ __noinline__ void gemm2_nt(float *C1, float s1, const float *A1, floa
                         const size_t o = (size_t)(m0 + wm + 16 * bm + 4 * g + i) * ldc + n0 + wn + 16 * bn + l16;
                         C1[o] = s1 * c1[bm][bn][i];
                         C2[o] = s2 * c2[bm][bn][i];
+                    }
+            __syncthreads();
+        }
+}
+
+// C1 = A B1 and C2 = A B2 (A row-major M x K, B1, B2 row-major K x N, as gemm's TA = false,
+// TB = false; both C with leading dimension ldc): two products that share A, so each step
+// stages A's panel once for both.  The second B's panels use the other half of the B panel
+// area (rows 2 kKc ..).
+__device__ __noinline__ void gemm2_nn(float *C1, float *C2, int ldc, const float *A, int lda, const float *B1,
+                                      const float *B2, int ldb, int M, int N, int K, float (*tA)[kPs],
+                                      float (*tB)[kPs]) {
+    static_assert(4 * kKc <= kPanel, "two double-buffered B panels fit the panel area");
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, g = lane / 16, l16 = lane % 16;
+    const int wm = 32 * (wave / 2), wn = 32 * (wave % 2);
+    const int nk = K / kKc;
+    // this thread's pieces of the second B's kKc x 64 panel (as panel_fetch / panel_store
+    // do for B with TB = false)
+    auto fetch2 = [&](int n0, int k0, float4 (&v)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = threadIdx.x + BT * i;
+            v[i] = ld4f(B2 + (size_t)(k0 + e / 16) * ldb + n0 + 4 * (e % 16));
+        }
+    };
+    auto store2 = [&](float (*pb)[kPs], const float4 (&v)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = threadIdx.x + BT * i;
+            *reinterpret_cast<float4 *>(&pb[e / 16][4 * (e % 16)]) = v[i];
+        }
+    };
+    for (int m0 = 0; m0 < M; m0 += 64)
+        for (int n0 = 0; n0 < N; n0 += 64) {
+            float4 va[2], vb[2], vb2[2];
+            panel_fetch<false, false>(A, lda, B1, ldb, m0, n0, 0, va, vb);
+            fetch2(n0, 0, vb2);
+            f32x4_t c1[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};
+            f32x4_t c2[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};
+            for (int kc = 0; kc < nk; ++kc) {
+                float(*pa)[kPs] = tA + (kc & 1) * kKc;
+                float(*pb)[kPs] = tB + (kc & 1) * kKc;
+                float(*pb2)[kPs] = tB + 2 * kKc + (kc & 1) * kKc;
+                panel_store<false, false>(pa, pb, va, vb);
+                store2(pb2, vb2);
+                __syncthreads();
+                // the next step's panels (the last step fetches its own again: no branch)
+                const int k1 = min(kc + 1, nk - 1) * kKc;
+                panel_fetch<false, false>(A, lda, B1, ldb, m0, n0, k1, va, vb);
+                fetch2(n0, k1, vb2);
+#pragma unroll 2
+                for (int k = 0; k < kKc; k += 4) {
+                    const float a0 = pa[k + g][wm + l16], a1 = pa[k + g][wm + 16 + l16];
+                    const float b0 = pb[k + g][wn + l16], b1 = pb[k + g][wn + 16 + l16];
+                    const float d0 = pb2[k + g][wn + l16], d1 = pb2[k + g][wn + 16 + l16];
+                    c1[0][0] = mma4(a0, b0, c1[0][0]);
+                    c1[0][1] = mma4(a0, b1, c1[0][1]);
+                    c1[1][0] = mma4(a1, b0, c1[1][0]);
+                    c1[1][1] = mma4(a1, b1, c1[1][1]);
+                    c2[0][0] = mma4(a0, d0, c2[0][0]);
+                    c2[0][1] = mma4(a0, d1, c2[0][1]);
+                    c2[1][0] = mma4(a1, d0, c2[1][0]);
+                    c2[1][1] = mma4(a1, d1, c2[1][1]);
+                }
+            }
+#pragma unroll
+            for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+                for (int bn = 0; bn < 2; ++bn)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const size_t o = (size_t)(m0 + wm + 16 * bm + 4 * g + i) * ldc + n0 + wn + 16 * bn + l16;
+                        C1[o] = c1[bm][bn][i];
+                        C2[o] = c2[bm][bn][i];
                     }
             __syncthreads();
         }
@@ -676,8 +750,12 @@ __device__ void chunk_forward(const KdaBwdArgs &a, const ChunkMats &c, int bh, i
     }
     __syncthreads();
     if (FULL) {   // (the gradient kernel folds beta into its products instead)
-        gemm<false, false>(c.W, DK, c.TmB, BC, c.Kt, DK, BC, DK, BC, 1.f, false, kNoMask, tA, tB);
-        gemm<false, false>(c.Ut, DV, c.TmB, BC, c.V, DV, BC, DV, BC, 1.f, false, kNoMask, tA, tB);
+        if (DK == DV) {   // one pass staging Tm Diag(beta) once for both
+            gemm2_nn(c.W, c.Ut, DK, c.TmB, BC, c.Kt, c.V, DK, BC, DK, BC, tA, tB);
+        } else {
+            gemm<false, false>(c.W, DK, c.TmB, BC, c.Kt, DK, BC, DK, BC, 1.f, false, kNoMask, tA, tB);
+            gemm<false, false>(c.Ut, DV, c.TmB, BC, c.V, DV, BC, DV, BC, 1.f, false, kNoMask, tA, tB);
+        }
     }
 }
 
